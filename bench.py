@@ -1,0 +1,175 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA chunked forward on one MI355X.
+
+One step = one kda_fwd call (both kernels: intra-chunk stage and scan) over
+the T=8192, H=96, D=128 fixed-length workload with a bf16 initial state and
+an fp32 final state, inputs already resident in HBM.  Prints ONE JSON line.
+
+Roofline accounting (algorithmic bytes, i.e. what the operation must move):
+  per (token, head): q, k, g, v 4 x 256 B, beta 2 B, out 256 B   = 1282 B
+  per (sequence, head): initial state (bf16 32 KiB) if given, final state
+  (fp32 64 KiB) if requested.
+  Split per kernel: the intra-chunk kernel must read q, k, g, beta (770 B);
+  the scan must read v and write out (512 B) plus the states.  The hand-off
+  records between the two kernels are design overhead, not algorithmic.
+Per-kernel durations come from HIP events the library records around each
+kernel (kda_set_stage_events) on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "KDA fwd tokens/s @T=8192,H=96,D=128 (fixed+varlen); % of MFMA/HBM roofline"
+CHUNK = 16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(w, has_init=True, has_final=True):
+    th = w.tokens * w.H
+    n_units = w.num_seqs * w.H
+    state_in = n_units * w.K * w.V * 2 if (has_init and w.initial_state) else 0
+    state_out = n_units * w.K * w.V * 4 if has_final else 0
+    intra = th * (3 * w.K * 2 + 2)
+    scan = th * (2 * w.V * 2) + state_in + state_out
+    # MACs per token-head of the chunkwise algorithm at chunk C: three state
+    # products, the two in-chunk Gram products at triangular useful size, the
+    # T-apply and Aqk E products, and the C x C inverse.
+    C = CHUNK
+    macs = 3 * w.K * w.V + C * w.K + (C + 1) * w.V + C * C / 6.0
+    return {"intra_bytes": intra, "scan_bytes": scan, "total_bytes": intra + scan,
+            "flops": 2.0 * macs * th}
+
+
+def cpu_baseline(inp, w, heads: int):
+    import oracle
+    sel = list(range(min(heads, w.H)))
+    t0 = time.perf_counter()
+    oracle.cref_forward(inp, heads=sel, want_final=True)
+    dt = time.perf_counter() - t0
+    # the whole workload takes H / len(sel) times as long (heads are independent)
+    tok_s = w.tokens / (dt * w.H / len(sel))
+    return {"value": tok_s, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{w.name}: heads 0..{len(sel) - 1} of {w.H}, all {w.tokens} tokens, "
+                      f"fp64 C/OpenMP token recurrence, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: the T=8192 H=96 fixed one)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=32, help="heads in the oracle's timed sample")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the KDA forward here runs on a single "
+              "MI355X and no multi-GPU path is built (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kda_inputs
+    import kimi_delta_attention_04_amd as kda
+
+    kda.load()
+    name = args.workload or kda_inputs.HEADLINE
+    w = kda_inputs.WORKLOADS[name]
+    log(f"[bench] generating {name} ...")
+    inp = kda_inputs.generate(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    out = torch.empty(w.B, w.T, w.H, w.V, dtype=torch.bfloat16, device=dev)
+    fin = torch.empty(w.num_seqs, w.H, w.K, w.V, dtype=torch.float32, device=dev)
+
+    def step():
+        kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], out, d["A_log"],
+                d["dt_bias"], d["lower_bound"], initial_state=d["initial_state"],
+                final_state=fin, cu_seqlens=d["cu_seqlens"])
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-step stage events (created by recording once)
+    evs = []
+    for _ in range(args.steps):
+        trip = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for e in trip:
+            e.record()
+        evs.append(trip)
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        kda.set_stage_events(evs[i][0].cuda_event, evs[i][1].cuda_event, evs[i][2].cuda_event)
+        step()
+    kda.set_stage_events(None, None, None)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / args.steps
+    intra_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]
+    scan_ms = [evs[i][1].elapsed_time(evs[i][2]) for i in range(args.steps)]
+    intra_avg = statistics.mean(intra_ms)
+    scan_avg = statistics.mean(scan_ms)
+
+    alg = algorithmic(w)
+    tok_s = w.tokens / (ms * 1e-3)
+    kernels = {
+        "kda_intra": {"ms": intra_avg, "bytes": alg["intra_bytes"]},
+        "kda_scan": {"ms": scan_avg, "bytes": alg["scan_bytes"]},
+    }
+    dom_name = max(kernels, key=lambda k: kernels[k]["ms"])
+    dom = kernels[dom_name]
+    achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom_name,
+                "bytes_per_launch": dom["bytes"], "avg_launch_ms": dom["ms"]}
+    path_gbs = alg["total_bytes"] / (ms * 1e-3) / 1e9
+    path_tflops = alg["flops"] / (ms * 1e-3) / 1e12
+    path = {"algorithmic_bytes": alg["total_bytes"], "hbm_achieved_GBs": path_gbs,
+            "hbm_frac": path_gbs / HBM_PEAK_GBS, "algorithmic_flops": alg["flops"],
+            "mfma_achieved_TFLOPs": path_tflops, "mfma_frac": path_tflops / BF16_PEAK_TFLOPS,
+            "stage_ms": {k: v["ms"] for k, v in kernels.items()},
+            "stage_ms_min": {"kda_intra": min(intra_ms), "kda_scan": min(scan_ms)}}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] oracle CPU baseline on {args.cpu_heads} heads")
+        cpu = cpu_baseline(inp, w, args.cpu_heads)
+
+    cfg = w.describe()
+    rec = {"metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic (seeded; shapes of the pages' workloads)",
+           "config": cfg, "roofline": roofline, "cpu_baseline": cpu, "path": path}
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * libkda — Kimi Delta Attention (KDA) chunked forward (prefill) for AMD
+ * MI355X (gfx950).
+ *
+ * Operation (per sequence n, head h; state S is K x V, here K = V = 128):
+ *
+ *   a_t[c]  = max(-exp(A_log[h]) * softplus(g_t[c] + dt_bias[h*K + c]),
+ *                 lower_bound)                      (log-decay, natural log)
+ *   beta_t  = sigmoid(beta_logit_t)
+ *   S_t     = (I - beta_t k_t k_t^T) Diag(exp(a_t)) S_{t-1} + beta_t k_t v_t^T
+ *   o_t     = scale * S_t^T q_t
+ *
+ * The argument list follows the flash_kda.fwd call described in "Moonshot AI
+ * Rilis FlashKDA" (API paragraphs): q, k, v, g (gate before activation) and
+ * beta logits in bf16, an fp32 scale, a caller-allocated bf16 output, fp32
+ * gate parameters A_log / dt_bias / lower_bound, optional initial and final
+ * recurrent states in bf16 or fp32, and cu_seqlens for variable-length
+ * batches.  The pages name the gate parameters but not the gate formula; the
+ * clamped softplus form above is the reading this library implements.  The
+ * head dimension is fixed at K = V = 128 ("Moonshot AI Open-Sources
+ * FlashKDA", section "Limitations before you integrate"); only the forward
+ * pass exists (same section).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are device pointers unless stated; every tensor is dense and
+ *     row-major with the last dimension contiguous.  q, k, v, g, out and the
+ *     state buffers must be 16-byte aligned; beta 2-byte; A_log, dt_bias and
+ *     cu_seqlens 4-byte.
+ *   - The caller owns every buffer.  The library never keeps a pointer past
+ *     the call and never frees caller memory.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     legacy default stream of the current device).  Outputs are valid once
+ *     the stream has completed the enqueued work.  No host synchronisation.
+ *   - Host-side argument validation happens before any HIP call; nothing
+ *     throws across the ABI.  Device-side contents (cu_seqlens values) are
+ *     preconditions, not checked.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1,   /* NULL/misaligned pointer, bad size or enum */
+    KDA_ERR_UNSUPPORTED = 2,   /* valid but outside what the kernels handle */
+    KDA_ERR_LAUNCH = 3,        /* a HIP launch or runtime call failed */
+    KDA_ERR_OUT_OF_MEMORY = 4  /* the stream-ordered workspace could not be allocated */
+} kda_status_t;
+
+typedef enum {
+    KDA_DTYPE_BF16 = 0,
+    KDA_DTYPE_FP32 = 1
+} kda_dtype_t;
+
+/*
+ * kda_fwd — KDA forward over a batch of sequences.
+ *
+ * Layout:
+ *   q, k, g     bf16 [B, T, H, K]
+ *   v           bf16 [B, T, H, V]
+ *   beta        bf16 [B, T, H]       logits; the sigmoid is applied inside
+ *   out         bf16 [B, T, H, V]    caller-allocated; every row in
+ *                                    [0, B*T) is written exactly once
+ *   A_log       fp32 [H]             per-head decay scale (A = exp(A_log))
+ *   dt_bias     fp32 [H*K]           per (head, channel), index h*K + c;
+ *                                    NULL means zeros
+ *   scale       host fp32, finite
+ *   lower_bound host fp32: finite, <= 0 and >= kda_lower_bound_min()
+ *   cu_seqlens  int32 [num_seqs + 1] prefix offsets into the packed token
+ *               axis, or NULL.  Non-NULL requires B == 1; then sequence n is
+ *               tokens [cu[n], cu[n+1]).  Preconditions (not checked):
+ *               cu[0] = 0, non-decreasing, cu[num_seqs] = T.  Zero-length
+ *               sequences are allowed.  NULL means B sequences of T tokens.
+ *   num_seqs    N: B when cu_seqlens is NULL, else len(cu_seqlens) - 1
+ *   initial_state  [N, H, K, V] in initial_state_dtype, or NULL (= zeros)
+ *   final_state    [N, H, K, V] in final_state_dtype, or NULL (not written);
+ *                  when given, every slab is written (a zero-length sequence
+ *                  gets its initial state)
+ *   B, T, H, K, V  sizes; K and V must both be 128.  When B*T == 0 the
+ *                  token buffers (q, k, v, g, beta, out) may be NULL; the
+ *                  call then only writes final_state (= initial state)
+ *
+ * The state of each sequence starts from initial_state (or zeros) and does
+ * not leak across sequences.  Internally the call takes a stream-ordered
+ * workspace of kda_workspace_size(B, T, H, num_seqs) bytes from a
+ * library-owned memory pool on the current device and returns it on the
+ * same stream.
+ *
+ * Returns KDA_OK, or KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED before any
+ * HIP call, KDA_ERR_OUT_OF_MEMORY, or KDA_ERR_LAUNCH.
+ */
+kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g,
+                     const void *beta, float scale,
+                     const float *A_log, const float *dt_bias, float lower_bound,
+                     const int32_t *cu_seqlens, int32_t num_seqs,
+                     const void *initial_state, kda_dtype_t initial_state_dtype,
+                     void *final_state, kda_dtype_t final_state_dtype,
+                     void *out,
+                     int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                     void *stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *kda_status_string(kda_status_t status);
+
+/*
+ * Smallest lower_bound the kernels accept.  Within one 16-token chunk the
+ * kernels factor exp(G_r - G_i) as exp(G_r) * exp(-G_i) with G the in-chunk
+ * cumulative log-decay, so 16 * |lower_bound| must keep both factors inside
+ * the fp32 / bf16 normal range.
+ */
+float kda_lower_bound_min(void);
+
+/* Tokens per chunk of the chunkwise algorithm (16). */
+int32_t kda_chunk_size(void);
+
+/*
+ * Bytes of device workspace one kda_fwd call with these sizes takes from
+ * the pool (the intra-chunk hand-off records).  0 on invalid sizes.
+ */
+size_t kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs);
+
+/*
+ * kda_debug_intra — test entry: runs only the intra-chunk stage (gate,
+ * in-chunk cumulative decay, A_kk / A_qk products, triangular inverse) and
+ * writes its hand-off records into the caller's `workspace` (device,
+ * kda_workspace_size(...) bytes, 16-byte aligned).  Arguments as kda_fwd.
+ * Record layout (per chunk slot and head, 13824 bytes) is described in the
+ * library source; tests decode it to compare each stage with fp64 maths.
+ */
+kda_status_t kda_debug_intra(const void *q, const void *k, const void *g,
+                             const void *beta,
+                             const float *A_log, const float *dt_bias, float lower_bound,
+                             const int32_t *cu_seqlens, int32_t num_seqs,
+                             int32_t B, int32_t T, int32_t H, int32_t K,
+                             void *workspace, void *stream);
+
+/*
+ * kda_set_stage_events — instrumentation for per-kernel timing.  When set
+ * (non-NULL hipEvent_t handles created by the caller on the device the calls
+ * run on), the next kda_fwd calls made from the calling thread record
+ * `before_intra` before the intra-chunk kernel, `before_scan` between the
+ * intra-chunk and scan kernels and `after_scan` after the scan, all on the
+ * call's stream.  Pass three NULLs to stop.  The setting is per host thread;
+ * the library does not own the events.  Always returns KDA_OK.
+ */
+kda_status_t kda_set_stage_events(void *before_intra, void *before_scan, void *after_scan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

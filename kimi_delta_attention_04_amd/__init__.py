@@ -1,0 +1,188 @@
+"""Python binding of libkda (Kimi Delta Attention forward on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C-ABI declared in include/kda.h.  PyTorch supplies device
+memory and the current HIP stream.  If the built library is missing the
+binding raises; there is no fallback implementation.
+
+    fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+        initial_state=None, final_state=None, cu_seqlens=None)
+
+mirrors the flash_kda.fwd argument list described in "Moonshot AI Rilis
+FlashKDA" (API paragraphs).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["fwd", "debug_intra", "set_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
+           "status_string", "KDAError", "library_path", "load", "HEAD_DIM"]
+
+HEAD_DIM = 128
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libkda.so")
+
+KDA_DTYPE_BF16 = 0
+KDA_DTYPE_FP32 = 1
+_STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
+           3: "KDA_ERR_LAUNCH", 4: "KDA_ERR_OUT_OF_MEMORY"}
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+def load():
+    """Load libkda.so (built by __graft_entry__.build / _build.py)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise ImportError(f"libkda.so is not built ({library_path}); run "
+                          "python -c 'import __graft_entry__ as g; g.build()'")
+    # torch ships its own HIP runtime under the same soname; loading torch
+    # first makes libkda bind to that one copy instead of a second runtime.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(library_path)
+    P, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    lib.kda_fwd.restype = ctypes.c_int
+    lib.kda_fwd.argtypes = [P, P, P, P, P, f32, P, P, f32, P, i32, P, ctypes.c_int, P,
+                            ctypes.c_int, P, i32, i32, i32, i32, i32, P]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_lower_bound_min.restype = f32
+    lib.kda_lower_bound_min.argtypes = []
+    lib.kda_chunk_size.restype = i32
+    lib.kda_chunk_size.argtypes = []
+    lib.kda_workspace_size.restype = ctypes.c_size_t
+    lib.kda_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.kda_set_stage_events.restype = ctypes.c_int
+    lib.kda_set_stage_events.argtypes = [P, P, P]
+    lib.kda_debug_intra.restype = ctypes.c_int
+    lib.kda_debug_intra.argtypes = [P, P, P, P, P, P, f32, P, i32, i32, i32, i32, i32, P, P]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    if _lib is not None:
+        return _lib.kda_status_string(int(status)).decode()
+    return _STATUS.get(int(status), "KDA_ERR_UNKNOWN")
+
+
+def lower_bound_min() -> float:
+    return float(load().kda_lower_bound_min())
+
+
+def chunk_size() -> int:
+    return int(load().kda_chunk_size())
+
+
+def workspace_size(B: int, T: int, H: int, num_seqs: int) -> int:
+    return int(load().kda_workspace_size(B, T, H, num_seqs))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t, name, dtype, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _state_dtype(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return KDA_DTYPE_FP32
+    raise TypeError(f"state tensors must be bf16 or fp32, got {t.dtype}")
+
+
+def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+        initial_state=None, final_state=None, cu_seqlens=None):
+    """KDA forward into `out` (and `final_state` when given); returns out.
+
+    q, k, g: bf16 [B, T, H, K]; v, out: bf16 [B, T, H, V]; beta: bf16
+    [B, T, H] logits; A_log: fp32 [H]; dt_bias: fp32 [H*K] or None;
+    initial_state / final_state: bf16 or fp32 [N, H, K, V] or None;
+    cu_seqlens: int32 [N+1] (B == 1) or None.  Enqueued on the current stream.
+    """
+    import torch
+    lib = load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, K]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    bf = torch.bfloat16
+    _check(q, "q", bf)
+    _check(k, "k", bf, q.shape)
+    _check(g, "g", bf, q.shape)
+    _check(v, "v", bf, (B, T, H, V))
+    _check(out, "out", bf, (B, T, H, V))
+    _check(beta, "beta", bf, (B, T, H))
+    _check(A_log, "A_log", torch.float32, (H,))
+    if dt_bias is not None:
+        _check(dt_bias, "dt_bias", torch.float32, (H * K,))
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    init_dt = fin_dt = KDA_DTYPE_FP32
+    if initial_state is not None:
+        init_dt = _state_dtype(initial_state)
+        _check(initial_state, "initial_state", initial_state.dtype, (N, H, K, V))
+    if final_state is not None:
+        fin_dt = _state_dtype(final_state)
+        _check(final_state, "final_state", final_state.dtype, (N, H, K, V))
+    rc = lib.kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+                     _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(cu_seqlens), int(N),
+                     _ptr(initial_state), init_dt, _ptr(final_state), fin_dt, _ptr(out),
+                     int(B), int(T), int(H), int(K), int(V), _stream(q.device))
+    if rc != 0:
+        raise KDAError(rc, "kda_fwd")
+    return out
+
+
+def set_stage_events(before_intra=None, before_scan=None, after_scan=None):
+    """Raw hipEvent_t handles (ints) recorded around the two kernels by the
+    next kda_fwd calls from this thread; all None to stop."""
+    P = ctypes.c_void_p
+    load().kda_set_stage_events(P(before_intra), P(before_scan), P(after_scan))
+
+
+def debug_intra(q, k, g, beta, A_log, dt_bias, lower_bound, cu_seqlens=None):
+    """Run only the intra-chunk stage; returns its hand-off records as a
+    uint8 device tensor of workspace_size(B, T, H, N) bytes."""
+    import torch
+    lib = load()
+    B, T, H, K = q.shape
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    ws = torch.zeros(workspace_size(B, T, H, N), dtype=torch.uint8, device=q.device)
+    rc = lib.kda_debug_intra(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
+                             float(lower_bound), _ptr(cu_seqlens), int(N), int(B), int(T),
+                             int(H), int(K), _ptr(ws), _stream(q.device))
+    if rc != 0:
+        raise KDAError(rc, "kda_debug_intra")
+    return ws

@@ -1,0 +1,186 @@
+// C-ABI of libkda: argument validation, workspace, launches.
+#include <math.h>
+#include <stdint.h>
+
+#include <mutex>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/kda.h"
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace {
+
+// 16 tokens * |lower_bound| * log2(e) must stay below ~125 so that both
+// 2^G and 2^-G of the in-chunk cumulative decay are normal fp32 / bf16.
+constexpr float kLowerBoundMin = -5.4f;
+constexpr int kMaxDevices = 64;
+
+std::mutex g_pool_mu;
+hipMemPool_t g_pools[kMaxDevices];
+bool g_pool_ready[kMaxDevices];
+
+kda_status_t device_pool(hipMemPool_t *pool) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KDA_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    if (!g_pool_ready[dev]) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t p = nullptr;
+        if (hipMemPoolCreate(&p, &props) != hipSuccess) return KDA_ERR_LAUNCH;
+        uint64_t keep = UINT64_MAX;   // keep freed blocks for reuse by later calls
+        if (hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep) != hipSuccess) {
+            (void)hipMemPoolDestroy(p);
+            return KDA_ERR_LAUNCH;
+        }
+        g_pools[dev] = p;
+        g_pool_ready[dev] = true;
+    }
+    *pool = g_pools[dev];
+    return KDA_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Optional per-thread stage events (kda_set_stage_events).
+thread_local hipEvent_t t_stage_events[3] = {nullptr, nullptr, nullptr};
+
+hipError_t mark(int i, hipStream_t s) {
+    return t_stage_events[i] ? hipEventRecord(t_stage_events[i], s) : hipSuccess;
+}
+
+int64_t num_slots(int32_t B, int32_t T, int32_t N) {
+    return ((int64_t)B * T) / kda::CS + N;
+}
+
+kda_status_t check_sizes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                         const int32_t *cu, int32_t N) {
+    if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID_ARG;
+    if (cu ? (B != 1) : (N != B)) return KDA_ERR_INVALID_ARG;
+    if (K != kda::HD || V != kda::HD) return KDA_ERR_UNSUPPORTED;
+    // token-row and unit counts must fit the int32 grid / index arithmetic
+    if ((int64_t)B * T > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (num_slots(B, T, N) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)N * H > INT32_MAX / 64) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+kda_status_t check_gate(float lower_bound) {
+    if (!isfinite(lower_bound) || lower_bound > 0.f) return KDA_ERR_INVALID_ARG;
+    if (lower_bound < kLowerBoundMin) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(kda_status_t s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH";
+        case KDA_ERR_OUT_OF_MEMORY: return "KDA_ERR_OUT_OF_MEMORY";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+float kda_lower_bound_min(void) { return kLowerBoundMin; }
+
+int32_t kda_chunk_size(void) { return kda::CS; }
+
+size_t kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs) {
+    if (B < 1 || T < 0 || H < 1 || num_seqs < 1) return 0;
+    return (size_t)num_slots(B, T, num_seqs) * (size_t)H * kda::REC_BYTES;
+}
+
+kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g,
+                     const void *beta, float scale,
+                     const float *A_log, const float *dt_bias, float lower_bound,
+                     const int32_t *cu_seqlens, int32_t num_seqs,
+                     const void *initial_state, kda_dtype_t initial_state_dtype,
+                     void *final_state, kda_dtype_t final_state_dtype,
+                     void *out,
+                     int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                     void *stream)
+{
+    // With no tokens the token buffers are never touched and may be NULL.
+    const bool no_tokens = (int64_t)B * T == 0;
+    if (!A_log) return KDA_ERR_INVALID_ARG;
+    if (!no_tokens && (!q || !k || !v || !g || !beta || !out)) return KDA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) ||
+        !aligned(out, 16) || !aligned(beta, 2) || !aligned(A_log, 4) ||
+        !aligned(dt_bias, 4) || !aligned(cu_seqlens, 4) || !aligned(initial_state, 16) ||
+        !aligned(final_state, 16))
+        return KDA_ERR_INVALID_ARG;
+    if ((initial_state_dtype != KDA_DTYPE_BF16 && initial_state_dtype != KDA_DTYPE_FP32) ||
+        (final_state_dtype != KDA_DTYPE_BF16 && final_state_dtype != KDA_DTYPE_FP32))
+        return KDA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    kda_status_t st = check_sizes(B, T, H, K, V, cu_seqlens, num_seqs);
+    if (st != KDA_OK) return st;
+    if ((st = check_gate(lower_bound)) != KDA_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t slots = num_slots(B, T, num_seqs);
+    const size_t bytes = kda_workspace_size(B, T, H, num_seqs);
+    hipMemPool_t pool;
+    if ((st = device_pool(&pool)) != KDA_OK) return st;
+    void *ws = nullptr;
+    if (hipMallocFromPoolAsync(&ws, bytes, pool, s) != hipSuccess || !ws) {
+        (void)hipGetLastError();
+        return KDA_ERR_OUT_OF_MEMORY;
+    }
+    hipError_t e = mark(0, s);
+    if (e == hipSuccess)
+        e = kda::launch_intra((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,
+                              (const uint16_t *)beta, A_log, dt_bias, lower_bound,
+                              cu_seqlens, num_seqs, T, H, slots, (uint8_t *)ws, s);
+    if (e == hipSuccess) e = mark(1, s);
+    if (e == hipSuccess)
+        e = kda::launch_scan((const uint16_t *)v, (const uint8_t *)ws, cu_seqlens, num_seqs, T, H,
+                             scale, initial_state, initial_state_dtype == KDA_DTYPE_FP32,
+                             final_state, final_state_dtype == KDA_DTYPE_FP32,
+                             (uint16_t *)out, s);
+    if (e == hipSuccess) e = mark(2, s);
+    hipError_t ef = hipFreeAsync(ws, s);
+    if (e != hipSuccess || ef != hipSuccess) return KDA_ERR_LAUNCH;
+    return KDA_OK;
+}
+
+kda_status_t kda_debug_intra(const void *q, const void *k, const void *g,
+                             const void *beta,
+                             const float *A_log, const float *dt_bias, float lower_bound,
+                             const int32_t *cu_seqlens, int32_t num_seqs,
+                             int32_t B, int32_t T, int32_t H, int32_t K,
+                             void *workspace, void *stream)
+{
+    if (!q || !k || !g || !beta || !A_log || !workspace) return KDA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(g, 16) || !aligned(workspace, 16) ||
+        !aligned(beta, 2) || !aligned(A_log, 4) || !aligned(dt_bias, 4) ||
+        !aligned(cu_seqlens, 4))
+        return KDA_ERR_INVALID_ARG;
+    kda_status_t st = check_sizes(B, T, H, K, K, cu_seqlens, num_seqs);
+    if (st != KDA_OK) return st;
+    if ((st = check_gate(lower_bound)) != KDA_OK) return st;
+    hipError_t e = kda::launch_intra((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,
+                                     (const uint16_t *)beta, A_log, dt_bias, lower_bound,
+                                     cu_seqlens, num_seqs, T, H, num_slots(B, T, num_seqs),
+                                     (uint8_t *)workspace, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_set_stage_events(void *before_intra, void *before_scan, void *after_scan) {
+    t_stage_events[0] = (hipEvent_t)before_intra;
+    t_stage_events[1] = (hipEvent_t)before_scan;
+    t_stage_events[2] = (hipEvent_t)after_scan;
+    return KDA_OK;
+}
+
+}  // extern "C"

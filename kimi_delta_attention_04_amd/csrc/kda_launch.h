@@ -1,0 +1,21 @@
+// Host-side launchers of the libkda kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Intra-chunk stage over num_slots chunk slots x H heads; writes hand-off
+// records (REC_BYTES each, slot-major then head) into ws.
+hipError_t launch_intra(const uint16_t *q, const uint16_t *k, const uint16_t *g,
+                        const uint16_t *beta, const float *A_log, const float *dt_bias,
+                        float lower_bound, const int32_t *cu, int N, int T, int H,
+                        int64_t num_slots, uint8_t *ws, hipStream_t stream);
+
+// Inter-chunk scan over N sequences x H heads x 8 column slices.
+hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, int N, int T,
+                       int H, float scale, const void *init, int init_fp32, void *fin,
+                       int fin_fp32, uint16_t *out, hipStream_t stream);
+
+}  // namespace kda
