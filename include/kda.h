@@ -130,7 +130,7 @@ size_t kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs);
  * in-chunk cumulative decay, A_kk / A_qk products, triangular inverse) and
  * writes its hand-off records into the caller's `workspace` (device,
  * kda_workspace_size(...) bytes, 16-byte aligned).  Arguments as kda_fwd.
- * Record layout (per chunk slot and head, 13824 bytes) is described in the
+ * Record layout (per chunk slot and head, 13312 bytes) is described in the
  * library source; tests decode it to compare each stage with fp64 maths.
  */
 kda_status_t kda_debug_intra(const void *q, const void *k, const void *g,

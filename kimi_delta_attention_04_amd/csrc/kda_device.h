@@ -3,16 +3,21 @@
 // Chunkwise form computed by the kernels (per head, chunk of n <= 16 tokens,
 // incoming state S0, in-chunk inclusive cumulative log-decay G):
 //   Kt  = k * e^{G},  Qt = q * e^{G},  Kb = k * e^{-G}           (n x 128)
-//   Akk = strict_lower(diag(beta) Kt Kb^T),  Aqk = lower_incl(Qt Kb^T)
-//   T   = (I + Akk)^{-1}                                         (16 x 16)
-//   E   = T diag(beta) (V - Kt S0)
-//   O   = scale (Qt S0 + Aqk E)
-//   S   = diag(e^{G_last}) (S0 + Kb^T E)
-// This is the "specialized DPLR" chunkwise algorithm the FlashKDA write-up
-// credits for KDA's efficiency ("Moonshot AI Open-Sources FlashKDA", section
-// "Why KDA?"), with the 16-token chunk and small triangular inverse of its
-// section "What makes the kernel fast"; it equals the token recurrence
-// exactly in real arithmetic.
+//   T   = (I + diag(beta) strict_lower(Kt Kb^T))^{-1}            (16 x 16)
+//   Aqk = lower_incl(Qt Kb^T)
+//   M   = Aqk T diag(beta),   W = (T diag(beta))^T Kb            (intra stage)
+//   X   = V - Kt S0
+//   O   = scale (Qt S0 + M X)
+//   S   = diag(e^{G_last}) (S0 + W^T X)                          (scan)
+// With E = T diag(beta) X the usual WY/UT form reads O = Qt S0 + Aqk E and
+// S = diag(e^{G_last})(S0 + Kb^T E); folding T diag(beta) into M and W
+// moves two products off the serial path and lets the intra stage round
+// M and W to bf16 once, from fp32 values.  This is the "specialized DPLR"
+// chunkwise algorithm the FlashKDA write-up credits for KDA's efficiency
+// ("Moonshot AI Open-Sources FlashKDA", section "Why KDA?"), with the
+// 16-token chunk and small triangular inverse of its section "What makes
+// the kernel fast"; it equals the token recurrence exactly in real
+// arithmetic.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,20 +30,19 @@ constexpr int CS = 16;           // tokens per chunk
 constexpr float LOG2E = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
-// Hand-off record written by the intra-chunk kernel for one (chunk slot,
-// head) and read by the scan kernel.  Every piece is stored in exactly the
-// register layout the scan's MFMA operands need, so the scan issues only
-// coalesced 16-byte loads.
+// Hand-off record written by the intra-chunk stage for one (chunk slot,
+// head) and read by the scan.  Every piece is stored in exactly the register
+// layout the scan's MFMA operands need.
 //
 //   KT  [kb 0..3][lane 0..63][8 bf16]  Kt rows as the A operand of a
 //        16x16x32 MFMA: lane l holds token l%16, channels 32kb + 8(l/16) + i
 //   QT  same for Qt
-//   KB  [tp 0..3][lane 0..63][8 bf16]  Kb^T as the A operand of eight
+//   WT  [tp 0..3][lane 0..63][8 bf16]  W^T as the A operand of eight
 //        16x16x16 MFMAs (state row tiles t = 2tp, 2tp+1): lane l holds
 //        channel chan(t, l%16) and tokens 4(l/16) + j, j = 0..3; tile 2tp in
 //        bf16 0..3, tile 2tp+1 in bf16 4..7
-//   TA  [lane][8 bf16]  T diag(beta) in bf16 0..3 and the masked Aqk in bf16
-//        4..7, both as 16x16x16 A operands (lane l: row l%16, k = 4(l/16)+j)
+//   M   [lane][4 bf16]  M as a 16x16x16 A operand (lane l: row l%16,
+//        k = 4(l/16) + j)
 //   GAM [128 fp32]      e^{G_last} per channel
 //
 // The state tiles permute their rows so that the accumulator of tile pair
@@ -48,10 +52,10 @@ constexpr float LOG2E = 1.4426950408889634f;
 // ---------------------------------------------------------------------------
 constexpr int REC_KT = 0;
 constexpr int REC_QT = 4096;
-constexpr int REC_KB = 8192;
-constexpr int REC_TA = 12288;
-constexpr int REC_GAM = 13312;
-constexpr int REC_BYTES = 13824;
+constexpr int REC_WT = 8192;
+constexpr int REC_M = 12288;
+constexpr int REC_GAM = 12800;
+constexpr int REC_BYTES = 13312;
 
 __host__ __device__ constexpr int state_chan(int t, int rho) {
     return 32 * (t >> 1) + 8 * (rho >> 2) + 4 * (t & 1) + (rho & 3);
@@ -95,6 +99,13 @@ __device__ __forceinline__ f32x4_t mfma_k16(u32x2_t a, u32x2_t b, f32x4_t c) {
 // D = A(16x4) B(4x16) + C in fp32; lane l supplies A[l%16][l/16], B[l/16][l%16].
 __device__ __forceinline__ f32x4_t mfma_k4(float a, float b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Raw buffer resource over [p, p + bytes): loads beyond return 0 and stores
+// beyond are dropped (checked per dword), which lets partial chunks run
+// without branches around memory instructions.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
 // Sequence n's token range [start, end) in the packed token axis.

@@ -1,20 +1,24 @@
 // Intra-chunk stage: token-parallel over (chunk, head).
 //
-// One wave handles one (16-token chunk, head); a 256-thread workgroup holds
-// four consecutive heads of the same chunk so every token row it touches is
-// one contiguous 1 KB run of q / k / g.  Per chunk it
+// One wave handles one (16-token chunk, head); a 128-thread workgroup holds
+// two consecutive heads of the same chunk so each token row it touches is one
+// contiguous 512-byte run of q / k / g.  Per chunk it
 //   1. evaluates the gate in base 2 (the exponent rebasing idea of "Moonshot
 //      AI Open-Sources FlashKDA", section "What makes the kernel fast"):
 //        log2 alpha = max(-A * log2(1 + 2^{(g + dt_bias) log2 e}), lb log2 e)
 //      and beta = sigmoid(logit);
 //   2. takes the in-chunk inclusive cumulative sum G of log2 alpha;
-//   3. forms Kt = k 2^G, Qt = q 2^G, Kb = k 2^-G (bf16, via LDS);
-//   4. A_kk = Kt Kb^T, its transpose and Aqk^T on bf16 MFMA;
+//   3. forms Kt = k 2^G, Qt = q 2^G, Kb = k 2^-G; Qt and Kb also as a bf16
+//      (hi, lo) pair whose sum carries ~16 mantissa bits;
+//   4. A_kk = Kt Kb^T on bf16 MFMA, and Aqk^T = Kb Qt^T from three bf16 MFMA
+//      products (hi hi + hi lo + lo hi) so that it is fp32-accurate;
 //   5. T = (I + diag(beta) strict_lower(A_kk))^{-1} by the product form of
 //      the Neumann series of a nilpotent matrix,
 //        (I - N)^{-1} = (I + N)(I + N^2)(I + N^4)(I + N^8),  N^16 = 0,
 //      on fp32 16x16x4 MFMAs (the small-inverse step of the same section);
-//   6. writes the hand-off record the scan consumes.
+//   6. M = Aqk T diag(beta) and W = (T diag(beta))^T Kb, again from (hi, lo)
+//      bf16 products, rounded to bf16 once;
+//   7. writes the hand-off record the scan consumes.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -22,8 +26,20 @@ namespace kda {
 
 namespace {
 
-constexpr int WAVES = 4;
-constexpr int LROW = 136;   // bf16 per LDS row: 128 + 8 padding (conflict-free row-strided reads)
+constexpr int WAVES = 2;
+constexpr int LROW = 136;   // bf16 per row of a token-major tile: 128 + 8 padding
+constexpr int LCOL = 20;    // bf16 per row of a channel-major tile: 16 tokens + 4 padding
+
+struct WaveLds {
+    uint16_t kt[CS][LROW];          // Kt (bf16), token-major
+    uint16_t qh[CS][LROW];          // Qt hi
+    uint16_t ql[CS][LROW];          // Qt lo
+    uint16_t bh[CS][LROW];          // Kb hi
+    uint16_t bl[CS][LROW];          // Kb lo
+    uint16_t bhT[HD][LCOL];         // Kb hi, channel-major
+    uint16_t blT[HD][LCOL];         // Kb lo, channel-major
+    float beta[CS];
+};
 
 // Z = X Y for 16x16 fp32 matrices held in MFMA accumulator layout: xt is the
 // accumulator layout of X^T (equal to the A-operand layout of X) and y that
@@ -42,16 +58,23 @@ __device__ __forceinline__ float elem(const u32x4_t &v, int i) {
     return (i & 1) ? bf16hi(w) : bf16lo(w);
 }
 
-__global__ __launch_bounds__(256) void intra_kernel(
+// bf16 (hi, lo) split of two fp32 values: hi = rne(x), lo = rne(x - hi).
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = pack2(a, b);
+    lo = pack2(a - bf16lo(hi), b - bf16hi(hi));
+}
+
+__device__ __forceinline__ uint32_t half16(uint32_t w, int i) {
+    return (i & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+__global__ __launch_bounds__(64 * WAVES) void intra_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
     const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb2,
     const int32_t *__restrict__ cu, int N, int T, int H, uint8_t *__restrict__ ws)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t sK[WAVES][CS][LROW];
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[WAVES][CS][LROW];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[WAVES][CS][LROW];
-    __shared__ float sBeta[WAVES][CS];
+    __shared__ __attribute__((aligned(16))) WaveLds lds[WAVES];
 
     const int w = threadIdx.x >> 6;
     const int l = threadIdx.x & 63;
@@ -61,6 +84,7 @@ __global__ __launch_bounds__(256) void intra_kernel(
     const int h = blockIdx.y * WAVES + w;
     const bool hv = h < H;         // wave-uniform
     const int hh = hv ? h : 0;
+    WaveLds &L = lds[w];
 
     // Which sequence owns this slot: largest n with slot0(n) <= slot.
     int lo = 0, hi = N - 1;
@@ -89,7 +113,7 @@ __global__ __launch_bounds__(256) void intra_kernel(
             float x = bf16f(beta[(size_t)(t0 + l) * H + hh]);
             b = __builtin_amdgcn_rcpf(1.f + fast_exp2(-x * LOG2E));
         }
-        sBeta[w][l] = b;
+        L.beta[l] = b;
     }
 
     // ---- load rows 4grp+p, channels 8cg..8cg+7 ----------------------------
@@ -107,7 +131,9 @@ __global__ __launch_bounds__(256) void intra_kernel(
         }
     }
 
-    // ---- gate and in-lane cumulative sum ---------------------------------
+    // ---- gate and cumulative sum ----------------------------------------
+    // A == 0 (A_log = -inf) means no decay at all; testing it once keeps the
+    // per-element path free of 0 * inf.
     float G[4][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -115,8 +141,8 @@ __global__ __launch_bounds__(256) void intra_kernel(
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const float x2 = elem(rg[p], i) * LOG2E + dtb2[i];
-            const float u = x2 > 64.f ? x2 : fast_log2(1.f + fast_exp2(x2));
-            const float la = fmaxf(-A * u, lb2);
+            const float u = fast_log2(1.f + fast_exp2(x2));
+            const float la = A > 0.f ? fmaxf(-A * u, lb2) : 0.f;
             acc += (4 * grp + p < len) ? la : 0.f;
             G[p][i] = acc;
         }
@@ -136,58 +162,55 @@ __global__ __launch_bounds__(256) void intra_kernel(
     }
 
     // ---- decayed operands ------------------------------------------------
-    u32x4_t kt4[4], qt4[4], kb4[4];
+    u32x4_t bh4[4], bl4[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        float kt[8], qt[8], kb[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float eg = fast_exp2(G[p][i]);
-            const float egi = fast_exp2(-G[p][i]);
-            const float kv = elem(rk[p], i), qv = elem(rq[p], i);
-            kt[i] = kv * eg;
-            qt[i] = qv * eg;
-            kb[i] = kv * egi;
-        }
+        u32x4_t kt4, qh4, ql4;
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd) {
-            kt4[p][wd] = pack2(kt[2 * wd], kt[2 * wd + 1]);
-            qt4[p][wd] = pack2(qt[2 * wd], qt[2 * wd + 1]);
-            kb4[p][wd] = pack2(kb[2 * wd], kb[2 * wd + 1]);
+            float kt[2], qt[2], kb[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i = 2 * wd + e;
+                const float eg = fast_exp2(G[p][i]);
+                const float egi = fast_exp2(-G[p][i]);
+                const float kv = elem(rk[p], i), qv = elem(rq[p], i);
+                kt[e] = kv * eg;
+                qt[e] = qv * eg;
+                kb[e] = kv * egi;
+            }
+            kt4[wd] = pack2(kt[0], kt[1]);
+            uint32_t a, b;
+            split2(qt[0], qt[1], a, b); qh4[wd] = a; ql4[wd] = b;
+            split2(kb[0], kb[1], a, b); bh4[p][wd] = a; bl4[p][wd] = b;
         }
         const int r = 4 * grp + p;
-        *(u32x4_t *)&sK[w][r][8 * cg] = kt4[p];
-        *(u32x4_t *)&sQ[w][r][8 * cg] = qt4[p];
-        *(u32x4_t *)&sB[w][r][8 * cg] = kb4[p];
+        *(u32x4_t *)&L.kt[r][8 * cg] = kt4;
+        *(u32x4_t *)&L.qh[r][8 * cg] = qh4;
+        *(u32x4_t *)&L.ql[r][8 * cg] = ql4;
+        *(u32x4_t *)&L.bh[r][8 * cg] = bh4[p];
+        *(u32x4_t *)&L.bl[r][8 * cg] = bl4[p];
+    }
+    // channel-major Kb: channel 8cg+i, tokens 4grp..4grp+3 (8 bytes)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        u32x2_t vh, vl;
+        vh[0] = half16(bh4[0][i >> 1], i) | (half16(bh4[1][i >> 1], i) << 16);
+        vh[1] = half16(bh4[2][i >> 1], i) | (half16(bh4[3][i >> 1], i) << 16);
+        vl[0] = half16(bl4[0][i >> 1], i) | (half16(bl4[1][i >> 1], i) << 16);
+        vl[1] = half16(bl4[2][i >> 1], i) | (half16(bl4[3][i >> 1], i) << 16);
+        *(u32x2_t *)&L.bhT[8 * cg + i][4 * grp] = vh;
+        *(u32x2_t *)&L.blT[8 * cg + i][4 * grp] = vl;
     }
 
-    if (hv) {
+    if (hv && grp == 3) {
         // decay over the whole chunk (rows past len contribute nothing)
-        if (grp == 3) {
-            f32x4_t g0, g1;
+        f32x4_t g0, g1;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { g0[i] = fast_exp2(G[3][i]); g1[i] = fast_exp2(G[3][4 + i]); }
-            float *gp = (float *)(rec + REC_GAM) + 8 * cg;
-            *(f32x4_t *)gp = g0;
-            *(f32x4_t *)(gp + 4) = g1;
-        }
-        // Kb^T tiles straight from registers: channel 8cg+i lands in state
-        // tile t = 2(cg/4) + i/4, row rho = 4(cg%4) + i%4, consumer lane
-        // 16grp + rho; channels i and i+4 share one 16-byte slot.
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            auto half = [&](int i, int p) -> uint32_t {
-                uint32_t wd = kb4[p][i >> 1];
-                return (i & 1) ? (wd >> 16) : (wd & 0xffffu);
-            };
-            u32x4_t o;
-            o[0] = half(jj, 0) | (half(jj, 1) << 16);
-            o[1] = half(jj, 2) | (half(jj, 3) << 16);
-            o[2] = half(jj + 4, 0) | (half(jj + 4, 1) << 16);
-            o[3] = half(jj + 4, 2) | (half(jj + 4, 3) << 16);
-            const int m = 16 * grp + 4 * (cg & 3) + jj;
-            *(u32x4_t *)(rec + REC_KB + ((cg >> 2) * 64 + m) * 16) = o;
-        }
+        for (int i = 0; i < 4; ++i) { g0[i] = fast_exp2(G[3][i]); g1[i] = fast_exp2(G[3][4 + i]); }
+        float *gp = (float *)(rec + REC_GAM) + 8 * cg;
+        *(f32x4_t *)gp = g0;
+        *(f32x4_t *)(gp + 4) = g1;
     }
 
     __syncthreads();
@@ -197,23 +220,28 @@ __global__ __launch_bounds__(256) void intra_kernel(
     f32x4_t Akk = {0.f, 0.f, 0.f, 0.f}, AkkT = Akk, AqkT = Akk;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        const u32x4_t aK = *(const u32x4_t *)&sK[w][cg][32 * kb + 8 * grp];
-        const u32x4_t aQ = *(const u32x4_t *)&sQ[w][cg][32 * kb + 8 * grp];
-        const u32x4_t aB = *(const u32x4_t *)&sB[w][cg][32 * kb + 8 * grp];
+        const int c0 = 32 * kb + 8 * grp;
+        const u32x4_t aK = *(const u32x4_t *)&L.kt[cg][c0];
+        const u32x4_t aQh = *(const u32x4_t *)&L.qh[cg][c0];
+        const u32x4_t aQl = *(const u32x4_t *)&L.ql[cg][c0];
+        const u32x4_t aBh = *(const u32x4_t *)&L.bh[cg][c0];
+        const u32x4_t aBl = *(const u32x4_t *)&L.bl[cg][c0];
         if (hv) {
             *(u32x4_t *)(rec + REC_KT + (kb * 64 + l) * 16) = aK;
-            *(u32x4_t *)(rec + REC_QT + (kb * 64 + l) * 16) = aQ;
+            *(u32x4_t *)(rec + REC_QT + (kb * 64 + l) * 16) = aQh;
         }
-        Akk = mfma_k32(aK, aB, Akk);     // Akk[4grp+j][cg]    = Kt_r . Kb_i
-        AkkT = mfma_k32(aB, aK, AkkT);   // AkkT[4grp+j][cg]   = Akk[cg][4grp+j]
-        AqkT = mfma_k32(aB, aQ, AqkT);   // AqkT[4grp+j][cg]   = Aqk[cg][4grp+j]
+        Akk = mfma_k32(aK, aBh, Akk);       // Akk[4grp+j][cg]  = Kt_r . Kb_i
+        AkkT = mfma_k32(aBh, aK, AkkT);     // AkkT[4grp+j][cg] = Akk[cg][4grp+j]
+        AqkT = mfma_k32(aBh, aQh, AqkT);    // AqkT[4grp+j][cg] = Aqk[cg][4grp+j]
+        AqkT = mfma_k32(aBh, aQl, AqkT);
+        AqkT = mfma_k32(aBl, aQh, AqkT);
     }
 
     // ---- T = (I + L)^{-1}, L = diag(beta) strict_lower(Akk) ---------------
     float br[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) br[j] = sBeta[w][4 * grp + j];
-    const float bc = sBeta[w][cg];
+    for (int j = 0; j < 4; ++j) br[j] = L.beta[4 * grp + j];
+    const float bc = L.beta[cg];
     f32x4_t N1, N1t, I;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -222,29 +250,67 @@ __global__ __launch_bounds__(256) void intra_kernel(
         N1t[j] = (r < cg) ? -bc * AkkT[j] : 0.f;
         I[j] = (r == cg) ? 1.f : 0.f;
     }
-    const f32x4_t P1 = I + N1, P1t = I + N1t;
+    const f32x4_t P1t = I + N1t;
     const f32x4_t N2 = mm16(N1t, N1), N2t = mm16(N1, N1t);
     const f32x4_t P2 = I + N2;
-    const f32x4_t Q12 = mm16(P1t, P2), Q12t = mm16(P2, P1t);
-    (void)Q12;
+    const f32x4_t Q12t = mm16(P2, P1t);                 // ((I+N)(I+N^2))^T
     const f32x4_t N4 = mm16(N2t, N2), N4t = mm16(N2, N2t);
     const f32x4_t P4 = I + N4;
     const f32x4_t Q3t = mm16(P4, Q12t);                 // ((I+N)(I+N^2)(I+N^4))^T
     const f32x4_t N8 = mm16(N4t, N4);
     const f32x4_t P8 = I + N8;
-    const f32x4_t Tt = mm16(P8, Q3t);                   // T^T in accumulator layout
+    const f32x4_t Tm = mm16(Q3t, P8);                   // T in accumulator layout
 
-    if (hv) {
-        // A-operand layouts: lane l holds row cg, k = 4grp + j.
-        u32x4_t ta;
-        ta[0] = pack2(Tt[0] * br[0], Tt[1] * br[1]);     // T diag(beta)
-        ta[1] = pack2(Tt[2] * br[2], Tt[3] * br[3]);
-        float aq[4];
+    if (!hv) return;                                    // wave-uniform; no barrier follows
+
+    // T diag(beta) in accumulator layout (row 4grp+j, column cg), as (hi, lo):
+    // this is also the A-operand layout of (T diag(beta))^T.
+    u32x2_t tbh, tbl;
+    {
+        uint32_t h0, l0, h1, l1;
+        split2(Tm[0] * bc, Tm[1] * bc, h0, l0);
+        split2(Tm[2] * bc, Tm[3] * bc, h1, l1);
+        tbh[0] = h0; tbh[1] = h1; tbl[0] = l0; tbl[1] = l1;
+    }
+    // masked Aqk^T (i <= r) as (hi, lo) B operand
+    float aq[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) aq[j] = (4 * grp + j <= cg) ? AqkT[j] : 0.f;
-        ta[2] = pack2(aq[0], aq[1]);
-        ta[3] = pack2(aq[2], aq[3]);
-        *(u32x4_t *)(rec + REC_TA + l * 16) = ta;
+    for (int j = 0; j < 4; ++j) aq[j] = (4 * grp + j <= cg) ? AqkT[j] : 0.f;
+    u32x2_t aqh, aql;
+    {
+        uint32_t h0, l0, h1, l1;
+        split2(aq[0], aq[1], h0, l0);
+        split2(aq[2], aq[3], h1, l1);
+        aqh[0] = h0; aqh[1] = h1; aql[0] = l0; aql[1] = l1;
+    }
+
+    // M^T = (T diag(beta))^T Aqk^T: its accumulator layout is M's A layout.
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t Mt = mfma_k16(tbh, aqh, zero);
+    Mt = mfma_k16(tbh, aql, Mt);
+    Mt = mfma_k16(tbl, aqh, Mt);
+    u32x2_t mo;
+    mo[0] = pack2(Mt[0], Mt[1]);
+    mo[1] = pack2(Mt[2], Mt[3]);
+    *(u32x2_t *)(rec + REC_M + l * 8) = mo;
+
+    // W tiles: W[:, chan(t, .)] = (T diag(beta))^T Kb[:, chan(t, .)]; the
+    // accumulator layout is the A layout of W^T tile t the scan needs.
+#pragma unroll
+    for (int tp = 0; tp < 4; ++tp) {
+        u32x4_t o;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int ch = state_chan(2 * tp + half, cg);
+            const u32x2_t bh = *(const u32x2_t *)&L.bhT[ch][4 * grp];
+            const u32x2_t bl = *(const u32x2_t *)&L.blT[ch][4 * grp];
+            f32x4_t Wt = mfma_k16(tbh, bh, zero);
+            Wt = mfma_k16(tbh, bl, Wt);
+            Wt = mfma_k16(tbl, bh, Wt);
+            o[2 * half] = pack2(Wt[0], Wt[1]);
+            o[2 * half + 1] = pack2(Wt[2], Wt[3]);
+        }
+        *(u32x4_t *)(rec + REC_WT + (tp * 64 + l) * 16) = o;
     }
 }
 

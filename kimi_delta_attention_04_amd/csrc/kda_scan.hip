@@ -1,20 +1,24 @@
 // Inter-chunk scan: the sequential part of the chunkwise algorithm.
 //
-// One wave owns one (sequence, head, 16-column slice of V).  Columns of the
-// state evolve independently (each column sees the same transition and its
-// own v entries), so the eight slices of a head need no communication.  The
-// 128 x 16 fp32 state slice stays in MFMA accumulators for the whole
-// sequence (8 tiles of 16 x 16); the row permutation of the tiles (see
-// kda_device.h) makes the accumulators of tile pair (2kb, 2kb+1), rounded to
-// bf16, exactly the B operand of the next chunk's 16x16x32 MFMAs, so the
-// state never goes through LDS.  Per chunk:
-//   P  = Kt S            X = V - P            E = T diag(beta) X
-//   O  = scale (Qt S + Aqk E)  -> bf16 out
-//   S  = diag(gamma) (S + Kb^T E)
-// The long serial chain is what the FlashKDA write-up calls the low-
-// parallelism second stage ("Moonshot AI Open-Sources FlashKDA", section
-// "What makes the kernel fast"); here it is spread over (sequence, head,
-// slice) waves instead of one block per head.
+// A workgroup of four waves owns one (sequence, head, column part); each wave
+// keeps CT 16-column slices of the 128-row fp32 state in MFMA accumulators
+// for the whole sequence.  Columns of the state evolve independently (each
+// sees the same transition and its own v entries), so column parts need no
+// communication.  The row permutation of the state tiles (kda_device.h)
+// makes the accumulators of tile pair (2kb, 2kb+1), rounded to bf16, exactly
+// the B operand of the next chunk's 16x16x32 MFMAs: the state never leaves
+// the registers.  Per chunk:
+//   P = Kt S,  X = V - P,  O = scale (Qt S + M X) -> bf16,  S = diag(gamma) (S + W^T X)
+//
+// The hand-off record of each chunk (13 KB) and the chunk's v tile are read
+// from memory once per workgroup, by buffer-to-LDS DMA into a ring of
+// DEPTH slots, DEPTH-1 chunks ahead of the compute; all four waves read their
+// MFMA operands from the ring.  Every memory access goes through a
+// range-checked buffer resource, so partial chunks need no branches and the
+// number of memory instructions per chunk is fixed, which is what the
+// explicit vmcnt accounting relies on.  The serial chain is what the FlashKDA write-up
+// calls the low-parallelism second stage ("Moonshot AI Open-Sources
+// FlashKDA", section "What makes the kernel fast").
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -22,130 +26,258 @@ namespace kda {
 
 namespace {
 
-struct ChunkOps {
-    u32x4_t kt[4], qt[4], kb[4], ta;
-    f32x4_t gam[8];
-};
+constexpr int SCAN_WAVES = 4;
+constexpr int SCAN_THREADS = 64 * SCAN_WAVES;
+constexpr int DEPTH = 5;                         // LDS ring slots: DEPTH - 1 chunks in flight
+constexpr int REC_KB = REC_BYTES / 1024;         // 13 one-kilobyte units per record
 
-__device__ __forceinline__ void load_ops(ChunkOps &o, const uint8_t *rec, int l, int grp) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        o.kt[kb] = *(const u32x4_t *)(rec + REC_KT + (kb * 64 + l) * 16);
-        o.qt[kb] = *(const u32x4_t *)(rec + REC_QT + (kb * 64 + l) * 16);
-        o.kb[kb] = *(const u32x4_t *)(rec + REC_KB + (kb * 64 + l) * 16);
-    }
-    o.ta = *(const u32x4_t *)(rec + REC_TA + l * 16);
-    const float *gp = (const float *)(rec + REC_GAM);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        o.gam[2 * kb] = *(const f32x4_t *)(gp + 32 * kb + 8 * grp);
-        o.gam[2 * kb + 1] = *(const f32x4_t *)(gp + 32 * kb + 8 * grp + 4);
-    }
+static_assert(REC_BYTES % 1024 == 0, "record must be a whole number of 1 KB units");
+
+// s_waitcnt vmcnt(n) followed by a workgroup barrier; waits for this wave's
+// LDS traffic too but, unlike __syncthreads(), not for every outstanding
+// global access.
+template <int NV>
+__device__ __forceinline__ void wait_vm_barrier() {
+    static_assert(NV >= 0 && NV <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(NV) : "memory");
 }
 
-__device__ __forceinline__ u32x2_t lo2(u32x4_t v) { u32x2_t r = {v[0], v[1]}; return r; }
-__device__ __forceinline__ u32x2_t hi2(u32x4_t v) { u32x2_t r = {v[2], v[3]}; return r; }
+template <int CW>
+struct alignas(16) ScanSlot {
+    uint8_t rec[REC_BYTES];
+    uint16_t v[CS][CW];
+};
 
-__global__ __launch_bounds__(64) void scan_kernel(
+template <int CT>
+__global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
     const uint16_t *__restrict__ v, const uint8_t *__restrict__ ws,
     const int32_t *__restrict__ cu, int N, int T, int H, float scale,
     const void *__restrict__ init, int init_fp32,
     void *__restrict__ fin, int fin_fp32, uint16_t *__restrict__ out)
 {
-    // Block b -> unit u (sequence, head) and slice s such that the eight
-    // slices of a unit share b mod 8, i.e. the same XCD and L2.
+    constexpr int CW = SCAN_WAVES * 16 * CT;         // columns per workgroup
+    constexpr int NSPLIT = HD / CW;
+    constexpr int V_KB = CS * CW * 2 / 1024;         // one-kilobyte units of a v tile
+    constexpr int UNITS = REC_KB + V_KB;             // DMA units per chunk
+    constexpr int LW = (UNITS + SCAN_WAVES - 1) / SCAN_WAVES;   // DMAs per wave per chunk
+    constexpr int SW = 4 * CT;                       // out stores per lane per chunk
+    constexpr int VROW_LANES = CW * 2 / 16;          // lanes per v row in a DMA unit
+    __shared__ ScanSlot<CW> ring[DEPTH];
+    __shared__ __attribute__((aligned(16))) uint8_t sink[1024];   // target of padding DMAs
+
+    // Block b -> (unit u, part): the parts of a unit share b mod 8 (same XCD, same L2).
     const int b = blockIdx.x;
-    const int u = 8 * (b >> 6) + (b & 7);
-    const int s = (b >> 3) & 7;
-    if (u >= N * H) return;
+    const int u = 8 * (b / (8 * NSPLIT)) + (b & 7);
+    const int part = (b >> 3) % NSPLIT;
+    if (u >= N * H) return;                           // block-uniform
     const int n = u / H, h = u % H;
-    const int l = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int l = tid & 63;
     const int grp = l >> 4, cg = l & 15;
-    const int col = 16 * s + cg;
+    const int wcol0 = w * 16 * CT;                    // first column of this wave within the part
+    const int col0 = part * CW;                       // first column of the part within the head
 
     int64_t start, end;
     seq_range(cu, n, T, start, end);
     const int64_t L = end - start;
     const int nch = (int)((L + CS - 1) / CS);
     const int64_t slot0 = seq_slot0(cu, n, T);
-    const size_t state_base = ((size_t)n * H + h) * HD * HD;
+    const size_t row_bytes = (size_t)H * HD * 2;      // one token row of v / out
 
-    // ---- state slice: S[t][j] = state[chan(t, 4grp+j)][col] ----------------
-    f32x4_t S[8];
+    // ---- state slices: S[ct][t][j] = state[chan(t, 4grp+j)][col] -------------
+    // (a zero-sized resource when there is no initial state: loads return 0)
+    f32x4_t S[CT][8];
+    {
+        const size_t slab = (size_t)HD * HD * (init_fp32 ? 4 : 2);
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc((const uint8_t *)init + (init ? ((size_t)n * H + h) * slab : 0),
+                      init ? (uint32_t)slab : 0u);
+        if (init_fp32) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const size_t idx = state_base + (size_t)state_chan(t, 4 * grp + j) * HD + col;
-            float x = 0.f;
-            if (init) x = init_fp32 ? ((const float *)init)[idx] : bf16f(((const uint16_t *)init)[idx]);
-            S[t][j] = x;
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int idx = state_chan(t, 4 * grp + j) * HD + col0 + wcol0 + 16 * ct + cg;
+                        S[ct][t][j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, idx * 4, 0, 0));
+                    }
+        } else {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int idx = state_chan(t, 4 * grp + j) * HD + col0 + wcol0 + 16 * ct + cg;
+                        S[ct][t][j] = bf16f(__builtin_amdgcn_raw_buffer_load_b16(rs, idx * 2, 0, 0));
+                    }
         }
+    }
+    // state loads complete before the DMA accounting starts
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    ChunkOps cur, nxt;
-    if (nch > 0) load_ops(cur, ws + ((size_t)slot0 * H + h) * REC_BYTES, l, grp);
+    // Chunk c -> ring slot c % DEPTH by DMA: unit k < REC_KB is kilobyte k of
+    // the record; the next V_KB units are the v tile of this part, one row of
+    // CW columns per VROW_LANES lanes (rows past the sequence end and chunks
+    // past the last one read as zeros).  Every wave issues exactly LW DMAs;
+    // units past UNITS go to the sink.
+    auto issue = [&](int c) {
+        const bool live = c < nch;
+        const __amdgpu_buffer_rsrc_t rr =
+            make_rsrc(ws + ((size_t)(slot0 + (live ? c : 0)) * H + h) * REC_BYTES,
+                      live ? (uint32_t)REC_BYTES : 0u);
+        const int64_t tb = start + (int64_t)c * CS;
+        const int len = live ? (int)min((int64_t)CS, end - tb) : 0;
+        const __amdgpu_buffer_rsrc_t rv =
+            make_rsrc(v + ((size_t)(live ? tb : start) * H + h) * HD + col0,
+                      (uint32_t)(len * row_bytes));
+        ScanSlot<CW> &sl = ring[c % DEPTH];
+#pragma unroll
+        for (int i = 0; i < LW; ++i) {
+            const int unit = w + i * SCAN_WAVES;
+            if (unit < REC_KB) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void *)&sl.rec[unit * 1024],
+                                                         16, unit * 1024 + l * 16, 0, 0, 0);
+            } else if (unit < UNITS) {
+                const int vu = unit - REC_KB;                       // 1 KB = 1024 / (2 CW) rows
+                const int row = vu * (1024 / (2 * CW)) + l / VROW_LANES;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void *)&sl.v[vu * (1024 / (2 * CW))][0],
+                                                         16, (int)(row * row_bytes) + (l % VROW_LANES) * 16, 0, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void *)sink,
+                                                         16, 0x7ffffff0, 0, 0, 0);
+            }
+        }
+    };
 
-    for (int c = 0; c < nch; ++c) {
-        if (c + 1 < nch) load_ops(nxt, ws + ((size_t)(slot0 + c + 1) * H + h) * REC_BYTES, l, grp);
-
+    auto compute = [&](int c) {
+        const ScanSlot<CW> &sl = ring[c % DEPTH];
+        const uint8_t *R = sl.rec;
+        u32x4_t kt[4], qt[4], wt[4];
+        f32x4_t gam[8];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            kt[kb] = *(const u32x4_t *)(R + REC_KT + (kb * 64 + l) * 16);
+            qt[kb] = *(const u32x4_t *)(R + REC_QT + (kb * 64 + l) * 16);
+            wt[kb] = *(const u32x4_t *)(R + REC_WT + (kb * 64 + l) * 16);
+            gam[2 * kb] = *(const f32x4_t *)(R + REC_GAM + (32 * kb + 8 * grp) * 4);
+            gam[2 * kb + 1] = *(const f32x4_t *)(R + REC_GAM + (32 * kb + 8 * grp + 4) * 4);
+        }
+        const u32x2_t m = *(const u32x2_t *)(R + REC_M + l * 8);
         const int64_t tb = start + (int64_t)c * CS;
         const int len = (int)min((int64_t)CS, end - tb);
-        float vv[4];
+        // rows past the sequence end fall outside the resource and are dropped
+        const __amdgpu_buffer_rsrc_t ro =
+            make_rsrc(out + ((size_t)tb * H + h) * HD + col0,
+                      (uint32_t)((len - 1) * row_bytes + CW * 2));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 4 * grp + j;
-            vv[j] = r < len ? bf16f(v[((size_t)(tb + r) * H + h) * HD + col]) : 0.f;
+        for (int ct = 0; ct < CT; ++ct) {
+            const int lc = wcol0 + 16 * ct + cg;         // column within the part
+            // bf16 copy of the state as B operand: k-slots 8grp..8grp+7 of pair kb
+            u32x4_t Sb[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                Sb[kb][0] = pack2(S[ct][2 * kb][0], S[ct][2 * kb][1]);
+                Sb[kb][1] = pack2(S[ct][2 * kb][2], S[ct][2 * kb][3]);
+                Sb[kb][2] = pack2(S[ct][2 * kb + 1][0], S[ct][2 * kb + 1][1]);
+                Sb[kb][3] = pack2(S[ct][2 * kb + 1][2], S[ct][2 * kb + 1][3]);
+            }
+            f32x4_t P = {0.f, 0.f, 0.f, 0.f}, Qs = P;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                P = mfma_k32(kt[kb], Sb[kb], P);
+                Qs = mfma_k32(qt[kb], Sb[kb], Qs);
+            }
+            float x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = bf16f(sl.v[4 * grp + j][lc]) - P[j];
+            u32x2_t Xb;
+            Xb[0] = pack2(x[0], x[1]);
+            Xb[1] = pack2(x[2], x[3]);
+            const f32x4_t O = mfma_k16(m, Xb, Qs);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                __builtin_amdgcn_raw_buffer_store_b16(tobf16(scale * O[j]), ro,
+                                                      (int)((4 * grp + j) * row_bytes) + lc * 2, 0, 0);
+#pragma unroll
+            for (int tp = 0; tp < 4; ++tp) {
+                u32x2_t lo = {wt[tp][0], wt[tp][1]}, hi = {wt[tp][2], wt[tp][3]};
+                S[ct][2 * tp] = mfma_k16(lo, Xb, S[ct][2 * tp]);
+                S[ct][2 * tp + 1] = mfma_k16(hi, Xb, S[ct][2 * tp + 1]);
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) S[ct][t] = S[ct][t] * gam[t];
         }
+    };
 
-        // bf16 copy of the state as B operand: k-slots 8grp..8grp+7 of pair kb
-        u32x4_t Sb[4];
+    // Prologue: chunks 0 .. DEPTH-2 in flight.
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            Sb[kb][0] = pack2(S[2 * kb][0], S[2 * kb][1]);
-            Sb[kb][1] = pack2(S[2 * kb][2], S[2 * kb][3]);
-            Sb[kb][2] = pack2(S[2 * kb + 1][0], S[2 * kb + 1][1]);
-            Sb[kb][3] = pack2(S[2 * kb + 1][2], S[2 * kb + 1][3]);
+    for (int c = 0; c < DEPTH - 1; ++c) issue(c);
+
+    // Iteration c: wait for chunk c, barrier, compute (SW stores), then
+    // refill the slot chunk c-1 used with chunk c+DEPTH-1 (LW DMAs; every
+    // wave finished chunk c-1 before the barrier).  Issue order is
+    //   P_0 .. P_{DEPTH-2} | S_0 I_{DEPTH-1} | S_1 I_{DEPTH} | ...
+    // (P: prologue DMAs, S_c: stores of iteration c, I_j: DMAs of chunk j), so
+    // at iteration c the operations issued after chunk c's DMAs number
+    //   (DEPTH-2) LW + min(c, DEPTH-2) SW,
+    // and waiting until at most that many are outstanding means chunk c has
+    // landed in LDS.
+    static_assert((DEPTH - 2) * (LW + SW) <= 63, "vmcnt holds at most 63");
+    for (int c = 0; c < nch; ++c) {
+        switch (c < DEPTH - 2 ? c : DEPTH - 2) {
+            case 0: wait_vm_barrier<(DEPTH - 2) * LW + 0 * SW>(); break;
+            case 1: wait_vm_barrier<(DEPTH - 2) * LW + 1 * SW>(); break;
+            case 2: wait_vm_barrier<(DEPTH - 2) * LW + 2 * SW>(); break;
+            default: wait_vm_barrier<(DEPTH - 2) * LW + (DEPTH - 2) * SW>(); break;
         }
-        f32x4_t P = {0.f, 0.f, 0.f, 0.f}, Qs = P;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            P = mfma_k32(cur.kt[kb], Sb[kb], P);
-            Qs = mfma_k32(cur.qt[kb], Sb[kb], Qs);
-        }
-        u32x2_t Xb;
-        Xb[0] = pack2(vv[0] - P[0], vv[1] - P[1]);
-        Xb[1] = pack2(vv[2] - P[2], vv[3] - P[3]);
-        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4_t E = mfma_k16(lo2(cur.ta), Xb, zero);
-        u32x2_t Eb;
-        Eb[0] = pack2(E[0], E[1]);
-        Eb[1] = pack2(E[2], E[3]);
-        const f32x4_t O = mfma_k16(hi2(cur.ta), Eb, Qs);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 4 * grp + j;
-            if (r < len) out[((size_t)(tb + r) * H + h) * HD + col] = tobf16(scale * O[j]);
-        }
-#pragma unroll
-        for (int tp = 0; tp < 4; ++tp) {
-            S[2 * tp] = mfma_k16(lo2(cur.kb[tp]), Eb, S[2 * tp]);
-            S[2 * tp + 1] = mfma_k16(hi2(cur.kb[tp]), Eb, S[2 * tp + 1]);
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) S[t] = S[t] * cur.gam[t];
-        if (c + 1 < nch) cur = nxt;
+        compute(c);
+        issue(c + DEPTH - 1);
     }
+    // drain the DMAs of the chunks past the end before the workgroup exits
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     if (fin) {
+        const size_t slab = (size_t)HD * HD * (fin_fp32 ? 4 : 2);
+        const __amdgpu_buffer_rsrc_t rf =
+            make_rsrc((uint8_t *)fin + ((size_t)n * H + h) * slab, (uint32_t)slab);
+        if (fin_fp32) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const size_t idx = state_base + (size_t)state_chan(t, 4 * grp + j) * HD + col;
-                if (fin_fp32) ((float *)fin)[idx] = S[t][j];
-                else ((uint16_t *)fin)[idx] = tobf16(S[t][j]);
-            }
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int idx = state_chan(t, 4 * grp + j) * HD + col0 + wcol0 + 16 * ct + cg;
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[ct][t][j]), rf, idx * 4, 0, 0);
+                    }
+        } else {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int idx = state_chan(t, 4 * grp + j) * HD + col0 + wcol0 + 16 * ct + cg;
+                        __builtin_amdgcn_raw_buffer_store_b16(tobf16(S[ct][t][j]), rf, idx * 2, 0, 0);
+                    }
+        }
     }
+}
+
+int num_cus() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 }  // namespace
@@ -155,10 +287,18 @@ hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, 
                        int fin_fp32, uint16_t *out, hipStream_t stream)
 {
     const int64_t units = (int64_t)N * H;
-    const int64_t blocks = 64 * ((units + 7) / 8);
-    if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)blocks), dim3(64), 0, stream,
-                       v, ws, cu, N, T, H, scale, init, init_fp32, fin, fin_fp32, out);
+    if (units <= 0) return hipSuccess;
+    // Few (sequence, head) units: split each head's columns over two
+    // workgroups so that more compute units share the scan.
+    const bool split = 2 * units <= num_cus();
+    const int nsplit = split ? 2 : 1;
+    const int64_t blocks = 8 * nsplit * ((units + 7) / 8);
+    if (split)
+        hipLaunchKernelGGL(scan_kernel<1>, dim3((unsigned)blocks), dim3(SCAN_THREADS), 0, stream,
+                           v, ws, cu, N, T, H, scale, init, init_fp32, fin, fin_fp32, out);
+    else
+        hipLaunchKernelGGL(scan_kernel<2>, dim3((unsigned)blocks), dim3(SCAN_THREADS), 0, stream,
+                           v, ws, cu, N, T, H, scale, init, init_fp32, fin, fin_fp32, out);
     return hipGetLastError();
 }
 

@@ -60,9 +60,9 @@ def test_constants(lib):
 
 
 def test_workspace_size(lib):
-    assert kda.workspace_size(1, 8192, 96, 1) == (8192 // 16 + 1) * 96 * 13824
-    assert kda.workspace_size(1, 8192, 96, 12) == (8192 // 16 + 12) * 96 * 13824
-    assert kda.workspace_size(3, 37, 2, 3) == (111 // 16 + 3) * 2 * 13824
+    assert kda.workspace_size(1, 8192, 96, 1) == (8192 // 16 + 1) * 96 * 13312
+    assert kda.workspace_size(1, 8192, 96, 12) == (8192 // 16 + 12) * 96 * 13312
+    assert kda.workspace_size(3, 37, 2, 3) == (111 // 16 + 3) * 2 * 13312
     assert kda.workspace_size(0, 16, 1, 1) == 0
     assert kda.workspace_size(1, 16, 1, 0) == 0
 
