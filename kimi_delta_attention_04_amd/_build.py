@@ -13,6 +13,9 @@ SOURCES = ["kda_api.hip", "kda_intra.hip", "kda_scan.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: no packed fp32 VALU instructions in the device code.
+# (The VGPR form of MFMA, -mllvm -amdgpu-mfma-vgpr-form, would save the AGPR
+# copies around the state decay but produced wrong outputs from the scan
+# with this compiler, so the default AGPR form is kept.)
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]

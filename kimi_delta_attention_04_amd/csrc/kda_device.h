@@ -5,14 +5,15 @@
 //   Kt  = k * e^{G},  Qt = q * e^{G},  Kb = k * e^{-G}           (n x 128)
 //   T   = (I + diag(beta) strict_lower(Kt Kb^T))^{-1}            (16 x 16)
 //   Aqk = lower_incl(Qt Kb^T)
-//   M   = Aqk T diag(beta),   W = (T diag(beta))^T Kb            (intra stage)
+//   M   = Aqk T diag(beta),   W = (T diag(beta))^T Kb diag(e^{G_last})
+//                                                                (intra stage)
 //   X   = V - Kt S0
 //   O   = scale (Qt S0 + M X)
-//   S   = diag(e^{G_last}) (S0 + W^T X)                          (scan)
+//   S   = diag(e^{G_last}) S0 + W^T X                             (scan)
 // With E = T diag(beta) X the usual WY/UT form reads O = Qt S0 + Aqk E and
-// S = diag(e^{G_last})(S0 + Kb^T E); folding T diag(beta) into M and W
-// moves two products off the serial path and lets the intra stage round
-// M and W to bf16 once, from fp32 values.  This is the "specialized DPLR"
+// S = diag(e^{G_last})(S0 + Kb^T E); folding T diag(beta) (and the chunk
+// decay) into M and W moves products off the serial path and lets the intra
+// stage round M and W to bf16 once, from fp32 values.  This is the "specialized DPLR"
 // chunkwise algorithm the FlashKDA write-up credits for KDA's efficiency
 // ("Moonshot AI Open-Sources FlashKDA", section "Why KDA?"), with the
 // 16-token chunk and small triangular inverse of its section "What makes
@@ -37,7 +38,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 //   KT  [kb 0..3][lane 0..63][8 bf16]  Kt rows as the A operand of a
 //        16x16x32 MFMA: lane l holds token l%16, channels 32kb + 8(l/16) + i
 //   QT  same for Qt
-//   WT  [tp 0..3][lane 0..63][8 bf16]  W^T as the A operand of eight
+//   WT  [tp 0..3][lane 0..63][8 bf16]  W^T (decay included) as the A operand of eight
 //        16x16x16 MFMAs (state row tiles t = 2tp, 2tp+1): lane l holds
 //        channel chan(t, l%16) and tokens 4(l/16) + j, j = 0..3; tile 2tp in
 //        bf16 0..3, tile 2tp+1 in bf16 4..7

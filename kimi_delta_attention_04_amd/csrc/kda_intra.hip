@@ -16,8 +16,8 @@
 //      the Neumann series of a nilpotent matrix,
 //        (I - N)^{-1} = (I + N)(I + N^2)(I + N^4)(I + N^8),  N^16 = 0,
 //      on fp32 16x16x4 MFMAs (the small-inverse step of the same section);
-//   6. M = Aqk T diag(beta) and W = (T diag(beta))^T Kb, again from (hi, lo)
-//      bf16 products, rounded to bf16 once;
+//   6. M = Aqk T diag(beta) and W = (T diag(beta))^T Kb diag(e^{G_last}),
+//      again from (hi, lo) bf16 products, rounded to bf16 once;
 //   7. writes the hand-off record the scan consumes.
 #include "kda_device.h"
 #include "kda_launch.h"
@@ -39,6 +39,7 @@ struct WaveLds {
     uint16_t bhT[HD][LCOL];         // Kb hi, channel-major
     uint16_t blT[HD][LCOL];         // Kb lo, channel-major
     float beta[CS];
+    float gam[HD];                  // e^{G_last} per channel
 };
 
 // Z = X Y for 16x16 fp32 matrices held in MFMA accumulator layout: xt is the
@@ -203,14 +204,18 @@ __global__ __launch_bounds__(64 * WAVES) void intra_kernel(
         *(u32x2_t *)&L.blT[8 * cg + i][4 * grp] = vl;
     }
 
-    if (hv && grp == 3) {
+    if (grp == 3) {
         // decay over the whole chunk (rows past len contribute nothing)
         f32x4_t g0, g1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) { g0[i] = fast_exp2(G[3][i]); g1[i] = fast_exp2(G[3][4 + i]); }
-        float *gp = (float *)(rec + REC_GAM) + 8 * cg;
-        *(f32x4_t *)gp = g0;
-        *(f32x4_t *)(gp + 4) = g1;
+        *(f32x4_t *)&L.gam[8 * cg] = g0;
+        *(f32x4_t *)&L.gam[8 * cg + 4] = g1;
+        if (hv) {
+            float *gp = (float *)(rec + REC_GAM) + 8 * cg;
+            *(f32x4_t *)gp = g0;
+            *(f32x4_t *)(gp + 4) = g1;
+        }
     }
 
     __syncthreads();
@@ -294,8 +299,9 @@ __global__ __launch_bounds__(64 * WAVES) void intra_kernel(
     mo[1] = pack2(Mt[2], Mt[3]);
     *(u32x2_t *)(rec + REC_M + l * 8) = mo;
 
-    // W tiles: W[:, chan(t, .)] = (T diag(beta))^T Kb[:, chan(t, .)]; the
-    // accumulator layout is the A layout of W^T tile t the scan needs.
+    // W tiles: W[:, chan(t, .)] = (T diag(beta))^T Kb[:, chan(t, .)] times the
+    // chunk decay of that channel; the accumulator layout is the A layout of
+    // W^T tile t the scan needs.
 #pragma unroll
     for (int tp = 0; tp < 4; ++tp) {
         u32x4_t o;
@@ -307,8 +313,9 @@ __global__ __launch_bounds__(64 * WAVES) void intra_kernel(
             f32x4_t Wt = mfma_k16(tbh, bh, zero);
             Wt = mfma_k16(tbh, bl, Wt);
             Wt = mfma_k16(tbl, bh, Wt);
-            o[2 * half] = pack2(Wt[0], Wt[1]);
-            o[2 * half + 1] = pack2(Wt[2], Wt[3]);
+            const float gch = L.gam[ch];
+            o[2 * half] = pack2(Wt[0] * gch, Wt[1] * gch);
+            o[2 * half + 1] = pack2(Wt[2] * gch, Wt[3] * gch);
         }
         *(u32x4_t *)(rec + REC_WT + (tp * 64 + l) * 16) = o;
     }

@@ -8,7 +8,9 @@
 // makes the accumulators of tile pair (2kb, 2kb+1), rounded to bf16, exactly
 // the B operand of the next chunk's 16x16x32 MFMAs: the state never leaves
 // the registers.  Per chunk:
-//   P = Kt S,  X = V - P,  O = scale (Qt S + M X) -> bf16,  S = diag(gamma) (S + W^T X)
+//   P = Kt S,  X = V - P,  O = scale (Qt S + M X) -> bf16,  S = W^T X + diag(gamma) S
+// (W carries the chunk decay, so diag(gamma) S is formed while the P
+// products run and enters the update MFMAs as their accumulator).
 //
 // The hand-off record of each chunk (13 KB) and the chunk's v tile are read
 // from memory once per workgroup, by buffer-to-LDS DMA into a ring of
@@ -40,6 +42,32 @@ template <int NV>
 __device__ __forceinline__ void wait_vm_barrier() {
     static_assert(NV >= 0 && NV <= 63, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(NV) : "memory");
+}
+
+// Raw buffer descriptor words (base, stride 0, num_records, the same
+// configuration word as make_rsrc) for the inline-assembly DMA below.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t rsrc_words(const void *p, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    i32x4_t r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);
+    r[2] = (int)bytes;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16-byte-per-lane buffer-to-LDS DMA: lane l's 16 bytes at byte offset `off`
+// of the resource land at LDS address lds + 16 l.  Issued from inline
+// assembly so that the compiler's own wait insertion, which cannot tell the
+// ring slots apart, does not serialise the prefetch; the waits are explicit
+// (wait_vm_barrier).  The loop that uses it issues no other loads.
+// m0 is set by the asm itself; nothing else in these kernels keeps a value
+// in m0 (checked in the generated code), so it is not listed as a clobber.
+__device__ __forceinline__ void dma16(i32x4_t rs, const void *lds, int off) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(m0), "v"(off), "s"(rs) : "memory");
 }
 
 template <int CW>
@@ -118,42 +146,55 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
     // state loads complete before the DMA accounting starts
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+    // Per-chunk addressing advances by fixed strides.
+    const size_t rec_stride = (size_t)H * REC_BYTES;
+    const size_t row_stride = (size_t)CS * H * HD;                 // elements per chunk of v / out
+    const uint8_t *rec_base = ws + ((size_t)slot0 * H + h) * REC_BYTES;
+    const uint16_t *v_base = v + ((size_t)start * H + h) * HD + col0;
+    uint16_t *out_base = out + ((size_t)start * H + h) * HD + col0;
+
     // Chunk c -> ring slot c % DEPTH by DMA: unit k < REC_KB is kilobyte k of
     // the record; the next V_KB units are the v tile of this part, one row of
     // CW columns per VROW_LANES lanes (rows past the sequence end and chunks
     // past the last one read as zeros).  Every wave issues exactly LW DMAs;
     // units past UNITS go to the sink.
-    auto issue = [&](int c) {
+    auto issue = [&](int c, int slot) {
         const bool live = c < nch;
-        const __amdgpu_buffer_rsrc_t rr =
-            make_rsrc(ws + ((size_t)(slot0 + (live ? c : 0)) * H + h) * REC_BYTES,
-                      live ? (uint32_t)REC_BYTES : 0u);
-        const int64_t tb = start + (int64_t)c * CS;
-        const int len = live ? (int)min((int64_t)CS, end - tb) : 0;
-        const __amdgpu_buffer_rsrc_t rv =
-            make_rsrc(v + ((size_t)(live ? tb : start) * H + h) * HD + col0,
-                      (uint32_t)(len * row_bytes));
-        ScanSlot<CW> &sl = ring[c % DEPTH];
+        const i32x4_t rr =
+            rsrc_words(rec_base + (live ? (size_t)c * rec_stride : 0), live ? (uint32_t)REC_BYTES : 0u);
+        const int64_t rem = L - (int64_t)c * CS;
+        const int len = live ? (int)(rem < CS ? rem : CS) : 0;
+        const i32x4_t rv =
+            rsrc_words(v_base + (live ? (size_t)c * row_stride : 0), (uint32_t)(len * row_bytes));
+        ScanSlot<CW> &sl = ring[slot];
+        // units w, w+4, w+8 are always record kilobytes: no selection needed
+        constexpr int FIXED = REC_KB / SCAN_WAVES;
 #pragma unroll
-        for (int i = 0; i < LW; ++i) {
+        for (int i = 0; i < FIXED; ++i) {
             const int unit = w + i * SCAN_WAVES;
-            if (unit < REC_KB) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void *)&sl.rec[unit * 1024],
-                                                         16, unit * 1024 + l * 16, 0, 0, 0);
-            } else if (unit < UNITS) {
-                const int vu = unit - REC_KB;                       // 1 KB = 1024 / (2 CW) rows
-                const int row = vu * (1024 / (2 * CW)) + l / VROW_LANES;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void *)&sl.v[vu * (1024 / (2 * CW))][0],
-                                                         16, (int)(row * row_bytes) + (l % VROW_LANES) * 16, 0, 0, 0);
-            } else {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void *)sink,
-                                                         16, 0x7ffffff0, 0, 0, 0);
-            }
+            dma16(rr, &sl.rec[unit * 1024], unit * 1024 + l * 16);
+        }
+        // the remaining units: record, v tile or sink, chosen with
+        // wave-uniform selects so that every wave issues one DMA per unit
+#pragma unroll
+        for (int i = FIXED; i < LW; ++i) {
+            const int unit = w + i * SCAN_WAVES;
+            const bool is_rec = unit < REC_KB;
+            const bool is_v = !is_rec && unit < UNITS;
+            const int vu = unit - REC_KB;                          // 1 KB = 1024 / (2 CW) rows
+            const int vrow0 = vu * (1024 / (2 * CW));
+            const i32x4_t rs = is_v ? rv : rr;
+            uint8_t *dst = is_rec ? &sl.rec[unit * 1024]
+                         : is_v ? (uint8_t *)&sl.v[vrow0][0] : sink;
+            const int off = is_rec ? unit * 1024 + l * 16
+                          : is_v ? (int)((vrow0 + l / VROW_LANES) * row_bytes) + (l % VROW_LANES) * 16
+                                 : 0x7ffffff0;
+            dma16(rs, dst, off);
         }
     };
 
-    auto compute = [&](int c) {
-        const ScanSlot<CW> &sl = ring[c % DEPTH];
+    auto compute = [&](int c, int slot) {
+        const ScanSlot<CW> &sl = ring[slot];
         const uint8_t *R = sl.rec;
         u32x4_t kt[4], qt[4], wt[4];
         f32x4_t gam[8];
@@ -166,12 +207,11 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
             gam[2 * kb + 1] = *(const f32x4_t *)(R + REC_GAM + (32 * kb + 8 * grp + 4) * 4);
         }
         const u32x2_t m = *(const u32x2_t *)(R + REC_M + l * 8);
-        const int64_t tb = start + (int64_t)c * CS;
-        const int len = (int)min((int64_t)CS, end - tb);
+        const int64_t rem = L - (int64_t)c * CS;
+        const int len = (int)(rem < CS ? rem : CS);
         // rows past the sequence end fall outside the resource and are dropped
         const __amdgpu_buffer_rsrc_t ro =
-            make_rsrc(out + ((size_t)tb * H + h) * HD + col0,
-                      (uint32_t)((len - 1) * row_bytes + CW * 2));
+            make_rsrc(out_base + (size_t)c * row_stride, (uint32_t)((len - 1) * row_bytes + CW * 2));
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             const int lc = wcol0 + 16 * ct + cg;         // column within the part
@@ -184,6 +224,9 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
                 Sb[kb][2] = pack2(S[ct][2 * kb + 1][0], S[ct][2 * kb + 1][1]);
                 Sb[kb][3] = pack2(S[ct][2 * kb + 1][2], S[ct][2 * kb + 1][3]);
             }
+            // decayed old state: the accumulator the update MFMAs add W^T X to
+#pragma unroll
+            for (int t = 0; t < 8; ++t) S[ct][t] = S[ct][t] * gam[t];
             f32x4_t P = {0.f, 0.f, 0.f, 0.f}, Qs = P;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
@@ -196,25 +239,23 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
             u32x2_t Xb;
             Xb[0] = pack2(x[0], x[1]);
             Xb[1] = pack2(x[2], x[3]);
-            const f32x4_t O = mfma_k16(m, Xb, Qs);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                __builtin_amdgcn_raw_buffer_store_b16(tobf16(scale * O[j]), ro,
-                                                      (int)((4 * grp + j) * row_bytes) + lc * 2, 0, 0);
 #pragma unroll
             for (int tp = 0; tp < 4; ++tp) {
                 u32x2_t lo = {wt[tp][0], wt[tp][1]}, hi = {wt[tp][2], wt[tp][3]};
                 S[ct][2 * tp] = mfma_k16(lo, Xb, S[ct][2 * tp]);
                 S[ct][2 * tp + 1] = mfma_k16(hi, Xb, S[ct][2 * tp + 1]);
             }
+            const f32x4_t O = mfma_k16(m, Xb, Qs);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) S[ct][t] = S[ct][t] * gam[t];
+            for (int j = 0; j < 4; ++j)
+                __builtin_amdgcn_raw_buffer_store_b16(tobf16(scale * O[j]), ro,
+                                                      (int)((4 * grp + j) * row_bytes) + lc * 2, 0, 0);
         }
     };
 
     // Prologue: chunks 0 .. DEPTH-2 in flight.
 #pragma unroll
-    for (int c = 0; c < DEPTH - 1; ++c) issue(c);
+    for (int c = 0; c < DEPTH - 1; ++c) issue(c, c);
 
     // Iteration c: wait for chunk c, barrier, compute (SW stores), then
     // refill the slot chunk c-1 used with chunk c+DEPTH-1 (LW DMAs; every
@@ -226,15 +267,17 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
     // and waiting until at most that many are outstanding means chunk c has
     // landed in LDS.
     static_assert((DEPTH - 2) * (LW + SW) <= 63, "vmcnt holds at most 63");
+    static_assert(DEPTH == 5, "the wait ladder below is written for 5 slots");
+    int slot = 0, refill = DEPTH - 1;                // ring slots of chunk c and chunk c+DEPTH-1
     for (int c = 0; c < nch; ++c) {
-        switch (c < DEPTH - 2 ? c : DEPTH - 2) {
-            case 0: wait_vm_barrier<(DEPTH - 2) * LW + 0 * SW>(); break;
-            case 1: wait_vm_barrier<(DEPTH - 2) * LW + 1 * SW>(); break;
-            case 2: wait_vm_barrier<(DEPTH - 2) * LW + 2 * SW>(); break;
-            default: wait_vm_barrier<(DEPTH - 2) * LW + (DEPTH - 2) * SW>(); break;
-        }
-        compute(c);
-        issue(c + DEPTH - 1);
+        if (c >= DEPTH - 2) wait_vm_barrier<(DEPTH - 2) * (LW + SW)>();
+        else if (c == 0) wait_vm_barrier<(DEPTH - 2) * LW>();
+        else if (c == 1) wait_vm_barrier<(DEPTH - 2) * LW + SW>();
+        else wait_vm_barrier<(DEPTH - 2) * LW + 2 * SW>();
+        compute(c, slot);
+        issue(c + DEPTH - 1, refill);
+        slot = slot == DEPTH - 1 ? 0 : slot + 1;
+        refill = refill == DEPTH - 1 ? 0 : refill + 1;
     }
     // drain the DMAs of the chunks past the end before the workgroup exits
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -4,7 +4,7 @@ the documented register layouts) against fp64 chunk maths.
 Per 16-token chunk with in-chunk inclusive cumulative log-decay G:
   gamma = e^{G_last}; Kt = k e^G; Qt = q e^G; Kb = k e^-G;
   Tb = (I + diag(beta) strict_lower(Kt Kb^T))^-1 diag(beta);
-  Aqk = lower_incl(Qt Kb^T); M = Aqk Tb; W = Tb^T Kb.
+  Aqk = lower_incl(Qt Kb^T); M = Aqk Tb; W = Tb^T Kb diag(gamma).
 """
 from __future__ import annotations
 
@@ -74,7 +74,7 @@ def expected_chunk(inp, t0, n_tok, h):
     T = np.linalg.inv(np.eye(n_tok) + L)
     Tb = T * beta[None, :]
     Aq = np.tril(Qt @ Kb.T)
-    return Kt, Qt, Tb.T @ Kb, Aq @ Tb, np.exp(G[-1])
+    return Kt, Qt, (Tb.T @ Kb) * np.exp(G[-1])[None, :], Aq @ Tb, np.exp(G[-1])
 
 
 def rel(a, b):
