@@ -54,6 +54,24 @@ def algorithmic(w, has_init=True, has_final=True):
             "flops": 2.0 * macs * th}
 
 
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/hbm_traffic_<workload>.json: FETCH_SIZE and WRITE_SIZE runs
+    scaled by a plain copy of known size), or None when there is none or the
+    kernel sources changed since the counters were taken."""
+    import kimi_delta_attention_04_amd as kda
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != kda.source_digest() or kernel not in rec.get("kernels", {}):
+        return None
+    k = rec["kernels"][kernel]
+    return {"read_bytes": k["read_bytes"], "write_bytes": k["write_bytes"],
+            "total_bytes": k["read_bytes"] + k["write_bytes"]}
+
+
 def cpu_baseline(inp, w, heads: int):
     import oracle
     sel = list(range(min(heads, w.H)))
@@ -159,15 +177,20 @@ def main():
     dom_name = max(kernels, key=lambda k: kernels[k]["ms"])
     dom = kernels[dom_name]
     achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+    tr = stored_traffic(name, dom_name)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom_name,
-                "bytes_per_launch": dom["bytes"], "avg_launch_ms": dom["ms"]}
+                "frac": achieved / HBM_PEAK_GBS,
+                "traffic": tr["total_bytes"] if tr else None,
+                "traffic_x_algorithmic": tr["total_bytes"] / dom["bytes"] if tr else None,
+                "kernel": dom_name, "bytes_per_launch": dom["bytes"], "avg_launch_ms": dom["ms"]}
     path_gbs = alg["total_bytes"] / (ms * 1e-3) / 1e9
     path_tflops = alg["flops"] / (ms * 1e-3) / 1e12
     path = {"algorithmic_bytes": alg["total_bytes"], "hbm_achieved_GBs": path_gbs,
             "hbm_frac": path_gbs / HBM_PEAK_GBS, "algorithmic_flops": alg["flops"],
             "mfma_achieved_TFLOPs": path_tflops, "mfma_frac": path_tflops / BF16_PEAK_TFLOPS,
             "stage_ms": {k: v["ms"] for k, v in kernels.items()},
+            "stage_traffic_bytes": {k: (t["total_bytes"] if t else None) for k, t in
+                                    ((k, stored_traffic(name, k)) for k in kernels)},
             "stage_ms_min": {"kda_intra": min(intra_ms), "kda_scan": min(scan_ms)}}
 
     cpu = None

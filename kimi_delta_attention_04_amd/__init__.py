@@ -69,6 +69,19 @@ def load():
     return lib
 
 
+def source_digest() -> str:
+    """sha256 over the HIP sources of the library (identifies the kernels a
+    stored profile was taken on)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(_HERE, "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
 def status_string(status: int) -> str:
     if _lib is not None:
         return _lib.kda_status_string(int(status)).decode()
