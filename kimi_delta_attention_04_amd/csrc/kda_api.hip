@@ -6,7 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/kda.h"
+#include "kda.h"
 #include "kda_device.h"
 #include "kda_launch.h"
 

@@ -30,7 +30,8 @@ namespace {
 
 constexpr int SCAN_WAVES = 4;
 constexpr int SCAN_THREADS = 64 * SCAN_WAVES;
-constexpr int DEPTH = 5;                         // LDS ring slots: DEPTH - 1 chunks in flight
+// LDS ring slots per workgroup (chunks in flight + the one being read)
+template <int CT> constexpr int RING_DEPTH = CT == 1 ? 5 : 5;
 constexpr int REC_KB = REC_BYTES / 1024;         // 13 one-kilobyte units per record
 
 static_assert(REC_BYTES % 1024 == 0, "record must be a whole number of 1 KB units");
@@ -42,6 +43,17 @@ template <int NV>
 __device__ __forceinline__ void wait_vm_barrier() {
     static_assert(NV >= 0 && NV <= 63, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(NV) : "memory");
+}
+
+// wait_vm_barrier<BASE + min(c, LAST) * STEP>() for a run-time c.
+template <int BASE, int STEP, int LAST, int I = 0>
+__device__ __forceinline__ void wait_ladder(int c) {
+    if constexpr (I == LAST) {
+        wait_vm_barrier<BASE + LAST * STEP>();
+    } else {
+        if (c == I) wait_vm_barrier<BASE + I * STEP>();
+        else wait_ladder<BASE, STEP, LAST, I + 1>(c);
+    }
 }
 
 // Raw buffer descriptor words (base, stride 0, num_records, the same
@@ -76,8 +88,35 @@ struct alignas(16) ScanSlot {
     uint16_t v[CS][CW];
 };
 
+// Lane n of each 16-lane row, broadcast to the whole row (DPP row_newbcast);
+// the compiler folds it into the consuming VALU instruction.
+template <int SRC>
+__device__ __forceinline__ float row_bcast(float x) {
+    static_assert(SRC >= 0 && SRC < 16, "row lane");
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                              0x150 + SRC, 0xf, 0xf, true));
+}
+
+// The MFMA operands of one chunk, as one wave holds them in registers.
 template <int CT>
-__global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
+struct ChunkOps {
+    u32x4_t kt[4], qt[4], wt[4];
+    u32x2_t m;
+    float gm[2];              // chunk decay of two state rows (see load_ops)
+    float v[CT][4];           // v[4grp + j][column] of each slice
+};
+
+// Row multiplier of the decay: S[t][j] (state row chan(t, 4grp + j)) takes
+// the chunk decay that lane 4(t/2) + 2(t%2) + j/2 of its 16-lane row holds
+// in gm[j%2].  Lane cg of row grp loads the decays of channels
+// 32(cg/4) + 8grp + 4((cg/2)%2) + 2(cg%2) + {0, 1}, which is exactly that.
+template <int T, int J>
+__device__ __forceinline__ float decay_of(const float (&gm)[2]) {
+    return row_bcast<4 * (T >> 1) + 2 * (T & 1) + (J >> 1)>(gm[J & 1]);
+}
+
+template <int CT>
+__global__ __launch_bounds__(SCAN_THREADS, CT == 1 ? 2 : 1) void scan_kernel(
     const uint16_t *__restrict__ v, const uint8_t *__restrict__ ws,
     const int32_t *__restrict__ cu, int N, int T, int H, float scale,
     const void *__restrict__ init, int init_fp32,
@@ -90,6 +129,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
     constexpr int LW = (UNITS + SCAN_WAVES - 1) / SCAN_WAVES;   // DMAs per wave per chunk
     constexpr int SW = 4 * CT;                       // out stores per lane per chunk
     constexpr int VROW_LANES = CW * 2 / 16;          // lanes per v row in a DMA unit
+    constexpr int DEPTH = RING_DEPTH<CT>;
     __shared__ ScanSlot<CW> ring[DEPTH];
     __shared__ __attribute__((aligned(16))) uint8_t sink[1024];   // target of padding DMAs
 
@@ -193,25 +233,34 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
         }
     };
 
-    auto compute = [&](int c, int slot) {
+    // LDS -> registers: the operands of the chunk in ring slot `slot`.
+    auto load_ops = [&](int slot, ChunkOps<CT> &op) {
         const ScanSlot<CW> &sl = ring[slot];
         const uint8_t *R = sl.rec;
-        u32x4_t kt[4], qt[4], wt[4];
-        f32x4_t gam[8];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            kt[kb] = *(const u32x4_t *)(R + REC_KT + (kb * 64 + l) * 16);
-            qt[kb] = *(const u32x4_t *)(R + REC_QT + (kb * 64 + l) * 16);
-            wt[kb] = *(const u32x4_t *)(R + REC_WT + (kb * 64 + l) * 16);
-            gam[2 * kb] = *(const f32x4_t *)(R + REC_GAM + (32 * kb + 8 * grp) * 4);
-            gam[2 * kb + 1] = *(const f32x4_t *)(R + REC_GAM + (32 * kb + 8 * grp + 4) * 4);
+            op.kt[kb] = *(const u32x4_t *)(R + REC_KT + (kb * 64 + l) * 16);
+            op.qt[kb] = *(const u32x4_t *)(R + REC_QT + (kb * 64 + l) * 16);
+            op.wt[kb] = *(const u32x4_t *)(R + REC_WT + (kb * 64 + l) * 16);
         }
-        const u32x2_t m = *(const u32x2_t *)(R + REC_M + l * 8);
+        op.m = *(const u32x2_t *)(R + REC_M + l * 8);
+        const int gch = 32 * (cg >> 2) + 8 * grp + 4 * ((cg >> 1) & 1) + 2 * (cg & 1);
+        const u32x2_t g2 = *(const u32x2_t *)(R + REC_GAM + gch * 4);
+        op.gm[0] = __uint_as_float(g2[0]);
+        op.gm[1] = __uint_as_float(g2[1]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) op.v[ct][j] = bf16f(sl.v[4 * grp + j][wcol0 + 16 * ct + cg]);
+    };
+
+    auto compute = [&](int c, const ChunkOps<CT> &op) {
         const int64_t rem = L - (int64_t)c * CS;
         const int len = (int)(rem < CS ? rem : CS);
         // rows past the sequence end fall outside the resource and are dropped
         const __amdgpu_buffer_rsrc_t ro =
             make_rsrc(out_base + (size_t)c * row_stride, (uint32_t)((len - 1) * row_bytes + CW * 2));
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             const int lc = wcol0 + 16 * ct + cg;         // column within the part
@@ -224,60 +273,71 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
                 Sb[kb][2] = pack2(S[ct][2 * kb + 1][0], S[ct][2 * kb + 1][1]);
                 Sb[kb][3] = pack2(S[ct][2 * kb + 1][2], S[ct][2 * kb + 1][3]);
             }
-            // decayed old state: the accumulator the update MFMAs add W^T X to
-#pragma unroll
-            for (int t = 0; t < 8; ++t) S[ct][t] = S[ct][t] * gam[t];
-            f32x4_t P = {0.f, 0.f, 0.f, 0.f}, Qs = P;
+            f32x4_t P = zero, Qs = zero;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                P = mfma_k32(kt[kb], Sb[kb], P);
-                Qs = mfma_k32(qt[kb], Sb[kb], Qs);
+                P = mfma_k32(op.kt[kb], Sb[kb], P);
+                Qs = mfma_k32(op.qt[kb], Sb[kb], Qs);
             }
-            float x[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = bf16f(sl.v[4 * grp + j][lc]) - P[j];
+            // decayed old state: the accumulator the update MFMAs add W^T X to
+#define KDA_DECAY(T_)                                              \
+            S[ct][T_][0] *= decay_of<T_, 0>(op.gm);                \
+            S[ct][T_][1] *= decay_of<T_, 1>(op.gm);                \
+            S[ct][T_][2] *= decay_of<T_, 2>(op.gm);                \
+            S[ct][T_][3] *= decay_of<T_, 3>(op.gm);
+            KDA_DECAY(0) KDA_DECAY(1) KDA_DECAY(2) KDA_DECAY(3)
+            KDA_DECAY(4) KDA_DECAY(5) KDA_DECAY(6) KDA_DECAY(7)
+#undef KDA_DECAY
             u32x2_t Xb;
-            Xb[0] = pack2(x[0], x[1]);
-            Xb[1] = pack2(x[2], x[3]);
+            Xb[0] = pack2(op.v[ct][0] - P[0], op.v[ct][1] - P[1]);
+            Xb[1] = pack2(op.v[ct][2] - P[2], op.v[ct][3] - P[3]);
 #pragma unroll
             for (int tp = 0; tp < 4; ++tp) {
-                u32x2_t lo = {wt[tp][0], wt[tp][1]}, hi = {wt[tp][2], wt[tp][3]};
+                u32x2_t lo = {op.wt[tp][0], op.wt[tp][1]}, hi = {op.wt[tp][2], op.wt[tp][3]};
                 S[ct][2 * tp] = mfma_k16(lo, Xb, S[ct][2 * tp]);
                 S[ct][2 * tp + 1] = mfma_k16(hi, Xb, S[ct][2 * tp + 1]);
             }
-            const f32x4_t O = mfma_k16(m, Xb, Qs);
+            // M X in an accumulator of its own (no accumulator chaining
+            // between MFMA opcodes of different shapes), added on the VALU
+            const f32x4_t MX = mfma_k16(op.m, Xb, zero);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                __builtin_amdgcn_raw_buffer_store_b16(tobf16(scale * O[j]), ro,
+                __builtin_amdgcn_raw_buffer_store_b16(tobf16(scale * (Qs[j] + MX[j])), ro,
                                                       (int)((4 * grp + j) * row_bytes) + lc * 2, 0, 0);
         }
     };
 
-    // Prologue: chunks 0 .. DEPTH-2 in flight.
+    // Software pipeline: iteration c computes chunk c from registers loaded
+    // in iteration c-1, loads chunk c+1 from the ring and refills the slot
+    // of chunk c with chunk c+DEPTH.  VMEM issue order per wave:
+    //   P_0 .. P_{DEPTH-1} | I_DEPTH S_0 | I_{DEPTH+1} S_1 | ...
+    // (P: prologue DMAs, I_j: DMAs of chunk j, LW each; S_c: the SW out
+    // stores of iteration c).  At the top of iteration c the operations
+    // issued after chunk c+1's DMAs number
+    //   (DEPTH-2) LW + min(c, DEPTH-1) SW,
+    // so waiting until at most that many are outstanding means chunk c+1 has
+    // landed; the barrier after it also means every wave has finished its
+    // reads of chunk c's slot (s_waitcnt lgkmcnt(0) before the barrier).
+    static_assert((DEPTH - 2) * LW + (DEPTH - 1) * SW <= 63, "vmcnt holds at most 63");
 #pragma unroll
-    for (int c = 0; c < DEPTH - 1; ++c) issue(c, c);
+    for (int c = 0; c < DEPTH; ++c) issue(c, c);
+    wait_vm_barrier<(DEPTH - 1) * LW>();              // chunk 0 landed
 
-    // Iteration c: wait for chunk c, barrier, compute (SW stores), then
-    // refill the slot chunk c-1 used with chunk c+DEPTH-1 (LW DMAs; every
-    // wave finished chunk c-1 before the barrier).  Issue order is
-    //   P_0 .. P_{DEPTH-2} | S_0 I_{DEPTH-1} | S_1 I_{DEPTH} | ...
-    // (P: prologue DMAs, S_c: stores of iteration c, I_j: DMAs of chunk j), so
-    // at iteration c the operations issued after chunk c's DMAs number
-    //   (DEPTH-2) LW + min(c, DEPTH-2) SW,
-    // and waiting until at most that many are outstanding means chunk c has
-    // landed in LDS.
-    static_assert((DEPTH - 2) * (LW + SW) <= 63, "vmcnt holds at most 63");
-    static_assert(DEPTH == 5, "the wait ladder below is written for 5 slots");
-    int slot = 0, refill = DEPTH - 1;                // ring slots of chunk c and chunk c+DEPTH-1
-    for (int c = 0; c < nch; ++c) {
-        if (c >= DEPTH - 2) wait_vm_barrier<(DEPTH - 2) * (LW + SW)>();
-        else if (c == 0) wait_vm_barrier<(DEPTH - 2) * LW>();
-        else if (c == 1) wait_vm_barrier<(DEPTH - 2) * LW + SW>();
-        else wait_vm_barrier<(DEPTH - 2) * LW + 2 * SW>();
-        compute(c, slot);
-        issue(c + DEPTH - 1, refill);
-        slot = slot == DEPTH - 1 ? 0 : slot + 1;
-        refill = refill == DEPTH - 1 ? 0 : refill + 1;
+    ChunkOps<CT> opA, opB;
+    load_ops(0, opA);
+    auto top_wait = [&](int c) { wait_ladder<(DEPTH - 2) * LW, SW, DEPTH - 1>(c); };
+    int slot = 0, next = 1;                           // ring slots of chunks c and c+1
+    auto step = [&](int c, const ChunkOps<CT> &cur, ChunkOps<CT> &nxt) {
+        top_wait(c);
+        load_ops(next, nxt);
+        issue(c + DEPTH, slot);
+        compute(c, cur);
+        slot = next;
+        next = next == DEPTH - 1 ? 0 : next + 1;
+    };
+    for (int c = 0; c < nch; c += 2) {
+        step(c, opA, opB);
+        if (c + 1 < nch) step(c + 1, opB, opA);
     }
     // drain the DMAs of the chunks past the end before the workgroup exits
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
