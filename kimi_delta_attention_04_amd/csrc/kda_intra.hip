@@ -1,8 +1,7 @@
 // Intra-chunk stage: token-parallel over (chunk, head).
 //
-// One wave handles one (16-token chunk, head); a 128-thread workgroup holds
-// two consecutive heads of the same chunk so each token row it touches is one
-// contiguous 512-byte run of q / k / g.  Per chunk it
+// One wave (a workgroup of its own) handles one (16-token chunk, head).  Per
+// chunk it
 //   1. evaluates the gate in base 2 (the exponent rebasing idea of "Moonshot
 //      AI Open-Sources FlashKDA", section "What makes the kernel fast"):
 //        log2 alpha = max(-A * log2(1 + 2^{(g + dt_bias) log2 e}), lb log2 e)
@@ -26,18 +25,28 @@ namespace kda {
 
 namespace {
 
-constexpr int WAVES = 2;
-constexpr int LROW = 136;   // bf16 per row of a token-major tile: 128 + 8 padding
-constexpr int LCOL = 20;    // bf16 per row of a channel-major tile: 16 tokens + 4 padding
+// Token-major operand tile: 16 rows (tokens) x 128 bf16 (channels) = 16
+// rows of sixteen 16-byte units; unit u of row r is stored at u ^ r, so that
+// both the row-wise writes of the elementwise stage and the column-block
+// reads of the MFMA stage touch eight different 16-byte bank groups per
+// eight lanes.
+constexpr int TILE = CS * HD;                 // bf16 per tile
+__device__ __forceinline__ int tile_off(int r, int u) { return r * HD + ((u ^ r) << 3); }
+
+// Channel-major tile (128 channels x 16 tokens, 8-byte units of 4 tokens):
+// channel ch sits in row slot (ch & ~3) | ((ch ^ (ch >> 5)) & 3) and its
+// token unit gq in unit gq ^ ((ch >> 3) & 3).  Both the writes (lanes vary
+// channel bits 3..6) and the W-operand reads (lanes vary bits 0, 1, 3, 4)
+// then hit sixteen different 8-byte bank pairs per sixteen lanes.
+__device__ __forceinline__ int cmaj_off(int ch, int gq) {
+    const int row = (ch & ~3) | ((ch ^ (ch >> 5)) & 3);
+    return row * CS + ((gq ^ ((ch >> 3) & 3)) << 2);
+}
 
 struct WaveLds {
-    uint16_t kt[CS][LROW];          // Kt (bf16), token-major
-    uint16_t qh[CS][LROW];          // Qt hi
-    uint16_t ql[CS][LROW];          // Qt lo
-    uint16_t bh[CS][LROW];          // Kb hi
-    uint16_t bl[CS][LROW];          // Kb lo
-    uint16_t bhT[HD][LCOL];         // Kb hi, channel-major
-    uint16_t blT[HD][LCOL];         // Kb lo, channel-major
+    // Kt, Qt hi, Qt lo, Kb hi, Kb lo (token-major).  Once the Gram products
+    // have read them, tiles 0 and 1 are reused for Kb hi / lo channel-major.
+    uint16_t tile[5][TILE];
     float beta[CS];
     float gam[HD];                  // e^{G_last} per channel
 };
@@ -69,84 +78,68 @@ __device__ __forceinline__ uint32_t half16(uint32_t w, int i) {
     return (i & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-__global__ __launch_bounds__(64 * WAVES) void intra_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+// One (chunk, head) of the intra-chunk stage by one wave.  FULL: all 16
+// rows are tokens of the sequence (no masking of the cumulative decay).
+template <bool FULL>
+__device__ __forceinline__ void intra_chunk(
+    WaveLds &L, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
-    const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb2,
-    const int32_t *__restrict__ cu, int N, int T, int H, uint8_t *__restrict__ ws)
+    float A, const float (&dtb2)[8], float lb2, int64_t t0, int len, int H, int hh,
+    uint8_t *__restrict__ rec)
 {
-    __shared__ __attribute__((aligned(16))) WaveLds lds[WAVES];
-
-    const int w = threadIdx.x >> 6;
     const int l = threadIdx.x & 63;
     const int grp = l >> 4;        // token group: rows 4grp .. 4grp+3 while loading
     const int cg = l & 15;         // channel group: channels 8cg .. 8cg+7 while loading
-    const int64_t slot = blockIdx.x;
-    const int h = blockIdx.y * WAVES + w;
-    const bool hv = h < H;         // wave-uniform
-    const int hh = hv ? h : 0;
-    WaveLds &L = lds[w];
-
-    // Which sequence owns this slot: largest n with slot0(n) <= slot.
-    int lo = 0, hi = N - 1;
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (seq_slot0(cu, mid, T) <= slot) lo = mid; else hi = mid - 1;
-    }
-    const int n = lo;
-    int64_t start, end;
-    seq_range(cu, n, T, start, end);
-    const int64_t t0 = start + (slot - seq_slot0(cu, n, T)) * CS;
-    if (t0 >= end) return;                         // gap slot, block-uniform
-    const int len = (int)min((int64_t)CS, end - t0);
-    uint8_t *rec = ws + ((size_t)slot * H + hh) * REC_BYTES;
-
-    // ---- gate parameters -------------------------------------------------
-    const float A = expf(A_log[hh]);
-    float dtb2[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        dtb2[i] = dt_bias ? dt_bias[(size_t)hh * HD + 8 * cg + i] * LOG2E : 0.f;
+    const size_t row_elems = (size_t)H * HD;
 
     if (l < CS) {
         float b = 0.f;
-        if (hv && l < len) {
+        if (FULL || l < len) {
             float x = bf16f(beta[(size_t)(t0 + l) * H + hh]);
             b = __builtin_amdgcn_rcpf(1.f + fast_exp2(-x * LOG2E));
         }
         L.beta[l] = b;
     }
 
-    // ---- load rows 4grp+p, channels 8cg..8cg+7 ----------------------------
+    // ---- load rows 4grp+p, channels 8cg..8cg+7 (rows past len read as 0) --
     u32x4_t rg[4], rq[4], rk[4];
+    {
+        const size_t base = ((size_t)t0 * H + hh) * HD;
+        const uint32_t bytes = (uint32_t)(((size_t)(len - 1) * row_elems + HD) * 2);
+        const __amdgpu_buffer_rsrc_t sg = make_rsrc(g + base, bytes);
+        const __amdgpu_buffer_rsrc_t sq = make_rsrc(q + base, bytes);
+        const __amdgpu_buffer_rsrc_t sk = make_rsrc(k + base, bytes);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int r = 4 * grp + p;
-        const u32x4_t z = {0u, 0u, 0u, 0u};
-        rg[p] = z; rq[p] = z; rk[p] = z;
-        if (hv && r < len) {
-            const size_t off = ((size_t)(t0 + r) * H + hh) * HD + 8 * cg;
-            rg[p] = *(const u32x4_t *)(g + off);
-            rq[p] = *(const u32x4_t *)(q + off);
-            rk[p] = *(const u32x4_t *)(k + off);
+        for (int p = 0; p < 4; ++p) {
+            const int off = (int)(((4 * grp + p) * row_elems + 8 * cg) * 2);
+            rg[p] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sg, off, 0, 0));
+            rq[p] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sq, off, 0, 0));
+            rk[p] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sk, off, 0, 0));
         }
     }
 
     // ---- gate and cumulative sum ----------------------------------------
-    // A == 0 (A_log = -inf) means no decay at all; testing it once keeps the
-    // per-element path free of 0 * inf.
+    // A == 0 (A_log = -inf) means no decay at all; the wave-uniform branch
+    // keeps the per-element path free of 0 * inf.
     float G[4][8];
+    if (A > 0.f) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float acc = 0.f;
+        for (int i = 0; i < 8; ++i) {
+            float acc = 0.f;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const float x2 = elem(rg[p], i) * LOG2E + dtb2[i];
-            const float u = fast_log2(1.f + fast_exp2(x2));
-            const float la = A > 0.f ? fmaxf(-A * u, lb2) : 0.f;
-            acc += (4 * grp + p < len) ? la : 0.f;
-            G[p][i] = acc;
+            for (int p = 0; p < 4; ++p) {
+                const float x2 = elem(rg[p], i) * LOG2E + dtb2[i];
+                const float u = fast_log2(1.f + fast_exp2(x2));
+                const float la = fmaxf(-A * u, lb2);
+                acc += (FULL || 4 * grp + p < len) ? la : 0.f;
+                G[p][i] = acc;
+            }
         }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) G[p][i] = 0.f;
     }
     // exclusive prefix over the four token groups (lanes 16 apart)
 #pragma unroll
@@ -186,22 +179,11 @@ __global__ __launch_bounds__(64 * WAVES) void intra_kernel(
             split2(kb[0], kb[1], a, b); bh4[p][wd] = a; bl4[p][wd] = b;
         }
         const int r = 4 * grp + p;
-        *(u32x4_t *)&L.kt[r][8 * cg] = kt4;
-        *(u32x4_t *)&L.qh[r][8 * cg] = qh4;
-        *(u32x4_t *)&L.ql[r][8 * cg] = ql4;
-        *(u32x4_t *)&L.bh[r][8 * cg] = bh4[p];
-        *(u32x4_t *)&L.bl[r][8 * cg] = bl4[p];
-    }
-    // channel-major Kb: channel 8cg+i, tokens 4grp..4grp+3 (8 bytes)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        u32x2_t vh, vl;
-        vh[0] = half16(bh4[0][i >> 1], i) | (half16(bh4[1][i >> 1], i) << 16);
-        vh[1] = half16(bh4[2][i >> 1], i) | (half16(bh4[3][i >> 1], i) << 16);
-        vl[0] = half16(bl4[0][i >> 1], i) | (half16(bl4[1][i >> 1], i) << 16);
-        vl[1] = half16(bl4[2][i >> 1], i) | (half16(bl4[3][i >> 1], i) << 16);
-        *(u32x2_t *)&L.bhT[8 * cg + i][4 * grp] = vh;
-        *(u32x2_t *)&L.blT[8 * cg + i][4 * grp] = vl;
+        *(u32x4_t *)&L.tile[0][tile_off(r, cg)] = kt4;
+        *(u32x4_t *)&L.tile[1][tile_off(r, cg)] = qh4;
+        *(u32x4_t *)&L.tile[2][tile_off(r, cg)] = ql4;
+        *(u32x4_t *)&L.tile[3][tile_off(r, cg)] = bh4[p];
+        *(u32x4_t *)&L.tile[4][tile_off(r, cg)] = bl4[p];
     }
 
     if (grp == 3) {
@@ -211,11 +193,9 @@ __global__ __launch_bounds__(64 * WAVES) void intra_kernel(
         for (int i = 0; i < 4; ++i) { g0[i] = fast_exp2(G[3][i]); g1[i] = fast_exp2(G[3][4 + i]); }
         *(f32x4_t *)&L.gam[8 * cg] = g0;
         *(f32x4_t *)&L.gam[8 * cg + 4] = g1;
-        if (hv) {
-            float *gp = (float *)(rec + REC_GAM) + 8 * cg;
-            *(f32x4_t *)gp = g0;
-            *(f32x4_t *)(gp + 4) = g1;
-        }
+        float *gp = (float *)(rec + REC_GAM) + 8 * cg;
+        *(f32x4_t *)gp = g0;
+        *(f32x4_t *)(gp + 4) = g1;
     }
 
     __syncthreads();
@@ -225,21 +205,32 @@ __global__ __launch_bounds__(64 * WAVES) void intra_kernel(
     f32x4_t Akk = {0.f, 0.f, 0.f, 0.f}, AkkT = Akk, AqkT = Akk;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        const int c0 = 32 * kb + 8 * grp;
-        const u32x4_t aK = *(const u32x4_t *)&L.kt[cg][c0];
-        const u32x4_t aQh = *(const u32x4_t *)&L.qh[cg][c0];
-        const u32x4_t aQl = *(const u32x4_t *)&L.ql[cg][c0];
-        const u32x4_t aBh = *(const u32x4_t *)&L.bh[cg][c0];
-        const u32x4_t aBl = *(const u32x4_t *)&L.bl[cg][c0];
-        if (hv) {
-            *(u32x4_t *)(rec + REC_KT + (kb * 64 + l) * 16) = aK;
-            *(u32x4_t *)(rec + REC_QT + (kb * 64 + l) * 16) = aQh;
-        }
+        const int o = tile_off(cg, 4 * kb + grp);
+        const u32x4_t aK = *(const u32x4_t *)&L.tile[0][o];
+        const u32x4_t aQh = *(const u32x4_t *)&L.tile[1][o];
+        const u32x4_t aQl = *(const u32x4_t *)&L.tile[2][o];
+        const u32x4_t aBh = *(const u32x4_t *)&L.tile[3][o];
+        const u32x4_t aBl = *(const u32x4_t *)&L.tile[4][o];
+        *(u32x4_t *)(rec + REC_KT + (kb * 64 + l) * 16) = aK;
+        *(u32x4_t *)(rec + REC_QT + (kb * 64 + l) * 16) = aQh;
         Akk = mfma_k32(aK, aBh, Akk);       // Akk[4grp+j][cg]  = Kt_r . Kb_i
         AkkT = mfma_k32(aBh, aK, AkkT);     // AkkT[4grp+j][cg] = Akk[cg][4grp+j]
         AqkT = mfma_k32(aBh, aQh, AqkT);    // AqkT[4grp+j][cg] = Aqk[cg][4grp+j]
         AqkT = mfma_k32(aBh, aQl, AqkT);
         AqkT = mfma_k32(aBl, aQh, AqkT);
+    }
+    // channel-major Kb (hi, lo) into tiles 0 and 1: channel 8cg+i, tokens
+    // 4grp..4grp+3 (the Gram reads above come first in this wave's LDS order)
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        u32x2_t vh, vl;
+        vh[0] = half16(bh4[0][i >> 1], i) | (half16(bh4[1][i >> 1], i) << 16);
+        vh[1] = half16(bh4[2][i >> 1], i) | (half16(bh4[3][i >> 1], i) << 16);
+        vl[0] = half16(bl4[0][i >> 1], i) | (half16(bl4[1][i >> 1], i) << 16);
+        vl[1] = half16(bl4[2][i >> 1], i) | (half16(bl4[3][i >> 1], i) << 16);
+        *(u32x2_t *)&L.tile[0][cmaj_off(8 * cg + i, grp)] = vh;
+        *(u32x2_t *)&L.tile[1][cmaj_off(8 * cg + i, grp)] = vl;
     }
 
     // ---- T = (I + L)^{-1}, L = diag(beta) strict_lower(Akk) ---------------
@@ -265,8 +256,6 @@ __global__ __launch_bounds__(64 * WAVES) void intra_kernel(
     const f32x4_t N8 = mm16(N4t, N4);
     const f32x4_t P8 = I + N8;
     const f32x4_t Tm = mm16(Q3t, P8);                   // T in accumulator layout
-
-    if (!hv) return;                                    // wave-uniform; no barrier follows
 
     // T diag(beta) in accumulator layout (row 4grp+j, column cg), as (hi, lo):
     // this is also the A-operand layout of (T diag(beta))^T.
@@ -299,6 +288,7 @@ __global__ __launch_bounds__(64 * WAVES) void intra_kernel(
     mo[1] = pack2(Mt[2], Mt[3]);
     *(u32x2_t *)(rec + REC_M + l * 8) = mo;
 
+    __syncthreads();
     // W tiles: W[:, chan(t, .)] = (T diag(beta))^T Kb[:, chan(t, .)] times the
     // chunk decay of that channel; the accumulator layout is the A layout of
     // W^T tile t the scan needs.
@@ -308,8 +298,8 @@ __global__ __launch_bounds__(64 * WAVES) void intra_kernel(
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int ch = state_chan(2 * tp + half, cg);
-            const u32x2_t bh = *(const u32x2_t *)&L.bhT[ch][4 * grp];
-            const u32x2_t bl = *(const u32x2_t *)&L.blT[ch][4 * grp];
+            const u32x2_t bh = *(const u32x2_t *)&L.tile[0][cmaj_off(ch, grp)];
+            const u32x2_t bl = *(const u32x2_t *)&L.tile[1][cmaj_off(ch, grp)];
             f32x4_t Wt = mfma_k16(tbh, bh, zero);
             Wt = mfma_k16(tbh, bl, Wt);
             Wt = mfma_k16(tbl, bh, Wt);
@@ -321,6 +311,46 @@ __global__ __launch_bounds__(64 * WAVES) void intra_kernel(
     }
 }
 
+// One wave per (chunk slot, head): workgroups of one wave, so that the
+// 21 KB of LDS a wave needs bounds the occupancy, not a pair of waves.
+__global__ __launch_bounds__(64, 2) void intra_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
+    const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb2,
+    const int32_t *__restrict__ cu, int N, int T, int H, uint8_t *__restrict__ ws)
+{
+    __shared__ __attribute__((aligned(16))) WaveLds lds;
+    const int l = threadIdx.x;
+    const int cg = l & 15;
+    const int64_t slot = blockIdx.x;
+    const int h = blockIdx.y;
+
+    // Which sequence owns this slot: largest n with slot0(n) <= slot.
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (seq_slot0(cu, mid, T) <= slot) lo = mid; else hi = mid - 1;
+    }
+    const int n = lo;
+    int64_t start, end;
+    seq_range(cu, n, T, start, end);
+    const int64_t t0 = start + (slot - seq_slot0(cu, n, T)) * CS;
+    if (t0 >= end) return;                         // gap slot, wave-uniform
+    const int len = (int)min((int64_t)CS, end - t0);
+    uint8_t *rec = ws + ((size_t)slot * H + h) * REC_BYTES;
+
+    const float A = expf(A_log[h]);
+    float dtb2[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        dtb2[i] = dt_bias ? dt_bias[(size_t)h * HD + 8 * cg + i] * LOG2E : 0.f;
+
+    if (len == CS)
+        intra_chunk<true>(lds, q, k, g, beta, A, dtb2, lb2, t0, len, H, h, rec);
+    else
+        intra_chunk<false>(lds, q, k, g, beta, A, dtb2, lb2, t0, len, H, h, rec);
+}
+
 }  // namespace
 
 hipError_t launch_intra(const uint16_t *q, const uint16_t *k, const uint16_t *g,
@@ -329,8 +359,8 @@ hipError_t launch_intra(const uint16_t *q, const uint16_t *k, const uint16_t *g,
                         int64_t num_slots, uint8_t *ws, hipStream_t stream)
 {
     if (num_slots <= 0) return hipSuccess;
-    dim3 grid((unsigned)num_slots, (unsigned)((H + WAVES - 1) / WAVES));
-    hipLaunchKernelGGL(intra_kernel, grid, dim3(64 * WAVES), 0, stream,
+    dim3 grid((unsigned)num_slots, (unsigned)H);
+    hipLaunchKernelGGL(intra_kernel, grid, dim3(64), 0, stream,
                        q, k, g, beta, A_log, dt_bias, lower_bound * LOG2E, cu, N, T, H, ws);
     return hipGetLastError();
 }
