@@ -102,6 +102,14 @@ __device__ __forceinline__ f32x4_t mfma_k4(float a, float b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Orders this wave's LDS accesses across its lanes: LDS instructions of one
+// wave execute in issue order, so only the compiler must be kept from
+// moving accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Raw buffer resource over [p, p + bytes): loads beyond return 0 and stores
 // beyond are dropped (checked per dword), which lets partial chunks run
 // without branches around memory instructions.

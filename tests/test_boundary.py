@@ -96,6 +96,7 @@ def call_fwd(lib, **over):
     (dict(lb=0.5), INVALID), (dict(lb=-6.0), UNSUPPORTED), (dict(lb=-100.0), UNSUPPORTED),
     (dict(B=2, N=2, T=2 ** 30 + 1), UNSUPPORTED),       # token rows overflow int32
     (dict(H=2 ** 26), UNSUPPORTED),                     # (sequence, head) units overflow the grid
+    (dict(H=2 ** 19), UNSUPPORTED),                     # 16-row byte offsets overflow int32
 ])
 def test_fwd_rejects_before_any_hip_call(lib, over, code):
     assert call_fwd(lib, **over) == code
