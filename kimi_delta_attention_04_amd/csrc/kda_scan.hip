@@ -14,13 +14,14 @@
 //
 // The hand-off record of each chunk (13 KB) and the chunk's v tile are read
 // from memory once per workgroup, by buffer-to-LDS DMA into a ring of
-// DEPTH slots, DEPTH-1 chunks ahead of the compute; all four waves read their
-// MFMA operands from the ring.  Every memory access goes through a
-// range-checked buffer resource, so partial chunks need no branches and the
-// number of memory instructions per chunk is fixed, which is what the
-// explicit vmcnt accounting relies on.  The serial chain is what the FlashKDA write-up
-// calls the low-parallelism second stage ("Moonshot AI Open-Sources
-// FlashKDA", section "What makes the kernel fast").
+// DEPTH slots, DEPTH-1 chunks ahead of the compute.  A fifth wave issues all
+// of the DMAs; the four compute waves read their MFMA operands from the
+// ring and never wait on the DMA themselves.  Every memory access goes
+// through a range-checked buffer resource, so partial chunks need no
+// branches and the number of DMAs per chunk is fixed, which is what the
+// DMA wave's explicit vmcnt accounting relies on.  The serial chain is what
+// the FlashKDA write-up calls the low-parallelism second stage ("Moonshot AI
+// Open-Sources FlashKDA", section "What makes the kernel fast").
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -28,10 +29,11 @@ namespace kda {
 
 namespace {
 
-constexpr int SCAN_WAVES = 4;
-constexpr int SCAN_THREADS = 64 * SCAN_WAVES;
-// LDS ring slots per workgroup (chunks in flight + the one being read)
-template <int CT> constexpr int RING_DEPTH = CT == 1 ? 5 : 5;
+constexpr int SCAN_WAVES = 4;                     // compute waves per workgroup
+constexpr int SCAN_THREADS = 64 * (SCAN_WAVES + 1);   // + the DMA wave
+// LDS ring slots per workgroup (chunks in flight + the one being read); the
+// DMA wave's vmcnt (at most 63) must cover DEPTH-1 chunks of DMAs.
+template <int CT> constexpr int RING_DEPTH = CT == 1 ? 5 : 4;
 constexpr int REC_KB = REC_BYTES / 1024;         // 13 one-kilobyte units per record
 
 static_assert(REC_BYTES % 1024 == 0, "record must be a whole number of 1 KB units");
@@ -45,15 +47,10 @@ __device__ __forceinline__ void wait_vm_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(NV) : "memory");
 }
 
-// wait_vm_barrier<BASE + min(c, LAST) * STEP>() for a run-time c.
-template <int BASE, int STEP, int LAST, int I = 0>
-__device__ __forceinline__ void wait_ladder(int c) {
-    if constexpr (I == LAST) {
-        wait_vm_barrier<BASE + LAST * STEP>();
-    } else {
-        if (c == I) wait_vm_barrier<BASE + I * STEP>();
-        else wait_ladder<BASE, STEP, LAST, I + 1>(c);
-    }
+// Workgroup barrier after this wave's LDS accesses have completed (its
+// global stores may still be in flight).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Raw buffer descriptor words (base, stride 0, num_records, the same
@@ -116,7 +113,7 @@ __device__ __forceinline__ float decay_of(const float (&gm)[2]) {
 }
 
 template <int CT>
-__global__ __launch_bounds__(SCAN_THREADS, CT == 1 ? 2 : 1) void scan_kernel(
+__global__ __launch_bounds__(SCAN_THREADS, 2) void scan_kernel(
     const uint16_t *__restrict__ v, const uint8_t *__restrict__ ws,
     const int32_t *__restrict__ cu, int N, int T, int H, float scale,
     const void *__restrict__ init, int init_fp32,
@@ -126,12 +123,10 @@ __global__ __launch_bounds__(SCAN_THREADS, CT == 1 ? 2 : 1) void scan_kernel(
     constexpr int NSPLIT = HD / CW;
     constexpr int V_KB = CS * CW * 2 / 1024;         // one-kilobyte units of a v tile
     constexpr int UNITS = REC_KB + V_KB;             // DMA units per chunk
-    constexpr int LW = (UNITS + SCAN_WAVES - 1) / SCAN_WAVES;   // DMAs per wave per chunk
-    constexpr int SW = 4 * CT;                       // out stores per lane per chunk
     constexpr int VROW_LANES = CW * 2 / 16;          // lanes per v row in a DMA unit
     constexpr int DEPTH = RING_DEPTH<CT>;
     __shared__ ScanSlot<CW> ring[DEPTH];
-    __shared__ __attribute__((aligned(16))) uint8_t sink[1024];   // target of padding DMAs
+    static_assert((DEPTH - 1) * UNITS <= 63, "vmcnt holds at most 63");
 
     // Block b -> (unit u, part): the parts of a unit share b mod 8 (same XCD, same L2).
     const int b = blockIdx.x;
@@ -143,7 +138,8 @@ __global__ __launch_bounds__(SCAN_THREADS, CT == 1 ? 2 : 1) void scan_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int l = tid & 63;
     const int grp = l >> 4, cg = l & 15;
-    const int wcol0 = w * 16 * CT;                    // first column of this wave within the part
+    const bool dma_wave = w == SCAN_WAVES;            // the wave that issues the ring DMAs
+    const int wcol0 = (dma_wave ? 0 : w) * 16 * CT;   // first column of this wave within the part
     const int col0 = part * CW;                       // first column of the part within the head
 
     int64_t start, end;
@@ -156,7 +152,7 @@ __global__ __launch_bounds__(SCAN_THREADS, CT == 1 ? 2 : 1) void scan_kernel(
     // ---- state slices: S[ct][t][j] = state[chan(t, 4grp+j)][col] -------------
     // (a zero-sized resource when there is no initial state: loads return 0)
     f32x4_t S[CT][8];
-    {
+    if (!dma_wave) {
         const size_t slab = (size_t)HD * HD * (init_fp32 ? 4 : 2);
         const __amdgpu_buffer_rsrc_t rs =
             make_rsrc((const uint8_t *)init + (init ? ((size_t)n * H + h) * slab : 0),
@@ -193,11 +189,11 @@ __global__ __launch_bounds__(SCAN_THREADS, CT == 1 ? 2 : 1) void scan_kernel(
     const uint16_t *v_base = v + ((size_t)start * H + h) * HD + col0;
     uint16_t *out_base = out + ((size_t)start * H + h) * HD + col0;
 
-    // Chunk c -> ring slot c % DEPTH by DMA: unit k < REC_KB is kilobyte k of
-    // the record; the next V_KB units are the v tile of this part, one row of
-    // CW columns per VROW_LANES lanes (rows past the sequence end and chunks
-    // past the last one read as zeros).  Every wave issues exactly LW DMAs;
-    // units past UNITS go to the sink.
+    // Chunk c -> ring slot c % DEPTH by DMA (DMA wave): unit k < REC_KB is
+    // kilobyte k of the record; the next V_KB units are the v tile of this
+    // part, one row of CW columns per VROW_LANES lanes (rows past the sequence
+    // end and chunks past the last one read as zeros).  Exactly UNITS DMAs
+    // per chunk.
     auto issue = [&](int c, int slot) {
         const bool live = c < nch;
         const i32x4_t rr =
@@ -207,29 +203,13 @@ __global__ __launch_bounds__(SCAN_THREADS, CT == 1 ? 2 : 1) void scan_kernel(
         const i32x4_t rv =
             rsrc_words(v_base + (live ? (size_t)c * row_stride : 0), (uint32_t)(len * row_bytes));
         ScanSlot<CW> &sl = ring[slot];
-        // units w, w+4, w+8 are always record kilobytes: no selection needed
-        constexpr int FIXED = REC_KB / SCAN_WAVES;
 #pragma unroll
-        for (int i = 0; i < FIXED; ++i) {
-            const int unit = w + i * SCAN_WAVES;
-            dma16(rr, &sl.rec[unit * 1024], unit * 1024 + l * 16);
-        }
-        // the remaining units: record, v tile or sink, chosen with
-        // wave-uniform selects so that every wave issues one DMA per unit
+        for (int unit = 0; unit < REC_KB; ++unit) dma16(rr, &sl.rec[unit * 1024], unit * 1024 + l * 16);
 #pragma unroll
-        for (int i = FIXED; i < LW; ++i) {
-            const int unit = w + i * SCAN_WAVES;
-            const bool is_rec = unit < REC_KB;
-            const bool is_v = !is_rec && unit < UNITS;
-            const int vu = unit - REC_KB;                          // 1 KB = 1024 / (2 CW) rows
-            const int vrow0 = vu * (1024 / (2 * CW));
-            const i32x4_t rs = is_v ? rv : rr;
-            uint8_t *dst = is_rec ? &sl.rec[unit * 1024]
-                         : is_v ? (uint8_t *)&sl.v[vrow0][0] : sink;
-            const int off = is_rec ? unit * 1024 + l * 16
-                          : is_v ? (int)((vrow0 + l / VROW_LANES) * row_bytes) + (l % VROW_LANES) * 16
-                                 : 0x7ffffff0;
-            dma16(rs, dst, off);
+        for (int vu = 0; vu < V_KB; ++vu) {
+            const int vrow0 = vu * (1024 / (2 * CW));                  // 1 KB = 1024 / (2 CW) rows
+            dma16(rv, &sl.v[vrow0][0],
+                  (int)((vrow0 + l / VROW_LANES) * row_bytes) + (l % VROW_LANES) * 16);
         }
     };
 
@@ -307,40 +287,43 @@ __global__ __launch_bounds__(SCAN_THREADS, CT == 1 ? 2 : 1) void scan_kernel(
         }
     };
 
-    // Software pipeline: iteration c computes chunk c from registers loaded
-    // in iteration c-1, loads chunk c+1 from the ring and refills the slot
-    // of chunk c with chunk c+DEPTH.  VMEM issue order per wave:
-    //   P_0 .. P_{DEPTH-1} | I_DEPTH S_0 | I_{DEPTH+1} S_1 | ...
-    // (P: prologue DMAs, I_j: DMAs of chunk j, LW each; S_c: the SW out
-    // stores of iteration c).  At the top of iteration c the operations
-    // issued after chunk c+1's DMAs number
-    //   (DEPTH-2) LW + min(c, DEPTH-1) SW,
-    // so waiting until at most that many are outstanding means chunk c+1 has
-    // landed; the barrier after it also means every wave has finished its
-    // reads of chunk c's slot (s_waitcnt lgkmcnt(0) before the barrier).
-    static_assert((DEPTH - 2) * LW + (DEPTH - 1) * SW <= 63, "vmcnt holds at most 63");
+    // Software pipeline.  Iteration c: the DMA wave waits for chunk c+1 to
+    // land, the compute waves finish their reads of chunk c (issued in
+    // iteration c-1), all five meet at a barrier; then the compute waves
+    // read chunk c+1 into registers and compute chunk c while the DMA wave
+    // refills chunk c's slot with chunk c+DEPTH.  The DMA wave issues chunks
+    // in order, UNITS DMAs each, so at the top of iteration c the DMAs issued
+    // after chunk c+1's number (DEPTH-2) UNITS (and (DEPTH-1) UNITS after
+    // chunk 0's before the first iteration).
+    if (dma_wave) {
 #pragma unroll
-    for (int c = 0; c < DEPTH; ++c) issue(c, c);
-    wait_vm_barrier<(DEPTH - 1) * LW>();              // chunk 0 landed
+        for (int c = 0; c < DEPTH; ++c) issue(c, c);
+        wait_vm_barrier<(DEPTH - 1) * UNITS>();      // chunk 0 landed
+        int slot = 0;
+        for (int c = 0; c < nch; ++c) {
+            wait_vm_barrier<(DEPTH - 2) * UNITS>();  // chunk c+1 landed; slot of c free
+            issue(c + DEPTH, slot);
+            slot = slot == DEPTH - 1 ? 0 : slot + 1;
+        }
+        // drain the DMAs of the chunks past the end before the workgroup exits
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        return;
+    }
+    lds_barrier();                                   // chunk 0 landed
 
     ChunkOps<CT> opA, opB;
     load_ops(0, opA);
-    auto top_wait = [&](int c) { wait_ladder<(DEPTH - 2) * LW, SW, DEPTH - 1>(c); };
-    int slot = 0, next = 1;                           // ring slots of chunks c and c+1
+    int next = 1;                                     // ring slot of chunk c+1
     auto step = [&](int c, const ChunkOps<CT> &cur, ChunkOps<CT> &nxt) {
-        top_wait(c);
+        lds_barrier();                               // own reads of chunk c done; chunk c+1 landed
         load_ops(next, nxt);
-        issue(c + DEPTH, slot);
         compute(c, cur);
-        slot = next;
         next = next == DEPTH - 1 ? 0 : next + 1;
     };
     for (int c = 0; c < nch; c += 2) {
         step(c, opA, opB);
         if (c + 1 < nch) step(c + 1, opB, opA);
     }
-    // drain the DMAs of the chunks past the end before the workgroup exits
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     if (fin) {
         const size_t slab = (size_t)HD * HD * (fin_fp32 ? 4 : 2);
