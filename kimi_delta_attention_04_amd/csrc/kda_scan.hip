@@ -100,7 +100,7 @@ struct ChunkOps {
     u32x4_t kt[4], qt[4], wt[4];
     u32x2_t m;
     float gm[2];              // chunk decay of two state rows (see load_ops)
-    float v[CT][4];           // v[4grp + j][column] of each slice
+    u32x2_t v[CT];            // v[row l%16][4(l/16) .. +3] of each slice: an MFMA A operand
 };
 
 // Row multiplier of the decay: S[t][j] (state row chan(t, 4grp + j)) takes
@@ -230,10 +230,19 @@ __global__ __launch_bounds__(SCAN_THREADS, 2) void scan_kernel(
         op.gm[1] = __uint_as_float(g2[1]);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) op.v[ct][j] = bf16f(sl.v[4 * grp + j][wcol0 + 16 * ct + cg]);
+            op.v[ct] = *(const u32x2_t *)&sl.v[cg][wcol0 + 16 * ct + 4 * grp];
     };
 
+    // Identity as a 16x16x16 B operand (lane l: k = 4(l/16) + j, column l%16):
+    // D = A I moves a tile from the A-operand layout to the accumulator
+    // layout, exactly for bf16 data.
+    u32x2_t eye;
+    {
+        const uint32_t one = 0x3f80u;                 // bf16 1.0
+        const int d = cg - 4 * grp;
+        eye[0] = (d == 0 ? one : 0u) | (d == 1 ? one << 16 : 0u);
+        eye[1] = (d == 2 ? one : 0u) | (d == 3 ? one << 16 : 0u);
+    }
     auto compute = [&](int c, const ChunkOps<CT> &op) {
         const int64_t rem = L - (int64_t)c * CS;
         const int len = (int)(rem < CS ? rem : CS);
@@ -253,12 +262,16 @@ __global__ __launch_bounds__(SCAN_THREADS, 2) void scan_kernel(
                 Sb[kb][2] = pack2(S[ct][2 * kb + 1][0], S[ct][2 * kb + 1][1]);
                 Sb[kb][3] = pack2(S[ct][2 * kb + 1][2], S[ct][2 * kb + 1][3]);
             }
-            f32x4_t P = zero, Qs = zero;
+            // P in two independent halves (a shorter dependent MFMA chain on
+            // the serial path); v into the accumulator layout
+            f32x4_t P0 = zero, P1 = zero, Qs = zero;
+            P0 = mfma_k32(op.kt[0], Sb[0], P0);
+            P1 = mfma_k32(op.kt[2], Sb[2], P1);
+            P0 = mfma_k32(op.kt[1], Sb[1], P0);
+            P1 = mfma_k32(op.kt[3], Sb[3], P1);
+            const f32x4_t vv = mfma_k16(op.v[ct], eye, zero);
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                P = mfma_k32(op.kt[kb], Sb[kb], P);
-                Qs = mfma_k32(op.qt[kb], Sb[kb], Qs);
-            }
+            for (int kb = 0; kb < 4; ++kb) Qs = mfma_k32(op.qt[kb], Sb[kb], Qs);
             // decayed old state: the accumulator the update MFMAs add W^T X to
 #define KDA_DECAY(T_)                                              \
             S[ct][T_][0] *= decay_of<T_, 0>(op.gm);                \
@@ -269,8 +282,8 @@ __global__ __launch_bounds__(SCAN_THREADS, 2) void scan_kernel(
             KDA_DECAY(4) KDA_DECAY(5) KDA_DECAY(6) KDA_DECAY(7)
 #undef KDA_DECAY
             u32x2_t Xb;
-            Xb[0] = pack2(op.v[ct][0] - P[0], op.v[ct][1] - P[1]);
-            Xb[1] = pack2(op.v[ct][2] - P[2], op.v[ct][3] - P[3]);
+            Xb[0] = pack2(vv[0] - (P0[0] + P1[0]), vv[1] - (P0[1] + P1[1]));
+            Xb[1] = pack2(vv[2] - (P0[2] + P1[2]), vv[3] - (P0[3] + P1[3]));
 #pragma unroll
             for (int tp = 0; tp < 4; ++tp) {
                 u32x2_t lo = {op.wt[tp][0], op.wt[tp][1]}, hi = {op.wt[tp][2], op.wt[tp][3]};
@@ -280,10 +293,13 @@ __global__ __launch_bounds__(SCAN_THREADS, 2) void scan_kernel(
             // M X in an accumulator of its own (no accumulator chaining
             // between MFMA opcodes of different shapes), added on the VALU
             const f32x4_t MX = mfma_k16(op.m, Xb, zero);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                __builtin_amdgcn_raw_buffer_store_b16(tobf16(scale * (Qs[j] + MX[j])), ro,
-                                                      (int)((4 * grp + j) * row_bytes) + lc * 2, 0, 0);
+            // O^T through the identity: lane (grp, cg) then holds token cg,
+            // columns 4grp .. 4grp+3 of the slice, one 8-byte store
+            const u32x2_t oa = {pack2(scale * (Qs[0] + MX[0]), scale * (Qs[1] + MX[1])),
+                                pack2(scale * (Qs[2] + MX[2]), scale * (Qs[3] + MX[3]))};
+            const f32x4_t ot = mfma_k16(oa, eye, zero);
+            const u32x2_t os = {pack2(ot[0], ot[1]), pack2(ot[2], ot[3])};
+            __builtin_amdgcn_raw_buffer_store_b64(os, ro, (int)(cg * row_bytes) + (lc - cg + 4 * grp) * 2, 0, 0);
         }
     };
 
