@@ -14,6 +14,11 @@ Roofline accounting (algorithmic bytes, i.e. what the operation must move):
   records between the two kernels are design overhead, not algorithmic.
 Per-kernel durations come from HIP events the library records around each
 kernel (kda_set_stage_events) on the stream the kernels run on.
+
+`--decode-batch N` instead measures the decode step (kda_decode, one kernel
+on the current stream): N one-token sequences x H heads with an fp32 state
+updated in place, algorithmic bytes per (sequence, head) = the state read and
+written (2 x 64 KiB) + q, k, g, v, beta, out (1282 B).
 """
 from __future__ import annotations
 
@@ -86,6 +91,60 @@ def cpu_baseline(inp, w, heads: int):
                       f"fp64 C/OpenMP token recurrence, {dt:.2f} s wall"}
 
 
+def bench_decode(args, torch, kda, kda_inputs):
+    N, H = args.decode_batch, args.decode_heads
+    log(f"[bench] decode: generating N={N} H={H} ...")
+    inp = kda_inputs.random_small(2, B=N, T=1, H=H)
+    gen = torch.Generator().manual_seed(2)
+    state0 = (torch.randn(N, H, 128, 128, generator=gen) * 0.05).float()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    flat = lambda t: t.reshape(N, H, -1).contiguous().to(dev)
+    q, k, v, g = (flat(inp[x]) for x in ("q", "k", "v", "g"))
+    beta = inp["beta"].reshape(N, H).contiguous().to(dev)
+    A_log, dtb = inp["A_log"].to(dev), inp["dt_bias"].to(dev)
+    state = state0.to(dev)
+    out = torch.empty(N, H, 128, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        kda.decode(q, k, v, g, beta, inp["scale"], out, A_log, dtb, inp["lower_bound"], state)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    units = N * H
+    bytes_ = units * (2 * 128 * 128 * 4 + 1282)
+    achieved = bytes_ / (ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "kda_decode",
+                "bytes_per_launch": bytes_, "avg_launch_ms": ms}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        inp["initial_state"] = state0
+        t0 = time.perf_counter()
+        oracle.cref_forward(inp, want_final=True)
+        dt = time.perf_counter() - t0
+        cpu = {"value": N / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+               "sample": f"the whole step: {N} sequences x {H} heads, fp64 C/OpenMP, {dt:.3f} s wall"}
+    rec = {"metric": f"KDA decode step tokens/s (one token per sequence) @N={N},H={H},D=128, fp32 state",
+           "value": N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "fp32", "data": "synthetic (seeded)",
+           "config": {"workload": f"decode_N{N}_H{H}", "N": N, "H": H, "K": 128, "V": 128,
+                      "state": "fp32, in place"},
+           "roofline": roofline, "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +153,9 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the T=8192 H=96 fixed one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=96, help="heads in the oracle's timed sample")
+    ap.add_argument("--decode-batch", type=int, default=0, metavar="N",
+                    help="measure the decode step on N one-token sequences instead")
+    ap.add_argument("--decode-heads", type=int, default=96)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times): the "
                          "reference kernel for scaling the HBM byte counters")
@@ -121,6 +183,9 @@ def main():
     import kimi_delta_attention_04_amd as kda
 
     kda.load()
+    if args.decode_batch:
+        bench_decode(args, torch, kda, kda_inputs)
+        return
     name = args.workload or kda_inputs.HEADLINE
     w = kda_inputs.WORKLOADS[name]
     log(f"[bench] generating {name} ...")

@@ -105,6 +105,38 @@ kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g,
                      int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
                      void *stream);
 
+/*
+ * kda_decode — one decode step: a single new token per sequence applied to
+ * the recurrent state in place (the step after a prefill; it consumes the
+ * final_state kda_fwd wrote, same layout).  "FlashKDA" product page, Main
+ * Features (recurrent state between prefill and decode); the update is the
+ * token recurrence above for one token:
+ *
+ *   S = (I - beta k k^T) Diag(exp(a)) S + beta k v^T,   o = scale * S^T q
+ *
+ * Layout:
+ *   q, k, g     bf16 [N, H, K]       the new token of each sequence
+ *   v           bf16 [N, H, V]
+ *   beta        bf16 [N, H]          logits; the sigmoid is applied inside
+ *   out         bf16 [N, H, V]       caller-allocated, every row written
+ *   A_log       fp32 [H];  dt_bias fp32 [H*K] or NULL (= zeros)
+ *   scale       host fp32, finite
+ *   lower_bound host fp32, finite and <= 0 (no chunk factorisation here, so
+ *               no lower limit beyond finiteness)
+ *   state       [N, H, K, V] in state_dtype (bf16 or fp32), read and
+ *               overwritten with the updated state (bf16: round to nearest
+ *               even); the arithmetic is fp32 either way
+ *   N, H, K, V  sizes; N, H >= 1; K and V must both be 128
+ *
+ * No workspace.  Returns KDA_OK, KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED
+ * before any HIP call, or KDA_ERR_LAUNCH.
+ */
+kda_status_t kda_decode(const void *q, const void *k, const void *v, const void *g,
+                        const void *beta, float scale,
+                        const float *A_log, const float *dt_bias, float lower_bound,
+                        void *state, kda_dtype_t state_dtype, void *out,
+                        int32_t N, int32_t H, int32_t K, int32_t V, void *stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *kda_status_string(kda_status_t status);
 

@@ -9,14 +9,18 @@ binding raises; there is no fallback implementation.
         initial_state=None, final_state=None, cu_seqlens=None)
 
 mirrors the flash_kda.fwd argument list described in "Moonshot AI Rilis
-FlashKDA" (API paragraphs).
+FlashKDA" (API paragraphs);
+
+    decode(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, state)
+
+applies one new token per sequence to the recurrent state in place.
 """
 from __future__ import annotations
 
 import ctypes
 import os
 
-__all__ = ["fwd", "debug_intra", "set_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
+__all__ = ["fwd", "decode", "debug_intra", "set_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
            "status_string", "KDAError", "library_path", "load", "HEAD_DIM"]
 
 HEAD_DIM = 128
@@ -63,6 +67,8 @@ def load():
     lib.kda_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.kda_set_stage_events.restype = ctypes.c_int
     lib.kda_set_stage_events.argtypes = [P, P, P]
+    lib.kda_decode.restype = ctypes.c_int
+    lib.kda_decode.argtypes = [P, P, P, P, P, f32, P, P, f32, P, ctypes.c_int, P, i32, i32, i32, i32, P]
     lib.kda_debug_intra.restype = ctypes.c_int
     lib.kda_debug_intra.argtypes = [P, P, P, P, P, P, f32, P, i32, i32, i32, i32, i32, P, P]
     _lib = lib
@@ -175,6 +181,40 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
                      int(B), int(T), int(H), int(K), int(V), _stream(q.device))
     if rc != 0:
         raise KDAError(rc, "kda_fwd")
+    return out
+
+
+def decode(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, state):
+    """One decode step: the new token of each sequence applied to `state`
+    (bf16 or fp32 [N, H, K, V]) in place; the output into `out`.
+
+    q, k, g: bf16 [N, H, K]; v, out: bf16 [N, H, V]; beta: bf16 [N, H]
+    logits; A_log: fp32 [H]; dt_bias: fp32 [H*K] or None.  Enqueued on the
+    current stream; returns out.
+    """
+    import torch
+    lib = load()
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, K]")
+    N, H, K = q.shape
+    V = v.shape[-1]
+    bf = torch.bfloat16
+    _check(q, "q", bf)
+    _check(k, "k", bf, q.shape)
+    _check(g, "g", bf, q.shape)
+    _check(v, "v", bf, (N, H, V))
+    _check(out, "out", bf, (N, H, V))
+    _check(beta, "beta", bf, (N, H))
+    _check(A_log, "A_log", torch.float32, (H,))
+    if dt_bias is not None:
+        _check(dt_bias, "dt_bias", torch.float32, (H * K,))
+    st_dt = _state_dtype(state)
+    _check(state, "state", state.dtype, (N, H, K, V))
+    rc = lib.kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+                        _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(state), st_dt,
+                        _ptr(out), int(N), int(H), int(K), int(V), _stream(q.device))
+    if rc != 0:
+        raise KDAError(rc, "kda_decode")
     return out
 
 

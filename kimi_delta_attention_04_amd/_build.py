@@ -9,13 +9,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_intra.hip", "kda_scan.hip"]
+SOURCES = ["kda_api.hip", "kda_intra.hip", "kda_scan.hip", "kda_decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: no packed fp32 VALU instructions in the device code.
-# (The VGPR form of MFMA, -mllvm -amdgpu-mfma-vgpr-form, would save the AGPR
-# copies around the state decay but produced wrong outputs from the scan
-# with this compiler, so the default AGPR form is kept.)
+# (-mllvm -amdgpu-mfma-vgpr-form produced wrong outputs from the scan with
+# this compiler; the kernels get the VGPR form of their MFMAs from launch
+# bounds that keep the register budget at 256 instead.)
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]

@@ -178,6 +178,30 @@ kda_status_t kda_debug_intra(const void *q, const void *k, const void *g,
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+kda_status_t kda_decode(const void *q, const void *k, const void *v, const void *g,
+                        const void *beta, float scale,
+                        const float *A_log, const float *dt_bias, float lower_bound,
+                        void *state, kda_dtype_t state_dtype, void *out,
+                        int32_t N, int32_t H, int32_t K, int32_t V, void *stream)
+{
+    if (!q || !k || !v || !g || !beta || !A_log || !state || !out) return KDA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) ||
+        !aligned(out, 16) || !aligned(state, 16) || !aligned(beta, 2) || !aligned(A_log, 4) ||
+        !aligned(dt_bias, 4))
+        return KDA_ERR_INVALID_ARG;
+    if (state_dtype != KDA_DTYPE_BF16 && state_dtype != KDA_DTYPE_FP32) return KDA_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !isfinite(lower_bound) || lower_bound > 0.f) return KDA_ERR_INVALID_ARG;
+    if (N < 1 || H < 1) return KDA_ERR_INVALID_ARG;
+    if (K != kda::HD || V != kda::HD) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)N * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    hipError_t e = kda::launch_decode((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v,
+                                      (const uint16_t *)g, (const uint16_t *)beta, scale, A_log,
+                                      dt_bias, lower_bound, N, H, state,
+                                      state_dtype == KDA_DTYPE_FP32, (uint16_t *)out,
+                                      (hipStream_t)stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 kda_status_t kda_set_stage_events(void *before_intra, void *before_scan, void *after_scan) {
     t_stage_events[0] = (hipEvent_t)before_intra;
     t_stage_events[1] = (hipEvent_t)before_scan;

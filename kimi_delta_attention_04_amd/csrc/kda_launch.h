@@ -18,4 +18,10 @@ hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, 
                        int H, float scale, const void *init, int init_fp32, void *fin,
                        int fin_fp32, uint16_t *out, hipStream_t stream);
 
+// One-token decode step on N x H states in place (fp32 or bf16).
+hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         const uint16_t *g, const uint16_t *beta, float scale,
+                         const float *A_log, const float *dt_bias, float lower_bound, int N,
+                         int H, void *state, int state_fp32, uint16_t *out, hipStream_t stream);
+
 }  // namespace kda

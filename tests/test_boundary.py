@@ -102,6 +102,27 @@ def test_fwd_rejects_before_any_hip_call(lib, over, code):
     assert call_fwd(lib, **over) == code
 
 
+def call_decode(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=0.088, A_log=FAKE, dt_bias=None,
+             lb=-5.0, state=FAKE, st_dt=1, out=FAKE, N=4, H=2, K=128, V=128)
+    a.update(over)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.kda_decode(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]), a["scale"],
+                          P(a["A_log"]), P(a["dt_bias"]), a["lb"], P(a["state"]), a["st_dt"],
+                          P(a["out"]), a["N"], a["H"], a["K"], a["V"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), INVALID), (dict(state=None), INVALID), (dict(out=None), INVALID),
+    (dict(A_log=None), INVALID), (dict(beta=FAKE + 1), INVALID), (dict(state=FAKE + 8), INVALID),
+    (dict(st_dt=2), INVALID), (dict(scale=float("nan")), INVALID), (dict(lb=0.5), INVALID),
+    (dict(lb=float("-inf")), INVALID), (dict(N=0), INVALID), (dict(H=0), INVALID),
+    (dict(K=64), UNSUPPORTED), (dict(V=256), UNSUPPORTED), (dict(N=2 ** 20, H=2 ** 12), UNSUPPORTED),
+])
+def test_decode_rejects_before_any_hip_call(lib, over, code):
+    assert call_decode(lib, **over) == code
+
+
 def test_debug_intra_validates(lib):
     P = ctypes.c_void_p
     f = lambda **o: lib.kda_debug_intra(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None,
