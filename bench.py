@@ -15,6 +15,10 @@ Roofline accounting (algorithmic bytes, i.e. what the operation must move):
 Per-kernel durations come from HIP events the library records around each
 kernel (kda_set_stage_events) on the stream the kernels run on.
 
+`--scalar-gate` measures the Gated DeltaNet form (kda_fwd_scalar_gate) on
+the same workload with g [B, T, H] and dt_bias [H]: g then moves 2 B per
+(token, head) instead of 256.
+
 `--decode-batch N` instead measures the decode step (kda_decode, one kernel
 on the current stream): N one-token sequences x H heads with an fp32 state
 updated in place, algorithmic bytes per (sequence, head) = the state read and
@@ -43,12 +47,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic(w, has_init=True, has_final=True):
+def algorithmic(w, has_init=True, has_final=True, scalar_gate=False):
     th = w.tokens * w.H
     n_units = w.num_seqs * w.H
     state_in = n_units * w.K * w.V * 2 if (has_init and w.initial_state) else 0
     state_out = n_units * w.K * w.V * 4 if has_final else 0
-    intra = th * (3 * w.K * 2 + 2)
+    intra = th * ((2 * w.K * 2 + 2 + 2) if scalar_gate else (3 * w.K * 2 + 2))
     scan = th * (2 * w.V * 2) + state_in + state_out
     # MACs per token-head of the chunkwise algorithm at chunk C: three state
     # products, the two in-chunk Gram products at triangular useful size, the
@@ -153,6 +157,8 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the T=8192 H=96 fixed one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=96, help="heads in the oracle's timed sample")
+    ap.add_argument("--scalar-gate", action="store_true",
+                    help="measure the Gated DeltaNet form (one gate value per token and head)")
     ap.add_argument("--decode-batch", type=int, default=0, metavar="N",
                     help="measure the decode step on N one-token sequences instead")
     ap.add_argument("--decode-heads", type=int, default=96)
@@ -196,10 +202,18 @@ def main():
     out = torch.empty(w.B, w.T, w.H, w.V, dtype=torch.bfloat16, device=dev)
     fin = torch.empty(w.num_seqs, w.H, w.K, w.V, dtype=torch.float32, device=dev)
 
+    if args.scalar_gate:
+        # one gate value per (token, head): channel 0 of the workload's gate
+        d["g"] = d["g"][..., 0].contiguous()
+        d["dt_bias"] = d["dt_bias"].view(w.H, w.K)[:, 0].contiguous()
+        fwd = kda.fwd_scalar_gate
+    else:
+        fwd = kda.fwd
+
     def step():
-        kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], out, d["A_log"],
-                d["dt_bias"], d["lower_bound"], initial_state=d["initial_state"],
-                final_state=fin, cu_seqlens=d["cu_seqlens"])
+        fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], out, d["A_log"],
+            d["dt_bias"], d["lower_bound"], initial_state=d["initial_state"],
+            final_state=fin, cu_seqlens=d["cu_seqlens"])
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -233,7 +247,7 @@ def main():
     intra_avg = statistics.mean(intra_ms)
     scan_avg = statistics.mean(scan_ms)
 
-    alg = algorithmic(w)
+    alg = algorithmic(w, scalar_gate=args.scalar_gate)
     tok_s = w.tokens / (ms * 1e-3)
     kernels = {
         "kda_intra": {"ms": intra_avg, "bytes": alg["intra_bytes"]},
@@ -242,7 +256,7 @@ def main():
     dom_name = max(kernels, key=lambda k: kernels[k]["ms"])
     dom = kernels[dom_name]
     achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
-    tr = stored_traffic(name, dom_name)
+    tr = None if args.scalar_gate else stored_traffic(name, dom_name)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
                 "traffic": tr["total_bytes"] if tr else None,
@@ -255,16 +269,21 @@ def main():
             "mfma_achieved_TFLOPs": path_tflops, "mfma_frac": path_tflops / BF16_PEAK_TFLOPS,
             "stage_ms": {k: v["ms"] for k, v in kernels.items()},
             "stage_traffic_bytes": {k: (t["total_bytes"] if t else None) for k, t in
-                                    ((k, stored_traffic(name, k)) for k in kernels)},
+                                    ((k, None if args.scalar_gate else stored_traffic(name, k))
+                                     for k in kernels)},
             "stage_ms_min": {"kda_intra": min(intra_ms), "kda_scan": min(scan_ms)}}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.scalar_gate:
         log(f"[bench] oracle CPU baseline on {args.cpu_heads} heads")
         cpu = cpu_baseline(inp, w, args.cpu_heads)
 
     cfg = w.describe()
-    rec = {"metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1,
+    metric = METRIC
+    if args.scalar_gate:
+        metric = "KDA fwd, scalar (Gated DeltaNet) gate, tokens/s @T=8192,H=96,D=128"
+        cfg = dict(cfg, gate="scalar per (token, head)")
+    rec = {"metric": metric, "value": tok_s, "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16", "data": "synthetic (seeded; shapes of the pages' workloads)",

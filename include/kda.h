@@ -106,6 +106,33 @@ kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g,
                      void *stream);
 
 /*
+ * kda_fwd_scalar_gate — the Gated DeltaNet special case of the same forward:
+ * one gate value per (token, head), shared by all K channels.  KDA is
+ * described as Gated DeltaNet refined with channel-wise gating ("Moonshot
+ * AI Open-Sources FlashKDA", section "Why KDA?"); this entry point is the
+ * coarser gate, read as the same gate formula with per-head inputs:
+ *
+ *   a_t = max(-exp(A_log[h]) * softplus(g_t + dt_bias[h]), lower_bound)
+ *
+ * for every channel, which equals kda_fwd on g and dt_bias broadcast over
+ * the channels (and the results are bit-identical to that call).
+ *
+ * Layout and everything else as kda_fwd, except:
+ *   g           bf16 [B, T, H]       one gate pre-activation per token and head
+ *                                    (2-byte aligned)
+ *   dt_bias     fp32 [H] or NULL (= zeros)
+ */
+kda_status_t kda_fwd_scalar_gate(const void *q, const void *k, const void *v, const void *g,
+                                 const void *beta, float scale,
+                                 const float *A_log, const float *dt_bias, float lower_bound,
+                                 const int32_t *cu_seqlens, int32_t num_seqs,
+                                 const void *initial_state, kda_dtype_t initial_state_dtype,
+                                 void *final_state, kda_dtype_t final_state_dtype,
+                                 void *out,
+                                 int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                 void *stream);
+
+/*
  * kda_decode — one decode step: a single new token per sequence applied to
  * the recurrent state in place (the step after a prefill; it consumes the
  * final_state kda_fwd wrote, same layout).  "FlashKDA" product page, Main

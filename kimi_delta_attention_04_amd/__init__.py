@@ -11,6 +11,8 @@ binding raises; there is no fallback implementation.
 mirrors the flash_kda.fwd argument list described in "Moonshot AI Rilis
 FlashKDA" (API paragraphs);
 
+    fwd_scalar_gate(...)   the same with one gate value per token and head
+                           (the Gated DeltaNet case): g [B, T, H], dt_bias [H]
     decode(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, state)
 
 applies one new token per sequence to the recurrent state in place.
@@ -20,7 +22,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "decode", "debug_intra", "set_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
+__all__ = ["fwd", "fwd_scalar_gate", "decode", "debug_intra", "set_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
            "status_string", "KDAError", "library_path", "load", "HEAD_DIM"]
 
 HEAD_DIM = 128
@@ -67,6 +69,8 @@ def load():
     lib.kda_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.kda_set_stage_events.restype = ctypes.c_int
     lib.kda_set_stage_events.argtypes = [P, P, P]
+    lib.kda_fwd_scalar_gate.restype = ctypes.c_int
+    lib.kda_fwd_scalar_gate.argtypes = lib.kda_fwd.argtypes
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode.argtypes = [P, P, P, P, P, f32, P, P, f32, P, ctypes.c_int, P, i32, i32, i32, i32, P]
     lib.kda_debug_intra.restype = ctypes.c_int
@@ -147,6 +151,21 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
     initial_state / final_state: bf16 or fp32 [N, H, K, V] or None;
     cu_seqlens: int32 [N+1] (B == 1) or None.  Enqueued on the current stream.
     """
+    return _fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                initial_state, final_state, cu_seqlens, scalar_gate=False)
+
+
+def fwd_scalar_gate(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                    initial_state=None, final_state=None, cu_seqlens=None):
+    """The Gated DeltaNet case: as fwd, but g is bf16 [B, T, H] (one gate
+    value per token and head, shared by all channels) and dt_bias fp32 [H]
+    or None."""
+    return _fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                initial_state, final_state, cu_seqlens, scalar_gate=True)
+
+
+def _fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+         initial_state, final_state, cu_seqlens, scalar_gate):
     import torch
     lib = load()
     if q.dim() != 4:
@@ -156,13 +175,13 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
     bf = torch.bfloat16
     _check(q, "q", bf)
     _check(k, "k", bf, q.shape)
-    _check(g, "g", bf, q.shape)
+    _check(g, "g", bf, (B, T, H) if scalar_gate else q.shape)
     _check(v, "v", bf, (B, T, H, V))
     _check(out, "out", bf, (B, T, H, V))
     _check(beta, "beta", bf, (B, T, H))
     _check(A_log, "A_log", torch.float32, (H,))
     if dt_bias is not None:
-        _check(dt_bias, "dt_bias", torch.float32, (H * K,))
+        _check(dt_bias, "dt_bias", torch.float32, (H,) if scalar_gate else (H * K,))
     if cu_seqlens is not None:
         _check(cu_seqlens, "cu_seqlens", torch.int32)
         N = cu_seqlens.numel() - 1
@@ -175,12 +194,13 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
     if final_state is not None:
         fin_dt = _state_dtype(final_state)
         _check(final_state, "final_state", final_state.dtype, (N, H, K, V))
-    rc = lib.kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
-                     _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(cu_seqlens), int(N),
-                     _ptr(initial_state), init_dt, _ptr(final_state), fin_dt, _ptr(out),
-                     int(B), int(T), int(H), int(K), int(V), _stream(q.device))
+    entry = lib.kda_fwd_scalar_gate if scalar_gate else lib.kda_fwd
+    rc = entry(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+               _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(cu_seqlens), int(N),
+               _ptr(initial_state), init_dt, _ptr(final_state), fin_dt, _ptr(out),
+               int(B), int(T), int(H), int(K), int(V), _stream(q.device))
     if rc != 0:
-        raise KDAError(rc, "kda_fwd")
+        raise KDAError(rc, "kda_fwd_scalar_gate" if scalar_gate else "kda_fwd")
     return out
 
 

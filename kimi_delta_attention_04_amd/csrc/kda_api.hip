@@ -102,21 +102,27 @@ size_t kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs) {
     return (size_t)num_slots(B, T, num_seqs) * (size_t)H * kda::REC_BYTES;
 }
 
-kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g,
-                     const void *beta, float scale,
-                     const float *A_log, const float *dt_bias, float lower_bound,
-                     const int32_t *cu_seqlens, int32_t num_seqs,
-                     const void *initial_state, kda_dtype_t initial_state_dtype,
-                     void *final_state, kda_dtype_t final_state_dtype,
-                     void *out,
-                     int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
-                     void *stream)
+}  // extern "C"
+
+namespace {
+
+// kda_fwd and kda_fwd_scalar_gate: scalar_gate selects the layout of g
+// ([B, T, H, K] or [B, T, H]) and dt_bias ([H*K] or [H]).
+kda_status_t fwd_impl(const void *q, const void *k, const void *v, const void *g,
+                      const void *beta, float scale,
+                      const float *A_log, const float *dt_bias, float lower_bound,
+                      const int32_t *cu_seqlens, int32_t num_seqs,
+                      const void *initial_state, kda_dtype_t initial_state_dtype,
+                      void *final_state, kda_dtype_t final_state_dtype,
+                      void *out,
+                      int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                      void *stream, bool scalar_gate)
 {
     // With no tokens the token buffers are never touched and may be NULL.
     const bool no_tokens = (int64_t)B * T == 0;
     if (!A_log) return KDA_ERR_INVALID_ARG;
     if (!no_tokens && (!q || !k || !v || !g || !beta || !out)) return KDA_ERR_INVALID_ARG;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) ||
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, scalar_gate ? 2 : 16) ||
         !aligned(out, 16) || !aligned(beta, 2) || !aligned(A_log, 4) ||
         !aligned(dt_bias, 4) || !aligned(cu_seqlens, 4) || !aligned(initial_state, 16) ||
         !aligned(final_state, 16))
@@ -143,7 +149,7 @@ kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g,
     if (e == hipSuccess)
         e = kda::launch_intra((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,
                               (const uint16_t *)beta, A_log, dt_bias, lower_bound,
-                              cu_seqlens, num_seqs, T, H, slots, (uint8_t *)ws, s);
+                              cu_seqlens, num_seqs, T, H, slots, (uint8_t *)ws, s, scalar_gate);
     if (e == hipSuccess) e = mark(1, s);
     if (e == hipSuccess)
         e = kda::launch_scan((const uint16_t *)v, (const uint8_t *)ws, cu_seqlens, num_seqs, T, H,
@@ -154,6 +160,40 @@ kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g,
     hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess || ef != hipSuccess) return KDA_ERR_LAUNCH;
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g,
+                     const void *beta, float scale,
+                     const float *A_log, const float *dt_bias, float lower_bound,
+                     const int32_t *cu_seqlens, int32_t num_seqs,
+                     const void *initial_state, kda_dtype_t initial_state_dtype,
+                     void *final_state, kda_dtype_t final_state_dtype,
+                     void *out,
+                     int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                     void *stream)
+{
+    return fwd_impl(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens, num_seqs,
+                    initial_state, initial_state_dtype, final_state, final_state_dtype, out,
+                    B, T, H, K, V, stream, false);
+}
+
+kda_status_t kda_fwd_scalar_gate(const void *q, const void *k, const void *v, const void *g,
+                                 const void *beta, float scale,
+                                 const float *A_log, const float *dt_bias, float lower_bound,
+                                 const int32_t *cu_seqlens, int32_t num_seqs,
+                                 const void *initial_state, kda_dtype_t initial_state_dtype,
+                                 void *final_state, kda_dtype_t final_state_dtype,
+                                 void *out,
+                                 int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                 void *stream)
+{
+    return fwd_impl(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens, num_seqs,
+                    initial_state, initial_state_dtype, final_state, final_state_dtype, out,
+                    B, T, H, K, V, stream, true);
 }
 
 kda_status_t kda_debug_intra(const void *q, const void *k, const void *g,

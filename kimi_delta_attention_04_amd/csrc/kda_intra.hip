@@ -9,7 +9,9 @@ namespace kda {
 
 namespace {
 
-// One wave per (chunk slot, head), a workgroup of its own.
+// One wave per (chunk slot, head), a workgroup of its own.  SG: scalar
+// (per-head) gate, g [B*T, H] and dt_bias [H].
+template <bool SG>
 __global__ __launch_bounds__(64, 2) void intra_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
@@ -36,15 +38,15 @@ __global__ __launch_bounds__(64, 2) void intra_kernel(
 
     const float A = expf(A_log[h]);
     __shared__ float dtb_lds[HD];
-    stage_dtb(dtb_lds, dt_bias, h);
+    stage_dtb<SG>(dtb_lds, dt_bias, h);
     wave_lds_sync();
 
     IntraIn in;
-    intra_load(in, q, k, g, beta, t0, len, H, h);
+    intra_load<SG>(in, q, k, g, beta, t0, len, H, h);
     if (len == CS)
-        intra_compute<true>(lds, in, A, dtb_lds, lb2, len, rec);
+        intra_compute<true, SG>(lds, in, A, dtb_lds, lb2, len, rec);
     else
-        intra_compute<false>(lds, in, A, dtb_lds, lb2, len, rec);
+        intra_compute<false, SG>(lds, in, A, dtb_lds, lb2, len, rec);
 }
 
 }  // namespace
@@ -52,12 +54,16 @@ __global__ __launch_bounds__(64, 2) void intra_kernel(
 hipError_t launch_intra(const uint16_t *q, const uint16_t *k, const uint16_t *g,
                         const uint16_t *beta, const float *A_log, const float *dt_bias,
                         float lower_bound, const int32_t *cu, int N, int T, int H,
-                        int64_t num_slots, uint8_t *ws, hipStream_t stream)
+                        int64_t num_slots, uint8_t *ws, hipStream_t stream, bool scalar_gate)
 {
     if (num_slots <= 0) return hipSuccess;
     dim3 grid((unsigned)num_slots, (unsigned)H);
-    hipLaunchKernelGGL(intra_kernel, grid, dim3(64), 0, stream,
-                       q, k, g, beta, A_log, dt_bias, lower_bound * LOG2E, cu, N, T, H, ws);
+    if (scalar_gate)
+        hipLaunchKernelGGL(intra_kernel<true>, grid, dim3(64), 0, stream,
+                           q, k, g, beta, A_log, dt_bias, lower_bound * LOG2E, cu, N, T, H, ws);
+    else
+        hipLaunchKernelGGL(intra_kernel<false>, grid, dim3(64), 0, stream,
+                           q, k, g, beta, A_log, dt_bias, lower_bound * LOG2E, cu, N, T, H, ws);
     return hipGetLastError();
 }
 

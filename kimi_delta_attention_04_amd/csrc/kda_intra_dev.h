@@ -42,8 +42,10 @@ struct WaveLds {
 struct IntraIn {
     u32x4_t g[4], q[4], k[4];       // [kb]: 8 bf16 channels of this lane's token
     uint32_t beta;                  // logit of this lane's token
+    uint32_t gs;                    // scalar gate of this lane's token (SG form)
 };
 
+template <bool SG>
 __device__ __forceinline__ void intra_load(IntraIn &in, const uint16_t *__restrict__ q,
                                            const uint16_t *__restrict__ k,
                                            const uint16_t *__restrict__ g,
@@ -60,20 +62,32 @@ __device__ __forceinline__ void intra_load(IntraIn &in, const uint16_t *__restri
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         const int off = (int)((tok * row_elems + 32 * kb + 8 * cgp) * 2);
-        in.g[kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sg, off, 0, 0));
+        if (!SG)
+            in.g[kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sg, off, 0, 0));
         in.q[kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sq, off, 0, 0));
         in.k[kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sk, off, 0, 0));
     }
-    const __amdgpu_buffer_rsrc_t sb =
-        make_rsrc(beta + (size_t)t0 * H + hh, len > 0 ? (uint32_t)(((size_t)(len - 1) * H + 1) * 2) : 0u);
+    // beta (and the scalar gate of the SG form) are [token, head]
+    const uint32_t tb = len > 0 ? (uint32_t)(((size_t)(len - 1) * H + 1) * 2) : 0u;
+    const __amdgpu_buffer_rsrc_t sb = make_rsrc(beta + (size_t)t0 * H + hh, tb);
     in.beta = __builtin_amdgcn_raw_buffer_load_b16(sb, tok * H * 2, 0, 0);
+    if (SG) {
+        const __amdgpu_buffer_rsrc_t ss = make_rsrc(g + (size_t)t0 * H + hh, tb);
+        in.gs = __builtin_amdgcn_raw_buffer_load_b16(ss, tok * H * 2, 0, 0);
+    }
 }
 
 // dt_bias of one head in log2 units into LDS (128 floats; zeros when absent),
-// by the lanes of the calling wave.
+// by the lanes of the calling wave.  SG form: dt_bias is [H], one value per
+// head, staged into dtb_lds[0].
+template <bool SG = false>
 __device__ __forceinline__ void stage_dtb(float *__restrict__ dtb_lds, const float *__restrict__ dt_bias,
                                           int hh) {
     const int l = threadIdx.x & 63;
+    if (SG) {
+        if (l == 0) dtb_lds[0] = dt_bias ? dt_bias[hh] * LOG2E : 0.f;
+        return;
+    }
 #pragma unroll
     for (int r = 0; r < 2; ++r)
         dtb_lds[64 * r + l] = dt_bias ? dt_bias[(size_t)hh * HD + 64 * r + l] * LOG2E : 0.f;
@@ -123,9 +137,14 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
 
 // One (chunk, head) by one wave, inputs in the token-per-lane layout.
 // FULL: all 16 rows are tokens of the sequence (no masking of the
-// cumulative decay).  dtb_lds: the head's dt_bias in log2 units (LDS).
-// `rec` is the record in global memory.
-template <bool FULL>
+// cumulative decay).  SG: the Gated DeltaNet form, one gate value per
+// (token, head) for all channels (in.gs, dt_bias in dtb_lds[0]); the gate
+// and its cumulative sum are then computed once per token with the same
+// operations as in the per-channel form, so the results equal the
+// per-channel form's on inputs broadcast over channels, bit for bit.
+// dtb_lds: the head's dt_bias in log2 units (LDS).  `rec` is the record in
+// global memory.
+template <bool FULL, bool SG = false>
 __device__ __forceinline__ void intra_compute(WaveLds &L, const IntraIn &in, float A,
                                               const float *__restrict__ dtb_lds, float lb2, int len,
                                               uint8_t *__restrict__ rec) {
@@ -160,10 +179,24 @@ __device__ __forceinline__ void intra_compute(WaveLds &L, const IntraIn &in, flo
     // B-operand layout of the W products (kbh/kbl[t], state row tile t).
     f32x4_t Akk = zero, AkkT = zero, AqkT = zero;
     u32x2_t kbh[8], kbl[8];
+    float Gs = 0.f;                                  // SG form: the one cumulative gate
+    if (SG && A > 0.f) {
+        const float x2 = bf16f((uint16_t)in.gs) * LOG2E + dtb_lds[0];
+        const float u = fast_log2(1.f + fast_exp2(x2));
+        const float la = fmaxf(-A * u, lb2);
+        Gs = live ? la : 0.f;
+        Gs += row_shr<1>(Gs);
+        Gs += row_shr<2>(Gs);
+        Gs += row_shr<4>(Gs);
+        Gs += row_shr<8>(Gs);
+    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         float G[8];
-        if (A > 0.f) {
+        if (SG) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) G[i] = Gs;
+        } else if (A > 0.f) {
             float dtb2[8];
             *(f32x4_t *)&dtb2[0] = *(const f32x4_t *)&dtb_lds[32 * kb + 8 * grp];
             *(f32x4_t *)&dtb2[4] = *(const f32x4_t *)&dtb_lds[32 * kb + 8 * grp + 4];

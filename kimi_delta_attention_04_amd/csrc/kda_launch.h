@@ -7,11 +7,13 @@
 namespace kda {
 
 // Intra-chunk stage over num_slots chunk slots x H heads; writes hand-off
-// records (REC_BYTES each, slot-major then head) into ws.
+// records (REC_BYTES each, slot-major then head) into ws.  scalar_gate: g is
+// [B*T, H] and dt_bias [H] (one gate value per token and head).
 hipError_t launch_intra(const uint16_t *q, const uint16_t *k, const uint16_t *g,
                         const uint16_t *beta, const float *A_log, const float *dt_bias,
                         float lower_bound, const int32_t *cu, int N, int T, int H,
-                        int64_t num_slots, uint8_t *ws, hipStream_t stream);
+                        int64_t num_slots, uint8_t *ws, hipStream_t stream,
+                        bool scalar_gate = false);
 
 // Inter-chunk scan over N sequences x H heads x 8 column slices.
 hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, int N, int T,

@@ -102,6 +102,25 @@ def test_fwd_rejects_before_any_hip_call(lib, over, code):
     assert call_fwd(lib, **over) == code
 
 
+@pytest.mark.parametrize("over,code", [
+    (dict(g=None), INVALID), (dict(g=FAKE + 1), INVALID), (dict(K=64), UNSUPPORTED),
+    (dict(lb=-6.0), UNSUPPORTED), (dict(cu=FAKE, B=2), INVALID),
+])
+def test_scalar_gate_rejects_before_any_hip_call(lib, over, code):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE + 2, beta=FAKE, scale=0.088, A_log=FAKE, dt_bias=None,
+             lb=-5.0, cu=None, N=1, init=None, init_dt=0, fin=None, fin_dt=1, out=FAKE,
+             B=1, T=32, H=2, K=128, V=128)
+    a.update(over)
+    if "cu" in over:
+        a["N"] = 1
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    rc = lib.kda_fwd_scalar_gate(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]), a["scale"],
+                                 P(a["A_log"]), P(a["dt_bias"]), a["lb"], P(a["cu"]), a["N"],
+                                 P(a["init"]), a["init_dt"], P(a["fin"]), a["fin_dt"], P(a["out"]),
+                                 a["B"], a["T"], a["H"], a["K"], a["V"], None)
+    assert rc == code
+
+
 def call_decode(lib, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=0.088, A_log=FAKE, dt_bias=None,
              lb=-5.0, state=FAKE, st_dt=1, out=FAKE, N=4, H=2, K=128, V=128)
