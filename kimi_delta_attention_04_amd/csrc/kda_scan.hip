@@ -29,11 +29,9 @@ namespace kda {
 
 namespace {
 
-constexpr int SCAN_WAVES = 4;                     // compute waves per workgroup
-constexpr int SCAN_THREADS = 64 * (SCAN_WAVES + 1);   // + the DMA wave
 // LDS ring slots per workgroup (chunks in flight + the one being read); the
 // DMA wave's vmcnt (at most 63) must cover DEPTH-1 chunks of DMAs.
-template <int CT> constexpr int RING_DEPTH = CT == 1 ? 5 : 4;
+template <int CW> constexpr int RING_DEPTH = CW <= 64 ? 5 : 4;
 constexpr int REC_KB = REC_BYTES / 1024;         // 13 one-kilobyte units per record
 
 static_assert(REC_BYTES % 1024 == 0, "record must be a whole number of 1 KB units");
@@ -112,19 +110,21 @@ __device__ __forceinline__ float decay_of(const float (&gm)[2]) {
     return row_bcast<4 * (T >> 1) + 2 * (T & 1) + (J >> 1)>(gm[J & 1]);
 }
 
-template <int CT>
-__global__ __launch_bounds__(SCAN_THREADS, 2) void scan_kernel(
+// CT 16-column slices per compute wave, NW compute waves (and the DMA wave)
+// per workgroup.
+template <int CT, int NW>
+__global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
     const uint16_t *__restrict__ v, const uint8_t *__restrict__ ws,
     const int32_t *__restrict__ cu, int N, int T, int H, float scale,
     const void *__restrict__ init, int init_fp32,
     void *__restrict__ fin, int fin_fp32, uint16_t *__restrict__ out)
 {
-    constexpr int CW = SCAN_WAVES * 16 * CT;         // columns per workgroup
+    constexpr int CW = NW * 16 * CT;                 // columns per workgroup
     constexpr int NSPLIT = HD / CW;
     constexpr int V_KB = CS * CW * 2 / 1024;         // one-kilobyte units of a v tile
     constexpr int UNITS = REC_KB + V_KB;             // DMA units per chunk
     constexpr int VROW_LANES = CW * 2 / 16;          // lanes per v row in a DMA unit
-    constexpr int DEPTH = RING_DEPTH<CT>;
+    constexpr int DEPTH = RING_DEPTH<CW>;
     __shared__ ScanSlot<CW> ring[DEPTH];
     static_assert((DEPTH - 1) * UNITS <= 63, "vmcnt holds at most 63");
 
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(SCAN_THREADS, 2) void scan_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int l = tid & 63;
     const int grp = l >> 4, cg = l & 15;
-    const bool dma_wave = w == SCAN_WAVES;            // the wave that issues the ring DMAs
+    const bool dma_wave = w == NW;                    // the wave that issues the ring DMAs
     const int wcol0 = (dma_wave ? 0 : w) * 16 * CT;   // first column of this wave within the part
     const int col0 = part * CW;                       // first column of the part within the head
 
@@ -390,16 +390,19 @@ hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, 
 {
     const int64_t units = (int64_t)N * H;
     if (units <= 0) return hipSuccess;
-    // Few (sequence, head) units: split each head's columns over two
+    // Few (sequence, head) units: split each head's columns over two or four
     // workgroups so that more compute units share the scan.
-    const bool split = 2 * units <= num_cus();
-    const int nsplit = split ? 2 : 1;
+    const int cus = num_cus();
+    const int nsplit = 4 * units <= cus ? 4 : 2 * units <= cus ? 2 : 1;
     const int64_t blocks = 8 * nsplit * ((units + 7) / 8);
-    if (split)
-        hipLaunchKernelGGL(scan_kernel<1>, dim3((unsigned)blocks), dim3(SCAN_THREADS), 0, stream,
+    if (nsplit == 4)
+        hipLaunchKernelGGL((scan_kernel<1, 2>), dim3((unsigned)blocks), dim3(64 * 3), 0, stream,
+                           v, ws, cu, N, T, H, scale, init, init_fp32, fin, fin_fp32, out);
+    else if (nsplit == 2)
+        hipLaunchKernelGGL((scan_kernel<1, 4>), dim3((unsigned)blocks), dim3(64 * 5), 0, stream,
                            v, ws, cu, N, T, H, scale, init, init_fp32, fin, fin_fp32, out);
     else
-        hipLaunchKernelGGL(scan_kernel<2>, dim3((unsigned)blocks), dim3(SCAN_THREADS), 0, stream,
+        hipLaunchKernelGGL((scan_kernel<2, 4>), dim3((unsigned)blocks), dim3(64 * 5), 0, stream,
                            v, ws, cu, N, T, H, scale, init, init_fp32, fin, fin_fp32, out);
     return hipGetLastError();
 }

@@ -63,6 +63,17 @@ def test_batched_fixed_length():
     check_against_oracle(inp, out, fin)
 
 
+@pytest.mark.parametrize("B,H", [(1, 4), (1, 80), (2, 70)])
+def test_scan_column_splits(B, H):
+    """The scan splits each head's 128 columns over four, two or one
+    workgroups depending on how many (sequence, head) units there are (at
+    most 64, at most 128, more, on 256 compute units); one case of each."""
+    inp = kda_inputs.random_small(900 + H, B=B, T=45, H=H, initial_state=True)
+    out, fin = run_kda(to_device(inp))
+    heads = sorted({0, H // 2, H - 1})
+    check_against_oracle(inp, out, fin, heads=heads)
+
+
 def test_varlen_with_empty_and_unit_sequences():
     inp = kda_inputs.random_small(8, B=1, T=100, H=4, seq_lens=[16, 1, 0, 33, 50, 0],
                                   initial_state=True)
