@@ -240,8 +240,6 @@ __device__ __forceinline__ void intra_compute(WaveLds &L, const IntraIn &in, flo
             const int ch = 32 * kb + 8 * grp;
             *(f32x4_t *)&L.gam[ch] = g0;
             *(f32x4_t *)&L.gam[ch + 4] = g1;
-            *(f32x4_t *)(rec + REC_GAM + ch * 4) = g0;
-            *(f32x4_t *)(rec + REC_GAM + ch * 4 + 16) = g1;
         }
         *(u32x4_t *)(rec + REC_KT + (kb * 64 + l) * 16) = kt4;
         *(u32x4_t *)(rec + REC_QT + (kb * 64 + l) * 16) = qh4;
@@ -263,6 +261,9 @@ __device__ __forceinline__ void intra_compute(WaveLds &L, const IntraIn &in, flo
     }
 
     wave_lds_sync();
+    // the chunk decay into the record from LDS in one coalesced store (four
+    // lanes' 16-byte pieces per block cost several times as much)
+    *(u32x2_t *)(rec + REC_GAM + l * 8) = *(const u32x2_t *)&L.gam[2 * l];
 
     // ---- T = (I + L)^{-1}, L = diag(beta) strict_lower(Akk) ---------------
     float br[4];
