@@ -66,6 +66,8 @@ kda_status_t check_sizes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
     // token-row and unit counts must fit the int32 grid / index arithmetic
     if ((int64_t)B * T > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     if (num_slots(B, T, N) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    // one intra workgroup per (chunk slot, head) in a 1-D grid
+    if (num_slots(B, T, N) * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     if ((int64_t)N * H > INT32_MAX / 64) return KDA_ERR_UNSUPPORTED;
     // byte offsets within one chunk's 16 token rows of all heads are 32-bit
     if ((int64_t)H * kda::HD * 2 * kda::CS > INT32_MAX) return KDA_ERR_UNSUPPORTED;

@@ -19,8 +19,10 @@ __global__ __launch_bounds__(64, 2) void intra_kernel(
     const int32_t *__restrict__ cu, int N, int T, int H, uint8_t *__restrict__ ws)
 {
     __shared__ __attribute__((aligned(16))) WaveLds lds;
-    const int64_t slot = blockIdx.x;
-    const int h = blockIdx.y;
+    // head fastest: the workgroups running together read neighbouring pieces
+    // of the same token rows and write neighbouring records
+    const int64_t slot = blockIdx.x / (unsigned)H;
+    const int h = (int)(blockIdx.x % (unsigned)H);
 
     // Which sequence owns this slot: largest n with slot0(n) <= slot.
     int lo = 0, hi = N - 1;
@@ -57,7 +59,7 @@ hipError_t launch_intra(const uint16_t *q, const uint16_t *k, const uint16_t *g,
                         int64_t num_slots, uint8_t *ws, hipStream_t stream, bool scalar_gate)
 {
     if (num_slots <= 0) return hipSuccess;
-    dim3 grid((unsigned)num_slots, (unsigned)H);
+    dim3 grid((unsigned)(num_slots * H));
     if (scalar_gate)
         hipLaunchKernelGGL(intra_kernel<true>, grid, dim3(64), 0, stream,
                            q, k, g, beta, A_log, dt_bias, lower_bound * LOG2E, cu, N, T, H, ws);

@@ -97,6 +97,7 @@ def call_fwd(lib, **over):
     (dict(B=2, N=2, T=2 ** 30 + 1), UNSUPPORTED),       # token rows overflow int32
     (dict(H=2 ** 26), UNSUPPORTED),                     # (sequence, head) units overflow the grid
     (dict(H=2 ** 19), UNSUPPORTED),                     # 16-row byte offsets overflow int32
+    (dict(T=2 ** 26, H=1024), UNSUPPORTED),             # (chunk slot, head) pairs overflow the grid
 ])
 def test_fwd_rejects_before_any_hip_call(lib, over, code):
     assert call_fwd(lib, **over) == code
