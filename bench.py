@@ -19,6 +19,8 @@ kernel (kda_set_stage_events) on the stream the kernels run on.
 the same workload with g [B, T, H] and dt_bias [H]: g then moves 2 B per
 (token, head) instead of 256.
 
+`--head-dim 64` measures the same workload at K = V = 64.
+
 `--decode-batch N` instead measures the decode step (kda_decode, one kernel
 on the current stream): N one-token sequences x H heads with an fp32 state
 updated in place, algorithmic bytes per (sequence, head) = the state read and
@@ -157,6 +159,8 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the T=8192 H=96 fixed one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=96, help="heads in the oracle's timed sample")
+    ap.add_argument("--head-dim", type=int, default=128, choices=(64, 128),
+                    help="K = V of the measured workload")
     ap.add_argument("--scalar-gate", action="store_true",
                     help="measure the Gated DeltaNet form (one gate value per token and head)")
     ap.add_argument("--decode-batch", type=int, default=0, metavar="N",
@@ -194,6 +198,10 @@ def main():
         return
     name = args.workload or kda_inputs.HEADLINE
     w = kda_inputs.WORKLOADS[name]
+    if args.head_dim != w.K:
+        import dataclasses
+        w = dataclasses.replace(w, name=f"{w.name}_D{args.head_dim}", K=args.head_dim, V=args.head_dim)
+        name = w.name
     log(f"[bench] generating {name} ...")
     inp = kda_inputs.generate(w)
     dev = torch.device("cuda:0")
@@ -274,12 +282,14 @@ def main():
             "stage_ms_min": {"kda_intra": min(intra_ms), "kda_scan": min(scan_ms)}}
 
     cpu = None
-    if not args.no_cpu_baseline and not args.scalar_gate:
+    if not args.no_cpu_baseline and not args.scalar_gate and args.head_dim == 128:
         log(f"[bench] oracle CPU baseline on {args.cpu_heads} heads")
         cpu = cpu_baseline(inp, w, args.cpu_heads)
 
     cfg = w.describe()
     metric = METRIC
+    if args.head_dim != 128:
+        metric = f"KDA fwd tokens/s @T={w.T},H={w.H},D={w.K}"
     if args.scalar_gate:
         metric = "KDA fwd, scalar (Gated DeltaNet) gate, tokens/s @T=8192,H=96,D=128"
         cfg = dict(cfg, gate="scalar per (token, head)")

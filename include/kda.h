@@ -17,9 +17,10 @@
  * recurrent states in bf16 or fp32, and cu_seqlens for variable-length
  * batches.  The pages name the gate parameters but not the gate formula; the
  * clamped softplus form above is the reading this library implements.  The
- * head dimension is fixed at K = V = 128 ("Moonshot AI Open-Sources
- * FlashKDA", section "Limitations before you integrate"); only the forward
- * pass exists (same section).
+ * original supports only K = V = 128 ("Moonshot AI Open-Sources FlashKDA",
+ * section "Limitations before you integrate"); this library also takes
+ * K = V = 64 in kda_fwd and kda_fwd_scalar_gate.  Only the forward pass
+ * exists (same section).
  *
  * Conventions shared by every entry point:
  *   - Pointers are device pointers unless stated; every tensor is dense and
@@ -82,7 +83,9 @@ typedef enum {
  *   final_state    [N, H, K, V] in final_state_dtype, or NULL (not written);
  *                  when given, every slab is written (a zero-length sequence
  *                  gets its initial state)
- *   B, T, H, K, V  sizes; K and V must both be 128.  When B*T == 0 the
+ *   B, T, H, K, V  sizes; K = V = 128, or K = V = 64 (run on the 128-wide
+ *                  kernels with the channels and columns from 64 on held at
+ *                  zero).  When B*T == 0 the
  *                  token buffers (q, k, v, g, beta, out) may be NULL; the
  *                  call then only writes final_state (= initial state)
  *

@@ -62,7 +62,8 @@ kda_status_t check_sizes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
                          const int32_t *cu, int32_t N) {
     if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID_ARG;
     if (cu ? (B != 1) : (N != B)) return KDA_ERR_INVALID_ARG;
-    if (K != kda::HD || V != kda::HD) return KDA_ERR_UNSUPPORTED;
+    // K = V = 128, or K = V = 64 (computed on the 128-wide tiles)
+    if (K != V || (K != kda::HD && K != 64)) return KDA_ERR_UNSUPPORTED;
     // token-row and unit counts must fit the int32 grid / index arithmetic
     if ((int64_t)B * T > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     if (num_slots(B, T, N) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
@@ -151,11 +152,11 @@ kda_status_t fwd_impl(const void *q, const void *k, const void *v, const void *g
     if (e == hipSuccess)
         e = kda::launch_intra((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,
                               (const uint16_t *)beta, A_log, dt_bias, lower_bound,
-                              cu_seqlens, num_seqs, T, H, slots, (uint8_t *)ws, s, scalar_gate);
+                              cu_seqlens, num_seqs, T, H, K, slots, (uint8_t *)ws, s, scalar_gate);
     if (e == hipSuccess) e = mark(1, s);
     if (e == hipSuccess)
         e = kda::launch_scan((const uint16_t *)v, (const uint8_t *)ws, cu_seqlens, num_seqs, T, H,
-                             scale, initial_state, initial_state_dtype == KDA_DTYPE_FP32,
+                             K, V, scale, initial_state, initial_state_dtype == KDA_DTYPE_FP32,
                              final_state, final_state_dtype == KDA_DTYPE_FP32,
                              (uint16_t *)out, s);
     if (e == hipSuccess) e = mark(2, s);
@@ -215,7 +216,7 @@ kda_status_t kda_debug_intra(const void *q, const void *k, const void *g,
     if ((st = check_gate(lower_bound)) != KDA_OK) return st;
     hipError_t e = kda::launch_intra((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,
                                      (const uint16_t *)beta, A_log, dt_bias, lower_bound,
-                                     cu_seqlens, num_seqs, T, H, num_slots(B, T, num_seqs),
+                                     cu_seqlens, num_seqs, T, H, K, num_slots(B, T, num_seqs),
                                      (uint8_t *)workspace, (hipStream_t)stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }

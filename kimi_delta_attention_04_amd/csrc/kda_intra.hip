@@ -10,14 +10,16 @@ namespace kda {
 namespace {
 
 // One wave per (chunk slot, head), a workgroup of its own.  SG: scalar
-// (per-head) gate, g [B*T, H] and dt_bias [H].
-template <bool SG>
+// (per-head) gate, g [B*T, H] and dt_bias [H].  KD: head dimension (128, or
+// 64 computed on 128 channels of which the last 64 are zeros).
+template <bool SG, int KD>
 __global__ __launch_bounds__(64, 2) void intra_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
     const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb2,
     const int32_t *__restrict__ cu, int N, int T, int H, uint8_t *__restrict__ ws)
 {
+    constexpr int K = KD;
     __shared__ __attribute__((aligned(16))) WaveLds lds;
     // head fastest: the workgroups running together read neighbouring pieces
     // of the same token rows and write neighbouring records
@@ -40,11 +42,11 @@ __global__ __launch_bounds__(64, 2) void intra_kernel(
 
     const float A = expf(A_log[h]);
     __shared__ float dtb_lds[HD];
-    stage_dtb<SG>(dtb_lds, dt_bias, h);
+    stage_dtb<SG>(dtb_lds, dt_bias, h, K);
     wave_lds_sync();
 
     IntraIn in;
-    intra_load<SG>(in, q, k, g, beta, t0, len, H, h);
+    intra_load<SG>(in, q, k, g, beta, t0, len, H, h, K);
     if (len == CS)
         intra_compute<true, SG>(lds, in, A, dtb_lds, lb2, len, rec);
     else
@@ -55,17 +57,21 @@ __global__ __launch_bounds__(64, 2) void intra_kernel(
 
 hipError_t launch_intra(const uint16_t *q, const uint16_t *k, const uint16_t *g,
                         const uint16_t *beta, const float *A_log, const float *dt_bias,
-                        float lower_bound, const int32_t *cu, int N, int T, int H,
+                        float lower_bound, const int32_t *cu, int N, int T, int H, int K,
                         int64_t num_slots, uint8_t *ws, hipStream_t stream, bool scalar_gate)
 {
     if (num_slots <= 0) return hipSuccess;
     dim3 grid((unsigned)(num_slots * H));
-    if (scalar_gate)
-        hipLaunchKernelGGL(intra_kernel<true>, grid, dim3(64), 0, stream,
-                           q, k, g, beta, A_log, dt_bias, lower_bound * LOG2E, cu, N, T, H, ws);
-    else
-        hipLaunchKernelGGL(intra_kernel<false>, grid, dim3(64), 0, stream,
-                           q, k, g, beta, A_log, dt_bias, lower_bound * LOG2E, cu, N, T, H, ws);
+    const float lb2 = lower_bound * LOG2E;
+#define KDA_INTRA(SG_, KD_)                                                               \
+    hipLaunchKernelGGL((intra_kernel<SG_, KD_>), grid, dim3(64), 0, stream,              \
+                       q, k, g, beta, A_log, dt_bias, lb2, cu, N, T, H, ws)
+    if (K == HD) {
+        if (scalar_gate) KDA_INTRA(true, HD); else KDA_INTRA(false, HD);
+    } else {
+        if (scalar_gate) KDA_INTRA(true, 64); else KDA_INTRA(false, 64);
+    }
+#undef KDA_INTRA
     return hipGetLastError();
 }
 

@@ -50,22 +50,28 @@ __device__ __forceinline__ void intra_load(IntraIn &in, const uint16_t *__restri
                                            const uint16_t *__restrict__ k,
                                            const uint16_t *__restrict__ g,
                                            const uint16_t *__restrict__ beta,
-                                           int64_t t0, int len, int H, int hh) {
+                                           int64_t t0, int len, int H, int hh, int K) {
+    // K = 128, or 64: channels from K on are zeros (zero keys and queries add
+    // nothing to the in-chunk products, the W rows or the state)
     const int l = threadIdx.x & 63;
     const int tok = l & 15, cgp = l >> 4;
-    const size_t row_elems = (size_t)H * HD;
-    const size_t base = ((size_t)t0 * H + hh) * HD;
-    const uint32_t bytes = len > 0 ? (uint32_t)(((size_t)(len - 1) * row_elems + HD) * 2) : 0u;
+    const size_t row_elems = (size_t)H * K;
+    const size_t base = ((size_t)t0 * H + hh) * K;
+    const uint32_t bytes = len > 0 ? (uint32_t)(((size_t)(len - 1) * row_elems + K) * 2) : 0u;
     const __amdgpu_buffer_rsrc_t sg = make_rsrc(g + base, bytes);
     const __amdgpu_buffer_rsrc_t sq = make_rsrc(q + base, bytes);
     const __amdgpu_buffer_rsrc_t sk = make_rsrc(k + base, bytes);
+    const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         const int off = (int)((tok * row_elems + 32 * kb + 8 * cgp) * 2);
-        if (!SG)
-            in.g[kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sg, off, 0, 0));
-        in.q[kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sq, off, 0, 0));
-        in.k[kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sk, off, 0, 0));
+        in.g[kb] = in.q[kb] = in.k[kb] = z;
+        if (32 * kb < K) {                          // block-uniform
+            if (!SG)
+                in.g[kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sg, off, 0, 0));
+            in.q[kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sq, off, 0, 0));
+            in.k[kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sk, off, 0, 0));
+        }
     }
     // beta (and the scalar gate of the SG form) are [token, head]
     const uint32_t tb = len > 0 ? (uint32_t)(((size_t)(len - 1) * H + 1) * 2) : 0u;
@@ -77,20 +83,22 @@ __device__ __forceinline__ void intra_load(IntraIn &in, const uint16_t *__restri
     }
 }
 
-// dt_bias of one head in log2 units into LDS (128 floats; zeros when absent),
-// by the lanes of the calling wave.  SG form: dt_bias is [H], one value per
+// dt_bias of one head in log2 units into LDS (128 floats; zeros when absent
+// and for channels from K on), by the lanes of the calling wave.  SG form: dt_bias is [H], one value per
 // head, staged into dtb_lds[0].
 template <bool SG = false>
 __device__ __forceinline__ void stage_dtb(float *__restrict__ dtb_lds, const float *__restrict__ dt_bias,
-                                          int hh) {
+                                          int hh, int K = HD) {
     const int l = threadIdx.x & 63;
     if (SG) {
         if (l == 0) dtb_lds[0] = dt_bias ? dt_bias[hh] * LOG2E : 0.f;
         return;
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-        dtb_lds[64 * r + l] = dt_bias ? dt_bias[(size_t)hh * HD + 64 * r + l] * LOG2E : 0.f;
+    for (int r = 0; r < 2; ++r) {
+        const int c = 64 * r + l;
+        dtb_lds[c] = (dt_bias && c < K) ? dt_bias[(size_t)hh * K + c] * LOG2E : 0.f;
+    }
 }
 
 // Inclusive prefix sum over the 16 lanes of each DPP row (lanes past the

@@ -7,18 +7,21 @@
 namespace kda {
 
 // Intra-chunk stage over num_slots chunk slots x H heads; writes hand-off
-// records (REC_BYTES each, slot-major then head) into ws.  scalar_gate: g is
-// [B*T, H] and dt_bias [H] (one gate value per token and head).
+// records (REC_BYTES each, slot-major then head) into ws.  K = 128 or 64
+// (channels from K on computed as zeros).  scalar_gate: g is [B*T, H] and
+// dt_bias [H] (one gate value per token and head).
 hipError_t launch_intra(const uint16_t *q, const uint16_t *k, const uint16_t *g,
                         const uint16_t *beta, const float *A_log, const float *dt_bias,
-                        float lower_bound, const int32_t *cu, int N, int T, int H,
+                        float lower_bound, const int32_t *cu, int N, int T, int H, int K,
                         int64_t num_slots, uint8_t *ws, hipStream_t stream,
                         bool scalar_gate = false);
 
-// Inter-chunk scan over N sequences x H heads x 8 column slices.
+// Inter-chunk scan over N sequences x H heads (column parts per head chosen
+// by the launch).  K = V = 128 or 64: the 128 x 128 state tiles carry zeros
+// in the rows from K on and the columns from V on.
 hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, int N, int T,
-                       int H, float scale, const void *init, int init_fp32, void *fin,
-                       int fin_fp32, uint16_t *out, hipStream_t stream);
+                       int H, int K, int V, float scale, const void *init, int init_fp32,
+                       void *fin, int fin_fp32, uint16_t *out, hipStream_t stream);
 
 // One-token decode step on N x H states in place (fp32 or bf16).
 hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,

@@ -111,8 +111,8 @@ __device__ __forceinline__ float decay_of(const float (&gm)[2]) {
 }
 
 // CT 16-column slices per compute wave, NW compute waves (and the DMA wave)
-// per workgroup.
-template <int CT, int NW>
+// per workgroup; head dimension K = V = VD (128, or 64 on the same tiles).
+template <int CT, int NW, int VD>
 __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
     const uint16_t *__restrict__ v, const uint8_t *__restrict__ ws,
     const int32_t *__restrict__ cu, int N, int T, int H, float scale,
@@ -120,7 +120,9 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
     void *__restrict__ fin, int fin_fp32, uint16_t *__restrict__ out)
 {
     constexpr int CW = NW * 16 * CT;                 // columns per workgroup
-    constexpr int NSPLIT = HD / CW;
+    constexpr int K = VD, V = VD;
+    constexpr int NSPLIT = V / CW;                   // column parts per head
+    static_assert(NSPLIT * CW == V, "column parts cover the head");
     constexpr int V_KB = CS * CW * 2 / 1024;         // one-kilobyte units of a v tile
     constexpr int UNITS = REC_KB + V_KB;             // DMA units per chunk
     constexpr int VROW_LANES = CW * 2 / 16;          // lanes per v row in a DMA unit
@@ -147,13 +149,16 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
     const int64_t L = end - start;
     const int nch = (int)((L + CS - 1) / CS);
     const int64_t slot0 = seq_slot0(cu, n, T);
-    const size_t row_bytes = (size_t)H * HD * 2;      // one token row of v / out
+    // K = V = 128, or 64 on the same tiles: state rows from K on stay zero
+    // (they load as zeros from the range-checked state buffers, receive no
+    // updates since their key channels are zero, and are not stored)
+    const size_t row_bytes = (size_t)H * V * 2;       // one token row of v / out
 
     // ---- state slices: S[ct][t][j] = state[chan(t, 4grp+j)][col] -------------
     // (a zero-sized resource when there is no initial state: loads return 0)
     f32x4_t S[CT][8];
     if (!dma_wave) {
-        const size_t slab = (size_t)HD * HD * (init_fp32 ? 4 : 2);
+        const size_t slab = (size_t)K * V * (init_fp32 ? 4 : 2);
         const __amdgpu_buffer_rsrc_t rs =
             make_rsrc((const uint8_t *)init + (init ? ((size_t)n * H + h) * slab : 0),
                       init ? (uint32_t)slab : 0u);
@@ -164,7 +169,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
                 for (int t = 0; t < 8; ++t)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const int idx = state_chan(t, 4 * grp + j) * HD + col0 + wcol0 + 16 * ct + cg;
+                        const int idx = state_chan(t, 4 * grp + j) * V + col0 + wcol0 + 16 * ct + cg;
                         S[ct][t][j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, idx * 4, 0, 0));
                     }
         } else {
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
                 for (int t = 0; t < 8; ++t)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const int idx = state_chan(t, 4 * grp + j) * HD + col0 + wcol0 + 16 * ct + cg;
+                        const int idx = state_chan(t, 4 * grp + j) * V + col0 + wcol0 + 16 * ct + cg;
                         S[ct][t][j] = bf16f(__builtin_amdgcn_raw_buffer_load_b16(rs, idx * 2, 0, 0));
                     }
         }
@@ -184,10 +189,10 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
 
     // Per-chunk addressing advances by fixed strides.
     const size_t rec_stride = (size_t)H * REC_BYTES;
-    const size_t row_stride = (size_t)CS * H * HD;                 // elements per chunk of v / out
+    const size_t row_stride = (size_t)CS * H * V;                  // elements per chunk of v / out
     const uint8_t *rec_base = ws + ((size_t)slot0 * H + h) * REC_BYTES;
-    const uint16_t *v_base = v + ((size_t)start * H + h) * HD + col0;
-    uint16_t *out_base = out + ((size_t)start * H + h) * HD + col0;
+    const uint16_t *v_base = v + ((size_t)start * H + h) * V + col0;
+    uint16_t *out_base = out + ((size_t)start * H + h) * V + col0;
 
     // Chunk c -> ring slot c % DEPTH by DMA (DMA wave): unit k < REC_KB is
     // kilobyte k of the record; the next V_KB units are the v tile of this
@@ -342,7 +347,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
     }
 
     if (fin) {
-        const size_t slab = (size_t)HD * HD * (fin_fp32 ? 4 : 2);
+        const size_t slab = (size_t)K * V * (fin_fp32 ? 4 : 2);
         const __amdgpu_buffer_rsrc_t rf =
             make_rsrc((uint8_t *)fin + ((size_t)n * H + h) * slab, (uint32_t)slab);
         if (fin_fp32) {
@@ -352,7 +357,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
                 for (int t = 0; t < 8; ++t)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const int idx = state_chan(t, 4 * grp + j) * HD + col0 + wcol0 + 16 * ct + cg;
+                        const int idx = state_chan(t, 4 * grp + j) * V + col0 + wcol0 + 16 * ct + cg;
                         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[ct][t][j]), rf, idx * 4, 0, 0);
                     }
         } else {
@@ -362,7 +367,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
                 for (int t = 0; t < 8; ++t)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const int idx = state_chan(t, 4 * grp + j) * HD + col0 + wcol0 + 16 * ct + cg;
+                        const int idx = state_chan(t, 4 * grp + j) * V + col0 + wcol0 + 16 * ct + cg;
                         __builtin_amdgcn_raw_buffer_store_b16(tobf16(S[ct][t][j]), rf, idx * 2, 0, 0);
                     }
         }
@@ -385,25 +390,30 @@ int num_cus() {
 }  // namespace
 
 hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, int N, int T,
-                       int H, float scale, const void *init, int init_fp32, void *fin,
-                       int fin_fp32, uint16_t *out, hipStream_t stream)
+                       int H, int K, int V, float scale, const void *init, int init_fp32,
+                       void *fin, int fin_fp32, uint16_t *out, hipStream_t stream)
 {
     const int64_t units = (int64_t)N * H;
     if (units <= 0) return hipSuccess;
-    // Few (sequence, head) units: split each head's columns over two or four
-    // workgroups so that more compute units share the scan.
+    // Few (sequence, head) units: split each head's columns over more
+    // workgroups (of fewer compute waves) so that more compute units share
+    // the scan.  Parts of 32, 64 or 128 columns; V / part workgroups a head.
     const int cus = num_cus();
-    const int nsplit = 4 * units <= cus ? 4 : 2 * units <= cus ? 2 : 1;
-    const int64_t blocks = 8 * nsplit * ((units + 7) / 8);
-    if (nsplit == 4)
-        hipLaunchKernelGGL((scan_kernel<1, 2>), dim3((unsigned)blocks), dim3(64 * 3), 0, stream,
-                           v, ws, cu, N, T, H, scale, init, init_fp32, fin, fin_fp32, out);
-    else if (nsplit == 2)
-        hipLaunchKernelGGL((scan_kernel<1, 4>), dim3((unsigned)blocks), dim3(64 * 5), 0, stream,
-                           v, ws, cu, N, T, H, scale, init, init_fp32, fin, fin_fp32, out);
-    else
-        hipLaunchKernelGGL((scan_kernel<2, 4>), dim3((unsigned)blocks), dim3(64 * 5), 0, stream,
-                           v, ws, cu, N, T, H, scale, init, init_fp32, fin, fin_fp32, out);
+    const int cw = (V == 128 ? 4 : 2) * units <= cus ? 32 : (V == 128 ? 2 : 1) * units <= cus ? 64 : 128;
+    const int part_cw = cw > V ? V : cw;
+    const int64_t blocks = 8 * (V / part_cw) * ((units + 7) / 8);
+#define KDA_SCAN(CT_, NW_, VD_)                                                               \
+    hipLaunchKernelGGL((scan_kernel<CT_, NW_, VD_>), dim3((unsigned)blocks), dim3(64 * (NW_ + 1)), \
+                       0, stream, v, ws, cu, N, T, H, scale, init, init_fp32, fin, fin_fp32, out)
+    if (V == HD) {
+        if (part_cw == 32) KDA_SCAN(1, 2, HD);
+        else if (part_cw == 64) KDA_SCAN(1, 4, HD);
+        else KDA_SCAN(2, 4, HD);
+    } else {
+        if (part_cw == 32) KDA_SCAN(1, 2, 64);
+        else KDA_SCAN(1, 4, 64);
+    }
+#undef KDA_SCAN
     return hipGetLastError();
 }
 

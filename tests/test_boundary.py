@@ -85,7 +85,8 @@ def call_fwd(lib, **over):
     (dict(out=None), INVALID),
     (dict(q=FAKE + 8), INVALID), (dict(out=FAKE + 2), INVALID), (dict(beta=FAKE + 1), INVALID),
     (dict(A_log=FAKE + 2), INVALID), (dict(init=FAKE + 4), INVALID),
-    (dict(K=64), UNSUPPORTED), (dict(V=256), UNSUPPORTED), (dict(K=64, V=64), UNSUPPORTED),
+    (dict(K=64), UNSUPPORTED), (dict(V=256), UNSUPPORTED), (dict(K=256, V=256), UNSUPPORTED),
+    (dict(K=64, V=128), UNSUPPORTED), (dict(K=32, V=32), UNSUPPORTED),
     (dict(B=0), INVALID), (dict(T=-1), INVALID), (dict(H=0), INVALID),
     (dict(N=2), INVALID),                              # fixed length needs N == B
     (dict(cu=FAKE, B=2, N=2), INVALID),                # cu_seqlens needs B == 1
@@ -148,7 +149,7 @@ def test_debug_intra_validates(lib):
     f = lambda **o: lib.kda_debug_intra(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None,
                                         o.get("lb", -5.0), None, 1, 1, 16, 1, o.get("K", 128),
                                         o.get("ws", P(FAKE)), None)
-    assert f(K=64) == UNSUPPORTED
+    assert f(K=256) == UNSUPPORTED and f(K=32) == UNSUPPORTED
     assert f(lb=-7.0) == UNSUPPORTED
     assert f(ws=None) == INVALID
 
