@@ -51,3 +51,42 @@ def test_full_size_workload(name):
         out_f, fin_f = run_kda(fixed)
         assert torch.equal(out.reshape(out_f.shape), out_f)
         assert torch.equal(fin, fin_f)
+
+
+def test_long_sequence_split_bitexact():
+    """T = 2^18 tokens on 2 heads.  The first 4096 output rows against the
+    oracle (they depend only on the first 4096 tokens), and the run split at
+    a chunk boundary: the second half started from the first half's fp32
+    final state must reproduce the full run's second half and final state
+    bit for bit (the scan keeps exactly that fp32 state at the boundary)."""
+    T, H, P = 1 << 18, 2, 4096
+    inp = kda_inputs.random_small(1001, B=1, T=T, H=H, initial_state=True)
+    d = to_device(inp)
+    out, fin = run_kda(d)
+    assert torch.isfinite(out).all().item() and torch.isfinite(fin).all().item()
+    pre = {key: (val[:, :P].contiguous() if key in ("q", "k", "v", "g", "beta") else val)
+           for key, val in inp.items()}
+    o_ref, _ = oracle.cref_forward(pre, want_final=False)
+    assert_close("o[:4096]", np64(out[:, :P]), o_ref)
+    half = T // 2
+    first = {key: (val[:, :half].contiguous() if key in ("q", "k", "v", "g", "beta") else val)
+             for key, val in d.items()}
+    _, fin1 = run_kda(first, final_dtype=torch.float32)
+    second = {key: (val[:, half:].contiguous() if key in ("q", "k", "v", "g", "beta") else val)
+              for key, val in d.items()}
+    second["initial_state"] = fin1
+    out2, fin2 = run_kda(second, final_dtype=torch.float32)
+    assert torch.equal(out[:, half:], out2)
+    assert torch.equal(fin, fin2)
+
+
+def test_many_heads():
+    """H = 4096 heads (one column part per head in the scan), sampled heads
+    against the oracle."""
+    H = 4096
+    inp = kda_inputs.random_small(1002, B=1, T=40, H=H, initial_state=True)
+    out, fin = run_kda(to_device(inp))
+    heads = sample_heads(H)
+    o_ref, f_ref = oracle.cref_forward(inp, heads=heads)
+    assert_close("o", np64(out[:, :, heads]), o_ref)
+    assert_close("final_state", np64(fin[:, heads]), f_ref)
