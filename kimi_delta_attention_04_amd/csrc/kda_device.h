@@ -26,7 +26,7 @@
 
 namespace kda {
 
-constexpr int HD = 128;          // head dimension (K = V)
+constexpr int HD = 128;          // head dimension of the tiles (K = V; 64 runs on them zero-padded)
 constexpr int CS = 16;           // tokens per chunk
 constexpr float LOG2E = 1.4426950408889634f;
 

@@ -1,8 +1,9 @@
 // Inter-chunk scan: the sequential part of the chunkwise algorithm.
 //
-// A workgroup of four waves owns one (sequence, head, column part); each wave
-// keeps CT 16-column slices of the 128-row fp32 state in MFMA accumulators
-// for the whole sequence.  Columns of the state evolve independently (each
+// A workgroup owns one (sequence, head, column part); each of its NW compute
+// waves (four, or two when a head is split over four workgroups) keeps CT
+// 16-column slices of the 128-row fp32 state in MFMA accumulators for the
+// whole sequence.  Columns of the state evolve independently (each
 // sees the same transition and its own v entries), so column parts need no
 // communication.  The row permutation of the state tiles (kda_device.h)
 // makes the accumulators of tile pair (2kb, 2kb+1), rounded to bf16, exactly
@@ -14,9 +15,9 @@
 //
 // The hand-off record of each chunk (13 KB) and the chunk's v tile are read
 // from memory once per workgroup, by buffer-to-LDS DMA into a ring of
-// DEPTH slots, DEPTH-1 chunks ahead of the compute.  A fifth wave issues all
-// of the DMAs; the four compute waves read their MFMA operands from the
-// ring and never wait on the DMA themselves.  Every memory access goes
+// DEPTH slots, DEPTH-1 chunks ahead of the compute.  One more wave issues
+// all of the DMAs; the compute waves read their MFMA operands from the ring
+// and never wait on the DMA themselves.  Every memory access goes
 // through a range-checked buffer resource, so partial chunks need no
 // branches and the number of DMAs per chunk is fixed, which is what the
 // DMA wave's explicit vmcnt accounting relies on.  The serial chain is what
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
 
     // Software pipeline.  Iteration c: the DMA wave waits for chunk c+1 to
     // land, the compute waves finish their reads of chunk c (issued in
-    // iteration c-1), all five meet at a barrier; then the compute waves
+    // iteration c-1), all the waves meet at a barrier; then the compute waves
     // read chunk c+1 into registers and compute chunk c while the DMA wave
     // refills chunk c's slot with chunk c+DEPTH.  The DMA wave issues chunks
     // in order, UNITS DMAs each, so at the top of iteration c the DMAs issued
