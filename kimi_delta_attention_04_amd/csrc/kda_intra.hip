@@ -21,9 +21,13 @@ __global__ __launch_bounds__(64, 2) void intra_kernel(
 {
     constexpr int K = KD;
     __shared__ __attribute__((aligned(16))) WaveLds lds;
-    // head fastest: the workgroups running together read neighbouring pieces
-    // of the same token rows and write neighbouring records
-    const int64_t slot = blockIdx.x / (unsigned)H;
+    // Head fastest: the workgroups running together read neighbouring pieces
+    // of the same token rows and write neighbouring records.  Last chunk
+    // slot first: the records of the first chunks, which the scan reads
+    // first, are then the most recently written when it starts, and part of
+    // them is still in the memory-side cache (measured: scan 316 -> 310 us
+    // at T = 8192, H = 96).
+    const int64_t slot = (int64_t)(gridDim.x / (unsigned)H) - 1 - blockIdx.x / (unsigned)H;
     const int h = (int)(blockIdx.x % (unsigned)H);
 
     // Which sequence owns this slot: largest n with slot0(n) <= slot.
