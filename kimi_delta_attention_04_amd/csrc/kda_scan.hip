@@ -69,13 +69,12 @@ __device__ __forceinline__ i32x4_t rsrc_words(const void *p, uint32_t bytes) {
 // of the resource land at LDS address lds + 16 l.  Issued from inline
 // assembly so that the compiler's own wait insertion, which cannot tell the
 // ring slots apart, does not serialise the prefetch; the waits are explicit
-// (wait_vm_barrier).  The loop that uses it issues no other loads.
-// m0 is set by the asm itself; nothing else in these kernels keeps a value
-// in m0 (checked in the generated code), so it is not listed as a clobber.
+// (wait_vm_barrier).  The loop that uses it issues no other loads.  m0 (the
+// LDS address of the DMA) is set by the asm itself and declared clobbered.
 __device__ __forceinline__ void dma16(i32x4_t rs, const void *lds, int off) {
     const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(m0), "v"(off), "s"(rs) : "memory");
+                 :: "s"(m0), "v"(off), "s"(rs) : "memory", "m0");
 }
 
 template <int CW>
