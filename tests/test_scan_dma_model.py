@@ -1,0 +1,88 @@
+"""CPU model of the scan's DMA wave schedule (no GPU).
+
+The DMA wave issues each chunk's loads in order (REC_KB record kilobytes,
+then V_KB v kilobytes) into a ring of DEPTH LDS slots and waits with
+explicit `s_waitcnt vmcnt(n)` counts: (DEPTH-1) x UNITS before the first
+iteration (chunk 0 landed) and (DEPTH-2) x UNITS at the top of iteration c
+(chunk c+1 landed).  Vector-memory loads of one wave complete in issue
+order, so vmcnt(n) means "all but the last n issued have completed".  This
+model replays the schedule for every column-part width the launch uses and
+checks that each wait leaves exactly the chunk the compute waves read next
+landed, that a slot is refilled only after the compute waves' reads of its
+previous chunk (read one iteration ahead, before the barrier that ends the
+iteration), and that the counts fit the 6-bit vmcnt field.
+"""
+from __future__ import annotations
+
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SCAN = os.path.join(ROOT, "kimi_delta_attention_04_amd", "csrc", "kda_scan.hip")
+REC_BYTES, CS = 13312, 16
+VMCNT_MAX = 63
+
+
+def ring_depth(cw: int) -> int:
+    """RING_DEPTH<CW> of the source: 5 slots for parts of up to 64 columns, else 4."""
+    return 5 if cw <= 64 else 4
+
+
+def test_source_constants_match_model():
+    src = open(SCAN).read()
+    assert re.search(r"RING_DEPTH\s*=\s*CW\s*<=\s*64\s*\?\s*5\s*:\s*4", src)
+    assert "wait_vm_barrier<(DEPTH - 1) * UNITS>()" in src
+    assert "wait_vm_barrier<(DEPTH - 2) * UNITS>()" in src
+
+
+@pytest.mark.parametrize("cw", [32, 64, 128])
+@pytest.mark.parametrize("nch", [0, 1, 2, 3, 4, 5, 7, 64])
+def test_dma_wait_ladder(cw, nch):
+    rec_kb = REC_BYTES // 1024
+    v_kb = CS * cw * 2 // 1024
+    units = rec_kb + v_kb
+    depth = ring_depth(cw)
+    assert (depth - 1) * units <= VMCNT_MAX
+
+    issued = []                      # chunk index of each issued load, in order
+    completed = 0                    # loads completed (a prefix of `issued`)
+
+    def issue(c):
+        issued.extend([c] * units)
+
+    def wait(n):
+        nonlocal completed
+        completed = max(completed, len(issued) - n)
+
+    def landed(c):                   # every load of chunk c has completed
+        return all(i < completed for i, x in enumerate(issued) if x == c)
+
+    reads_done = set()               # chunks the compute waves have read into registers
+    slot_of = {}
+
+    for c in range(depth):           # prologue: fill the ring
+        issue(c)
+        slot_of[c] = c
+    wait((depth - 1) * units)
+    assert landed(0)
+    reads_done.add(0)                # compute waves read chunk 0 after barrier B0
+    slot = 0
+    for c in range(nch):
+        wait((depth - 2) * units)    # top of iteration c
+        if c + 1 < nch + depth:
+            assert landed(c + 1), (cw, nch, c)
+        # barrier: the compute waves' reads of chunk c (issued in iteration
+        # c-1) are complete; they now read chunk c+1
+        assert c in reads_done
+        reads_done.add(c + 1)
+        # refill the slot chunk c occupied with chunk c + depth
+        assert slot_of[c] == slot
+        issue(c + depth)
+        slot_of[c + depth] = slot
+        # the slot being refilled holds no chunk the compute waves still need
+        assert all(x <= c for x, s in slot_of.items() if s == slot and x != c + depth)
+        slot = 0 if slot == depth - 1 else slot + 1
+    wait(0)                          # the final drain
+    assert completed == len(issued)
