@@ -172,3 +172,18 @@ def random_small(seed: int, B: int, T: int, H: int, K: int = 128, V: int = 128,
     d = generate(w)
     d["workload"] = w
     return d
+
+
+def output_grads(seed: int, B: int, T: int, H: int, V: int = HEAD_DIM, N: Optional[int] = None,
+                 K: int = HEAD_DIM, final: bool = True) -> tuple:
+    """Seeded incoming gradients for the backward pass: d_out ~ N(0, 1) cast
+    to bf16 [B, T, H, V] and, when `final`, d_final ~ N(0, 0.1) fp32
+    [N, H, K, V] (N defaults to B); drawn in that order from a torch CPU
+    generator seeded with `seed`."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    d_out = torch.randn(B, T, H, V, generator=gen).to(torch.bfloat16)
+    d_final = None
+    if final:
+        d_final = torch.randn(B if N is None else N, H, K, V, generator=gen) * 0.1
+    return d_out, d_final

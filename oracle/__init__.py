@@ -6,7 +6,9 @@ implementations of the same token recurrence:
 
   * kda_ref.kda_forward  - numpy, vectorised over heads (small sizes);
   * cref_forward         - the C/OpenMP version in kda_ref_cpu.c (full sizes,
-                           optionally a subset of heads).
+                           optionally a subset of heads);
+and the exact gradient of that recurrence, kda_ref_bwd.kda_backward (numpy,
+reverse-mode through the token steps; numpy_backward below).
 """
 from __future__ import annotations
 
@@ -16,6 +18,7 @@ import os
 import numpy as np
 
 from .kda_ref import gate_log_decay, kda_forward, sigmoid, softplus  # noqa: F401
+from .kda_ref_bwd import kda_backward  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda_ref.so")
@@ -110,3 +113,30 @@ def numpy_forward(inp: dict):
                        initial_state=f64(inp.get("initial_state")),
                        cu_seqlens=None if inp.get("cu_seqlens") is None
                        else inp["cu_seqlens"].numpy())
+
+
+def numpy_backward(inp: dict, d_out, d_final=None, heads=None, checkpoint: int = 64):
+    """Run the numpy gradient oracle on a generated input dict.
+
+    d_out: [B, T, H, V] tensor; d_final: [N, H, K, V] tensor or None.
+    heads: optional list of head indices (heads are independent); every
+    output then holds only those heads, in that order.
+    """
+    import torch
+
+    def f64(t):
+        return None if t is None else t.to(torch.float64).numpy()
+
+    H, K = inp["q"].shape[-2], inp["q"].shape[-1]
+    sel = list(range(H)) if heads is None else [int(h) for h in heads]
+    tok = lambda t: f64(t)[:, :, sel]
+    dtb = inp.get("dt_bias")
+    dtb = None if dtb is None else f64(dtb).reshape(H, K)[sel].reshape(-1)
+    init = inp.get("initial_state")
+    cu = inp.get("cu_seqlens")
+    return kda_backward(tok(inp["q"]), tok(inp["k"]), tok(inp["v"]), tok(inp["g"]),
+                        f64(inp["beta"])[:, :, sel], f64(inp["A_log"])[sel], dtb,
+                        float(inp["lower_bound"]), float(inp["scale"]), tok(d_out),
+                        d_final=None if d_final is None else f64(d_final)[:, sel],
+                        initial_state=None if init is None else f64(init)[:, sel],
+                        cu_seqlens=None if cu is None else cu.numpy(), checkpoint=checkpoint)
