@@ -167,6 +167,47 @@ kda_status_t kda_decode(const void *q, const void *k, const void *v, const void 
                         void *state, kda_dtype_t state_dtype, void *out,
                         int32_t N, int32_t H, int32_t K, int32_t V, void *stream);
 
+/*
+ * kda_bwd — the backward pass for training: gradients of the forward above
+ * with respect to every input.  The pages provide the forward only and leave
+ * training to another backend ("Moonshot AI Open-Sources FlashKDA", section
+ * "Limitations before you integrate"); this is the exact derivative of the
+ * forward kda_fwd computes, for the loss
+ *
+ *   L = <d_out, o> + <d_final_state, final_state>
+ *
+ * (no gradient flows through the clamped branch of the gate).
+ *
+ * Inputs (as kda_fwd, K = V = 128 only):
+ *   q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens,
+ *   num_seqs, initial_state (+ dtype), B, T, H, K, V
+ *   d_out          bf16 [B, T, H, V]   gradient reaching o
+ *   d_final_state  fp32 [N, H, K, V] or NULL (= zeros)
+ * Outputs (caller-allocated, fully written):
+ *   dq, dk, dg     bf16 [B, T, H, K]
+ *   dv             bf16 [B, T, H, V]
+ *   dbeta          bf16 [B, T, H]       gradient of the beta logits
+ *   dA_log         fp32 [H]
+ *   ddt_bias       fp32 [H*K] or NULL (not written)
+ *   d_initial_state fp32 [N, H, K, V] or NULL (not written)
+ *
+ * Arithmetic is fp32 throughout; every sum runs in a fixed order, so the
+ * results are bitwise reproducible.  Device workspace of about 157 KiB per
+ * (16-token chunk slot, head) comes from the library's stream-ordered pool
+ * (the fp32 chunk factors and every chunk's start state and state
+ * gradient).  Returns KDA_OK, KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED
+ * before any HIP call, KDA_ERR_OUT_OF_MEMORY, or KDA_ERR_LAUNCH.
+ */
+kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
+                     const void *beta, float scale,
+                     const float *A_log, const float *dt_bias, float lower_bound,
+                     const int32_t *cu_seqlens, int32_t num_seqs,
+                     const void *initial_state, kda_dtype_t initial_state_dtype,
+                     const void *d_out, const float *d_final_state,
+                     void *dq, void *dk, void *dv, void *dg, void *dbeta,
+                     float *dA_log, float *ddt_bias, float *d_initial_state,
+                     int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, void *stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *kda_status_string(kda_status_t status);
 

@@ -15,14 +15,18 @@ FlashKDA" (API paragraphs);
                            (the Gated DeltaNet case): g [B, T, H], dt_bias [H]
     decode(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, state)
 
-applies one new token per sequence to the recurrent state in place.
+applies one new token per sequence to the recurrent state in place;
+
+    bwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, d_out, ...)
+
+computes the gradients of the forward (training).
 """
 from __future__ import annotations
 
 import ctypes
 import os
 
-__all__ = ["fwd", "fwd_scalar_gate", "decode", "debug_intra", "set_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
+__all__ = ["fwd", "fwd_scalar_gate", "decode", "bwd", "debug_intra", "set_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
            "status_string", "KDAError", "library_path", "load", "HEAD_DIM"]
 
 HEAD_DIM = 128
@@ -73,6 +77,9 @@ def load():
     lib.kda_fwd_scalar_gate.argtypes = lib.kda_fwd.argtypes
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode.argtypes = [P, P, P, P, P, f32, P, P, f32, P, ctypes.c_int, P, i32, i32, i32, i32, P]
+    lib.kda_bwd.restype = ctypes.c_int
+    lib.kda_bwd.argtypes = [P, P, P, P, P, f32, P, P, f32, P, i32, P, ctypes.c_int, P, P,
+                            P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
     lib.kda_debug_intra.restype = ctypes.c_int
     lib.kda_debug_intra.argtypes = [P, P, P, P, P, P, f32, P, i32, i32, i32, i32, i32, P, P]
     _lib = lib
@@ -236,6 +243,58 @@ def decode(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, state):
     if rc != 0:
         raise KDAError(rc, "kda_decode")
     return out
+
+
+def bwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, d_out, dq, dk, dv, dg, dbeta,
+        dA_log, ddt_bias=None, initial_state=None, d_final_state=None, d_initial_state=None,
+        cu_seqlens=None):
+    """Gradients of L = <d_out, o> + <d_final_state, final_state> of the
+    forward with these inputs, written into the caller's tensors.
+
+    Inputs as fwd (K = V = 128); d_out: bf16 [B, T, H, V]; d_final_state:
+    fp32 [N, H, K, V] or None.  Outputs: dq, dk, dg bf16 [B, T, H, K]; dv
+    bf16 [B, T, H, V]; dbeta bf16 [B, T, H]; dA_log fp32 [H]; ddt_bias fp32
+    [H*K] or None; d_initial_state fp32 [N, H, K, V] or None.  Enqueued on
+    the current stream.
+    """
+    import torch
+    lib = load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, K]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    bf, f32 = torch.bfloat16, torch.float32
+    for t, name, shape in ((q, "q", None), (k, "k", q.shape), (g, "g", q.shape),
+                           (v, "v", (B, T, H, V)), (beta, "beta", (B, T, H)),
+                           (d_out, "d_out", (B, T, H, V)), (dq, "dq", q.shape),
+                           (dk, "dk", q.shape), (dg, "dg", q.shape), (dv, "dv", (B, T, H, V)),
+                           (dbeta, "dbeta", (B, T, H))):
+        _check(t, name, bf, shape)
+    _check(A_log, "A_log", f32, (H,))
+    _check(dA_log, "dA_log", f32, (H,))
+    for t, name in ((dt_bias, "dt_bias"), (ddt_bias, "ddt_bias")):
+        if t is not None:
+            _check(t, name, f32, (H * K,))
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    init_dt = KDA_DTYPE_FP32
+    if initial_state is not None:
+        init_dt = _state_dtype(initial_state)
+        _check(initial_state, "initial_state", initial_state.dtype, (N, H, K, V))
+    for t, name in ((d_final_state, "d_final_state"), (d_initial_state, "d_initial_state")):
+        if t is not None:
+            _check(t, name, f32, (N, H, K, V))
+    rc = lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(A_log),
+                     _ptr(dt_bias), float(lower_bound), _ptr(cu_seqlens), int(N),
+                     _ptr(initial_state), init_dt, _ptr(d_out), _ptr(d_final_state),
+                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dA_log),
+                     _ptr(ddt_bias), _ptr(d_initial_state), int(B), int(T), int(H), int(K),
+                     int(V), _stream(q.device))
+    if rc != 0:
+        raise KDAError(rc, "kda_bwd")
 
 
 def set_stage_events(before_intra=None, before_scan=None, after_scan=None):

@@ -245,6 +245,58 @@ kda_status_t kda_decode(const void *q, const void *k, const void *v, const void 
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
+                     const void *beta, float scale,
+                     const float *A_log, const float *dt_bias, float lower_bound,
+                     const int32_t *cu_seqlens, int32_t num_seqs,
+                     const void *initial_state, kda_dtype_t initial_state_dtype,
+                     const void *d_out, const float *d_final_state,
+                     void *dq, void *dk, void *dv, void *dg, void *dbeta,
+                     float *dA_log, float *ddt_bias, float *d_initial_state,
+                     int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, void *stream)
+{
+    const bool no_tokens = (int64_t)B * T == 0;
+    if (!A_log || !dA_log) return KDA_ERR_INVALID_ARG;
+    if (!no_tokens && (!q || !k || !v || !g || !beta || !d_out || !dq || !dk || !dv || !dg ||
+                       !dbeta))
+        return KDA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) ||
+        !aligned(d_out, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        !aligned(dg, 16) || !aligned(beta, 2) || !aligned(dbeta, 2) || !aligned(A_log, 4) ||
+        !aligned(dt_bias, 4) || !aligned(dA_log, 4) || !aligned(ddt_bias, 4) ||
+        !aligned(cu_seqlens, 4) || !aligned(initial_state, 16) ||
+        !aligned(d_final_state, 16) || !aligned(d_initial_state, 16))
+        return KDA_ERR_INVALID_ARG;
+    if (initial_state_dtype != KDA_DTYPE_BF16 && initial_state_dtype != KDA_DTYPE_FP32)
+        return KDA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    kda_status_t st = check_sizes(B, T, H, K, V, cu_seqlens, num_seqs);
+    if (st != KDA_OK) return st;
+    if (K != kda::HD) return KDA_ERR_UNSUPPORTED;          // the backward runs K = V = 128 only
+    if ((st = check_gate(lower_bound)) != KDA_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t slots = num_slots(B, T, num_seqs);
+    const size_t bytes = kda::bwd_workspace_bytes(slots, H);
+    hipMemPool_t pool;
+    if ((st = device_pool(&pool)) != KDA_OK) return st;
+    void *ws = nullptr;
+    if (hipMallocFromPoolAsync(&ws, bytes, pool, s) != hipSuccess || !ws) {
+        (void)hipGetLastError();
+        return KDA_ERR_OUT_OF_MEMORY;
+    }
+    hipError_t e = kda::launch_bwd((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v,
+                                   (const uint16_t *)g, (const uint16_t *)beta, scale, A_log,
+                                   dt_bias, lower_bound, cu_seqlens, num_seqs, T, H, slots,
+                                   initial_state, initial_state_dtype == KDA_DTYPE_FP32,
+                                   (const uint16_t *)d_out, d_final_state, (uint16_t *)dq,
+                                   (uint16_t *)dk, (uint16_t *)dv, (uint16_t *)dg,
+                                   (uint16_t *)dbeta, dA_log, ddt_bias, d_initial_state, ws, s);
+    hipError_t ef = hipFreeAsync(ws, s);
+    if (e != hipSuccess || ef != hipSuccess) return KDA_ERR_LAUNCH;
+    return KDA_OK;
+}
+
 kda_status_t kda_set_stage_events(void *before_intra, void *before_scan, void *after_scan) {
     t_stage_events[0] = (hipEvent_t)before_intra;
     t_stage_events[1] = (hipEvent_t)before_scan;

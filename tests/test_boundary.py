@@ -160,3 +160,32 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(mod, "library_path", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         mod.load()
+
+
+def call_bwd(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=0.088, A_log=FAKE, dt_bias=None,
+             lb=-5.0, cu=None, N=1, init=None, init_dt=0, dout=FAKE, dfin=None,
+             dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, dbeta=FAKE, dA_log=FAKE, ddtb=None, dinit=None,
+             B=1, T=32, H=2, K=128, V=128)
+    a.update(over)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.kda_bwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]), a["scale"],
+                       P(a["A_log"]), P(a["dt_bias"]), a["lb"], P(a["cu"]), a["N"],
+                       P(a["init"]), a["init_dt"], P(a["dout"]), P(a["dfin"]),
+                       P(a["dq"]), P(a["dk"]), P(a["dv"]), P(a["dg"]), P(a["dbeta"]),
+                       P(a["dA_log"]), P(a["ddtb"]), P(a["dinit"]),
+                       a["B"], a["T"], a["H"], a["K"], a["V"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), INVALID), (dict(dout=None), INVALID), (dict(dq=None), INVALID),
+    (dict(dbeta=None), INVALID), (dict(dA_log=None), INVALID), (dict(A_log=None), INVALID),
+    (dict(dk=FAKE + 8), INVALID), (dict(dinit=FAKE + 4), INVALID), (dict(dfin=FAKE + 4), INVALID),
+    (dict(ddtb=FAKE + 2), INVALID), (dict(init_dt=5), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(lb=0.5), INVALID), (dict(lb=-6.0), UNSUPPORTED),
+    (dict(K=64, V=64), UNSUPPORTED), (dict(K=256, V=256), UNSUPPORTED), (dict(V=64), UNSUPPORTED),
+    (dict(N=2), INVALID), (dict(cu=FAKE, B=2, N=2), INVALID), (dict(H=0), INVALID),
+    (dict(T=2 ** 26, H=1024), UNSUPPORTED),
+])
+def test_bwd_rejects_before_any_hip_call(lib, over, code):
+    assert call_bwd(lib, **over) == code
