@@ -21,6 +21,12 @@ the same workload with g [B, T, H] and dt_bias [H]: g then moves 2 B per
 
 `--head-dim 64` measures the same workload at K = V = 64.
 
+`--backward` measures the backward pass (kda_bwd, five kernels) on the same
+workload: gradients of every input for an incoming bf16 d_out and fp32
+d_final_state.  Algorithmic bytes per (token, head): q, k, v, g, beta, d_out
+read and dq, dk, dv, dg, dbeta written (2308 B); per (sequence, head): the
+initial state and d_final_state read, the initial-state gradient written.
+
 `--decode-batch N` instead measures the decode step (kda_decode, one kernel
 on the current stream): N one-token sequences x H heads with an fp32 state
 updated in place, algorithmic bytes per (sequence, head) = the state read and
@@ -151,6 +157,101 @@ def bench_decode(args, torch, kda, kda_inputs):
     print(json.dumps(rec), flush=True)
 
 
+def bench_backward(args, torch, kda, kda_inputs):
+    """One step = one kda_bwd call over the workload (all five kernels)."""
+    name = args.workload or kda_inputs.HEADLINE
+    w = kda_inputs.WORKLOADS[name]
+    log(f"[bench] backward: generating {name} ...")
+    inp = kda_inputs.generate(w)
+    d_out, d_final = kda_inputs.output_grads(w.seed + 1, w.B, w.T, w.H, N=w.num_seqs)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    dO, dF = d_out.to(dev), d_final.to(dev)
+    bf = torch.bfloat16
+    shp = (w.B, w.T, w.H, w.K)
+    dq, dk, dg = (torch.empty(shp, dtype=bf, device=dev) for _ in range(3))
+    dv = torch.empty(w.B, w.T, w.H, w.V, dtype=bf, device=dev)
+    dbeta = torch.empty(w.B, w.T, w.H, dtype=bf, device=dev)
+    dA = torch.empty(w.H, device=dev)
+    ddtb = torch.empty(w.H * w.K, device=dev)
+    dinit = torch.empty(w.num_seqs, w.H, w.K, w.V, device=dev)
+
+    def step():
+        kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], d["A_log"], d["dt_bias"],
+                d["lower_bound"], dO, dq, dk, dv, dg, dbeta, dA, ddt_bias=ddtb,
+                initial_state=d["initial_state"], d_final_state=dF, d_initial_state=dinit,
+                cu_seqlens=d["cu_seqlens"])
+
+    log(f"[bench] backward warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    names = ["kda_bwd_prep", "kda_bwd_states", "kda_bwd_dstates", "kda_bwd_chunk", "kda_bwd_reduce"]
+    evs = []
+    for _ in range(args.steps):
+        six = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for e in six:
+            e.record()
+        evs.append(six)
+    torch.cuda.synchronize()
+    log(f"[bench] backward timing {args.steps} steps")
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        kda.set_bwd_stage_events([e.cuda_event for e in evs[i]])
+        step()
+    kda.set_bwd_stage_events(None)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    stage = {n: statistics.mean(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps))
+             for j, n in enumerate(names)}
+
+    # algorithmic bytes: per (token, head) the inputs q, k, v, g, beta and
+    # d_out read once and dq, dk, dv, dg, dbeta written once (2308 B); per
+    # (sequence, head) the initial state, d_final read and the initial-state
+    # gradient written.  Per kernel, the part of that each kernel must move.
+    th, units = w.tokens * w.H, w.num_seqs * w.H
+    st_in = units * w.K * w.V * 2 if w.initial_state else 0
+    st32 = units * w.K * w.V * 4
+    kb = {"kda_bwd_prep": th * 770, "kda_bwd_states": th * 256 + st_in,
+          "kda_bwd_dstates": th * 512 + 2 * st32, "kda_bwd_chunk": th * (1282 + 770),
+          "kda_bwd_reduce": 0}
+    total_bytes = th * 2308 + st_in + 2 * st32
+    dom = max(names, key=lambda n: stage[n])
+    achieved = kb[dom] / (stage[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
+                "bytes_per_launch": kb[dom], "avg_launch_ms": stage[dom]}
+    path_gbs = total_bytes / (ms * 1e-3) / 1e9
+    path = {"algorithmic_bytes": total_bytes, "hbm_achieved_GBs": path_gbs,
+            "hbm_frac": path_gbs / HBM_PEAK_GBS, "stage_ms": stage,
+            "workspace_bytes": int(w.H * (w.tokens // CHUNK + w.num_seqs) * 4 *
+                                   (3 * CHUNK * w.K + CHUNK * CHUNK + w.K + 2 * w.K * w.V + 1 + w.K))}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        heads = list(range(min(2, w.H)))
+        log(f"[bench] gradient oracle CPU baseline on heads {heads}")
+        t0 = time.perf_counter()
+        oracle.numpy_backward(inp, d_out, d_final, heads=heads)
+        dt = time.perf_counter() - t0
+        cpu = {"value": w.tokens / (dt * w.H / len(heads)), "unit": "tokens/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{w.name}: heads {heads[0]}..{heads[-1]} of {w.H}, all {w.tokens} "
+                         f"tokens, fp64 numpy reverse-mode token recurrence, {dt:.2f} s wall"}
+    rec = {"metric": f"KDA bwd tokens/s @T={w.T},H={w.H},D={w.K} (gradients of every input)",
+           "value": w.tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+           "data": "synthetic (seeded; shapes of the pages' workloads)",
+           "config": dict(w.describe(), d_out="bf16", d_final_state="fp32"),
+           "roofline": roofline, "cpu_baseline": cpu, "path": path}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +267,8 @@ def main():
     ap.add_argument("--decode-batch", type=int, default=0, metavar="N",
                     help="measure the decode step on N one-token sequences instead")
     ap.add_argument("--decode-heads", type=int, default=96)
+    ap.add_argument("--backward", action="store_true",
+                    help="measure the backward pass (kda_bwd) on the workload instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times): the "
                          "reference kernel for scaling the HBM byte counters")
@@ -195,6 +298,9 @@ def main():
     kda.load()
     if args.decode_batch:
         bench_decode(args, torch, kda, kda_inputs)
+        return
+    if args.backward:
+        bench_backward(args, torch, kda, kda_inputs)
         return
     name = args.workload or kda_inputs.HEADLINE
     w = kda_inputs.WORKLOADS[name]

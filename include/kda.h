@@ -254,6 +254,15 @@ kda_status_t kda_debug_intra(const void *q, const void *k, const void *g,
  */
 kda_status_t kda_set_stage_events(void *before_intra, void *before_scan, void *after_scan);
 
+/*
+ * kda_set_bwd_stage_events — the same instrumentation for kda_bwd: `events`
+ * is NULL (stop) or an array of six hipEvent_t handles, recorded on the
+ * call's stream before each of the five backward kernels (prep, states,
+ * dstates, chunk, reduce) and after the last.  Per host thread; the array is
+ * read at this call and the events are not owned.  Always returns KDA_OK.
+ */
+kda_status_t kda_set_bwd_stage_events(void *const *events);
+
 #ifdef __cplusplus
 }
 #endif

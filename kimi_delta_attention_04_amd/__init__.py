@@ -26,7 +26,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "fwd_scalar_gate", "decode", "bwd", "debug_intra", "set_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
+__all__ = ["fwd", "fwd_scalar_gate", "decode", "bwd", "debug_intra", "set_stage_events", "set_bwd_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
            "status_string", "KDAError", "library_path", "load", "HEAD_DIM"]
 
 HEAD_DIM = 128
@@ -77,6 +77,8 @@ def load():
     lib.kda_fwd_scalar_gate.argtypes = lib.kda_fwd.argtypes
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode.argtypes = [P, P, P, P, P, f32, P, P, f32, P, ctypes.c_int, P, i32, i32, i32, i32, P]
+    lib.kda_set_bwd_stage_events.restype = ctypes.c_int
+    lib.kda_set_bwd_stage_events.argtypes = [P]
     lib.kda_bwd.restype = ctypes.c_int
     lib.kda_bwd.argtypes = [P, P, P, P, P, f32, P, P, f32, P, i32, P, ctypes.c_int, P, P,
                             P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
@@ -295,6 +297,17 @@ def bwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, d_out, dq, dk, dv,
                      int(V), _stream(q.device))
     if rc != 0:
         raise KDAError(rc, "kda_bwd")
+
+
+def set_bwd_stage_events(events=None):
+    """Six raw hipEvent_t handles (ints) recorded around the five backward
+    kernels by the next kda_bwd calls from this thread; None to stop."""
+    lib = load()
+    if events is None:
+        lib.kda_set_bwd_stage_events(None)
+        return
+    arr = (ctypes.c_void_p * 6)(*[int(e) for e in events])
+    lib.kda_set_bwd_stage_events(ctypes.cast(arr, ctypes.c_void_p))
 
 
 def set_stage_events(before_intra=None, before_scan=None, after_scan=None):

@@ -49,6 +49,7 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Optional per-thread stage events (kda_set_stage_events).
 thread_local hipEvent_t t_stage_events[3] = {nullptr, nullptr, nullptr};
+thread_local hipEvent_t t_bwd_events[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
 
 hipError_t mark(int i, hipStream_t s) {
     return t_stage_events[i] ? hipEventRecord(t_stage_events[i], s) : hipSuccess;
@@ -291,9 +292,15 @@ kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
                                    initial_state, initial_state_dtype == KDA_DTYPE_FP32,
                                    (const uint16_t *)d_out, d_final_state, (uint16_t *)dq,
                                    (uint16_t *)dk, (uint16_t *)dv, (uint16_t *)dg,
-                                   (uint16_t *)dbeta, dA_log, ddt_bias, d_initial_state, ws, s);
+                                   (uint16_t *)dbeta, dA_log, ddt_bias, d_initial_state, ws, s,
+                                   t_bwd_events);
     hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess || ef != hipSuccess) return KDA_ERR_LAUNCH;
+    return KDA_OK;
+}
+
+kda_status_t kda_set_bwd_stage_events(void *const *events) {
+    for (int i = 0; i < 6; ++i) t_bwd_events[i] = events ? (hipEvent_t)events[i] : nullptr;
     return KDA_OK;
 }
 

@@ -25,12 +25,13 @@
 //
 // Five launches, all fp32 arithmetic:
 //   prep    (chunk slot, head)  the chunk factors Kt, Qt, Wm, M, Gam -> workspace
-//   states  (sequence, head, 32-column part)  forward scan storing every
-//           chunk's start state S0
-//   dstates (sequence, head, 32-column part)  reverse scan of dS, storing
-//           every chunk's dS1, writing dv and the initial-state gradient
-//   chunk   (chunk slot, head)  the products with S0 / dS1 and the in-chunk
-//           backward: dq, dk, dg, dbeta, per-chunk dA_log / ddt_bias sums
+//   states  (sequence, head, 16-column part)  forward scan storing every
+//           chunk's start state S0 and X
+//   dstates (sequence, head, 16-column part)  reverse scan of dS, storing
+//           every chunk's dS1 and dX, writing dv and the initial-state gradient
+//   chunk   (chunk slot, head)  the products with S0 / dS1 (fp32 MFMA) and
+//           the in-chunk backward: dq, dk, dg, dbeta, per-chunk dA_log /
+//           ddt_bias sums
 //   reduce  (head)  sums the per-chunk parameter gradients in slot order
 // Every sum runs in a fixed order, so results are bitwise reproducible.
 #include <math.h>
@@ -45,12 +46,15 @@ namespace {
 constexpr int BT = 256;               // threads per workgroup
 constexpr int RS = HD + 4;            // padded LDS row stride (floats)
 constexpr int SP = CS + 1;            // padded stride of 16 x 16 tiles
-constexpr int CWB = 32;               // state columns per scan workgroup
+constexpr int CWB = 16;               // state columns per scan workgroup
 constexpr int NPART = HD / CWB;
-constexpr int NRG = BT / CWB;         // row groups of 16 state rows
-static_assert(NRG * 16 == HD, "row groups cover the state rows");
+constexpr int NRG = BT / CWB;         // row groups of the state rows
+constexpr int RPT = HD / NRG;         // state rows per thread
+static_assert(NRG == CS && NRG * RPT == HD, "row groups cover the state rows, one per token row");
 
-// Chunk-factor record, fp32, per (chunk slot, head).
+// Chunk-factor record, fp32, per (chunk slot, head): Kt, Qt and Wm
+// transposed ([channel][token], 16 floats per channel), M [16][16] and
+// e^{G_last} [128].
 constexpr int BR_KT = 0;
 constexpr int BR_QT = CS * HD;
 constexpr int BR_WM = 2 * CS * HD;
@@ -138,13 +142,20 @@ __device__ void chunk_factors(Factors &L, const uint16_t *__restrict__ q,
     }
     __syncthreads();
     if (tid < CS) {
-        // column i of T = (I + diag(beta) A)^-1 by forward substitution
+        // column i of T = (I + diag(beta) A)^-1 by forward substitution, in
+        // registers (entries above the diagonal come out zero)
         const int i = tid;
+        float x[CS];
+#pragma unroll
         for (int r = 0; r < CS; ++r) {
             float acc = r == i ? 1.f : 0.f;
-            for (int s = i; s < r; ++s) acc -= L.beta[r] * L.A[r][s] * L.T[s][i];
-            L.T[r][i] = acc;
+            const float br = L.beta[r];
+#pragma unroll
+            for (int s = 0; s < r; ++s) acc -= br * L.A[r][s] * x[s];
+            x[r] = acc;
         }
+#pragma unroll
+        for (int r = 0; r < CS; ++r) L.T[r][i] = x[r];
     }
     __syncthreads();
     {
@@ -187,7 +198,7 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(
     float *rec = brec + ((size_t)slot * H + h) * BR_FLOATS;
     const int tid = threadIdx.x;
     for (int idx = tid; idx < CS * HD; idx += BT) {
-        const int r = idx / HD, c = idx % HD;
+        const int c = idx / CS, r = idx % CS;
         rec[BR_KT + idx] = L.kt[r][c];
         rec[BR_QT + idx] = L.qt[r][c];
         rec[BR_WM + idx] = L.wm[r][c];
@@ -197,16 +208,49 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// states: forward scan per (sequence, head, 32-column part) that stores each
-// chunk's start state S0 (fp32 [slot][head][K][V]).  Thread t holds column
-// t % 32 of the part and rows 16 (t / 32) .. +15 of the state.
+// The two scans run one workgroup per (sequence, head, 16-column part).
+// Thread t holds column t % 16 of the part and the 8 state rows
+// t / 16 + 16 i (i = 0..7) in registers.  The next chunk's factors are
+// loaded into registers while the current chunk computes (software
+// pipelining).  The factors are kept transposed ([channel][token]) in LDS,
+// so a thread reads the 16 token values of each of its rows as four 16-byte
+// vectors.
+//
+// Stored states (S0 and dS1 of every chunk) are part-major: per (slot,
+// head) [part][K][16] fp32, so a wave's store of one register row is 256
+// contiguous bytes.  X and dX of every chunk are stored as [16][V] fp32.
+// ---------------------------------------------------------------------------
+// A 16 x 128 factor block is two 16-byte loads per thread; the prefetched
+// values live in named registers (no local arrays, which the compiler may
+// place in scratch memory).
+__device__ __forceinline__ void fetch_block(float4 &d0, float4 &d1, const float *__restrict__ src) {
+    d0 = *(const float4 *)&src[4 * threadIdx.x];
+    d1 = *(const float4 *)&src[4 * (threadIdx.x + BT)];
+}
+
+// [128][16] transposed factor block (as stored in the record) into LDS
+__device__ __forceinline__ void put_cols(float (&dst)[HD][CS], const float4 &d0, const float4 &d1) {
+    const int e0 = 4 * threadIdx.x, e1 = 4 * (threadIdx.x + BT);
+    *(float4 *)&dst[e0 / CS][e0 % CS] = d0;
+    *(float4 *)&dst[e1 / CS][e1 % CS] = d1;
+}
+
+__device__ __forceinline__ size_t state_off(int part, int c, int j) {
+    return ((size_t)part * HD + c) * CWB + j;
+}
+
+// ---------------------------------------------------------------------------
+// states: forward scan that stores each chunk's start state S0 and X.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(BT) void bwd_states_kernel(
     const uint16_t *__restrict__ v, const float *__restrict__ brec,
     const int32_t *__restrict__ cu, int N, int T, int H,
-    const void *__restrict__ init, int init_fp32, float *__restrict__ st0)
+    const void *__restrict__ init, int init_fp32, float *__restrict__ st0,
+    float *__restrict__ xws)
 {
-    __shared__ float kt[CS][HD], wm[CS][HD], gam[HD];
+    __shared__ __attribute__((aligned(16))) float ktT[HD][CS];
+    __shared__ __attribute__((aligned(16))) float wmT[HD][CS];
+    __shared__ __attribute__((aligned(16))) float gam[HD];
     __shared__ float vv[CS][CWB], xs[CS][CWB], xp[NRG][CS][CWB];
     const int unit = blockIdx.x;
     const int part = unit % NPART, nh = unit / NPART;
@@ -215,10 +259,10 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(
     const int col = part * CWB + j;
     const size_t sbase = ((size_t)n * H + h) * HD * HD;
 
-    float s[16];
+    float s[RPT];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const size_t idx = sbase + (size_t)(rg * 16 + i) * HD + col;
+    for (int i = 0; i < RPT; ++i) {
+        const size_t idx = sbase + (size_t)(rg + NRG * i) * HD + col;
         s[i] = !init ? 0.f : init_fp32 ? ((const float *)init)[idx]
                                        : bf16f(((const uint16_t *)init)[idx]);
     }
@@ -226,63 +270,99 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(
     seq_range(cu, n, T, start, end);
     const int nch = (int)((end - start + CS - 1) / CS);
     const int64_t slot0 = seq_slot0(cu, n, T);
+
+    // next chunk's Kt^T, Wm^T, e^{G_last} and v element, in flight
+    // (the v element is loaded raw from a clamped row and masked at use, so
+    // no branch forces a wait on the loads in flight)
+    float4 pa0, pa1, pb0, pb1, pg = {0.f, 0.f, 0.f, 0.f};
+    uint16_t pd = 0;
+    bool pvalid = false;
+#define KDA_STATES_FETCH(ci_)                                                                 \
+    do {                                                                                      \
+        const float *rec_ = brec + ((size_t)(slot0 + (ci_)) * H + h) * BR_FLOATS;             \
+        fetch_block(pa0, pa1, rec_ + BR_KT);                                                  \
+        fetch_block(pb0, pb1, rec_ + BR_WM);                                                  \
+        if (tid < HD / 4) pg = *(const float4 *)&rec_[BR_GAM + 4 * tid];                      \
+        const int64_t tr_ = start + (int64_t)(ci_) * CS + tid / CWB;                          \
+        pvalid = tr_ < end;                                                                   \
+        pd = v[((size_t)min(tr_, end - 1) * H + h) * HD + col];                               \
+    } while (0)
+    if (nch > 0) KDA_STATES_FETCH(0);
     for (int ci = 0; ci < nch; ++ci) {
-        const int64_t slot = slot0 + ci;
-        const float *rec = brec + ((size_t)slot * H + h) * BR_FLOATS;
-        float *dst = st0 + ((size_t)slot * H + h) * HD * HD;
+        const size_t sh = (size_t)(slot0 + ci) * H + h;
+        float *dst = st0 + sh * HD * HD;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dst[(size_t)(rg * 16 + i) * HD + col] = s[i];
-        const int64_t t0 = start + (int64_t)ci * CS;
-        const int len = (int)min((int64_t)CS, end - t0);
-        __syncthreads();                                    // last chunk's readers are done
-        for (int idx = tid; idx < CS * HD; idx += BT) {
-            kt[idx / HD][idx % HD] = rec[BR_KT + idx];
-            wm[idx / HD][idx % HD] = rec[BR_WM + idx];
-        }
-        if (tid < HD) gam[tid] = rec[BR_GAM + tid];
-        for (int idx = tid; idx < CS * CWB; idx += BT) {
-            const int r = idx / CWB, jj = idx % CWB;
-            vv[r][jj] = r < len ? bf16f(v[((size_t)(t0 + r) * H + h) * HD + part * CWB + jj]) : 0.f;
-        }
+        for (int i = 0; i < RPT; ++i) dst[state_off(part, rg + NRG * i, j)] = s[i];
+        __syncthreads();                                // last chunk's readers are done
+        put_cols(ktT, pa0, pa1);
+        put_cols(wmT, pb0, pb1);
+        if (tid < HD / 4) *(float4 *)&gam[4 * tid] = pg;
+        vv[tid / CWB][j] = pvalid ? bf16f(pd) : 0.f;
+        if (ci + 1 < nch) KDA_STATES_FETCH(ci + 1);     // in flight during this chunk
         __syncthreads();
-        // X = V - Kt S0: partial sums over this thread's 16 rows
-        for (int r = 0; r < CS; ++r) {
-            float p = 0.f;
+        // X = V - Kt S0: partial sums over this thread's rows
+        {
+            float p[CS];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) p += kt[r][rg * 16 + i] * s[i];
-            xp[rg][r][j] = p;
+            for (int r = 0; r < CS; ++r) p[r] = 0.f;
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int c = rg + NRG * i;
+#pragma unroll
+                for (int r = 0; r < CS; r += 4) {
+                    const float4 k4 = *(const float4 *)&ktT[c][r];
+                    p[r] += k4.x * s[i];
+                    p[r + 1] += k4.y * s[i];
+                    p[r + 2] += k4.z * s[i];
+                    p[r + 3] += k4.w * s[i];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < CS; ++r) xp[rg][r][j] = p[r];
         }
         __syncthreads();
-        for (int m = 0; m < 2; ++m) {
-            const int r = 2 * rg + m;
-            float x = vv[r][j];
-            for (int gq = 0; gq < NRG; ++gq) x -= xp[gq][r][j];
-            xs[r][j] = x;
+        {
+            float x = vv[rg][j];                        // row rg (NRG == CS)
+#pragma unroll
+            for (int gq = 0; gq < NRG; ++gq) x -= xp[gq][rg][j];
+            xs[rg][j] = x;
+            xws[sh * CS * HD + (size_t)rg * HD + col] = x;
         }
         __syncthreads();
+        float xr[CS];
+#pragma unroll
+        for (int r = 0; r < CS; ++r) xr[r] = xs[r][j];
         // S1 = Gam S0 + Wm^T X
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int c = rg * 16 + i;
+        for (int i = 0; i < RPT; ++i) {
+            const int c = rg + NRG * i;
             float acc = gam[c] * s[i];
-            for (int r = 0; r < CS; ++r) acc += wm[r][c] * xs[r][j];
+#pragma unroll
+            for (int r = 0; r < CS; r += 4) {
+                const float4 w4 = *(const float4 *)&wmT[c][r];
+                acc += w4.x * xr[r] + w4.y * xr[r + 1] + w4.z * xr[r + 2] + w4.w * xr[r + 3];
+            }
             s[i] = acc;
         }
     }
+#undef KDA_STATES_FETCH
 }
 
 // ---------------------------------------------------------------------------
-// dstates: reverse scan per (sequence, head, 32-column part) of the state
-// gradient.  Stores dS1 of every chunk (fp32 [slot][head][K][V]), writes dv
-// and, at the sequence start, the initial-state gradient.
+// dstates: reverse scan of the state gradient.  Stores dS1 and dX of every
+// chunk, writes dv and, at the sequence start, the initial-state gradient.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
     const uint16_t *__restrict__ dout, const float *__restrict__ brec,
     const int32_t *__restrict__ cu, int N, int T, int H, float scale,
-    const float *__restrict__ dfin, float *__restrict__ dst1, uint16_t *__restrict__ dv,
-    float *__restrict__ dinit)
+    const float *__restrict__ dfin, float *__restrict__ dst1, float *__restrict__ dxws,
+    uint16_t *__restrict__ dv, float *__restrict__ dinit)
 {
-    __shared__ float kt[CS][HD], qt[CS][HD], wm[CS][HD], gam[HD], Ml[CS][SP];
+    __shared__ __attribute__((aligned(16))) float wmT[HD][CS];
+    __shared__ __attribute__((aligned(16))) float ktT[HD][CS];
+    __shared__ __attribute__((aligned(16))) float qtT[HD][CS];
+    __shared__ __attribute__((aligned(16))) float gam[HD];
+    __shared__ __attribute__((aligned(16))) float Ml[CS][CS];
     __shared__ float dol[CS][CWB], dxs[CS][CWB], xp[NRG][CS][CWB];
     const int unit = blockIdx.x;
     const int part = unit % NPART, nh = unit / NPART;
@@ -291,66 +371,108 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
     const int col = part * CWB + j;
     const size_t sbase = ((size_t)n * H + h) * HD * HD;
 
-    float ds[16];
+    float ds[RPT];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        ds[i] = dfin ? dfin[sbase + (size_t)(rg * 16 + i) * HD + col] : 0.f;
+    for (int i = 0; i < RPT; ++i)
+        ds[i] = dfin ? dfin[sbase + (size_t)(rg + NRG * i) * HD + col] : 0.f;
     int64_t start, end;
     seq_range(cu, n, T, start, end);
     const int nch = (int)((end - start + CS - 1) / CS);
     const int64_t slot0 = seq_slot0(cu, n, T);
+
+    // next chunk's Kt^T, Qt^T, Wm^T, M, e^{G_last} and dO element, in flight
+    float4 pa0, pa1, pb0, pb1, pc0, pc1;
+    float4 pm = {0.f, 0.f, 0.f, 0.f}, pg = {0.f, 0.f, 0.f, 0.f};
+    uint16_t pd = 0;
+    bool pvalid = false;
+#define KDA_DSTATES_FETCH(ci_)                                                                \
+    do {                                                                                      \
+        const float *rec_ = brec + ((size_t)(slot0 + (ci_)) * H + h) * BR_FLOATS;             \
+        fetch_block(pa0, pa1, rec_ + BR_KT);                                                  \
+        fetch_block(pb0, pb1, rec_ + BR_QT);                                                  \
+        fetch_block(pc0, pc1, rec_ + BR_WM);                                                  \
+        if (tid < CS * CS / 4) pm = *(const float4 *)&rec_[BR_M + 4 * tid];                   \
+        if (tid < HD / 4) pg = *(const float4 *)&rec_[BR_GAM + 4 * tid];                      \
+        const int64_t tr_ = start + (int64_t)(ci_) * CS + tid / CWB;                          \
+        pvalid = tr_ < end;                                                                   \
+        pd = dout[((size_t)min(tr_, end - 1) * H + h) * HD + col];                            \
+    } while (0)
+    if (nch > 0) KDA_DSTATES_FETCH(nch - 1);
     for (int ci = nch - 1; ci >= 0; --ci) {
-        const int64_t slot = slot0 + ci;
-        const float *rec = brec + ((size_t)slot * H + h) * BR_FLOATS;
-        float *dst = dst1 + ((size_t)slot * H + h) * HD * HD;
+        const size_t sh = (size_t)(slot0 + ci) * H + h;
+        float *dst = dst1 + sh * HD * HD;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dst[(size_t)(rg * 16 + i) * HD + col] = ds[i];
+        for (int i = 0; i < RPT; ++i) dst[state_off(part, rg + NRG * i, j)] = ds[i];
         const int64_t t0 = start + (int64_t)ci * CS;
         const int len = (int)min((int64_t)CS, end - t0);
         __syncthreads();
-        for (int idx = tid; idx < CS * HD; idx += BT) {
-            kt[idx / HD][idx % HD] = rec[BR_KT + idx];
-            qt[idx / HD][idx % HD] = rec[BR_QT + idx];
-            wm[idx / HD][idx % HD] = rec[BR_WM + idx];
-        }
-        Ml[tid >> 4][tid & 15] = rec[BR_M + tid];
-        if (tid < HD) gam[tid] = rec[BR_GAM + tid];
-        for (int idx = tid; idx < CS * CWB; idx += BT) {
-            const int r = idx / CWB, jj = idx % CWB;
-            dol[r][jj] = r < len
-                ? scale * bf16f(dout[((size_t)(t0 + r) * H + h) * HD + part * CWB + jj]) : 0.f;
-        }
+        put_cols(ktT, pa0, pa1);
+        put_cols(qtT, pb0, pb1);
+        put_cols(wmT, pc0, pc1);
+        if (tid < CS * CS / 4) *(float4 *)&Ml[(4 * tid) / CS][(4 * tid) % CS] = pm;
+        if (tid < HD / 4) *(float4 *)&gam[4 * tid] = pg;
+        dol[tid / CWB][j] = pvalid ? scale * bf16f(pd) : 0.f;
+        if (ci > 0) KDA_DSTATES_FETCH(ci - 1);          // in flight during this chunk
         __syncthreads();
         // dX = scale M^T dO + Wm dS1: partial sums of Wm dS1 over this thread's rows
-        for (int r = 0; r < CS; ++r) {
-            float p = 0.f;
+        {
+            float p[CS];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) p += wm[r][rg * 16 + i] * ds[i];
-            xp[rg][r][j] = p;
+            for (int r = 0; r < CS; ++r) p[r] = 0.f;
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int c = rg + NRG * i;
+#pragma unroll
+                for (int r = 0; r < CS; r += 4) {
+                    const float4 w4 = *(const float4 *)&wmT[c][r];
+                    p[r] += w4.x * ds[i];
+                    p[r + 1] += w4.y * ds[i];
+                    p[r + 2] += w4.z * ds[i];
+                    p[r + 3] += w4.w * ds[i];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < CS; ++r) xp[rg][r][j] = p[r];
         }
         __syncthreads();
-        for (int m = 0; m < 2; ++m) {
-            const int r = 2 * rg + m;
+        {
+            const int r = rg;                           // NRG == CS
             float x = 0.f;
+#pragma unroll
             for (int sr = 0; sr < CS; ++sr) x += Ml[sr][r] * dol[sr][j];
+#pragma unroll
             for (int gq = 0; gq < NRG; ++gq) x += xp[gq][r][j];
             dxs[r][j] = x;
+            dxws[sh * CS * HD + (size_t)r * HD + col] = x;
             if (r < len) dv[((size_t)(t0 + r) * H + h) * HD + col] = tobf16(x);
         }
         __syncthreads();
+        float dor[CS], dxr[CS];
+#pragma unroll
+        for (int r = 0; r < CS; ++r) {
+            dor[r] = dol[r][j];
+            dxr[r] = dxs[r][j];
+        }
         // dS0 = Gam dS1 + scale Qt^T dO - Kt^T dX
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int c = rg * 16 + i;
+        for (int i = 0; i < RPT; ++i) {
+            const int c = rg + NRG * i;
             float acc = gam[c] * ds[i];
-            for (int r = 0; r < CS; ++r) acc += qt[r][c] * dol[r][j] - kt[r][c] * dxs[r][j];
+#pragma unroll
+            for (int r = 0; r < CS; r += 4) {
+                const float4 q4 = *(const float4 *)&qtT[c][r];
+                const float4 k4 = *(const float4 *)&ktT[c][r];
+                acc += q4.x * dor[r] + q4.y * dor[r + 1] + q4.z * dor[r + 2] + q4.w * dor[r + 3];
+                acc -= k4.x * dxr[r] + k4.y * dxr[r + 1] + k4.z * dxr[r + 2] + k4.w * dxr[r + 3];
+            }
             ds[i] = acc;
         }
     }
     if (dinit) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dinit[sbase + (size_t)(rg * 16 + i) * HD + col] = ds[i];
+        for (int i = 0; i < RPT; ++i) dinit[sbase + (size_t)(rg + NRG * i) * HD + col] = ds[i];
     }
+#undef KDA_DSTATES_FETCH
 }
 
 // ---------------------------------------------------------------------------
@@ -359,31 +481,35 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
 // ---------------------------------------------------------------------------
 struct ChunkLds {
     Factors f;
-    float dol[CS][RS], vl[CS][RS];        // scale * dO, v
+    float dol[CS][RS], xl[CS][RS], dxl[CS][RS];  // scale * dO, X, dX
     float s0b[CS][RS], ds1b[CS][RS];      // 16-channel row blocks of S0 and dS1
-    float x[CS][RS], dx[CS][RS];
     float dqt[CS][RS], dkt[CS][RS], dwm[CS][RS];
     float dM[CS][SP], dAqk[CS][SP], dP[CS][SP], Y[CS][SP], dL[CS][SP], dA[CS][SP];
     float dgam[HD], dgam2[2][HD], red[BT / 64];
 };
 
-__device__ __forceinline__ void load_block(float (&dst)[CS][RS], const float *__restrict__ src) {
-    // 16 rows x 128 floats, contiguous in global memory
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const int idx = 4 * (tid + m * BT);
-        *(float4 *)&dst[idx / HD][idx % HD] = *(const float4 *)&src[idx];
-    }
+// 16-channel block cb (all 128 columns) of a part-major stored state:
+// eight contiguous 1 KiB pieces, two 16-byte loads per thread
+__device__ __forceinline__ void fetch_state_block(float4 &d0, float4 &d1,
+                                                  const float *__restrict__ base, int cb) {
+    const int f0 = threadIdx.x, f1 = threadIdx.x + BT;
+    d0 = *(const float4 *)&base[state_off(f0 >> 6, 16 * cb, 4 * (f0 & 63))];
+    d1 = *(const float4 *)&base[state_off(f1 >> 6, 16 * cb, 4 * (f1 & 63))];
+}
+__device__ __forceinline__ void put_state_block(float (&dst)[CS][RS], const float4 &d0,
+                                                const float4 &d1) {
+    const int f0 = threadIdx.x, f1 = threadIdx.x + BT;
+    *(float4 *)&dst[(f0 & 63) >> 2][(f0 >> 6) * CWB + 4 * (f0 & 3)] = d0;
+    *(float4 *)&dst[(f1 & 63) >> 2][(f1 >> 6) * CWB + 4 * (f1 & 3)] = d1;
 }
 
 __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, const uint16_t *__restrict__ g,
-    const uint16_t *__restrict__ beta, const float *__restrict__ A_log,
-    const float *__restrict__ dt_bias, float lb, float scale, const uint16_t *__restrict__ dout,
-    const int32_t *__restrict__ cu, int N, int T, int H,
+    const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
+    const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb, float scale,
+    const uint16_t *__restrict__ dout, const int32_t *__restrict__ cu, int N, int T, int H,
     const float *__restrict__ st0, const float *__restrict__ dst1,
+    const float *__restrict__ xws, const float *__restrict__ dxws,
     uint16_t *__restrict__ dq, uint16_t *__restrict__ dk, uint16_t *__restrict__ dg,
     uint16_t *__restrict__ dbeta, float *__restrict__ part_alog, float *__restrict__ part_dtb)
 {
@@ -400,90 +526,83 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
         if (tid == 0) part_alog[sh] = 0.f;
         return;
     }
+    const float *S0 = st0 + sh * HD * HD;
+    const float *DS = dst1 + sh * HD * HD;
+    // two blocks in flight: (ps, pd) holds block cb, (qs, qd) block cb + 1
+    float4 ps0, ps1, pd0, pd1, qs0, qs1, qd0, qd1;
+    fetch_state_block(ps0, ps1, S0, 0);                     // in flight during the factors
+    fetch_state_block(pd0, pd1, DS, 0);
+    fetch_state_block(qs0, qs1, S0, 1);
+    fetch_state_block(qd0, qd1, DS, 1);
     const float Aexp = expf(A_log[h]);
     chunk_factors(F, q, k, g, beta, Aexp, dt_bias, lb, t0, len, H, h);
 
     for (int idx = tid; idx < CS * HD; idx += BT) {
         const int r = idx / HD, c = idx % HD;
-        const size_t off = ((size_t)(t0 + r) * H + h) * HD + c;
-        L.dol[r][c] = r < len ? scale * bf16f(dout[off]) : 0.f;
-        L.vl[r][c] = r < len ? bf16f(v[off]) : 0.f;
+        L.dol[r][c] = r < len ? scale * bf16f(dout[((size_t)(t0 + r) * H + h) * HD + c]) : 0.f;
     }
-    const float *S0 = st0 + sh * HD * HD;
-    const float *DS = dst1 + sh * HD * HD;
-
-    // pass 1 over 16-channel blocks: X, dX (accumulated), dQt, dGam
-    const int r_ = tid >> 4, lo = tid & 15, j0 = lo * 8;
-    float xa[8], dxa[8];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) xa[m] = dxa[m] = 0.f;
+    for (int m = 0; m < 2; ++m) {
+        const int e = 4 * (tid + m * BT);
+        *(float4 *)&L.xl[e / HD][e % HD] = *(const float4 *)&xws[sh * CS * HD + e];
+        *(float4 *)&L.dxl[e / HD][e % HD] = *(const float4 *)&dxws[sh * CS * HD + e];
+    }
+    __syncthreads();
+
+    // Products with the states, over 16-channel blocks of S0 / dS1 (blocks
+    // cb + 1 and cb + 2 in flight while block cb computes), on fp32 16x16x4 MFMAs
+    // contracting over the 128 value columns:
+    //   wave 0: dQt = scale dO S0^T,  wave 1: dKt = -dX S0^T,
+    //   wave 2: dWm = X dS1^T  (A operands resident for all blocks)
+    //   wave 3: dGam = diag(dS1 S0^T) on the vector ALUs
+    const int wave = tid >> 6, l = tid & 63;
+    float aop[HD / 4];
+    if (wave < 3) {
+        const float(&src)[CS][RS] = wave == 0 ? L.dol : wave == 1 ? L.dxl : L.xl;
+        const float sg = wave == 1 ? -1.f : 1.f;
+#pragma unroll
+        for (int ks = 0; ks < HD / 4; ++ks) aop[ks] = sg * src[l & 15][4 * ks + (l >> 4)];
+    }
+    float(&dsto)[CS][RS] = wave == 0 ? L.dqt : wave == 1 ? L.dkt : L.dwm;
     for (int cb = 0; cb < HD / 16; ++cb) {
         __syncthreads();
-        load_block(L.s0b, S0 + (size_t)cb * 16 * HD);
-        load_block(L.ds1b, DS + (size_t)cb * 16 * HD);
+        put_state_block(L.s0b, ps0, ps1);
+        put_state_block(L.ds1b, pd0, pd1);
+        ps0 = qs0; ps1 = qs1; pd0 = qd0; pd1 = qd1;
+        if (cb + 2 < HD / 16) {
+            fetch_state_block(qs0, qs1, S0, cb + 2);
+            fetch_state_block(qd0, qd1, DS, cb + 2);
+        }
         __syncthreads();
-        for (int cc = 0; cc < 16; ++cc) {
-            const int c = cb * 16 + cc;
-            const float ktv = F.kt[r_][c], wmv = F.wm[r_][c];
+        if (wave < 3) {
+            const float(&bsrc)[CS][RS] = wave == 2 ? L.ds1b : L.s0b;
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                xa[m] -= ktv * L.s0b[cc][j0 + m];
-                dxa[m] += wmv * L.ds1b[cc][j0 + m];
-            }
-        }
-        {
-            float acc = 0.f;
-            for (int jj = 0; jj < HD; jj += 4) {
-                const float4 a4 = *(const float4 *)&L.dol[r_][jj];
-                const float4 b4 = *(const float4 *)&L.s0b[lo][jj];
-                acc += a4.x * b4.x + a4.y * b4.y + a4.z * b4.z + a4.w * b4.w;
-            }
-            L.dqt[r_][cb * 16 + lo] = acc;
-        }
-        {
-            // dGam[c] = sum_j dS1[c][j] S0[c][j]: 16 lanes per channel, 8 columns each
-            const int cc = tid >> 4;
+            for (int ks = 0; ks < HD / 4; ++ks)
+                acc = mfma_k4(aop[ks], bsrc[l & 15][4 * ks + (l >> 4)], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dsto[4 * (l >> 4) + i][16 * cb + (l & 15)] = acc[i];
+        } else {
+            const int cc = l >> 2, qq = l & 3;
             float p = 0.f;
 #pragma unroll
-            for (int m = 0; m < 8; ++m) p += L.ds1b[cc][j0 + m] * L.s0b[cc][j0 + m];
-            p += __shfl_xor(p, 8, 16);
-            p += __shfl_xor(p, 4, 16);
-            p += __shfl_xor(p, 2, 16);
-            p += __shfl_xor(p, 1, 16);
-            if (lo == 0) L.dgam[cb * 16 + cc] = p;
+            for (int m = 0; m < 32; m += 4) {
+                const float4 a4 = *(const float4 *)&L.ds1b[cc][32 * qq + m];
+                const float4 b4 = *(const float4 *)&L.s0b[cc][32 * qq + m];
+                p += a4.x * b4.x + a4.y * b4.y + a4.z * b4.z + a4.w * b4.w;
+            }
+            p += __shfl_xor(p, 1, 64);
+            p += __shfl_xor(p, 2, 64);
+            if (qq == 0) L.dgam[16 * cb + cc] = p;
         }
     }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        float d = dxa[m];
-        for (int sr = 0; sr < CS; ++sr) d += F.M[sr][r_] * L.dol[sr][j0 + m];
-        L.x[r_][j0 + m] = xa[m] + L.vl[r_][j0 + m];
-        L.dx[r_][j0 + m] = d;
-    }
-    // pass 2 over 16-channel blocks: dKt = -dX S0^T, dWm = X dS1^T
-    for (int cb = 0; cb < HD / 16; ++cb) {
-        __syncthreads();
-        load_block(L.s0b, S0 + (size_t)cb * 16 * HD);
-        load_block(L.ds1b, DS + (size_t)cb * 16 * HD);
-        __syncthreads();
-        float a = 0.f, b = 0.f;
-        for (int jj = 0; jj < HD; jj += 4) {
-            const float4 dx4 = *(const float4 *)&L.dx[r_][jj];
-            const float4 x4 = *(const float4 *)&L.x[r_][jj];
-            const float4 s4 = *(const float4 *)&L.s0b[lo][jj];
-            const float4 d4 = *(const float4 *)&L.ds1b[lo][jj];
-            a += dx4.x * s4.x + dx4.y * s4.y + dx4.z * s4.z + dx4.w * s4.w;
-            b += x4.x * d4.x + x4.y * d4.y + x4.z * d4.z + x4.w * d4.w;
-        }
-        L.dkt[r_][cb * 16 + lo] = -a;
-        L.dwm[r_][cb * 16 + lo] = b;
-    }
+    const int r_ = tid >> 4, lo = tid & 15;
     {
         // dM = scale dO X^T
         float acc = 0.f;
         for (int jj = 0; jj < HD; jj += 4) {
             const float4 a4 = *(const float4 *)&L.dol[r_][jj];
-            const float4 b4 = *(const float4 *)&L.x[lo][jj];
+            const float4 b4 = *(const float4 *)&L.xl[lo][jj];
             acc += a4.x * b4.x + a4.y * b4.y + a4.z * b4.z + a4.w * b4.w;
         }
         L.dM[r_][lo] = acc;
@@ -498,7 +617,12 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
             a += L.dM[r][s] * F.P[i][s];
             p += F.aqk[s][r] * L.dM[s][i];
         }
-        for (int c = 0; c < HD; ++c) p += F.kb[r][c] * F.gam[c] * L.dwm[i][c];
+        for (int c = 0; c < HD; c += 4) {
+            const float4 k4 = *(const float4 *)&F.kb[r][c];
+            const float4 g4 = *(const float4 *)&F.gam[c];
+            const float4 w4 = *(const float4 *)&L.dwm[i][c];
+            p += k4.x * g4.x * w4.x + k4.y * g4.y * w4.y + k4.z * g4.z * w4.z + k4.w * g4.w * w4.w;
+        }
         L.dAqk[r][i] = i <= r ? a : 0.f;
         L.dP[r][i] = p;
     }
@@ -523,20 +647,36 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
     __syncthreads();
     {
         // per (token row r, channel c): the gradients of Qt, Kt, Kb, then q, k, G
+        // Thread: channel c, rows rh + 2 mm.  The loop over s reads this
+        // thread's column of kb, dWm, qt, kt once; the 16 x 16 factors are
+        // the same for the whole wave (broadcast reads).
         const int c = tid & (HD - 1), rh = tid >> 7;
-        float dgk = 0.f;
-#pragma unroll 1
+        float dQ[CS / 2], dK[CS / 2], dKG[CS / 2], dKB[CS / 2];
+#pragma unroll
         for (int mm = 0; mm < CS / 2; ++mm) {
             const int r = rh + 2 * mm;
-            float dQt = L.dqt[r][c], dKt = L.dkt[r][c], dKbG = 0.f, dKb = 0.f;
-            for (int s = 0; s < CS; ++s) {
-                const float kbs = F.kb[s][c];
-                dQt += L.dAqk[r][s] * kbs;                  // zero for s > r
-                dKt += L.dA[r][s] * kbs;                    // zero for s >= r
-                dKbG += F.P[r][s] * L.dwm[s][c];
-                dKb += L.dAqk[s][r] * F.qt[s][c] + L.dA[s][r] * F.kt[s][c];
+            dQ[mm] = L.dqt[r][c];
+            dK[mm] = L.dkt[r][c];
+            dKG[mm] = dKB[mm] = 0.f;
+        }
+#pragma unroll 4
+        for (int s = 0; s < CS; ++s) {
+            const float kbs = F.kb[s][c], dws = L.dwm[s][c], qts = F.qt[s][c], kts = F.kt[s][c];
+#pragma unroll
+            for (int mm = 0; mm < CS / 2; ++mm) {
+                const int r = rh + 2 * mm;
+                dQ[mm] += L.dAqk[r][s] * kbs;               // zero for s > r
+                dK[mm] += L.dA[r][s] * kbs;                 // zero for s >= r
+                dKG[mm] += F.P[r][s] * dws;
+                dKB[mm] += L.dAqk[s][r] * qts + L.dA[s][r] * kts;
             }
-            dKb += F.gam[c] * dKbG;
+        }
+        float dgk = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < CS / 2; ++mm) {
+            const int r = rh + 2 * mm;
+            const float dQt = dQ[mm], dKt = dK[mm], dKbG = dKG[mm];
+            const float dKb = dKB[mm] + F.gam[c] * dKbG;
             dgk += dKbG * F.kb[r][c];
             const float e = F.e[r][c];
             if (r < len) {
@@ -615,7 +755,8 @@ __global__ __launch_bounds__(HD) void bwd_reduce_kernel(
 
 size_t bwd_workspace_bytes(int64_t num_slots, int H) {
     const size_t sh = (size_t)num_slots * H;
-    return sh * ((size_t)BR_FLOATS + 2 * (size_t)HD * HD + 1 + HD) * sizeof(float);
+    return sh * ((size_t)BR_FLOATS + 2 * (size_t)HD * HD + 2 * (size_t)CS * HD + 1 + HD) *
+           sizeof(float);
 }
 
 hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
@@ -624,27 +765,41 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
                       int H, int64_t num_slots, const void *init, int init_fp32,
                       const uint16_t *dout, const float *dfin, uint16_t *dq, uint16_t *dk,
                       uint16_t *dv, uint16_t *dg, uint16_t *dbeta, float *dA_log,
-                      float *ddt_bias, float *dinit, void *ws, hipStream_t stream)
+                      float *ddt_bias, float *dinit, void *ws, hipStream_t stream,
+                      const hipEvent_t *events)
 {
     const size_t sh = (size_t)num_slots * H;
     float *brec = (float *)ws;
     float *st0 = brec + sh * BR_FLOATS;
     float *dst1 = st0 + sh * HD * HD;
-    float *pdtb = dst1 + sh * HD * HD;
+    float *xws = dst1 + sh * HD * HD;
+    float *dxws = xws + sh * CS * HD;
+    float *pdtb = dxws + sh * CS * HD;
     float *palog = pdtb + sh * HD;
     const dim3 chunks((unsigned)sh), scans((unsigned)((size_t)N * H * NPART));
+    hipError_t e = hipSuccess;
+    auto mark = [&](int i) {
+        if (events && events[i] && e == hipSuccess) e = hipEventRecord(events[i], stream);
+    };
+    mark(0);
     hipLaunchKernelGGL(bwd_prep_kernel, chunks, dim3(BT), 0, stream,
                        q, k, g, beta, A_log, dt_bias, lower_bound, cu, N, T, H, brec);
+    mark(1);
     hipLaunchKernelGGL(bwd_states_kernel, scans, dim3(BT), 0, stream,
-                       v, brec, cu, N, T, H, init, init_fp32, st0);
+                       v, brec, cu, N, T, H, init, init_fp32, st0, xws);
+    mark(2);
     hipLaunchKernelGGL(bwd_dstates_kernel, scans, dim3(BT), 0, stream,
-                       dout, brec, cu, N, T, H, scale, dfin, dst1, dv, dinit);
+                       dout, brec, cu, N, T, H, scale, dfin, dst1, dxws, dv, dinit);
+    mark(3);
     hipLaunchKernelGGL(bwd_chunk_kernel, chunks, dim3(BT), 0, stream,
-                       q, k, v, g, beta, A_log, dt_bias, lower_bound, scale, dout, cu, N, T, H,
-                       st0, dst1, dq, dk, dg, dbeta, palog, pdtb);
+                       q, k, g, beta, A_log, dt_bias, lower_bound, scale, dout, cu, N, T, H,
+                       st0, dst1, xws, dxws, dq, dk, dg, dbeta, palog, pdtb);
+    mark(4);
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)H), dim3(HD), 0, stream,
                        palog, pdtb, num_slots, H, dA_log, ddt_bias);
-    return hipGetLastError();
+    mark(5);
+    const hipError_t le = hipGetLastError();
+    return e != hipSuccess ? e : le;
 }
 
 }  // namespace kda
