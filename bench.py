@@ -260,7 +260,7 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the T=8192 H=96 fixed one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=96, help="heads in the oracle's timed sample")
-    ap.add_argument("--head-dim", type=int, default=128, choices=(64, 128),
+    ap.add_argument("--head-dim", type=int, default=128, choices=(64, 128, 256),
                     help="K = V of the measured workload")
     ap.add_argument("--scalar-gate", action="store_true",
                     help="measure the Gated DeltaNet form (one gate value per token and head)")

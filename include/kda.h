@@ -19,8 +19,9 @@
  * clamped softplus form above is the reading this library implements.  The
  * original supports only K = V = 128 ("Moonshot AI Open-Sources FlashKDA",
  * section "Limitations before you integrate"); this library also takes
- * K = V = 64 in kda_fwd and kda_fwd_scalar_gate.  Only the forward pass
- * exists (same section).
+ * K = V = 64 and K = V = 256 in kda_fwd and kda_fwd_scalar_gate.  The
+ * original ships only the forward pass (same section); kda_bwd here adds
+ * the gradients (K = V = 128).
  *
  * Conventions shared by every entry point:
  *   - Pointers are device pointers unless stated; every tensor is dense and
@@ -83,9 +84,10 @@ typedef enum {
  *   final_state    [N, H, K, V] in final_state_dtype, or NULL (not written);
  *                  when given, every slab is written (a zero-length sequence
  *                  gets its initial state)
- *   B, T, H, K, V  sizes; K = V = 128, or K = V = 64 (run on the 128-wide
- *                  kernels with the channels and columns from 64 on held at
- *                  zero).  When B*T == 0 the
+ *   B, T, H, K, V  sizes; K = V = 128, K = V = 256 (sixteen state row
+ *                  tiles per column slice, 26 KB hand-off records), or
+ *                  K = V = 64 (run on the 128-wide kernels with the channels
+ *                  and columns from 64 on held at zero).  When B*T == 0 the
  *                  token buffers (q, k, v, g, beta, out) may be NULL; the
  *                  call then only writes final_state (= initial state)
  *
@@ -223,18 +225,27 @@ float kda_lower_bound_min(void);
 int32_t kda_chunk_size(void);
 
 /*
- * Bytes of device workspace one kda_fwd call with these sizes takes from
- * the pool (the intra-chunk hand-off records).  0 on invalid sizes.
+ * Bytes of device workspace one kda_fwd call with these sizes and head
+ * dimension K = V = 64 or 128 takes from the pool (the intra-chunk hand-off
+ * records).  0 on invalid sizes.
  */
 size_t kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs);
+
+/*
+ * The same for any supported head dimension K (64, 128 or 256; head
+ * dimension 256 takes 26 KB records per (chunk, head) instead of 13 KB).
+ * 0 on invalid sizes or an unsupported K.
+ */
+size_t kda_workspace_size_hd(int32_t B, int32_t T, int32_t H, int32_t num_seqs, int32_t K);
 
 /*
  * kda_debug_intra — test entry: runs only the intra-chunk stage (gate,
  * in-chunk cumulative decay, A_kk / A_qk products, triangular inverse) and
  * writes its hand-off records into the caller's `workspace` (device,
- * kda_workspace_size(...) bytes, 16-byte aligned).  Arguments as kda_fwd.
- * Record layout (per chunk slot and head, 13312 bytes) is described in the
- * library source; tests decode it to compare each stage with fp64 maths.
+ * kda_workspace_size_hd(..., K) bytes, 16-byte aligned).  Arguments as kda_fwd.
+ * Record layout (per chunk slot and head, 13312 bytes, or 26624 for K = 256)
+ * is described in the library source; tests decode it to compare each stage
+ * with fp64 maths.
  */
 kda_status_t kda_debug_intra(const void *q, const void *k, const void *g,
                              const void *beta,

@@ -71,6 +71,8 @@ def load():
     lib.kda_chunk_size.argtypes = []
     lib.kda_workspace_size.restype = ctypes.c_size_t
     lib.kda_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.kda_workspace_size_hd.restype = ctypes.c_size_t
+    lib.kda_workspace_size_hd.argtypes = [i32, i32, i32, i32, i32]
     lib.kda_set_stage_events.restype = ctypes.c_int
     lib.kda_set_stage_events.argtypes = [P, P, P]
     lib.kda_fwd_scalar_gate.restype = ctypes.c_int
@@ -115,8 +117,9 @@ def chunk_size() -> int:
     return int(load().kda_chunk_size())
 
 
-def workspace_size(B: int, T: int, H: int, num_seqs: int) -> int:
-    return int(load().kda_workspace_size(B, T, H, num_seqs))
+def workspace_size(B: int, T: int, H: int, num_seqs: int, K: int = 128) -> int:
+    """Bytes of the hand-off records of one forward call (head dimension K)."""
+    return int(load().kda_workspace_size_hd(B, T, H, num_seqs, K))
 
 
 def _ptr(t):
@@ -324,7 +327,7 @@ def debug_intra(q, k, g, beta, A_log, dt_bias, lower_bound, cu_seqlens=None):
     lib = load()
     B, T, H, K = q.shape
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
-    ws = torch.zeros(workspace_size(B, T, H, N), dtype=torch.uint8, device=q.device)
+    ws = torch.zeros(workspace_size(B, T, H, N, K), dtype=torch.uint8, device=q.device)
     rc = lib.kda_debug_intra(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
                              float(lower_bound), _ptr(cu_seqlens), int(N), int(B), int(T),
                              int(H), int(K), _ptr(ws), _stream(q.device))

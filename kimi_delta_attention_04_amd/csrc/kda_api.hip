@@ -63,8 +63,8 @@ kda_status_t check_sizes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
                          const int32_t *cu, int32_t N) {
     if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID_ARG;
     if (cu ? (B != 1) : (N != B)) return KDA_ERR_INVALID_ARG;
-    // K = V = 128, or K = V = 64 (computed on the 128-wide tiles)
-    if (K != V || (K != kda::HD && K != 64)) return KDA_ERR_UNSUPPORTED;
+    // K = V = 128 or 256, or K = V = 64 (computed on the 128-wide tiles)
+    if (K != V || (K != kda::HD && K != 2 * kda::HD && K != 64)) return KDA_ERR_UNSUPPORTED;
     // token-row and unit counts must fit the int32 grid / index arithmetic
     if ((int64_t)B * T > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     if (num_slots(B, T, N) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
@@ -72,7 +72,7 @@ kda_status_t check_sizes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
     if (num_slots(B, T, N) * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     if ((int64_t)N * H > INT32_MAX / 64) return KDA_ERR_UNSUPPORTED;
     // byte offsets within one chunk's 16 token rows of all heads are 32-bit
-    if ((int64_t)H * kda::HD * 2 * kda::CS > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)H * (K > kda::HD ? K : kda::HD) * 2 * kda::CS > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
 }
 
@@ -102,8 +102,13 @@ float kda_lower_bound_min(void) { return kLowerBoundMin; }
 int32_t kda_chunk_size(void) { return kda::CS; }
 
 size_t kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs) {
+    return kda_workspace_size_hd(B, T, H, num_seqs, kda::HD);
+}
+
+size_t kda_workspace_size_hd(int32_t B, int32_t T, int32_t H, int32_t num_seqs, int32_t K) {
     if (B < 1 || T < 0 || H < 1 || num_seqs < 1) return 0;
-    return (size_t)num_slots(B, T, num_seqs) * (size_t)H * kda::REC_BYTES;
+    if (K != 64 && K != kda::HD && K != 2 * kda::HD) return 0;
+    return (size_t)num_slots(B, T, num_seqs) * (size_t)H * (size_t)kda::rec_bytes_for(K);
 }
 
 }  // extern "C"
@@ -141,7 +146,7 @@ kda_status_t fwd_impl(const void *q, const void *k, const void *v, const void *g
 
     hipStream_t s = (hipStream_t)stream;
     const int64_t slots = num_slots(B, T, num_seqs);
-    const size_t bytes = kda_workspace_size(B, T, H, num_seqs);
+    const size_t bytes = kda_workspace_size_hd(B, T, H, num_seqs, K);
     hipMemPool_t pool;
     if ((st = device_pool(&pool)) != KDA_OK) return st;
     void *ws = nullptr;

@@ -28,6 +28,7 @@ namespace kda {
 
 constexpr int HD = 128;          // head dimension of the tiles (K = V; 64 runs on them zero-padded)
 constexpr int CS = 16;           // tokens per chunk
+constexpr int CS_TOKENS = CS;
 constexpr float LOG2E = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
@@ -57,6 +58,29 @@ constexpr int REC_WT = 8192;
 constexpr int REC_M = 12288;
 constexpr int REC_GAM = 12800;
 constexpr int REC_BYTES = 13312;
+
+// The same record for tiles of KT key channels (128, or 256 for head
+// dimension 256): KT/32 channel blocks in KT, QT and WT, KT chunk decays,
+// and the whole padded to a multiple of 1 KB (the scan moves records in
+// 1 KB DMA units).
+template <int KT>
+struct RecLayout {
+    static_assert(KT == 128 || KT == 256, "tile widths");
+    static constexpr int KTO = 0;
+    static constexpr int QT = CS_TOKENS * KT * 2;
+    static constexpr int WT = 2 * QT;
+    static constexpr int M = 3 * QT;
+    static constexpr int GAM = M + CS_TOKENS * CS_TOKENS * 2;
+    static constexpr int BYTES = (GAM + KT * 4 + 1023) / 1024 * 1024;
+};
+static_assert(RecLayout<128>::QT == REC_QT && RecLayout<128>::WT == REC_WT &&
+              RecLayout<128>::M == REC_M && RecLayout<128>::GAM == REC_GAM &&
+              RecLayout<128>::BYTES == REC_BYTES, "the 128-wide record");
+
+// Record bytes for head dimension K (64 and 128 share the 128-wide tiles).
+__host__ __device__ constexpr int rec_bytes_for(int K) {
+    return K > 128 ? RecLayout<256>::BYTES : RecLayout<128>::BYTES;
+}
 
 __host__ __device__ constexpr int state_chan(int t, int rho) {
     return 32 * (t >> 1) + 8 * (rho >> 2) + 4 * (t & 1) + (rho & 3);

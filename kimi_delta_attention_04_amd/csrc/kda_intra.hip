@@ -10,8 +10,8 @@ namespace kda {
 namespace {
 
 // One wave per (chunk slot, head), a workgroup of its own.  SG: scalar
-// (per-head) gate, g [B*T, H] and dt_bias [H].  KD: head dimension (128, or
-// 64 computed on 128 channels of which the last 64 are zeros).
+// (per-head) gate, g [B*T, H] and dt_bias [H].  KD: head dimension (128,
+// 256, or 64 computed on 128 channels of which the last 64 are zeros).
 template <bool SG, int KD>
 __global__ __launch_bounds__(64, 2) void intra_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -20,7 +20,8 @@ __global__ __launch_bounds__(64, 2) void intra_kernel(
     const int32_t *__restrict__ cu, int N, int T, int H, uint8_t *__restrict__ ws)
 {
     constexpr int K = KD;
-    __shared__ __attribute__((aligned(16))) WaveLds lds;
+    constexpr int KT = KD > HD ? 2 * HD : HD;     // channels of the tiles
+    __shared__ __attribute__((aligned(16))) WaveLdsT<KT> lds;
     // Head fastest: the workgroups running together read neighbouring pieces
     // of the same token rows and write neighbouring records.  Last chunk
     // slot first: the records of the first chunks, which the scan reads
@@ -42,19 +43,19 @@ __global__ __launch_bounds__(64, 2) void intra_kernel(
     const int64_t t0 = start + (slot - seq_slot0(cu, n, T)) * CS;
     if (t0 >= end) return;                         // gap slot, wave-uniform
     const int len = (int)min((int64_t)CS, end - t0);
-    uint8_t *rec = ws + ((size_t)slot * H + h) * REC_BYTES;
+    uint8_t *rec = ws + ((size_t)slot * H + h) * RecLayout<KT>::BYTES;
 
     const float A = expf(A_log[h]);
-    __shared__ float dtb_lds[HD];
-    stage_dtb<SG>(dtb_lds, dt_bias, h, K);
+    __shared__ float dtb_lds[KT];
+    stage_dtb<SG, KT>(dtb_lds, dt_bias, h, K);
     wave_lds_sync();
 
-    IntraIn in;
-    intra_load<SG>(in, q, k, g, beta, t0, len, H, h, K);
+    IntraInT<KT / 32> in;
+    intra_load<SG, KT>(in, q, k, g, beta, t0, len, H, h, K);
     if (len == CS)
-        intra_compute<true, SG>(lds, in, A, dtb_lds, lb2, len, rec);
+        intra_compute<true, SG, KT>(lds, in, A, dtb_lds, lb2, len, rec);
     else
-        intra_compute<false, SG>(lds, in, A, dtb_lds, lb2, len, rec);
+        intra_compute<false, SG, KT>(lds, in, A, dtb_lds, lb2, len, rec);
 }
 
 }  // namespace
@@ -72,6 +73,8 @@ hipError_t launch_intra(const uint16_t *q, const uint16_t *k, const uint16_t *g,
                        q, k, g, beta, A_log, dt_bias, lb2, cu, N, T, H, ws)
     if (K == HD) {
         if (scalar_gate) KDA_INTRA(true, HD); else KDA_INTRA(false, HD);
+    } else if (K == 2 * HD) {
+        if (scalar_gate) KDA_INTRA(true, 2 * HD); else KDA_INTRA(false, 2 * HD);
     } else {
         if (scalar_gate) KDA_INTRA(true, 64); else KDA_INTRA(false, 64);
     }

@@ -27,10 +27,12 @@ namespace kda {
 // LDS scratch of one intra wave: the per-token beta and per-channel chunk
 // decay, the two values the wave needs in a layout other than the one it
 // computes them in.
-struct WaveLds {
+template <int KT>
+struct WaveLdsT {
     float beta[CS];
-    float gam[HD];                  // e^{G_last} per channel
+    float gam[KT];                  // e^{G_last} per channel
 };
+using WaveLds = WaveLdsT<HD>;
 
 // Token-per-lane layout: lane l holds token tok = l % 16 and, for each
 // 32-channel block kb, the eight channels 32kb + 8(l/16) + i.  For every kb
@@ -39,19 +41,22 @@ struct WaveLds {
 // in-chunk Gram products and the Kt / Qt records come straight from the
 // registers; the cumulative decay over tokens runs across the 16 lanes of a
 // DPP row.
-struct IntraIn {
-    u32x4_t g[4], q[4], k[4];       // [kb]: 8 bf16 channels of this lane's token
+// NKB 32-channel blocks: 4 for the 128-wide tiles, 8 for head dimension 256.
+template <int NKB>
+struct IntraInT {
+    u32x4_t g[NKB], q[NKB], k[NKB]; // [kb]: 8 bf16 channels of this lane's token
     uint32_t beta;                  // logit of this lane's token
     uint32_t gs;                    // scalar gate of this lane's token (SG form)
 };
+using IntraIn = IntraInT<4>;
 
-template <bool SG>
-__device__ __forceinline__ void intra_load(IntraIn &in, const uint16_t *__restrict__ q,
+template <bool SG, int KT = HD>
+__device__ __forceinline__ void intra_load(IntraInT<KT / 32> &in, const uint16_t *__restrict__ q,
                                            const uint16_t *__restrict__ k,
                                            const uint16_t *__restrict__ g,
                                            const uint16_t *__restrict__ beta,
                                            int64_t t0, int len, int H, int hh, int K) {
-    // K = 128, or 64: channels from K on are zeros (zero keys and queries add
+    // K = KT, or K = 64 on KT = 128: channels from K on are zeros (zero keys and queries add
     // nothing to the in-chunk products, the W rows or the state)
     const int l = threadIdx.x & 63;
     const int tok = l & 15, cgp = l >> 4;
@@ -63,7 +68,7 @@ __device__ __forceinline__ void intra_load(IntraIn &in, const uint16_t *__restri
     const __amdgpu_buffer_rsrc_t sk = make_rsrc(k + base, bytes);
     const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < KT / 32; ++kb) {
         const int off = (int)((tok * row_elems + 32 * kb + 8 * cgp) * 2);
         in.g[kb] = in.q[kb] = in.k[kb] = z;
         if (32 * kb < K) {                          // block-uniform
@@ -83,10 +88,10 @@ __device__ __forceinline__ void intra_load(IntraIn &in, const uint16_t *__restri
     }
 }
 
-// dt_bias of one head in log2 units into LDS (128 floats; zeros when absent
+// dt_bias of one head in log2 units into LDS (KT floats; zeros when absent
 // and for channels from K on), by the lanes of the calling wave.  SG form: dt_bias is [H], one value per
 // head, staged into dtb_lds[0].
-template <bool SG = false>
+template <bool SG = false, int KT = HD>
 __device__ __forceinline__ void stage_dtb(float *__restrict__ dtb_lds, const float *__restrict__ dt_bias,
                                           int hh, int K = HD) {
     const int l = threadIdx.x & 63;
@@ -95,7 +100,7 @@ __device__ __forceinline__ void stage_dtb(float *__restrict__ dtb_lds, const flo
         return;
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < KT / 64; ++r) {
         const int c = 64 * r + l;
         dtb_lds[c] = (dt_bias && c < K) ? dt_bias[(size_t)hh * K + c] * LOG2E : 0.f;
     }
@@ -151,11 +156,14 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
 // operations as in the per-channel form, so the results equal the
 // per-channel form's on inputs broadcast over channels, bit for bit.
 // dtb_lds: the head's dt_bias in log2 units (LDS).  `rec` is the record in
-// global memory.
-template <bool FULL, bool SG = false>
-__device__ __forceinline__ void intra_compute(WaveLds &L, const IntraIn &in, float A,
+// global memory.  KT: key channels of the tiles (128, or 256 for head
+// dimension 256: eight channel blocks, sixteen state row tiles).
+template <bool FULL, bool SG = false, int KT = HD>
+__device__ __forceinline__ void intra_compute(WaveLdsT<KT> &L, const IntraInT<KT / 32> &in, float A,
                                               const float *__restrict__ dtb_lds, float lb2, int len,
                                               uint8_t *__restrict__ rec) {
+    typedef RecLayout<KT> R;
+    constexpr int NKB = KT / 32;
     const int l = threadIdx.x & 63;
     const int tok = l & 15;        // token of this lane (operand view)
     const int grp = l >> 4;        // accumulator view: rows 4grp .. 4grp+3, column tok
@@ -186,7 +194,7 @@ __device__ __forceinline__ void intra_compute(WaveLds &L, const IntraIn &in, flo
     // (fp32-accurate from hi/lo parts); Kb hi/lo also transposed into the
     // B-operand layout of the W products (kbh/kbl[t], state row tile t).
     f32x4_t Akk = zero, AkkT = zero, AqkT = zero;
-    u32x2_t kbh[8], kbl[8];
+    u32x2_t kbh[2 * NKB], kbl[2 * NKB];
     float Gs = 0.f;                                  // SG form: the one cumulative gate
     if (SG && A > 0.f) {
         const float x2 = bf16f((uint16_t)in.gs) * LOG2E + dtb_lds[0];
@@ -199,7 +207,7 @@ __device__ __forceinline__ void intra_compute(WaveLds &L, const IntraIn &in, flo
         Gs += row_shr<8>(Gs);
     }
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
         float G[8];
         if (SG) {
 #pragma unroll
@@ -249,8 +257,8 @@ __device__ __forceinline__ void intra_compute(WaveLds &L, const IntraIn &in, flo
             *(f32x4_t *)&L.gam[ch] = g0;
             *(f32x4_t *)&L.gam[ch + 4] = g1;
         }
-        *(u32x4_t *)(rec + REC_KT + (kb * 64 + l) * 16) = kt4;
-        *(u32x4_t *)(rec + REC_QT + (kb * 64 + l) * 16) = qh4;
+        *(u32x4_t *)(rec + R::KTO + (kb * 64 + l) * 16) = kt4;
+        *(u32x4_t *)(rec + R::QT + (kb * 64 + l) * 16) = qh4;
         Akk = mfma_k32(kt4, bh4, Akk);          // Akk[4grp+j][cg]  = Kt_r . Kb_i
         AkkT = mfma_k32(bh4, kt4, AkkT);        // AkkT[4grp+j][cg] = Akk[cg][4grp+j]
         AqkT = mfma_k32(bh4, qh4, AqkT);        // AqkT[4grp+j][cg] = Aqk[cg][4grp+j]
@@ -271,7 +279,9 @@ __device__ __forceinline__ void intra_compute(WaveLds &L, const IntraIn &in, flo
     wave_lds_sync();
     // the chunk decay into the record from LDS in one coalesced store (four
     // lanes' 16-byte pieces per block cost several times as much)
-    *(u32x2_t *)(rec + REC_GAM + l * 8) = *(const u32x2_t *)&L.gam[2 * l];
+#pragma unroll
+    for (int p = 0; p < KT / 128; ++p)
+        *(u32x2_t *)(rec + R::GAM + (64 * p + l) * 8) = *(const u32x2_t *)&L.gam[2 * (64 * p + l)];
 
     // ---- T = (I + L)^{-1}, L = diag(beta) strict_lower(Akk) ---------------
     float br[4];
@@ -325,13 +335,13 @@ __device__ __forceinline__ void intra_compute(WaveLds &L, const IntraIn &in, flo
     u32x2_t mo;
     mo[0] = pack2(Mt[0], Mt[1]);
     mo[1] = pack2(Mt[2], Mt[3]);
-    *(u32x2_t *)(rec + REC_M + l * 8) = mo;
+    *(u32x2_t *)(rec + R::M + l * 8) = mo;
 
     // W tiles: W[:, chan(t, .)] = (T diag(beta))^T Kb[:, chan(t, .)] times the
     // chunk decay of that channel; the accumulator layout is the A layout of
     // W^T tile t the scan needs.
 #pragma unroll
-    for (int tp = 0; tp < 4; ++tp) {
+    for (int tp = 0; tp < NKB; ++tp) {
         u32x4_t o;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -343,7 +353,7 @@ __device__ __forceinline__ void intra_compute(WaveLds &L, const IntraIn &in, flo
             o[2 * half] = pack2(Wt[0] * gch, Wt[1] * gch);
             o[2 * half + 1] = pack2(Wt[2] * gch, Wt[3] * gch);
         }
-        *(u32x4_t *)(rec + REC_WT + (tp * 64 + l) * 16) = o;
+        *(u32x4_t *)(rec + R::WT + (tp * 64 + l) * 16) = o;
     }
 }
 

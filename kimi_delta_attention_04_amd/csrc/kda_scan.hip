@@ -33,9 +33,13 @@ namespace {
 // LDS ring slots per workgroup (chunks in flight + the one being read); the
 // DMA wave's vmcnt (at most 63) must cover DEPTH-1 chunks of DMAs.
 template <int CW> constexpr int RING_DEPTH = CW <= 64 ? 5 : 4;
+// Head dimension 256: 26 KB records, read one chunk at a time (no operand
+// prefetch, see scan_kernel), so the vmcnt covers DEPTH-2 chunks of DMAs.
+constexpr int RING_DEPTH_256 = 4;
 constexpr int REC_KB = REC_BYTES / 1024;         // 13 one-kilobyte units per record
 
 static_assert(REC_BYTES % 1024 == 0, "record must be a whole number of 1 KB units");
+static_assert(RecLayout<256>::BYTES % 1024 == 0, "record must be a whole number of 1 KB units");
 
 // s_waitcnt vmcnt(n) followed by a workgroup barrier; waits for this wave's
 // LDS traffic too but, unlike __syncthreads(), not for every outstanding
@@ -77,9 +81,9 @@ __device__ __forceinline__ void dma16(i32x4_t rs, const void *lds, int off) {
                  :: "s"(m0), "v"(off), "s"(rs) : "memory", "m0");
 }
 
-template <int CW>
+template <int CW, int RB = REC_BYTES>
 struct alignas(16) ScanSlot {
-    uint8_t rec[REC_BYTES];
+    uint8_t rec[RB];
     uint16_t v[CS][CW];
 };
 
@@ -93,27 +97,50 @@ __device__ __forceinline__ float row_bcast(float x) {
 }
 
 // The MFMA operands of one chunk, as one wave holds them in registers.
-template <int CT>
+// NKB 32-channel blocks of the key dimension (4, or 8 for head dimension 256).
+template <int CT, int NKB = 4>
 struct ChunkOps {
-    u32x4_t kt[4], qt[4], wt[4];
+    u32x4_t kt[NKB], qt[NKB], wt[NKB];
     u32x2_t m;
-    float gm[2];              // chunk decay of two state rows (see load_ops)
+    float gm[NKB / 2];        // chunk decay of two state rows per 128 channels (see load_ops)
     u32x2_t v[CT];            // v[row l%16][4(l/16) .. +3] of each slice: an MFMA A operand
 };
 
 // Row multiplier of the decay: S[t][j] (state row chan(t, 4grp + j)) takes
-// the chunk decay that lane 4(t/2) + 2(t%2) + j/2 of its 16-lane row holds
-// in gm[j%2].  Lane cg of row grp loads the decays of channels
-// 32(cg/4) + 8grp + 4((cg/2)%2) + 2(cg%2) + {0, 1}, which is exactly that.
-template <int T, int J>
-__device__ __forceinline__ float decay_of(const float (&gm)[2]) {
-    return row_bcast<4 * (T >> 1) + 2 * (T & 1) + (J >> 1)>(gm[J & 1]);
+// the chunk decay that lane 4(t'/2) + 2(t'%2) + j/2 of its 16-lane row holds
+// in gm[2(t/8) + j%2], t' = t % 8.  Lane cg of row grp loads the decays of
+// channels 128p + 32(cg/4) + 8grp + 4((cg/2)%2) + 2(cg%2) + {0, 1} into
+// gm[2p], gm[2p+1], which is exactly that.
+template <int T, int J, int NG>
+__device__ __forceinline__ float decay_of(const float (&gm)[NG]) {
+    constexpr int TT = T & 7;
+    return row_bcast<4 * (TT >> 1) + 2 * (TT & 1) + (J >> 1)>(gm[2 * (T >> 3) + (J & 1)]);
+}
+
+// S[t] *= diag(chunk decay) for the state row tiles t = T .. NT-1.
+template <int T, int NT, int NG>
+__device__ __forceinline__ void decay_tiles(f32x4_t (&S)[NT], const float (&gm)[NG]) {
+    if constexpr (T < NT) {
+        S[T][0] *= decay_of<T, 0>(gm);
+        S[T][1] *= decay_of<T, 1>(gm);
+        S[T][2] *= decay_of<T, 2>(gm);
+        S[T][3] *= decay_of<T, 3>(gm);
+        decay_tiles<T + 1, NT>(S, gm);
+    }
 }
 
 // CT 16-column slices per compute wave, NW compute waves (and the DMA wave)
-// per workgroup; head dimension K = V = VD (128, or 64 on the same tiles).
+// per workgroup; head dimension K = V = VD (128, 256, or 64 on the 128-wide
+// tiles).
+//
+// Two ring protocols.  128-wide tiles: the compute waves read chunk c+1's
+// operands into registers while they compute chunk c (two operand sets in
+// registers).  256-wide tiles: one operand set (96 registers for Kt, Qt and
+// W^T alone) is all the register file allows, so the compute waves read
+// chunk c's operands at the top of its own iteration, and the DMA wave
+// refills the slot of chunk c-1 instead of chunk c's.
 template <int CT, int NW, int VD>
-__global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
+__global__ __launch_bounds__(64 * (NW + 1), VD > HD ? 1 : 2) void scan_kernel(
     const uint16_t *__restrict__ v, const uint8_t *__restrict__ ws,
     const int32_t *__restrict__ cu, int N, int T, int H, float scale,
     const void *__restrict__ init, int init_fp32,
@@ -121,14 +148,20 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
 {
     constexpr int CW = NW * 16 * CT;                 // columns per workgroup
     constexpr int K = VD, V = VD;
+    constexpr bool WIDE = VD > HD;                   // 256-wide tiles
+    constexpr int KTL = WIDE ? 2 * HD : HD;          // key channels of the tiles
+    constexpr int NT = KTL / 16;                     // state row tiles per slice
+    constexpr int NKB = KTL / 32;                    // 32-channel blocks
+    typedef RecLayout<KTL> R;
+    constexpr int RKB = R::BYTES / 1024;             // one-kilobyte units per record
     constexpr int NSPLIT = V / CW;                   // column parts per head
     static_assert(NSPLIT * CW == V, "column parts cover the head");
     constexpr int V_KB = CS * CW * 2 / 1024;         // one-kilobyte units of a v tile
-    constexpr int UNITS = REC_KB + V_KB;             // DMA units per chunk
+    constexpr int UNITS = RKB + V_KB;                // DMA units per chunk
     constexpr int VROW_LANES = CW * 2 / 16;          // lanes per v row in a DMA unit
-    constexpr int DEPTH = RING_DEPTH<CW>;
-    __shared__ ScanSlot<CW> ring[DEPTH];
-    static_assert((DEPTH - 1) * UNITS <= 63, "vmcnt holds at most 63");
+    constexpr int DEPTH = WIDE ? RING_DEPTH_256 : RING_DEPTH<CW>;
+    __shared__ ScanSlot<CW, R::BYTES> ring[DEPTH];
+    static_assert((DEPTH - (WIDE ? 2 : 1)) * UNITS <= 63, "vmcnt holds at most 63");
 
     // Block b -> (unit u, part): the parts of a unit share b mod 8 (same XCD, same L2).
     const int b = blockIdx.x;
@@ -149,14 +182,14 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
     const int64_t L = end - start;
     const int nch = (int)((L + CS - 1) / CS);
     const int64_t slot0 = seq_slot0(cu, n, T);
-    // K = V = 128, or 64 on the same tiles: state rows from K on stay zero
+    // K = V = 128 or 256, or 64 on the 128-wide tiles: state rows from K on stay zero
     // (they load as zeros from the range-checked state buffers, receive no
     // updates since their key channels are zero, and are not stored)
     const size_t row_bytes = (size_t)H * V * 2;       // one token row of v / out
 
     // ---- state slices: S[ct][t][j] = state[chan(t, 4grp+j)][col] -------------
     // (a zero-sized resource when there is no initial state: loads return 0)
-    f32x4_t S[CT][8];
+    f32x4_t S[CT][NT];
     if (!dma_wave) {
         const size_t slab = (size_t)K * V * (init_fp32 ? 4 : 2);
         const __amdgpu_buffer_rsrc_t rs =
@@ -166,7 +199,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int t = 0; t < 8; ++t)
+                for (int t = 0; t < NT; ++t)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int idx = state_chan(t, 4 * grp + j) * V + col0 + wcol0 + 16 * ct + cg;
@@ -176,7 +209,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int t = 0; t < 8; ++t)
+                for (int t = 0; t < NT; ++t)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int idx = state_chan(t, 4 * grp + j) * V + col0 + wcol0 + 16 * ct + cg;
@@ -188,13 +221,13 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Per-chunk addressing advances by fixed strides.
-    const size_t rec_stride = (size_t)H * REC_BYTES;
+    const size_t rec_stride = (size_t)H * R::BYTES;
     const size_t row_stride = (size_t)CS * H * V;                  // elements per chunk of v / out
-    const uint8_t *rec_base = ws + ((size_t)slot0 * H + h) * REC_BYTES;
+    const uint8_t *rec_base = ws + ((size_t)slot0 * H + h) * R::BYTES;
     const uint16_t *v_base = v + ((size_t)start * H + h) * V + col0;
     uint16_t *out_base = out + ((size_t)start * H + h) * V + col0;
 
-    // Chunk c -> ring slot c % DEPTH by DMA (DMA wave): unit k < REC_KB is
+    // Chunk c -> ring slot c % DEPTH by DMA (DMA wave): unit k < RKB is
     // kilobyte k of the record; the next V_KB units are the v tile of this
     // part, one row of CW columns per VROW_LANES lanes (rows past the sequence
     // end and chunks past the last one read as zeros).  Exactly UNITS DMAs
@@ -202,14 +235,14 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
     auto issue = [&](int c, int slot) {
         const bool live = c < nch;
         const i32x4_t rr =
-            rsrc_words(rec_base + (live ? (size_t)c * rec_stride : 0), live ? (uint32_t)REC_BYTES : 0u);
+            rsrc_words(rec_base + (live ? (size_t)c * rec_stride : 0), live ? (uint32_t)R::BYTES : 0u);
         const int64_t rem = L - (int64_t)c * CS;
         const int len = live ? (int)(rem < CS ? rem : CS) : 0;
         const i32x4_t rv =
             rsrc_words(v_base + (live ? (size_t)c * row_stride : 0), (uint32_t)(len * row_bytes));
-        ScanSlot<CW> &sl = ring[slot];
+        ScanSlot<CW, R::BYTES> &sl = ring[slot];
 #pragma unroll
-        for (int unit = 0; unit < REC_KB; ++unit) dma16(rr, &sl.rec[unit * 1024], unit * 1024 + l * 16);
+        for (int unit = 0; unit < RKB; ++unit) dma16(rr, &sl.rec[unit * 1024], unit * 1024 + l * 16);
 #pragma unroll
         for (int vu = 0; vu < V_KB; ++vu) {
             const int vrow0 = vu * (1024 / (2 * CW));                  // 1 KB = 1024 / (2 CW) rows
@@ -219,20 +252,23 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
     };
 
     // LDS -> registers: the operands of the chunk in ring slot `slot`.
-    auto load_ops = [&](int slot, ChunkOps<CT> &op) {
-        const ScanSlot<CW> &sl = ring[slot];
-        const uint8_t *R = sl.rec;
+    auto load_ops = [&](int slot, ChunkOps<CT, NKB> &op) {
+        const ScanSlot<CW, R::BYTES> &sl = ring[slot];
+        const uint8_t *Rp = sl.rec;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            op.kt[kb] = *(const u32x4_t *)(R + REC_KT + (kb * 64 + l) * 16);
-            op.qt[kb] = *(const u32x4_t *)(R + REC_QT + (kb * 64 + l) * 16);
-            op.wt[kb] = *(const u32x4_t *)(R + REC_WT + (kb * 64 + l) * 16);
+        for (int kb = 0; kb < NKB; ++kb) {
+            op.kt[kb] = *(const u32x4_t *)(Rp + R::KTO + (kb * 64 + l) * 16);
+            op.qt[kb] = *(const u32x4_t *)(Rp + R::QT + (kb * 64 + l) * 16);
+            op.wt[kb] = *(const u32x4_t *)(Rp + R::WT + (kb * 64 + l) * 16);
         }
-        op.m = *(const u32x2_t *)(R + REC_M + l * 8);
+        op.m = *(const u32x2_t *)(Rp + R::M + l * 8);
         const int gch = 32 * (cg >> 2) + 8 * grp + 4 * ((cg >> 1) & 1) + 2 * (cg & 1);
-        const u32x2_t g2 = *(const u32x2_t *)(R + REC_GAM + gch * 4);
-        op.gm[0] = __uint_as_float(g2[0]);
-        op.gm[1] = __uint_as_float(g2[1]);
+#pragma unroll
+        for (int p = 0; p < NKB / 4; ++p) {
+            const u32x2_t g2 = *(const u32x2_t *)(Rp + R::GAM + (128 * p + gch) * 4);
+            op.gm[2 * p] = __uint_as_float(g2[0]);
+            op.gm[2 * p + 1] = __uint_as_float(g2[1]);
+        }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
             op.v[ct] = *(const u32x2_t *)&sl.v[cg][wcol0 + 16 * ct + 4 * grp];
@@ -248,7 +284,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
         eye[0] = (d == 0 ? one : 0u) | (d == 1 ? one << 16 : 0u);
         eye[1] = (d == 2 ? one : 0u) | (d == 3 ? one << 16 : 0u);
     }
-    auto compute = [&](int c, const ChunkOps<CT> &op) {
+    auto compute = [&](int c, const ChunkOps<CT, NKB> &op) {
         const int64_t rem = L - (int64_t)c * CS;
         const int len = (int)(rem < CS ? rem : CS);
         // rows past the sequence end fall outside the resource and are dropped
@@ -259,9 +295,9 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
         for (int ct = 0; ct < CT; ++ct) {
             const int lc = wcol0 + 16 * ct + cg;         // column within the part
             // bf16 copy of the state as B operand: k-slots 8grp..8grp+7 of pair kb
-            u32x4_t Sb[4];
+            u32x4_t Sb[NKB];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
+            for (int kb = 0; kb < NKB; ++kb) {
                 Sb[kb][0] = pack2(S[ct][2 * kb][0], S[ct][2 * kb][1]);
                 Sb[kb][1] = pack2(S[ct][2 * kb][2], S[ct][2 * kb][3]);
                 Sb[kb][2] = pack2(S[ct][2 * kb + 1][0], S[ct][2 * kb + 1][1]);
@@ -270,27 +306,21 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
             // P in two independent halves (a shorter dependent MFMA chain on
             // the serial path); v into the accumulator layout
             f32x4_t P0 = zero, P1 = zero, Qs = zero;
-            P0 = mfma_k32(op.kt[0], Sb[0], P0);
-            P1 = mfma_k32(op.kt[2], Sb[2], P1);
-            P0 = mfma_k32(op.kt[1], Sb[1], P0);
-            P1 = mfma_k32(op.kt[3], Sb[3], P1);
+#pragma unroll
+            for (int i = 0; i < NKB / 2; ++i) {
+                P0 = mfma_k32(op.kt[i], Sb[i], P0);
+                P1 = mfma_k32(op.kt[NKB / 2 + i], Sb[NKB / 2 + i], P1);
+            }
             const f32x4_t vv = mfma_k16(op.v[ct], eye, zero);
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) Qs = mfma_k32(op.qt[kb], Sb[kb], Qs);
+            for (int kb = 0; kb < NKB; ++kb) Qs = mfma_k32(op.qt[kb], Sb[kb], Qs);
             // decayed old state: the accumulator the update MFMAs add W^T X to
-#define KDA_DECAY(T_)                                              \
-            S[ct][T_][0] *= decay_of<T_, 0>(op.gm);                \
-            S[ct][T_][1] *= decay_of<T_, 1>(op.gm);                \
-            S[ct][T_][2] *= decay_of<T_, 2>(op.gm);                \
-            S[ct][T_][3] *= decay_of<T_, 3>(op.gm);
-            KDA_DECAY(0) KDA_DECAY(1) KDA_DECAY(2) KDA_DECAY(3)
-            KDA_DECAY(4) KDA_DECAY(5) KDA_DECAY(6) KDA_DECAY(7)
-#undef KDA_DECAY
+            decay_tiles<0, NT>(S[ct], op.gm);
             u32x2_t Xb;
             Xb[0] = pack2(vv[0] - (P0[0] + P1[0]), vv[1] - (P0[1] + P1[1]));
             Xb[1] = pack2(vv[2] - (P0[2] + P1[2]), vv[3] - (P0[3] + P1[3]));
 #pragma unroll
-            for (int tp = 0; tp < 4; ++tp) {
+            for (int tp = 0; tp < NKB; ++tp) {
                 u32x2_t lo = {op.wt[tp][0], op.wt[tp][1]}, hi = {op.wt[tp][2], op.wt[tp][3]};
                 S[ct][2 * tp] = mfma_k16(lo, Xb, S[ct][2 * tp]);
                 S[ct][2 * tp + 1] = mfma_k16(hi, Xb, S[ct][2 * tp + 1]);
@@ -316,6 +346,35 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
     // in order, UNITS DMAs each, so at the top of iteration c the DMAs issued
     // after chunk c+1's number (DEPTH-2) UNITS (and (DEPTH-1) UNITS after
     // chunk 0's before the first iteration).
+    if constexpr (WIDE) {
+        // 256-wide tiles.  Iteration c: the DMA wave waits for chunk c to
+        // land, the compute waves finish their reads of chunk c-1, all the
+        // waves meet at a barrier; then the compute waves read chunk c and
+        // compute it while the DMA wave refills chunk c-1's slot with chunk
+        // c-1+DEPTH.  DEPTH-1 chunks are issued before the first iteration,
+        // so at the top of iteration c the DMAs issued after chunk c's number
+        // (DEPTH-2) UNITS.
+        if (dma_wave) {
+#pragma unroll
+            for (int c = 0; c < DEPTH - 1; ++c) issue(c, c);
+            int slot = DEPTH - 1;                    // ring slot of chunk c-1
+            for (int c = 0; c < nch; ++c) {
+                wait_vm_barrier<(DEPTH - 2) * UNITS>();  // chunk c landed; slot of c-1 free
+                issue(c - 1 + DEPTH, slot);
+                slot = slot == DEPTH - 1 ? 0 : slot + 1;
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            return;
+        }
+        ChunkOps<CT, NKB> op;
+        int cur = 0;                                 // ring slot of chunk c
+        for (int c = 0; c < nch; ++c) {
+            lds_barrier();                           // own reads of chunk c-1 done; chunk c landed
+            load_ops(cur, op);
+            compute(c, op);
+            cur = cur == DEPTH - 1 ? 0 : cur + 1;
+        }
+    } else {
     if (dma_wave) {
 #pragma unroll
         for (int c = 0; c < DEPTH; ++c) issue(c, c);
@@ -332,10 +391,10 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
     }
     lds_barrier();                                   // chunk 0 landed
 
-    ChunkOps<CT> opA, opB;
+    ChunkOps<CT, NKB> opA, opB;
     load_ops(0, opA);
     int next = 1;                                     // ring slot of chunk c+1
-    auto step = [&](int c, const ChunkOps<CT> &cur, ChunkOps<CT> &nxt) {
+    auto step = [&](int c, const ChunkOps<CT, NKB> &cur, ChunkOps<CT, NKB> &nxt) {
         lds_barrier();                               // own reads of chunk c done; chunk c+1 landed
         load_ops(next, nxt);
         compute(c, cur);
@@ -344,6 +403,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
     for (int c = 0; c < nch; c += 2) {
         step(c, opA, opB);
         if (c + 1 < nch) step(c + 1, opB, opA);
+    }
     }
 
     if (fin) {
@@ -354,7 +414,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int t = 0; t < 8; ++t)
+                for (int t = 0; t < NT; ++t)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int idx = state_chan(t, 4 * grp + j) * V + col0 + wcol0 + 16 * ct + cg;
@@ -364,7 +424,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void scan_kernel(
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int t = 0; t < 8; ++t)
+                for (int t = 0; t < NT; ++t)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int idx = state_chan(t, 4 * grp + j) * V + col0 + wcol0 + 16 * ct + cg;
@@ -399,7 +459,9 @@ hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, 
     // workgroups (of fewer compute waves) so that more compute units share
     // the scan.  Parts of 32, 64 or 128 columns; V / part workgroups a head.
     const int cus = num_cus();
-    const int cw = (V == 128 ? 4 : 2) * units <= cus ? 32 : (V == 128 ? 2 : 1) * units <= cus ? 64 : 128;
+    // (head dimension 256: parts of 32 or 64 columns, one slice per wave)
+    const int cw = V == 2 * HD ? (8 * units <= cus ? 32 : 64)
+                 : (V == 128 ? 4 : 2) * units <= cus ? 32 : (V == 128 ? 2 : 1) * units <= cus ? 64 : 128;
     const int part_cw = cw > V ? V : cw;
     const int64_t blocks = 8 * (V / part_cw) * ((units + 7) / 8);
 #define KDA_SCAN(CT_, NW_, VD_)                                                               \
@@ -409,6 +471,9 @@ hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, 
         if (part_cw == 32) KDA_SCAN(1, 2, HD);
         else if (part_cw == 64) KDA_SCAN(1, 4, HD);
         else KDA_SCAN(2, 4, HD);
+    } else if (V == 2 * HD) {
+        if (part_cw == 32) KDA_SCAN(1, 2, 2 * HD);
+        else KDA_SCAN(1, 4, 2 * HD);
     } else {
         if (part_cw == 32) KDA_SCAN(1, 2, 64);
         else KDA_SCAN(1, 4, 64);

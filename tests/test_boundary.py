@@ -65,6 +65,11 @@ def test_workspace_size(lib):
     assert kda.workspace_size(3, 37, 2, 3) == (111 // 16 + 3) * 2 * 13312
     assert kda.workspace_size(0, 16, 1, 1) == 0
     assert kda.workspace_size(1, 16, 1, 0) == 0
+    # head dimension 64 shares the 128-wide records; 256 takes 26 KB ones
+    assert kda.workspace_size(1, 8192, 96, 1, K=64) == (8192 // 16 + 1) * 96 * 13312
+    assert kda.workspace_size(1, 8192, 96, 1, K=256) == (8192 // 16 + 1) * 96 * 26624
+    assert kda.workspace_size(1, 8192, 96, 1, K=96) == 0
+    assert lib.kda_workspace_size(1, 100, 3, 1) == kda.workspace_size(1, 100, 3, 1, K=128)
 
 
 def call_fwd(lib, **over):
@@ -85,8 +90,9 @@ def call_fwd(lib, **over):
     (dict(out=None), INVALID),
     (dict(q=FAKE + 8), INVALID), (dict(out=FAKE + 2), INVALID), (dict(beta=FAKE + 1), INVALID),
     (dict(A_log=FAKE + 2), INVALID), (dict(init=FAKE + 4), INVALID),
-    (dict(K=64), UNSUPPORTED), (dict(V=256), UNSUPPORTED), (dict(K=256, V=256), UNSUPPORTED),
+    (dict(K=64), UNSUPPORTED), (dict(V=256), UNSUPPORTED), (dict(K=256, V=128), UNSUPPORTED),
     (dict(K=64, V=128), UNSUPPORTED), (dict(K=32, V=32), UNSUPPORTED),
+    (dict(K=512, V=512), UNSUPPORTED), (dict(K=192, V=192), UNSUPPORTED),
     (dict(B=0), INVALID), (dict(T=-1), INVALID), (dict(H=0), INVALID),
     (dict(N=2), INVALID),                              # fixed length needs N == B
     (dict(cu=FAKE, B=2, N=2), INVALID),                # cu_seqlens needs B == 1
@@ -149,7 +155,7 @@ def test_debug_intra_validates(lib):
     f = lambda **o: lib.kda_debug_intra(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None,
                                         o.get("lb", -5.0), None, 1, 1, 16, 1, o.get("K", 128),
                                         o.get("ws", P(FAKE)), None)
-    assert f(K=256) == UNSUPPORTED and f(K=32) == UNSUPPORTED
+    assert f(K=512) == UNSUPPORTED and f(K=32) == UNSUPPORTED
     assert f(lb=-7.0) == UNSUPPORTED
     assert f(ws=None) == INVALID
 

@@ -86,3 +86,61 @@ def test_dma_wait_ladder(cw, nch):
         slot = 0 if slot == depth - 1 else slot + 1
     wait(0)                          # the final drain
     assert completed == len(issued)
+
+
+REC_BYTES_256 = 26624                # head dimension 256: 26 KB records
+
+
+def test_wide_source_constants_match_model():
+    src = open(SCAN).read()
+    assert re.search(r"RING_DEPTH_256\s*=\s*4;", src)
+    assert "for (int c = 0; c < DEPTH - 1; ++c) issue(c, c);" in src
+    assert "issue(c - 1 + DEPTH, slot);" in src
+
+
+@pytest.mark.parametrize("cw", [32, 64])
+@pytest.mark.parametrize("nch", [0, 1, 2, 3, 4, 5, 7, 64])
+def test_dma_wait_ladder_wide(cw, nch):
+    """The 256-wide protocol: DEPTH-1 chunks issued before the first
+    iteration; at the top of iteration c a wait of (DEPTH-2) x UNITS leaves
+    chunk c landed; after the barrier the compute waves read chunk c (their
+    reads of chunk c-1 completed before it) and the DMA wave refills chunk
+    c-1's slot with chunk c-1+DEPTH."""
+    rec_kb = REC_BYTES_256 // 1024
+    v_kb = CS * cw * 2 // 1024
+    units = rec_kb + v_kb
+    depth = 4
+    assert (depth - 2) * units <= VMCNT_MAX
+
+    issued, completed = [], 0
+    slot_of = {}
+
+    def issue(c, slot):
+        issued.extend([c] * units)
+        slot_of[c] = slot
+
+    def wait(n):
+        nonlocal completed
+        completed = max(completed, len(issued) - n)
+
+    def landed(c):
+        return all(i < completed for i, x in enumerate(issued) if x == c)
+
+    for c in range(depth - 1):
+        issue(c, c)
+    reading = None                   # chunk whose slot the compute waves read
+    slot = depth - 1
+    for c in range(nch):
+        wait((depth - 2) * units)
+        assert landed(c), (cw, nch, c)
+        # barrier: reads of chunk c-1 are complete; the compute waves read chunk c
+        reading = c
+        assert slot_of[c] == c % depth
+        assert slot == (c - 1) % depth
+        # the slot refilled now holds chunk c-1 (done) or nothing yet
+        holder = [x for x, s in slot_of.items() if s == slot]
+        assert all(x <= c - 1 for x in holder) and reading not in holder
+        issue(c - 1 + depth, slot)
+        slot = 0 if slot == depth - 1 else slot + 1
+    wait(0)
+    assert completed == len(issued)
