@@ -90,16 +90,19 @@ def load():
     return lib
 
 
+# The sources the forward kernels (intra stage and scan) are compiled from.
+FORWARD_KERNEL_SOURCES = ("kda_device.h", "kda_intra_dev.h", "kda_intra.hip", "kda_scan.hip")
+
+
 def source_digest() -> str:
-    """sha256 over the HIP sources of the library (identifies the kernels a
-    stored profile was taken on)."""
+    """sha256 over the sources of the forward kernels (identifies the kernels
+    a stored profile of the forward was taken on)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(_HERE, "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in FORWARD_KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
