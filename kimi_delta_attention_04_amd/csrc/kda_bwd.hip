@@ -62,10 +62,18 @@ constexpr int BR_M = 3 * CS * HD;
 constexpr int BR_GAM = 3 * CS * HD + CS * CS;
 constexpr int BR_FLOATS = BR_GAM + HD;
 
+// The transcendentals on the hardware base-2 units (v_exp_f32, v_log_f32,
+// v_rcp_f32).  softplus keeps the form max(x, 0) + log(1 + e^-|x|), finite
+// for every finite x, so that -exp(A_log) softplus(x) is -0, not NaN, when
+// A_log = -inf.
+constexpr float LN2 = 0.6931471805599453f;
 __device__ __forceinline__ float softplus_f(float x) {
-    return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+    return fmaxf(x, 0.f) + LN2 * fast_log2(1.f + fast_exp2(-fabsf(x) * LOG2E));
 }
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float sigmoid_f(float x) {
+    return __builtin_amdgcn_rcpf(1.f + fast_exp2(-x * LOG2E));
+}
+__device__ __forceinline__ float exp_f(float x) { return fast_exp2(x * LOG2E); }
 
 // Token range of chunk slot `slot`: returns its token count (0 for a gap
 // slot) and the first token row in t0.
@@ -92,7 +100,7 @@ struct Factors {
     float beta[CS], gam[HD], dtb[HD];
 };
 
-__device__ void chunk_factors(Factors &L, const uint16_t *__restrict__ q,
+__device__ __forceinline__ void chunk_factors(Factors &L, const uint16_t *__restrict__ q,
                               const uint16_t *__restrict__ k, const uint16_t *__restrict__ g,
                               const uint16_t *__restrict__ bl, float Aexp,
                               const float *__restrict__ dt_bias, float lb, int64_t t0, int len,
@@ -104,21 +112,30 @@ __device__ void chunk_factors(Factors &L, const uint16_t *__restrict__ q,
         const int c = tid;
         const float dtb = dt_bias ? dt_bias[(size_t)h * HD + c] : 0.f;
         L.dtb[c] = dtb;
+        // every row's loads first, so that their latencies overlap (rows
+        // past len read row len-1 and are masked below)
+        float gr[CS], kr[CS], qr[CS];
+#pragma unroll
+        for (int r = 0; r < CS; ++r) {
+            const size_t off = ((size_t)(t0 + (r < len ? r : len - 1)) * H + h) * HD + c;
+            gr[r] = bf16f(g[off]);
+            kr[r] = bf16f(k[off]);
+            qr[r] = bf16f(q[off]);
+        }
         float G = 0.f;
 #pragma unroll
         for (int r = 0; r < CS; ++r) {
             float kv = 0.f, qv = 0.f;
             if (r < len) {
-                const size_t off = ((size_t)(t0 + r) * H + h) * HD + c;
-                G += fmaxf(-Aexp * softplus_f(bf16f(g[off]) + dtb), lb);
-                kv = bf16f(k[off]);
-                qv = bf16f(q[off]);
+                G += fmaxf(-Aexp * softplus_f(gr[r] + dtb), lb);
+                kv = kr[r];
+                qv = qr[r];
             }
-            const float e = expf(G);
+            const float e = exp_f(G);
             L.e[r][c] = e;
             L.kt[r][c] = kv * e;
             L.qt[r][c] = qv * e;
-            L.kb[r][c] = kv * expf(-G);
+            L.kb[r][c] = kv * exp_f(-G);
         }
         L.gam[c] = L.e[CS - 1][c];
     } else if (tid < HD + CS) {
@@ -537,9 +554,20 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
     const float Aexp = expf(A_log[h]);
     chunk_factors(F, q, k, g, beta, Aexp, dt_bias, lb, t0, len, H, h);
 
-    for (int idx = tid; idx < CS * HD; idx += BT) {
-        const int r = idx / HD, c = idx % HD;
-        L.dol[r][c] = r < len ? scale * bf16f(dout[((size_t)(t0 + r) * H + h) * HD + c]) : 0.f;
+    {
+        // all eight loads of this thread first (rows past len read row
+        // len-1 and are masked)
+        float dov[CS * HD / BT];
+#pragma unroll
+        for (int m = 0; m < CS * HD / BT; ++m) {
+            const int idx = tid + m * BT, r = idx / HD, c = idx % HD;
+            dov[m] = bf16f(dout[((size_t)(t0 + (r < len ? r : len - 1)) * H + h) * HD + c]);
+        }
+#pragma unroll
+        for (int m = 0; m < CS * HD / BT; ++m) {
+            const int idx = tid + m * BT, r = idx / HD, c = idx % HD;
+            L.dol[r][c] = r < len ? scale * dov[m] : 0.f;
+        }
     }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -694,14 +722,19 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
         // reverse cumulative sum of dG is the gradient of the per-token log-decay;
         // then the gate chain
         const int c = tid;
+        float gs[CS];                                   // loads first (rows past len masked)
+#pragma unroll
+        for (int s = 0; s < CS; ++s)
+            gs[s] = bf16f(g[((size_t)(t0 + (s < len ? s : len - 1)) * H + h) * HD + c]);
         const float dgam = L.dgam[c] + L.dgam2[0][c] + L.dgam2[1][c];
         float acc = dgam * F.gam[c];
         float pdtb = 0.f, pa = 0.f;
+#pragma unroll
         for (int s = CS - 1; s >= 0; --s) {
             acc += L.dqt[s][c];
             if (s < len) {
                 const size_t off = ((size_t)(t0 + s) * H + h) * HD + c;
-                const float x = bf16f(g[off]) + F.dtb[c];
+                const float x = gs[s] + F.dtb[c];
                 const float y = -Aexp * softplus_f(x);
                 const float dy = y >= lb ? acc : 0.f;
                 const float dx = -dy * Aexp * sigmoid_f(x);
