@@ -100,6 +100,8 @@ struct Factors {
     float beta[CS], gam[HD], dtb[HD];
 };
 
+// WANT_W: also form Wm (the prep kernel stores it; the chunk kernel does not use it).
+template <bool WANT_W>
 __device__ __forceinline__ void chunk_factors(Factors &L, const uint16_t *__restrict__ q,
                               const uint16_t *__restrict__ k, const uint16_t *__restrict__ g,
                               const uint16_t *__restrict__ bl, float Aexp,
@@ -144,18 +146,25 @@ __device__ __forceinline__ void chunk_factors(Factors &L, const uint16_t *__rest
     }
     __syncthreads();
     {
-        // A = strict_lower(Kt Kb^T), Aqk = lower_incl(Qt Kb^T)
-        const int r = tid >> 4, i = tid & 15;
-        float a = 0.f, aq = 0.f;
-        for (int c = 0; c < HD; c += 4) {
-            const float4 b4 = *(const float4 *)&L.kb[i][c];
-            const float4 t4 = *(const float4 *)&L.kt[r][c];
-            const float4 q4 = *(const float4 *)&L.qt[r][c];
-            a += t4.x * b4.x + t4.y * b4.y + t4.z * b4.z + t4.w * b4.w;
-            aq += q4.x * b4.x + q4.y * b4.y + q4.z * b4.z + q4.w * b4.w;
+        // A = strict_lower(Kt Kb^T) on wave 0, Aqk = lower_incl(Qt Kb^T) on
+        // wave 1: fp32 16x16x4 MFMAs over the 128 channels (lane l supplies
+        // row l%16, channel 4ks + l/16 of each operand and holds rows
+        // 4(l/16) .. +3, column l%16 of the product)
+        const int wave = tid >> 6, l = tid & 63;
+        if (wave < 2) {
+            const float(&lhs)[CS][RS] = wave == 0 ? L.kt : L.qt;
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+            for (int ks = 0; ks < HD / 4; ++ks)
+                acc = mfma_k4(lhs[l & 15][4 * ks + (l >> 4)], L.kb[l & 15][4 * ks + (l >> 4)], acc);
+            const int i = l & 15;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * (l >> 4) + j;
+                if (wave == 0) L.A[r][i] = i < r ? acc[j] : 0.f;
+                else L.aqk[r][i] = i <= r ? acc[j] : 0.f;
+            }
         }
-        L.A[r][i] = i < r ? a : 0.f;
-        L.aqk[r][i] = i <= r ? aq : 0.f;
     }
     __syncthreads();
     if (tid < CS) {
@@ -185,12 +194,14 @@ __device__ __forceinline__ void chunk_factors(Factors &L, const uint16_t *__rest
         float m = 0.f;
         for (int s = 0; s < CS; ++s) m += L.aqk[r][s] * L.P[s][i];
         L.M[r][i] = m;
-        const int c = tid & (HD - 1), i0 = tid >> 7;
-        for (int mm = 0; mm < CS / 2; ++mm) {
-            const int ii = i0 + 2 * mm;
-            float w = 0.f;
-            for (int s = 0; s < CS; ++s) w += L.P[s][ii] * L.kb[s][c];
-            L.wm[ii][c] = w * L.gam[c];
+        if constexpr (WANT_W) {
+            const int c = tid & (HD - 1), i0 = tid >> 7;
+            for (int mm = 0; mm < CS / 2; ++mm) {
+                const int ii = i0 + 2 * mm;
+                float w = 0.f;
+                for (int s = 0; s < CS; ++s) w += L.P[s][ii] * L.kb[s][c];
+                L.wm[ii][c] = w * L.gam[c];
+            }
         }
     }
     __syncthreads();
@@ -211,7 +222,7 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(
     int64_t t0;
     const int len = slot_chunk(cu, N, T, slot, t0);
     if (len == 0) return;                                   // gap slot
-    chunk_factors(L, q, k, g, beta, expf(A_log[h]), dt_bias, lb, t0, len, H, h);
+    chunk_factors<true>(L, q, k, g, beta, expf(A_log[h]), dt_bias, lb, t0, len, H, h);
     float *rec = brec + ((size_t)slot * H + h) * BR_FLOATS;
     const int tid = threadIdx.x;
     for (int idx = tid; idx < CS * HD; idx += BT) {
@@ -552,7 +563,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
     fetch_state_block(qs0, qs1, S0, 1);
     fetch_state_block(qd0, qd1, DS, 1);
     const float Aexp = expf(A_log[h]);
-    chunk_factors(F, q, k, g, beta, Aexp, dt_bias, lb, t0, len, H, h);
+    chunk_factors<false>(F, q, k, g, beta, Aexp, dt_bias, lb, t0, len, H, h);
 
     {
         // all eight loads of this thread first (rows past len read row
