@@ -158,7 +158,8 @@ kda_status_t kda_fwd_scalar_gate(const void *q, const void *k, const void *v, co
  *   state       [N, H, K, V] in state_dtype (bf16 or fp32), read and
  *               overwritten with the updated state (bf16: round to nearest
  *               even); the arithmetic is fp32 either way
- *   N, H, K, V  sizes; N, H >= 1; K and V must both be 128
+ *   N, H, K, V  sizes; N, H >= 1; K = V = 64, 128 or 256 (one workgroup
+ *               of K*K/64 threads per (sequence, head))
  *
  * No workspace.  Returns KDA_OK, KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED
  * before any HIP call, or KDA_ERR_LAUNCH.

@@ -241,11 +241,11 @@ kda_status_t kda_decode(const void *q, const void *k, const void *v, const void 
     if (state_dtype != KDA_DTYPE_BF16 && state_dtype != KDA_DTYPE_FP32) return KDA_ERR_INVALID_ARG;
     if (!isfinite(scale) || !isfinite(lower_bound) || lower_bound > 0.f) return KDA_ERR_INVALID_ARG;
     if (N < 1 || H < 1) return KDA_ERR_INVALID_ARG;
-    if (K != kda::HD || V != kda::HD) return KDA_ERR_UNSUPPORTED;
+    if (K != V || (K != 64 && K != kda::HD && K != 2 * kda::HD)) return KDA_ERR_UNSUPPORTED;
     if ((int64_t)N * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     hipError_t e = kda::launch_decode((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v,
                                       (const uint16_t *)g, (const uint16_t *)beta, scale, A_log,
-                                      dt_bias, lower_bound, N, H, state,
+                                      dt_bias, lower_bound, N, H, K, state,
                                       state_dtype == KDA_DTYPE_FP32, (uint16_t *)out,
                                       (hipStream_t)stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;

@@ -12,14 +12,15 @@
 //
 // which is the token recurrence of the prefill for a single token.
 //
-// One 256-thread workgroup per (sequence, head).  Thread t holds the 16 x 4
-// block of the state at rows 16 (t / 32) .. +15 and columns 4 (t % 32) .. +3
-// in registers: each state row is read and written by 32 consecutive lanes
-// as 512 contiguous bytes.  The two contractions over rows (S^T k, S^T q)
-// are summed per thread over its 16 rows and then over the eight row groups
-// through LDS, in a fixed order.  The step moves the whole state through
-// HBM twice (read and write), so it is HBM-bound: 128 KiB per (sequence,
-// head) for an fp32 state.
+// One workgroup of D^2 / 64 threads per (sequence, head), head dimension
+// K = V = D (64, 128 or 256: 64, 256 or 1024 threads).  Thread t holds the
+// 16 x 4 block of the state at rows 16 (t / (D/4)) .. +15 and columns
+// 4 (t % (D/4)) .. +3 in registers: each state row is read and written by
+// D/4 consecutive lanes as one contiguous row.  The two contractions over
+// rows (S^T k, S^T q) are summed per thread over its 16 rows and then over
+// the D/16 row groups through LDS, in a fixed order.  The step moves the
+// whole state through HBM twice (read and write), so it is HBM-bound:
+// 128 KiB per (sequence, head) for an fp32 state at D = 128.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -27,33 +28,34 @@ namespace kda {
 
 namespace {
 
-constexpr int DEC_THREADS = 256;
-constexpr int DEC_RG = DEC_THREADS / 32;   // row groups of 16 rows
-static_assert(DEC_RG * 16 == HD, "row groups cover the state");
+template <int D> constexpr int DEC_THREADS = D * D / 64;
 
-template <bool F32>
-__global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
+template <bool F32, int D>
+__global__ __launch_bounds__(DEC_THREADS<D>) void decode_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ g,
     const uint16_t *__restrict__ beta, float scale, const float *__restrict__ A_log,
     const float *__restrict__ dt_bias, float lb2, int H, void *__restrict__ state,
     uint16_t *__restrict__ out)
 {
+    constexpr int CG = D / 4;                    // column groups of 4 columns
+    constexpr int RG = D / 16;                   // row groups of 16 rows
+    static_assert(CG * RG == DEC_THREADS<D>, "one 16 x 4 block per thread");
     const int u = blockIdx.x;                    // (n, h) pair, n-major
     const int h = u % H;
     const int t = threadIdx.x;
-    const int cgp = t & 31, rg = t >> 5;
-    __shared__ float kk[HD], qq[HD], al[HD];
-    __shared__ f32x4_t part[DEC_RG][32];
-    const size_t vec = (size_t)u * HD;
+    const int cgp = t % CG, rg = t / CG;
+    __shared__ float kk[D], qq[D], al[D];
+    __shared__ f32x4_t part[RG][CG];
+    const size_t vec = (size_t)u * D;
 
     // per-channel decay in base 2 and the key / query vectors
-    if (t < HD) {
+    if (t < D) {
         const float A = expf(A_log[h]);
         float la2 = 0.f;                         // A = 0 (A_log = -inf): no decay
         if (A > 0.f) {
             const float x2 = bf16f(g[vec + t]) * LOG2E +
-                             (dt_bias ? dt_bias[(size_t)h * HD + t] * LOG2E : 0.f);
+                             (dt_bias ? dt_bias[(size_t)h * D + t] * LOG2E : 0.f);
             la2 = fmaxf(-A * fast_log2(1.f + fast_exp2(x2)), lb2);
         }
         al[t] = fast_exp2(la2);
@@ -64,16 +66,16 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     __syncthreads();
 
     // this thread's 16 x 4 block of the state
-    const size_t base = (size_t)u * HD * HD + (size_t)(16 * rg) * HD + 4 * cgp;
+    const size_t base = (size_t)u * D * D + (size_t)(16 * rg) * D + 4 * cgp;
     float S[16][4];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         if (F32) {
-            const f32x4_t x = *(const f32x4_t *)((const float *)state + base + (size_t)r * HD);
+            const f32x4_t x = *(const f32x4_t *)((const float *)state + base + (size_t)r * D);
 #pragma unroll
             for (int c = 0; c < 4; ++c) S[r][c] = x[c];
         } else {
-            const u32x2_t x = *(const u32x2_t *)((const uint16_t *)state + base + (size_t)r * HD);
+            const u32x2_t x = *(const u32x2_t *)((const uint16_t *)state + base + (size_t)r * D);
             S[r][0] = bf16lo(x[0]); S[r][1] = bf16hi(x[0]);
             S[r][2] = bf16lo(x[1]); S[r][3] = bf16hi(x[1]);
         }
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     __syncthreads();
     f32x4_t su = part[0][cgp];
 #pragma unroll
-    for (int j = 1; j < DEC_RG; ++j) su += part[j][cgp];
+    for (int j = 1; j < RG; ++j) su += part[j][cgp];
     const u32x2_t vw = *(const u32x2_t *)(v + vec + 4 * cgp);
     const float vv[4] = {bf16lo(vw[0]), bf16hi(vw[0]), bf16lo(vw[1]), bf16hi(vw[1])};
     float d[4];
@@ -114,10 +116,10 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
         }
         if (F32) {
             const f32x4_t x = {S[r][0], S[r][1], S[r][2], S[r][3]};
-            *(f32x4_t *)((float *)state + base + (size_t)r * HD) = x;
+            *(f32x4_t *)((float *)state + base + (size_t)r * D) = x;
         } else {
             const u32x2_t x = {pack2(S[r][0], S[r][1]), pack2(S[r][2], S[r][3])};
-            *(u32x2_t *)((uint16_t *)state + base + (size_t)r * HD) = x;
+            *(u32x2_t *)((uint16_t *)state + base + (size_t)r * D) = x;
         }
     }
     part[rg][cgp] = po;
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     if (rg == 0) {
         f32x4_t so = part[0][cgp];
 #pragma unroll
-        for (int j = 1; j < DEC_RG; ++j) so += part[j][cgp];
+        for (int j = 1; j < RG; ++j) so += part[j][cgp];
         const u32x2_t o = {pack2(scale * so[0], scale * so[1]), pack2(scale * so[2], scale * so[3])};
         *(u32x2_t *)(out + vec + 4 * cgp) = o;
     }
@@ -136,17 +138,23 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
 hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const uint16_t *g, const uint16_t *beta, float scale,
                          const float *A_log, const float *dt_bias, float lower_bound, int N,
-                         int H, void *state, int state_fp32, uint16_t *out, hipStream_t stream)
+                         int H, int D, void *state, int state_fp32, uint16_t *out,
+                         hipStream_t stream)
 {
     const unsigned blocks = (unsigned)((int64_t)N * H);
     if (blocks == 0) return hipSuccess;
     const float lb2 = lower_bound * LOG2E;
-    if (state_fp32)
-        hipLaunchKernelGGL(decode_kernel<true>, dim3(blocks), dim3(DEC_THREADS), 0, stream,
-                           q, k, v, g, beta, scale, A_log, dt_bias, lb2, H, state, out);
-    else
-        hipLaunchKernelGGL(decode_kernel<false>, dim3(blocks), dim3(DEC_THREADS), 0, stream,
-                           q, k, v, g, beta, scale, A_log, dt_bias, lb2, H, state, out);
+#define KDA_DECODE(F32_, D_)                                                                  \
+    hipLaunchKernelGGL((decode_kernel<F32_, D_>), dim3(blocks), dim3(DEC_THREADS<D_>), 0, stream, \
+                       q, k, v, g, beta, scale, A_log, dt_bias, lb2, H, state, out)
+    if (D == 64) {
+        if (state_fp32) KDA_DECODE(true, 64); else KDA_DECODE(false, 64);
+    } else if (D == 256) {
+        if (state_fp32) KDA_DECODE(true, 256); else KDA_DECODE(false, 256);
+    } else {
+        if (state_fp32) KDA_DECODE(true, 128); else KDA_DECODE(false, 128);
+    }
+#undef KDA_DECODE
     return hipGetLastError();
 }
 

@@ -23,11 +23,13 @@ hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, 
                        int H, int K, int V, float scale, const void *init, int init_fp32,
                        void *fin, int fin_fp32, uint16_t *out, hipStream_t stream);
 
-// One-token decode step on N x H states in place (fp32 or bf16).
+// One-token decode step on N x H states of D x D (D = 64, 128 or 256) in
+// place (fp32 or bf16).
 hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const uint16_t *g, const uint16_t *beta, float scale,
                          const float *A_log, const float *dt_bias, float lower_bound, int N,
-                         int H, void *state, int state_fp32, uint16_t *out, hipStream_t stream);
+                         int H, int D, void *state, int state_fp32, uint16_t *out,
+                         hipStream_t stream);
 
 // Backward pass (K = V = 128): five launches on `stream` using the caller's
 // workspace of bwd_workspace_bytes(num_slots, H) bytes (16-byte aligned).

@@ -144,7 +144,8 @@ def call_decode(lib, **over):
     (dict(A_log=None), INVALID), (dict(beta=FAKE + 1), INVALID), (dict(state=FAKE + 8), INVALID),
     (dict(st_dt=2), INVALID), (dict(scale=float("nan")), INVALID), (dict(lb=0.5), INVALID),
     (dict(lb=float("-inf")), INVALID), (dict(N=0), INVALID), (dict(H=0), INVALID),
-    (dict(K=64), UNSUPPORTED), (dict(V=256), UNSUPPORTED), (dict(N=2 ** 20, H=2 ** 12), UNSUPPORTED),
+    (dict(K=64), UNSUPPORTED), (dict(V=256), UNSUPPORTED), (dict(K=96, V=96), UNSUPPORTED),
+    (dict(K=512, V=512), UNSUPPORTED), (dict(N=2 ** 20, H=2 ** 12), UNSUPPORTED),
 ])
 def test_decode_rejects_before_any_hip_call(lib, over, code):
     assert call_decode(lib, **over) == code

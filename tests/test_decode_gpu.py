@@ -32,11 +32,12 @@ def _need_gpu():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
 
 
-def single_token_inputs(seed, N, H, state_dtype, state_std=0.05):
-    """N one-token sequences (B = N, T = 1) with a random initial state."""
-    inp = kda_inputs.random_small(seed, B=N, T=1, H=H)
+def single_token_inputs(seed, N, H, state_dtype, state_std=0.05, D=128):
+    """N one-token sequences (B = N, T = 1) with a random initial state;
+    head dimension K = V = D."""
+    inp = kda_inputs.random_small(seed, B=N, T=1, H=H, K=D, V=D)
     gen = torch.Generator().manual_seed(10_000 + seed)
-    st = torch.randn(N, H, 128, 128, generator=gen) * state_std
+    st = torch.randn(N, H, D, D, generator=gen) * state_std
     inp["initial_state"] = st.to(state_dtype)
     return inp
 
@@ -47,7 +48,7 @@ def run_decode(inp, state):
     d = to_device(inp)
     N, _, H, K = d["q"].shape
     flat = lambda t: t.reshape(N, H, -1).contiguous()
-    out = torch.full((N, H, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((N, H, d["v"].shape[-1]), float("nan"), dtype=torch.bfloat16, device="cuda")
     kda.decode(flat(d["q"]), flat(d["k"]), flat(d["v"]), flat(d["g"]),
                d["beta"].reshape(N, H).contiguous(), d["scale"], out, d["A_log"],
                d.get("dt_bias"), d["lower_bound"], state)
@@ -154,3 +155,31 @@ def test_decode_batch64_h96_sampled_heads():
     state = inp["initial_state"].cuda()
     out = run_decode(inp, state)
     check(inp, out, state, state_tol=STATE_FP32_TOL, heads=[0, 31, 64, 95])
+
+
+@pytest.mark.parametrize("state_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("N,H", [(1, 1), (5, 3)])
+def test_other_head_dims_match_oracle(D, N, H, state_dtype):
+    """Head dimension 64 and 256: 64 and 1024 threads per (sequence, head)."""
+    inp = single_token_inputs(31 * N + H + D, N, H, state_dtype, D=D)
+    state = inp["initial_state"].cuda()
+    out = run_decode(inp, state)
+    check(inp, out, state, state_tol=STATE_FP32_TOL if state_dtype == torch.float32 else None)
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_other_head_dims_prefill_then_decode(D):
+    T = 37
+    full = kda_inputs.random_small(600 + D, B=1, T=T + 1, H=2, K=D, V=D, initial_state=True)
+    head = dict(full)
+    step = dict(full)
+    for name in ("q", "k", "v", "g", "beta"):
+        head[name] = full[name][:, :T].contiguous()
+        step[name] = full[name][:, T:].contiguous()
+    _, fin = run_kda(to_device(head), final_dtype=torch.float32)
+    out = run_decode(step, fin)
+    o_ref, f_ref = oracle.cref_forward(full)
+    ro = assert_close("o", np64(out)[:, None], o_ref[:, T:])
+    rf = assert_close("state", np64(fin), f_ref)
+    print(f"D={D}: o rel_l2={ro[0]:.3e}; state rel_l2={rf[0]:.3e}", flush=True)
