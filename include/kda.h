@@ -2,7 +2,7 @@
  * libkda — Kimi Delta Attention (KDA) chunked forward (prefill) for AMD
  * MI355X (gfx950).
  *
- * Operation (per sequence n, head h; state S is K x V, here K = V = 128):
+ * Operation (per sequence n, head h; state S is K x V, K = V = 64, 128 or 256):
  *
  *   a_t[c]  = max(-exp(A_log[h]) * softplus(g_t[c] + dt_bias[h*K + c]),
  *                 lower_bound)                      (log-decay, natural log)
@@ -19,7 +19,7 @@
  * clamped softplus form above is the reading this library implements.  The
  * original supports only K = V = 128 ("Moonshot AI Open-Sources FlashKDA",
  * section "Limitations before you integrate"); this library also takes
- * K = V = 64 and K = V = 256 in kda_fwd and kda_fwd_scalar_gate.  The
+ * K = V = 64 and K = V = 256 in kda_fwd, kda_fwd_scalar_gate and kda_decode.  The
  * original ships only the forward pass (same section); kda_bwd here adds
  * the gradients (K = V = 128).
  *
