@@ -21,7 +21,7 @@
  * section "Limitations before you integrate"); this library also takes
  * K = V = 64 and K = V = 256 in kda_fwd, kda_fwd_scalar_gate and kda_decode.  The
  * original ships only the forward pass (same section); kda_bwd here adds
- * the gradients (K = V = 128).
+ * the gradients (K = V = 64 or 128).
  *
  * Conventions shared by every entry point:
  *   - Pointers are device pointers unless stated; every tensor is dense and
@@ -181,7 +181,8 @@ kda_status_t kda_decode(const void *q, const void *k, const void *v, const void 
  *
  * (no gradient flows through the clamped branch of the gate).
  *
- * Inputs (as kda_fwd, K = V = 128 only):
+ * Inputs (as kda_fwd; K = V = 128, or 64 run on the 128-wide kernels with
+ * the channels and columns from 64 on held at zero):
  *   q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens,
  *   num_seqs, initial_state (+ dtype), B, T, H, K, V
  *   d_out          bf16 [B, T, H, V]   gradient reaching o

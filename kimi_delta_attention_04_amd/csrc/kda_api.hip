@@ -278,7 +278,7 @@ kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
     if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
     kda_status_t st = check_sizes(B, T, H, K, V, cu_seqlens, num_seqs);
     if (st != KDA_OK) return st;
-    if (K != kda::HD) return KDA_ERR_UNSUPPORTED;          // the backward runs K = V = 128 only
+    if (K != kda::HD && K != 64) return KDA_ERR_UNSUPPORTED;   // K = V = 128 or 64
     if ((st = check_gate(lower_bound)) != KDA_OK) return st;
 
     hipStream_t s = (hipStream_t)stream;
@@ -293,7 +293,7 @@ kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
     }
     hipError_t e = kda::launch_bwd((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v,
                                    (const uint16_t *)g, (const uint16_t *)beta, scale, A_log,
-                                   dt_bias, lower_bound, cu_seqlens, num_seqs, T, H, slots,
+                                   dt_bias, lower_bound, cu_seqlens, num_seqs, T, H, K, slots,
                                    initial_state, initial_state_dtype == KDA_DTYPE_FP32,
                                    (const uint16_t *)d_out, d_final_state, (uint16_t *)dq,
                                    (uint16_t *)dk, (uint16_t *)dv, (uint16_t *)dg,

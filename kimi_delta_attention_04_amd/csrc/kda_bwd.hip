@@ -106,23 +106,36 @@ __device__ __forceinline__ void chunk_factors(Factors &L, const uint16_t *__rest
                               const uint16_t *__restrict__ k, const uint16_t *__restrict__ g,
                               const uint16_t *__restrict__ bl, float Aexp,
                               const float *__restrict__ dt_bias, float lb, int64_t t0, int len,
-                              int H, int h) {
+                              int H, int h, int kd) {
     const int tid = threadIdx.x;
     if (tid < HD) {
         // one channel per thread: gate, in-chunk cumulative log-decay G
         // (natural log) and the scaled rows
         const int c = tid;
-        const float dtb = dt_bias ? dt_bias[(size_t)h * HD + c] : 0.f;
+        // head dimension kd = 64 runs on the 128-wide tiles: channels from kd
+        // on have zero k and q (and zero gate inputs), so every factor row
+        // and column they touch is zero
+        const bool ch = c < kd;
+        const int cc = ch ? c : 0;                   // an address that is always in range
+        const float dtb = (dt_bias && ch) ? dt_bias[(size_t)h * kd + c] : 0.f;
         L.dtb[c] = dtb;
-        // every row's loads first, so that their latencies overlap (rows
-        // past len read row len-1 and are masked below)
+        // every row's loads first and unconditionally, so that their
+        // latencies overlap (rows past len read row len-1; both are masked
+        // after the loads)
+        uint16_t gw[CS], kw[CS], qw[CS];
+#pragma unroll
+        for (int r = 0; r < CS; ++r) {
+            const size_t off = ((size_t)(t0 + (r < len ? r : len - 1)) * H + h) * kd + cc;
+            gw[r] = g[off];
+            kw[r] = k[off];
+            qw[r] = q[off];
+        }
         float gr[CS], kr[CS], qr[CS];
 #pragma unroll
         for (int r = 0; r < CS; ++r) {
-            const size_t off = ((size_t)(t0 + (r < len ? r : len - 1)) * H + h) * HD + c;
-            gr[r] = bf16f(g[off]);
-            kr[r] = bf16f(k[off]);
-            qr[r] = bf16f(q[off]);
+            gr[r] = ch ? bf16f(gw[r]) : 0.f;
+            kr[r] = ch ? bf16f(kw[r]) : 0.f;
+            qr[r] = ch ? bf16f(qw[r]) : 0.f;
         }
         float G = 0.f;
 #pragma unroll
@@ -214,7 +227,7 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
     const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb,
-    const int32_t *__restrict__ cu, int N, int T, int H, float *__restrict__ brec)
+    const int32_t *__restrict__ cu, int N, int T, int H, int kd, float *__restrict__ brec)
 {
     __shared__ __attribute__((aligned(16))) Factors L;
     const int64_t slot = blockIdx.x / (unsigned)H;
@@ -222,7 +235,7 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(
     int64_t t0;
     const int len = slot_chunk(cu, N, T, slot, t0);
     if (len == 0) return;                                   // gap slot
-    chunk_factors<true>(L, q, k, g, beta, expf(A_log[h]), dt_bias, lb, t0, len, H, h);
+    chunk_factors<true>(L, q, k, g, beta, expf(A_log[h]), dt_bias, lb, t0, len, H, h, kd);
     float *rec = brec + ((size_t)slot * H + h) * BR_FLOATS;
     const int tid = threadIdx.x;
     for (int idx = tid; idx < CS * HD; idx += BT) {
@@ -272,7 +285,7 @@ __device__ __forceinline__ size_t state_off(int part, int c, int j) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(BT) void bwd_states_kernel(
     const uint16_t *__restrict__ v, const float *__restrict__ brec,
-    const int32_t *__restrict__ cu, int N, int T, int H,
+    const int32_t *__restrict__ cu, int N, int T, int H, int kd,
     const void *__restrict__ init, int init_fp32, float *__restrict__ st0,
     float *__restrict__ xws)
 {
@@ -285,14 +298,16 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(
     const int h = nh % H, n = nh / H;
     const int tid = threadIdx.x, j = tid % CWB, rg = tid / CWB;
     const int col = part * CWB + j;
-    const size_t sbase = ((size_t)n * H + h) * HD * HD;
+    const bool colv = col < kd;                      // columns from kd on are zeros
+    const size_t sbase = ((size_t)n * H + h) * kd * kd;
 
     float s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const size_t idx = sbase + (size_t)(rg + NRG * i) * HD + col;
-        s[i] = !init ? 0.f : init_fp32 ? ((const float *)init)[idx]
-                                       : bf16f(((const uint16_t *)init)[idx]);
+        const int row = rg + NRG * i;
+        const size_t idx = sbase + (size_t)row * kd + col;
+        s[i] = (!init || !colv || row >= kd) ? 0.f
+             : init_fp32 ? ((const float *)init)[idx] : bf16f(((const uint16_t *)init)[idx]);
     }
     int64_t start, end;
     seq_range(cu, n, T, start, end);
@@ -312,8 +327,8 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(
         fetch_block(pb0, pb1, rec_ + BR_WM);                                                  \
         if (tid < HD / 4) pg = *(const float4 *)&rec_[BR_GAM + 4 * tid];                      \
         const int64_t tr_ = start + (int64_t)(ci_) * CS + tid / CWB;                          \
-        pvalid = tr_ < end;                                                                   \
-        pd = v[((size_t)min(tr_, end - 1) * H + h) * HD + col];                               \
+        pvalid = tr_ < end && colv;                                                           \
+        pd = v[((size_t)min(tr_, end - 1) * H + h) * kd + (colv ? col : 0)];                  \
     } while (0)
     if (nch > 0) KDA_STATES_FETCH(0);
     for (int ci = 0; ci < nch; ++ci) {
@@ -382,7 +397,7 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
     const uint16_t *__restrict__ dout, const float *__restrict__ brec,
-    const int32_t *__restrict__ cu, int N, int T, int H, float scale,
+    const int32_t *__restrict__ cu, int N, int T, int H, int kd, float scale,
     const float *__restrict__ dfin, float *__restrict__ dst1, float *__restrict__ dxws,
     uint16_t *__restrict__ dv, float *__restrict__ dinit)
 {
@@ -397,12 +412,15 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
     const int h = nh % H, n = nh / H;
     const int tid = threadIdx.x, j = tid % CWB, rg = tid / CWB;
     const int col = part * CWB + j;
-    const size_t sbase = ((size_t)n * H + h) * HD * HD;
+    const bool colv = col < kd;                      // columns from kd on are zeros
+    const size_t sbase = ((size_t)n * H + h) * kd * kd;
 
     float ds[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-        ds[i] = dfin ? dfin[sbase + (size_t)(rg + NRG * i) * HD + col] : 0.f;
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + NRG * i;
+        ds[i] = (dfin && colv && row < kd) ? dfin[sbase + (size_t)row * kd + col] : 0.f;
+    }
     int64_t start, end;
     seq_range(cu, n, T, start, end);
     const int nch = (int)((end - start + CS - 1) / CS);
@@ -422,8 +440,8 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
         if (tid < CS * CS / 4) pm = *(const float4 *)&rec_[BR_M + 4 * tid];                   \
         if (tid < HD / 4) pg = *(const float4 *)&rec_[BR_GAM + 4 * tid];                      \
         const int64_t tr_ = start + (int64_t)(ci_) * CS + tid / CWB;                          \
-        pvalid = tr_ < end;                                                                   \
-        pd = dout[((size_t)min(tr_, end - 1) * H + h) * HD + col];                            \
+        pvalid = tr_ < end && colv;                                                           \
+        pd = dout[((size_t)min(tr_, end - 1) * H + h) * kd + (colv ? col : 0)];               \
     } while (0)
     if (nch > 0) KDA_DSTATES_FETCH(nch - 1);
     for (int ci = nch - 1; ci >= 0; --ci) {
@@ -472,7 +490,7 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
             for (int gq = 0; gq < NRG; ++gq) x += xp[gq][r][j];
             dxs[r][j] = x;
             dxws[sh * CS * HD + (size_t)r * HD + col] = x;
-            if (r < len) dv[((size_t)(t0 + r) * H + h) * HD + col] = tobf16(x);
+            if (r < len && colv) dv[((size_t)(t0 + r) * H + h) * kd + col] = tobf16(x);
         }
         __syncthreads();
         float dor[CS], dxr[CS];
@@ -498,7 +516,10 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
     }
     if (dinit) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) dinit[sbase + (size_t)(rg + NRG * i) * HD + col] = ds[i];
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg + NRG * i;
+            if (colv && row < kd) dinit[sbase + (size_t)row * kd + col] = ds[i];
+        }
     }
 #undef KDA_DSTATES_FETCH
 }
@@ -535,7 +556,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
     const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb, float scale,
-    const uint16_t *__restrict__ dout, const int32_t *__restrict__ cu, int N, int T, int H,
+    const uint16_t *__restrict__ dout, const int32_t *__restrict__ cu, int N, int T, int H, int kd,
     const float *__restrict__ st0, const float *__restrict__ dst1,
     const float *__restrict__ xws, const float *__restrict__ dxws,
     uint16_t *__restrict__ dq, uint16_t *__restrict__ dk, uint16_t *__restrict__ dg,
@@ -563,21 +584,21 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
     fetch_state_block(qs0, qs1, S0, 1);
     fetch_state_block(qd0, qd1, DS, 1);
     const float Aexp = expf(A_log[h]);
-    chunk_factors<false>(F, q, k, g, beta, Aexp, dt_bias, lb, t0, len, H, h);
+    chunk_factors<false>(F, q, k, g, beta, Aexp, dt_bias, lb, t0, len, H, h, kd);
 
     {
         // all eight loads of this thread first (rows past len read row
         // len-1 and are masked)
-        float dov[CS * HD / BT];
+        uint16_t dov[CS * HD / BT];
 #pragma unroll
         for (int m = 0; m < CS * HD / BT; ++m) {
             const int idx = tid + m * BT, r = idx / HD, c = idx % HD;
-            dov[m] = bf16f(dout[((size_t)(t0 + (r < len ? r : len - 1)) * H + h) * HD + c]);
+            dov[m] = dout[((size_t)(t0 + (r < len ? r : len - 1)) * H + h) * kd + (c < kd ? c : 0)];
         }
 #pragma unroll
         for (int m = 0; m < CS * HD / BT; ++m) {
             const int idx = tid + m * BT, r = idx / HD, c = idx % HD;
-            L.dol[r][c] = r < len ? scale * dov[m] : 0.f;
+            L.dol[r][c] = (r < len && c < kd) ? scale * bf16f(dov[m]) : 0.f;
         }
     }
 #pragma unroll
@@ -718,8 +739,8 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
             const float dKb = dKB[mm] + F.gam[c] * dKbG;
             dgk += dKbG * F.kb[r][c];
             const float e = F.e[r][c];
-            if (r < len) {
-                const size_t off = ((size_t)(t0 + r) * H + h) * HD + c;
+            if (r < len && c < kd) {
+                const size_t off = ((size_t)(t0 + r) * H + h) * kd + c;
                 dq[off] = tobf16(dQt * e);
                 dk[off] = tobf16(dKt * e + dKb / e);
             }
@@ -733,10 +754,13 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
         // reverse cumulative sum of dG is the gradient of the per-token log-decay;
         // then the gate chain
         const int c = tid;
-        float gs[CS];                                   // loads first (rows past len masked)
+        uint16_t gw[CS];                                // loads first (rows past len masked)
 #pragma unroll
         for (int s = 0; s < CS; ++s)
-            gs[s] = bf16f(g[((size_t)(t0 + (s < len ? s : len - 1)) * H + h) * HD + c]);
+            gw[s] = g[((size_t)(t0 + (s < len ? s : len - 1)) * H + h) * kd + (c < kd ? c : 0)];
+        float gs[CS];
+#pragma unroll
+        for (int s = 0; s < CS; ++s) gs[s] = c < kd ? bf16f(gw[s]) : 0.f;
         const float dgam = L.dgam[c] + L.dgam2[0][c] + L.dgam2[1][c];
         float acc = dgam * F.gam[c];
         float pdtb = 0.f, pa = 0.f;
@@ -744,12 +768,12 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
         for (int s = CS - 1; s >= 0; --s) {
             acc += L.dqt[s][c];
             if (s < len) {
-                const size_t off = ((size_t)(t0 + s) * H + h) * HD + c;
+                const size_t off = ((size_t)(t0 + s) * H + h) * kd + c;
                 const float x = gs[s] + F.dtb[c];
                 const float y = -Aexp * softplus_f(x);
                 const float dy = y >= lb ? acc : 0.f;
                 const float dx = -dy * Aexp * sigmoid_f(x);
-                dg[off] = tobf16(dx);
+                if (c < kd) dg[off] = tobf16(dx);
                 pdtb += dx;
                 pa += dy * y;
             }
@@ -778,14 +802,14 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(HD) void bwd_reduce_kernel(
     const float *__restrict__ part_alog, const float *__restrict__ part_dtb, int64_t slots,
-    int H, float *__restrict__ dA_log, float *__restrict__ ddt_bias)
+    int H, int kd, float *__restrict__ dA_log, float *__restrict__ ddt_bias)
 {
     __shared__ float red[HD];
     const int h = blockIdx.x, c = threadIdx.x;
     float s = 0.f, a = 0.f;
     for (int64_t sl = 0; sl < slots; ++sl) s += part_dtb[((size_t)sl * H + h) * HD + c];
     for (int64_t sl = c; sl < slots; sl += HD) a += part_alog[(size_t)sl * H + h];
-    if (ddt_bias) ddt_bias[(size_t)h * HD + c] = s;
+    if (ddt_bias && c < kd) ddt_bias[(size_t)h * kd + c] = s;
     red[c] = a;
     __syncthreads();
     for (int o = HD / 2; o >= 1; o >>= 1) {
@@ -806,7 +830,7 @@ size_t bwd_workspace_bytes(int64_t num_slots, int H) {
 hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
                       const uint16_t *beta, float scale, const float *A_log,
                       const float *dt_bias, float lower_bound, const int32_t *cu, int N, int T,
-                      int H, int64_t num_slots, const void *init, int init_fp32,
+                      int H, int K, int64_t num_slots, const void *init, int init_fp32,
                       const uint16_t *dout, const float *dfin, uint16_t *dq, uint16_t *dk,
                       uint16_t *dv, uint16_t *dg, uint16_t *dbeta, float *dA_log,
                       float *ddt_bias, float *dinit, void *ws, hipStream_t stream,
@@ -827,20 +851,20 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
     };
     mark(0);
     hipLaunchKernelGGL(bwd_prep_kernel, chunks, dim3(BT), 0, stream,
-                       q, k, g, beta, A_log, dt_bias, lower_bound, cu, N, T, H, brec);
+                       q, k, g, beta, A_log, dt_bias, lower_bound, cu, N, T, H, K, brec);
     mark(1);
     hipLaunchKernelGGL(bwd_states_kernel, scans, dim3(BT), 0, stream,
-                       v, brec, cu, N, T, H, init, init_fp32, st0, xws);
+                       v, brec, cu, N, T, H, K, init, init_fp32, st0, xws);
     mark(2);
     hipLaunchKernelGGL(bwd_dstates_kernel, scans, dim3(BT), 0, stream,
-                       dout, brec, cu, N, T, H, scale, dfin, dst1, dxws, dv, dinit);
+                       dout, brec, cu, N, T, H, K, scale, dfin, dst1, dxws, dv, dinit);
     mark(3);
     hipLaunchKernelGGL(bwd_chunk_kernel, chunks, dim3(BT), 0, stream,
-                       q, k, g, beta, A_log, dt_bias, lower_bound, scale, dout, cu, N, T, H,
+                       q, k, g, beta, A_log, dt_bias, lower_bound, scale, dout, cu, N, T, H, K,
                        st0, dst1, xws, dxws, dq, dk, dg, dbeta, palog, pdtb);
     mark(4);
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)H), dim3(HD), 0, stream,
-                       palog, pdtb, num_slots, H, dA_log, ddt_bias);
+                       palog, pdtb, num_slots, H, K, dA_log, ddt_bias);
     mark(5);
     const hipError_t le = hipGetLastError();
     return e != hipSuccess ? e : le;

@@ -31,14 +31,16 @@ hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v
                          int H, int D, void *state, int state_fp32, uint16_t *out,
                          hipStream_t stream);
 
-// Backward pass (K = V = 128): five launches on `stream` using the caller's
-// workspace of bwd_workspace_bytes(num_slots, H) bytes (16-byte aligned).
-// events: NULL, or six events recorded before each launch and after the last.
+// Backward pass (K = V = 128, or 64 on the 128-wide kernels with the
+// channels and columns from 64 on held at zero): five launches on `stream`
+// using the caller's workspace of bwd_workspace_bytes(num_slots, H) bytes
+// (16-byte aligned).  events: NULL, or six events recorded before each
+// launch and after the last.
 size_t bwd_workspace_bytes(int64_t num_slots, int H);
 hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
                       const uint16_t *beta, float scale, const float *A_log,
                       const float *dt_bias, float lower_bound, const int32_t *cu, int N, int T,
-                      int H, int64_t num_slots, const void *init, int init_fp32,
+                      int H, int K, int64_t num_slots, const void *init, int init_fp32,
                       const uint16_t *dout, const float *dfin, uint16_t *dq, uint16_t *dk,
                       uint16_t *dv, uint16_t *dg, uint16_t *dbeta, float *dA_log,
                       float *ddt_bias, float *dinit, void *ws, hipStream_t stream,

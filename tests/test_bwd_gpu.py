@@ -150,3 +150,19 @@ def test_full_size_h96_sampled_heads():
     d_out, d_final = kda_inputs.output_grads(962, 1, 8192, 96)
     out = run_bwd(to_device(inp), d_out, d_final)
     check(inp, out, d_out, d_final, heads=[0, 95])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=1, T=64, H=2, initial_state=True),
+    dict(B=2, T=37, H=3),
+    dict(B=1, T=300, H=2, seq_lens=(0, 17, 1, 200, 82), initial_state=True),
+])
+def test_head_dim_64_matches_oracle(kw):
+    """K = V = 64 on the 128-wide kernels (channels and columns from 64 on
+    held at zero): every gradient against the oracle at K = V = 64."""
+    inp = kda_inputs.random_small(950 + kw["T"] + kw["H"], K=64, V=64, **kw)
+    N = len(kw["seq_lens"]) if "seq_lens" in kw else kw["B"]
+    d_out, d_final = kda_inputs.output_grads(951 + kw["T"], kw["B"], kw["T"], kw["H"], V=64, N=N,
+                                             K=64)
+    out = run_bwd(to_device(inp), d_out, d_final)
+    check(inp, out, d_out, d_final)
