@@ -706,48 +706,67 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
     }
     __syncthreads();
     {
-        // per (token row r, channel c): the gradients of Qt, Kt, Kb, then q, k, G
-        // Thread: channel c, rows rh + 2 mm.  The loop over s reads this
-        // thread's column of kb, dWm, qt, kt once; the 16 x 16 factors are
-        // the same for the whole wave (broadcast reads).
-        const int c = tid & (HD - 1), rh = tid >> 7;
-        float dQ[CS / 2], dK[CS / 2], dKG[CS / 2], dKB[CS / 2];
+        // per (token row r, channel c): the gradients of Qt, Kt, Kb, then q, k, G.
+        // The 16 x 16 by 16 x 128 products on fp32 16x16x4 MFMAs, wave w
+        // taking channel tiles 2w and 2w+1:
+        //   dQt += dAqk Kb,  dKt += dA Kb,  dKbG = P dWm,  dKb = dAqk^T Qt + dA^T Kt
+        // Lane l supplies row l%16, token 4ks + l/16 of each 16 x 16 factor
+        // (A operand) and token 4ks + l/16, channel l%16 of the tile (B
+        // operand), and holds rows 4(l/16) .. +3, channel l%16 of each
+        // product: every (row, channel) belongs to one lane, which then
+        // forms its gradients elementwise.
+        const int wave = tid >> 6, l = tid & 63;
+        const int ar = l & 15, ak = l >> 4;
+        float aAqk[4], aA[4], aP[4], aAqkT[4], aAT[4];
 #pragma unroll
-        for (int mm = 0; mm < CS / 2; ++mm) {
-            const int r = rh + 2 * mm;
-            dQ[mm] = L.dqt[r][c];
-            dK[mm] = L.dkt[r][c];
-            dKG[mm] = dKB[mm] = 0.f;
+        for (int ks = 0; ks < 4; ++ks) {
+            aAqk[ks] = L.dAqk[ar][4 * ks + ak];
+            aA[ks] = L.dA[ar][4 * ks + ak];
+            aP[ks] = F.P[ar][4 * ks + ak];
+            aAqkT[ks] = L.dAqk[4 * ks + ak][ar];
+            aAT[ks] = L.dA[4 * ks + ak][ar];
         }
-#pragma unroll 4
-        for (int s = 0; s < CS; ++s) {
-            const float kbs = F.kb[s][c], dws = L.dwm[s][c], qts = F.qt[s][c], kts = F.kt[s][c];
 #pragma unroll
-            for (int mm = 0; mm < CS / 2; ++mm) {
-                const int r = rh + 2 * mm;
-                dQ[mm] += L.dAqk[r][s] * kbs;               // zero for s > r
-                dK[mm] += L.dA[r][s] * kbs;                 // zero for s >= r
-                dKG[mm] += F.P[r][s] * dws;
-                dKB[mm] += L.dAqk[s][r] * qts + L.dA[s][r] * kts;
+        for (int tt = 0; tt < 2; ++tt) {
+            const int c = 16 * (2 * wave + tt) + ar;   // channel of this lane
+            f32x4_t dQ = {0.f, 0.f, 0.f, 0.f}, dK = dQ, dKG = dQ, dKB = dQ;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int tk = 4 * ks + ak;             // token of the B operand
+                const float kbs = F.kb[tk][c], dws = L.dwm[tk][c];
+                const float qts = F.qt[tk][c], kts = F.kt[tk][c];
+                dQ = mfma_k4(aAqk[ks], kbs, dQ);        // dAqk zero for s > r
+                dK = mfma_k4(aA[ks], kbs, dK);          // dA zero for s >= r
+                dKG = mfma_k4(aP[ks], dws, dKG);
+                dKB = mfma_k4(aAqkT[ks], qts, dKB);
+                dKB = mfma_k4(aAT[ks], kts, dKB);
+            }
+            float dgc = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * ak + j;
+                const float dQt = L.dqt[r][c] + dQ[j], dKt = L.dkt[r][c] + dK[j];
+                const float dKbG = dKG[j];
+                const float dKb = dKB[j] + F.gam[c] * dKbG;
+                dgc += dKbG * F.kb[r][c];
+                const float e = F.e[r][c];
+                if (r < len && c < kd) {
+                    const size_t off = ((size_t)(t0 + r) * H + h) * kd + c;
+                    dq[off] = tobf16(dQt * e);
+                    dk[off] = tobf16(dKt * e + dKb / e);
+                }
+                // dG (natural log) of this row; stored over dqt, read and
+                // written only by this lane
+                L.dqt[r][c] = dKt * F.kt[r][c] + dQt * F.qt[r][c] - dKb * F.kb[r][c];
+            }
+            // sum over the four row groups (lanes l, l^16, l^32, l^48)
+            dgc += __shfl_xor(dgc, 16, 64);
+            dgc += __shfl_xor(dgc, 32, 64);
+            if (ak == 0) {
+                L.dgam2[0][c] = dgc;
+                L.dgam2[1][c] = 0.f;
             }
         }
-        float dgk = 0.f;
-#pragma unroll
-        for (int mm = 0; mm < CS / 2; ++mm) {
-            const int r = rh + 2 * mm;
-            const float dQt = dQ[mm], dKt = dK[mm], dKbG = dKG[mm];
-            const float dKb = dKB[mm] + F.gam[c] * dKbG;
-            dgk += dKbG * F.kb[r][c];
-            const float e = F.e[r][c];
-            if (r < len && c < kd) {
-                const size_t off = ((size_t)(t0 + r) * H + h) * kd + c;
-                dq[off] = tobf16(dQt * e);
-                dk[off] = tobf16(dKt * e + dKb / e);
-            }
-            // dG (natural log) of this row; stored over dqt, read only by this thread
-            L.dqt[r][c] = dKt * F.kt[r][c] + dQt * F.qt[r][c] - dKb * F.kb[r][c];
-        }
-        L.dgam2[rh][c] = dgk;
     }
     __syncthreads();
     if (tid < HD) {
