@@ -658,31 +658,42 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
     }
     const int r_ = tid >> 4, lo = tid & 15;
     {
-        // dM = scale dO X^T
-        float acc = 0.f;
-        for (int jj = 0; jj < HD; jj += 4) {
-            const float4 a4 = *(const float4 *)&L.dol[r_][jj];
-            const float4 b4 = *(const float4 *)&L.xl[lo][jj];
-            acc += a4.x * b4.x + a4.y * b4.y + a4.z * b4.z + a4.w * b4.w;
+        // The two contractions over 128 channels on fp32 16x16x4 MFMAs:
+        // wave 0 dM = scale dO X^T, wave 1 the Wm path of dP, Kb Gam dWm^T
+        // (held in Y, which is free until the phase after next).  Lane l
+        // supplies row l%16, channel 4ks + l/16 of both operands and holds
+        // rows 4(l/16) .. +3, column l%16.
+        const int wave = tid >> 6, l = tid & 63;
+        const int ar = l & 15, ak = l >> 4;
+        if (wave < 2) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            if (wave == 0) {
+#pragma unroll 8
+                for (int ks = 0; ks < HD / 4; ++ks)
+                    acc = mfma_k4(L.dol[ar][4 * ks + ak], L.xl[ar][4 * ks + ak], acc);
+            } else {
+#pragma unroll 8
+                for (int ks = 0; ks < HD / 4; ++ks) {
+                    const int c = 4 * ks + ak;
+                    acc = mfma_k4(F.kb[ar][c] * F.gam[c], L.dwm[ar][c], acc);
+                }
+            }
+            float(&dst)[CS][SP] = wave == 0 ? L.dM : L.Y;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[4 * ak + j][ar] = acc[j];
         }
-        L.dM[r_][lo] = acc;
     }
     __syncthreads();
     {
         // M = Aqk P:  dAqk = dM P^T (lower incl.),  dP = Aqk^T dM
-        // Wm = P^T Kb Gam:  dP += Kb Gam dWm^T
+        // Wm = P^T Kb Gam:  dP += Kb Gam dWm^T (from the MFMAs above)
         const int r = r_, i = lo;
         float a = 0.f, p = 0.f;
         for (int s = 0; s < CS; ++s) {
             a += L.dM[r][s] * F.P[i][s];
             p += F.aqk[s][r] * L.dM[s][i];
         }
-        for (int c = 0; c < HD; c += 4) {
-            const float4 k4 = *(const float4 *)&F.kb[r][c];
-            const float4 g4 = *(const float4 *)&F.gam[c];
-            const float4 w4 = *(const float4 *)&L.dwm[i][c];
-            p += k4.x * g4.x * w4.x + k4.y * g4.y * w4.y + k4.z * g4.z * w4.z + k4.w * g4.w * w4.w;
-        }
+        p += L.Y[r][i];
         L.dAqk[r][i] = i <= r ? a : 0.f;
         L.dP[r][i] = p;
     }
