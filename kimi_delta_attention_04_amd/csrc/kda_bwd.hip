@@ -401,26 +401,37 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
     const float *__restrict__ dfin, float *__restrict__ dst1, float *__restrict__ dxws,
     uint16_t *__restrict__ dv, float *__restrict__ dinit)
 {
+    // The recurrence on fp32 16x16x4 MFMAs.  Wave w holds state row tiles
+    // 2w and 2w+1 of the part's 16 columns in accumulator layout: lane l has
+    // rows 16t + 4(l/16) + jj (jj = 0..3) of column l%16.  A contraction over
+    // the 16 rows of a tile runs as four k-steps, step jj taking rows
+    // 4g + jj from lane group g = l/16, so the accumulator registers are the
+    // B operand as they stand; the same holds for contractions over the 16
+    // tokens of dX.
     __shared__ __attribute__((aligned(16))) float wmT[HD][CS];
     __shared__ __attribute__((aligned(16))) float ktT[HD][CS];
     __shared__ __attribute__((aligned(16))) float qtT[HD][CS];
     __shared__ __attribute__((aligned(16))) float gam[HD];
     __shared__ __attribute__((aligned(16))) float Ml[CS][CS];
-    __shared__ float dol[CS][CWB], dxs[CS][CWB], xp[NRG][CS][CWB];
+    __shared__ float dol[CS][CWB];
+    __shared__ f32x4_t xpw[BT / 64][64];             // per-wave partial Wm dS1
     const int unit = blockIdx.x;
     const int part = unit % NPART, nh = unit / NPART;
     const int h = nh % H, n = nh / H;
-    const int tid = threadIdx.x, j = tid % CWB, rg = tid / CWB;
-    const int col = part * CWB + j;
+    const int tid = threadIdx.x, j = tid % CWB;
+    const int wave = tid >> 6, l = tid & 63, g = l >> 4;
+    const int col = part * CWB + j;                  // j == l % 16
     const bool colv = col < kd;                      // columns from kd on are zeros
     const size_t sbase = ((size_t)n * H + h) * kd * kd;
 
-    float ds[RPT];
+    f32x4_t dsa[2];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int row = rg + NRG * i;
-        ds[i] = (dfin && colv && row < kd) ? dfin[sbase + (size_t)row * kd + col] : 0.f;
-    }
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int row = 16 * (2 * wave + tt) + 4 * g + jj;
+            dsa[tt][jj] = (dfin && colv && row < kd) ? dfin[sbase + (size_t)row * kd + col] : 0.f;
+        }
     int64_t start, end;
     seq_range(cu, n, T, start, end);
     const int nch = (int)((end - start + CS - 1) / CS);
@@ -448,7 +459,10 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
         const size_t sh = (size_t)(slot0 + ci) * H + h;
         float *dst = dst1 + sh * HD * HD;
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) dst[state_off(part, rg + NRG * i, j)] = ds[i];
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                dst[state_off(part, 16 * (2 * wave + tt) + 4 * g + jj, j)] = dsa[tt][jj];
         const int64_t t0 = start + (int64_t)ci * CS;
         const int len = (int)min((int64_t)CS, end - t0);
         __syncthreads();
@@ -460,66 +474,62 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
         dol[tid / CWB][j] = pvalid ? scale * bf16f(pd) : 0.f;
         if (ci > 0) KDA_DSTATES_FETCH(ci - 1);          // in flight during this chunk
         __syncthreads();
-        // dX = scale M^T dO + Wm dS1: partial sums of Wm dS1 over this thread's rows
+        // dX = scale M^T dO + Wm dS1: this wave's rows of Wm dS1 (A: Wm
+        // row l%16, column 16t + 4g + jj), then scale M^T dO (A: M^T row
+        // l%16, token 4ks + g; B: scale dO token 4ks + g)
         {
-            float p[CS];
+            const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+            f32x4_t xpart = zero;
 #pragma unroll
-            for (int r = 0; r < CS; ++r) p[r] = 0.f;
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const int c = rg + NRG * i;
-#pragma unroll
-                for (int r = 0; r < CS; r += 4) {
-                    const float4 w4 = *(const float4 *)&wmT[c][r];
-                    p[r] += w4.x * ds[i];
-                    p[r + 1] += w4.y * ds[i];
-                    p[r + 2] += w4.z * ds[i];
-                    p[r + 3] += w4.w * ds[i];
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < CS; ++r) xp[rg][r][j] = p[r];
+                for (int jj = 0; jj < 4; ++jj)
+                    xpart = mfma_k4(wmT[16 * (2 * wave + tt) + 4 * g + jj][l & 15], dsa[tt][jj], xpart);
+            xpw[wave][l] = xpart;
         }
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t dX = zero;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            dX = mfma_k4(Ml[4 * ks + g][l & 15], dol[4 * ks + g][l & 15], dX);
         __syncthreads();
-        {
-            const int r = rg;                           // NRG == CS
-            float x = 0.f;
+        // every wave sums the same partials in the same order: lane l holds
+        // dX tokens 4g + jj of column l%16
+        dX += xpw[0][l];
+        dX += xpw[1][l];
+        dX += xpw[2][l];
+        dX += xpw[3][l];
+        if (wave == 0) {
 #pragma unroll
-            for (int sr = 0; sr < CS; ++sr) x += Ml[sr][r] * dol[sr][j];
-#pragma unroll
-            for (int gq = 0; gq < NRG; ++gq) x += xp[gq][r][j];
-            dxs[r][j] = x;
-            dxws[sh * CS * HD + (size_t)r * HD + col] = x;
-            if (r < len && colv) dv[((size_t)(t0 + r) * H + h) * kd + col] = tobf16(x);
-        }
-        __syncthreads();
-        float dor[CS], dxr[CS];
-#pragma unroll
-        for (int r = 0; r < CS; ++r) {
-            dor[r] = dol[r][j];
-            dxr[r] = dxs[r][j];
-        }
-        // dS0 = Gam dS1 + scale Qt^T dO - Kt^T dX
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int c = rg + NRG * i;
-            float acc = gam[c] * ds[i];
-#pragma unroll
-            for (int r = 0; r < CS; r += 4) {
-                const float4 q4 = *(const float4 *)&qtT[c][r];
-                const float4 k4 = *(const float4 *)&ktT[c][r];
-                acc += q4.x * dor[r] + q4.y * dor[r + 1] + q4.z * dor[r + 2] + q4.w * dor[r + 3];
-                acc -= k4.x * dxr[r] + k4.y * dxr[r + 1] + k4.z * dxr[r + 2] + k4.w * dxr[r + 3];
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = 4 * g + jj;
+                dxws[sh * CS * HD + (size_t)r * HD + col] = dX[jj];
+                if (r < len && colv) dv[((size_t)(t0 + r) * H + h) * kd + col] = tobf16(dX[jj]);
             }
-            ds[i] = acc;
+        }
+        // dS0 = Gam dS1 + scale Qt^T dO - Kt^T dX, per row tile (A: Qt^T /
+        // Kt^T row 16t + l%16, token 4g + jj; B: dO / dX token 4g + jj)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int t = 2 * wave + tt;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) dsa[tt][jj] *= gam[16 * t + 4 * g + jj];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                dsa[tt] = mfma_k4(qtT[16 * t + (l & 15)][4 * g + jj], dol[4 * g + jj][l & 15], dsa[tt]);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                dsa[tt] = mfma_k4(-ktT[16 * t + (l & 15)][4 * g + jj], dX[jj], dsa[tt]);
         }
     }
     if (dinit) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int row = rg + NRG * i;
-            if (colv && row < kd) dinit[sbase + (size_t)row * kd + col] = ds[i];
-        }
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int row = 16 * (2 * wave + tt) + 4 * g + jj;
+                if (colv && row < kd) dinit[sbase + (size_t)row * kd + col] = dsa[tt][jj];
+            }
     }
 #undef KDA_DSTATES_FETCH
 }
