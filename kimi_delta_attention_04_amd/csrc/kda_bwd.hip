@@ -289,26 +289,34 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(
     const void *__restrict__ init, int init_fp32, float *__restrict__ st0,
     float *__restrict__ xws)
 {
+    // The recurrence on fp32 16x16x4 MFMAs, in the layout of the dstates
+    // kernel: wave w holds state row tiles 2w and 2w+1 (lane l: rows
+    // 16t + 4(l/16) + jj of column l%16), and the k-steps of a contraction
+    // take rows (or tokens) 4g + jj from lane group g in step jj.
     __shared__ __attribute__((aligned(16))) float ktT[HD][CS];
     __shared__ __attribute__((aligned(16))) float wmT[HD][CS];
     __shared__ __attribute__((aligned(16))) float gam[HD];
-    __shared__ float vv[CS][CWB], xs[CS][CWB], xp[NRG][CS][CWB];
+    __shared__ float vv[CS][CWB];
+    __shared__ f32x4_t xpw[BT / 64][64];             // per-wave partial Kt S0
     const int unit = blockIdx.x;
     const int part = unit % NPART, nh = unit / NPART;
     const int h = nh % H, n = nh / H;
-    const int tid = threadIdx.x, j = tid % CWB, rg = tid / CWB;
-    const int col = part * CWB + j;
+    const int tid = threadIdx.x, j = tid % CWB;
+    const int wave = tid >> 6, l = tid & 63, g = l >> 4;
+    const int col = part * CWB + j;                  // j == l % 16
     const bool colv = col < kd;                      // columns from kd on are zeros
     const size_t sbase = ((size_t)n * H + h) * kd * kd;
 
-    float s[RPT];
+    f32x4_t sa[2];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int row = rg + NRG * i;
-        const size_t idx = sbase + (size_t)row * kd + col;
-        s[i] = (!init || !colv || row >= kd) ? 0.f
-             : init_fp32 ? ((const float *)init)[idx] : bf16f(((const uint16_t *)init)[idx]);
-    }
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int row = 16 * (2 * wave + tt) + 4 * g + jj;
+            const size_t idx = sbase + (size_t)row * kd + col;
+            sa[tt][jj] = (!init || !colv || row >= kd) ? 0.f
+                       : init_fp32 ? ((const float *)init)[idx] : bf16f(((const uint16_t *)init)[idx]);
+        }
     int64_t start, end;
     seq_range(cu, n, T, start, end);
     const int nch = (int)((end - start + CS - 1) / CS);
@@ -335,7 +343,10 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(
         const size_t sh = (size_t)(slot0 + ci) * H + h;
         float *dst = st0 + sh * HD * HD;
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) dst[state_off(part, rg + NRG * i, j)] = s[i];
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                dst[state_off(part, 16 * (2 * wave + tt) + 4 * g + jj, j)] = sa[tt][jj];
         __syncthreads();                                // last chunk's readers are done
         put_cols(ktT, pa0, pa1);
         put_cols(wmT, pb0, pb1);
@@ -343,49 +354,42 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(
         vv[tid / CWB][j] = pvalid ? bf16f(pd) : 0.f;
         if (ci + 1 < nch) KDA_STATES_FETCH(ci + 1);     // in flight during this chunk
         __syncthreads();
-        // X = V - Kt S0: partial sums over this thread's rows
+        // X = V - Kt S0: this wave's rows of Kt S0 (A: Kt token l%16,
+        // channel 16t + 4g + jj; B: the state registers)
         {
-            float p[CS];
+            f32x4_t xpart = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < CS; ++r) p[r] = 0.f;
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const int c = rg + NRG * i;
-#pragma unroll
-                for (int r = 0; r < CS; r += 4) {
-                    const float4 k4 = *(const float4 *)&ktT[c][r];
-                    p[r] += k4.x * s[i];
-                    p[r + 1] += k4.y * s[i];
-                    p[r + 2] += k4.z * s[i];
-                    p[r + 3] += k4.w * s[i];
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < CS; ++r) xp[rg][r][j] = p[r];
+                for (int jj = 0; jj < 4; ++jj)
+                    xpart = mfma_k4(ktT[16 * (2 * wave + tt) + 4 * g + jj][l & 15], sa[tt][jj], xpart);
+            xpw[wave][l] = xpart;
         }
         __syncthreads();
-        {
-            float x = vv[rg][j];                        // row rg (NRG == CS)
+        // every wave forms the same X in the same order: lane l holds tokens
+        // 4g + jj of column l%16
+        f32x4_t X;
 #pragma unroll
-            for (int gq = 0; gq < NRG; ++gq) x -= xp[gq][rg][j];
-            xs[rg][j] = x;
-            xws[sh * CS * HD + (size_t)rg * HD + col] = x;
+        for (int jj = 0; jj < 4; ++jj) X[jj] = vv[4 * g + jj][l & 15];
+        X -= xpw[0][l];
+        X -= xpw[1][l];
+        X -= xpw[2][l];
+        X -= xpw[3][l];
+        if (wave == 0) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                xws[sh * CS * HD + (size_t)(4 * g + jj) * HD + col] = X[jj];
         }
-        __syncthreads();
-        float xr[CS];
+        // S1 = Gam S0 + Wm^T X, per row tile (A: Wm^T row 16t + l%16,
+        // token 4g + jj; B: X token 4g + jj)
 #pragma unroll
-        for (int r = 0; r < CS; ++r) xr[r] = xs[r][j];
-        // S1 = Gam S0 + Wm^T X
+        for (int tt = 0; tt < 2; ++tt) {
+            const int t = 2 * wave + tt;
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int c = rg + NRG * i;
-            float acc = gam[c] * s[i];
+            for (int jj = 0; jj < 4; ++jj) sa[tt][jj] *= gam[16 * t + 4 * g + jj];
 #pragma unroll
-            for (int r = 0; r < CS; r += 4) {
-                const float4 w4 = *(const float4 *)&wmT[c][r];
-                acc += w4.x * xr[r] + w4.y * xr[r + 1] + w4.z * xr[r + 2] + w4.w * xr[r + 3];
-            }
-            s[i] = acc;
+            for (int jj = 0; jj < 4; ++jj)
+                sa[tt] = mfma_k4(wmT[16 * t + (l & 15)][4 * g + jj], X[jj], sa[tt]);
         }
     }
 #undef KDA_STATES_FETCH
