@@ -76,8 +76,12 @@ typedef enum {
  *   lower_bound host fp32: finite, <= 0 and >= kda_lower_bound_min()
  *   cu_seqlens  int32 [num_seqs + 1] prefix offsets into the packed token
  *               axis, or NULL.  Non-NULL requires B == 1; then sequence n is
- *               tokens [cu[n], cu[n+1]).  Preconditions (not checked):
- *               cu[0] = 0, non-decreasing, cu[num_seqs] = T.  Zero-length
+ *               tokens [cu[n], cu[n+1]).  Preconditions, not checked by
+ *               default: cu[0] = 0, non-decreasing, cu[num_seqs] = T.
+ *               With KDA_CHECK_CU_SEQLENS=1 in the environment, a one-block
+ *               device check runs first and the call synchronises with the
+ *               stream; bad contents then return KDA_ERR_INVALID_ARG with
+ *               nothing else launched (kda_bwd alike).  Zero-length
  *               sequences are allowed.  NULL means B sequences of T tokens.
  *   num_seqs    N: B when cu_seqlens is NULL, else len(cu_seqlens) - 1
  *   initial_state  [N, H, K, V] in initial_state_dtype, or NULL (= zeros)

@@ -1,5 +1,6 @@
 // C-ABI of libkda: argument validation, workspace, launches.
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 
 #include <mutex>
@@ -76,6 +77,41 @@ kda_status_t check_sizes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
     return KDA_OK;
 }
 
+// Opt-in device check of the cu_seqlens contents (KDA_CHECK_CU_SEQLENS set
+// to a value other than "0" in the environment): cu[0] = 0, non-decreasing,
+// cu[N] = T.  One workgroup; the result is copied back to the host, so the
+// call synchronises with the stream (a debugging aid, off by default).
+__global__ void check_cu_kernel(const int32_t *__restrict__ cu, int N, int T, int *__restrict__ bad) {
+    int b = 0;
+    for (int i = threadIdx.x; i < N; i += blockDim.x)
+        if (cu[i + 1] < cu[i]) b = 1;
+    if (threadIdx.x == 0 && (cu[0] != 0 || cu[N] != T)) b = 1;
+    b = __syncthreads_or(b);
+    if (threadIdx.x == 0) *bad = b;
+}
+
+bool cu_check_enabled() {
+    const char *e = getenv("KDA_CHECK_CU_SEQLENS");
+    return e && e[0] && !(e[0] == '0' && e[1] == 0);
+}
+
+// KDA_OK, KDA_ERR_INVALID_ARG for bad contents, or KDA_ERR_LAUNCH.
+kda_status_t check_cu_contents(const int32_t *cu, int N, int T, hipStream_t s, hipMemPool_t pool) {
+    int *bad = nullptr;
+    if (hipMallocFromPoolAsync((void **)&bad, sizeof(int), pool, s) != hipSuccess || !bad) {
+        (void)hipGetLastError();
+        return KDA_ERR_OUT_OF_MEMORY;
+    }
+    int host_bad = 1;
+    hipLaunchKernelGGL(check_cu_kernel, dim3(1), dim3(256), 0, s, cu, N, T, bad);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = hipMemcpyAsync(&host_bad, bad, sizeof(int), hipMemcpyDeviceToHost, s);
+    const hipError_t ef = hipFreeAsync(bad, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess || ef != hipSuccess) return KDA_ERR_LAUNCH;
+    return host_bad ? KDA_ERR_INVALID_ARG : KDA_OK;
+}
+
 kda_status_t check_gate(float lower_bound) {
     if (!isfinite(lower_bound) || lower_bound > 0.f) return KDA_ERR_INVALID_ARG;
     if (lower_bound < kLowerBoundMin) return KDA_ERR_UNSUPPORTED;
@@ -149,6 +185,9 @@ kda_status_t fwd_impl(const void *q, const void *k, const void *v, const void *g
     const size_t bytes = kda_workspace_size_hd(B, T, H, num_seqs, K);
     hipMemPool_t pool;
     if ((st = device_pool(&pool)) != KDA_OK) return st;
+    if (cu_seqlens && cu_check_enabled() &&
+        (st = check_cu_contents(cu_seqlens, num_seqs, (int)((int64_t)B * T), s, pool)) != KDA_OK)
+        return st;
     void *ws = nullptr;
     if (hipMallocFromPoolAsync(&ws, bytes, pool, s) != hipSuccess || !ws) {
         (void)hipGetLastError();
@@ -286,6 +325,9 @@ kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
     const size_t bytes = kda::bwd_workspace_bytes(slots, H);
     hipMemPool_t pool;
     if ((st = device_pool(&pool)) != KDA_OK) return st;
+    if (cu_seqlens && cu_check_enabled() &&
+        (st = check_cu_contents(cu_seqlens, num_seqs, (int)((int64_t)B * T), s, pool)) != KDA_OK)
+        return st;
     void *ws = nullptr;
     if (hipMallocFromPoolAsync(&ws, bytes, pool, s) != hipSuccess || !ws) {
         (void)hipGetLastError();
