@@ -94,6 +94,17 @@ def stored_traffic(workload: str, kernel: str):
             "total_bytes": k["read_bytes"] + k["write_bytes"]}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, w, heads: int):
     import oracle
     sel = list(range(min(heads, w.H)))
@@ -103,7 +114,7 @@ def cpu_baseline(inp, w, heads: int):
     # the whole workload takes H / len(sel) times as long (heads are independent)
     tok_s = w.tokens / (dt * w.H / len(sel))
     return {"value": tok_s, "unit": "tokens/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{w.name}: heads 0..{len(sel) - 1} of {w.H}, all {w.tokens} tokens, "
                       f"fp64 C/OpenMP token recurrence, {dt:.2f} s wall"}
 
@@ -375,6 +386,7 @@ def main():
     kda.set_stage_events(None, None, None)
     torch.cuda.synchronize()
     intra_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]
+    kern_ms = [evs[i][0].elapsed_time(evs[i][2]) for i in range(args.steps)]
     scan_ms = [evs[i][1].elapsed_time(evs[i][2]) for i in range(args.steps)]
     intra_avg = statistics.mean(intra_ms)
     scan_avg = statistics.mean(scan_ms)
@@ -403,7 +415,11 @@ def main():
             "stage_traffic_bytes": {k: (t["total_bytes"] if t else None) for k, t in
                                     ((k, None if args.scalar_gate else stored_traffic(name, k))
                                      for k in kernels)},
-            "stage_ms_min": {"kda_intra": min(intra_ms), "kda_scan": min(scan_ms)}}
+            "stage_ms_min": {"kda_intra": min(intra_ms), "kda_scan": min(scan_ms)},
+            # first kernel start to last kernel end of each instrumented step
+            # (no gap between calls)
+            "kernels_ms_per_step": {"median": statistics.median(kern_ms), "min": min(kern_ms),
+                                    "mean": statistics.mean(kern_ms)}}
 
     cpu = None
     if not args.no_cpu_baseline and not args.scalar_gate and args.head_dim == 128:
