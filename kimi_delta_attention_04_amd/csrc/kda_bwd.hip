@@ -298,8 +298,13 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(
     __shared__ __attribute__((aligned(16))) float gam[HD];
     __shared__ float vv[CS][CWB];
     __shared__ f32x4_t xpw[BT / 64][64];             // per-wave partial Kt S0
-    const int unit = blockIdx.x;
-    const int part = unit % NPART, nh = unit / NPART;
+    // Block b -> ((sequence, head) unit, column part): the eight parts of a
+    // unit share b mod 8, so they run on one XCD and read the chunk factors
+    // through one L2
+    const int b = blockIdx.x;
+    const int nh = 8 * (b / (8 * NPART)) + (b & 7);
+    const int part = (b >> 3) % NPART;
+    if (nh >= N * H) return;                          // block-uniform
     const int h = nh % H, n = nh / H;
     const int tid = threadIdx.x, j = tid % CWB;
     const int wave = tid >> 6, l = tid & 63, g = l >> 4;
@@ -419,8 +424,13 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
     __shared__ __attribute__((aligned(16))) float Ml[CS][CS];
     __shared__ float dol[CS][CWB];
     __shared__ f32x4_t xpw[BT / 64][64];             // per-wave partial Wm dS1
-    const int unit = blockIdx.x;
-    const int part = unit % NPART, nh = unit / NPART;
+    // Block b -> ((sequence, head) unit, column part): the eight parts of a
+    // unit share b mod 8, so they run on one XCD and read the chunk factors
+    // through one L2
+    const int b = blockIdx.x;
+    const int nh = 8 * (b / (8 * NPART)) + (b & 7);
+    const int part = (b >> 3) % NPART;
+    if (nh >= N * H) return;                          // block-uniform
     const int h = nh % H, n = nh / H;
     const int tid = threadIdx.x, j = tid % CWB;
     const int wave = tid >> 6, l = tid & 63, g = l >> 4;
@@ -888,7 +898,7 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
     float *dxws = xws + sh * CS * HD;
     float *pdtb = dxws + sh * CS * HD;
     float *palog = pdtb + sh * HD;
-    const dim3 chunks((unsigned)sh), scans((unsigned)((size_t)N * H * NPART));
+    const dim3 chunks((unsigned)sh), scans((unsigned)(8 * NPART * (((size_t)N * H + 7) / 8)));
     hipError_t e = hipSuccess;
     auto mark = [&](int i) {
         if (events && events[i] && e == hipSuccess) e = hipEventRecord(events[i], stream);
