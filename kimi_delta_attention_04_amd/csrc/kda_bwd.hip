@@ -257,9 +257,12 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(
 // so a thread reads the 16 token values of each of its rows as four 16-byte
 // vectors.
 //
-// Stored states (S0 and dS1 of every chunk) are part-major: per (slot,
-// head) [part][K][16] fp32, so a wave's store of one register row is 256
-// contiguous bytes.  X and dX of every chunk are stored as [16][V] fp32.
+// Stored states (S0 and dS1 of every chunk), per (slot, head): one 1 KiB
+// piece per (16-column part p, 16-row tile t) at float offset
+// (8 p + t) * 256, holding rows 16t + 4g + jj, columns 16p + n at
+// 64 jj + 16 g + n: the scans' accumulator order, so that each store
+// instruction of a wave writes 256 contiguous bytes.  X and dX of every
+// chunk are stored as [16][V] fp32.
 // ---------------------------------------------------------------------------
 // A 16 x 128 factor block is two 16-byte loads per thread; the prefetched
 // values live in named registers (no local arrays, which the compiler may
@@ -276,8 +279,9 @@ __device__ __forceinline__ void put_cols(float (&dst)[HD][CS], const float4 &d0,
     *(float4 *)&dst[e1 / CS][e1 % CS] = d1;
 }
 
-__device__ __forceinline__ size_t state_off(int part, int c, int j) {
-    return ((size_t)part * HD + c) * CWB + j;
+// Float offset of (part, row tile t, step jj, lane l) in a stored state.
+__device__ __forceinline__ size_t state_acc_off(int part, int t, int jj, int l) {
+    return ((size_t)part * (HD / 16) + t) * 256 + jj * 64 + l;
 }
 
 // ---------------------------------------------------------------------------
@@ -351,7 +355,7 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                dst[state_off(part, 16 * (2 * wave + tt) + 4 * g + jj, j)] = sa[tt][jj];
+                dst[state_acc_off(part, 2 * wave + tt, jj, l)] = sa[tt][jj];
         __syncthreads();                                // last chunk's readers are done
         put_cols(ktT, pa0, pa1);
         put_cols(wmT, pb0, pb1);
@@ -476,7 +480,7 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                dst[state_off(part, 16 * (2 * wave + tt) + 4 * g + jj, j)] = dsa[tt][jj];
+                dst[state_acc_off(part, 2 * wave + tt, jj, l)] = dsa[tt][jj];
         const int64_t t0 = start + (int64_t)ci * CS;
         const int len = (int)min((int64_t)CS, end - t0);
         __syncthreads();
@@ -566,14 +570,16 @@ struct ChunkLds {
 __device__ __forceinline__ void fetch_state_block(float4 &d0, float4 &d1,
                                                   const float *__restrict__ base, int cb) {
     const int f0 = threadIdx.x, f1 = threadIdx.x + BT;
-    d0 = *(const float4 *)&base[state_off(f0 >> 6, 16 * cb, 4 * (f0 & 63))];
-    d1 = *(const float4 *)&base[state_off(f1 >> 6, 16 * cb, 4 * (f1 & 63))];
+    d0 = *(const float4 *)&base[state_acc_off(f0 >> 6, cb, 0, 0) + 4 * (f0 & 63)];
+    d1 = *(const float4 *)&base[state_acc_off(f1 >> 6, cb, 0, 0) + 4 * (f1 & 63)];
 }
 __device__ __forceinline__ void put_state_block(float (&dst)[CS][RS], const float4 &d0,
                                                 const float4 &d1) {
     const int f0 = threadIdx.x, f1 = threadIdx.x + BT;
-    *(float4 *)&dst[(f0 & 63) >> 2][(f0 >> 6) * CWB + 4 * (f0 & 3)] = d0;
-    *(float4 *)&dst[(f1 & 63) >> 2][(f1 >> 6) * CWB + 4 * (f1 & 3)] = d1;
+    // float 4 (f & 63) + q of piece f >> 6 is row 4 g + jj, column 4 (f & 3) + q
+    // of that part, with jj = (f & 63) >> 4 and g = ((f & 63) >> 2) & 3
+    *(float4 *)&dst[4 * (((f0 & 63) >> 2) & 3) + ((f0 & 63) >> 4)][(f0 >> 6) * CWB + 4 * (f0 & 3)] = d0;
+    *(float4 *)&dst[4 * (((f1 & 63) >> 2) & 3) + ((f1 & 63) >> 4)][(f1 >> 6) * CWB + 4 * (f1 & 3)] = d1;
 }
 
 __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
