@@ -101,12 +101,16 @@ struct Factors {
 };
 
 // WANT_W: also form Wm (the prep kernel stores it; the chunk kernel does not use it).
-template <bool WANT_W>
+// KEEP_GATE: also return, per row, the gate before its clamp,
+// y = -exp(A_log) softplus(g + dt_bias), and sigmoid(g + dt_bias) in ysv /
+// sgv (the calling thread's channel, threads below HD), for the gate chain
+// of the chunk kernel.
+template <bool WANT_W, bool KEEP_GATE = false>
 __device__ __forceinline__ void chunk_factors(Factors &L, const uint16_t *__restrict__ q,
                               const uint16_t *__restrict__ k, const uint16_t *__restrict__ g,
                               const uint16_t *__restrict__ bl, float Aexp,
                               const float *__restrict__ dt_bias, float lb, int64_t t0, int len,
-                              int H, int h, int kd) {
+                              int H, int h, int kd, float *ysv = nullptr, float *sgv = nullptr) {
     const int tid = threadIdx.x;
     if (tid < HD) {
         // one channel per thread: gate, in-chunk cumulative log-decay G
@@ -142,7 +146,12 @@ __device__ __forceinline__ void chunk_factors(Factors &L, const uint16_t *__rest
         for (int r = 0; r < CS; ++r) {
             float kv = 0.f, qv = 0.f;
             if (r < len) {
-                G += fmaxf(-Aexp * softplus_f(gr[r] + dtb), lb);
+                const float y = -Aexp * softplus_f(gr[r] + dtb);
+                if (KEEP_GATE) {
+                    ysv[r] = y;
+                    sgv[r] = sigmoid_f(gr[r] + dtb);
+                }
+                G += fmaxf(y, lb);
                 kv = kr[r];
                 qv = qr[r];
             }
@@ -614,7 +623,8 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
     fetch_state_block(qs0, qs1, S0, 1);
     fetch_state_block(qd0, qd1, DS, 1);
     const float Aexp = expf(A_log[h]);
-    chunk_factors<false>(F, q, k, g, beta, Aexp, dt_bias, lb, t0, len, H, h, kd);
+    float ysv[CS], sgv[CS];                                 // this thread's gate per row (threads < HD)
+    chunk_factors<false, true>(F, q, k, g, beta, Aexp, dt_bias, lb, t0, len, H, h, kd, ysv, sgv);
 
     {
         // all eight loads of this thread first (rows past len read row
@@ -814,13 +824,6 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
         // reverse cumulative sum of dG is the gradient of the per-token log-decay;
         // then the gate chain
         const int c = tid;
-        uint16_t gw[CS];                                // loads first (rows past len masked)
-#pragma unroll
-        for (int s = 0; s < CS; ++s)
-            gw[s] = g[((size_t)(t0 + (s < len ? s : len - 1)) * H + h) * kd + (c < kd ? c : 0)];
-        float gs[CS];
-#pragma unroll
-        for (int s = 0; s < CS; ++s) gs[s] = c < kd ? bf16f(gw[s]) : 0.f;
         const float dgam = L.dgam[c] + L.dgam2[0][c] + L.dgam2[1][c];
         float acc = dgam * F.gam[c];
         float pdtb = 0.f, pa = 0.f;
@@ -829,10 +832,9 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
             acc += L.dqt[s][c];
             if (s < len) {
                 const size_t off = ((size_t)(t0 + s) * H + h) * kd + c;
-                const float x = gs[s] + F.dtb[c];
-                const float y = -Aexp * softplus_f(x);
+                const float y = ysv[s];                 // as in chunk_factors, same thread
                 const float dy = y >= lb ? acc : 0.f;
-                const float dx = -dy * Aexp * sigmoid_f(x);
+                const float dx = -dy * Aexp * sgv[s];
                 if (c < kd) dg[off] = tobf16(dx);
                 pdtb += dx;
                 pa += dy * y;
