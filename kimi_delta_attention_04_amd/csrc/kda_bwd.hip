@@ -869,7 +869,16 @@ __global__ __launch_bounds__(HD) void bwd_reduce_kernel(
     __shared__ float red[HD];
     const int h = blockIdx.x, c = threadIdx.x;
     float s = 0.f, a = 0.f;
-    for (int64_t sl = 0; sl < slots; ++sl) s += part_dtb[((size_t)sl * H + h) * HD + c];
+    // slot order, sixteen loads issued ahead of their adds
+    int64_t sl = 0;
+    for (; sl + 16 <= slots; sl += 16) {
+        float pv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pv[i] = part_dtb[((size_t)(sl + i) * H + h) * HD + c];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += pv[i];
+    }
+    for (; sl < slots; ++sl) s += part_dtb[((size_t)sl * H + h) * HD + c];
     for (int64_t sl = c; sl < slots; sl += HD) a += part_alog[(size_t)sl * H + h];
     if (ddt_bias && c < kd) ddt_bias[(size_t)h * kd + c] = s;
     red[c] = a;
