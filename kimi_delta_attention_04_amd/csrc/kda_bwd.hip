@@ -37,6 +37,7 @@
 #include <math.h>
 
 #include "kda_device.h"
+#include "kda_intra_dev.h"                            // mm16: 16 x 16 fp32 products on MFMA
 #include "kda_launch.h"
 
 namespace kda {
@@ -189,21 +190,30 @@ __device__ __forceinline__ void chunk_factors(Factors &L, const uint16_t *__rest
         }
     }
     __syncthreads();
-    if (tid < CS) {
-        // column i of T = (I + diag(beta) A)^-1 by forward substitution, in
-        // registers (entries above the diagonal come out zero)
-        const int i = tid;
-        float x[CS];
+    if (tid < 64) {
+        // T = (I + diag(beta) A)^-1 = (I - N)^-1 with N = -diag(beta) A
+        // strictly lower, hence nilpotent: (I + N)(I + N^2)(I + N^4)(I + N^8),
+        // on fp32 16x16x4 MFMAs in one wave.  Lane l holds rows 4(l/16) + j,
+        // column l%16 of each matrix and of its transpose (the A-operand
+        // layout of the matrix itself).
+        const int l = tid, grp = l >> 4, cg = l & 15;
+        f32x4_t N1, N1t, I;
 #pragma unroll
-        for (int r = 0; r < CS; ++r) {
-            float acc = r == i ? 1.f : 0.f;
-            const float br = L.beta[r];
-#pragma unroll
-            for (int s = 0; s < r; ++s) acc -= br * L.A[r][s] * x[s];
-            x[r] = acc;
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * grp + j;
+            N1[j] = -L.beta[r] * L.A[r][cg];          // A is zero on and above the diagonal
+            N1t[j] = -L.beta[cg] * L.A[cg][r];
+            I[j] = r == cg ? 1.f : 0.f;
         }
+        const f32x4_t P1t = I + N1t;
+        const f32x4_t N2 = mm16(N1t, N1), N2t = mm16(N1, N1t);
+        const f32x4_t Q12t = mm16(I + N2, P1t);       // ((I+N)(I+N^2))^T
+        const f32x4_t N4 = mm16(N2t, N2), N4t = mm16(N2, N2t);
+        const f32x4_t Q3t = mm16(I + N4, Q12t);       // ((I+N)(I+N^2)(I+N^4))^T
+        const f32x4_t N8 = mm16(N4t, N4);
+        const f32x4_t Tm = mm16(Q3t, I + N8);
 #pragma unroll
-        for (int r = 0; r < CS; ++r) L.T[r][i] = x[r];
+        for (int j = 0; j < 4; ++j) L.T[4 * grp + j][cg] = Tm[j];
     }
     __syncthreads();
     {
