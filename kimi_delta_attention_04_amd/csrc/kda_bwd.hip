@@ -227,12 +227,20 @@ __device__ __forceinline__ void chunk_factors(Factors &L, const uint16_t *__rest
         for (int s = 0; s < CS; ++s) m += L.aqk[r][s] * L.P[s][i];
         L.M[r][i] = m;
         if constexpr (WANT_W) {
-            const int c = tid & (HD - 1), i0 = tid >> 7;
-            for (int mm = 0; mm < CS / 2; ++mm) {
-                const int ii = i0 + 2 * mm;
-                float w = 0.f;
-                for (int s = 0; s < CS; ++s) w += L.P[s][ii] * L.kb[s][c];
-                L.wm[ii][c] = w * L.gam[c];
+            // Wm = P^T Kb Gam on fp32 16x16x4 MFMAs, wave w taking channel
+            // tiles 2w and 2w+1 (lane l: A = P^T row l%16, token 4ks + l/16;
+            // B = Kb token 4ks + l/16, channel l%16; result rows 4(l/16) + j)
+            const int wave = tid >> 6, l = tid & 63;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const int c = 16 * (2 * wave + tt) + (l & 15);
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    acc = mfma_k4(L.P[4 * ks + (l >> 4)][l & 15], L.kb[4 * ks + (l >> 4)][c], acc);
+                const float gc = L.gam[c];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) L.wm[4 * (l >> 4) + j][c] = acc[j] * gc;
             }
         }
     }
