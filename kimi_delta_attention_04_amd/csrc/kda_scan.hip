@@ -140,7 +140,7 @@ __device__ __forceinline__ void decay_tiles(f32x4_t (&S)[NT], const float (&gm)[
 // chunk c's operands at the top of its own iteration, and the DMA wave
 // refills the slot of chunk c-1 instead of chunk c's.
 template <int CT, int NW, int VD>
-__global__ __launch_bounds__(64 * (NW + 1), VD > HD ? 1 : 2) void scan_kernel(
+__global__ __launch_bounds__(64 * (NW + 1), VD > HD ? 1 : (CT == 2 ? 3 : 2)) void scan_kernel(
     const uint16_t *__restrict__ v, const uint8_t *__restrict__ ws,
     const int32_t *__restrict__ cu, int N, int T, int H, float scale,
     const void *__restrict__ init, int init_fp32,
@@ -159,9 +159,12 @@ __global__ __launch_bounds__(64 * (NW + 1), VD > HD ? 1 : 2) void scan_kernel(
     constexpr int V_KB = CS * CW * 2 / 1024;         // one-kilobyte units of a v tile
     constexpr int UNITS = RKB + V_KB;                // DMA units per chunk
     constexpr int VROW_LANES = CW * 2 / 16;          // lanes per v row in a DMA unit
-    constexpr int DEPTH = WIDE ? RING_DEPTH_256 : RING_DEPTH<CW>;
+    // one operand set in registers (the protocol of 256-wide tiles) also for
+    // two slices per wave, so that two workgroups fit a CU's register file
+    constexpr bool ONESET = WIDE || CT == 2;
+    constexpr int DEPTH = ONESET ? RING_DEPTH_256 : RING_DEPTH<CW>;
     __shared__ ScanSlot<CW, R::BYTES> ring[DEPTH];
-    static_assert((DEPTH - (WIDE ? 2 : 1)) * UNITS <= 63, "vmcnt holds at most 63");
+    static_assert((DEPTH - (ONESET ? 2 : 1)) * UNITS <= 63, "vmcnt holds at most 63");
 
     // Block b -> (unit u, part): the parts of a unit share b mod 8 (same XCD, same L2).
     const int b = blockIdx.x;
@@ -346,8 +349,8 @@ __global__ __launch_bounds__(64 * (NW + 1), VD > HD ? 1 : 2) void scan_kernel(
     // in order, UNITS DMAs each, so at the top of iteration c the DMAs issued
     // after chunk c+1's number (DEPTH-2) UNITS (and (DEPTH-1) UNITS after
     // chunk 0's before the first iteration).
-    if constexpr (WIDE) {
-        // 256-wide tiles.  Iteration c: the DMA wave waits for chunk c to
+    if constexpr (ONESET) {
+        // One operand set (256-wide tiles, or two slices per wave).  Iteration c: the DMA wave waits for chunk c to
         // land, the compute waves finish their reads of chunk c-1, all the
         // waves meet at a barrier; then the compute waves read chunk c and
         // compute it while the DMA wave refills chunk c-1's slot with chunk

@@ -94,19 +94,22 @@ REC_BYTES_256 = 26624                # head dimension 256: 26 KB records
 def test_wide_source_constants_match_model():
     src = open(SCAN).read()
     assert re.search(r"RING_DEPTH_256\s*=\s*4;", src)
+    assert re.search(r"ONESET\s*=\s*WIDE\s*\|\|\s*CT\s*==\s*2;", src)
     assert "for (int c = 0; c < DEPTH - 1; ++c) issue(c, c);" in src
     assert "issue(c - 1 + DEPTH, slot);" in src
 
 
-@pytest.mark.parametrize("cw", [32, 64])
+@pytest.mark.parametrize("rec_bytes,cw", [(REC_BYTES_256, 32), (REC_BYTES_256, 64),
+                                          (REC_BYTES, 128)])
 @pytest.mark.parametrize("nch", [0, 1, 2, 3, 4, 5, 7, 64])
-def test_dma_wait_ladder_wide(cw, nch):
-    """The 256-wide protocol: DEPTH-1 chunks issued before the first
+def test_dma_wait_ladder_wide(rec_bytes, cw, nch):
+    """The one-operand-set protocol (256-wide tiles, and two slices per
+    wave at 128): DEPTH-1 chunks issued before the first
     iteration; at the top of iteration c a wait of (DEPTH-2) x UNITS leaves
     chunk c landed; after the barrier the compute waves read chunk c (their
     reads of chunk c-1 completed before it) and the DMA wave refills chunk
     c-1's slot with chunk c-1+DEPTH."""
-    rec_kb = REC_BYTES_256 // 1024
+    rec_kb = rec_bytes // 1024
     v_kb = CS * cw * 2 // 1024
     units = rec_kb + v_kb
     depth = 4
