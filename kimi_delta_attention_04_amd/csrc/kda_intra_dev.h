@@ -257,8 +257,9 @@ __device__ __forceinline__ void intra_compute(WaveLdsT<KT> &L, const IntraInT<KT
             *(f32x4_t *)&L.gam[ch] = g0;
             *(f32x4_t *)&L.gam[ch + 4] = g1;
         }
-        *(u32x4_t *)(rec + R::KTO + (kb * 64 + l) * 16) = kt4;
-        *(u32x4_t *)(rec + R::QT + (kb * 64 + l) * 16) = qh4;
+        // records are written with non-temporal stores (see intra_kernel)
+        __builtin_nontemporal_store(kt4, (u32x4_t *)(rec + R::KTO + (kb * 64 + l) * 16));
+        __builtin_nontemporal_store(qh4, (u32x4_t *)(rec + R::QT + (kb * 64 + l) * 16));
         Akk = mfma_k32(kt4, bh4, Akk);          // Akk[4grp+j][cg]  = Kt_r . Kb_i
         AkkT = mfma_k32(bh4, kt4, AkkT);        // AkkT[4grp+j][cg] = Akk[cg][4grp+j]
         AqkT = mfma_k32(bh4, qh4, AqkT);        // AqkT[4grp+j][cg] = Aqk[cg][4grp+j]
@@ -281,7 +282,7 @@ __device__ __forceinline__ void intra_compute(WaveLdsT<KT> &L, const IntraInT<KT
     // lanes' 16-byte pieces per block cost several times as much)
 #pragma unroll
     for (int p = 0; p < KT / 128; ++p)
-        *(u32x2_t *)(rec + R::GAM + (64 * p + l) * 8) = *(const u32x2_t *)&L.gam[2 * (64 * p + l)];
+        __builtin_nontemporal_store(*(const u32x2_t *)&L.gam[2 * (64 * p + l)], (u32x2_t *)(rec + R::GAM + (64 * p + l) * 8));
 
     // ---- T = (I + L)^{-1}, L = diag(beta) strict_lower(Akk) ---------------
     float br[4];
@@ -335,7 +336,7 @@ __device__ __forceinline__ void intra_compute(WaveLdsT<KT> &L, const IntraInT<KT
     u32x2_t mo;
     mo[0] = pack2(Mt[0], Mt[1]);
     mo[1] = pack2(Mt[2], Mt[3]);
-    *(u32x2_t *)(rec + R::M + l * 8) = mo;
+    __builtin_nontemporal_store(mo, (u32x2_t *)(rec + R::M + l * 8));
 
     // W tiles: W[:, chan(t, .)] = (T diag(beta))^T Kb[:, chan(t, .)] times the
     // chunk decay of that channel; the accumulator layout is the A layout of
@@ -353,7 +354,7 @@ __device__ __forceinline__ void intra_compute(WaveLdsT<KT> &L, const IntraInT<KT
             o[2 * half] = pack2(Wt[0] * gch, Wt[1] * gch);
             o[2 * half + 1] = pack2(Wt[2] * gch, Wt[3] * gch);
         }
-        *(u32x4_t *)(rec + R::WT + (tp * 64 + l) * 16) = o;
+        __builtin_nontemporal_store(o, (u32x4_t *)(rec + R::WT + (tp * 64 + l) * 16));
     }
 }
 
