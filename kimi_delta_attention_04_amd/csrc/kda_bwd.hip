@@ -284,7 +284,8 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(
 // so a thread reads the 16 token values of each of its rows as four 16-byte
 // vectors.
 //
-// Stored states (S0 and dS1 of every chunk), per (slot, head): one 1 KiB
+// Stored states (S0 and dS1 of every chunk; written with non-temporal
+// stores, which measured faster for both scans), per (slot, head): one 1 KiB
 // piece per (16-column part p, 16-row tile t) at float offset
 // (8 p + t) * 256, holding rows 16t + 4g + jj, columns 16p + n at
 // 64 jj + 16 g + n: the scans' accumulator order, so that each store
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                dst[state_acc_off(part, 2 * wave + tt, jj, l)] = sa[tt][jj];
+                __builtin_nontemporal_store(sa[tt][jj], &dst[state_acc_off(part, 2 * wave + tt, jj, l)]);
         __syncthreads();                                // last chunk's readers are done
         put_cols(ktT, pa0, pa1);
         put_cols(wmT, pb0, pb1);
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                dst[state_acc_off(part, 2 * wave + tt, jj, l)] = dsa[tt][jj];
+                __builtin_nontemporal_store(dsa[tt][jj], &dst[state_acc_off(part, 2 * wave + tt, jj, l)]);
         const int64_t t0 = start + (int64_t)ci * CS;
         const int len = (int)min((int64_t)CS, end - t0);
         __syncthreads();
