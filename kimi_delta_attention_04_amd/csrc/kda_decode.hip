@@ -20,7 +20,11 @@
 // rows (S^T k, S^T q) are summed per thread over its 16 rows and then over
 // the D/16 row groups through LDS, in a fixed order.  The step moves the
 // whole state through HBM twice (read and write), so it is HBM-bound:
-// 128 KiB per (sequence, head) for an fp32 state at D = 128.
+// 128 KiB per (sequence, head) for an fp32 state at D = 128.  The updated
+// state is written with non-temporal stores: a batch of states is larger
+// than the memory-side cache, and written the normal way it sits there
+// dirty and is written back under the next step's reads (measured at
+// 64 sequences x 96 heads: 0.151 -> 0.121 ms per step).
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -116,10 +120,10 @@ __global__ __launch_bounds__(DEC_THREADS<D>) void decode_kernel(
         }
         if (F32) {
             const f32x4_t x = {S[r][0], S[r][1], S[r][2], S[r][3]};
-            *(f32x4_t *)((float *)state + base + (size_t)r * D) = x;
+            __builtin_nontemporal_store(x, (f32x4_t *)((float *)state + base + (size_t)r * D));
         } else {
             const u32x2_t x = {pack2(S[r][0], S[r][1]), pack2(S[r][2], S[r][3])};
-            *(u32x2_t *)((uint16_t *)state + base + (size_t)r * D) = x;
+            __builtin_nontemporal_store(x, (u32x2_t *)((uint16_t *)state + base + (size_t)r * D));
         }
     }
     part[rg][cgp] = po;
