@@ -95,14 +95,20 @@ FORWARD_KERNEL_SOURCES = ("kda_device.h", "kda_intra_dev.h", "kda_intra.hip", "k
 
 
 def source_digest() -> str:
-    """sha256 over the sources of the forward kernels (identifies the kernels
-    a stored profile of the forward was taken on)."""
+    """sha256 over the code of the forward kernels' sources, comments and
+    whitespace removed (identifies the kernels a stored profile of the
+    forward was taken on)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(_HERE, "csrc")
     for name in FORWARD_KERNEL_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)     # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                   # line comments
+        text = " ".join(text.split())
+        h.update(name.encode() + b"\0" + text.encode())
     return h.hexdigest()
 
 

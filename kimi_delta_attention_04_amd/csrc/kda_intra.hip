@@ -23,14 +23,14 @@ __global__ __launch_bounds__(64, 2) void intra_kernel(
     constexpr int KT = KD > HD ? 2 * HD : HD;     // channels of the tiles
     __shared__ __attribute__((aligned(16))) WaveLdsT<KT> lds;
     // Head fastest: the workgroups running together read neighbouring pieces
-    // of the same token rows and write neighbouring records.  Last chunk
-    // slot first: the records of the first chunks, which the scan reads
-    // first, are then the most recently written when it starts, and part of
-    // them is still in the memory-side cache (measured: scan 316 -> 310 us
-    // at T = 8192, H = 96).  The records are stored non-temporally: written
-    // the normal way they stay dirty in the memory-side cache and are
-    // written back while the scan runs (measured at T = 8192, H = 96: intra
-    // 234 -> 243 us, scan 307 -> 292 us, the two together 7 us faster).
+    // of the same token rows and write neighbouring records.  The records
+    // are stored non-temporally: written the normal way they stay dirty in
+    // the memory-side cache and are written back while the scan runs
+    // (measured at T = 8192, H = 96: intra 234 -> 243 us, scan 307 -> 292 us,
+    // the two together 7 us faster).  Slots run last first, which helped
+    // when the records went through that cache (the scan's first records
+    // were the freshest); with non-temporal stores either order measures
+    // the same.
     const int64_t slot = (int64_t)(gridDim.x / (unsigned)H) - 1 - blockIdx.x / (unsigned)H;
     const int h = (int)(blockIdx.x % (unsigned)H);
 
