@@ -2,8 +2,8 @@
 //
 // A workgroup owns one (sequence, head, column part); each of its NW compute
 // waves (four, or two when a head is split over four workgroups) keeps CT
-// 16-column slices of the 128-row fp32 state in MFMA accumulators for the
-// whole sequence.  Columns of the state evolve independently (each
+// 16-column slices of the 128-row (256-row at head dimension 256) fp32 state
+// in MFMA accumulators for the whole sequence.  Columns of the state evolve independently (each
 // sees the same transition and its own v entries), so column parts need no
 // communication.  The row permutation of the state tiles (kda_device.h)
 // makes the accumulators of tile pair (2kb, 2kb+1), rounded to bf16, exactly
@@ -13,9 +13,10 @@
 // (W carries the chunk decay, so diag(gamma) S is formed while the P
 // products run and enters the update MFMAs as their accumulator).
 //
-// The hand-off record of each chunk (13 KB) and the chunk's v tile are read
-// from memory once per workgroup, by buffer-to-LDS DMA into a ring of
-// DEPTH slots, DEPTH-1 chunks ahead of the compute.  One more wave issues
+// The hand-off record of each chunk (13 KB, 26 KB at head dimension 256)
+// and the chunk's v tile are read from memory once per workgroup, by
+// buffer-to-LDS DMA into a ring of DEPTH slots, DEPTH-1 chunks ahead of the
+// compute.  One more wave issues
 // all of the DMAs; the compute waves read their MFMA operands from the ring
 // and never wait on the DMA themselves.  Every memory access goes
 // through a range-checked buffer resource, so partial chunks need no
@@ -33,8 +34,9 @@ namespace {
 // LDS ring slots per workgroup (chunks in flight + the one being read); the
 // DMA wave's vmcnt (at most 63) must cover DEPTH-1 chunks of DMAs.
 template <int CW> constexpr int RING_DEPTH = CW <= 64 ? 5 : 4;
-// Head dimension 256: 26 KB records, read one chunk at a time (no operand
-// prefetch, see scan_kernel), so the vmcnt covers DEPTH-2 chunks of DMAs.
+// One operand set in registers (head dimension 256, or two slices per
+// wave): the operands are read one chunk at a time (no operand prefetch, see
+// scan_kernel), so the vmcnt covers DEPTH-2 chunks of DMAs.
 constexpr int RING_DEPTH_256 = 4;
 constexpr int REC_KB = REC_BYTES / 1024;         // 13 one-kilobyte units per record
 
@@ -133,12 +135,15 @@ __device__ __forceinline__ void decay_tiles(f32x4_t (&S)[NT], const float (&gm)[
 // per workgroup; head dimension K = V = VD (128, 256, or 64 on the 128-wide
 // tiles).
 //
-// Two ring protocols.  128-wide tiles: the compute waves read chunk c+1's
-// operands into registers while they compute chunk c (two operand sets in
-// registers).  256-wide tiles: one operand set (96 registers for Kt, Qt and
-// W^T alone) is all the register file allows, so the compute waves read
-// chunk c's operands at the top of its own iteration, and the DMA wave
-// refills the slot of chunk c-1 instead of chunk c's.
+// Two ring protocols.  One slice per wave on 128-wide tiles: the compute
+// waves read chunk c+1's operands into registers while they compute chunk c
+// (two operand sets in registers).  256-wide tiles, and two slices per wave:
+// one operand set (at 256, 96 registers for Kt, Qt and W^T alone; with two
+// slices per wave, so that 168 registers let two workgroups share a CU), so
+// the compute waves read chunk c's operands at the top of its own
+// iteration, and the DMA wave refills the slot of chunk c-1 instead of
+// chunk c's.  The second launch-bounds argument is the minimum number of
+// waves per SIMD the register allocation must allow.
 template <int CT, int NW, int VD>
 __global__ __launch_bounds__(64 * (NW + 1), VD > HD ? 1 : (CT == 2 ? 3 : 2)) void scan_kernel(
     const uint16_t *__restrict__ v, const uint8_t *__restrict__ ws,
