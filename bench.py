@@ -76,18 +76,20 @@ def algorithmic(w, has_init=True, has_final=True, scalar_gate=False):
             "flops": 2.0 * macs * th}
 
 
-def stored_traffic(workload: str, kernel: str):
+def stored_traffic(workload: str, kernel: str, backward: bool = False):
     """HBM bytes per launch of `kernel` from the committed counter summary
-    (profiles/hbm_traffic_<workload>.json: FETCH_SIZE and WRITE_SIZE runs
-    scaled by a plain copy of known size), or None when there is none or the
-    kernel sources changed since the counters were taken."""
+    (profiles/hbm_traffic_[bwd_]<workload>.json: FETCH_SIZE and WRITE_SIZE
+    runs scaled by a plain copy of known size), or None when there is none or
+    the kernel sources changed since the counters were taken."""
     import kimi_delta_attention_04_amd as kda
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    tag = "bwd_" if backward else ""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{tag}{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_digest") != kda.source_digest() or kernel not in rec.get("kernels", {}):
+    sources = kda.BACKWARD_KERNEL_SOURCES if backward else kda.FORWARD_KERNEL_SOURCES
+    if rec.get("source_digest") != kda.source_digest(sources) or kernel not in rec.get("kernels", {}):
         return None
     k = rec["kernels"][kernel]
     return {"read_bytes": k["read_bytes"], "write_bytes": k["write_bytes"],
@@ -243,12 +245,16 @@ def bench_backward(args, torch, kda, kda_inputs):
     total_bytes = th * 2308 + st_in + 2 * st32
     dom = max(names, key=lambda n: stage[n])
     achieved = kb[dom] / (stage[dom] * 1e-3) / 1e9
+    tr = stored_traffic(name, dom, backward=True)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
-                "bytes_per_launch": kb[dom], "avg_launch_ms": stage[dom]}
+                "frac": achieved / HBM_PEAK_GBS, "traffic": tr["total_bytes"] if tr else None,
+                "traffic_x_algorithmic": tr["total_bytes"] / kb[dom] if tr else None,
+                "kernel": dom, "bytes_per_launch": kb[dom], "avg_launch_ms": stage[dom]}
     path_gbs = total_bytes / (ms * 1e-3) / 1e9
     path = {"algorithmic_bytes": total_bytes, "hbm_achieved_GBs": path_gbs,
             "hbm_frac": path_gbs / HBM_PEAK_GBS, "stage_ms": stage,
+            "stage_traffic_bytes": {k: (t["total_bytes"] if t else None) for k, t in
+                                    ((k, stored_traffic(name, k, backward=True)) for k in names)},
             "workspace_bytes": int(w.H * (w.tokens // CHUNK + w.num_seqs) * 4 *
                                    (3 * CHUNK * w.K + CHUNK * CHUNK + w.K + 2 * w.K * w.V + 1 + w.K))}
     cpu = None

@@ -90,19 +90,21 @@ def load():
     return lib
 
 
-# The sources the forward kernels (intra stage and scan) are compiled from.
+# The sources the forward kernels (intra stage and scan) are compiled from,
+# and those of the backward kernels.
 FORWARD_KERNEL_SOURCES = ("kda_device.h", "kda_intra_dev.h", "kda_intra.hip", "kda_scan.hip")
+BACKWARD_KERNEL_SOURCES = ("kda_device.h", "kda_intra_dev.h", "kda_bwd.hip")
 
 
-def source_digest() -> str:
-    """sha256 over the code of the forward kernels' sources, comments and
-    whitespace removed (identifies the kernels a stored profile of the
-    forward was taken on)."""
+def source_digest(sources=FORWARD_KERNEL_SOURCES) -> str:
+    """sha256 over the code of the given kernel sources (the forward's by
+    default), comments and whitespace removed: identifies the kernels a
+    stored profile was taken on."""
     import hashlib
     import re
     h = hashlib.sha256()
     csrc = os.path.join(_HERE, "csrc")
-    for name in FORWARD_KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(csrc, name)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)     # block comments
