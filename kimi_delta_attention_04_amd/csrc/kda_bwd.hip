@@ -95,19 +95,23 @@ __device__ int slot_chunk(const int32_t *cu, int N, int T, int64_t slot, int64_t
 // zero k, q and beta and a zero log-decay, which makes every factor row and
 // column they touch zero (and e^{G_last} that of the last real token).
 // ---------------------------------------------------------------------------
-struct Factors {
-    float kt[CS][RS], qt[CS][RS], kb[CS][RS], e[CS][RS], wm[CS][RS];
+struct FactorsBase {
+    float kt[CS][RS], qt[CS][RS], kb[CS][RS], e[CS][RS];
     float A[CS][SP], aqk[CS][SP], T[CS][SP], P[CS][SP], M[CS][SP];
     float beta[CS], gam[HD], dtb[HD];
 };
+struct Factors : FactorsBase {
+    float wm[CS][RS];                 // Wm = P^T Kb Gam (the prep kernel's record)
+};
 
-// WANT_W: also form Wm (the prep kernel stores it; the chunk kernel does not use it).
+// WANT_W: also form Wm in L.wm (L a Factors; the prep kernel stores it).  The
+// chunk kernel does not use Wm and passes a FactorsBase.
 // KEEP_GATE: also return, per row, the gate before its clamp,
 // y = -exp(A_log) softplus(g + dt_bias), and sigmoid(g + dt_bias) in ysv /
 // sgv (the calling thread's channel, threads below HD), for the gate chain
 // of the chunk kernel.
-template <bool WANT_W, bool KEEP_GATE = false>
-__device__ __forceinline__ void chunk_factors(Factors &L, const uint16_t *__restrict__ q,
+template <bool WANT_W, bool KEEP_GATE = false, class FL>
+__device__ __forceinline__ void chunk_factors(FL &L, const uint16_t *__restrict__ q,
                               const uint16_t *__restrict__ k, const uint16_t *__restrict__ g,
                               const uint16_t *__restrict__ bl, float Aexp,
                               const float *__restrict__ dt_bias, float lb, int64_t t0, int len,
@@ -584,33 +588,42 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
 // chunk: per (chunk slot, head), everything that needs S0 and dS1 of the
 // chunk, then the in-chunk backward down to the inputs.
 // ---------------------------------------------------------------------------
-struct ChunkLds {
-    Factors f;
-    float dol[CS][RS], xl[CS][RS], dxl[CS][RS];  // scale * dO, X, dX
-    float s0b[CS][RS], ds1b[CS][RS];      // 16-channel row blocks of S0 and dS1
-    float dqt[CS][RS], dkt[CS][RS], dwm[CS][RS];
+// Buffers whose lifetimes do not overlap share storage, which keeps the
+// workgroup at 73 KB of LDS (two workgroups per compute unit):
+//   dol  scale * dO: the state products and dM; then dG of every (row, channel)
+//   xl   X: the state products and dM
+//   u    dX for the state products; then the 16 x 16 gradient tiles
+//   dwm  dWm: written by the state products, read by the later phases
+struct ChunkTiles {
     float dM[CS][SP], dAqk[CS][SP], dP[CS][SP], Y[CS][SP], dL[CS][SP], dA[CS][SP];
-    float dgam[HD], dgam2[2][HD], red[BT / 64];
 };
+struct ChunkLds {
+    FactorsBase f;
+    float dol[CS][RS], xl[CS][RS];
+    union {
+        float dxl[CS][RS];
+        ChunkTiles t;
+    } u;
+    float dwm[CS][RS];
+    float dgam[HD], dgam2[HD], red[BT / 64];
+};
+static_assert(2 * sizeof(ChunkLds) <= 160 * 1024, "two chunk workgroups per compute unit");
 
-// 16-channel block cb (all 128 columns) of a part-major stored state:
-// eight contiguous 1 KiB pieces, two 16-byte loads per thread
-__device__ __forceinline__ void fetch_state_block(float4 &d0, float4 &d1,
-                                                  const float *__restrict__ base, int cb) {
-    const int f0 = threadIdx.x, f1 = threadIdx.x + BT;
-    d0 = *(const float4 *)&base[state_acc_off(f0 >> 6, cb, 0, 0) + 4 * (f0 & 63)];
-    d1 = *(const float4 *)&base[state_acc_off(f1 >> 6, cb, 0, 0) + 4 * (f1 & 63)];
-}
-__device__ __forceinline__ void put_state_block(float (&dst)[CS][RS], const float4 &d0,
-                                                const float4 &d1) {
-    const int f0 = threadIdx.x, f1 = threadIdx.x + BT;
-    // float 4 (f & 63) + q of piece f >> 6 is row 4 g + jj, column 4 (f & 3) + q
-    // of that part, with jj = (f & 63) >> 4 and g = ((f & 63) >> 2) & 3
-    *(float4 *)&dst[4 * (((f0 & 63) >> 2) & 3) + ((f0 & 63) >> 4)][(f0 >> 6) * CWB + 4 * (f0 & 3)] = d0;
-    *(float4 *)&dst[4 * (((f1 & 63) >> 2) & 3) + ((f1 & 63) >> 4)][(f1 >> 6) * CWB + 4 * (f1 & 3)] = d1;
+// Row r (a channel) of the 16-channel block cb of a stored state as the B
+// operand of eight 16x16x4 k-step groups: lane (r, j) loads, from each of the
+// eight 16-column parts p, the four columns 16 p + 4 j .. + 3 (one 16-byte load
+// per part; the 64 lanes of one load cover the part's 1 KiB piece of the block).
+// In the scans' accumulator order row 4 gq + jj, column cl of a piece is at
+// float 64 jj + 16 gq + cl.
+__device__ __forceinline__ void fetch_state_rows(float4 (&d)[NPART], const float *__restrict__ base,
+                                                 int cb, int l) {
+    const int r = l & 15, j = l >> 4;
+#pragma unroll
+    for (int p = 0; p < NPART; ++p)
+        d[p] = *(const float4 *)&base[state_acc_off(p, cb, 0, 0) + 64 * (r & 3) + 16 * (r >> 2) + 4 * j];
 }
 
-__global__ __launch_bounds__(BT) void bwd_chunk_kernel(
+__global__ __launch_bounds__(BT, 2) void bwd_chunk_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
     const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb, float scale,
@@ -621,7 +634,8 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
     uint16_t *__restrict__ dbeta, float *__restrict__ part_alog, float *__restrict__ part_dtb)
 {
     __shared__ __attribute__((aligned(16))) ChunkLds L;
-    Factors &F = L.f;
+    FactorsBase &F = L.f;
+    ChunkTiles &Lt = L.u.t;
     const int64_t slot = blockIdx.x / (unsigned)H;
     const int h = (int)(blockIdx.x % (unsigned)H);
     const int tid = threadIdx.x;
@@ -635,12 +649,12 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
     }
     const float *S0 = st0 + sh * HD * HD;
     const float *DS = dst1 + sh * HD * HD;
-    // two blocks in flight: (ps, pd) holds block cb, (qs, qd) block cb + 1
-    float4 ps0, ps1, pd0, pd1, qs0, qs1, qd0, qd1;
-    fetch_state_block(ps0, ps1, S0, 0);                     // in flight during the factors
-    fetch_state_block(pd0, pd1, DS, 0);
-    fetch_state_block(qs0, qs1, S0, 1);
-    fetch_state_block(qd0, qd1, DS, 1);
+    // Wave w takes the 16-channel blocks 2w and 2w + 1 of S0 and dS1; the
+    // first block's rows are in flight during the factors.
+    const int wave = tid >> 6, l = tid & 63;
+    float4 sb[NPART], db[NPART];
+    fetch_state_rows(sb, S0, 2 * wave, l);
+    fetch_state_rows(db, DS, 2 * wave, l);
     const float Aexp = expf(A_log[h]);
     float ysv[CS], sgv[CS];                                 // this thread's gate per row (threads < HD)
     chunk_factors<false, true>(F, q, k, g, beta, Aexp, dt_bias, lb, t0, len, H, h, kd, ysv, sgv);
@@ -664,57 +678,67 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
     for (int m = 0; m < 2; ++m) {
         const int e = 4 * (tid + m * BT);
         *(float4 *)&L.xl[e / HD][e % HD] = *(const float4 *)&xws[sh * CS * HD + e];
-        *(float4 *)&L.dxl[e / HD][e % HD] = *(const float4 *)&dxws[sh * CS * HD + e];
+        *(float4 *)&L.u.dxl[e / HD][e % HD] = *(const float4 *)&dxws[sh * CS * HD + e];
     }
     __syncthreads();
 
-    // Products with the states, over 16-channel blocks of S0 / dS1 (blocks
-    // cb + 1 and cb + 2 in flight while block cb computes), on fp32 16x16x4 MFMAs
-    // contracting over the 128 value columns:
-    //   wave 0: dQt = scale dO S0^T,  wave 1: dKt = -dX S0^T,
-    //   wave 2: dWm = X dS1^T  (A operands resident for all blocks)
-    //   wave 3: dGam = diag(dS1 S0^T) on the vector ALUs
-    const int wave = tid >> 6, l = tid & 63;
-    float aop[HD / 4];
-    if (wave < 3) {
-        const float(&src)[CS][RS] = wave == 0 ? L.dol : wave == 1 ? L.dxl : L.xl;
-        const float sg = wave == 1 ? -1.f : 1.f;
+    // Products with the states on fp32 16x16x4 MFMAs, contracting over the
+    // 128 value columns; wave w forms them for channel blocks cb = 2w + tt:
+    //   dQt = scale dO S0^T,  dKt = -dX S0^T,  dWm = X dS1^T,
+    //   dGam = diag(dS1 S0^T) (vector ALUs, summed over the four lane groups).
+    // k-step 4p + i takes column 16p + 4(l/16) + i from lane l (the order of the
+    // state rows as loaded); the A operands follow the same order.  Lane l
+    // holds rows 4(l/16) .. +3, channel 16cb + l%16 of each product, the
+    // layout of the per-(row, channel) phase below, so dQt and dKt stay in
+    // registers.
+    f32x4_t dQs[2], dKs[2];
 #pragma unroll
-        for (int ks = 0; ks < HD / 4; ++ks) aop[ks] = sg * src[l & 15][4 * ks + (l >> 4)];
-    }
-    float(&dsto)[CS][RS] = wave == 0 ? L.dqt : wave == 1 ? L.dkt : L.dwm;
-    for (int cb = 0; cb < HD / 16; ++cb) {
-        __syncthreads();
-        put_state_block(L.s0b, ps0, ps1);
-        put_state_block(L.ds1b, pd0, pd1);
-        ps0 = qs0; ps1 = qs1; pd0 = qd0; pd1 = qd1;
-        if (cb + 2 < HD / 16) {
-            fetch_state_block(qs0, qs1, S0, cb + 2);
-            fetch_state_block(qd0, qd1, DS, cb + 2);
+    for (int tt = 0; tt < 2; ++tt) {
+        const int cb = 2 * wave + tt;
+        float4 sn[NPART], dn[NPART];
+        if (tt == 0) {                                      // the next block in flight
+            fetch_state_rows(sn, S0, cb + 1, l);
+            fetch_state_rows(dn, DS, cb + 1, l);
         }
-        __syncthreads();
-        if (wave < 3) {
-            const float(&bsrc)[CS][RS] = wave == 2 ? L.ds1b : L.s0b;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t aq = {0.f, 0.f, 0.f, 0.f}, ak = aq, aw = aq;
+        float pg = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < HD / 4; ++ks)
-                acc = mfma_k4(aop[ks], bsrc[l & 15][4 * ks + (l >> 4)], acc);
+        for (int p = 0; p < NPART; ++p) {
+            const int c0 = 16 * p + 4 * (l >> 4);
+            const float4 ad = *(const float4 *)&L.dol[l & 15][c0];
+            const float4 ax = *(const float4 *)&L.u.dxl[l & 15][c0];
+            const float4 aX = *(const float4 *)&L.xl[l & 15][c0];
+            aq = mfma_k4(ad.x, sb[p].x, aq);
+            aq = mfma_k4(ad.y, sb[p].y, aq);
+            aq = mfma_k4(ad.z, sb[p].z, aq);
+            aq = mfma_k4(ad.w, sb[p].w, aq);
+            ak = mfma_k4(-ax.x, sb[p].x, ak);
+            ak = mfma_k4(-ax.y, sb[p].y, ak);
+            ak = mfma_k4(-ax.z, sb[p].z, ak);
+            ak = mfma_k4(-ax.w, sb[p].w, ak);
+            aw = mfma_k4(aX.x, db[p].x, aw);
+            aw = mfma_k4(aX.y, db[p].y, aw);
+            aw = mfma_k4(aX.z, db[p].z, aw);
+            aw = mfma_k4(aX.w, db[p].w, aw);
+            pg += db[p].x * sb[p].x + db[p].y * sb[p].y + db[p].z * sb[p].z + db[p].w * sb[p].w;
+        }
+        dQs[tt] = aq;
+        dKs[tt] = ak;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dsto[4 * (l >> 4) + i][16 * cb + (l & 15)] = acc[i];
-        } else {
-            const int cc = l >> 2, qq = l & 3;
-            float p = 0.f;
+        for (int i = 0; i < 4; ++i) L.dwm[4 * (l >> 4) + i][16 * cb + (l & 15)] = aw[i];
+        pg += __shfl_xor(pg, 16, 64);
+        pg += __shfl_xor(pg, 32, 64);
+        if ((l >> 4) == 0) L.dgam[16 * cb + (l & 15)] = pg;
+        if (tt == 0) {
 #pragma unroll
-            for (int m = 0; m < 32; m += 4) {
-                const float4 a4 = *(const float4 *)&L.ds1b[cc][32 * qq + m];
-                const float4 b4 = *(const float4 *)&L.s0b[cc][32 * qq + m];
-                p += a4.x * b4.x + a4.y * b4.y + a4.z * b4.z + a4.w * b4.w;
+            for (int p = 0; p < NPART; ++p) {
+                sb[p] = sn[p];
+                db[p] = dn[p];
             }
-            p += __shfl_xor(p, 1, 64);
-            p += __shfl_xor(p, 2, 64);
-            if (qq == 0) L.dgam[16 * cb + cc] = p;
         }
     }
+    // dWm complete and dX no longer read (its storage holds the 16 x 16 tiles next)
+    __syncthreads();
     const int r_ = tid >> 4, lo = tid & 15;
     {
         // The two contractions over 128 channels on fp32 16x16x4 MFMAs:
@@ -722,7 +746,6 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
         // (held in Y, which is free until the phase after next).  Lane l
         // supplies row l%16, channel 4ks + l/16 of both operands and holds
         // rows 4(l/16) .. +3, column l%16.
-        const int wave = tid >> 6, l = tid & 63;
         const int ar = l & 15, ak = l >> 4;
         if (wave < 2) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -737,7 +760,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
                     acc = mfma_k4(F.kb[ar][c] * F.gam[c], L.dwm[ar][c], acc);
                 }
             }
-            float(&dst)[CS][SP] = wave == 0 ? L.dM : L.Y;
+            float(&dst)[CS][SP] = wave == 0 ? Lt.dM : Lt.Y;
 #pragma unroll
             for (int j = 0; j < 4; ++j) dst[4 * ak + j][ar] = acc[j];
         }
@@ -749,30 +772,30 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
         const int r = r_, i = lo;
         float a = 0.f, p = 0.f;
         for (int s = 0; s < CS; ++s) {
-            a += L.dM[r][s] * F.P[i][s];
-            p += F.aqk[s][r] * L.dM[s][i];
+            a += Lt.dM[r][s] * F.P[i][s];
+            p += F.aqk[s][r] * Lt.dM[s][i];
         }
-        p += L.Y[r][i];
-        L.dAqk[r][i] = i <= r ? a : 0.f;
-        L.dP[r][i] = p;
+        p += Lt.Y[r][i];
+        Lt.dAqk[r][i] = i <= r ? a : 0.f;
+        Lt.dP[r][i] = p;
     }
     __syncthreads();
     {
         // P = T diag(beta):  dT = dP diag(beta);  Y = dT T^T
         const int a = r_, s = lo;
         float y = 0.f;
-        for (int b = 0; b < CS; ++b) y += L.dP[a][b] * F.beta[b] * F.T[s][b];
-        L.Y[a][s] = y;
+        for (int b = 0; b < CS; ++b) y += Lt.dP[a][b] * F.beta[b] * F.T[s][b];
+        Lt.Y[a][s] = y;
     }
     __syncthreads();
     {
         // T = (I + L)^-1:  dL = -T^T dT T^T (strictly lower);  L = diag(beta) A
         const int r = r_, s = lo;
         float d = 0.f;
-        for (int a = 0; a < CS; ++a) d += F.T[a][r] * L.Y[a][s];
+        for (int a = 0; a < CS; ++a) d += F.T[a][r] * Lt.Y[a][s];
         d = s < r ? -d : 0.f;
-        L.dL[r][s] = d;
-        L.dA[r][s] = F.beta[r] * d;
+        Lt.dL[r][s] = d;
+        Lt.dA[r][s] = F.beta[r] * d;
     }
     __syncthreads();
     {
@@ -785,16 +808,15 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
         // operand), and holds rows 4(l/16) .. +3, channel l%16 of each
         // product: every (row, channel) belongs to one lane, which then
         // forms its gradients elementwise.
-        const int wave = tid >> 6, l = tid & 63;
         const int ar = l & 15, ak = l >> 4;
         float aAqk[4], aA[4], aP[4], aAqkT[4], aAT[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            aAqk[ks] = L.dAqk[ar][4 * ks + ak];
-            aA[ks] = L.dA[ar][4 * ks + ak];
+            aAqk[ks] = Lt.dAqk[ar][4 * ks + ak];
+            aA[ks] = Lt.dA[ar][4 * ks + ak];
             aP[ks] = F.P[ar][4 * ks + ak];
-            aAqkT[ks] = L.dAqk[4 * ks + ak][ar];
-            aAT[ks] = L.dA[4 * ks + ak][ar];
+            aAqkT[ks] = Lt.dAqk[4 * ks + ak][ar];
+            aAT[ks] = Lt.dA[4 * ks + ak][ar];
         }
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -815,7 +837,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * ak + j;
-                const float dQt = L.dqt[r][c] + dQ[j], dKt = L.dkt[r][c] + dK[j];
+                const float dQt = dQs[tt][j] + dQ[j], dKt = dKs[tt][j] + dK[j];
                 const float dKbG = dKG[j];
                 const float dKb = dKB[j] + F.gam[c] * dKbG;
                 dgc += dKbG * F.kb[r][c];
@@ -825,16 +847,14 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
                     dq[off] = tobf16(dQt * e);
                     dk[off] = tobf16(dKt * e + dKb / e);
                 }
-                // dG (natural log) of this row; stored over dqt, read and
-                // written only by this lane
-                L.dqt[r][c] = dKt * F.kt[r][c] + dQt * F.qt[r][c] - dKb * F.kb[r][c];
+                // dG (natural log) of this row, stored over dO
+                L.dol[r][c] = dKt * F.kt[r][c] + dQt * F.qt[r][c] - dKb * F.kb[r][c];
             }
             // sum over the four row groups (lanes l, l^16, l^32, l^48)
             dgc += __shfl_xor(dgc, 16, 64);
             dgc += __shfl_xor(dgc, 32, 64);
             if (ak == 0) {
-                L.dgam2[0][c] = dgc;
-                L.dgam2[1][c] = 0.f;
+                L.dgam2[c] = dgc;
             }
         }
     }
@@ -843,12 +863,12 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
         // reverse cumulative sum of dG is the gradient of the per-token log-decay;
         // then the gate chain
         const int c = tid;
-        const float dgam = L.dgam[c] + L.dgam2[0][c] + L.dgam2[1][c];
+        const float dgam = L.dgam[c] + L.dgam2[c];
         float acc = dgam * F.gam[c];
         float pdtb = 0.f, pa = 0.f;
 #pragma unroll
         for (int s = CS - 1; s >= 0; --s) {
-            acc += L.dqt[s][c];
+            acc += L.dol[s][c];
             if (s < len) {
                 const size_t off = ((size_t)(t0 + s) * H + h) * kd + c;
                 const float y = ysv[s];                 // as in chunk_factors, same thread
@@ -867,7 +887,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(
         // beta enters P = T diag(beta) and L = diag(beta) A
         const int r = tid - HD;
         float db = 0.f;
-        for (int s = 0; s < CS; ++s) db += L.dP[s][r] * F.T[s][r] + L.dL[r][s] * F.A[r][s];
+        for (int s = 0; s < CS; ++s) db += Lt.dP[s][r] * F.T[s][r] + Lt.dL[r][s] * F.A[r][s];
         if (r < len) {
             const float b = F.beta[r];
             dbeta[(size_t)(t0 + r) * H + h] = tobf16(db * b * (1.f - b));
