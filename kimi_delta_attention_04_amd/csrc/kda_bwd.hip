@@ -52,13 +52,14 @@ constexpr int NPART = HD / CWB;
 constexpr int NRG = BT / CWB;         // row groups of the state rows
 constexpr int RPT = HD / NRG;         // state rows per thread
 static_assert(NRG == CS && NRG * RPT == HD, "row groups cover the state rows, one per token row");
+constexpr int SCAN_PG = 4;            // column parts per scan workgroup
 
-// Chunk-factor record, fp32, per (chunk slot, head): Kt, Qt and Wm
+// Chunk-factor record, fp32, per (chunk slot, head): Kt, Wm and Qt
 // transposed ([channel][token], 16 floats per channel), M [16][16] and
 // e^{G_last} [128].
 constexpr int BR_KT = 0;
-constexpr int BR_QT = CS * HD;
-constexpr int BR_WM = 2 * CS * HD;
+constexpr int BR_WM = CS * HD;       // next to Kt^T: the states kernel reads the two as one span
+constexpr int BR_QT = 2 * CS * HD;
 constexpr int BR_M = 3 * CS * HD;
 constexpr int BR_GAM = 3 * CS * HD + CS * CS;
 constexpr int BR_FLOATS = BR_GAM + HD;
@@ -280,13 +281,12 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// The two scans run one workgroup per (sequence, head, 16-column part).
-// Thread t holds column t % 16 of the part and the 8 state rows
-// t / 16 + 16 i (i = 0..7) in registers.  The next chunk's factors are
-// loaded into registers while the current chunk computes (software
-// pipelining).  The factors are kept transposed ([channel][token]) in LDS,
-// so a thread reads the 16 token values of each of its rows as four 16-byte
-// vectors.
+// The two scans run on 16-column parts of the state, four parts (1,024
+// threads) per workgroup, two workgroups per (sequence, head).  Each part's
+// four waves hold its 128 x 16 state slice in MFMA accumulator layout; the
+// four parts share one LDS copy of each chunk's factors, whose record is
+// loaded into registers while the previous chunk computes (software
+// pipelining).  The factors are kept transposed ([channel][token]).
 //
 // Stored states (S0 and dS1 of every chunk; written with non-temporal
 // stores, which measured faster for both scans), per (slot, head): one 1 KiB
@@ -296,21 +296,6 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(
 // instruction of a wave writes 256 contiguous bytes.  X and dX of every
 // chunk are stored as [16][V] fp32.
 // ---------------------------------------------------------------------------
-// A 16 x 128 factor block is two 16-byte loads per thread; the prefetched
-// values live in named registers (no local arrays, which the compiler may
-// place in scratch memory).
-__device__ __forceinline__ void fetch_block(float4 &d0, float4 &d1, const float *__restrict__ src) {
-    d0 = *(const float4 *)&src[4 * threadIdx.x];
-    d1 = *(const float4 *)&src[4 * (threadIdx.x + BT)];
-}
-
-// [128][16] transposed factor block (as stored in the record) into LDS
-__device__ __forceinline__ void put_cols(float (&dst)[HD][CS], const float4 &d0, const float4 &d1) {
-    const int e0 = 4 * threadIdx.x, e1 = 4 * (threadIdx.x + BT);
-    *(float4 *)&dst[e0 / CS][e0 % CS] = d0;
-    *(float4 *)&dst[e1 / CS][e1 % CS] = d1;
-}
-
 // Float offset of (part, row tile t, step jj, lane l) in a stored state.
 __device__ __forceinline__ size_t state_acc_off(int part, int t, int jj, int l) {
     return ((size_t)part * (HD / 16) + t) * 256 + jj * 64 + l;
@@ -319,31 +304,41 @@ __device__ __forceinline__ size_t state_acc_off(int part, int t, int jj, int l) 
 // ---------------------------------------------------------------------------
 // states: forward scan that stores each chunk's start state S0 and X.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(BT) void bwd_states_kernel(
+// PG 16-column parts per workgroup (256 threads each), sharing one LDS copy
+// of each chunk's factors, so the record is read once per PG parts.
+template <int PG>
+__global__ __launch_bounds__(BT * PG) void bwd_states_kernel(
     const uint16_t *__restrict__ v, const float *__restrict__ brec,
     const int32_t *__restrict__ cu, int N, int T, int H, int kd,
     const void *__restrict__ init, int init_fp32, float *__restrict__ st0,
     float *__restrict__ xws)
 {
     // The recurrence on fp32 16x16x4 MFMAs, in the layout of the dstates
-    // kernel: wave w holds state row tiles 2w and 2w+1 (lane l: rows
-    // 16t + 4(l/16) + jj of column l%16), and the k-steps of a contraction
-    // take rows (or tokens) 4g + jj from lane group g in step jj.
-    __shared__ __attribute__((aligned(16))) float ktT[HD][CS];
-    __shared__ __attribute__((aligned(16))) float wmT[HD][CS];
+    // kernel: wave w of a part holds state row tiles 2w and 2w+1 (lane l:
+    // rows 16t + 4(l/16) + jj of column l%16), and the k-steps of a
+    // contraction take rows (or tokens) 4g + jj from lane group g in step jj.
+    constexpr int NG = NPART / PG;                    // workgroups per (sequence, head)
+    constexpr int NF = 2 * CS * HD / 4 / (BT * PG);   // 16-byte factor loads per thread
+    static_assert(NPART % PG == 0 && NF == 1 && BT * PG * 4 == 2 * CS * HD,
+                  "one 16-byte factor load per thread covers Kt and Wm");
+    __shared__ __attribute__((aligned(16))) float fac[2][HD][CS];   // Kt^T, Wm^T
     __shared__ __attribute__((aligned(16))) float gam[HD];
-    __shared__ float vv[CS][CWB];
-    __shared__ f32x4_t xpw[BT / 64][64];             // per-wave partial Kt S0
-    // Block b -> ((sequence, head) unit, column part): the eight parts of a
-    // unit share b mod 8, so they run on one XCD and read the chunk factors
+    __shared__ float vv[PG][CS][CWB];
+    __shared__ f32x4_t xpw[PG][BT / 64][64];         // per-wave partial Kt S0
+    float(&ktT)[HD][CS] = fac[0];
+    float(&wmT)[HD][CS] = fac[1];
+    // Block b -> ((sequence, head) unit, part group): the groups of a unit
+    // share b mod 8, so they run on one XCD and read the chunk factors
     // through one L2
     const int b = blockIdx.x;
-    const int nh = 8 * (b / (8 * NPART)) + (b & 7);
-    const int part = (b >> 3) % NPART;
+    const int nh = 8 * (b / (8 * NG)) + (b & 7);
+    const int grp = (b >> 3) % NG;
     if (nh >= N * H) return;                          // block-uniform
     const int h = nh % H, n = nh / H;
-    const int tid = threadIdx.x, j = tid % CWB;
-    const int wave = tid >> 6, l = tid & 63, g = l >> 4;
+    const int tid = threadIdx.x, sub = tid / BT, ptid = tid % BT;
+    const int part = grp * PG + sub;
+    const int j = ptid % CWB;
+    const int wave = ptid >> 6, l = ptid & 63, g = l >> 4;
     const int col = part * CWB + j;                  // j == l % 16
     const bool colv = col < kd;                      // columns from kd on are zeros
     const size_t sbase = ((size_t)n * H + h) * kd * kd;
@@ -363,19 +358,20 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(
     const int nch = (int)((end - start + CS - 1) / CS);
     const int64_t slot0 = seq_slot0(cu, n, T);
 
-    // next chunk's Kt^T, Wm^T, e^{G_last} and v element, in flight
-    // (the v element is loaded raw from a clamped row and masked at use, so
-    // no branch forces a wait on the loads in flight)
-    float4 pa0, pa1, pb0, pb1, pg = {0.f, 0.f, 0.f, 0.f};
+    // next chunk's Kt^T and Wm^T (16-byte piece tid of the two blocks, which
+    // lie next to each other in the record), e^{G_last} and v
+    // element, in flight (the v element is loaded raw from a clamped row and
+    // masked at use, so no branch forces a wait on the loads in flight)
+    static_assert(BR_WM == BR_KT + CS * HD, "Kt^T and Wm^T adjacent in the record");
+    float4 pf, pg = {0.f, 0.f, 0.f, 0.f};
     uint16_t pd = 0;
     bool pvalid = false;
 #define KDA_STATES_FETCH(ci_)                                                                 \
     do {                                                                                      \
         const float *rec_ = brec + ((size_t)(slot0 + (ci_)) * H + h) * BR_FLOATS;             \
-        fetch_block(pa0, pa1, rec_ + BR_KT);                                                  \
-        fetch_block(pb0, pb1, rec_ + BR_WM);                                                  \
+        pf = *(const float4 *)&rec_[BR_KT + 4 * tid];                                         \
         if (tid < HD / 4) pg = *(const float4 *)&rec_[BR_GAM + 4 * tid];                      \
-        const int64_t tr_ = start + (int64_t)(ci_) * CS + tid / CWB;                          \
+        const int64_t tr_ = start + (int64_t)(ci_) * CS + ptid / CWB;                         \
         pvalid = tr_ < end && colv;                                                           \
         pd = v[((size_t)min(tr_, end - 1) * H + h) * kd + (colv ? col : 0)];                  \
     } while (0)
@@ -389,10 +385,9 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(
             for (int jj = 0; jj < 4; ++jj)
                 __builtin_nontemporal_store(sa[tt][jj], &dst[state_acc_off(part, 2 * wave + tt, jj, l)]);
         __syncthreads();                                // last chunk's readers are done
-        put_cols(ktT, pa0, pa1);
-        put_cols(wmT, pb0, pb1);
+        *(float4 *)&fac[(4 * tid) / (CS * HD)][((4 * tid) % (CS * HD)) / CS][(4 * tid) % CS] = pf;
         if (tid < HD / 4) *(float4 *)&gam[4 * tid] = pg;
-        vv[tid / CWB][j] = pvalid ? bf16f(pd) : 0.f;
+        vv[sub][ptid / CWB][j] = pvalid ? bf16f(pd) : 0.f;
         if (ci + 1 < nch) KDA_STATES_FETCH(ci + 1);     // in flight during this chunk
         __syncthreads();
         // X = V - Kt S0: this wave's rows of Kt S0 (A: Kt token l%16,
@@ -404,18 +399,18 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
                     xpart = mfma_k4(ktT[16 * (2 * wave + tt) + 4 * g + jj][l & 15], sa[tt][jj], xpart);
-            xpw[wave][l] = xpart;
+            xpw[sub][wave][l] = xpart;
         }
         __syncthreads();
-        // every wave forms the same X in the same order: lane l holds tokens
-        // 4g + jj of column l%16
+        // every wave of the part forms the same X in the same order: lane l
+        // holds tokens 4g + jj of column l%16
         f32x4_t X;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) X[jj] = vv[4 * g + jj][l & 15];
-        X -= xpw[0][l];
-        X -= xpw[1][l];
-        X -= xpw[2][l];
-        X -= xpw[3][l];
+        for (int jj = 0; jj < 4; ++jj) X[jj] = vv[sub][4 * g + jj][l & 15];
+        X -= xpw[sub][0][l];
+        X -= xpw[sub][1][l];
+        X -= xpw[sub][2][l];
+        X -= xpw[sub][3][l];
         if (wave == 0) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
@@ -440,7 +435,8 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(
 // dstates: reverse scan of the state gradient.  Stores dS1 and dX of every
 // chunk, writes dv and, at the sequence start, the initial-state gradient.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(BT) void bwd_dstates_kernel(
+template <int PG>
+__global__ __launch_bounds__(BT * PG) void bwd_dstates_kernel(
     const uint16_t *__restrict__ dout, const float *__restrict__ brec,
     const int32_t *__restrict__ cu, int N, int T, int H, int kd, float scale,
     const float *__restrict__ dfin, float *__restrict__ dst1, float *__restrict__ dxws,
@@ -453,23 +449,32 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
     // 4g + jj from lane group g = l/16, so the accumulator registers are the
     // B operand as they stand; the same holds for contractions over the 16
     // tokens of dX.
-    __shared__ __attribute__((aligned(16))) float wmT[HD][CS];
-    __shared__ __attribute__((aligned(16))) float ktT[HD][CS];
-    __shared__ __attribute__((aligned(16))) float qtT[HD][CS];
-    __shared__ __attribute__((aligned(16))) float gam[HD];
-    __shared__ __attribute__((aligned(16))) float Ml[CS][CS];
-    __shared__ float dol[CS][CWB];
-    __shared__ f32x4_t xpw[BT / 64][64];             // per-wave partial Wm dS1
-    // Block b -> ((sequence, head) unit, column part): the eight parts of a
-    // unit share b mod 8, so they run on one XCD and read the chunk factors
+    // PG 16-column parts per workgroup (256 threads each) share one LDS copy
+    // of the chunk's record (same layout as in memory).
+    constexpr int NG = NPART / PG;                    // workgroups per (sequence, head)
+    constexpr int NREC = BR_FLOATS / 4;               // 16-byte pieces of a record
+    static_assert(NPART % PG == 0 && BR_FLOATS % 4 == 0 && NREC > BT * PG && NREC <= 2 * BT * PG,
+                  "two 16-byte loads per thread cover the record");
+    __shared__ __attribute__((aligned(16))) float recl[BR_FLOATS];
+    __shared__ float dol[PG][CS][CWB];
+    __shared__ f32x4_t xpw[PG][BT / 64][64];         // per-wave partial Wm dS1
+    const auto ktT = reinterpret_cast<const float (*)[CS]>(&recl[BR_KT]);
+    const auto wmT = reinterpret_cast<const float (*)[CS]>(&recl[BR_WM]);
+    const auto qtT = reinterpret_cast<const float (*)[CS]>(&recl[BR_QT]);
+    const auto Ml = reinterpret_cast<const float (*)[CS]>(&recl[BR_M]);
+    const float *gam = &recl[BR_GAM];
+    // Block b -> ((sequence, head) unit, part group): the groups of a unit
+    // share b mod 8, so they run on one XCD and read the chunk factors
     // through one L2
     const int b = blockIdx.x;
-    const int nh = 8 * (b / (8 * NPART)) + (b & 7);
-    const int part = (b >> 3) % NPART;
+    const int nh = 8 * (b / (8 * NG)) + (b & 7);
+    const int grp = (b >> 3) % NG;
     if (nh >= N * H) return;                          // block-uniform
     const int h = nh % H, n = nh / H;
-    const int tid = threadIdx.x, j = tid % CWB;
-    const int wave = tid >> 6, l = tid & 63, g = l >> 4;
+    const int tid = threadIdx.x, sub = tid / BT, ptid = tid % BT;
+    const int part = grp * PG + sub;
+    const int j = ptid % CWB;
+    const int wave = ptid >> 6, l = ptid & 63, g = l >> 4;
     const int col = part * CWB + j;                  // j == l % 16
     const bool colv = col < kd;                      // columns from kd on are zeros
     const size_t sbase = ((size_t)n * H + h) * kd * kd;
@@ -487,20 +492,18 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
     const int nch = (int)((end - start + CS - 1) / CS);
     const int64_t slot0 = seq_slot0(cu, n, T);
 
-    // next chunk's Kt^T, Qt^T, Wm^T, M, e^{G_last} and dO element, in flight
-    float4 pa0, pa1, pb0, pb1, pc0, pc1;
-    float4 pm = {0.f, 0.f, 0.f, 0.f}, pg = {0.f, 0.f, 0.f, 0.f};
+    // next chunk's record (16-byte pieces tid and tid + BT * PG) and dO
+    // element, in flight
+    float4 pr0, pr1 = {0.f, 0.f, 0.f, 0.f};
+    const bool two = tid + BT * PG < NREC;
     uint16_t pd = 0;
     bool pvalid = false;
 #define KDA_DSTATES_FETCH(ci_)                                                                \
     do {                                                                                      \
         const float *rec_ = brec + ((size_t)(slot0 + (ci_)) * H + h) * BR_FLOATS;             \
-        fetch_block(pa0, pa1, rec_ + BR_KT);                                                  \
-        fetch_block(pb0, pb1, rec_ + BR_QT);                                                  \
-        fetch_block(pc0, pc1, rec_ + BR_WM);                                                  \
-        if (tid < CS * CS / 4) pm = *(const float4 *)&rec_[BR_M + 4 * tid];                   \
-        if (tid < HD / 4) pg = *(const float4 *)&rec_[BR_GAM + 4 * tid];                      \
-        const int64_t tr_ = start + (int64_t)(ci_) * CS + tid / CWB;                          \
+        pr0 = *(const float4 *)&rec_[4 * tid];                                                \
+        if (two) pr1 = *(const float4 *)&rec_[4 * (tid + BT * PG)];                           \
+        const int64_t tr_ = start + (int64_t)(ci_) * CS + ptid / CWB;                         \
         pvalid = tr_ < end && colv;                                                           \
         pd = dout[((size_t)min(tr_, end - 1) * H + h) * kd + (colv ? col : 0)];               \
     } while (0)
@@ -516,12 +519,9 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
         const int64_t t0 = start + (int64_t)ci * CS;
         const int len = (int)min((int64_t)CS, end - t0);
         __syncthreads();
-        put_cols(ktT, pa0, pa1);
-        put_cols(qtT, pb0, pb1);
-        put_cols(wmT, pc0, pc1);
-        if (tid < CS * CS / 4) *(float4 *)&Ml[(4 * tid) / CS][(4 * tid) % CS] = pm;
-        if (tid < HD / 4) *(float4 *)&gam[4 * tid] = pg;
-        dol[tid / CWB][j] = pvalid ? scale * bf16f(pd) : 0.f;
+        *(float4 *)&recl[4 * tid] = pr0;
+        if (two) *(float4 *)&recl[4 * (tid + BT * PG)] = pr1;
+        dol[sub][ptid / CWB][j] = pvalid ? scale * bf16f(pd) : 0.f;
         if (ci > 0) KDA_DSTATES_FETCH(ci - 1);          // in flight during this chunk
         __syncthreads();
         // dX = scale M^T dO + Wm dS1: this wave's rows of Wm dS1 (A: Wm
@@ -535,20 +535,20 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
                     xpart = mfma_k4(wmT[16 * (2 * wave + tt) + 4 * g + jj][l & 15], dsa[tt][jj], xpart);
-            xpw[wave][l] = xpart;
+            xpw[sub][wave][l] = xpart;
         }
         const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
         f32x4_t dX = zero;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-            dX = mfma_k4(Ml[4 * ks + g][l & 15], dol[4 * ks + g][l & 15], dX);
+            dX = mfma_k4(Ml[4 * ks + g][l & 15], dol[sub][4 * ks + g][l & 15], dX);
         __syncthreads();
         // every wave sums the same partials in the same order: lane l holds
         // dX tokens 4g + jj of column l%16
-        dX += xpw[0][l];
-        dX += xpw[1][l];
-        dX += xpw[2][l];
-        dX += xpw[3][l];
+        dX += xpw[sub][0][l];
+        dX += xpw[sub][1][l];
+        dX += xpw[sub][2][l];
+        dX += xpw[sub][3][l];
         if (wave == 0) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
@@ -566,7 +566,7 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(
             for (int jj = 0; jj < 4; ++jj) dsa[tt][jj] *= gam[16 * t + 4 * g + jj];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                dsa[tt] = mfma_k4(qtT[16 * t + (l & 15)][4 * g + jj], dol[4 * g + jj][l & 15], dsa[tt]);
+                dsa[tt] = mfma_k4(qtT[16 * t + (l & 15)][4 * g + jj], dol[sub][4 * g + jj][l & 15], dsa[tt]);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
                 dsa[tt] = mfma_k4(-ktT[16 * t + (l & 15)][4 * g + jj], dX[jj], dsa[tt]);
@@ -954,7 +954,9 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
     float *dxws = xws + sh * CS * HD;
     float *pdtb = dxws + sh * CS * HD;
     float *palog = pdtb + sh * HD;
-    const dim3 chunks((unsigned)sh), scans((unsigned)(8 * NPART * (((size_t)N * H + 7) / 8)));
+    const size_t units8 = ((size_t)N * H + 7) / 8;
+    const dim3 chunks((unsigned)sh);
+    const dim3 sgrid((unsigned)(8 * (NPART / SCAN_PG) * units8));
     hipError_t e = hipSuccess;
     auto mark = [&](int i) {
         if (events && events[i] && e == hipSuccess) e = hipEventRecord(events[i], stream);
@@ -963,10 +965,10 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
     hipLaunchKernelGGL(bwd_prep_kernel, chunks, dim3(BT), 0, stream,
                        q, k, g, beta, A_log, dt_bias, lower_bound, cu, N, T, H, K, brec);
     mark(1);
-    hipLaunchKernelGGL(bwd_states_kernel, scans, dim3(BT), 0, stream,
+    hipLaunchKernelGGL(bwd_states_kernel<SCAN_PG>, sgrid, dim3(BT * SCAN_PG), 0, stream,
                        v, brec, cu, N, T, H, K, init, init_fp32, st0, xws);
     mark(2);
-    hipLaunchKernelGGL(bwd_dstates_kernel, scans, dim3(BT), 0, stream,
+    hipLaunchKernelGGL(bwd_dstates_kernel<SCAN_PG>, sgrid, dim3(BT * SCAN_PG), 0, stream,
                        dout, brec, cu, N, T, H, K, scale, dfin, dst1, dxws, dv, dinit);
     mark(3);
     hipLaunchKernelGGL(bwd_chunk_kernel, chunks, dim3(BT), 0, stream,
