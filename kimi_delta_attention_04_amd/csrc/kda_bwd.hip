@@ -25,10 +25,11 @@
 //
 // Five launches, all fp32 arithmetic:
 //   prep    (chunk slot, head)  the chunk factors Kt, Qt, Wm, M, Gam -> workspace
-//   states  (sequence, head, 16-column part)  forward scan storing every
-//           chunk's start state S0 and X
-//   dstates (sequence, head, 16-column part)  reverse scan of dS, storing
-//           every chunk's dS1 and dX, writing dv and the initial-state gradient
+//   states  (sequence, head, four 16-column parts)  forward scan storing
+//           every chunk's start state S0 and X
+//   dstates (sequence, head, four 16-column parts)  reverse scan of dS,
+//           storing every chunk's dS1 and dX, writing dv and the
+//           initial-state gradient
 //   chunk   (chunk slot, head)  the products with S0 / dS1 (fp32 MFMA) and
 //           the in-chunk backward: dq, dk, dg, dbeta, per-chunk dA_log /
 //           ddt_bias sums

@@ -166,3 +166,24 @@ def test_head_dim_64_matches_oracle(kw):
                                              K=64)
     out = run_bwd(to_device(inp), d_out, d_final)
     check(inp, out, d_out, d_final)
+
+
+def test_many_heads_sampled():
+    """N x H = 80 (sequence, head) units: ten groups of eight in the scans'
+    XCD-aware block mapping, two four-part workgroups each."""
+    inp = kda_inputs.random_small(971, B=2, T=100, H=40, initial_state=True)
+    d_out, d_final = kda_inputs.output_grads(972, 2, 100, 40)
+    out = run_bwd(to_device(inp), d_out, d_final)
+    check(inp, out, d_out, d_final, heads=[0, 17, 39])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["varlen_mixed12_H96", "varlen_uniform_8x1024_H96"])
+def test_full_size_varlen_sampled_heads(name):
+    """The benchmark's varlen workloads at full size (8192 tokens, 96 heads),
+    every gradient of the sampled heads against the oracle."""
+    w = kda_inputs.WORKLOADS[name]
+    inp = kda_inputs.generate(w)
+    d_out, d_final = kda_inputs.output_grads(w.seed + 1, w.B, w.T, w.H, N=w.num_seqs)
+    out = run_bwd(to_device(inp), d_out, d_final)
+    check(inp, out, d_out, d_final, heads=[0, 47, 95])
