@@ -467,8 +467,12 @@ hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, 
     // workgroups (of fewer compute waves) so that more compute units share
     // the scan.  Parts of 32, 64 or 128 columns; V / part workgroups a head.
     const int cus = num_cus();
-    // (head dimension 256: parts of 32 or 64 columns, one slice per wave)
-    const int cw = V == 2 * HD ? (8 * units <= cus ? 32 : 64)
+    // (head dimension 256: parts of 32, 64 or 128 columns, one slice per
+    // wave.  The ring of 26 KB records leaves room for one workgroup per
+    // compute unit, so past 64 units (on 256 compute units) the parts are
+    // 128 columns wide, eight compute waves: two workgroups a head, one
+    // round of workgroups up to 128 units.)
+    const int cw = V == 2 * HD ? (8 * units <= cus ? 32 : 4 * units <= cus ? 64 : 128)
                  : (V == 128 ? 4 : 2) * units <= cus ? 32 : (V == 128 ? 2 : 1) * units <= cus ? 64 : 128;
     const int part_cw = cw > V ? V : cw;
     const int64_t blocks = 8 * (V / part_cw) * ((units + 7) / 8);
@@ -481,7 +485,8 @@ hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, 
         else KDA_SCAN(2, 4, HD);
     } else if (V == 2 * HD) {
         if (part_cw == 32) KDA_SCAN(1, 2, 2 * HD);
-        else KDA_SCAN(1, 4, 2 * HD);
+        else if (part_cw == 64) KDA_SCAN(1, 4, 2 * HD);
+        else KDA_SCAN(1, 8, 2 * HD);
     } else {
         if (part_cw == 32) KDA_SCAN(1, 2, 64);
         else KDA_SCAN(1, 4, 64);

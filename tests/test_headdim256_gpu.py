@@ -38,6 +38,7 @@ def check(inp, out, fin, heads=None):
     dict(B=2, T=100, H=2, initial_state=True),
     dict(B=1, T=300, H=3, seq_lens=(0, 17, 1, 200, 82), initial_state=True),
     dict(B=1, T=45, H=40, initial_state=True),               # four 64-column parts per head
+    dict(B=2, T=60, H=40, initial_state=True),               # 80 units: two 128-column parts per head
     dict(B=1, T=16, H=1),                                    # one full chunk
 ])
 def test_matches_oracle(kw):

@@ -100,6 +100,7 @@ def test_wide_source_constants_match_model():
 
 
 @pytest.mark.parametrize("rec_bytes,cw", [(REC_BYTES_256, 32), (REC_BYTES_256, 64),
+                                          (REC_BYTES_256, 128),
                                           (REC_BYTES, 128)])
 @pytest.mark.parametrize("nch", [0, 1, 2, 3, 4, 5, 7, 64])
 def test_dma_wait_ladder_wide(rec_bytes, cw, nch):
