@@ -122,11 +122,11 @@ def cpu_baseline(inp, w, heads: int):
 
 
 def bench_decode(args, torch, kda, kda_inputs):
-    N, H = args.decode_batch, args.decode_heads
-    log(f"[bench] decode: generating N={N} H={H} ...")
-    inp = kda_inputs.random_small(2, B=N, T=1, H=H)
+    N, H, D = args.decode_batch, args.decode_heads, args.head_dim
+    log(f"[bench] decode: generating N={N} H={H} D={D} ...")
+    inp = kda_inputs.random_small(2, B=N, T=1, H=H, K=D, V=D)
     gen = torch.Generator().manual_seed(2)
-    state0 = (torch.randn(N, H, 128, 128, generator=gen) * 0.05).float()
+    state0 = (torch.randn(N, H, D, D, generator=gen) * 0.05).float()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     flat = lambda t: t.reshape(N, H, -1).contiguous().to(dev)
@@ -134,7 +134,7 @@ def bench_decode(args, torch, kda, kda_inputs):
     beta = inp["beta"].reshape(N, H).contiguous().to(dev)
     A_log, dtb = inp["A_log"].to(dev), inp["dt_bias"].to(dev)
     state = state0.to(dev)
-    out = torch.empty(N, H, 128, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(N, H, D, dtype=torch.bfloat16, device=dev)
 
     def step():
         kda.decode(q, k, v, g, beta, inp["scale"], out, A_log, dtb, inp["lower_bound"], state)
@@ -151,7 +151,9 @@ def bench_decode(args, torch, kda, kda_inputs):
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
     units = N * H
-    bytes_ = units * (2 * 128 * 128 * 4 + 1282)
+    # per (sequence, head): the fp32 state read and written; q, k, v, g and
+    # o (bf16, D each) and beta
+    bytes_ = units * (2 * D * D * 4 + 10 * D + 2)
     achieved = bytes_ / (ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "kda_decode",
@@ -165,11 +167,12 @@ def bench_decode(args, torch, kda, kda_inputs):
         dt = time.perf_counter() - t0
         cpu = {"value": N / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
                "sample": f"the whole step: {N} sequences x {H} heads, fp64 C/OpenMP, {dt:.3f} s wall"}
-    rec = {"metric": f"KDA decode step tokens/s (one token per sequence) @N={N},H={H},D=128, fp32 state",
+    rec = {"metric": f"KDA decode step tokens/s (one token per sequence) @N={N},H={H},D={D}, fp32 state",
            "value": N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "fp32", "data": "synthetic (seeded)",
-           "config": {"workload": f"decode_N{N}_H{H}", "N": N, "H": H, "K": 128, "V": 128,
+           "config": {"workload": f"decode_N{N}_H{H}" + ("" if D == 128 else f"_D{D}"), "N": N, "H": H,
+                      "K": D, "V": D,
                       "state": "fp32, in place"},
            "roofline": roofline, "cpu_baseline": cpu}
     print(json.dumps(rec), flush=True)
