@@ -53,7 +53,6 @@ constexpr int NPART = HD / CWB;
 constexpr int NRG = BT / CWB;         // row groups of the state rows
 constexpr int RPT = HD / NRG;         // state rows per thread
 static_assert(NRG == CS && NRG * RPT == HD, "row groups cover the state rows, one per token row");
-constexpr int SCAN_PG = 4;            // column parts per scan workgroup
 
 // Chunk-factor record, fp32, per (chunk slot, head): Kt, Wm and Qt
 // transposed ([channel][token], 16 floats per channel), M [16][16] and
@@ -281,11 +280,26 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(
     if (tid < HD) rec[BR_GAM + tid] = L.gam[tid];
 }
 
+// Compute units of the current device (cached per device).
+int bwd_num_cus() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 // ---------------------------------------------------------------------------
 // The two scans run on 16-column parts of the state, four parts (1,024
-// threads) per workgroup, two workgroups per (sequence, head).  Each part's
-// four waves hold its 128 x 16 state slice in MFMA accumulator layout; the
-// four parts share one LDS copy of each chunk's factors, whose record is
+// threads; two workgroups per (sequence, head)) or two parts (512 threads)
+// per workgroup.  Each part's four waves hold its 128 x 16 state slice in
+// MFMA accumulator layout; the parts share one LDS copy of each chunk's
+// factors, whose record is
 // loaded into registers while the previous chunk computes (software
 // pipelining).  The factors are kept transposed ([channel][token]).
 //
@@ -320,8 +334,8 @@ __global__ __launch_bounds__(BT * PG) void bwd_states_kernel(
     // contraction take rows (or tokens) 4g + jj from lane group g in step jj.
     constexpr int NG = NPART / PG;                    // workgroups per (sequence, head)
     constexpr int NF = 2 * CS * HD / 4 / (BT * PG);   // 16-byte factor loads per thread
-    static_assert(NPART % PG == 0 && NF == 1 && BT * PG * 4 == 2 * CS * HD,
-                  "one 16-byte factor load per thread covers Kt and Wm");
+    static_assert(NPART % PG == 0 && (NF == 1 || NF == 2) && NF * BT * PG * 4 == 2 * CS * HD,
+                  "one or two 16-byte factor loads per thread cover Kt and Wm");
     __shared__ __attribute__((aligned(16))) float fac[2][HD][CS];   // Kt^T, Wm^T
     __shared__ __attribute__((aligned(16))) float gam[HD];
     __shared__ float vv[PG][CS][CWB];
@@ -359,18 +373,20 @@ __global__ __launch_bounds__(BT * PG) void bwd_states_kernel(
     const int nch = (int)((end - start + CS - 1) / CS);
     const int64_t slot0 = seq_slot0(cu, n, T);
 
-    // next chunk's Kt^T and Wm^T (16-byte piece tid of the two blocks, which
-    // lie next to each other in the record), e^{G_last} and v
+    // next chunk's Kt^T and Wm^T (16-byte pieces tid and, with two parts per
+    // workgroup, tid + BT PG of the two blocks, which lie next to each other
+    // in the record; named registers, not an array), e^{G_last} and v
     // element, in flight (the v element is loaded raw from a clamped row and
     // masked at use, so no branch forces a wait on the loads in flight)
     static_assert(BR_WM == BR_KT + CS * HD, "Kt^T and Wm^T adjacent in the record");
-    float4 pf, pg = {0.f, 0.f, 0.f, 0.f};
+    float4 pf, pf1, pg = {0.f, 0.f, 0.f, 0.f};
     uint16_t pd = 0;
     bool pvalid = false;
 #define KDA_STATES_FETCH(ci_)                                                                 \
     do {                                                                                      \
         const float *rec_ = brec + ((size_t)(slot0 + (ci_)) * H + h) * BR_FLOATS;             \
         pf = *(const float4 *)&rec_[BR_KT + 4 * tid];                                         \
+        if constexpr (NF == 2) pf1 = *(const float4 *)&rec_[BR_KT + 4 * (tid + BT * PG)];     \
         if (tid < HD / 4) pg = *(const float4 *)&rec_[BR_GAM + 4 * tid];                      \
         const int64_t tr_ = start + (int64_t)(ci_) * CS + ptid / CWB;                         \
         pvalid = tr_ < end && colv;                                                           \
@@ -387,6 +403,10 @@ __global__ __launch_bounds__(BT * PG) void bwd_states_kernel(
                 __builtin_nontemporal_store(sa[tt][jj], &dst[state_acc_off(part, 2 * wave + tt, jj, l)]);
         __syncthreads();                                // last chunk's readers are done
         *(float4 *)&fac[(4 * tid) / (CS * HD)][((4 * tid) % (CS * HD)) / CS][(4 * tid) % CS] = pf;
+        if constexpr (NF == 2) {
+            const int e1 = 4 * (tid + BT * PG);
+            *(float4 *)&fac[e1 / (CS * HD)][(e1 % (CS * HD)) / CS][e1 % CS] = pf1;
+        }
         if (tid < HD / 4) *(float4 *)&gam[4 * tid] = pg;
         vv[sub][ptid / CWB][j] = pvalid ? bf16f(pd) : 0.f;
         if (ci + 1 < nch) KDA_STATES_FETCH(ci + 1);     // in flight during this chunk
@@ -454,8 +474,9 @@ __global__ __launch_bounds__(BT * PG) void bwd_dstates_kernel(
     // of the chunk's record (same layout as in memory).
     constexpr int NG = NPART / PG;                    // workgroups per (sequence, head)
     constexpr int NREC = BR_FLOATS / 4;               // 16-byte pieces of a record
-    static_assert(NPART % PG == 0 && BR_FLOATS % 4 == 0 && NREC > BT * PG && NREC <= 2 * BT * PG,
-                  "two 16-byte loads per thread cover the record");
+    constexpr int NL = (NREC + BT * PG - 1) / (BT * PG);  // 16-byte loads per thread (2 or 4)
+    static_assert(NPART % PG == 0 && BR_FLOATS % 4 == 0 && (NL == 2 || NL == 4),
+                  "two (four parts) or four (two parts) 16-byte loads per thread cover the record");
     __shared__ __attribute__((aligned(16))) float recl[BR_FLOATS];
     __shared__ float dol[PG][CS][CWB];
     __shared__ f32x4_t xpw[PG][BT / 64][64];         // per-wave partial Wm dS1
@@ -493,17 +514,24 @@ __global__ __launch_bounds__(BT * PG) void bwd_dstates_kernel(
     const int nch = (int)((end - start + CS - 1) / CS);
     const int64_t slot0 = seq_slot0(cu, n, T);
 
-    // next chunk's record (16-byte pieces tid and tid + BT * PG) and dO
-    // element, in flight
-    float4 pr0, pr1 = {0.f, 0.f, 0.f, 0.f};
-    const bool two = tid + BT * PG < NREC;
+    // next chunk's record (16-byte pieces tid + m BT PG, m < NL, the last
+    // partly; named registers, not an array) and dO element, in flight
+    const float4 z4 = {0.f, 0.f, 0.f, 0.f};
+    float4 pr0 = z4, pr1 = z4, pr2 = z4, pr3 = z4;
+    const bool lastv = tid + (NL - 1) * BT * PG < NREC;   // this thread's last piece exists
     uint16_t pd = 0;
     bool pvalid = false;
 #define KDA_DSTATES_FETCH(ci_)                                                                \
     do {                                                                                      \
         const float *rec_ = brec + ((size_t)(slot0 + (ci_)) * H + h) * BR_FLOATS;             \
         pr0 = *(const float4 *)&rec_[4 * tid];                                                \
-        if (two) pr1 = *(const float4 *)&rec_[4 * (tid + BT * PG)];                           \
+        if constexpr (NL == 2) {                                                              \
+            if (lastv) pr1 = *(const float4 *)&rec_[4 * (tid + BT * PG)];                     \
+        } else {                                                                              \
+            pr1 = *(const float4 *)&rec_[4 * (tid + BT * PG)];                                \
+            pr2 = *(const float4 *)&rec_[4 * (tid + 2 * BT * PG)];                            \
+            if (lastv) pr3 = *(const float4 *)&rec_[4 * (tid + 3 * BT * PG)];                 \
+        }                                                                                     \
         const int64_t tr_ = start + (int64_t)(ci_) * CS + ptid / CWB;                         \
         pvalid = tr_ < end && colv;                                                           \
         pd = dout[((size_t)min(tr_, end - 1) * H + h) * kd + (colv ? col : 0)];               \
@@ -521,7 +549,13 @@ __global__ __launch_bounds__(BT * PG) void bwd_dstates_kernel(
         const int len = (int)min((int64_t)CS, end - t0);
         __syncthreads();
         *(float4 *)&recl[4 * tid] = pr0;
-        if (two) *(float4 *)&recl[4 * (tid + BT * PG)] = pr1;
+        if constexpr (NL == 2) {
+            if (lastv) *(float4 *)&recl[4 * (tid + BT * PG)] = pr1;
+        } else {
+            *(float4 *)&recl[4 * (tid + BT * PG)] = pr1;
+            *(float4 *)&recl[4 * (tid + 2 * BT * PG)] = pr2;
+            if (lastv) *(float4 *)&recl[4 * (tid + 3 * BT * PG)] = pr3;
+        }
         dol[sub][ptid / CWB][j] = pvalid ? scale * bf16f(pd) : 0.f;
         if (ci > 0) KDA_DSTATES_FETCH(ci - 1);          // in flight during this chunk
         __syncthreads();
@@ -957,7 +991,14 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
     float *palog = pdtb + sh * HD;
     const size_t units8 = ((size_t)N * H + 7) / 8;
     const dim3 chunks((unsigned)sh);
-    const dim3 sgrid((unsigned)(8 * (NPART / SCAN_PG) * units8));
+    // Four column parts per scan workgroup (each record read twice per head)
+    // when those workgroups cover at least three quarters of the compute
+    // units, else two (measured on 256 CUs: 96 heads run faster on 192
+    // four-part workgroups than on 384 two-part ones, 64 heads faster on 256
+    // two-part workgroups than on 128 four-part ones).
+    const bool pg4 = 8 * (int64_t)N * H >= 3 * (int64_t)bwd_num_cus();
+    const int pg = pg4 ? 4 : 2;
+    const dim3 sgrid((unsigned)(8 * (NPART / pg) * units8)), sblock((unsigned)(BT * pg));
     hipError_t e = hipSuccess;
     auto mark = [&](int i) {
         if (events && events[i] && e == hipSuccess) e = hipEventRecord(events[i], stream);
@@ -966,11 +1007,19 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
     hipLaunchKernelGGL(bwd_prep_kernel, chunks, dim3(BT), 0, stream,
                        q, k, g, beta, A_log, dt_bias, lower_bound, cu, N, T, H, K, brec);
     mark(1);
-    hipLaunchKernelGGL(bwd_states_kernel<SCAN_PG>, sgrid, dim3(BT * SCAN_PG), 0, stream,
-                       v, brec, cu, N, T, H, K, init, init_fp32, st0, xws);
+    if (pg4)
+        hipLaunchKernelGGL(bwd_states_kernel<4>, sgrid, sblock, 0, stream,
+                           v, brec, cu, N, T, H, K, init, init_fp32, st0, xws);
+    else
+        hipLaunchKernelGGL(bwd_states_kernel<2>, sgrid, sblock, 0, stream,
+                           v, brec, cu, N, T, H, K, init, init_fp32, st0, xws);
     mark(2);
-    hipLaunchKernelGGL(bwd_dstates_kernel<SCAN_PG>, sgrid, dim3(BT * SCAN_PG), 0, stream,
-                       dout, brec, cu, N, T, H, K, scale, dfin, dst1, dxws, dv, dinit);
+    if (pg4)
+        hipLaunchKernelGGL(bwd_dstates_kernel<4>, sgrid, sblock, 0, stream,
+                           dout, brec, cu, N, T, H, K, scale, dfin, dst1, dxws, dv, dinit);
+    else
+        hipLaunchKernelGGL(bwd_dstates_kernel<2>, sgrid, sblock, 0, stream,
+                           dout, brec, cu, N, T, H, K, scale, dfin, dst1, dxws, dv, dinit);
     mark(3);
     hipLaunchKernelGGL(bwd_chunk_kernel, chunks, dim3(BT), 0, stream,
                        q, k, g, beta, A_log, dt_bias, lower_bound, scale, dout, cu, N, T, H, K,
