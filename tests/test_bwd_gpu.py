@@ -187,3 +187,13 @@ def test_full_size_varlen_sampled_heads(name):
     d_out, d_final = kda_inputs.output_grads(w.seed + 1, w.B, w.T, w.H, N=w.num_seqs)
     out = run_bwd(to_device(inp), d_out, d_final)
     check(inp, out, d_out, d_final, heads=[0, 47, 95])
+
+
+def test_four_part_scans_with_empty_sequences():
+    """200 (sequence, head) units take the four-part scan workgroups; the
+    batch holds empty and one-token sequences."""
+    lens = (0, 17, 1, 60, 0)
+    inp = kda_inputs.random_small(981, B=1, T=sum(lens), H=40, seq_lens=lens, initial_state=True)
+    d_out, d_final = kda_inputs.output_grads(982, 1, sum(lens), 40, N=len(lens))
+    out = run_bwd(to_device(inp), d_out, d_final)
+    check(inp, out, d_out, d_final, heads=[0, 21, 39])
