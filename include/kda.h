@@ -97,9 +97,9 @@ typedef enum {
  *
  * The state of each sequence starts from initial_state (or zeros) and does
  * not leak across sequences.  Internally the call takes a stream-ordered
- * workspace of kda_workspace_size(B, T, H, num_seqs) bytes from a
+ * workspace of kda_workspace_size_hd(B, T, H, num_seqs, K) bytes from a
  * library-owned memory pool on the current device and returns it on the
- * same stream.
+ * same stream (see kda_trim_workspace for how much of it stays reserved).
  *
  * Returns KDA_OK, or KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED before any
  * HIP call, KDA_ERR_OUT_OF_MEMORY, or KDA_ERR_LAUNCH.
@@ -229,6 +229,27 @@ float kda_lower_bound_min(void);
 
 /* Tokens per chunk of the chunkwise algorithm (16). */
 int32_t kda_chunk_size(void);
+
+/*
+ * Workspace memory.  kda_fwd, kda_fwd_scalar_gate and kda_bwd take their
+ * workspace from a memory pool the library owns, one per device, with
+ * stream-ordered allocations (hipMallocFromPoolAsync / hipFreeAsync on the
+ * call's stream).  Freed blocks stay reserved for later calls up to 1 GiB
+ * per device; whatever is above that is returned to the device when a
+ * stream or the device synchronises.  (A backward at T = 8192, H = 96 takes
+ * about 7.8 GB, of which 1 GiB then stays reserved.)
+ *
+ * kda_trim_workspace — returns reserved but unused pool memory of the
+ * current device until at most keep_bytes stay reserved (keep_bytes = 0:
+ * everything not in use).  Blocks still in use by enqueued work are not
+ * released; call it after synchronising the streams that used the library.
+ * Returns KDA_OK (also when the pool was never created) or KDA_ERR_LAUNCH.
+ *
+ * kda_workspace_reserved — bytes the pool of the current device holds
+ * reserved (in use or cached); 0 when the pool was never created.
+ */
+kda_status_t kda_trim_workspace(size_t keep_bytes);
+size_t kda_workspace_reserved(void);
 
 /*
  * Bytes of device workspace one kda_fwd call with these sizes and head

@@ -118,6 +118,9 @@ WORKLOADS = {
 }
 
 HEADLINE = "fixed_T8192_H96"
+# The T = 8192 workloads a benchmark run times (the headline first).
+BENCH_WORKLOADS = ("fixed_T8192_H96", "fixed_T8192_H64", "varlen_uniform_8x1024_H96",
+                   "varlen_mixed12_H96", "varlen_mixed12_H64")
 
 
 def custom(name: str, seed: int, B: int, T: int, H: int, seq_lens=None,

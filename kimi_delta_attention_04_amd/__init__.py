@@ -86,6 +86,10 @@ def load():
                             P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
     lib.kda_debug_intra.restype = ctypes.c_int
     lib.kda_debug_intra.argtypes = [P, P, P, P, P, P, f32, P, i32, i32, i32, i32, i32, P, P]
+    lib.kda_trim_workspace.restype = ctypes.c_int
+    lib.kda_trim_workspace.argtypes = [ctypes.c_size_t]
+    lib.kda_workspace_reserved.restype = ctypes.c_size_t
+    lib.kda_workspace_reserved.argtypes = []
     _lib = lib
     return lib
 
@@ -131,6 +135,19 @@ def chunk_size() -> int:
 def workspace_size(B: int, T: int, H: int, num_seqs: int, K: int = 128) -> int:
     """Bytes of the hand-off records of one forward call (head dimension K)."""
     return int(load().kda_workspace_size_hd(B, T, H, num_seqs, K))
+
+
+def trim_workspace(keep_bytes: int = 0) -> None:
+    """Return the library pool's unused reserved memory on the current
+    device until at most keep_bytes stay reserved (kda_trim_workspace)."""
+    st = load().kda_trim_workspace(int(keep_bytes))
+    if st != 0:
+        raise KDAError(st, "kda_trim_workspace")
+
+
+def workspace_reserved() -> int:
+    """Bytes the library pool holds reserved on the current device."""
+    return int(load().kda_workspace_reserved())
 
 
 def _ptr(t):

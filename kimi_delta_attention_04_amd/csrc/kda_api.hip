@@ -18,15 +18,21 @@ namespace {
 constexpr float kLowerBoundMin = -5.4f;
 constexpr int kMaxDevices = 64;
 
+// Workspace memory the library's pool keeps reserved across calls once the
+// stream that freed it has synchronised; anything above is returned to the
+// device (kda_trim_workspace releases the rest on demand).
+constexpr uint64_t kDefaultKeepBytes = 1ull << 30;
+
 std::mutex g_pool_mu;
 hipMemPool_t g_pools[kMaxDevices];
 bool g_pool_ready[kMaxDevices];
 
-kda_status_t device_pool(hipMemPool_t *pool) {
+kda_status_t device_pool(hipMemPool_t *pool, bool create = true) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KDA_ERR_LAUNCH;
     std::lock_guard<std::mutex> lock(g_pool_mu);
     if (!g_pool_ready[dev]) {
+        if (!create) { *pool = nullptr; return KDA_OK; }
         hipMemPoolProps props = {};
         props.allocType = hipMemAllocationTypePinned;
         props.handleTypes = hipMemHandleTypeNone;
@@ -34,7 +40,7 @@ kda_status_t device_pool(hipMemPool_t *pool) {
         props.location.id = dev;
         hipMemPool_t p = nullptr;
         if (hipMemPoolCreate(&p, &props) != hipSuccess) return KDA_ERR_LAUNCH;
-        uint64_t keep = UINT64_MAX;   // keep freed blocks for reuse by later calls
+        uint64_t keep = kDefaultKeepBytes;   // freed blocks up to this are kept for later calls
         if (hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep) != hipSuccess) {
             (void)hipMemPoolDestroy(p);
             return KDA_ERR_LAUNCH;
@@ -136,6 +142,21 @@ const char *kda_status_string(kda_status_t s) {
 float kda_lower_bound_min(void) { return kLowerBoundMin; }
 
 int32_t kda_chunk_size(void) { return kda::CS; }
+
+kda_status_t kda_trim_workspace(size_t keep_bytes) {
+    hipMemPool_t pool = nullptr;
+    kda_status_t st = device_pool(&pool, false);
+    if (st != KDA_OK || !pool) return st;
+    return hipMemPoolTrimTo(pool, keep_bytes) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+size_t kda_workspace_reserved(void) {
+    hipMemPool_t pool = nullptr;
+    if (device_pool(&pool, false) != KDA_OK || !pool) return 0;
+    uint64_t v = 0;
+    if (hipMemPoolGetAttribute(pool, hipMemPoolAttrReservedMemCurrent, &v) != hipSuccess) return 0;
+    return (size_t)v;
+}
 
 size_t kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs) {
     return kda_workspace_size_hd(B, T, H, num_seqs, kda::HD);

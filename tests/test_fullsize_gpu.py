@@ -1,9 +1,9 @@
 """Full-size parity on the T=8192, D=128 workloads, in the same launch
 configuration the benchmark times (kda.fwd with its defaults).
 
-Heads are independent, so the oracle computes a sample of heads exactly
-(all 8192 tokens of each) and the GPU output of those heads is compared
-element by element.  The uniform varlen workload is also checked bitwise
+The C oracle computes every head (all 8192 tokens of each, about a second
+on the host's cores) and the whole GPU output is compared element by
+element.  The uniform varlen workload is also checked bitwise
 against the same tokens run as a fixed-length batch of 8 x 1024.
 """
 from __future__ import annotations
@@ -19,10 +19,6 @@ from gpu_util import assert_close, np64, run_kda, to_device
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-def sample_heads(H):
-    return sorted({0, H // 3, (2 * H) // 3, H - 1})
-
-
 @pytest.mark.parametrize("name", ["fixed_T8192_H64", "fixed_T8192_H96",
                                   "varlen_uniform_8x1024_H96", "varlen_mixed12_H96",
                                   "varlen_mixed12_H64"])
@@ -32,17 +28,17 @@ def test_full_size_workload(name):
     inp = kda_inputs.generate(w)
     d = to_device(inp)
     out, fin = run_kda(d)
-    heads = sample_heads(w.H)
-    o_ref, f_ref = oracle.cref_forward(inp, heads=heads)
-    o_gpu = np64(out[:, :, heads])
-    f_gpu = np64(fin[:, heads])
+    o_ref, f_ref = oracle.cref_forward(inp)
+    o_gpu = np64(out)
+    f_gpu = np64(fin)
     r_o = assert_close(f"{name} o", o_gpu, o_ref)
     r_f = assert_close(f"{name} final_state", f_gpu, f_ref)
     print(f"{name}: o rel_l2={r_o[0]:.3e} max_abs={r_o[1]:.3e}; "
           f"final rel_l2={r_f[0]:.3e} max_abs={r_f[1]:.3e}", flush=True)
-    # every output row written (outputs were NaN-poisoned before the call)
-    assert torch.isfinite(out).all().item()
-    assert torch.isfinite(fin).all().item()
+    # per-head bar too, so that one wrong head cannot hide in the whole-tensor norm
+    for h in range(w.H):
+        assert_close(f"{name} o head {h}", o_gpu[:, :, h], o_ref[:, :, h])
+        assert_close(f"{name} final_state head {h}", f_gpu[:, h], f_ref[:, h])
     if name == "varlen_uniform_8x1024_H96":
         fixed = dict(d)
         for key in ("q", "k", "v", "g", "beta"):
@@ -81,12 +77,11 @@ def test_long_sequence_split_bitexact():
 
 
 def test_many_heads():
-    """H = 4096 heads (one column part per head in the scan), sampled heads
+    """H = 4096 heads (one column part per head in the scan), every head
     against the oracle."""
     H = 4096
     inp = kda_inputs.random_small(1002, B=1, T=40, H=H, initial_state=True)
     out, fin = run_kda(to_device(inp))
-    heads = sample_heads(H)
-    o_ref, f_ref = oracle.cref_forward(inp, heads=heads)
-    assert_close("o", np64(out[:, :, heads]), o_ref)
-    assert_close("final_state", np64(fin[:, heads]), f_ref)
+    o_ref, f_ref = oracle.cref_forward(inp)
+    assert_close("o", np64(out), o_ref)
+    assert_close("final_state", np64(fin), f_ref)

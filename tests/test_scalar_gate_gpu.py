@@ -91,12 +91,11 @@ def test_no_dt_bias_and_clamped_gates():
 
 
 @pytest.mark.slow
-def test_full_size_h96_sampled_heads():
-    """T = 8192, H = 96 with the scalar gate, four heads against the oracle."""
+def test_full_size_h96_all_heads():
+    """T = 8192, H = 96 with the scalar gate, every head against the oracle."""
     inp, g_s, dtb_s = scalar_gate_inputs(601, B=1, T=8192, H=96, initial_state=True)
     out, fin = run_scalar(inp, g_s, dtb_s)
-    heads = [0, 33, 66, 95]
-    o_ref, f_ref = oracle.cref_forward(inp, heads=heads)
-    ro = assert_close("o", np64(out)[:, :, heads], o_ref)
-    rf = assert_close("final_state", np64(fin)[:, heads], f_ref)
+    o_ref, f_ref = oracle.cref_forward(inp)
+    ro = assert_close("o", np64(out), o_ref)
+    rf = assert_close("final_state", np64(fin), f_ref)
     print(f"o rel_l2={ro[0]:.3e}; final rel_l2={rf[0]:.3e}", flush=True)
