@@ -56,7 +56,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 METRIC = "KDA fwd tokens/s @T=8192,H=96,D=128 (fixed+varlen); % of MFMA/HBM roofline"
-CHUNK = 16
+CHUNK = 32           # tokens per chunk of the forward at K = V = 128
+BWD_CHUNK = 16       # the backward's chunk factors
 
 
 def log(*a):
@@ -261,8 +262,9 @@ def bench_backward(args, torch, kda, kda_inputs):
             "hbm_frac": path_gbs / HBM_PEAK_GBS, "stage_ms": stage,
             "stage_traffic_bytes": {k: (t["total_bytes"] if t else None) for k, t in
                                     ((k, stored_traffic(name, k, backward=True)) for k in names)},
-            "workspace_bytes": int(w.H * (w.tokens // CHUNK + w.num_seqs) * 4 *
-                                   (3 * CHUNK * w.K + CHUNK * CHUNK + w.K + 2 * w.K * w.V + 1 + w.K))}
+            "workspace_bytes": int(w.H * (w.tokens // BWD_CHUNK + w.num_seqs) * 4 *
+                                   (3 * BWD_CHUNK * w.K + BWD_CHUNK * BWD_CHUNK + w.K +
+                                    2 * w.K * w.V + 1 + w.K))}
     cpu = None
     if not args.no_cpu_baseline:
         import oracle

@@ -96,7 +96,7 @@ def load():
 
 # The sources the forward kernels (intra stage and scan) are compiled from,
 # and those of the backward kernels.
-FORWARD_KERNEL_SOURCES = ("kda_device.h", "kda_intra_dev.h", "kda_intra.hip", "kda_scan.hip")
+FORWARD_KERNEL_SOURCES = ("kda_device.h", "kda_intra_dev.h", "kda_c32_dev.h", "kda_c32.hip")
 BACKWARD_KERNEL_SOURCES = ("kda_device.h", "kda_intra_dev.h", "kda_bwd.hip")
 
 

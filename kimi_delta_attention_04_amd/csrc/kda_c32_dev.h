@@ -73,57 +73,74 @@ __device__ __forceinline__ int64_t seq_slot0_32(const int32_t *cu, int n, int T)
 struct Wave32Lds {
     float beta[C32];
     float gam[HD];
+    // Khat of sub-block b, state row tile t, as (hi, lo) B operands of the
+    // W products: [b][t][hi/lo][lane]
+    u32x2_t khat[2][8][2][64];
 };
 
 // Token-per-lane inputs of one 32-token chunk: lane l holds tokens l%16
 // (sub-block 0) and 16 + l%16 (sub-block 1), eight channels 32kb + 8(l/16) + i
-// of each 32-channel block kb.
-struct Intra32In {
-    u32x4_t g[2][4], q[2][4], k[2][4];
+// of a 32-channel block kb.  The wave reads one block at a time, one block
+// ahead of its use.
+struct Intra32Src {
+    __amdgpu_buffer_rsrc_t g, q, k;
+    int row_bytes;                     // bytes between consecutive token rows
+    int K;
     uint32_t beta[2];
     uint32_t gs[2];                    // scalar gate (Gated DeltaNet form)
 };
+struct Intra32Blk {
+    u32x4_t g[2], q[2], k[2];
+};
 
-// Loads one chunk of len tokens starting at token row t0 (K = 128, or 64
-// with the channels from 64 on read as zeros).  Rows past len read as zeros.
+// Sets up the reads of one chunk of len tokens starting at token row t0
+// (K = 128, or 64 with the channels from 64 on read as zeros) and reads the
+// per-token values.  Rows past len read as zeros.
 template <bool SG>
-__device__ __forceinline__ void intra32_load(Intra32In &in, const uint16_t *__restrict__ q,
-                                             const uint16_t *__restrict__ k,
-                                             const uint16_t *__restrict__ g,
-                                             const uint16_t *__restrict__ beta, int64_t t0,
-                                             int len, int H, int hh, int K) {
+__device__ __forceinline__ void intra32_src(Intra32Src &s, const uint16_t *__restrict__ q,
+                                            const uint16_t *__restrict__ k,
+                                            const uint16_t *__restrict__ g,
+                                            const uint16_t *__restrict__ beta, int64_t t0,
+                                            int len, int H, int hh, int K) {
     const int l = threadIdx.x & 63;
-    const int tok = l & 15, cgp = l >> 4;
+    const int tok = l & 15;
     const size_t row_elems = (size_t)H * K;
     const size_t base = ((size_t)t0 * H + hh) * K;
     const uint32_t bytes = len > 0 ? (uint32_t)(((size_t)(len - 1) * row_elems + K) * 2) : 0u;
-    const __amdgpu_buffer_rsrc_t sg = make_rsrc(g + base, bytes);
-    const __amdgpu_buffer_rsrc_t sq = make_rsrc(q + base, bytes);
-    const __amdgpu_buffer_rsrc_t sk = make_rsrc(k + base, bytes);
-    const u32x4_t z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int off = (int)(((16 * b + tok) * row_elems + 32 * kb + 8 * cgp) * 2);
-            in.g[b][kb] = in.q[b][kb] = in.k[b][kb] = z;
-            if (32 * kb < K) {                  // uniform
-                if (!SG)
-                    in.g[b][kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sg, off, 0, 0));
-                in.q[b][kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sq, off, 0, 0));
-                in.k[b][kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sk, off, 0, 0));
-            }
-        }
+    s.g = make_rsrc(g + base, SG ? 0u : bytes);
+    s.q = make_rsrc(q + base, bytes);
+    s.k = make_rsrc(k + base, bytes);
+    s.row_bytes = (int)(row_elems * 2);
+    s.K = K;
     const uint32_t tb = len > 0 ? (uint32_t)(((size_t)(len - 1) * H + 1) * 2) : 0u;
     const __amdgpu_buffer_rsrc_t sb = make_rsrc(beta + (size_t)t0 * H + hh, tb);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
-        in.beta[b] = __builtin_amdgcn_raw_buffer_load_b16(sb, (16 * b + tok) * H * 2, 0, 0);
+        s.beta[b] = __builtin_amdgcn_raw_buffer_load_b16(sb, (16 * b + tok) * H * 2, 0, 0);
     if (SG) {
         const __amdgpu_buffer_rsrc_t ss = make_rsrc(g + (size_t)t0 * H + hh, tb);
 #pragma unroll
         for (int b = 0; b < 2; ++b)
-            in.gs[b] = __builtin_amdgcn_raw_buffer_load_b16(ss, (16 * b + tok) * H * 2, 0, 0);
+            s.gs[b] = __builtin_amdgcn_raw_buffer_load_b16(ss, (16 * b + tok) * H * 2, 0, 0);
+    } else {
+        s.gs[0] = s.gs[1] = 0u;
+    }
+}
+
+template <bool SG>
+__device__ __forceinline__ void intra32_read(Intra32Blk &x, const Intra32Src &s, int kb) {
+    const int l = threadIdx.x & 63;
+    const int tok = l & 15, cgp = l >> 4;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int off = (16 * b + tok) * s.row_bytes + (32 * kb + 8 * cgp) * 2;
+        x.g[b] = x.q[b] = x.k[b] = z;
+        if (32 * kb < s.K) {                    // uniform
+            if (!SG) x.g[b] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(s.g, off, 0, 0));
+            x.q[b] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(s.q, off, 0, 0));
+            x.k[b] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(s.k, off, 0, 0));
+        }
     }
 }
 
@@ -175,7 +192,7 @@ __device__ __forceinline__ f32x4_t mfma3_k16(u32x2_t ah, u32x2_t al, u32x2_t bh,
 // memory, or any address space the stores reach).  NT: non-temporal record
 // stores.
 template <bool FULL, bool SG, bool NT = true>
-__device__ __forceinline__ void intra32_compute(Wave32Lds &L, const Intra32In &in, float A,
+__device__ __forceinline__ void intra32_compute(Wave32Lds &L, const Intra32Src &in, float A,
                                                 const float *__restrict__ dtb_lds, float lb2, int len,
                                                 uint8_t *__restrict__ rec) {
     typedef Rec32 R;
@@ -208,9 +225,6 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, const Intra32In &i
     // 0), AkkT the transposes of the diagonal ones, AqkT[i][r] = Aqk[r][i].
     f32x4_t A00 = zero, A00t = zero, A11 = zero, A11t = zero, A10 = zero;
     f32x4_t Q00t = zero, Q11t = zero, Q10t = zero;
-    // Khat of each sub-block as (hi, lo) B operands of the W products,
-    // per state row tile t (rows token, columns chan(t, .)).
-    u32x2_t kh[2][8], kl[2][8];
 
     float gsc[2] = {0.f, 0.f};         // SG form: the cumulative gate of each sub-block
     if (SG && A > 0.f) {
@@ -227,8 +241,12 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, const Intra32In &i
             gsc[b] = s;
         }
     }
+    Intra32Blk nxt;
+    intra32_read<SG>(nxt, in, 0);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
+        const Intra32Blk cur = nxt;
+        if (kb + 1 < 4) intra32_read<SG>(nxt, in, kb + 1);
         float gl[2][8];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -241,7 +259,7 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, const Intra32In &i
                 *(f32x4_t *)&dtb2[4] = *(const f32x4_t *)&dtb_lds[32 * kb + 8 * grp + 4];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float x2 = elem(in.g[b][kb], i) * LOG2E + dtb2[i];
+                    const float x2 = elem(cur.g[b], i) * LOG2E + dtb2[i];
                     const float u = fast_log2(1.f + fast_exp2(x2));
                     const float la = fmaxf(-A * u, lb2);
                     gl[b][i] = live[b] ? la : 0.f;
@@ -275,18 +293,18 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, const Intra32In &i
                 const int i = 2 * wd + e;
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
-                    const float kv = elem(in.k[b][kb], i), qv = elem(in.q[b][kb], i);
+                    const float kv = elem(cur.k[b], i), qv = elem(cur.q[b], i);
                     kF[b][e] = kv * F[b][e];
                     qF[b][e] = qv * F[b][e];
                     kB[b][e] = kv * Bv[b][e];
                 }
                 const float e0 = Bv[0][e] * eg[0][e];            // 2^{Gam_0 - g^0}
                 const float e1 = Bv[1][e] * eg[1][e];            // 2^{Gam_1 - g^1}
-                ke0[e] = elem(in.k[0][kb], i) * e0;
+                ke0[e] = elem(cur.k[0], i) * e0;
                 kt1f[e] = kF[1][e] * eg[0][e];                   // chunk-level Kt, Qt of sub-block 1
                 qt1f[e] = qF[1][e] * eg[0][e];
                 khat[0][e] = ke0[e] * eg[1][e];                  // k 2^{G_last - G}
-                khat[1][e] = elem(in.k[1][kb], i) * e1;
+                khat[1][e] = elem(cur.k[1], i) * e1;
             }
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
@@ -344,8 +362,8 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, const Intra32In &i
                 const u32x2_t al = {klt[b][2 * h], klt[b][2 * h + 1]};
                 const f32x4_t dh = mfma_k16(ah, eye, zero);
                 const f32x4_t dl = mfma_k16(al, eye, zero);
-                kh[b][2 * kb + h] = {pack2(dh[0], dh[1]), pack2(dh[2], dh[3])};
-                kl[b][2 * kb + h] = {pack2(dl[0], dl[1]), pack2(dl[2], dl[3])};
+                L.khat[b][2 * kb + h][0][l] = {pack2(dh[0], dh[1]), pack2(dh[2], dh[3])};
+                L.khat[b][2 * kb + h][1][l] = {pack2(dl[0], dl[1]), pack2(dl[2], dl[3])};
             }
     }
 
@@ -412,9 +430,11 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, const Intra32In &i
     // ---- W tiles: W = Tb^T Khat ---------------------------------------------
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        f32x4_t w0 = mfma3_k16(tb00h, tb00l, kh[0][t], kl[0][t], zero);
-        w0 = mfma3_k16(tb10h, tb10l, kh[1][t], kl[1][t], w0);
-        const f32x4_t w1 = mfma3_k16(tb11h, tb11l, kh[1][t], kl[1][t], zero);
+        const u32x2_t k0h = L.khat[0][t][0][l], k0l = L.khat[0][t][1][l];
+        const u32x2_t k1h = L.khat[1][t][0][l], k1l = L.khat[1][t][1][l];
+        f32x4_t w0 = mfma3_k16(tb00h, tb00l, k0h, k0l, zero);
+        w0 = mfma3_k16(tb10h, tb10l, k1h, k1l, w0);
+        const f32x4_t w1 = mfma3_k16(tb11h, tb11l, k1h, k1l, zero);
         const u32x4_t o = {pack2(w0[0], w0[1]), pack2(w0[2], w0[3]), pack2(w1[0], w1[1]),
                            pack2(w1[2], w1[3])};
         st16(o, R::WT + (t * 64 + l) * 16);
