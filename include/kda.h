@@ -142,6 +142,34 @@ kda_status_t kda_fwd_scalar_gate(const void *q, const void *k, const void *v, co
                                  void *stream);
 
 /*
+ * kda_fwd_noalloc — kda_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Arguments, layouts, results and errors are those of kda_fwd
+ * (the results are bitwise identical to kda_fwd's), except:
+ *   - no allocation or free happens: the workspace is a file-scope device
+ *     array of the library, KDA_NOALLOC_WORKSPACE_BYTES (64 MiB) plus 256
+ *     bytes, which every device the library runs on holds until the
+ *     process ends;
+ *   - calls whose workspace, kda_workspace_size_hd(B, T, H, num_seqs, K),
+ *     exceeds KDA_NOALLOC_WORKSPACE_BYTES return KDA_ERR_UNSUPPORTED before
+ *     any HIP call (e.g. T = 8192 fits up to H = 9 at K = 128);
+ *   - every call on a device shares that device's array, which keeps the
+ *     last call's contents (every byte a call reads it has written first):
+ *     calls that overlap on one device (on different streams, or from
+ *     different host threads without ordering) race and must not be made.
+ */
+#define KDA_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+kda_status_t kda_fwd_noalloc(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, float scale,
+                             const float *A_log, const float *dt_bias, float lower_bound,
+                             const int32_t *cu_seqlens, int32_t num_seqs,
+                             const void *initial_state, kda_dtype_t initial_state_dtype,
+                             void *final_state, kda_dtype_t final_state_dtype,
+                             void *out,
+                             int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                             void *stream);
+
+/*
  * kda_decode — one decode step: a single new token per sequence applied to
  * the recurrent state in place (the step after a prefill; it consumes the
  * final_state kda_fwd wrote, same layout).  "FlashKDA" product page, Main

@@ -26,7 +26,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "fwd_scalar_gate", "decode", "bwd", "debug_intra", "set_stage_events", "set_bwd_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
+__all__ = ["fwd", "fwd_noalloc", "fwd_scalar_gate", "decode", "bwd", "debug_intra", "set_stage_events", "set_bwd_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
            "status_string", "KDAError", "library_path", "load", "HEAD_DIM"]
 
 HEAD_DIM = 128
@@ -86,6 +86,8 @@ def load():
                             P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
     lib.kda_debug_intra.restype = ctypes.c_int
     lib.kda_debug_intra.argtypes = [P, P, P, P, P, P, f32, P, i32, i32, i32, i32, i32, P, P]
+    lib.kda_fwd_noalloc.restype = ctypes.c_int
+    lib.kda_fwd_noalloc.argtypes = lib.kda_fwd.argtypes
     lib.kda_trim_workspace.restype = ctypes.c_int
     lib.kda_trim_workspace.argtypes = [ctypes.c_size_t]
     lib.kda_workspace_reserved.restype = ctypes.c_size_t
@@ -195,6 +197,19 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
                 initial_state, final_state, cu_seqlens, scalar_gate=False)
 
 
+def fwd_noalloc(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                initial_state=None, final_state=None, cu_seqlens=None):
+    """As fwd, through kda_fwd_noalloc: the library allocates nothing (its
+    workspace is a fixed device array of NOALLOC_WORKSPACE_BYTES); calls
+    needing more workspace raise KDAError (KDA_ERR_UNSUPPORTED)."""
+    return _fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                initial_state, final_state, cu_seqlens, scalar_gate=False, noalloc=True)
+
+
+# kda.h: KDA_NOALLOC_WORKSPACE_BYTES
+NOALLOC_WORKSPACE_BYTES = 64 << 20
+
+
 def fwd_scalar_gate(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
                     initial_state=None, final_state=None, cu_seqlens=None):
     """The Gated DeltaNet case: as fwd, but g is bf16 [B, T, H] (one gate
@@ -205,7 +220,7 @@ def fwd_scalar_gate(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
 
 
 def _fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
-         initial_state, final_state, cu_seqlens, scalar_gate):
+         initial_state, final_state, cu_seqlens, scalar_gate, noalloc=False):
     import torch
     lib = load()
     if q.dim() != 4:
@@ -234,13 +249,14 @@ def _fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
     if final_state is not None:
         fin_dt = _state_dtype(final_state)
         _check(final_state, "final_state", final_state.dtype, (N, H, K, V))
-    entry = lib.kda_fwd_scalar_gate if scalar_gate else lib.kda_fwd
+    name = "kda_fwd_scalar_gate" if scalar_gate else ("kda_fwd_noalloc" if noalloc else "kda_fwd")
+    entry = getattr(lib, name)
     rc = entry(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
                _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(cu_seqlens), int(N),
                _ptr(initial_state), init_dt, _ptr(final_state), fin_dt, _ptr(out),
                int(B), int(T), int(H), int(K), int(V), _stream(q.device))
     if rc != 0:
-        raise KDAError(rc, "kda_fwd_scalar_gate" if scalar_gate else "kda_fwd")
+        raise KDAError(rc, name)
     return out
 
 

@@ -111,21 +111,27 @@ bool cu_check_enabled() {
     return e && e[0] && !(e[0] == '0' && e[1] == 0);
 }
 
-// KDA_OK, KDA_ERR_INVALID_ARG for bad contents, or KDA_ERR_LAUNCH.
+// KDA_OK, KDA_ERR_INVALID_ARG for bad contents, or KDA_ERR_LAUNCH.  `bad`:
+// one device int the check may overwrite.
+kda_status_t check_cu_flag(const int32_t *cu, int N, int T, hipStream_t s, int *bad) {
+    int host_bad = 1;
+    hipLaunchKernelGGL(check_cu_kernel, dim3(1), dim3(256), 0, s, cu, N, T, bad);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = hipMemcpyAsync(&host_bad, bad, sizeof(int), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return KDA_ERR_LAUNCH;
+    return host_bad ? KDA_ERR_INVALID_ARG : KDA_OK;
+}
+
 kda_status_t check_cu_contents(const int32_t *cu, int N, int T, hipStream_t s, hipMemPool_t pool) {
     int *bad = nullptr;
     if (hipMallocFromPoolAsync((void **)&bad, sizeof(int), pool, s) != hipSuccess || !bad) {
         (void)hipGetLastError();
         return KDA_ERR_OUT_OF_MEMORY;
     }
-    int host_bad = 1;
-    hipLaunchKernelGGL(check_cu_kernel, dim3(1), dim3(256), 0, s, cu, N, T, bad);
-    hipError_t e = hipGetLastError();
-    if (e == hipSuccess) e = hipMemcpyAsync(&host_bad, bad, sizeof(int), hipMemcpyDeviceToHost, s);
-    const hipError_t ef = hipFreeAsync(bad, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e != hipSuccess || ef != hipSuccess) return KDA_ERR_LAUNCH;
-    return host_bad ? KDA_ERR_INVALID_ARG : KDA_OK;
+    kda_status_t st = check_cu_flag(cu, N, T, s, bad);
+    if (hipFreeAsync(bad, s) != hipSuccess && st == KDA_OK) st = KDA_ERR_LAUNCH;
+    return st;
 }
 
 kda_status_t check_gate(float lower_bound) {
@@ -183,17 +189,14 @@ size_t kda_workspace_size_hd(int32_t B, int32_t T, int32_t H, int32_t num_seqs, 
 
 namespace {
 
-// kda_fwd and kda_fwd_scalar_gate: scalar_gate selects the layout of g
-// ([B, T, H, K] or [B, T, H]) and dt_bias ([H*K] or [H]).
-kda_status_t fwd_impl(const void *q, const void *k, const void *v, const void *g,
-                      const void *beta, float scale,
-                      const float *A_log, const float *dt_bias, float lower_bound,
-                      const int32_t *cu_seqlens, int32_t num_seqs,
-                      const void *initial_state, kda_dtype_t initial_state_dtype,
-                      void *final_state, kda_dtype_t final_state_dtype,
-                      void *out,
-                      int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
-                      void *stream, bool scalar_gate)
+// Argument checks shared by the forward entry points (before any HIP call).
+kda_status_t fwd_validate(const void *q, const void *k, const void *v, const void *g,
+                          const void *beta, float scale, const float *A_log,
+                          const float *dt_bias, float lower_bound, const int32_t *cu_seqlens,
+                          int32_t num_seqs, const void *initial_state,
+                          kda_dtype_t initial_state_dtype, const void *final_state,
+                          kda_dtype_t final_state_dtype, const void *out, int32_t B, int32_t T,
+                          int32_t H, int32_t K, int32_t V, bool scalar_gate)
 {
     // With no tokens the token buffers are never touched and may be NULL.
     const bool no_tokens = (int64_t)B * T == 0;
@@ -210,10 +213,65 @@ kda_status_t fwd_impl(const void *q, const void *k, const void *v, const void *g
     if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
     kda_status_t st = check_sizes(B, T, H, K, V, cu_seqlens, num_seqs);
     if (st != KDA_OK) return st;
-    if ((st = check_gate(lower_bound)) != KDA_OK) return st;
+    return check_gate(lower_bound);
+}
 
-    hipStream_t s = (hipStream_t)stream;
+// The forward's kernels on stream s with the workspace ws of
+// kda_workspace_size_hd(B, T, H, num_seqs, K) bytes.
+hipError_t fwd_launch(const void *q, const void *k, const void *v, const void *g,
+                      const void *beta, float scale, const float *A_log, const float *dt_bias,
+                      float lower_bound, const int32_t *cu_seqlens, int32_t num_seqs,
+                      const void *initial_state, kda_dtype_t initial_state_dtype,
+                      void *final_state, kda_dtype_t final_state_dtype, void *out, int32_t B,
+                      int32_t T, int32_t H, int32_t K, int32_t V, hipStream_t s,
+                      bool scalar_gate, void *ws)
+{
     const int64_t slots = fwd_slots(B, T, num_seqs, K);
+    const int init32 = initial_state_dtype == KDA_DTYPE_FP32;
+    const int fin32 = final_state_dtype == KDA_DTYPE_FP32;
+    hipError_t e = mark(0, s);
+    if (K <= kda::HD) {
+        if (e == hipSuccess)
+            e = kda::launch_intra32((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,
+                                    (const uint16_t *)beta, A_log, dt_bias, lower_bound, cu_seqlens,
+                                    num_seqs, T, H, K, slots, (uint8_t *)ws, s, scalar_gate);
+        if (e == hipSuccess) e = mark(1, s);
+        if (e == hipSuccess)
+            e = kda::launch_scan32((const uint16_t *)v, (const uint8_t *)ws, cu_seqlens, num_seqs, T,
+                                   H, K, V, scale, initial_state, init32, final_state, fin32,
+                                   (uint16_t *)out, s);
+    } else {
+        if (e == hipSuccess)
+            e = kda::launch_intra((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,
+                                  (const uint16_t *)beta, A_log, dt_bias, lower_bound, cu_seqlens,
+                                  num_seqs, T, H, K, slots, (uint8_t *)ws, s, scalar_gate);
+        if (e == hipSuccess) e = mark(1, s);
+        if (e == hipSuccess)
+            e = kda::launch_scan((const uint16_t *)v, (const uint8_t *)ws, cu_seqlens, num_seqs, T, H,
+                                 K, V, scale, initial_state, init32, final_state, fin32,
+                                 (uint16_t *)out, s);
+    }
+    if (e == hipSuccess) e = mark(2, s);
+    return e;
+}
+
+// kda_fwd and kda_fwd_scalar_gate: scalar_gate selects the layout of g
+// ([B, T, H, K] or [B, T, H]) and dt_bias ([H*K] or [H]).
+kda_status_t fwd_impl(const void *q, const void *k, const void *v, const void *g,
+                      const void *beta, float scale,
+                      const float *A_log, const float *dt_bias, float lower_bound,
+                      const int32_t *cu_seqlens, int32_t num_seqs,
+                      const void *initial_state, kda_dtype_t initial_state_dtype,
+                      void *final_state, kda_dtype_t final_state_dtype,
+                      void *out,
+                      int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                      void *stream, bool scalar_gate)
+{
+    kda_status_t st = fwd_validate(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound,
+                                   cu_seqlens, num_seqs, initial_state, initial_state_dtype,
+                                   final_state, final_state_dtype, out, B, T, H, K, V, scalar_gate);
+    if (st != KDA_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
     const size_t bytes = kda_workspace_size_hd(B, T, H, num_seqs, K);
     hipMemPool_t pool;
     if ((st = device_pool(&pool)) != KDA_OK) return st;
@@ -225,35 +283,11 @@ kda_status_t fwd_impl(const void *q, const void *k, const void *v, const void *g
         (void)hipGetLastError();
         return KDA_ERR_OUT_OF_MEMORY;
     }
-    hipError_t e = mark(0, s);
-    if (K <= kda::HD) {
-        if (e == hipSuccess)
-            e = kda::launch_intra32((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,
-                                    (const uint16_t *)beta, A_log, dt_bias, lower_bound, cu_seqlens,
-                                    num_seqs, T, H, K, slots, (uint8_t *)ws, s, scalar_gate);
-        if (e == hipSuccess) e = mark(1, s);
-        if (e == hipSuccess)
-            e = kda::launch_scan32((const uint16_t *)v, (const uint8_t *)ws, cu_seqlens, num_seqs, T,
-                                   H, K, V, scale, initial_state,
-                                   initial_state_dtype == KDA_DTYPE_FP32, final_state,
-                                   final_state_dtype == KDA_DTYPE_FP32, (uint16_t *)out, s);
-        if (e == hipSuccess) e = mark(2, s);
-        hipError_t ef = hipFreeAsync(ws, s);
-        if (e != hipSuccess || ef != hipSuccess) return KDA_ERR_LAUNCH;
-        return KDA_OK;
-    }
-    if (e == hipSuccess)
-        e = kda::launch_intra((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,
-                              (const uint16_t *)beta, A_log, dt_bias, lower_bound,
-                              cu_seqlens, num_seqs, T, H, K, slots, (uint8_t *)ws, s, scalar_gate);
-    if (e == hipSuccess) e = mark(1, s);
-    if (e == hipSuccess)
-        e = kda::launch_scan((const uint16_t *)v, (const uint8_t *)ws, cu_seqlens, num_seqs, T, H,
-                             K, V, scale, initial_state, initial_state_dtype == KDA_DTYPE_FP32,
-                             final_state, final_state_dtype == KDA_DTYPE_FP32,
-                             (uint16_t *)out, s);
-    if (e == hipSuccess) e = mark(2, s);
-    hipError_t ef = hipFreeAsync(ws, s);
+    const hipError_t e = fwd_launch(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound,
+                                    cu_seqlens, num_seqs, initial_state, initial_state_dtype,
+                                    final_state, final_state_dtype, out, B, T, H, K, V, s,
+                                    scalar_gate, ws);
+    const hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess || ef != hipSuccess) return KDA_ERR_LAUNCH;
     return KDA_OK;
 }
@@ -398,6 +432,70 @@ kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
     hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess || ef != hipSuccess) return KDA_ERR_LAUNCH;
     return KDA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of kda_fwd_noalloc: a file-scope device array.  Each device the
+// library runs on holds its own copy until the process ends; its address on
+// a device is read once with hipGetSymbolAddress (the array's name in host
+// code is only a stand-in) and kept per device.  The last 256 bytes hold the
+// optional cu_seqlens check's flag.
+constexpr size_t kNoallocScratchBytes = KDA_NOALLOC_WORKSPACE_BYTES + 256;
+__device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+kda_status_t scratch_on_device(void **p) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KDA_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return KDA_ERR_LAUNCH;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *p = g_scratch_ptr[dev];
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_fwd_noalloc(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, float scale,
+                             const float *A_log, const float *dt_bias, float lower_bound,
+                             const int32_t *cu_seqlens, int32_t num_seqs,
+                             const void *initial_state, kda_dtype_t initial_state_dtype,
+                             void *final_state, kda_dtype_t final_state_dtype,
+                             void *out,
+                             int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                             void *stream)
+{
+    kda_status_t st = fwd_validate(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound,
+                                   cu_seqlens, num_seqs, initial_state, initial_state_dtype,
+                                   final_state, final_state_dtype, out, B, T, H, K, V, false);
+    if (st != KDA_OK) return st;
+    if (kda_workspace_size_hd(B, T, H, num_seqs, K) > KDA_NOALLOC_WORKSPACE_BYTES)
+        return KDA_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    void *ws = nullptr;
+    if ((st = scratch_on_device(&ws)) != KDA_OK) return st;
+    if (cu_seqlens && cu_check_enabled() &&
+        (st = check_cu_flag(cu_seqlens, num_seqs, (int)((int64_t)B * T), s,
+                            (int *)((uint8_t *)ws + KDA_NOALLOC_WORKSPACE_BYTES))) != KDA_OK)
+        return st;
+    const hipError_t e = fwd_launch(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound,
+                                    cu_seqlens, num_seqs, initial_state, initial_state_dtype,
+                                    final_state, final_state_dtype, out, B, T, H, K, V, s, false,
+                                    ws);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 kda_status_t kda_set_bwd_stage_events(void *const *events) {

@@ -73,13 +73,13 @@ def test_workspace_size(lib):
     assert lib.kda_workspace_size(1, 100, 3, 1) == kda.workspace_size(1, 100, 3, 1, K=128)
 
 
-def call_fwd(lib, **over):
+def call_fwd(lib, entry="kda_fwd", **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=0.088, A_log=FAKE, dt_bias=None,
              lb=-5.0, cu=None, N=1, init=None, init_dt=0, fin=None, fin_dt=1, out=FAKE,
              B=1, T=32, H=2, K=128, V=128)
     a.update(over)
     P = lambda x: None if x is None else ctypes.c_void_p(x)
-    return lib.kda_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]), a["scale"],
+    return getattr(lib, entry)(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]), a["scale"],
                        P(a["A_log"]), P(a["dt_bias"]), a["lb"], P(a["cu"]), a["N"],
                        P(a["init"]), a["init_dt"], P(a["fin"]), a["fin_dt"], P(a["out"]),
                        a["B"], a["T"], a["H"], a["K"], a["V"], None)
@@ -109,6 +109,18 @@ def call_fwd(lib, **over):
 ])
 def test_fwd_rejects_before_any_hip_call(lib, over, code):
     assert call_fwd(lib, **over) == code
+    # the allocation-free entry point validates the same way
+    assert call_fwd(lib, entry="kda_fwd_noalloc", **over) == code
+
+
+@pytest.mark.parametrize("over", [dict(T=8192, H=96), dict(T=8192, H=10), dict(B=4, N=4, T=4096, H=5)])
+def test_noalloc_rejects_workspace_beyond_its_array(lib, over):
+    """kda_fwd_noalloc rejects, before any HIP call, calls whose workspace
+    exceeds KDA_NOALLOC_WORKSPACE_BYTES (64 MiB)."""
+    a = dict(B=1, N=1, K=128)
+    a.update(over)
+    assert kda.workspace_size(a["B"], a["T"], a["H"], a["N"]) > 64 << 20
+    assert call_fwd(lib, entry="kda_fwd_noalloc", **over) == UNSUPPORTED
 
 
 @pytest.mark.parametrize("over,code", [
