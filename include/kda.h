@@ -280,9 +280,12 @@ kda_status_t kda_trim_workspace(size_t keep_bytes);
 size_t kda_workspace_reserved(void);
 
 /*
- * Bytes of device workspace one kda_fwd call with these sizes and head
- * dimension K = V = 64 or 128 takes from the pool (the intra-chunk hand-off
- * records).  0 on invalid sizes.
+ * Bytes of device workspace one kda_fwd (or kda_fwd_scalar_gate) call with
+ * these sizes and head dimension K = V = 64 or 128 takes from the pool on
+ * the current device: the hand-off record rings and flags of the fused
+ * kernel when it applies (up to 128 (sequence, head) units at K = 128 on a
+ * 256-CU device, about 0.14 MB per unit), else one hand-off record per
+ * (chunk slot, head).  0 on invalid sizes.
  */
 size_t kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs);
 
@@ -296,12 +299,14 @@ size_t kda_workspace_size_hd(int32_t B, int32_t T, int32_t H, int32_t num_seqs, 
 /*
  * kda_debug_intra — test entry: runs only the intra-chunk stage (gate,
  * in-chunk cumulative decay, A_kk / A_qk products, triangular inverse) and
- * writes its hand-off records into the caller's `workspace` (device,
- * kda_workspace_size_hd(..., K) bytes, 16-byte aligned).  Arguments as kda_fwd.
- * Record layout (per chunk slot and head, 13312 bytes, or 26624 for K = 256)
- * is described in the library source; tests decode it to compare each stage
- * with fp64 maths.
+ * writes the hand-off record of every (chunk slot, head) into the caller's
+ * `workspace` (device, kda_record_workspace_size(B, T, H, num_seqs, K)
+ * bytes, 16-byte aligned).  Arguments as kda_fwd.  Record layout (per chunk
+ * slot and head: 27648 bytes for the 32-token chunks of K = 64 and 128,
+ * 26624 bytes for the 16-token chunks of K = 256) is described in the
+ * library source; tests decode it to compare each stage with fp64 maths.
  */
+size_t kda_record_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs, int32_t K);
 kda_status_t kda_debug_intra(const void *q, const void *k, const void *g,
                              const void *beta,
                              const float *A_log, const float *dt_bias, float lower_bound,

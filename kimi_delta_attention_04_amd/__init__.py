@@ -88,6 +88,8 @@ def load():
     lib.kda_debug_intra.argtypes = [P, P, P, P, P, P, f32, P, i32, i32, i32, i32, i32, P, P]
     lib.kda_fwd_noalloc.restype = ctypes.c_int
     lib.kda_fwd_noalloc.argtypes = lib.kda_fwd.argtypes
+    lib.kda_record_workspace_size.restype = ctypes.c_size_t
+    lib.kda_record_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.kda_trim_workspace.restype = ctypes.c_int
     lib.kda_trim_workspace.argtypes = [ctypes.c_size_t]
     lib.kda_workspace_reserved.restype = ctypes.c_size_t
@@ -366,12 +368,13 @@ def set_stage_events(before_intra=None, before_scan=None, after_scan=None):
 
 def debug_intra(q, k, g, beta, A_log, dt_bias, lower_bound, cu_seqlens=None):
     """Run only the intra-chunk stage; returns its hand-off records as a
-    uint8 device tensor of workspace_size(B, T, H, N) bytes."""
+    uint8 device tensor of kda_record_workspace_size(B, T, H, N, K) bytes."""
     import torch
     lib = load()
     B, T, H, K = q.shape
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
-    ws = torch.zeros(workspace_size(B, T, H, N, K), dtype=torch.uint8, device=q.device)
+    ws = torch.zeros(int(lib.kda_record_workspace_size(B, T, H, N, K)), dtype=torch.uint8,
+                     device=q.device)
     rc = lib.kda_debug_intra(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
                              float(lower_bound), _ptr(cu_seqlens), int(N), int(B), int(T),
                              int(H), int(K), _ptr(ws), _stream(q.device))

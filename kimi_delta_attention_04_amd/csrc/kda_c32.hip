@@ -29,6 +29,7 @@ __global__ __launch_bounds__(64, 2) void intra32_kernel(
     const int32_t *__restrict__ cu, int N, int T, int H, int K, uint8_t *__restrict__ ws)
 {
     __shared__ __attribute__((aligned(16))) Wave32Lds lds;
+    __shared__ __attribute__((aligned(16))) Khat32Lds klds;
     __shared__ __attribute__((aligned(16))) float dtb_lds[HD];
     // head fastest; slots last first (see intra_kernel)
     const int64_t slot = (int64_t)(gridDim.x / (unsigned)H) - 1 - blockIdx.x / (unsigned)H;
@@ -52,9 +53,9 @@ __global__ __launch_bounds__(64, 2) void intra32_kernel(
     Intra32Src in;
     intra32_src<SG>(in, q, k, g, beta, t0, len, H, h, K);
     if (len == C32)
-        intra32_compute<true, SG>(lds, in, A, dtb_lds, lb2, len, rec);
+        intra32_compute<true, SG>(lds, &klds, in, A, dtb_lds, lb2, len, rec);
     else
-        intra32_compute<false, SG>(lds, in, A, dtb_lds, lb2, len, rec);
+        intra32_compute<false, SG>(lds, &klds, in, A, dtb_lds, lb2, len, rec);
 }
 
 // s_waitcnt vmcnt(n) followed by a workgroup barrier (waits for this

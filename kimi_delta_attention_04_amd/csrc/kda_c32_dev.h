@@ -73,10 +73,18 @@ __device__ __forceinline__ int64_t seq_slot0_32(const int32_t *cu, int n, int T)
 struct Wave32Lds {
     float beta[C32];
     float gam[HD];
-    // Khat of sub-block b, state row tile t, as (hi, lo) B operands of the
-    // W products: [b][t][hi/lo][lane]
+};
+// Khat of sub-block b, state row tile t, as (hi, lo) B operands of the W
+// products, [b][t][hi/lo][lane], held between the channel-block loop and
+// the W products.
+struct Khat32Lds {
     u32x2_t khat[2][8][2][64];
 };
+// The same in global memory, inside the record being written: the hi parts
+// of tiles (b, t) at index 2t + b of the WT area (W tile t later overwrites
+// exactly the two pieces it is computed from), the lo parts at the same
+// offsets past the record's end (KHAT_LO bytes more per record slot).
+constexpr int KHAT_LO = 8192;
 
 // Token-per-lane inputs of one 32-token chunk: lane l holds tokens l%16
 // (sub-block 0) and 16 + l%16 (sub-block 1), eight channels 32kb + 8(l/16) + i
@@ -191,10 +199,14 @@ __device__ __forceinline__ f32x4_t mfma3_k16(u32x2_t ah, u32x2_t al, u32x2_t bh,
 // form's on broadcast inputs bit for bit.  `rec`: the record (global
 // memory, or any address space the stores reach).  NT: non-temporal record
 // stores.
-template <bool FULL, bool SG, bool NT = true>
-__device__ __forceinline__ void intra32_compute(Wave32Lds &L, const Intra32Src &in, float A,
-                                                const float *__restrict__ dtb_lds, float lb2, int len,
-                                                uint8_t *__restrict__ rec) {
+// GSTAGE: Khat staged inside the record (global memory, see KHAT_LO),
+// else in KL (LDS).  The record's stores are non-temporal when NT.
+// PREFETCH: read the next channel block's inputs while computing this one
+// (more registers, fewer exposed load latencies).
+template <bool FULL, bool SG, bool NT = true, bool GSTAGE = false, bool PREFETCH = true>
+__device__ __forceinline__ void intra32_compute(Wave32Lds &L, Khat32Lds *KL, const Intra32Src &in,
+                                                float A, const float *__restrict__ dtb_lds, float lb2,
+                                                int len, uint8_t *__restrict__ rec) {
     typedef Rec32 R;
     const int l = threadIdx.x & 63;
     const int tok = l & 15, grp = l >> 4, cg = tok;
@@ -226,6 +238,29 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, const Intra32Src &
     f32x4_t A00 = zero, A00t = zero, A11 = zero, A11t = zero, A10 = zero;
     f32x4_t Q00t = zero, Q11t = zero, Q10t = zero;
 
+    // Khat of sub-block b, channel block kb (token-per-lane hi / lo words)
+    // into the B layout of the W products through the identity (exact for
+    // bf16 values), staged until the W products
+    auto stage_khat = [&](int b, int kb, const u32x4_t &kht, const u32x4_t &klt) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const u32x2_t ah = {kht[2 * h], kht[2 * h + 1]};
+            const u32x2_t al = {klt[2 * h], klt[2 * h + 1]};
+            const f32x4_t dh = mfma_k16(ah, eye, zero);
+            const f32x4_t dl = mfma_k16(al, eye, zero);
+            const u32x2_t ph = {pack2(dh[0], dh[1]), pack2(dh[2], dh[3])};
+            const u32x2_t pl = {pack2(dl[0], dl[1]), pack2(dl[2], dl[3])};
+            const int t = 2 * kb + h;
+            if (GSTAGE) {
+                *(u32x2_t *)(rec + R::WT + ((2 * t + b) * 64 + l) * 8) = ph;
+                *(u32x2_t *)(rec + R::BYTES + ((2 * t + b) * 64 + l) * 8) = pl;
+            } else {
+                KL->khat[b][t][0][l] = ph;
+                KL->khat[b][t][1][l] = pl;
+            }
+        }
+    };
+
     float gsc[2] = {0.f, 0.f};         // SG form: the cumulative gate of each sub-block
     if (SG && A > 0.f) {
 #pragma unroll
@@ -242,11 +277,16 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, const Intra32Src &
         }
     }
     Intra32Blk nxt;
-    intra32_read<SG>(nxt, in, 0);
+    if (PREFETCH) intra32_read<SG>(nxt, in, 0);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        const Intra32Blk cur = nxt;
-        if (kb + 1 < 4) intra32_read<SG>(nxt, in, kb + 1);
+        Intra32Blk cur;
+        if (PREFETCH) {
+            cur = nxt;
+            if (kb + 1 < 4) intra32_read<SG>(nxt, in, kb + 1);
+        } else {
+            intra32_read<SG>(cur, in, kb);
+        }
         float gl[2][8];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -271,105 +311,106 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, const Intra32Src &
             }
         }
         // per channel: F = 2^{g}, Bv = 2^{-g}, eg = 2^{Gam} (F at the
-        // sub-block's last row), e = 2^{Gam - g}
-        u32x4_t kf[2], kbh[2], kbl[2], qfh[2], qfl[2], ke0h, ke0l, kt1, qt1, kht[2], klt[2];
-        float egam[2][8];
+        // sub-block's last row), e = 2^{Gam - g}.  Sub-block 1 first, its
+        // products issued before sub-block 0's operands exist, so that only
+        // its Kt / Qt pieces stay live for the off-diagonal block.
+        float F0[8], eg0[8], eg1[8];
 #pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-            float F[2][2], Bv[2][2], eg[2][2];
+        for (int i = 0; i < 8; ++i) {
+            F0[i] = fast_exp2(gl[0][i]);
+            eg0[i] = row_last(F0[i]);
+        }
+        u32x4_t kf1, qfh1, qfl1;
+        {
+            u32x4_t kbh1, kbl1, kt1, qt1, kht1, klt1;
 #pragma unroll
-            for (int e = 0; e < 2; ++e)
+            for (int wd = 0; wd < 4; ++wd) {
+                float kF[2], qF[2], kB[2], kt[2], qt[2], kh[2];
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
+                for (int e = 0; e < 2; ++e) {
                     const int i = 2 * wd + e;
-                    F[b][e] = fast_exp2(gl[b][i]);
-                    Bv[b][e] = fast_exp2(-gl[b][i]);
-                    eg[b][e] = row_last(F[b][e]);
-                    egam[b][i] = eg[b][e];
+                    const float F = fast_exp2(gl[1][i]);
+                    const float Bv = fast_exp2(-gl[1][i]);
+                    eg1[i] = row_last(F);
+                    const float kv = elem(cur.k[1], i), qv = elem(cur.q[1], i);
+                    kF[e] = kv * F;
+                    qF[e] = qv * F;
+                    kB[e] = kv * Bv;
+                    kt[e] = kF[e] * eg0[i];              // chunk-level Kt, Qt of sub-block 1
+                    qt[e] = qF[e] * eg0[i];
+                    kh[e] = kv * (Bv * eg1[i]);          // k 2^{G_last - G} = k 2^{Gam_1 - g^1}
                 }
-            float kF[2][2], qF[2][2], kB[2][2], ke0[2], kt1f[2], qt1f[2], khat[2][2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int i = 2 * wd + e;
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    const float kv = elem(cur.k[b], i), qv = elem(cur.q[b], i);
-                    kF[b][e] = kv * F[b][e];
-                    qF[b][e] = qv * F[b][e];
-                    kB[b][e] = kv * Bv[b][e];
-                }
-                const float e0 = Bv[0][e] * eg[0][e];            // 2^{Gam_0 - g^0}
-                const float e1 = Bv[1][e] * eg[1][e];            // 2^{Gam_1 - g^1}
-                ke0[e] = elem(cur.k[0], i) * e0;
-                kt1f[e] = kF[1][e] * eg[0][e];                   // chunk-level Kt, Qt of sub-block 1
-                qt1f[e] = qF[1][e] * eg[0][e];
-                khat[0][e] = ke0[e] * eg[1][e];                  // k 2^{G_last - G}
-                khat[1][e] = elem(cur.k[1], i) * e1;
-            }
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                kf[b][wd] = pack2(kF[b][0], kF[b][1]);
                 uint32_t h, lo;
-                split2(kB[b][0], kB[b][1], h, lo); kbh[b][wd] = h; kbl[b][wd] = lo;
-                split2(qF[b][0], qF[b][1], h, lo); qfh[b][wd] = h; qfl[b][wd] = lo;
-                split2(khat[b][0], khat[b][1], h, lo); kht[b][wd] = h; klt[b][wd] = lo;
+                kf1[wd] = pack2(kF[0], kF[1]);
+                split2(kB[0], kB[1], h, lo); kbh1[wd] = h; kbl1[wd] = lo;
+                split2(qF[0], qF[1], h, lo); qfh1[wd] = h; qfl1[wd] = lo;
+                split2(kh[0], kh[1], h, lo); kht1[wd] = h; klt1[wd] = lo;
+                kt1[wd] = pack2(kt[0], kt[1]);
+                qt1[wd] = pack2(qt[0], qt[1]);
             }
-            uint32_t h, lo;
-            split2(ke0[0], ke0[1], h, lo); ke0h[wd] = h; ke0l[wd] = lo;
-            kt1[wd] = pack2(kt1f[0], kt1f[1]);
-            qt1[wd] = pack2(qt1f[0], qt1f[1]);
+            st16(kt1, R::KT + ((kb * 2 + 1) * 64 + l) * 16);
+            st16(qt1, R::QT + ((kb * 2 + 1) * 64 + l) * 16);
+            A11 = mfma_k32(kf1, kbh1, A11);
+            A11t = mfma_k32(kbh1, kf1, A11t);
+            Q11t = mfma_k32(kbh1, qfh1, Q11t);
+            Q11t = mfma_k32(kbh1, qfl1, Q11t);
+            Q11t = mfma_k32(kbl1, qfh1, Q11t);
+            stage_khat(1, kb, kht1, klt1);
+        }
+        {
+            u32x4_t kf0, kbh0, kbl0, qfh0, qfl0, ke0h, ke0l, kht0, klt0;
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd) {
+                float kF[2], qF[2], kB[2], ke[2], kh[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int i = 2 * wd + e;
+                    const float Bv = fast_exp2(-gl[0][i]);
+                    const float kv = elem(cur.k[0], i), qv = elem(cur.q[0], i);
+                    kF[e] = kv * F0[i];
+                    qF[e] = qv * F0[i];
+                    kB[e] = kv * Bv;
+                    ke[e] = kv * (Bv * eg0[i]);          // k 2^{Gam_0 - g^0}
+                    kh[e] = ke[e] * eg1[i];              // k 2^{G_last - G}
+                }
+                uint32_t h, lo;
+                kf0[wd] = pack2(kF[0], kF[1]);
+                split2(kB[0], kB[1], h, lo); kbh0[wd] = h; kbl0[wd] = lo;
+                split2(qF[0], qF[1], h, lo); qfh0[wd] = h; qfl0[wd] = lo;
+                split2(ke[0], ke[1], h, lo); ke0h[wd] = h; ke0l[wd] = lo;
+                split2(kh[0], kh[1], h, lo); kht0[wd] = h; klt0[wd] = lo;
+            }
+            // sub-block 0: the local factors are the chunk-level ones (Qt's
+            // record is its hi part)
+            st16(kf0, R::KT + ((kb * 2 + 0) * 64 + l) * 16);
+            st16(qfh0, R::QT + ((kb * 2 + 0) * 64 + l) * 16);
+            A00 = mfma_k32(kf0, kbh0, A00);
+            A00t = mfma_k32(kbh0, kf0, A00t);
+            A10 = mfma_k32(kf1, ke0h, A10);
+            Q00t = mfma_k32(kbh0, qfh0, Q00t);
+            Q00t = mfma_k32(kbh0, qfl0, Q00t);
+            Q00t = mfma_k32(kbl0, qfh0, Q00t);
+            Q10t = mfma_k32(ke0h, qfh1, Q10t);
+            Q10t = mfma_k32(ke0h, qfl1, Q10t);
+            Q10t = mfma_k32(ke0l, qfh1, Q10t);
+            stage_khat(0, kb, kht0, klt0);
         }
         // chunk decay per channel: 2^{Gam_0 + Gam_1}
         if (tok == 15) {
             f32x4_t g0, g1;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                g0[i] = egam[0][i] * egam[1][i];
-                g1[i] = egam[0][4 + i] * egam[1][4 + i];
+                g0[i] = eg0[i] * eg1[i];
+                g1[i] = eg0[4 + i] * eg1[4 + i];
             }
             const int ch = 32 * kb + 8 * grp;
             *(f32x4_t *)&L.gam[ch] = g0;
             *(f32x4_t *)&L.gam[ch + 4] = g1;
         }
-        // records: Kt, Qt of both sub-blocks (sub-block 0: the local factors
-        // are the chunk-level ones; Qt's record is its hi part)
-        st16(kf[0], R::KT + ((kb * 2 + 0) * 64 + l) * 16);
-        st16(kt1, R::KT + ((kb * 2 + 1) * 64 + l) * 16);
-        st16(qfh[0], R::QT + ((kb * 2 + 0) * 64 + l) * 16);
-        st16(qt1, R::QT + ((kb * 2 + 1) * 64 + l) * 16);
-        // Gram blocks
-        A00 = mfma_k32(kf[0], kbh[0], A00);
-        A00t = mfma_k32(kbh[0], kf[0], A00t);
-        A11 = mfma_k32(kf[1], kbh[1], A11);
-        A11t = mfma_k32(kbh[1], kf[1], A11t);
-        A10 = mfma_k32(kf[1], ke0h, A10);
-        Q00t = mfma_k32(kbh[0], qfh[0], Q00t);
-        Q00t = mfma_k32(kbh[0], qfl[0], Q00t);
-        Q00t = mfma_k32(kbl[0], qfh[0], Q00t);
-        Q11t = mfma_k32(kbh[1], qfh[1], Q11t);
-        Q11t = mfma_k32(kbh[1], qfl[1], Q11t);
-        Q11t = mfma_k32(kbl[1], qfh[1], Q11t);
-        Q10t = mfma_k32(ke0h, qfh[1], Q10t);
-        Q10t = mfma_k32(ke0h, qfl[1], Q10t);
-        Q10t = mfma_k32(ke0l, qfh[1], Q10t);
-        // Khat into the B layout of the W products (transpose through the
-        // identity: exact for bf16 values)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const u32x2_t ah = {kht[b][2 * h], kht[b][2 * h + 1]};
-                const u32x2_t al = {klt[b][2 * h], klt[b][2 * h + 1]};
-                const f32x4_t dh = mfma_k16(ah, eye, zero);
-                const f32x4_t dl = mfma_k16(al, eye, zero);
-                L.khat[b][2 * kb + h][0][l] = {pack2(dh[0], dh[1]), pack2(dh[2], dh[3])};
-                L.khat[b][2 * kb + h][1][l] = {pack2(dl[0], dl[1]), pack2(dl[2], dl[3])};
-            }
     }
 
     wave_lds_sync();
-#pragma unroll
-    for (int p = 0; p < 1; ++p) {
+    {
         const u32x2_t gw = *(const u32x2_t *)&L.gam[2 * l];
         if (NT) __builtin_nontemporal_store(gw, (u32x2_t *)(rec + R::GAM + l * 8));
         else *(u32x2_t *)(rec + R::GAM + l * 8) = gw;
@@ -428,10 +469,28 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, const Intra32Src &
     }
 
     // ---- W tiles: W = Tb^T Khat ---------------------------------------------
+    // The staged Khat is read back once its stores have completed.  The
+    // record slot is reused and the vector L1 may hold its older contents
+    // (stores do not refresh lines another wave's reads left there):
+    // invalidate the L1, then read from L2.
+    __amdgpu_buffer_rsrc_t rk;
+    if (GSTAGE) {
+        asm volatile("s_waitcnt vmcnt(0)\n\tbuffer_inv sc0" ::: "memory");
+        rk = make_rsrc(rec, (uint32_t)(R::BYTES + KHAT_LO));
+    }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const u32x2_t k0h = L.khat[0][t][0][l], k0l = L.khat[0][t][1][l];
-        const u32x2_t k1h = L.khat[1][t][0][l], k1l = L.khat[1][t][1][l];
+        u32x2_t k0h, k0l, k1h, k1l;
+        if (GSTAGE) {
+            const int o0 = ((2 * t) * 64 + l) * 8, o1 = ((2 * t + 1) * 64 + l) * 8;
+            k0h = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rk, R::WT + o0, 0, 1));
+            k1h = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rk, R::WT + o1, 0, 1));
+            k0l = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rk, R::BYTES + o0, 0, 1));
+            k1l = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rk, R::BYTES + o1, 0, 1));
+        } else {
+            k0h = KL->khat[0][t][0][l]; k0l = KL->khat[0][t][1][l];
+            k1h = KL->khat[1][t][0][l]; k1l = KL->khat[1][t][1][l];
+        }
         f32x4_t w0 = mfma3_k16(tb00h, tb00l, k0h, k0l, zero);
         w0 = mfma3_k16(tb10h, tb10l, k1h, k1l, w0);
         const f32x4_t w1 = mfma3_k16(tb11h, tb11l, k1h, k1l, zero);

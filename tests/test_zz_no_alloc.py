@@ -34,7 +34,7 @@ def test_noalloc_matches_fwd_twice_second_smaller():
     kda.load()
     cases = [
         kda_inputs.random_small(1301, B=1, T=1000, H=16, initial_state=True),
-        kda_inputs.random_small(1302, B=1, T=300, H=4, seq_lens=(0, 33, 1, 200, 66),
+        kda_inputs.random_small(1302, B=1, T=300, H=2, seq_lens=(0, 33, 1, 200, 66),
                                 initial_state=True),
     ]
     sizes = []
@@ -55,13 +55,16 @@ def test_noalloc_matches_fwd_twice_second_smaller():
 
 
 def test_noalloc_rejects_workspace_beyond_the_array():
+    """8 sequences x 96 heads (768 (sequence, head) units) take the
+    two-kernel path, whose records exceed the array."""
     kda.load()
     T, H = 8192, 96
-    assert kda.workspace_size(1, T, H, 1) > kda.NOALLOC_WORKSPACE_BYTES
-    inp = kda_inputs.random_small(1303, B=1, T=T, H=H)
+    lens = (1024,) * 8
+    assert kda.workspace_size(1, T, H, len(lens)) > kda.NOALLOC_WORKSPACE_BYTES
+    inp = kda_inputs.random_small(1303, B=1, T=T, H=H, seq_lens=lens)
     d = to_device(inp)
     out = torch.empty_like(d["v"])
     with pytest.raises(kda.KDAError) as err:
         kda.fwd_noalloc(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], out, d["A_log"],
-                        d["dt_bias"], d["lower_bound"])
+                        d["dt_bias"], d["lower_bound"], cu_seqlens=d["cu_seqlens"])
     assert err.value.status == 2            # KDA_ERR_UNSUPPORTED
