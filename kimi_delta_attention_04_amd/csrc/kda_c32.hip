@@ -376,10 +376,10 @@ hipError_t launch_intra32(const uint16_t *q, const uint16_t *k, const uint16_t *
     dim3 grid((unsigned)(num_slots * H));
     const float lb2 = lower_bound * LOG2E;
     if (scalar_gate)
-        hipLaunchKernelGGL((intra_team_kernel<true>), grid, dim3(256), 0, stream, q, k, g, beta, A_log,
+        hipLaunchKernelGGL((intra32_kernel<true>), grid, dim3(64), 0, stream, q, k, g, beta, A_log,
                            dt_bias, lb2, cu, N, T, H, K, ws);
     else
-        hipLaunchKernelGGL((intra_team_kernel<false>), grid, dim3(256), 0, stream, q, k, g, beta, A_log,
+        hipLaunchKernelGGL((intra32_kernel<false>), grid, dim3(64), 0, stream, q, k, g, beta, A_log,
                            dt_bias, lb2, cu, N, T, H, K, ws);
     return hipGetLastError();
 }

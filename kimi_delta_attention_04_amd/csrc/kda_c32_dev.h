@@ -74,17 +74,13 @@ struct Wave32Lds {
     float beta[C32];
     float gam[HD];
 };
-// Khat of sub-block b, state row tile t, as (hi, lo) B operands of the W
-// products, [b][t][hi/lo][lane], held between the channel-block loop and
-// the W products.
+// Khat of sub-block b, state row tile t, as bf16 B operands of the W
+// products, [b][t][lane], held between the channel-block loop and the W
+// products.  W is stored in bf16 and Khat enters it through one product, so
+// Khat's own bf16 rounding adds no more than the record's.
 struct Khat32Lds {
-    u32x2_t khat[2][8][2][64];
+    u32x2_t khat[2][8][64];
 };
-// The same in global memory, inside the record being written: the hi parts
-// of tiles (b, t) at index 2t + b of the WT area (W tile t later overwrites
-// exactly the two pieces it is computed from), the lo parts at the same
-// offsets past the record's end (KHAT_LO bytes more per record slot).
-constexpr int KHAT_LO = 8192;
 
 // Token-per-lane inputs of one 32-token chunk: lane l holds tokens l%16
 // (sub-block 0) and 16 + l%16 (sub-block 1), eight channels 32kb + 8(l/16) + i
@@ -199,11 +195,9 @@ __device__ __forceinline__ f32x4_t mfma3_k16(u32x2_t ah, u32x2_t al, u32x2_t bh,
 // form's on broadcast inputs bit for bit.  `rec`: the record (global
 // memory, or any address space the stores reach).  NT: non-temporal record
 // stores.
-// GSTAGE: Khat staged inside the record (global memory, see KHAT_LO),
-// else in KL (LDS).  The record's stores are non-temporal when NT.
 // PREFETCH: read the next channel block's inputs while computing this one
 // (more registers, fewer exposed load latencies).
-template <bool FULL, bool SG, bool NT = true, bool GSTAGE = false, bool PREFETCH = true>
+template <bool FULL, bool SG, bool NT = true, bool PREFETCH = true>
 __device__ __forceinline__ void intra32_compute(Wave32Lds &L, Khat32Lds *KL, const Intra32Src &in,
                                                 float A, const float *__restrict__ dtb_lds, float lb2,
                                                 int len, uint8_t *__restrict__ rec) {
@@ -238,26 +232,15 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, Khat32Lds *KL, con
     f32x4_t A00 = zero, A00t = zero, A11 = zero, A11t = zero, A10 = zero;
     f32x4_t Q00t = zero, Q11t = zero, Q10t = zero;
 
-    // Khat of sub-block b, channel block kb (token-per-lane hi / lo words)
-    // into the B layout of the W products through the identity (exact for
-    // bf16 values), staged until the W products
-    auto stage_khat = [&](int b, int kb, const u32x4_t &kht, const u32x4_t &klt) {
+    // Khat of sub-block b, channel block kb (token-per-lane words) into the
+    // B layout of the W products through the identity (exact for bf16
+    // values), staged in LDS until the W products
+    auto stage_khat = [&](int b, int kb, const u32x4_t &kht) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const u32x2_t ah = {kht[2 * h], kht[2 * h + 1]};
-            const u32x2_t al = {klt[2 * h], klt[2 * h + 1]};
             const f32x4_t dh = mfma_k16(ah, eye, zero);
-            const f32x4_t dl = mfma_k16(al, eye, zero);
-            const u32x2_t ph = {pack2(dh[0], dh[1]), pack2(dh[2], dh[3])};
-            const u32x2_t pl = {pack2(dl[0], dl[1]), pack2(dl[2], dl[3])};
-            const int t = 2 * kb + h;
-            if (GSTAGE) {
-                *(u32x2_t *)(rec + R::WT + ((2 * t + b) * 64 + l) * 8) = ph;
-                *(u32x2_t *)(rec + R::BYTES + ((2 * t + b) * 64 + l) * 8) = pl;
-            } else {
-                KL->khat[b][t][0][l] = ph;
-                KL->khat[b][t][1][l] = pl;
-            }
+            KL->khat[b][2 * kb + h][l] = {pack2(dh[0], dh[1]), pack2(dh[2], dh[3])};
         }
     };
 
@@ -322,7 +305,7 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, Khat32Lds *KL, con
         }
         u32x4_t kf1, qfh1, qfl1;
         {
-            u32x4_t kbh1, kbl1, kt1, qt1, kht1, klt1;
+            u32x4_t kbh1, kbl1, kt1, qt1, kht1;
 #pragma unroll
             for (int wd = 0; wd < 4; ++wd) {
                 float kF[2], qF[2], kB[2], kt[2], qt[2], kh[2];
@@ -344,7 +327,7 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, Khat32Lds *KL, con
                 kf1[wd] = pack2(kF[0], kF[1]);
                 split2(kB[0], kB[1], h, lo); kbh1[wd] = h; kbl1[wd] = lo;
                 split2(qF[0], qF[1], h, lo); qfh1[wd] = h; qfl1[wd] = lo;
-                split2(kh[0], kh[1], h, lo); kht1[wd] = h; klt1[wd] = lo;
+                kht1[wd] = pack2(kh[0], kh[1]);
                 kt1[wd] = pack2(kt[0], kt[1]);
                 qt1[wd] = pack2(qt[0], qt[1]);
             }
@@ -355,10 +338,10 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, Khat32Lds *KL, con
             Q11t = mfma_k32(kbh1, qfh1, Q11t);
             Q11t = mfma_k32(kbh1, qfl1, Q11t);
             Q11t = mfma_k32(kbl1, qfh1, Q11t);
-            stage_khat(1, kb, kht1, klt1);
+            stage_khat(1, kb, kht1);
         }
         {
-            u32x4_t kf0, kbh0, kbl0, qfh0, qfl0, ke0h, ke0l, kht0, klt0;
+            u32x4_t kf0, kbh0, kbl0, qfh0, qfl0, ke0h, ke0l, kht0;
 #pragma unroll
             for (int wd = 0; wd < 4; ++wd) {
                 float kF[2], qF[2], kB[2], ke[2], kh[2];
@@ -378,7 +361,7 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, Khat32Lds *KL, con
                 split2(kB[0], kB[1], h, lo); kbh0[wd] = h; kbl0[wd] = lo;
                 split2(qF[0], qF[1], h, lo); qfh0[wd] = h; qfl0[wd] = lo;
                 split2(ke[0], ke[1], h, lo); ke0h[wd] = h; ke0l[wd] = lo;
-                split2(kh[0], kh[1], h, lo); kht0[wd] = h; klt0[wd] = lo;
+                kht0[wd] = pack2(kh[0], kh[1]);
             }
             // sub-block 0: the local factors are the chunk-level ones (Qt's
             // record is its hi part)
@@ -393,7 +376,7 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, Khat32Lds *KL, con
             Q10t = mfma_k32(ke0h, qfh1, Q10t);
             Q10t = mfma_k32(ke0h, qfl1, Q10t);
             Q10t = mfma_k32(ke0l, qfh1, Q10t);
-            stage_khat(0, kb, kht0, klt0);
+            stage_khat(0, kb, kht0);
         }
         // chunk decay per channel: 2^{Gam_0 + Gam_1}
         if (tok == 15) {
@@ -469,31 +452,15 @@ __device__ __forceinline__ void intra32_compute(Wave32Lds &L, Khat32Lds *KL, con
     }
 
     // ---- W tiles: W = Tb^T Khat ---------------------------------------------
-    // The staged Khat is read back once its stores have completed.  The
-    // record slot is reused and the vector L1 may hold its older contents
-    // (stores do not refresh lines another wave's reads left there):
-    // invalidate the L1, then read from L2.
-    __amdgpu_buffer_rsrc_t rk;
-    if (GSTAGE) {
-        asm volatile("s_waitcnt vmcnt(0)\n\tbuffer_inv sc0" ::: "memory");
-        rk = make_rsrc(rec, (uint32_t)(R::BYTES + KHAT_LO));
-    }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        u32x2_t k0h, k0l, k1h, k1l;
-        if (GSTAGE) {
-            const int o0 = ((2 * t) * 64 + l) * 8, o1 = ((2 * t + 1) * 64 + l) * 8;
-            k0h = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rk, R::WT + o0, 0, 1));
-            k1h = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rk, R::WT + o1, 0, 1));
-            k0l = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rk, R::BYTES + o0, 0, 1));
-            k1l = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rk, R::BYTES + o1, 0, 1));
-        } else {
-            k0h = KL->khat[0][t][0][l]; k0l = KL->khat[0][t][1][l];
-            k1h = KL->khat[1][t][0][l]; k1l = KL->khat[1][t][1][l];
-        }
-        f32x4_t w0 = mfma3_k16(tb00h, tb00l, k0h, k0l, zero);
-        w0 = mfma3_k16(tb10h, tb10l, k1h, k1l, w0);
-        const f32x4_t w1 = mfma3_k16(tb11h, tb11l, k1h, k1l, zero);
+        const u32x2_t k0 = KL->khat[0][t][l], k1 = KL->khat[1][t][l];
+        f32x4_t w0 = mfma_k16(tb00h, k0, zero);
+        w0 = mfma_k16(tb00l, k0, w0);
+        w0 = mfma_k16(tb10h, k1, w0);
+        w0 = mfma_k16(tb10l, k1, w0);
+        f32x4_t w1 = mfma_k16(tb11h, k1, zero);
+        w1 = mfma_k16(tb11l, k1, w1);
         const u32x4_t o = {pack2(w0[0], w0[1]), pack2(w0[2], w0[3]), pack2(w1[0], w1[1]),
                            pack2(w1[2], w1[3])};
         st16(o, R::WT + (t * 64 + l) * 16);

@@ -41,6 +41,7 @@
 
 #include "kda_c32_dev.h"
 #include "kda_launch.h"
+#include "kda_team_dev.h"
 
 namespace kda {
 
@@ -49,13 +50,13 @@ namespace {
 constexpr int FW_SCAN = 4;                 // scan waves (16 columns each)
 constexpr int FW_LOADER = 4;               // record DMA wave
 constexpr int FW_POLLER = 5;               // global <-> LDS flag wave
-constexpr int FW_INTRA0 = 6;               // first intra wave
-constexpr int FW_WAVES = 12;
-constexpr int FW_NI = FW_WAVES - FW_INTRA0;
+constexpr int FW_INTRA0 = 6;               // first wave of the intra teams
+constexpr int FW_TEAMS = 2;                // teams of four waves
+constexpr int FW_WAVES = FW_INTRA0 + 4 * FW_TEAMS;
 constexpr int PART_CW = 64;                // columns per scan part
-constexpr int RG = 4;                      // record slots per unit in the L2 ring
-constexpr int RL = 4;                      // LDS ring slots
-constexpr int SLOT_BYTES = Rec32::BYTES + KHAT_LO;
+constexpr int RG = 8;                      // record slots per unit in the L2 ring
+constexpr int RL = 3;                      // LDS ring slots
+constexpr int SLOT_BYTES = Rec32::BYTES;
 constexpr int REC_UNITS = Rec32::BYTES / 1024;   // 1 KB DMAs per record
 constexpr int NFLAGS = RG + 2;             // per unit: ready[RG], consumed[2]
 // Bounds of the waits: global flag polls take a memory round trip (about a
@@ -85,8 +86,7 @@ struct alignas(16) FusedLds {
     int lfree[RL];                         // scan-wave releases per slot (four per use)
     int gready;                            // chunks whose records are ready in the L2 ring
     int lcons;                             // chunks copied into the LDS ring
-    Wave32Lds iw[FW_NI];
-    float dtb[FW_NI][HD];
+    TeamLds team[FW_TEAMS];
 };
 
 __device__ __forceinline__ uint32_t flag_load(const uint32_t *p) {
@@ -183,6 +183,7 @@ __global__ __launch_bounds__(64 * FW_WAVES, 1) void fused_kernel(FusedArgs a)
     uint32_t *err = a.flags + (size_t)NH * NFLAGS;
 
     if (threadIdx.x < RL) { L.lready[threadIdx.x] = 0; L.lfree[threadIdx.x] = 0; }
+    if (threadIdx.x < 64 * FW_TEAMS && (threadIdx.x & 63) == 0) team_init(L.team[threadIdx.x >> 6]);
     if (threadIdx.x == 0) {
         L.gready = 0;
         L.lcons = 0;
@@ -193,13 +194,16 @@ __global__ __launch_bounds__(64 * FW_WAVES, 1) void fused_kernel(FusedArgs a)
     }
     __syncthreads();                                   // the only workgroup barrier
 
-    // ---- intra waves: records of the XCD's units, chunk-major -------------
+    // ---- intra teams: records of the XCD's units, chunk-major --------------
     if (w >= FW_INTRA0) {
-        const int iw = w - FW_INTRA0;
-        const int W = Q * FW_NI;                       // intra waves on the XCD
+        const int tw = w - FW_INTRA0;
+        const int tm = tw >> 2, kb = tw & 3;           // team, its channel block
+        TeamLds &T = L.team[tm];
+        const int NT = Q * FW_TEAMS;                   // teams on the XCD
         const int64_t items = (int64_t)Ux * a.nchmax;
         bool ok = true;                                // false once a wait ran out: no more waits
-        for (int64_t kk = (int64_t)wi * FW_NI + iw; kk < items; kk += W) {
+        int done = 0;                                  // chunks this team has made
+        for (int64_t kk = (int64_t)wi * FW_TEAMS + tm; kk < items; kk += NT) {
             const int j = (int)(kk / Ux);
             const int m = (int)(kk - (int64_t)j * Ux);
             const int u = x + 8 * m;
@@ -207,35 +211,34 @@ __global__ __launch_bounds__(64 * FW_WAVES, 1) void fused_kernel(FusedArgs a)
             int64_t start, end;
             seq_range(a.cu, n, a.T, start, end);
             const int64_t t0 = start + (int64_t)j * C32;
-            if (t0 >= end) continue;                   // past this sequence's end
+            if (t0 >= end) continue;                   // past this sequence's end (uniform in the team)
             const int len = (int)min((int64_t)C32, end - t0);
             uint32_t *fl = a.flags + (size_t)u * NFLAGS;
             const int gs = j % RG;
             if (ok && j >= RG) {                       // the slot's previous record copied by every part
-                bool done = false;
-                for (uint32_t p = 0; p < MAX_GPOLLS && !done; ++p) {
-                    done = true;
+                bool free_ = false;
+                for (uint32_t p = 0; p < MAX_GPOLLS && !free_; ++p) {
+                    const uint32_t c = (l < PP) ? flag_load(fl + RG + l) : 0xffffffffu;
+                    uint32_t cmin = c;
 #pragma unroll
-                    for (int pp = 0; pp < PP; ++pp) done = done && flag_load(fl + RG + pp) >= (uint32_t)(j - RG + 1);
-                    if (!done) __builtin_amdgcn_s_sleep(2);
+                    for (int pp = 0; pp < PP; ++pp) cmin = min(cmin, (uint32_t)__builtin_amdgcn_readlane((int)c, pp));
+                    free_ = cmin >= (uint32_t)(j - RG + 1);
+                    if (!free_) __builtin_amdgcn_s_sleep(2);
                 }
-                if (!done) { ok = false; flag_store(err, 1u); }
+                if (!free_) { ok = false; flag_store(err, 1u); }
             }
             uint8_t *rec = a.ring + ((size_t)u * RG + gs) * SLOT_BYTES;
             const float A = expf(a.A_log[h]);
-            stage_dtb<SG, HD>(L.dtb[iw], a.dt_bias, h, a.K);
-            wave_lds_sync();
-            Intra32Src in;
-            intra32_src<SG>(in, a.q, a.k, a.g, a.beta, t0, len, a.H, h, a.K);
-            // one instantiation (rows past len masked) keeps the register
-            // budget of the 12-wave workgroup
-            intra32_compute<false, SG, false, true, false>(L.iw[iw], nullptr, in, A, L.dtb[iw], a.lb2, len, rec);
-            // every store of the record acknowledged by L2 (and none moved
-            // past this point by the compiler) before the ready flag
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-            flag_store(fl + gs, (uint32_t)(j + 1));
-            wave_lds_sync();                           // LDS scratch reads done before reuse
+            ok = team_chunk<SG, false>(T, kb, done, a.q, a.k, a.g, a.beta, a.dt_bias, A, a.lb2, t0, len,
+                                       a.H, h, a.K, rec) && ok;
+            ++done;
+            if (kb == 0) {
+                // every wave's stores of the record acknowledged by L2
+                ok = ok && team_wait(&T.p3, 4 * done);
+                flag_store(fl + gs, (uint32_t)(j + 1));
+            }
         }
+        if (!ok) flag_store(err, 1u);
         return;
     }
 
@@ -252,10 +255,16 @@ __global__ __launch_bounds__(64 * FW_WAVES, 1) void fused_kernel(FusedArgs a)
     const uint8_t *ring_u = a.ring + (size_t)u * RG * SLOT_BYTES;
 
     if (w == FW_POLLER) {
-        // ready flags of the unit's ring -> L.gready; L.lcons -> consumed flag
+        // ready flags of the unit's ring (all RG in one load) -> L.gready;
+        // L.lcons -> this part's consumed flag
         int ready = 0, published = 0;
         for (uint32_t p = 0; p < MAX_GPOLLS; ++p) {
-            while (ready < nch && flag_load(fl + ready % RG) >= (uint32_t)(ready + 1)) ++ready;
+            const uint32_t f = (l < RG) ? flag_load(fl + l) : 0u;
+#pragma unroll
+            for (int step = 0; step < RG; ++step) {
+                const uint32_t fs = (uint32_t)__builtin_amdgcn_readlane((int)f, ready % RG);
+                if (ready < nch && fs >= (uint32_t)(ready + 1)) ++ready;
+            }
             lds_store(&L.gready, ready);
             const int c = lds_load(&L.lcons);
             if (c > published) { flag_store(fl + RG + part, (uint32_t)c); published = c; }

@@ -54,7 +54,7 @@ __device__ __forceinline__ void team_init(TeamLds &T) {
 // this one (the phase counters' targets).  dt_bias: per (head, channel),
 // or [H] in the SG form.  Returns false if one of the waits ran out.
 template <bool SG, bool NT>
-__device__ bool team_chunk(TeamLds &T, int kb, int n, const uint16_t *__restrict__ q,
+__device__ __forceinline__ bool team_chunk(TeamLds &T, int kb, int n, const uint16_t *__restrict__ q,
                            const uint16_t *__restrict__ k, const uint16_t *__restrict__ g,
                            const uint16_t *__restrict__ beta, const float *__restrict__ dt_bias,
                            float A, float lb2, int64_t t0, int len, int H, int hh, int K,
