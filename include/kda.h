@@ -281,17 +281,16 @@ size_t kda_workspace_reserved(void);
 
 /*
  * Bytes of device workspace one kda_fwd (or kda_fwd_scalar_gate) call with
- * these sizes and head dimension K = V = 64 or 128 takes from the pool on
- * the current device: the hand-off record rings and flags of the fused
- * kernel when it applies (up to 128 (sequence, head) units at K = 128 on a
- * 256-CU device, about 0.14 MB per unit), else one hand-off record per
- * (chunk slot, head).  0 on invalid sizes.
+ * these sizes at head dimension K = V = 128 takes from the pool on the
+ * current device: one hand-off record (27 KB) per (32-token chunk slot,
+ * head), floor(B T / 32) + num_seqs slots.  0 on invalid sizes.
  */
 size_t kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs);
 
 /*
- * The same for any supported head dimension K (64, 128 or 256; head
- * dimension 256 takes 26 KB records per (chunk, head) instead of 13 KB).
+ * The same for any supported head dimension K (64, 128 or 256): K = 64 and
+ * 128 take 27 KB records per 32-token chunk slot and head, K = 256 26 KB
+ * records per 16-token chunk slot and head.
  * 0 on invalid sizes or an unsupported K.
  */
 size_t kda_workspace_size_hd(int32_t B, int32_t T, int32_t H, int32_t num_seqs, int32_t K);

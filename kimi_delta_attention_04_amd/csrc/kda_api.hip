@@ -106,14 +106,6 @@ __global__ void check_cu_kernel(const int32_t *__restrict__ cu, int N, int T, in
     if (threadIdx.x == 0) *bad = b;
 }
 
-// KDA_CHECK_FUSED set to a value other than "0": after the fused kernel
-// the call synchronises and fails with KDA_ERR_LAUNCH if the kernel's error
-// word is set.
-bool fused_check_enabled() {
-    const char *e = getenv("KDA_CHECK_FUSED");
-    return e && e[0] && !(e[0] == '0' && e[1] == 0);
-}
-
 bool cu_check_enabled() {
     const char *e = getenv("KDA_CHECK_CU_SEQLENS");
     return e && e[0] && !(e[0] == '0' && e[1] == 0);
@@ -196,8 +188,6 @@ size_t kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs) {
 size_t kda_workspace_size_hd(int32_t B, int32_t T, int32_t H, int32_t num_seqs, int32_t K) {
     if (B < 1 || T < 0 || H < 1 || num_seqs < 1) return 0;
     if (K != 64 && K != kda::HD && K != 2 * kda::HD) return 0;
-    if (kda::fused_applicable((int64_t)B * T, num_seqs, H, K))
-        return kda::fused_workspace_bytes(num_seqs, H);
     return kda_record_workspace_size(B, T, H, num_seqs, K);
 }
 
@@ -246,26 +236,6 @@ hipError_t fwd_launch(const void *q, const void *k, const void *v, const void *g
     const int init32 = initial_state_dtype == KDA_DTYPE_FP32;
     const int fin32 = final_state_dtype == KDA_DTYPE_FP32;
     hipError_t e = mark(0, s);
-    if (kda::fused_applicable((int64_t)B * T, num_seqs, H, K)) {
-        if (e == hipSuccess) e = mark(1, s);
-        if (e == hipSuccess)
-            e = kda::launch_fused((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v,
-                                  (const uint16_t *)g, (const uint16_t *)beta, scale, A_log, dt_bias,
-                                  lower_bound, cu_seqlens, num_seqs, T, H, K, (int64_t)B * T,
-                                  initial_state, init32, final_state, fin32, (uint16_t *)out, ws, s,
-                                  scalar_gate);
-        if (e == hipSuccess) e = mark(2, s);
-        if (e == hipSuccess && fused_check_enabled()) {
-            // debugging aid: synchronise and report a wait that ran out or a
-            // workgroup on an unexpected XCD
-            uint32_t word = 0;
-            e = hipMemcpyAsync(&word, kda::fused_error_word(ws, num_seqs, H), sizeof(word),
-                               hipMemcpyDeviceToHost, s);
-            if (e == hipSuccess) e = hipStreamSynchronize(s);
-            if (e == hipSuccess && word != 0) e = hipErrorLaunchFailure;
-        }
-        return e;
-    }
     if (K <= kda::HD) {
         if (e == hipSuccess)
             e = kda::launch_intra32((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,

@@ -16,7 +16,6 @@
 // chunks ahead.
 #include "kda_c32_dev.h"
 #include "kda_launch.h"
-#include "kda_team_dev.h"
 
 namespace kda {
 
@@ -57,36 +56,6 @@ __global__ __launch_bounds__(64, 2) void intra32_kernel(
         intra32_compute<true, SG>(lds, &klds, in, A, dtb_lds, lb2, len, rec);
     else
         intra32_compute<false, SG>(lds, &klds, in, A, dtb_lds, lb2, len, rec);
-}
-
-// One team of four waves (one per 32-channel block) per (chunk slot, head).
-template <bool SG>
-__global__ __launch_bounds__(256, 2) void intra_team_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
-    const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb2,
-    const int32_t *__restrict__ cu, int N, int T, int H, int K, uint8_t *__restrict__ ws)
-{
-    __shared__ __attribute__((aligned(16))) TeamLds team;
-    const int64_t slot = (int64_t)(gridDim.x / (unsigned)H) - 1 - blockIdx.x / (unsigned)H;
-    const int h = (int)(blockIdx.x % (unsigned)H);
-    int lo = 0, hi = N - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (seq_slot0_32(cu, mid, T) <= slot) lo = mid; else hi = mid - 1;
-    }
-    const int n = lo;
-    int64_t start, end;
-    seq_range(cu, n, T, start, end);
-    const int64_t t0 = start + (slot - seq_slot0_32(cu, n, T)) * C32;
-    if (t0 >= end) return;                             // gap slot, uniform
-    const int len = (int)min((int64_t)C32, end - t0);
-    uint8_t *rec = ws + ((size_t)slot * H + h) * Rec32::BYTES;
-    const int kb = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    team_init(team);
-    __syncthreads();
-    const float A = expf(A_log[h]);
-    team_chunk<SG, true>(team, kb, 0, q, k, g, beta, dt_bias, A, lb2, t0, len, H, h, K, rec);
 }
 
 // s_waitcnt vmcnt(n) followed by a workgroup barrier (waits for this

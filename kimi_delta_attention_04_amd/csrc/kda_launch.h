@@ -27,22 +27,6 @@ hipError_t launch_scan32(const uint16_t *v, const uint8_t *ws, const int32_t *cu
                          int H, int K, int V, float scale, const void *init, int init_fp32,
                          void *fin, int fin_fp32, uint16_t *out, hipStream_t stream);
 
-// Fused forward (32-token chunks, K = V = 128 or 64): one cooperative launch
-// whose hand-off records stay in the L2 of the XCD that makes and consumes
-// them.  Applicable while every scan part of the batch is resident at once
-// (N * H up to 128 units at K = 128 on 256 compute units).  Workspace:
-// fused_workspace_bytes(N, H), 256-byte aligned; the word at
-// fused_error_word() is non-zero after the launch when a wait ran out or a
-// workgroup ran on an unexpected XCD.
-bool fused_applicable(int64_t tokens, int N, int H, int K);
-size_t fused_workspace_bytes(int N, int H);
-hipError_t launch_fused(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
-                        const uint16_t *beta, float scale, const float *A_log, const float *dt_bias,
-                        float lower_bound, const int32_t *cu, int N, int T, int H, int K,
-                        int64_t tokens, const void *init, int init_fp32, void *fin, int fin_fp32,
-                        uint16_t *out, void *ws, hipStream_t stream, bool scalar_gate);
-const uint32_t *fused_error_word(const void *ws, int N, int H);
-
 // Inter-chunk scan over N sequences x H heads (column parts per head chosen
 // by the launch).  K = V = 128 or 64: the 128 x 128 state tiles carry zeros
 // in the rows from K on and the columns from V on.
