@@ -314,6 +314,31 @@ kda_status_t kda_debug_intra(const void *q, const void *k, const void *g,
                              void *workspace, void *stream);
 
 /*
+ * kda_debug_scan_step — test entry: runs only the inter-chunk scan of the
+ * 32-token forward (K = V = 64 or 128) over hand-off records the caller
+ * provides, one chunk step per record in order from the given state: per
+ * chunk with state S (rows = key channels, columns = value channels)
+ *   X = V - Kt S,   O = scale (Qt S + M X),   S <- diag(gamma) S + W^T X
+ * (the chunkwise recurrence of the FlashKDA write-up, "Moonshot AI
+ * Open-Sources FlashKDA", section "Why KDA?"; Kt, Qt, W, M and gamma as in
+ * the records).  With sequences of at most 32 tokens this is exactly one
+ * step from initial_state.  `records`: device, laid out as kda_debug_intra
+ * writes them (kda_record_workspace_size(B, T, H, num_seqs, K) bytes,
+ * 16-byte aligned; read only).  `v`, `out`, `cu_seqlens`, the states and
+ * their dtypes as in kda_fwd (a NULL initial_state is zero, a NULL
+ * final_state is not written).  `part_cols`: columns of the state per scan
+ * workgroup, 32, 64 or 128 (at most V), or 0 for the width kda_fwd picks.
+ * KDA_ERR_UNSUPPORTED for K = 256; otherwise errors as kda_fwd.  Enqueued on
+ * `stream`; returns before the kernel runs.
+ */
+kda_status_t kda_debug_scan_step(const void *v, const void *records, const int32_t *cu_seqlens,
+                                 int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                                 int32_t V, float scale, const void *initial_state,
+                                 kda_dtype_t initial_state_dtype, void *final_state,
+                                 kda_dtype_t final_state_dtype, void *out, int32_t part_cols,
+                                 void *stream);
+
+/*
  * kda_set_stage_events — instrumentation for per-kernel timing.  When set
  * (non-NULL hipEvent_t handles created by the caller on the device the calls
  * run on), the next kda_fwd calls made from the calling thread record

@@ -26,7 +26,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "fwd_noalloc", "fwd_scalar_gate", "decode", "bwd", "debug_intra", "set_stage_events", "set_bwd_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
+__all__ = ["fwd", "fwd_noalloc", "fwd_scalar_gate", "decode", "bwd", "debug_intra", "debug_scan_step", "set_stage_events", "set_bwd_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
            "status_string", "KDAError", "library_path", "load", "HEAD_DIM"]
 
 HEAD_DIM = 128
@@ -86,6 +86,9 @@ def load():
                             P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
     lib.kda_debug_intra.restype = ctypes.c_int
     lib.kda_debug_intra.argtypes = [P, P, P, P, P, P, f32, P, i32, i32, i32, i32, i32, P, P]
+    lib.kda_debug_scan_step.restype = ctypes.c_int
+    lib.kda_debug_scan_step.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, f32, P, ctypes.c_int,
+                                        P, ctypes.c_int, P, i32, P]
     lib.kda_fwd_noalloc.restype = ctypes.c_int
     lib.kda_fwd_noalloc.argtypes = lib.kda_fwd.argtypes
     lib.kda_record_workspace_size.restype = ctypes.c_size_t
@@ -364,6 +367,44 @@ def set_stage_events(before_intra=None, before_scan=None, after_scan=None):
     next kda_fwd calls from this thread; all None to stop."""
     P = ctypes.c_void_p
     load().kda_set_stage_events(P(before_intra), P(before_scan), P(after_scan))
+
+
+def debug_scan_step(v, records, scale, out, initial_state=None, final_state=None,
+                    cu_seqlens=None, part_cols=0):
+    """Run only the inter-chunk scan (K = V = 64 or 128) over `records` (as
+    debug_intra returns them) from initial_state, writing out and
+    final_state; part_cols fixes the columns per scan workgroup (0: the
+    forward's choice)."""
+    import torch
+    lib = load()
+    if v.dim() != 4:
+        raise ValueError("v must be [B, T, H, V]")
+    B, T, H, V = v.shape
+    bf = torch.bfloat16
+    _check(v, "v", bf)
+    _check(out, "out", bf, (B, T, H, V))
+    _check(records, "records", torch.uint8)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    need = int(lib.kda_record_workspace_size(B, T, H, N, V))
+    if records.numel() < need:
+        raise ValueError(f"records holds {records.numel()} bytes, the scan reads {need}")
+    init_dt = fin_dt = KDA_DTYPE_FP32
+    if initial_state is not None:
+        init_dt = _state_dtype(initial_state)
+        _check(initial_state, "initial_state", initial_state.dtype, (N, H, V, V))
+    if final_state is not None:
+        fin_dt = _state_dtype(final_state)
+        _check(final_state, "final_state", final_state.dtype, (N, H, V, V))
+    rc = lib.kda_debug_scan_step(_ptr(v), _ptr(records), _ptr(cu_seqlens), int(N), int(B), int(T),
+                                 int(H), int(V), int(V), float(scale), _ptr(initial_state),
+                                 int(init_dt), _ptr(final_state), int(fin_dt), _ptr(out),
+                                 int(part_cols), _stream(v.device))
+    if rc != 0:
+        raise KDAError(rc, "kda_debug_scan_step")
 
 
 def debug_intra(q, k, g, beta, A_log, dt_bias, lower_bound, cu_seqlens=None):

@@ -360,6 +360,35 @@ kda_status_t kda_debug_intra(const void *q, const void *k, const void *g,
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+kda_status_t kda_debug_scan_step(const void *v, const void *records, const int32_t *cu_seqlens,
+                                 int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+                                 int32_t V, float scale, const void *initial_state,
+                                 kda_dtype_t initial_state_dtype, void *final_state,
+                                 kda_dtype_t final_state_dtype, void *out, int32_t part_cols,
+                                 void *stream)
+{
+    const bool no_tokens = (int64_t)B * T == 0;
+    if (!records || (!no_tokens && (!v || !out))) return KDA_ERR_INVALID_ARG;
+    if (!aligned(v, 16) || !aligned(records, 16) || !aligned(out, 16) ||
+        !aligned(cu_seqlens, 4) || !aligned(initial_state, 16) || !aligned(final_state, 16))
+        return KDA_ERR_INVALID_ARG;
+    if ((initial_state_dtype != KDA_DTYPE_BF16 && initial_state_dtype != KDA_DTYPE_FP32) ||
+        (final_state_dtype != KDA_DTYPE_BF16 && final_state_dtype != KDA_DTYPE_FP32))
+        return KDA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    kda_status_t st = check_sizes(B, T, H, K, V, cu_seqlens, num_seqs);
+    if (st != KDA_OK) return st;
+    if (K > kda::HD) return KDA_ERR_UNSUPPORTED;
+    if (part_cols != 0 && part_cols != 32 && part_cols != 64 && part_cols != 128)
+        return KDA_ERR_INVALID_ARG;
+    if (part_cols > V) return KDA_ERR_INVALID_ARG;
+    const hipError_t e = kda::launch_scan32(
+        (const uint16_t *)v, (const uint8_t *)records, cu_seqlens, num_seqs, T, H, K, V, scale,
+        initial_state, initial_state_dtype == KDA_DTYPE_FP32, final_state,
+        final_state_dtype == KDA_DTYPE_FP32, (uint16_t *)out, (hipStream_t)stream, part_cols);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 kda_status_t kda_decode(const void *q, const void *k, const void *v, const void *g,
                         const void *beta, float scale,
                         const float *A_log, const float *dt_bias, float lower_bound,

@@ -355,15 +355,17 @@ hipError_t launch_intra32(const uint16_t *q, const uint16_t *k, const uint16_t *
 
 hipError_t launch_scan32(const uint16_t *v, const uint8_t *ws, const int32_t *cu, int N, int T,
                          int H, int K, int V, float scale, const void *init, int init_fp32,
-                         void *fin, int fin_fp32, uint16_t *out, hipStream_t stream)
+                         void *fin, int fin_fp32, uint16_t *out, hipStream_t stream, int part_cols)
 {
     const int64_t units = (int64_t)N * H;
     if (units <= 0) return hipSuccess;
     const int cus = cu_count32();
     // columns per workgroup: 32 while four parts a head still leave compute
-    // units free, then 64, then the whole head
+    // units free, then 64, then the whole head (unless the caller fixes it)
     int cw = (V / 32) * units <= cus ? 32 : (V / 64) * units <= cus ? 64 : 128;
+    if (part_cols) cw = part_cols;
     if (cw > V) cw = V;
+    if (cw != 32 && cw != 64 && cw != 128) return hipErrorInvalidValue;
     const int64_t blocks = 8 * (V / cw) * ((units + 7) / 8);
 #define KDA_SCAN32(NW_, VD_)                                                                     \
     hipLaunchKernelGGL((scan32_kernel<NW_, VD_>), dim3((unsigned)blocks), dim3(64 * (NW_ + 1)), 0, \

@@ -23,9 +23,12 @@ hipError_t launch_intra32(const uint16_t *q, const uint16_t *k, const uint16_t *
                           const uint16_t *beta, const float *A_log, const float *dt_bias,
                           float lower_bound, const int32_t *cu, int N, int T, int H, int K,
                           int64_t num_slots, uint8_t *ws, hipStream_t stream, bool scalar_gate);
+// part_cols: columns per scan workgroup (32, 64 or 128; 0 = chosen from the
+// number of (sequence, head) units and compute units).
 hipError_t launch_scan32(const uint16_t *v, const uint8_t *ws, const int32_t *cu, int N, int T,
                          int H, int K, int V, float scale, const void *init, int init_fp32,
-                         void *fin, int fin_fp32, uint16_t *out, hipStream_t stream);
+                         void *fin, int fin_fp32, uint16_t *out, hipStream_t stream,
+                         int part_cols = 0);
 
 // Inter-chunk scan over N sequences x H heads (column parts per head chosen
 // by the launch).  K = V = 128 or 64: the 128 x 128 state tiles carry zeros

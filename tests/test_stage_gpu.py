@@ -18,50 +18,9 @@ import kda_inputs
 import kimi_delta_attention_04_amd as kda
 import oracle
 from gpu_util import to_device
+from records import CS, REC, decode
 
 pytestmark = pytest.mark.gpu
-
-REC = 27648
-CS = 32
-
-
-def state_chan(t, rho):
-    return 32 * (t // 2) + 8 * (rho // 4) + 4 * (t % 2) + rho % 4
-
-
-def tau(kappa):
-    """Token of k index kappa in the W^T and M operands."""
-    g, i = kappa // 8, kappa % 8
-    return 4 * g + i if i < 4 else 16 + 4 * g + i - 4
-
-
-def bf16_words_to_f64(u16: np.ndarray) -> np.ndarray:
-    return (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-
-
-def decode(rec: np.ndarray):
-    """One 27648-byte record -> natural-layout matrices."""
-    u16 = rec.view(np.uint16)
-    kt = bf16_words_to_f64(u16[0:4096]).reshape(4, 2, 64, 8)
-    qt = bf16_words_to_f64(u16[4096:8192]).reshape(4, 2, 64, 8)
-    wt = bf16_words_to_f64(u16[8192:12288]).reshape(8, 64, 8)
-    mm = bf16_words_to_f64(u16[12288:13312]).reshape(2, 64, 8)
-    Kt = np.zeros((CS, 128)); Qt = np.zeros((CS, 128)); W = np.zeros((CS, 128))
-    M = np.zeros((CS, CS))
-    for l in range(64):
-        r, grp = l % 16, l // 16
-        for kb in range(4):
-            for rt in range(2):
-                Kt[16 * rt + r, 32 * kb + 8 * grp: 32 * kb + 8 * grp + 8] = kt[kb, rt, l]
-                Qt[16 * rt + r, 32 * kb + 8 * grp: 32 * kb + 8 * grp + 8] = qt[kb, rt, l]
-        for i in range(8):
-            tok = tau(8 * grp + i)
-            for t in range(8):
-                W[tok, state_chan(t, r)] = wt[t, l, i]
-            for rt in range(2):
-                M[16 * rt + r, tok] = mm[rt, l, i]
-    gam = rec[26624:27136].view(np.float32).astype(np.float64)
-    return Kt, Qt, W, M, gam
 
 
 def expected_chunk(inp, t0, n_tok, h):
