@@ -56,7 +56,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 METRIC = "KDA fwd tokens/s @T=8192,H=96,D=128 (fixed+varlen); % of MFMA/HBM roofline"
-CHUNK = 32           # tokens per chunk of the forward at K = V = 128
+CHUNK = 16           # tokens per chunk of the forward
 BWD_CHUNK = 16       # the backward's chunk factors
 
 

@@ -282,15 +282,14 @@ size_t kda_workspace_reserved(void);
 /*
  * Bytes of device workspace one kda_fwd (or kda_fwd_scalar_gate) call with
  * these sizes at head dimension K = V = 128 takes from the pool on the
- * current device: one hand-off record (27 KB) per (32-token chunk slot,
- * head), floor(B T / 32) + num_seqs slots.  0 on invalid sizes.
+ * current device: one hand-off record (13 KB) per (16-token chunk slot,
+ * head), floor(B T / 16) + num_seqs slots.  0 on invalid sizes.
  */
 size_t kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs);
 
 /*
  * The same for any supported head dimension K (64, 128 or 256): K = 64 and
- * 128 take 27 KB records per 32-token chunk slot and head, K = 256 26 KB
- * records per 16-token chunk slot and head.
+ * 128 take 13 KB records per chunk slot and head, K = 256 26 KB records.
  * 0 on invalid sizes or an unsupported K.
  */
 size_t kda_workspace_size_hd(int32_t B, int32_t T, int32_t H, int32_t num_seqs, int32_t K);
@@ -300,10 +299,10 @@ size_t kda_workspace_size_hd(int32_t B, int32_t T, int32_t H, int32_t num_seqs, 
  * in-chunk cumulative decay, A_kk / A_qk products, triangular inverse) and
  * writes the hand-off record of every (chunk slot, head) into the caller's
  * `workspace` (device, kda_record_workspace_size(B, T, H, num_seqs, K)
- * bytes, 16-byte aligned).  Arguments as kda_fwd.  Record layout (per chunk
- * slot and head: 27648 bytes for the 32-token chunks of K = 64 and 128,
- * 26624 bytes for the 16-token chunks of K = 256) is described in the
- * library source; tests decode it to compare each stage with fp64 maths.
+ * bytes, 16-byte aligned).  Arguments as kda_fwd.  Record layout (per
+ * 16-token chunk slot and head: 13312 bytes for K = 64 and 128, 26624
+ * bytes for K = 256) is described in the library source; tests decode it to
+ * compare each stage with fp64 maths.
  */
 size_t kda_record_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs, int32_t K);
 kda_status_t kda_debug_intra(const void *q, const void *k, const void *g,
@@ -315,20 +314,20 @@ kda_status_t kda_debug_intra(const void *q, const void *k, const void *g,
 
 /*
  * kda_debug_scan_step — test entry: runs only the inter-chunk scan of the
- * 32-token forward (K = V = 64 or 128) over hand-off records the caller
+ * forward (K = V = 64, 128 or 256) over hand-off records the caller
  * provides, one chunk step per record in order from the given state: per
  * chunk with state S (rows = key channels, columns = value channels)
  *   X = V - Kt S,   O = scale (Qt S + M X),   S <- diag(gamma) S + W^T X
  * (the chunkwise recurrence of the FlashKDA write-up, "Moonshot AI
  * Open-Sources FlashKDA", section "Why KDA?"; Kt, Qt, W, M and gamma as in
- * the records).  With sequences of at most 32 tokens this is exactly one
+ * the records).  With sequences of at most 16 tokens this is exactly one
  * step from initial_state.  `records`: device, laid out as kda_debug_intra
  * writes them (kda_record_workspace_size(B, T, H, num_seqs, K) bytes,
  * 16-byte aligned; read only).  `v`, `out`, `cu_seqlens`, the states and
  * their dtypes as in kda_fwd (a NULL initial_state is zero, a NULL
  * final_state is not written).  `part_cols`: columns of the state per scan
- * workgroup, 32, 64 or 128 (at most V), or 0 for the width kda_fwd picks.
- * KDA_ERR_UNSUPPORTED for K = 256; otherwise errors as kda_fwd.  Enqueued on
+ * workgroup, 32, 64 or 128 (at most V), or 0 for the width kda_fwd picks;
+ * otherwise KDA_ERR_INVALID_ARG.  Other errors as kda_fwd.  Enqueued on
  * `stream`; returns before the kernel runs.
  */
 kda_status_t kda_debug_scan_step(const void *v, const void *records, const int32_t *cu_seqlens,

@@ -103,7 +103,7 @@ def load():
 
 # The sources the forward kernels (intra stage and scan) are compiled from,
 # and those of the backward kernels.
-FORWARD_KERNEL_SOURCES = ("kda_device.h", "kda_intra_dev.h", "kda_c32_dev.h", "kda_c32.hip")
+FORWARD_KERNEL_SOURCES = ("kda_device.h", "kda_intra_dev.h", "kda_intra.hip", "kda_scan.hip")
 BACKWARD_KERNEL_SOURCES = ("kda_device.h", "kda_intra_dev.h", "kda_bwd.hip")
 
 
@@ -371,7 +371,7 @@ def set_stage_events(before_intra=None, before_scan=None, after_scan=None):
 
 def debug_scan_step(v, records, scale, out, initial_state=None, final_state=None,
                     cu_seqlens=None, part_cols=0):
-    """Run only the inter-chunk scan (K = V = 64 or 128) over `records` (as
+    """Run only the inter-chunk scan (K = V = 64, 128 or 256) over `records` (as
     debug_intra returns them) from initial_state, writing out and
     final_state; part_cols fixes the columns per scan workgroup (0: the
     forward's choice)."""

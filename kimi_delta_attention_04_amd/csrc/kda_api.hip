@@ -8,16 +8,13 @@
 #include <hip/hip_runtime.h>
 
 #include "kda.h"
-#include "kda_c32_dev.h"
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace {
 
 // 16 tokens * |lower_bound| * log2(e) must stay below ~125 so that both
-// 2^g and 2^-g of the cumulative decay within a 16-token (sub-)block are
-// normal fp32 / bf16 (the 32-token chunks re-reference the decay at each
-// 16-token sub-block).
+// 2^G and 2^-G of the in-chunk cumulative decay are normal fp32 / bf16.
 constexpr float kLowerBoundMin = -5.4f;
 constexpr int kMaxDevices = 64;
 
@@ -65,15 +62,9 @@ hipError_t mark(int i, hipStream_t s) {
     return t_stage_events[i] ? hipEventRecord(t_stage_events[i], s) : hipSuccess;
 }
 
-// 16-token chunk slots (head dimension 256, and the backward)
+// 16-token chunk slots: floor(B T / 16) + N
 int64_t num_slots(int32_t B, int32_t T, int32_t N) {
     return ((int64_t)B * T) / kda::CS + N;
-}
-
-// Chunk slots of the forward at head dimension K: 32-token chunks for
-// K = 64 and 128, 16-token chunks for 256.
-int64_t fwd_slots(int32_t B, int32_t T, int32_t N, int32_t K) {
-    return K > kda::HD ? num_slots(B, T, N) : kda::c32_num_slots((int64_t)B * T, N);
 }
 
 kda_status_t check_sizes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
@@ -88,8 +79,8 @@ kda_status_t check_sizes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
     // one intra workgroup per (chunk slot, head) in a 1-D grid
     if (num_slots(B, T, N) * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     if ((int64_t)N * H > INT32_MAX / 64) return KDA_ERR_UNSUPPORTED;
-    // byte offsets within one chunk's 32 token rows of all heads are 32-bit
-    if ((int64_t)H * (K > kda::HD ? K : kda::HD) * 2 * kda::C32 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    // byte offsets within one chunk's 16 token rows of all heads are 32-bit
+    if ((int64_t)H * (K > kda::HD ? K : kda::HD) * 2 * kda::CS > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
 }
 
@@ -157,7 +148,7 @@ const char *kda_status_string(kda_status_t s) {
 
 float kda_lower_bound_min(void) { return kLowerBoundMin; }
 
-int32_t kda_chunk_size(void) { return kda::C32; }
+int32_t kda_chunk_size(void) { return kda::CS; }
 
 kda_status_t kda_trim_workspace(size_t keep_bytes) {
     hipMemPool_t pool = nullptr;
@@ -177,8 +168,9 @@ size_t kda_workspace_reserved(void) {
 size_t kda_record_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs, int32_t K) {
     if (B < 1 || T < 0 || H < 1 || num_seqs < 1) return 0;
     if (K != 64 && K != kda::HD && K != 2 * kda::HD) return 0;
-    const size_t rec = K > kda::HD ? (size_t)kda::RecLayout<2 * kda::HD>::BYTES : (size_t)kda::Rec32::BYTES;
-    return (size_t)fwd_slots(B, T, num_seqs, K) * (size_t)H * rec;
+    const size_t rec = K > kda::HD ? (size_t)kda::RecLayout<2 * kda::HD>::BYTES
+                                   : (size_t)kda::RecLayout<kda::HD>::BYTES;
+    return (size_t)num_slots(B, T, num_seqs) * (size_t)H * rec;
 }
 
 size_t kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs) {
@@ -232,31 +224,18 @@ hipError_t fwd_launch(const void *q, const void *k, const void *v, const void *g
                       int32_t T, int32_t H, int32_t K, int32_t V, hipStream_t s,
                       bool scalar_gate, void *ws)
 {
-    const int64_t slots = fwd_slots(B, T, num_seqs, K);
+    const int64_t slots = num_slots(B, T, num_seqs);
     const int init32 = initial_state_dtype == KDA_DTYPE_FP32;
     const int fin32 = final_state_dtype == KDA_DTYPE_FP32;
     hipError_t e = mark(0, s);
-    if (K <= kda::HD) {
-        if (e == hipSuccess)
-            e = kda::launch_intra32((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,
-                                    (const uint16_t *)beta, A_log, dt_bias, lower_bound, cu_seqlens,
-                                    num_seqs, T, H, K, slots, (uint8_t *)ws, s, scalar_gate);
-        if (e == hipSuccess) e = mark(1, s);
-        if (e == hipSuccess)
-            e = kda::launch_scan32((const uint16_t *)v, (const uint8_t *)ws, cu_seqlens, num_seqs, T,
-                                   H, K, V, scale, initial_state, init32, final_state, fin32,
-                                   (uint16_t *)out, s);
-    } else {
-        if (e == hipSuccess)
-            e = kda::launch_intra((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,
-                                  (const uint16_t *)beta, A_log, dt_bias, lower_bound, cu_seqlens,
-                                  num_seqs, T, H, K, slots, (uint8_t *)ws, s, scalar_gate);
-        if (e == hipSuccess) e = mark(1, s);
-        if (e == hipSuccess)
-            e = kda::launch_scan((const uint16_t *)v, (const uint8_t *)ws, cu_seqlens, num_seqs, T, H,
-                                 K, V, scale, initial_state, init32, final_state, fin32,
-                                 (uint16_t *)out, s);
-    }
+    if (e == hipSuccess)
+        e = kda::launch_intra((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,
+                              (const uint16_t *)beta, A_log, dt_bias, lower_bound, cu_seqlens,
+                              num_seqs, T, H, K, slots, (uint8_t *)ws, s, scalar_gate);
+    if (e == hipSuccess) e = mark(1, s);
+    if (e == hipSuccess)
+        e = kda::launch_scan((const uint16_t *)v, (const uint8_t *)ws, cu_seqlens, num_seqs, T, H, K,
+                             V, scale, initial_state, init32, final_state, fin32, (uint16_t *)out, s);
     if (e == hipSuccess) e = mark(2, s);
     return e;
 }
@@ -347,16 +326,11 @@ kda_status_t kda_debug_intra(const void *q, const void *k, const void *g,
     kda_status_t st = check_sizes(B, T, H, K, K, cu_seqlens, num_seqs);
     if (st != KDA_OK) return st;
     if ((st = check_gate(lower_bound)) != KDA_OK) return st;
-    hipError_t e =
-        K <= kda::HD
-            ? kda::launch_intra32((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,
-                                  (const uint16_t *)beta, A_log, dt_bias, lower_bound, cu_seqlens,
-                                  num_seqs, T, H, K, fwd_slots(B, T, num_seqs, K),
-                                  (uint8_t *)workspace, (hipStream_t)stream, false)
-            : kda::launch_intra((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,
-                                (const uint16_t *)beta, A_log, dt_bias, lower_bound, cu_seqlens,
-                                num_seqs, T, H, K, num_slots(B, T, num_seqs), (uint8_t *)workspace,
-                                (hipStream_t)stream);
+    const hipError_t e =
+        kda::launch_intra((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)g,
+                          (const uint16_t *)beta, A_log, dt_bias, lower_bound, cu_seqlens, num_seqs,
+                          T, H, K, num_slots(B, T, num_seqs), (uint8_t *)workspace,
+                          (hipStream_t)stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -378,11 +352,10 @@ kda_status_t kda_debug_scan_step(const void *v, const void *records, const int32
     if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
     kda_status_t st = check_sizes(B, T, H, K, V, cu_seqlens, num_seqs);
     if (st != KDA_OK) return st;
-    if (K > kda::HD) return KDA_ERR_UNSUPPORTED;
     if (part_cols != 0 && part_cols != 32 && part_cols != 64 && part_cols != 128)
         return KDA_ERR_INVALID_ARG;
     if (part_cols > V) return KDA_ERR_INVALID_ARG;
-    const hipError_t e = kda::launch_scan32(
+    const hipError_t e = kda::launch_scan(
         (const uint16_t *)v, (const uint8_t *)records, cu_seqlens, num_seqs, T, H, K, V, scale,
         initial_state, initial_state_dtype == KDA_DTYPE_FP32, final_state,
         final_state_dtype == KDA_DTYPE_FP32, (uint16_t *)out, (hipStream_t)stream, part_cols);

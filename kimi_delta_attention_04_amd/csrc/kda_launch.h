@@ -16,26 +16,15 @@ hipError_t launch_intra(const uint16_t *q, const uint16_t *k, const uint16_t *g,
                         int64_t num_slots, uint8_t *ws, hipStream_t stream,
                         bool scalar_gate = false);
 
-// 32-token chunks (K = V = 128, or 64 on the 128-wide tiles): chunk slots
-// floor(tokens / 32) + N; records of Rec32::BYTES (27 KB) per (slot, head).
-int64_t c32_num_slots(int64_t tokens, int N);
-hipError_t launch_intra32(const uint16_t *q, const uint16_t *k, const uint16_t *g,
-                          const uint16_t *beta, const float *A_log, const float *dt_bias,
-                          float lower_bound, const int32_t *cu, int N, int T, int H, int K,
-                          int64_t num_slots, uint8_t *ws, hipStream_t stream, bool scalar_gate);
-// part_cols: columns per scan workgroup (32, 64 or 128; 0 = chosen from the
-// number of (sequence, head) units and compute units).
-hipError_t launch_scan32(const uint16_t *v, const uint8_t *ws, const int32_t *cu, int N, int T,
-                         int H, int K, int V, float scale, const void *init, int init_fp32,
-                         void *fin, int fin_fp32, uint16_t *out, hipStream_t stream,
-                         int part_cols = 0);
-
-// Inter-chunk scan over N sequences x H heads (column parts per head chosen
-// by the launch).  K = V = 128 or 64: the 128 x 128 state tiles carry zeros
-// in the rows from K on and the columns from V on.
+// Inter-chunk scan over N sequences x H heads.  K = V = 128 or 64 (the
+// 128 x 128 state tiles carry zeros in the rows from K on and the columns
+// from V on), or 256.  part_cols: columns of the state per workgroup (32,
+// 64 or 128, at most V); 0 = chosen from the number of (sequence, head)
+// units and compute units.
 hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, int N, int T,
                        int H, int K, int V, float scale, const void *init, int init_fp32,
-                       void *fin, int fin_fp32, uint16_t *out, hipStream_t stream);
+                       void *fin, int fin_fp32, uint16_t *out, hipStream_t stream,
+                       int part_cols = 0);
 
 // One-token decode step on N x H states of D x D (D = 64, 128 or 256) in
 // place (fp32 or bf16).

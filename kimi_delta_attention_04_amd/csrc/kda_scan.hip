@@ -459,7 +459,7 @@ int num_cus() {
 
 hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, int N, int T,
                        int H, int K, int V, float scale, const void *init, int init_fp32,
-                       void *fin, int fin_fp32, uint16_t *out, hipStream_t stream)
+                       void *fin, int fin_fp32, uint16_t *out, hipStream_t stream, int part_cols)
 {
     const int64_t units = (int64_t)N * H;
     if (units <= 0) return hipSuccess;
@@ -474,7 +474,8 @@ hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, 
     // round of workgroups up to 128 units.)
     const int cw = V == 2 * HD ? (8 * units <= cus ? 32 : 4 * units <= cus ? 64 : 128)
                  : (V == 128 ? 4 : 2) * units <= cus ? 32 : (V == 128 ? 2 : 1) * units <= cus ? 64 : 128;
-    const int part_cw = cw > V ? V : cw;
+    const int part_cw = part_cols ? part_cols : cw > V ? V : cw;
+    if ((part_cw != 32 && part_cw != 64 && part_cw != 128) || part_cw > V) return hipErrorInvalidValue;
     const int64_t blocks = 8 * (V / part_cw) * ((units + 7) / 8);
 #define KDA_SCAN(CT_, NW_, VD_)                                                               \
     hipLaunchKernelGGL((scan_kernel<CT_, NW_, VD_>), dim3((unsigned)blocks), dim3(64 * (NW_ + 1)), \

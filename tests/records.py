@@ -1,38 +1,36 @@
-"""Codec of the 32-token hand-off record (K = V = 64 or 128), test helper.
+"""Codec of the 16-token hand-off record, test helper.
 
-A record holds one (32-token chunk, head) in the register layouts of the
-scan's 16x16x32 bf16 MFMA operands; lane l of a wave holds row l % 16 of a
-16-row tile and 8 consecutive k values starting at 8 (l / 16):
-  bytes     0 ..  8191  Kt  [kb 0..3][rt 0..1][lane][8 bf16]:
-                        Kt[16 rt + l%16][32 kb + 8 (l/16) + i]
-  bytes  8192 .. 16383  Qt  the same for Qt
-  bytes 16384 .. 24575  W^T [t 0..7][lane][8 bf16]:
-                        W[tau(8 (l/16) + i)][state_chan(t, l%16)]
-  bytes 24576 .. 26623  M   [rt 0..1][lane][8 bf16]:
-                        M[16 rt + l%16][tau(8 (l/16) + i)]
-  bytes 26624 .. 27135  gamma, 128 fp32 (chunk decay per key channel)
-  bytes 27136 .. 27647  unused
-with tau the token order in which the scan's accumulators hold the rows of
-X and state_chan the state-row order of its accumulator tiles.  K = 64 uses
-the same layout with the channels from 64 on zero.
+A record holds one (16-token chunk, head) for KT key channels (128, also
+used by K = 64 with the channels from 64 on zero, or 256) in the register
+layouts of the scan's MFMA operands; lane l of a wave holds row l % 16:
+  KT  [kb 0..KT/32-1][lane][8 bf16]  Kt[l%16][32 kb + 8 (l/16) + i]
+  QT  the same for Qt                                       (at 32 KT bytes)
+  WT  [tp 0..KT/32-1][lane][8 bf16]  W[4 (l/16) + j][state_chan(2 tp + h, l%16)]
+      at bf16 4 h + j (two 16x16x16 A operands, tiles 2tp and 2tp+1)
+                                                            (at 64 KT bytes)
+  M   [lane][4 bf16]                 M[l%16][4 (l/16) + j]  (at 96 KT bytes)
+  GAM [KT fp32]                      chunk decay per key channel (512 bytes on)
+and the whole padded to a multiple of 1 KB (13312 bytes at KT = 128, 26624
+at 256).  state_chan is the state-row order of the scan's accumulator
+tiles.
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-REC = 27648
-CS = 32
+CS = 16
+
+
+def rec_bytes(KT=128):
+    return (96 * KT + 512 + 4 * KT + 1023) // 1024 * 1024
+
+
+REC = rec_bytes(128)
 
 
 def state_chan(t, rho):
     return 32 * (t // 2) + 8 * (rho // 4) + 4 * (t % 2) + rho % 4
-
-
-def tau(kappa):
-    """Token of k index kappa in the W^T and M operands."""
-    g, i = kappa // 8, kappa % 8
-    return 4 * g + i if i < 4 else 16 + 4 * g + i - 4
 
 
 def bf16_words_to_f64(u16: np.ndarray) -> np.ndarray:
@@ -49,53 +47,54 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return bf16_words_to_f64(to_bf16_words(x)).reshape(np.shape(x))
 
 
-def decode(rec: np.ndarray):
-    """One 27648-byte record -> (Kt, Qt, W, M, gamma) in natural layout."""
+def _offsets(KT):
+    q = 32 * KT                     # bytes of one 16 x KT bf16 operand
+    return 0, q, 2 * q, 3 * q, 3 * q + 512
+
+
+def decode(rec: np.ndarray, KT=128):
+    """One record -> (Kt, Qt, W [16, KT], M [16, 16], gamma [KT])."""
+    o_kt, o_qt, o_wt, o_m, o_g = _offsets(KT)
+    nkb = KT // 32
     u16 = rec.view(np.uint16)
-    kt = bf16_words_to_f64(u16[0:4096]).reshape(4, 2, 64, 8)
-    qt = bf16_words_to_f64(u16[4096:8192]).reshape(4, 2, 64, 8)
-    wt = bf16_words_to_f64(u16[8192:12288]).reshape(8, 64, 8)
-    mm = bf16_words_to_f64(u16[12288:13312]).reshape(2, 64, 8)
-    Kt = np.zeros((CS, 128)); Qt = np.zeros((CS, 128)); W = np.zeros((CS, 128))
+    kt = bf16_words_to_f64(u16[o_kt // 2:o_qt // 2]).reshape(nkb, 64, 8)
+    qt = bf16_words_to_f64(u16[o_qt // 2:o_wt // 2]).reshape(nkb, 64, 8)
+    wt = bf16_words_to_f64(u16[o_wt // 2:o_m // 2]).reshape(nkb, 64, 8)
+    mm = bf16_words_to_f64(u16[o_m // 2:o_g // 2]).reshape(64, 4)
+    Kt = np.zeros((CS, KT)); Qt = np.zeros((CS, KT)); W = np.zeros((CS, KT))
     M = np.zeros((CS, CS))
     for l in range(64):
         r, grp = l % 16, l // 16
-        for kb in range(4):
-            for rt in range(2):
-                Kt[16 * rt + r, 32 * kb + 8 * grp: 32 * kb + 8 * grp + 8] = kt[kb, rt, l]
-                Qt[16 * rt + r, 32 * kb + 8 * grp: 32 * kb + 8 * grp + 8] = qt[kb, rt, l]
-        for i in range(8):
-            tok = tau(8 * grp + i)
-            for t in range(8):
-                W[tok, state_chan(t, r)] = wt[t, l, i]
-            for rt in range(2):
-                M[16 * rt + r, tok] = mm[rt, l, i]
-    gam = rec[26624:27136].view(np.float32).astype(np.float64)
+        for kb in range(nkb):
+            Kt[r, 32 * kb + 8 * grp: 32 * kb + 8 * grp + 8] = kt[kb, l]
+            Qt[r, 32 * kb + 8 * grp: 32 * kb + 8 * grp + 8] = qt[kb, l]
+            for h in range(2):
+                W[4 * grp: 4 * grp + 4, state_chan(2 * kb + h, r)] = wt[kb, l, 4 * h: 4 * h + 4]
+        M[r, 4 * grp: 4 * grp + 4] = mm[l]
+    gam = rec[o_g:o_g + 4 * KT].view(np.float32).astype(np.float64)
     return Kt, Qt, W, M, gam
 
 
-def encode(Kt, Qt, W, M, gam) -> np.ndarray:
-    """(Kt, Qt, W [32 x 128], M [32 x 32], gamma [128]) -> one record; the
+def encode(Kt, Qt, W, M, gam, KT=128) -> np.ndarray:
+    """(Kt, Qt, W [16, KT], M [16, 16], gamma [KT]) -> one record; the
     matrices are rounded to bf16, gamma to fp32."""
-    kt = np.zeros((4, 2, 64, 8)); qt = np.zeros((4, 2, 64, 8))
-    wt = np.zeros((8, 64, 8)); mm = np.zeros((2, 64, 8))
+    o_kt, o_qt, o_wt, o_m, o_g = _offsets(KT)
+    nkb = KT // 32
+    kt = np.zeros((nkb, 64, 8)); qt = np.zeros((nkb, 64, 8)); wt = np.zeros((nkb, 64, 8))
+    mm = np.zeros((64, 4))
     for l in range(64):
         r, grp = l % 16, l // 16
-        for kb in range(4):
-            for rt in range(2):
-                kt[kb, rt, l] = Kt[16 * rt + r, 32 * kb + 8 * grp: 32 * kb + 8 * grp + 8]
-                qt[kb, rt, l] = Qt[16 * rt + r, 32 * kb + 8 * grp: 32 * kb + 8 * grp + 8]
-        for i in range(8):
-            tok = tau(8 * grp + i)
-            for t in range(8):
-                wt[t, l, i] = W[tok, state_chan(t, r)]
-            for rt in range(2):
-                mm[rt, l, i] = M[16 * rt + r, tok]
-    rec = np.zeros(REC, dtype=np.uint8)
+        for kb in range(nkb):
+            kt[kb, l] = Kt[r, 32 * kb + 8 * grp: 32 * kb + 8 * grp + 8]
+            qt[kb, l] = Qt[r, 32 * kb + 8 * grp: 32 * kb + 8 * grp + 8]
+            for h in range(2):
+                wt[kb, l, 4 * h: 4 * h + 4] = W[4 * grp: 4 * grp + 4, state_chan(2 * kb + h, r)]
+        mm[l] = M[r, 4 * grp: 4 * grp + 4]
+    rec = np.zeros(rec_bytes(KT), dtype=np.uint8)
     u16 = rec.view(np.uint16)
-    u16[0:4096] = to_bf16_words(kt.ravel())
-    u16[4096:8192] = to_bf16_words(qt.ravel())
-    u16[8192:12288] = to_bf16_words(wt.ravel())
-    u16[12288:13312] = to_bf16_words(mm.ravel())
-    rec[26624:27136] = np.asarray(gam, dtype=np.float32).view(np.uint8)
+    u16[o_kt // 2:o_qt // 2] = to_bf16_words(kt.ravel())
+    u16[o_qt // 2:o_wt // 2] = to_bf16_words(qt.ravel())
+    u16[o_wt // 2:o_m // 2] = to_bf16_words(wt.ravel())
+    u16[o_m // 2:o_g // 2] = to_bf16_words(mm.ravel())
+    rec[o_g:o_g + 4 * KT] = np.asarray(gam, dtype=np.float32).view(np.uint8)
     return rec

@@ -52,7 +52,7 @@ def test_status_strings(lib):
 
 
 def test_constants(lib):
-    assert kda.chunk_size() == 32
+    assert kda.chunk_size() == 16
     lb = kda.lower_bound_min()
     # 16 tokens at the bound keep 2^(+-G) inside the fp32 normal range
     assert -5.5 < lb <= -5.0
@@ -60,14 +60,14 @@ def test_constants(lib):
 
 
 def test_workspace_size(lib):
-    # 32-token chunks with 27 KB records at K = 64 and 128
-    assert kda.workspace_size(1, 8192, 96, 1) == (8192 // 32 + 1) * 96 * 27648
-    assert kda.workspace_size(1, 8192, 96, 12) == (8192 // 32 + 12) * 96 * 27648
-    assert kda.workspace_size(3, 37, 2, 3) == (111 // 32 + 3) * 2 * 27648
+    # 16-token chunks with 13 KB records at K = 64 and 128
+    assert kda.workspace_size(1, 8192, 96, 1) == (8192 // 16 + 1) * 96 * 13312
+    assert kda.workspace_size(1, 8192, 96, 12) == (8192 // 16 + 12) * 96 * 13312
+    assert kda.workspace_size(3, 37, 2, 3) == (111 // 16 + 3) * 2 * 13312
     assert kda.workspace_size(0, 16, 1, 1) == 0
     assert kda.workspace_size(1, 16, 1, 0) == 0
     # head dimension 64 shares the 128-wide records; 256 takes 26 KB ones
-    assert kda.workspace_size(1, 8192, 96, 1, K=64) == (8192 // 32 + 1) * 96 * 27648
+    assert kda.workspace_size(1, 8192, 96, 1, K=64) == (8192 // 16 + 1) * 96 * 13312
     assert kda.workspace_size(1, 8192, 96, 1, K=256) == (8192 // 16 + 1) * 96 * 26624
     assert kda.workspace_size(1, 8192, 96, 1, K=96) == 0
     assert lib.kda_workspace_size(1, 100, 3, 1) == kda.workspace_size(1, 100, 3, 1, K=128)
@@ -104,7 +104,7 @@ def call_fwd(lib, entry="kda_fwd", **over):
     (dict(lb=0.5), INVALID), (dict(lb=-6.0), UNSUPPORTED), (dict(lb=-100.0), UNSUPPORTED),
     (dict(B=2, N=2, T=2 ** 30 + 1), UNSUPPORTED),       # token rows overflow int32
     (dict(H=2 ** 26), UNSUPPORTED),                     # (sequence, head) units overflow the grid
-    (dict(H=2 ** 18), UNSUPPORTED),                     # 32-row byte offsets overflow int32
+    (dict(H=2 ** 19), UNSUPPORTED),                     # 16-row byte offsets overflow int32
     (dict(T=2 ** 26, H=1024), UNSUPPORTED),             # (chunk slot, head) pairs overflow the grid
 ])
 def test_fwd_rejects_before_any_hip_call(lib, over, code):

@@ -1,10 +1,11 @@
 """Stage parity of the inter-chunk scan alone, through kda_debug_scan_step.
 
-Per 32-token chunk with incoming state S (key channels x value channels)
+Per 16-token chunk with incoming state S (key channels x value channels)
 the scan computes X = V - Kt S, O = scale (Qt S + M X) and the new state
 diag(gamma) S + W^T X ("Moonshot AI Open-Sources FlashKDA", section "Why
 KDA?": the chunkwise form).  Two checks, each at every column-part width the
-launch can pick (32, 64, 128 columns per workgroup; 32 and 64 at K = V = 64):
+launch can pick (32, 64, 128 columns per workgroup; 32 and 64 at K = V = 64)
+and at head dimensions 64, 128 and 256:
 
   * Records the test encodes itself (random bf16 operands, zero rows past
     the chunk's length as the intra stage writes them) against fp64 maths
@@ -33,24 +34,31 @@ def rel(a, b):
     return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
 
 
-WIDTHS = [(128, 32), (128, 64), (128, 128), (64, 32), (64, 64)]
+WIDTHS = [(128, 32), (128, 64), (128, 128), (64, 32), (64, 64), (256, 32), (256, 64), (256, 128)]
+LENGTHS = [16, 9, 1]
+
+
+def tile(D):
+    """Key channels of the record tiles at head dimension D."""
+    return 256 if D == 256 else 128
 
 
 def test_record_codec_round_trip():
     """encode and decode are inverse on bf16-exact operands (CPU)."""
     rng = np.random.default_rng(0)
-    Kt, Qt, W = (bf16_round(rng.normal(size=(CS, 128))) for _ in range(3))
-    M = bf16_round(rng.normal(size=(CS, CS)))
-    gam = rng.random(128).astype(np.float32)
-    out = decode(encode(Kt, Qt, W, M, gam))
-    for x, y in zip(out, (Kt, Qt, W, M, gam.astype(np.float64))):
-        assert np.array_equal(x, y)
+    for KT in (128, 256):
+        Kt, Qt, W = (bf16_round(rng.normal(size=(CS, KT))) for _ in range(3))
+        M = bf16_round(rng.normal(size=(CS, CS)))
+        gam = rng.random(KT).astype(np.float32)
+        out = decode(encode(Kt, Qt, W, M, gam, KT=KT), KT)
+        for x, y in zip(out, (Kt, Qt, W, M, gam.astype(np.float64))):
+            assert np.array_equal(x, y)
 
 
 def chunk_operands(rng, H, D, n, exact):
-    """Per head: Kt, Qt, W [32, 128] and M [32, 32] (rows, and M's columns,
+    """Per head: Kt, Qt, W [16, KT] and M [16, 16] (rows, and M's columns,
     past n zero as the intra stage writes them; channels past D zero), gamma
-    [128] in (0.05, 1], S0 [D, D] and v [n, D].
+    [KT] in (0.05, 1], S0 [D, D] and v [n, D] (KT = tile(D)).
 
     exact: quantised values whose products and partial sums are all exact in
     fp32 (Kt, Qt, W, M in {-2..2}/8, S0 in {0, +-1/8, +-1/4, +-1/2}, v in
@@ -61,9 +69,10 @@ def chunk_operands(rng, H, D, n, exact):
     the final sum of the update rounds).  Otherwise: random normal values
     rounded to bf16."""
     ops = []
+    KT = tile(D)
     for _ in range(H):
-        Kt = np.zeros((CS, 128)); Qt = np.zeros((CS, 128)); W = np.zeros((CS, 128))
-        M = np.zeros((CS, CS)); gam = np.zeros(128)
+        Kt = np.zeros((CS, KT)); Qt = np.zeros((CS, KT)); W = np.zeros((CS, KT))
+        M = np.zeros((CS, CS)); gam = np.zeros(KT)
         if exact:
             q8 = lambda shape: rng.integers(-2, 3, size=shape) / 8.0
             Kt[:n, :D], Qt[:n, :D], W[:n, :D] = q8((n, D)), q8((n, D)), q8((n, D))
@@ -83,7 +92,7 @@ def chunk_operands(rng, H, D, n, exact):
 
 def run_scan_step(ops, D, n, scale, cw):
     H = len(ops)
-    rec = np.stack([encode(*o[:5]) for o in ops])              # [H, REC]: chunk slot 0
+    rec = np.stack([encode(*o[:5], KT=tile(D)) for o in ops])   # [H, bytes]: chunk slot 0
     need = int(kda.load().kda_record_workspace_size(1, n, H, 1, D))
     recs = torch.zeros(max(need, rec.size), dtype=torch.uint8)
     recs[:rec.size] = torch.from_numpy(rec.reshape(-1))
@@ -99,7 +108,7 @@ def run_scan_step(ops, D, n, scale, cw):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("D,cw", WIDTHS)
-@pytest.mark.parametrize("n", [32, 19, 1])
+@pytest.mark.parametrize("n", LENGTHS)
 def test_scan_step_exact_operands(D, cw, n):
     """Quantised records: output bitwise, new state within 4 fp32 ulps of
     the magnitudes summed."""
@@ -119,7 +128,7 @@ def test_scan_step_exact_operands(D, cw, n):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("D,cw", WIDTHS)
-@pytest.mark.parametrize("n", [32, 19, 1])
+@pytest.mark.parametrize("n", LENGTHS)
 def test_scan_step_random_operands(D, cw, n):
     """Random bf16 records against exact fp64 maths, to the parity bar."""
     H, scale = 3, D ** -0.5
@@ -137,7 +146,7 @@ def test_scan_step_random_operands(D, cw, n):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("D,cw", WIDTHS)
-@pytest.mark.parametrize("n", [32, 19, 1])
+@pytest.mark.parametrize("n", LENGTHS)
 def test_one_chunk_intra_then_scan_step(D, cw, n):
     """kda_debug_intra then kda_debug_scan_step on one chunk from an fp32
     state, against the dense one-block formula."""
@@ -167,7 +176,7 @@ def test_one_chunk_intra_then_scan_step(D, cw, n):
 
 @pytest.mark.gpu
 def test_scan_step_rejects_bad_width():
-    v = torch.zeros(1, 32, 2, 64, dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros(1, 16, 2, 64, dtype=torch.bfloat16, device="cuda")
     recs = torch.zeros(REC * 2 * 2, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(v)
     for cw in (16, 128, 96):
