@@ -23,13 +23,16 @@
 // a = max(-exp(A_log) softplus(g + dt_bias), lower_bound) then yields dg,
 // dA_log and ddt_bias (no gradient through the clamped branch).
 //
-// Five launches, all fp32 arithmetic:
-//   prep    (chunk slot, head)  the chunk factors Kt, Qt, Wm, M, Gam -> workspace
+// Five launches:
+//   prep    (chunk slot, head)  the chunk factors in fp32: Kt and Wm (with the
+//           chunk decay) for the states scan, and the reverse scan's bf16
+//           record (Wm, scale Qt, -Kt, scale M^T in MFMA operand layouts)
 //   states  (sequence, head, four 16-column parts)  forward scan storing
-//           every chunk's start state S0 and X
-//   dstates (sequence, head, four 16-column parts)  reverse scan of dS,
-//           storing every chunk's dS1 and dX, writing dv and the
-//           initial-state gradient
+//           every chunk's start state S0 and X (fp32 16x16x4 MFMA)
+//   rscan   (sequence, head, column part)  reverse scan of dS on the forward
+//           scan's structure (kda_scan.hip: bf16 MFMA operands, fp32
+//           accumulators), storing every chunk's dS1 (bf16) and dX,
+//           writing dv and the initial-state gradient
 //   chunk   (chunk slot, head)  the products with S0 / dS1 (fp32 MFMA) and
 //           the in-chunk backward: dq, dk, dg, dbeta, per-chunk dA_log /
 //           ddt_bias sums
@@ -48,21 +51,8 @@ namespace {
 constexpr int BT = 256;               // threads per workgroup
 constexpr int RS = HD + 4;            // padded LDS row stride (floats)
 constexpr int SP = CS + 1;            // padded stride of 16 x 16 tiles
-constexpr int CWB = 16;               // state columns per scan workgroup
+constexpr int CWB = 16;               // state columns of one stored part
 constexpr int NPART = HD / CWB;
-constexpr int NRG = BT / CWB;         // row groups of the state rows
-constexpr int RPT = HD / NRG;         // state rows per thread
-static_assert(NRG == CS && NRG * RPT == HD, "row groups cover the state rows, one per token row");
-
-// Chunk-factor record, fp32, per (chunk slot, head): Kt, Wm and Qt
-// transposed ([channel][token], 16 floats per channel), M [16][16] and
-// e^{G_last} [128].
-constexpr int BR_KT = 0;
-constexpr int BR_WM = CS * HD;       // next to Kt^T: the states kernel reads the two as one span
-constexpr int BR_QT = 2 * CS * HD;
-constexpr int BR_M = 3 * CS * HD;
-constexpr int BR_GAM = 3 * CS * HD + CS * CS;
-constexpr int BR_FLOATS = BR_GAM + HD;
 
 // The transcendentals on the hardware base-2 units (v_exp_f32, v_log_f32,
 // v_rcp_f32).  softplus keeps the form max(x, 0) + log(1 + e^-|x|), finite
@@ -253,13 +243,22 @@ __device__ __forceinline__ void chunk_factors(FL &L, const uint16_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
-// prep: chunk factors -> workspace record (fp32, BR_FLOATS per slot x head)
+// prep: the chunk factors in fp32, into the two scans' bf16 records (in the
+// forward record's MFMA operand layouts, RecLayout<HD>):
+//   states record (StatesRec): Kt and Wm = P^T Kb Gam as (hi, lo) bf16
+//     pairs in the Kt and W^T layouts, and the chunk decay, the operands of
+//     X = V - Kt S0 and S1 = Gam S0 + Wm^T X;
+//   reverse record: Wm as the A operand of Wm dS (the Kt slot), scale Qt
+//     and -Kt transposed as the A operands of the state-gradient update (the
+//     Qt and W^T slots, both in the W^T layout), scale M^T (the M slot) and
+//     the chunk decay.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(BT) void bwd_prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
-    const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb,
-    const int32_t *__restrict__ cu, int N, int T, int H, int kd, float *__restrict__ brec)
+    const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb, float scale,
+    const int32_t *__restrict__ cu, int N, int T, int H, int kd, uint8_t *__restrict__ srec,
+    uint8_t *__restrict__ rrec)
 {
     __shared__ __attribute__((aligned(16))) Factors L;
     const int64_t slot = blockIdx.x / (unsigned)H;
@@ -268,356 +267,40 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(
     const int len = slot_chunk(cu, N, T, slot, t0);
     if (len == 0) return;                                   // gap slot
     chunk_factors<true>(L, q, k, g, beta, expf(A_log[h]), dt_bias, lb, t0, len, H, h, kd);
-    float *rec = brec + ((size_t)slot * H + h) * BR_FLOATS;
     const int tid = threadIdx.x;
-    for (int idx = tid; idx < CS * HD; idx += BT) {
-        const int c = idx / CS, r = idx % CS;
-        rec[BR_KT + idx] = L.kt[r][c];
-        rec[BR_QT + idx] = L.qt[r][c];
-        rec[BR_WM + idx] = L.wm[r][c];
+
+    typedef RecLayout<HD> R;
+    typedef StatesRec SR;
+    uint8_t *sr = srec + ((size_t)slot * H + h) * SR::BYTES;
+    uint8_t *rr = rrec + ((size_t)slot * H + h) * R::BYTES;
+    uint16_t *s_kt = (uint16_t *)(sr + SR::KTH), *s_ktl = (uint16_t *)(sr + SR::KTL);
+    uint16_t *s_wt = (uint16_t *)(sr + SR::WTH), *s_wtl = (uint16_t *)(sr + SR::WTL);
+    uint16_t *r_kt = (uint16_t *)(rr + R::KTO), *r_qt = (uint16_t *)(rr + R::QT);
+    uint16_t *r_wt = (uint16_t *)(rr + R::WT), *r_m = (uint16_t *)(rr + R::M);
+    // Kt slot: element (kb, lane l, i) = X[l%16][32 kb + 8 (l/16) + i]
+    // W^T-layout slots: element (tp, lane l, 4 hf + j) = X[4 (l/16) + j][chan(2 tp + hf, l%16)]
+    for (int e = tid; e < 4 * 64 * 8; e += BT) {
+        const int kb = e >> 9, l = (e >> 3) & 63, i = e & 7;
+        const int ck = 32 * kb + 8 * (l >> 4) + i;
+        const float ktv = L.kt[l & 15][ck];
+        s_kt[e] = tobf16(ktv);
+        s_ktl[e] = tobf16(ktv - bf16f(s_kt[e]));
+        r_kt[e] = tobf16(L.wm[l & 15][ck]);
+        const int tok = 4 * (l >> 4) + (i & 3), ch = state_chan(2 * kb + (i >> 2), l & 15);
+        const float wmv = L.wm[tok][ch];
+        s_wt[e] = tobf16(wmv);
+        s_wtl[e] = tobf16(wmv - bf16f(s_wt[e]));
+        r_qt[e] = tobf16(scale * L.qt[tok][ch]);
+        r_wt[e] = tobf16(-L.kt[tok][ch]);
     }
-    rec[BR_M + tid] = L.M[tid >> 4][tid & 15];
-    if (tid < HD) rec[BR_GAM + tid] = L.gam[tid];
+    // M slot: element (lane l, j) = scale M[4 (l/16) + j][l%16]
+    r_m[tid] = tobf16(scale * L.M[4 * ((tid >> 2) >> 4) + (tid & 3)][(tid >> 2) & 15]);
+    if (tid < HD) {
+        ((float *)(sr + SR::GAM))[tid] = L.gam[tid];
+        ((float *)(rr + R::GAM))[tid] = L.gam[tid];
+    }
 }
 
-// Compute units of the current device (cached per device).
-int bwd_num_cus() {
-    static int cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
-// ---------------------------------------------------------------------------
-// The two scans run on 16-column parts of the state, four parts (1,024
-// threads; two workgroups per (sequence, head)) or two parts (512 threads)
-// per workgroup.  Each part's four waves hold its 128 x 16 state slice in
-// MFMA accumulator layout; the parts share one LDS copy of each chunk's
-// factors, whose record is
-// loaded into registers while the previous chunk computes (software
-// pipelining).  The factors are kept transposed ([channel][token]).
-//
-// Stored states (S0 and dS1 of every chunk; written with non-temporal
-// stores, which measured faster for both scans), per (slot, head): one 1 KiB
-// piece per (16-column part p, 16-row tile t) at float offset
-// (8 p + t) * 256, holding rows 16t + 4g + jj, columns 16p + n at
-// 64 jj + 16 g + n: the scans' accumulator order, so that each store
-// instruction of a wave writes 256 contiguous bytes.  X and dX of every
-// chunk are stored as [16][V] fp32.
-// ---------------------------------------------------------------------------
-// Float offset of (part, row tile t, step jj, lane l) in a stored state.
-__device__ __forceinline__ size_t state_acc_off(int part, int t, int jj, int l) {
-    return ((size_t)part * (HD / 16) + t) * 256 + jj * 64 + l;
-}
-
-// ---------------------------------------------------------------------------
-// states: forward scan that stores each chunk's start state S0 and X.
-// ---------------------------------------------------------------------------
-// PG 16-column parts per workgroup (256 threads each), sharing one LDS copy
-// of each chunk's factors, so the record is read once per PG parts.
-template <int PG>
-__global__ __launch_bounds__(BT * PG) void bwd_states_kernel(
-    const uint16_t *__restrict__ v, const float *__restrict__ brec,
-    const int32_t *__restrict__ cu, int N, int T, int H, int kd,
-    const void *__restrict__ init, int init_fp32, float *__restrict__ st0,
-    float *__restrict__ xws)
-{
-    // The recurrence on fp32 16x16x4 MFMAs, in the layout of the dstates
-    // kernel: wave w of a part holds state row tiles 2w and 2w+1 (lane l:
-    // rows 16t + 4(l/16) + jj of column l%16), and the k-steps of a
-    // contraction take rows (or tokens) 4g + jj from lane group g in step jj.
-    constexpr int NG = NPART / PG;                    // workgroups per (sequence, head)
-    constexpr int NF = 2 * CS * HD / 4 / (BT * PG);   // 16-byte factor loads per thread
-    static_assert(NPART % PG == 0 && (NF == 1 || NF == 2) && NF * BT * PG * 4 == 2 * CS * HD,
-                  "one or two 16-byte factor loads per thread cover Kt and Wm");
-    __shared__ __attribute__((aligned(16))) float fac[2][HD][CS];   // Kt^T, Wm^T
-    __shared__ __attribute__((aligned(16))) float gam[HD];
-    __shared__ float vv[PG][CS][CWB];
-    __shared__ f32x4_t xpw[PG][BT / 64][64];         // per-wave partial Kt S0
-    float(&ktT)[HD][CS] = fac[0];
-    float(&wmT)[HD][CS] = fac[1];
-    // Block b -> ((sequence, head) unit, part group): the groups of a unit
-    // share b mod 8, so they run on one XCD and read the chunk factors
-    // through one L2
-    const int b = blockIdx.x;
-    const int nh = 8 * (b / (8 * NG)) + (b & 7);
-    const int grp = (b >> 3) % NG;
-    if (nh >= N * H) return;                          // block-uniform
-    const int h = nh % H, n = nh / H;
-    const int tid = threadIdx.x, sub = tid / BT, ptid = tid % BT;
-    const int part = grp * PG + sub;
-    const int j = ptid % CWB;
-    const int wave = ptid >> 6, l = ptid & 63, g = l >> 4;
-    const int col = part * CWB + j;                  // j == l % 16
-    const bool colv = col < kd;                      // columns from kd on are zeros
-    const size_t sbase = ((size_t)n * H + h) * kd * kd;
-
-    f32x4_t sa[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int row = 16 * (2 * wave + tt) + 4 * g + jj;
-            const size_t idx = sbase + (size_t)row * kd + col;
-            sa[tt][jj] = (!init || !colv || row >= kd) ? 0.f
-                       : init_fp32 ? ((const float *)init)[idx] : bf16f(((const uint16_t *)init)[idx]);
-        }
-    int64_t start, end;
-    seq_range(cu, n, T, start, end);
-    const int nch = (int)((end - start + CS - 1) / CS);
-    const int64_t slot0 = seq_slot0(cu, n, T);
-
-    // next chunk's Kt^T and Wm^T (16-byte pieces tid and, with two parts per
-    // workgroup, tid + BT PG of the two blocks, which lie next to each other
-    // in the record; named registers, not an array), e^{G_last} and v
-    // element, in flight (the v element is loaded raw from a clamped row and
-    // masked at use, so no branch forces a wait on the loads in flight)
-    static_assert(BR_WM == BR_KT + CS * HD, "Kt^T and Wm^T adjacent in the record");
-    float4 pf, pf1, pg = {0.f, 0.f, 0.f, 0.f};
-    uint16_t pd = 0;
-    bool pvalid = false;
-#define KDA_STATES_FETCH(ci_)                                                                 \
-    do {                                                                                      \
-        const float *rec_ = brec + ((size_t)(slot0 + (ci_)) * H + h) * BR_FLOATS;             \
-        pf = *(const float4 *)&rec_[BR_KT + 4 * tid];                                         \
-        if constexpr (NF == 2) pf1 = *(const float4 *)&rec_[BR_KT + 4 * (tid + BT * PG)];     \
-        if (tid < HD / 4) pg = *(const float4 *)&rec_[BR_GAM + 4 * tid];                      \
-        const int64_t tr_ = start + (int64_t)(ci_) * CS + ptid / CWB;                         \
-        pvalid = tr_ < end && colv;                                                           \
-        pd = v[((size_t)min(tr_, end - 1) * H + h) * kd + (colv ? col : 0)];                  \
-    } while (0)
-    if (nch > 0) KDA_STATES_FETCH(0);
-    for (int ci = 0; ci < nch; ++ci) {
-        const size_t sh = (size_t)(slot0 + ci) * H + h;
-        float *dst = st0 + sh * HD * HD;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                __builtin_nontemporal_store(sa[tt][jj], &dst[state_acc_off(part, 2 * wave + tt, jj, l)]);
-        __syncthreads();                                // last chunk's readers are done
-        *(float4 *)&fac[(4 * tid) / (CS * HD)][((4 * tid) % (CS * HD)) / CS][(4 * tid) % CS] = pf;
-        if constexpr (NF == 2) {
-            const int e1 = 4 * (tid + BT * PG);
-            *(float4 *)&fac[e1 / (CS * HD)][(e1 % (CS * HD)) / CS][e1 % CS] = pf1;
-        }
-        if (tid < HD / 4) *(float4 *)&gam[4 * tid] = pg;
-        vv[sub][ptid / CWB][j] = pvalid ? bf16f(pd) : 0.f;
-        if (ci + 1 < nch) KDA_STATES_FETCH(ci + 1);     // in flight during this chunk
-        __syncthreads();
-        // X = V - Kt S0: this wave's rows of Kt S0 (A: Kt token l%16,
-        // channel 16t + 4g + jj; B: the state registers)
-        {
-            f32x4_t xpart = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    xpart = mfma_k4(ktT[16 * (2 * wave + tt) + 4 * g + jj][l & 15], sa[tt][jj], xpart);
-            xpw[sub][wave][l] = xpart;
-        }
-        __syncthreads();
-        // every wave of the part forms the same X in the same order: lane l
-        // holds tokens 4g + jj of column l%16
-        f32x4_t X;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) X[jj] = vv[sub][4 * g + jj][l & 15];
-        X -= xpw[sub][0][l];
-        X -= xpw[sub][1][l];
-        X -= xpw[sub][2][l];
-        X -= xpw[sub][3][l];
-        if (wave == 0) {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                xws[sh * CS * HD + (size_t)(4 * g + jj) * HD + col] = X[jj];
-        }
-        // S1 = Gam S0 + Wm^T X, per row tile (A: Wm^T row 16t + l%16,
-        // token 4g + jj; B: X token 4g + jj)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int t = 2 * wave + tt;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) sa[tt][jj] *= gam[16 * t + 4 * g + jj];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                sa[tt] = mfma_k4(wmT[16 * t + (l & 15)][4 * g + jj], X[jj], sa[tt]);
-        }
-    }
-#undef KDA_STATES_FETCH
-}
-
-// ---------------------------------------------------------------------------
-// dstates: reverse scan of the state gradient.  Stores dS1 and dX of every
-// chunk, writes dv and, at the sequence start, the initial-state gradient.
-// ---------------------------------------------------------------------------
-template <int PG>
-__global__ __launch_bounds__(BT * PG) void bwd_dstates_kernel(
-    const uint16_t *__restrict__ dout, const float *__restrict__ brec,
-    const int32_t *__restrict__ cu, int N, int T, int H, int kd, float scale,
-    const float *__restrict__ dfin, float *__restrict__ dst1, float *__restrict__ dxws,
-    uint16_t *__restrict__ dv, float *__restrict__ dinit)
-{
-    // The recurrence on fp32 16x16x4 MFMAs.  Wave w holds state row tiles
-    // 2w and 2w+1 of the part's 16 columns in accumulator layout: lane l has
-    // rows 16t + 4(l/16) + jj (jj = 0..3) of column l%16.  A contraction over
-    // the 16 rows of a tile runs as four k-steps, step jj taking rows
-    // 4g + jj from lane group g = l/16, so the accumulator registers are the
-    // B operand as they stand; the same holds for contractions over the 16
-    // tokens of dX.
-    // PG 16-column parts per workgroup (256 threads each) share one LDS copy
-    // of the chunk's record (same layout as in memory).
-    constexpr int NG = NPART / PG;                    // workgroups per (sequence, head)
-    constexpr int NREC = BR_FLOATS / 4;               // 16-byte pieces of a record
-    constexpr int NL = (NREC + BT * PG - 1) / (BT * PG);  // 16-byte loads per thread (2 or 4)
-    static_assert(NPART % PG == 0 && BR_FLOATS % 4 == 0 && (NL == 2 || NL == 4),
-                  "two (four parts) or four (two parts) 16-byte loads per thread cover the record");
-    __shared__ __attribute__((aligned(16))) float recl[BR_FLOATS];
-    __shared__ float dol[PG][CS][CWB];
-    __shared__ f32x4_t xpw[PG][BT / 64][64];         // per-wave partial Wm dS1
-    const auto ktT = reinterpret_cast<const float (*)[CS]>(&recl[BR_KT]);
-    const auto wmT = reinterpret_cast<const float (*)[CS]>(&recl[BR_WM]);
-    const auto qtT = reinterpret_cast<const float (*)[CS]>(&recl[BR_QT]);
-    const auto Ml = reinterpret_cast<const float (*)[CS]>(&recl[BR_M]);
-    const float *gam = &recl[BR_GAM];
-    // Block b -> ((sequence, head) unit, part group): the groups of a unit
-    // share b mod 8, so they run on one XCD and read the chunk factors
-    // through one L2
-    const int b = blockIdx.x;
-    const int nh = 8 * (b / (8 * NG)) + (b & 7);
-    const int grp = (b >> 3) % NG;
-    if (nh >= N * H) return;                          // block-uniform
-    const int h = nh % H, n = nh / H;
-    const int tid = threadIdx.x, sub = tid / BT, ptid = tid % BT;
-    const int part = grp * PG + sub;
-    const int j = ptid % CWB;
-    const int wave = ptid >> 6, l = ptid & 63, g = l >> 4;
-    const int col = part * CWB + j;                  // j == l % 16
-    const bool colv = col < kd;                      // columns from kd on are zeros
-    const size_t sbase = ((size_t)n * H + h) * kd * kd;
-
-    f32x4_t dsa[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int row = 16 * (2 * wave + tt) + 4 * g + jj;
-            dsa[tt][jj] = (dfin && colv && row < kd) ? dfin[sbase + (size_t)row * kd + col] : 0.f;
-        }
-    int64_t start, end;
-    seq_range(cu, n, T, start, end);
-    const int nch = (int)((end - start + CS - 1) / CS);
-    const int64_t slot0 = seq_slot0(cu, n, T);
-
-    // next chunk's record (16-byte pieces tid + m BT PG, m < NL, the last
-    // partly; named registers, not an array) and dO element, in flight
-    const float4 z4 = {0.f, 0.f, 0.f, 0.f};
-    float4 pr0 = z4, pr1 = z4, pr2 = z4, pr3 = z4;
-    const bool lastv = tid + (NL - 1) * BT * PG < NREC;   // this thread's last piece exists
-    uint16_t pd = 0;
-    bool pvalid = false;
-#define KDA_DSTATES_FETCH(ci_)                                                                \
-    do {                                                                                      \
-        const float *rec_ = brec + ((size_t)(slot0 + (ci_)) * H + h) * BR_FLOATS;             \
-        pr0 = *(const float4 *)&rec_[4 * tid];                                                \
-        if constexpr (NL == 2) {                                                              \
-            if (lastv) pr1 = *(const float4 *)&rec_[4 * (tid + BT * PG)];                     \
-        } else {                                                                              \
-            pr1 = *(const float4 *)&rec_[4 * (tid + BT * PG)];                                \
-            pr2 = *(const float4 *)&rec_[4 * (tid + 2 * BT * PG)];                            \
-            if (lastv) pr3 = *(const float4 *)&rec_[4 * (tid + 3 * BT * PG)];                 \
-        }                                                                                     \
-        const int64_t tr_ = start + (int64_t)(ci_) * CS + ptid / CWB;                         \
-        pvalid = tr_ < end && colv;                                                           \
-        pd = dout[((size_t)min(tr_, end - 1) * H + h) * kd + (colv ? col : 0)];               \
-    } while (0)
-    if (nch > 0) KDA_DSTATES_FETCH(nch - 1);
-    for (int ci = nch - 1; ci >= 0; --ci) {
-        const size_t sh = (size_t)(slot0 + ci) * H + h;
-        float *dst = dst1 + sh * HD * HD;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                __builtin_nontemporal_store(dsa[tt][jj], &dst[state_acc_off(part, 2 * wave + tt, jj, l)]);
-        const int64_t t0 = start + (int64_t)ci * CS;
-        const int len = (int)min((int64_t)CS, end - t0);
-        __syncthreads();
-        *(float4 *)&recl[4 * tid] = pr0;
-        if constexpr (NL == 2) {
-            if (lastv) *(float4 *)&recl[4 * (tid + BT * PG)] = pr1;
-        } else {
-            *(float4 *)&recl[4 * (tid + BT * PG)] = pr1;
-            *(float4 *)&recl[4 * (tid + 2 * BT * PG)] = pr2;
-            if (lastv) *(float4 *)&recl[4 * (tid + 3 * BT * PG)] = pr3;
-        }
-        dol[sub][ptid / CWB][j] = pvalid ? scale * bf16f(pd) : 0.f;
-        if (ci > 0) KDA_DSTATES_FETCH(ci - 1);          // in flight during this chunk
-        __syncthreads();
-        // dX = scale M^T dO + Wm dS1: this wave's rows of Wm dS1 (A: Wm
-        // row l%16, column 16t + 4g + jj), then scale M^T dO (A: M^T row
-        // l%16, token 4ks + g; B: scale dO token 4ks + g)
-        {
-            const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-            f32x4_t xpart = zero;
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    xpart = mfma_k4(wmT[16 * (2 * wave + tt) + 4 * g + jj][l & 15], dsa[tt][jj], xpart);
-            xpw[sub][wave][l] = xpart;
-        }
-        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-        f32x4_t dX = zero;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            dX = mfma_k4(Ml[4 * ks + g][l & 15], dol[sub][4 * ks + g][l & 15], dX);
-        __syncthreads();
-        // every wave sums the same partials in the same order: lane l holds
-        // dX tokens 4g + jj of column l%16
-        dX += xpw[sub][0][l];
-        dX += xpw[sub][1][l];
-        dX += xpw[sub][2][l];
-        dX += xpw[sub][3][l];
-        if (wave == 0) {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int r = 4 * g + jj;
-                dxws[sh * CS * HD + (size_t)r * HD + col] = dX[jj];
-                if (r < len && colv) dv[((size_t)(t0 + r) * H + h) * kd + col] = tobf16(dX[jj]);
-            }
-        }
-        // dS0 = Gam dS1 + scale Qt^T dO - Kt^T dX, per row tile (A: Qt^T /
-        // Kt^T row 16t + l%16, token 4g + jj; B: dO / dX token 4g + jj)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int t = 2 * wave + tt;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) dsa[tt][jj] *= gam[16 * t + 4 * g + jj];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                dsa[tt] = mfma_k4(qtT[16 * t + (l & 15)][4 * g + jj], dol[sub][4 * g + jj][l & 15], dsa[tt]);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                dsa[tt] = mfma_k4(-ktT[16 * t + (l & 15)][4 * g + jj], dX[jj], dsa[tt]);
-        }
-    }
-    if (dinit) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int row = 16 * (2 * wave + tt) + 4 * g + jj;
-                if (colv && row < kd) dinit[sbase + (size_t)row * kd + col] = dsa[tt][jj];
-            }
-    }
-#undef KDA_DSTATES_FETCH
-}
 
 // ---------------------------------------------------------------------------
 // chunk: per (chunk slot, head), everything that needs S0 and dS1 of the
@@ -644,18 +327,24 @@ struct ChunkLds {
 };
 static_assert(2 * sizeof(ChunkLds) <= 160 * 1024, "two chunk workgroups per compute unit");
 
-// Row r (a channel) of the 16-channel block cb of a stored state as the B
-// operand of eight 16x16x4 k-step groups: lane (r, j) loads, from each of the
-// eight 16-column parts p, the four columns 16 p + 4 j .. + 3 (one 16-byte load
-// per part; the 64 lanes of one load cover the part's 1 KiB piece of the block).
-// In the scans' accumulator order row 4 gq + jj, column cl of a piece is at
-// float 64 jj + 16 gq + cl.
-__device__ __forceinline__ void fetch_state_rows(float4 (&d)[NPART], const float *__restrict__ base,
-                                                 int cb, int l) {
+// Row r (a channel) of the 16-channel block cb of a stored state (S0 or
+// dS1, which the backward's scans store in bf16 as rows of each 16-column
+// part, [part][128 rows][16 columns]) as the B operand of eight 16x16x4
+// k-step groups: lane (r, j) loads, from each part p, the four columns
+// 16 p + 4 j .. + 3 (8 bytes, widened).  Parts from np on (columns past the
+// head dimension) are not stored and read as zeros; their loads are issued
+// anyway (at part 0) so that no branch forces a wait on the loads in flight.
+__device__ __forceinline__ void fetch_state_rows(float4 (&d)[NPART], const uint16_t *__restrict__ base,
+                                                 int cb, int l, int np) {
     const int r = l & 15, j = l >> 4;
 #pragma unroll
-    for (int p = 0; p < NPART; ++p)
-        d[p] = *(const float4 *)&base[state_acc_off(p, cb, 0, 0) + 64 * (r & 3) + 16 * (r >> 2) + 4 * j];
+    for (int p = 0; p < NPART; ++p) {
+        const int pp = p < np ? p : 0;
+        const u32x2_t w = *(const u32x2_t *)&base[((size_t)pp * HD + 16 * cb + r) * 16 + 4 * j];
+        const bool in = p < np;
+        d[p] = make_float4(in ? bf16lo(w[0]) : 0.f, in ? bf16hi(w[0]) : 0.f,
+                           in ? bf16lo(w[1]) : 0.f, in ? bf16hi(w[1]) : 0.f);
+    }
 }
 
 __global__ __launch_bounds__(BT, 2) void bwd_chunk_kernel(
@@ -663,7 +352,7 @@ __global__ __launch_bounds__(BT, 2) void bwd_chunk_kernel(
     const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
     const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb, float scale,
     const uint16_t *__restrict__ dout, const int32_t *__restrict__ cu, int N, int T, int H, int kd,
-    const float *__restrict__ st0, const float *__restrict__ dst1,
+    const uint16_t *__restrict__ st0, const uint16_t *__restrict__ dst1,
     const float *__restrict__ xws, const float *__restrict__ dxws,
     uint16_t *__restrict__ dq, uint16_t *__restrict__ dk, uint16_t *__restrict__ dg,
     uint16_t *__restrict__ dbeta, float *__restrict__ part_alog, float *__restrict__ part_dtb)
@@ -682,14 +371,15 @@ __global__ __launch_bounds__(BT, 2) void bwd_chunk_kernel(
         if (tid == 0) part_alog[sh] = 0.f;
         return;
     }
-    const float *S0 = st0 + sh * HD * HD;
-    const float *DS = dst1 + sh * HD * HD;
+    const uint16_t *S0 = st0 + sh * HD * HD;
+    const uint16_t *DS = dst1 + sh * HD * HD;
+    const int np = kd / CWB;                                // stored parts of S0 and dS1
     // Wave w takes the 16-channel blocks 2w and 2w + 1 of S0 and dS1; the
     // first block's rows are in flight during the factors.
     const int wave = tid >> 6, l = tid & 63;
     float4 sb[NPART], db[NPART];
-    fetch_state_rows(sb, S0, 2 * wave, l);
-    fetch_state_rows(db, DS, 2 * wave, l);
+    fetch_state_rows(sb, S0, 2 * wave, l, np);
+    fetch_state_rows(db, DS, 2 * wave, l, np);
     const float Aexp = expf(A_log[h]);
     float ysv[CS], sgv[CS];                                 // this thread's gate per row (threads < HD)
     chunk_factors<false, true>(F, q, k, g, beta, Aexp, dt_bias, lb, t0, len, H, h, kd, ysv, sgv);
@@ -711,9 +401,16 @@ __global__ __launch_bounds__(BT, 2) void bwd_chunk_kernel(
     }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
+        // X and dX; the columns past the head dimension are not stored by
+        // the reverse scan and are zeros here
         const int e = 4 * (tid + m * BT);
-        *(float4 *)&L.xl[e / HD][e % HD] = *(const float4 *)&xws[sh * CS * HD + e];
-        *(float4 *)&L.u.dxl[e / HD][e % HD] = *(const float4 *)&dxws[sh * CS * HD + e];
+        const bool cv = e % HD < kd;
+        const float4 xv = *(const float4 *)&xws[sh * CS * HD + e];
+        const float4 dxv = *(const float4 *)&dxws[sh * CS * HD + e];
+        *(float4 *)&L.xl[e / HD][e % HD] =
+            make_float4(cv ? xv.x : 0.f, cv ? xv.y : 0.f, cv ? xv.z : 0.f, cv ? xv.w : 0.f);
+        *(float4 *)&L.u.dxl[e / HD][e % HD] =
+            make_float4(cv ? dxv.x : 0.f, cv ? dxv.y : 0.f, cv ? dxv.z : 0.f, cv ? dxv.w : 0.f);
     }
     __syncthreads();
 
@@ -732,8 +429,8 @@ __global__ __launch_bounds__(BT, 2) void bwd_chunk_kernel(
         const int cb = 2 * wave + tt;
         float4 sn[NPART], dn[NPART];
         if (tt == 0) {                                      // the next block in flight
-            fetch_state_rows(sn, S0, cb + 1, l);
-            fetch_state_rows(dn, DS, cb + 1, l);
+            fetch_state_rows(sn, S0, cb + 1, l, np);
+            fetch_state_rows(dn, DS, cb + 1, l, np);
         }
         f32x4_t aq = {0.f, 0.f, 0.f, 0.f}, ak = aq, aw = aq;
         float pg = 0.f;
@@ -968,8 +665,8 @@ __global__ __launch_bounds__(HD) void bwd_reduce_kernel(
 
 size_t bwd_workspace_bytes(int64_t num_slots, int H) {
     const size_t sh = (size_t)num_slots * H;
-    return sh * ((size_t)BR_FLOATS + 2 * (size_t)HD * HD + 2 * (size_t)CS * HD + 1 + HD) *
-           sizeof(float);
+    return sh * ((size_t)StatesRec::BYTES + (size_t)RecLayout<HD>::BYTES +
+                 2 * (size_t)HD * HD * sizeof(uint16_t) + (2 * (size_t)CS * HD + HD + 1) * sizeof(float));
 }
 
 hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
@@ -982,44 +679,31 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
                       const hipEvent_t *events)
 {
     const size_t sh = (size_t)num_slots * H;
-    float *brec = (float *)ws;
-    float *st0 = brec + sh * BR_FLOATS;
-    float *dst1 = st0 + sh * HD * HD;
-    float *xws = dst1 + sh * HD * HD;
+    // every region starts at a multiple of 256 bytes (each per-(slot, head)
+    // size is one, the last region's aside)
+    static_assert(RecLayout<HD>::BYTES % 256 == 0 && StatesRec::BYTES % 256 == 0, "256-byte regions");
+    uint8_t *srec = (uint8_t *)ws;
+    uint8_t *rrec = srec + sh * StatesRec::BYTES;
+    uint16_t *st0 = (uint16_t *)(rrec + sh * RecLayout<HD>::BYTES);
+    uint16_t *dst1 = st0 + sh * HD * HD;
+    float *xws = (float *)(dst1 + sh * HD * HD);
     float *dxws = xws + sh * CS * HD;
     float *pdtb = dxws + sh * CS * HD;
     float *palog = pdtb + sh * HD;
-    const size_t units8 = ((size_t)N * H + 7) / 8;
     const dim3 chunks((unsigned)sh);
-    // Four column parts per scan workgroup (each record read twice per head)
-    // when those workgroups cover at least three quarters of the compute
-    // units, else two (measured on 256 CUs: 96 heads run faster on 192
-    // four-part workgroups than on 384 two-part ones, 64 heads faster on 256
-    // two-part workgroups than on 128 four-part ones).
-    const bool pg4 = 8 * (int64_t)N * H >= 3 * (int64_t)bwd_num_cus();
-    const int pg = pg4 ? 4 : 2;
-    const dim3 sgrid((unsigned)(8 * (NPART / pg) * units8)), sblock((unsigned)(BT * pg));
     hipError_t e = hipSuccess;
     auto mark = [&](int i) {
         if (events && events[i] && e == hipSuccess) e = hipEventRecord(events[i], stream);
     };
     mark(0);
     hipLaunchKernelGGL(bwd_prep_kernel, chunks, dim3(BT), 0, stream,
-                       q, k, g, beta, A_log, dt_bias, lower_bound, cu, N, T, H, K, brec);
+                       q, k, g, beta, A_log, dt_bias, lower_bound, scale, cu, N, T, H, K, srec, rrec);
     mark(1);
-    if (pg4)
-        hipLaunchKernelGGL(bwd_states_kernel<4>, sgrid, sblock, 0, stream,
-                           v, brec, cu, N, T, H, K, init, init_fp32, st0, xws);
-    else
-        hipLaunchKernelGGL(bwd_states_kernel<2>, sgrid, sblock, 0, stream,
-                           v, brec, cu, N, T, H, K, init, init_fp32, st0, xws);
+    if (e == hipSuccess)
+        e = launch_bwd_fscan(v, srec, cu, N, T, H, K, init, init_fp32, st0, xws, stream);
     mark(2);
-    if (pg4)
-        hipLaunchKernelGGL(bwd_dstates_kernel<4>, sgrid, sblock, 0, stream,
-                           dout, brec, cu, N, T, H, K, scale, dfin, dst1, dxws, dv, dinit);
-    else
-        hipLaunchKernelGGL(bwd_dstates_kernel<2>, sgrid, sblock, 0, stream,
-                           dout, brec, cu, N, T, H, K, scale, dfin, dst1, dxws, dv, dinit);
+    if (e == hipSuccess)
+        e = launch_bwd_rscan(dout, rrec, cu, N, T, H, K, dfin, dinit, dv, dst1, dxws, stream);
     mark(3);
     hipLaunchKernelGGL(bwd_chunk_kernel, chunks, dim3(BT), 0, stream,
                        q, k, g, beta, A_log, dt_bias, lower_bound, scale, dout, cu, N, T, H, K,

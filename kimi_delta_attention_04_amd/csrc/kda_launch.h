@@ -26,6 +26,24 @@ hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, 
                        void *fin, int fin_fp32, uint16_t *out, hipStream_t stream,
                        int part_cols = 0);
 
+// Forward scan of the backward (K = V = 128 or 64): the state from init
+// (bf16 or fp32 [N, H, V, V], or NULL) through every chunk over the states
+// records srec (RecLayout<HD>: Kt, Wm in the W^T slot, the chunk decay);
+// stores per (chunk slot, head) S0 (bf16, [part of 16 columns][128 rows][16])
+// and X (fp32 [16][128]).
+hipError_t launch_bwd_fscan(const uint16_t *v, const uint8_t *srec, const int32_t *cu, int N, int T,
+                            int H, int V, const void *init, int init_fp32, uint16_t *s0, float *xws,
+                            hipStream_t stream);
+
+// Reverse scan of the backward (K = V = 128 or 64): the state gradient from
+// dfin (fp32 [N, H, V, V] or NULL) back through every chunk, over the
+// reverse records rrec (RecLayout<HD>, per (chunk slot, head)); writes dv,
+// dinit (fp32, if not NULL), and per (chunk slot, head) dS1 (bf16, [part of
+// 16 columns][128 rows][16]) and dX (fp32 [16][128]).
+hipError_t launch_bwd_rscan(const uint16_t *dout, const uint8_t *rrec, const int32_t *cu, int N,
+                            int T, int H, int V, const float *dfin, float *dinit, uint16_t *dv,
+                            uint16_t *ds1, float *dxws, hipStream_t stream);
+
 // One-token decode step on N x H states of D x D (D = 64, 128 or 256) in
 // place (fp32 or bf16).
 hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
