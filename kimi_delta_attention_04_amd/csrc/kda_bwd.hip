@@ -27,15 +27,15 @@
 //   prep    (chunk slot, head)  the chunk factors in fp32: Kt and Wm (with the
 //           chunk decay) for the states scan, and the reverse scan's bf16
 //           record (Wm, scale Qt, -Kt, scale M^T in MFMA operand layouts)
-//   states  (sequence, head, four 16-column parts)  forward scan storing
-//           every chunk's start state S0 and X (fp32 16x16x4 MFMA)
-//   rscan   (sequence, head, column part)  reverse scan of dS on the forward
-//           scan's structure (kda_scan.hip: bf16 MFMA operands, fp32
-//           accumulators), storing every chunk's dS1 (bf16) and dX,
+//   states  (sequence, head, column part)  forward scan on the forward
+//           scan's structure (kda_scan.hip), storing every chunk's start
+//           state S0 (bf16 rows) and X (fp32)
+//   rscan   (sequence, head, column part)  reverse scan of dS on the same
+//           structure, storing every chunk's dS1 (bf16 rows) and dX,
 //           writing dv and the initial-state gradient
-//   chunk   (chunk slot, head)  the products with S0 / dS1 (fp32 MFMA) and
-//           the in-chunk backward: dq, dk, dg, dbeta, per-chunk dA_log /
-//           ddt_bias sums
+//   chunk   (chunk slot, head), one wave  the products with S0 / dS1 and the
+//           in-chunk backward on bf16 MFMAs with (hi, lo) operands: dq, dk,
+//           dg, dbeta, per-chunk dA_log / ddt_bias sums
 //   reduce  (head)  sums the per-chunk parameter gradients in slot order
 // Every sum runs in a fixed order, so results are bitwise reproducible.
 #include <math.h>
@@ -51,8 +51,6 @@ namespace {
 constexpr int BT = 256;               // threads per workgroup
 constexpr int RS = HD + 4;            // padded LDS row stride (floats)
 constexpr int SP = CS + 1;            // padded stride of 16 x 16 tiles
-constexpr int CWB = 16;               // state columns of one stored part
-constexpr int NPART = HD / CWB;
 
 // The transcendentals on the hardware base-2 units (v_exp_f32, v_log_f32,
 // v_rcp_f32).  softplus keeps the form max(x, 0) + log(1 + e^-|x|), finite
@@ -303,330 +301,543 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(
 
 
 // ---------------------------------------------------------------------------
-// chunk: per (chunk slot, head), everything that needs S0 and dS1 of the
-// chunk, then the in-chunk backward down to the inputs.
+// chunk: one wave per (chunk slot, head), everything that needs S0 and dS1
+// of the chunk, then the in-chunk backward down to the inputs.  No barrier:
+// the wave keeps its operands in MFMA register layouts and moves 16 x 16
+// tiles between layouts through a few hundred bytes of its own LDS.
+//
+// Layouts (lane l, tok = l%16, grp = l/16):
+//   token-per-lane  lane l holds token tok, channels 32kb + 8grp + i
+//                   (i = 0..7) of each 32-channel block kb: the A and B
+//                   operand layout of a 16x16x32 MFMA contracting over
+//                   channels (or value columns), as in the intra stage
+//   tile            16 x 16 matrices in accumulator layout: rows 4grp + j,
+//                   column tok
+//   W^T             tile t of a tokens x channels matrix: tokens 4grp + j,
+//                   channel chan(t, tok) (kda_device.h), the A operand
+//                   layout of a 16x16x16 MFMA contracting over tokens
+// A product whose rows are the state rows chan(t, .) of tiles 2kb and
+// 2kb + 1 lands, in accumulator layout, in the token-per-lane layout of
+// block kb; an identity MFMA turns token-per-lane bf16 into W^T bf16 and
+// back, exactly.  fp32 operands enter the bf16 MFMAs as (hi, lo) pairs with
+// three products (hi hi + hi lo + lo hi), about 16 significant bits.
 // ---------------------------------------------------------------------------
-// Buffers whose lifetimes do not overlap share storage, which keeps the
-// workgroup at 73 KB of LDS (two workgroups per compute unit):
-//   dol  scale * dO: the state products and dM; then dG of every (row, channel)
-//   xl   X: the state products and dM
-//   u    dX for the state products; then the 16 x 16 gradient tiles
-//   dwm  dWm: written by the state products, read by the later phases
-struct ChunkTiles {
-    float dM[CS][SP], dAqk[CS][SP], dP[CS][SP], Y[CS][SP], dL[CS][SP], dA[CS][SP];
+struct ChunkWaveLds {
+    float beta[CS];
+    float daq[CS];                    // diagonal of dAqk
+    float dtb[HD];                    // dt_bias in log2 units
+    float gam[HD];                    // e^{G_last} per key channel
+    float gl[HD];                     // G_last in log2 units
+    float dgs[HD];                    // diag(dS1 S0^T) per key channel
+    float tile[CS][CS + 1];           // 16 x 16 transposes
+    f32x4_t qs[HD / 16][64];          // (dO S0^T)^T and (dX S0^T)^T per state row
+    f32x4_t ks[HD / 16][64];          // tile and lane, between their two phases
 };
-struct ChunkLds {
-    FactorsBase f;
-    float dol[CS][RS], xl[CS][RS];
-    union {
-        float dxl[CS][RS];
-        ChunkTiles t;
-    } u;
-    float dwm[CS][RS];
-    float dgam[HD], dgam2[HD], red[BT / 64];
-};
-static_assert(2 * sizeof(ChunkLds) <= 160 * 1024, "two chunk workgroups per compute unit");
 
-// Row r (a channel) of the 16-channel block cb of a stored state (S0 or
-// dS1, which the backward's scans store in bf16 as rows of each 16-column
-// part, [part][128 rows][16 columns]) as the B operand of eight 16x16x4
-// k-step groups: lane (r, j) loads, from each part p, the four columns
-// 16 p + 4 j .. + 3 (8 bytes, widened).  Parts from np on (columns past the
-// head dimension) are not stored and read as zeros; their loads are issued
-// anyway (at part 0) so that no branch forces a wait on the loads in flight.
-__device__ __forceinline__ void fetch_state_rows(float4 (&d)[NPART], const uint16_t *__restrict__ base,
-                                                 int cb, int l, int np) {
-    const int r = l & 15, j = l >> 4;
+// The tile layout of Z -> the tile layout of Z^T, through the wave's LDS.
+__device__ __forceinline__ f32x4_t tr16(float (&b)[CS][CS + 1], f32x4_t x) {
+    const int l = threadIdx.x & 63, tok = l & 15, grp = l >> 4;
+    wave_lds_sync();
 #pragma unroll
-    for (int p = 0; p < NPART; ++p) {
-        const int pp = p < np ? p : 0;
-        const u32x2_t w = *(const u32x2_t *)&base[((size_t)pp * HD + 16 * cb + r) * 16 + 4 * j];
-        const bool in = p < np;
-        d[p] = make_float4(in ? bf16lo(w[0]) : 0.f, in ? bf16hi(w[0]) : 0.f,
-                           in ? bf16lo(w[1]) : 0.f, in ? bf16hi(w[1]) : 0.f);
+    for (int j = 0; j < 4; ++j) b[4 * grp + j][tok] = x[j];
+    wave_lds_sync();
+    f32x4_t y;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = b[tok][4 * grp + j];
+    return y;
+}
+
+// (hi, lo) bf16 parts of a tile (four fp32) and of eight fp32 values.
+__device__ __forceinline__ void split4(f32x4_t x, u32x2_t &hi, u32x2_t &lo) {
+    uint32_t h0, l0, h1, l1;
+    split2(x[0], x[1], h0, l0);
+    split2(x[2], x[3], h1, l1);
+    hi = {h0, h1};
+    lo = {l0, l1};
+}
+__device__ __forceinline__ void split8(f32x4_t a, f32x4_t b, u32x4_t &hi, u32x4_t &lo) {
+    uint32_t h, w;
+    split2(a[0], a[1], h, w); hi[0] = h; lo[0] = w;
+    split2(a[2], a[3], h, w); hi[1] = h; lo[1] = w;
+    split2(b[0], b[1], h, w); hi[2] = h; lo[2] = w;
+    split2(b[2], b[3], h, w); hi[3] = h; lo[3] = w;
+}
+// C + A B from (hi, lo) parts: hi hi + hi lo + lo hi.
+__device__ __forceinline__ f32x4_t mm3_k16(u32x2_t ah, u32x2_t al, u32x2_t bh, u32x2_t bl, f32x4_t c) {
+    c = mfma_k16(ah, bh, c);
+    c = mfma_k16(ah, bl, c);
+    return mfma_k16(al, bh, c);
+}
+__device__ __forceinline__ f32x4_t mm3_k32(u32x4_t ah, u32x4_t al, u32x4_t bh, u32x4_t bl, f32x4_t c) {
+    c = mfma_k32(ah, bh, c);
+    c = mfma_k32(ah, bl, c);
+    return mfma_k32(al, bh, c);
+}
+
+// Sum over the 16 lanes of each DPP row, in every lane of the row.
+template <int SH>
+__device__ __forceinline__ float row_ror(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 0x120 + SH, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+    x += row_ror<8>(x);
+    x += row_ror<4>(x);
+    x += row_ror<2>(x);
+    return x + row_ror<1>(x);
+}
+// Inclusive suffix sum over the 16 lanes of each DPP row (lane i: lanes i..15).
+template <int SH>
+__device__ __forceinline__ float row_shl(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 0x100 + SH, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row_suffix16(float x) {
+    x += row_shl<1>(x);
+    x += row_shl<2>(x);
+    x += row_shl<4>(x);
+    return x + row_shl<8>(x);
+}
+
+// The identity as a 16x16x16 B operand: mfma_k16(a, eye) is the tile layout
+// of the matrix whose A operand is a.
+__device__ __forceinline__ u32x2_t identity_b() {
+    const int l = threadIdx.x & 63;
+    const int d = (l & 15) - 4 * (l >> 4);
+    const uint32_t one = 0x3f80u;                           // bf16 1.0
+    u32x2_t e;
+    e[0] = (d == 0 ? one : 0u) | (d == 1 ? one << 16 : 0u);
+    e[1] = (d == 2 ? one : 0u) | (d == 3 ? one << 16 : 0u);
+    return e;
+}
+
+// Four bf16 channels 32kb + 8grp + 4hh + j (j = 0..3) of this lane's token
+// (the A operand layout of a 16x16x16 MFMA) -> the W^T layout of tile
+// 2kb + hh, exactly.
+__device__ __forceinline__ u32x2_t to_wt(u32x2_t a, u32x2_t eye) {
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4_t d = mfma_k16(a, eye, z);
+    return {pack2(d[0], d[1]), pack2(d[2], d[3])};
+}
+
+// Log-decay in log2 units, as the forward's intra stage forms it, of the NI
+// channels 32kb + 8grp + i0 + i of this lane's token: per (token, channel)
+// x2 = (g + dt_bias) log2 e, the clamped gate max(-A log2(1 + 2^x2),
+// lb log2 e) (zero on padding rows), and its inclusive cumulative sum G over
+// the chunk's tokens (across the 16 lanes of the DPP row).
+template <int NI>
+__device__ __forceinline__ void block_decay(const u32x4_t gw, const float *__restrict__ dtb_lds,
+                                            int kb, int i0, float A, float lb2, bool live,
+                                            float (&G)[NI]) {
+    const int grp = (threadIdx.x & 63) >> 4;
+    if (A > 0.f) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const float x2 = elem(gw, i0 + i) * LOG2E + dtb_lds[32 * kb + 8 * grp + i0 + i];
+            const float la = fmaxf(-A * fast_log2(1.f + fast_exp2(x2)), lb2);
+            G[i] = live ? la : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) G[i] += row_shr<1>(G[i]);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) G[i] += row_shr<2>(G[i]);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) G[i] += row_shr<4>(G[i]);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) G[i] += row_shr<8>(G[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) G[i] = 0.f;
     }
 }
 
-__global__ __launch_bounds__(BT, 2) void bwd_chunk_kernel(
+template <int KD>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_chunk_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
     const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb, float scale,
-    const uint16_t *__restrict__ dout, const int32_t *__restrict__ cu, int N, int T, int H, int kd,
+    const uint16_t *__restrict__ dout, const int32_t *__restrict__ cu, int N, int T, int H,
     const uint16_t *__restrict__ st0, const uint16_t *__restrict__ dst1,
     const float *__restrict__ xws, const float *__restrict__ dxws,
     uint16_t *__restrict__ dq, uint16_t *__restrict__ dk, uint16_t *__restrict__ dg,
     uint16_t *__restrict__ dbeta, float *__restrict__ part_alog, float *__restrict__ part_dtb)
 {
-    __shared__ __attribute__((aligned(16))) ChunkLds L;
-    FactorsBase &F = L.f;
-    ChunkTiles &Lt = L.u.t;
+    constexpr int NKB = KD / 32;                            // channel blocks = 32-column steps
+    constexpr int NT = 2 * NKB;                             // state row tiles
+    __shared__ __attribute__((aligned(16))) ChunkWaveLds L;
     const int64_t slot = blockIdx.x / (unsigned)H;
     const int h = (int)(blockIdx.x % (unsigned)H);
-    const int tid = threadIdx.x;
+    const int l = threadIdx.x, tok = l & 15, grp = l >> 4;
     const size_t sh = (size_t)slot * H + h;
     int64_t t0;
     const int len = slot_chunk(cu, N, T, slot, t0);
     if (len == 0) {                                         // gap slot: zero partial sums
-        if (tid < HD) part_dtb[sh * HD + tid] = 0.f;
-        if (tid == 0) part_alog[sh] = 0.f;
+        part_dtb[sh * HD + l] = 0.f;
+        part_dtb[sh * HD + 64 + l] = 0.f;
+        if (l == 0) part_alog[sh] = 0.f;
         return;
     }
-    const uint16_t *S0 = st0 + sh * HD * HD;
-    const uint16_t *DS = dst1 + sh * HD * HD;
-    const int np = kd / CWB;                                // stored parts of S0 and dS1
-    // Wave w takes the 16-channel blocks 2w and 2w + 1 of S0 and dS1; the
-    // first block's rows are in flight during the factors.
-    const int wave = tid >> 6, l = tid & 63;
-    float4 sb[NPART], db[NPART];
-    fetch_state_rows(sb, S0, 2 * wave, l, np);
-    fetch_state_rows(db, DS, 2 * wave, l, np);
-    const float Aexp = expf(A_log[h]);
-    float ysv[CS], sgv[CS];                                 // this thread's gate per row (threads < HD)
-    chunk_factors<false, true>(F, q, k, g, beta, Aexp, dt_bias, lb, t0, len, H, h, kd, ysv, sgv);
+    const bool live = tok < len;
+    const float A = expf(A_log[h]);
+    const float lb2 = lb * LOG2E;
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+    const u32x2_t eye = identity_b();
 
-    {
-        // all eight loads of this thread first (rows past len read row
-        // len-1 and are masked)
-        uint16_t dov[CS * HD / BT];
-#pragma unroll
-        for (int m = 0; m < CS * HD / BT; ++m) {
-            const int idx = tid + m * BT, r = idx / HD, c = idx % HD;
-            dov[m] = dout[((size_t)(t0 + (r < len ? r : len - 1)) * H + h) * kd + (c < kd ? c : 0)];
-        }
-#pragma unroll
-        for (int m = 0; m < CS * HD / BT; ++m) {
-            const int idx = tid + m * BT, r = idx / HD, c = idx % HD;
-            L.dol[r][c] = (r < len && c < kd) ? scale * bf16f(dov[m]) : 0.f;
-        }
-    }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        // X and dX; the columns past the head dimension are not stored by
-        // the reverse scan and are zeros here
-        const int e = 4 * (tid + m * BT);
-        const bool cv = e % HD < kd;
-        const float4 xv = *(const float4 *)&xws[sh * CS * HD + e];
-        const float4 dxv = *(const float4 *)&dxws[sh * CS * HD + e];
-        *(float4 *)&L.xl[e / HD][e % HD] =
-            make_float4(cv ? xv.x : 0.f, cv ? xv.y : 0.f, cv ? xv.z : 0.f, cv ? xv.w : 0.f);
-        *(float4 *)&L.u.dxl[e / HD][e % HD] =
-            make_float4(cv ? dxv.x : 0.f, cv ? dxv.y : 0.f, cv ? dxv.z : 0.f, cv ? dxv.w : 0.f);
-    }
-    __syncthreads();
+    // token rows of this chunk ([token, head, channel] tensors): loads past
+    // the chunk's tokens return zeros, stores there are dropped
+    const size_t rowe = (size_t)H * KD;
+    const uint32_t rbytes = (uint32_t)(((size_t)(len - 1) * rowe + KD) * 2);
+    const size_t rbase = ((size_t)t0 * H + h) * KD;
+    const __amdgpu_buffer_rsrc_t r_do = make_rsrc(dout + rbase, rbytes);
+    auto row_off = [&](int kb) { return (int)((tok * rowe + 32 * kb + 8 * grp) * 2); };
 
-    // Products with the states on fp32 16x16x4 MFMAs, contracting over the
-    // 128 value columns; wave w forms them for channel blocks cb = 2w + tt:
-    //   dQt = scale dO S0^T,  dKt = -dX S0^T,  dWm = X dS1^T,
-    //   dGam = diag(dS1 S0^T) (vector ALUs, summed over the four lane groups).
-    // k-step 4p + i takes column 16p + 4(l/16) + i from lane l (the order of the
-    // state rows as loaded); the A operands follow the same order.  Lane l
-    // holds rows 4(l/16) .. +3, channel 16cb + l%16 of each product, the
-    // layout of the per-(row, channel) phase below, so dQt and dKt stay in
-    // registers.
-    f32x4_t dQs[2], dKs[2];
+    // ---- products with the states ------------------------------------------
+    // Over the value columns in 32-column steps s, state row tile t:
+    //   (dO S0^T)^T, (dX S0^T)^T   rows chan(t, .): token-per-lane results
+    //   dWm = X dS1^T              W^T layout (A = X, B = dS1 rows)
+    //   dM / scale = dO X^T        tile
+    //   diag(dS1 S0^T)             per lane, summed over its four lane groups
+    // The stored states are bf16 rows [16-column part][128 rows][16]; the A
+    // operand of tile t, step s is row chan(t, tok), columns 32s + 8grp .. +7.
+    f32x4_t QS[NT], KS[NT], WW[NT], dM = zero;
+    float dgp[NT];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        const int cb = 2 * wave + tt;
-        float4 sn[NPART], dn[NPART];
-        if (tt == 0) {                                      // the next block in flight
-            fetch_state_rows(sn, S0, cb + 1, l, np);
-            fetch_state_rows(dn, DS, cb + 1, l, np);
-        }
-        f32x4_t aq = {0.f, 0.f, 0.f, 0.f}, ak = aq, aw = aq;
-        float pg = 0.f;
-#pragma unroll
-        for (int p = 0; p < NPART; ++p) {
-            const int c0 = 16 * p + 4 * (l >> 4);
-            const float4 ad = *(const float4 *)&L.dol[l & 15][c0];
-            const float4 ax = *(const float4 *)&L.u.dxl[l & 15][c0];
-            const float4 aX = *(const float4 *)&L.xl[l & 15][c0];
-            aq = mfma_k4(ad.x, sb[p].x, aq);
-            aq = mfma_k4(ad.y, sb[p].y, aq);
-            aq = mfma_k4(ad.z, sb[p].z, aq);
-            aq = mfma_k4(ad.w, sb[p].w, aq);
-            ak = mfma_k4(-ax.x, sb[p].x, ak);
-            ak = mfma_k4(-ax.y, sb[p].y, ak);
-            ak = mfma_k4(-ax.z, sb[p].z, ak);
-            ak = mfma_k4(-ax.w, sb[p].w, ak);
-            aw = mfma_k4(aX.x, db[p].x, aw);
-            aw = mfma_k4(aX.y, db[p].y, aw);
-            aw = mfma_k4(aX.z, db[p].z, aw);
-            aw = mfma_k4(aX.w, db[p].w, aw);
-            pg += db[p].x * sb[p].x + db[p].y * sb[p].y + db[p].z * sb[p].z + db[p].w * sb[p].w;
-        }
-        dQs[tt] = aq;
-        dKs[tt] = ak;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) L.dwm[4 * (l >> 4) + i][16 * cb + (l & 15)] = aw[i];
-        pg += __shfl_xor(pg, 16, 64);
-        pg += __shfl_xor(pg, 32, 64);
-        if ((l >> 4) == 0) L.dgam[16 * cb + (l & 15)] = pg;
-        if (tt == 0) {
-#pragma unroll
-            for (int p = 0; p < NPART; ++p) {
-                sb[p] = sn[p];
-                db[p] = dn[p];
-            }
-        }
-    }
-    // dWm complete and dX no longer read (its storage holds the 16 x 16 tiles next)
-    __syncthreads();
-    const int r_ = tid >> 4, lo = tid & 15;
+    for (int t = 0; t < NT; ++t) { QS[t] = KS[t] = WW[t] = zero; dgp[t] = 0.f; }
     {
-        // The two contractions over 128 channels on fp32 16x16x4 MFMAs:
-        // wave 0 dM = scale dO X^T, wave 1 the Wm path of dP, Kb Gam dWm^T
-        // (held in Y, which is free until the phase after next).  Lane l
-        // supplies row l%16, channel 4ks + l/16 of both operands and holds
-        // rows 4(l/16) .. +3, column l%16.
-        const int ar = l & 15, ak = l >> 4;
-        if (wave < 2) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            if (wave == 0) {
-#pragma unroll 8
-                for (int ks = 0; ks < HD / 4; ++ks)
-                    acc = mfma_k4(L.dol[ar][4 * ks + ak], L.xl[ar][4 * ks + ak], acc);
-            } else {
-#pragma unroll 8
-                for (int ks = 0; ks < HD / 4; ++ks) {
-                    const int c = 4 * ks + ak;
-                    acc = mfma_k4(F.kb[ar][c] * F.gam[c], L.dwm[ar][c], acc);
+        const uint16_t *S0 = st0 + sh * HD * HD + (size_t)(l >> 5) * HD * 16 + 8 * ((l >> 4) & 1);
+        const uint16_t *DS = dst1 + sh * HD * HD + (size_t)(l >> 5) * HD * 16 + 8 * ((l >> 4) & 1);
+        auto sld = [&](const uint16_t *b, int s, int t) {
+            return *(const u32x4_t *)&b[((size_t)2 * s * HD + state_chan(t, tok)) * 16];
+        };
+        const float *xr = xws + sh * CS * HD + tok * HD + 8 * grp;
+        const float *dxr = dxws + sh * CS * HD + tok * HD + 8 * grp;
+        // a ring of DEPTH (S0, dS1) operand pairs in flight; the step loop
+        // stays rolled so that the loads are issued where written
+        constexpr int DEPTH = 4;
+        static_assert(NT % DEPTH == 0, "ring slots repeat every step");
+        u32x4_t ra[DEPTH], rd[DEPTH];
+#pragma unroll
+        for (int p = 0; p < DEPTH; ++p) { ra[p] = sld(S0, 0, p); rd[p] = sld(DS, 0, p); }
+        u32x4_t on = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_do, row_off(0), 0, 0));
+        f32x4_t xa = *(const f32x4_t *)&xr[0], xb = *(const f32x4_t *)&xr[4];
+        f32x4_t da = *(const f32x4_t *)&dxr[0], db = *(const f32x4_t *)&dxr[4];
+#pragma unroll 1
+        for (int s = 0; s < NKB; ++s) {
+            const u32x4_t ob = on;
+            u32x4_t xh, xl, dxh, dxl;
+            split8(xa, xb, xh, xl);
+            split8(da, db, dxh, dxl);
+            const bool more = s + 1 < NKB;
+            if (more) {
+                on = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_do, row_off(s + 1), 0, 0));
+                xa = *(const f32x4_t *)&xr[32 * (s + 1)];
+                xb = *(const f32x4_t *)&xr[32 * (s + 1) + 4];
+                da = *(const f32x4_t *)&dxr[32 * (s + 1)];
+                db = *(const f32x4_t *)&dxr[32 * (s + 1) + 4];
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const u32x4_t sa = ra[t % DEPTH], sd = rd[t % DEPTH];
+                if (t + DEPTH < NT) {
+                    ra[t % DEPTH] = sld(S0, s, t + DEPTH);
+                    rd[t % DEPTH] = sld(DS, s, t + DEPTH);
+                } else if (more) {
+                    ra[t % DEPTH] = sld(S0, s + 1, t + DEPTH - NT);
+                    rd[t % DEPTH] = sld(DS, s + 1, t + DEPTH - NT);
                 }
-            }
-            float(&dst)[CS][SP] = wave == 0 ? Lt.dM : Lt.Y;
+                QS[t] = mfma_k32(sa, ob, QS[t]);
+                KS[t] = mfma_k32(sa, dxh, KS[t]);
+                KS[t] = mfma_k32(sa, dxl, KS[t]);
+                WW[t] = mfma_k32(xh, sd, WW[t]);
+                WW[t] = mfma_k32(xl, sd, WW[t]);
+                float d = dgp[t];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dst[4 * ak + j][ar] = acc[j];
+                for (int i = 0; i < 8; ++i) d = fmaf(elem(sa, i), elem(sd, i), d);
+                dgp[t] = d;
+            }
+            dM = mfma_k32(ob, xh, dM);
+            dM = mfma_k32(ob, xl, dM);
         }
     }
-    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        float d = dgp[t];
+        d += __shfl_xor(d, 16, 64);
+        d += __shfl_xor(d, 32, 64);
+        if (grp == 0) L.dgs[state_chan(t, tok)] = d;
+        L.qs[t][l] = QS[t];
+        L.ks[t][l] = KS[t];
+    }
+
+    // ---- chunk factors, and Y = Kb Gam dWm^T --------------------------------
+    stage_dtb<false, HD>(L.dtb, dt_bias, h, KD);
+    IntraIn in;
+    intra_load<false, HD>(in, q, k, g, beta, t0, len, H, h, KD);
     {
-        // M = Aqk P:  dAqk = dM P^T (lower incl.),  dP = Aqk^T dM
-        // Wm = P^T Kb Gam:  dP += Kb Gam dWm^T (from the MFMAs above)
-        const int r = r_, i = lo;
-        float a = 0.f, p = 0.f;
-        for (int s = 0; s < CS; ++s) {
-            a += Lt.dM[r][s] * F.P[i][s];
-            p += F.aqk[s][r] * Lt.dM[s][i];
-        }
-        p += Lt.Y[r][i];
-        Lt.dAqk[r][i] = i <= r ? a : 0.f;
-        Lt.dP[r][i] = p;
+        const float x = bf16f((uint16_t)in.beta);
+        const float b = __builtin_amdgcn_rcpf(1.f + fast_exp2(-x * LOG2E));
+        if (grp == 0) L.beta[tok] = live ? b : 0.f;
     }
-    __syncthreads();
+    // dWm (hi, lo) in the W^T layout as computed
+    u32x2_t wwh[NT], wwl[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) split4(WW[t], wwh[t], wwl[t]);
+    wave_lds_sync();                                        // dt_bias staged
+    f32x4_t Akk = zero, AkkT = zero, Aqk = zero, Y = zero;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        float G[8];
+        block_decay<8>(in.g[kb], L.dtb, kb, 0, A, lb2, live, G);
+        if (tok == CS - 1) {
+            f32x4_t g0, g1, l0, l1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                g0[i] = fast_exp2(G[i]); g1[i] = fast_exp2(G[4 + i]);
+                l0[i] = G[i]; l1[i] = G[4 + i];
+            }
+            *(f32x4_t *)&L.gam[32 * kb + 8 * grp] = g0;
+            *(f32x4_t *)&L.gam[32 * kb + 8 * grp + 4] = g1;
+            *(f32x4_t *)&L.gl[32 * kb + 8 * grp] = l0;
+            *(f32x4_t *)&L.gl[32 * kb + 8 * grp + 4] = l1;
+        }
+        wave_lds_sync();
+        float gl[8];
+        *(f32x4_t *)&gl[0] = *(const f32x4_t *)&L.gl[32 * kb + 8 * grp];
+        *(f32x4_t *)&gl[4] = *(const f32x4_t *)&L.gl[32 * kb + 8 * grp + 4];
+        // The Grams are formed from Kt, Qt and Kb rescaled by e^{-G_last/2}
+        // and e^{G_last/2} per channel, which leaves Kt Kb^T and Qt Kb^T
+        // unchanged: at the lowest lower bound G_last reaches -86 (natural
+        // log), where k e^G falls among the denormals and the bf16 (hi, lo)
+        // parts of such a value keep only a few bits; rescaled, every factor
+        // stays within e^{+-43}.  Kb Gam = k e^{G_last - G} needs no rescale.
+        u32x4_t kth, ktl, qth, qtl, kbh, kbl, kgh, kgl;
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+            float kt[2], qt[2], kbv[2], kg[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i = 2 * wd + e;
+                const float gh = 0.5f * gl[i];
+                const float eg = fast_exp2(G[i] - gh), egi = fast_exp2(gh - G[i]);
+                const float kv = elem(in.k[kb], i), qv = elem(in.q[kb], i);
+                kt[e] = kv * eg;
+                qt[e] = qv * eg;
+                kbv[e] = kv * egi;
+                kg[e] = kv * fast_exp2(gl[i] - G[i]);
+            }
+            uint32_t a, b;
+            split2(kt[0], kt[1], a, b); kth[wd] = a; ktl[wd] = b;
+            split2(qt[0], qt[1], a, b); qth[wd] = a; qtl[wd] = b;
+            split2(kbv[0], kbv[1], a, b); kbh[wd] = a; kbl[wd] = b;
+            split2(kg[0], kg[1], a, b); kgh[wd] = a; kgl[wd] = b;
+        }
+        Akk = mm3_k32(kth, ktl, kbh, kbl, Akk);             // Akk[r][c]  = Kt_r . Kb_c
+        AkkT = mm3_k32(kbh, kbl, kth, ktl, AkkT);           // AkkT[r][c] = Akk[c][r]
+        Aqk = mm3_k32(qth, qtl, kbh, kbl, Aqk);             // Aqk[r][c]  = Qt_r . Kb_c
+        // dWm of block kb token-per-lane, through the identity (exact)
+        u32x4_t dwh, dwl;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const f32x4_t a = mfma_k16(wwh[2 * kb + hh], eye, zero), b = mfma_k16(wwl[2 * kb + hh], eye, zero);
+            dwh[2 * hh] = pack2(a[0], a[1]);
+            dwh[2 * hh + 1] = pack2(a[2], a[3]);
+            dwl[2 * hh] = pack2(b[0], b[1]);
+            dwl[2 * hh + 1] = pack2(b[2], b[3]);
+        }
+        Y = mm3_k32(kgh, kgl, dwh, dwl, Y);                 // (Kb Gam dWm^T)[r][c]
+    }
+
+    // ---- the 16 x 16 chain (tiles; row r = 4grp + j, column tok) ------------
+    float br[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) br[j] = L.beta[4 * grp + j];
+    const float bc = L.beta[tok];
+    f32x4_t Tm;
     {
-        // P = T diag(beta):  dT = dP diag(beta);  Y = dT T^T
-        const int a = r_, s = lo;
-        float y = 0.f;
-        for (int b = 0; b < CS; ++b) y += Lt.dP[a][b] * F.beta[b] * F.T[s][b];
-        Lt.Y[a][s] = y;
+        // T = (I + diag(beta) strict_lower(Akk))^-1 = (I - N)^-1, N strictly
+        // lower hence nilpotent: (I + N)(I + N^2)(I + N^4)(I + N^8)
+        f32x4_t N1, N1t, I;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * grp + j;
+            N1[j] = tok < r ? -br[j] * Akk[j] : 0.f;
+            N1t[j] = r < tok ? -bc * AkkT[j] : 0.f;
+            I[j] = r == tok ? 1.f : 0.f;
+        }
+        const f32x4_t N2 = mm16(N1t, N1), N2t = mm16(N1, N1t);
+        const f32x4_t Q12t = mm16(I + N2, I + N1t);         // ((I+N)(I+N^2))^T
+        const f32x4_t N4 = mm16(N2t, N2), N4t = mm16(N2, N2t);
+        const f32x4_t Q3t = mm16(I + N4, Q12t);
+        const f32x4_t N8 = mm16(N4t, N4);
+        Tm = mm16(Q3t, I + N8);
     }
-    __syncthreads();
+    const f32x4_t Tt = tr16(L.tile, Tm);                   // T^T
+    f32x4_t Pt, Aq, Amt, dMs;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * grp + j;
+        Pt[j] = Tt[j] * br[j];                              // P^T, P = T diag(beta)
+        Aq[j] = tok <= r ? Aqk[j] : 0.f;                    // lower_incl(Qt Kb^T)
+        Amt[j] = r < tok ? AkkT[j] : 0.f;                   // A^T, A = strict_lower(Kt Kb^T)
+        dMs[j] = scale * dM[j];
+    }
+    // M = Aqk P:  dAqk = lower_incl(dM P^T),  dP = Aqk^T dM (+ Y from Wm = P^T Kb Gam)
+    f32x4_t dAqk = mm16(tr16(L.tile, dMs), Pt);
+    const f32x4_t dP = mm16(Aq, dMs) + Y;
+    // The diagonal of Aqk, Qt_r . Kb_r = q_r . k_r, does not depend on the
+    // decay: its terms in dG (through Qt and through Kb) cancel exactly.
+    // Formed in the products they would cancel only to the products'
+    // rounding, which under strong decay is larger than dG itself; so the
+    // products take dAqk strictly lower and the diagonal's gradients enter
+    // dq and dk directly (dAqk[r][r] k_r and dAqk[r][r] q_r).
+    f32x4_t dT;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * grp + j;
+        if (tok == r) L.daq[tok] = dAqk[j];
+        dAqk[j] = tok < r ? dAqk[j] : 0.f;
+        dT[j] = dP[j] * bc;                                 // P = T diag(beta)
+    }
+    // T = (I + L)^-1:  dL = -T^T (dT T^T), strictly lower;  L = diag(beta) A
+    const f32x4_t Y2 = mm16(tr16(L.tile, dT), Tt);
+    f32x4_t dL = mm16(Tm, Y2), dA;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        dL[j] = tok < 4 * grp + j ? -dL[j] : 0.f;
+        dA[j] = br[j] * dL[j];
+    }
     {
-        // T = (I + L)^-1:  dL = -T^T dT T^T (strictly lower);  L = diag(beta) A
-        const int r = r_, s = lo;
-        float d = 0.f;
-        for (int a = 0; a < CS; ++a) d += F.T[a][r] * Lt.Y[a][s];
-        d = s < r ? -d : 0.f;
-        Lt.dL[r][s] = d;
-        Lt.dA[r][s] = F.beta[r] * d;
-    }
-    __syncthreads();
-    {
-        // per (token row r, channel c): the gradients of Qt, Kt, Kb, then q, k, G.
-        // The 16 x 16 by 16 x 128 products on fp32 16x16x4 MFMAs, wave w
-        // taking channel tiles 2w and 2w+1:
-        //   dQt += dAqk Kb,  dKt += dA Kb,  dKbG = P dWm,  dKb = dAqk^T Qt + dA^T Kt
-        // Lane l supplies row l%16, token 4ks + l/16 of each 16 x 16 factor
-        // (A operand) and token 4ks + l/16, channel l%16 of the tile (B
-        // operand), and holds rows 4(l/16) .. +3, channel l%16 of each
-        // product: every (row, channel) belongs to one lane, which then
-        // forms its gradients elementwise.
-        const int ar = l & 15, ak = l >> 4;
-        float aAqk[4], aA[4], aP[4], aAqkT[4], aAT[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            aAqk[ks] = Lt.dAqk[ar][4 * ks + ak];
-            aA[ks] = Lt.dA[ar][4 * ks + ak];
-            aP[ks] = F.P[ar][4 * ks + ak];
-            aAqkT[ks] = Lt.dAqk[4 * ks + ak][ar];
-            aAT[ks] = Lt.dA[4 * ks + ak][ar];
-        }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int c = 16 * (2 * wave + tt) + ar;   // channel of this lane
-            f32x4_t dQ = {0.f, 0.f, 0.f, 0.f}, dK = dQ, dKG = dQ, dKB = dQ;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int tk = 4 * ks + ak;             // token of the B operand
-                const float kbs = F.kb[tk][c], dws = L.dwm[tk][c];
-                const float qts = F.qt[tk][c], kts = F.kt[tk][c];
-                dQ = mfma_k4(aAqk[ks], kbs, dQ);        // dAqk zero for s > r
-                dK = mfma_k4(aA[ks], kbs, dK);          // dA zero for s >= r
-                dKG = mfma_k4(aP[ks], dws, dKG);
-                dKB = mfma_k4(aAqkT[ks], qts, dKB);
-                dKB = mfma_k4(aAT[ks], kts, dKB);
-            }
-            float dgc = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * ak + j;
-                const float dQt = dQs[tt][j] + dQ[j], dKt = dKs[tt][j] + dK[j];
-                const float dKbG = dKG[j];
-                const float dKb = dKB[j] + F.gam[c] * dKbG;
-                dgc += dKbG * F.kb[r][c];
-                const float e = F.e[r][c];
-                if (r < len && c < kd) {
-                    const size_t off = ((size_t)(t0 + r) * H + h) * kd + c;
-                    dq[off] = tobf16(dQt * e);
-                    dk[off] = tobf16(dKt * e + dKb / e);
-                }
-                // dG (natural log) of this row, stored over dO
-                L.dol[r][c] = dKt * F.kt[r][c] + dQt * F.qt[r][c] - dKb * F.kb[r][c];
-            }
-            // sum over the four row groups (lanes l, l^16, l^32, l^48)
-            dgc += __shfl_xor(dgc, 16, 64);
-            dgc += __shfl_xor(dgc, 32, 64);
-            if (ak == 0) {
-                L.dgam2[c] = dgc;
-            }
-        }
-    }
-    __syncthreads();
-    if (tid < HD) {
-        // reverse cumulative sum of dG is the gradient of the per-token log-decay;
-        // then the gate chain
-        const int c = tid;
-        const float dgam = L.dgam[c] + L.dgam2[c];
-        float acc = dgam * F.gam[c];
-        float pdtb = 0.f, pa = 0.f;
-#pragma unroll
-        for (int s = CS - 1; s >= 0; --s) {
-            acc += L.dol[s][c];
-            if (s < len) {
-                const size_t off = ((size_t)(t0 + s) * H + h) * kd + c;
-                const float y = ysv[s];                 // as in chunk_factors, same thread
-                const float dy = y >= lb ? acc : 0.f;
-                const float dx = -dy * Aexp * sgv[s];
-                if (c < kd) dg[off] = tobf16(dx);
-                pdtb += dx;
-                pa += dy * y;
-            }
-        }
-        part_dtb[sh * HD + c] = pdtb;
-        // sum pa over the 128 channel threads (two waves) in a fixed order
-        for (int o = 32; o >= 1; o >>= 1) pa += __shfl_xor(pa, o, 64);
-        if ((tid & 63) == 0) L.red[tid >> 6] = pa;
-    } else if (tid < HD + CS) {
-        // beta enters P = T diag(beta) and L = diag(beta) A
-        const int r = tid - HD;
+        // beta enters P (column sums of dP o T) and L (row sums of dL o A)
+        const f32x4_t dLt = tr16(L.tile, dL);
         float db = 0.f;
-        for (int s = 0; s < CS; ++s) db += Lt.dP[s][r] * F.T[s][r] + Lt.dL[r][s] * F.A[r][s];
-        if (r < len) {
-            const float b = F.beta[r];
-            dbeta[(size_t)(t0 + r) * H + h] = tobf16(db * b * (1.f - b));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) db += dP[j] * Tm[j] + dLt[j] * Amt[j];
+        db += __shfl_xor(db, 16, 64);
+        db += __shfl_xor(db, 32, 64);
+        if (grp == 0 && live) dbeta[(size_t)(t0 + tok) * H + h] = tobf16(db * bc * (1.f - bc));
+    }
+    // B operands of the per-channel products
+    u32x2_t qAh, qAl, aAh, aAl, pTh, pTl, dQh, dQl, dAh, dAl;
+    split4(tr16(L.tile, dAqk), qAh, qAl);                  // dAqk^T
+    split4(tr16(L.tile, dA), aAh, aAl);                    // dA^T
+    split4(Pt, pTh, pTl);
+    split4(dAqk, dQh, dQl);
+    split4(dA, dAh, dAl);
+
+    // ---- per state row tile t (channels 32kb + 8grp + 4hh + j of each
+    // token, kb = t/2, hh = t%2): gradients of Qt, Kt, Kb, then q, k, the gate
+    const __amdgpu_buffer_rsrc_t r_dq = make_rsrc(dq + rbase, rbytes);
+    const __amdgpu_buffer_rsrc_t r_dk = make_rsrc(dk + rbase, rbytes);
+    const __amdgpu_buffer_rsrc_t r_dg = make_rsrc(dg + rbase, rbytes);
+    // q, k and g again, four channels at a time (the first loads are
+    // cache hits), so that the chunk's inputs need not stay in registers
+    const __amdgpu_buffer_rsrc_t r_q = make_rsrc(q + rbase, rbytes);
+    const __amdgpu_buffer_rsrc_t r_k = make_rsrc(k + rbase, rbytes);
+    const __amdgpu_buffer_rsrc_t r_g = make_rsrc(g + rbase, rbytes);
+    float pa = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int kb = t >> 1, hh = t & 1, c0 = 32 * kb + 8 * grp + 4 * hh;
+        const int off = (int)((tok * rowe + c0) * 2);
+        u32x4_t gq = {0u, 0u, 0u, 0u}, kq = gq, qq = gq;    // words 2hh, 2hh + 1 used
+        {
+            const u32x2_t gw = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r_g, off, 0, 0));
+            const u32x2_t kw = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r_k, off, 0, 0));
+            const u32x2_t qw = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r_q, off, 0, 0));
+            gq[2 * hh] = gw[0]; gq[2 * hh + 1] = gw[1];
+            kq[2 * hh] = kw[0]; kq[2 * hh + 1] = kw[1];
+            qq[2 * hh] = qw[0]; qq[2 * hh + 1] = qw[1];
+        }
+        float G[4];
+        block_decay<4>(gq, L.dtb, kb, 4 * hh, A, lb2, live, G);
+        // as in the factors: Kt, Qt, Kb rescaled by e^{-+G_last/2} (rs, ri) for
+        // the products with the 16 x 16 gradients, whose results are then
+        // scaled back into dq = dQt e^G and dk = dKt e^G + dKb e^-G directly
+        const f32x4_t glv = *(const f32x4_t *)&L.gl[c0];
+        float e[4], rs[4], ri[4], kg[4], kv[4], qv[4], kt[4], qt[4], kbv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float gh = 0.5f * glv[j];
+            e[j] = fast_exp2(G[j]);
+            rs[j] = fast_exp2(G[j] - gh);
+            ri[j] = fast_exp2(gh - G[j]);
+            kg[j] = fast_exp2(glv[j] - G[j]);               // e^{G_last - G}
+            kv[j] = elem(kq, 4 * hh + j);
+            qv[j] = elem(qq, 4 * hh + j);
+            kt[j] = kv[j] * rs[j];
+            qt[j] = qv[j] * rs[j];
+            kbv[j] = kv[j] * ri[j];
+        }
+        // (hi, lo) bf16 of the four channels: the A operand of the identity
+        // that yields their W^T tile
+        u32x2_t kth, ktl, qth, qtl, kbh, kbl;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            uint32_t a, b;
+            split2(kt[2 * w], kt[2 * w + 1], a, b); kth[w] = a; ktl[w] = b;
+            split2(qt[2 * w], qt[2 * w + 1], a, b); qth[w] = a; qtl[w] = b;
+            split2(kbv[2 * w], kbv[2 * w + 1], a, b); kbh[w] = a; kbl[w] = b;
+        }
+        const u32x2_t bwh = to_wt(kbh, eye), bwl = to_wt(kbl, eye);
+        const u32x2_t qwh = to_wt(qth, eye), qwl = to_wt(qtl, eye);
+        const u32x2_t kwh = to_wt(kth, eye), kwl = to_wt(ktl, eye);
+        // rows chan(t, .) of (dAqk Kb)^T, (dA Kb)^T, (P dWm)^T and
+        // (dAqk^T Qt + dA^T Kt)^T: this lane's token, channels c0 + j
+        const f32x4_t pq = mm3_k16(bwh, bwl, qAh, qAl, zero);
+        const f32x4_t pk = mm3_k16(bwh, bwl, aAh, aAl, zero);
+        const f32x4_t pg = mm3_k16(wwh[t], wwl[t], pTh, pTl, zero);
+        const f32x4_t pb = mm3_k16(kwh, kwl, dAh, dAl, mm3_k16(qwh, qwl, dQh, dQl, zero));
+        const f32x4_t qs = L.qs[t][l], ks = L.ks[t][l];
+        const f32x4_t gm = *(const f32x4_t *)&L.gam[c0], dgs = *(const f32x4_t *)&L.dgs[c0];
+        const f32x4_t dtb2 = *(const f32x4_t *)&L.dtb[c0];
+        const float daq = L.daq[tok];
+        float vq[4], vk[4], vg[4], pd[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // dQt e^G, dKt e^G and dKb e^-G (dKb = dAqk^T Qt + dA^T Kt + Gam P dWm),
+            // without the diagonal of dAqk
+            const float dQe = scale * qs[j] * e[j] + pq[j] * rs[j];
+            const float dKe = pk[j] * rs[j] - ks[j] * e[j];
+            const float dKi = pb[j] * ri[j] + pg[j] * kg[j];
+            // dG = dKt Kt + dQt Qt - dKb Kb, from the scaled terms
+            const float dG = dQe * qv[j] + (dKe - dKi) * kv[j];
+            // the chunk decay times its gradient: diag(dS1 S0^T) and the Wm
+            // path's sum over tokens of (P dWm) o Kb Gam
+            const float gdg = gm[j] * dgs[j] + row_sum16(pg[j] * kv[j] * kg[j]);
+            // per-token log-decay (natural log): reverse cumulative sum of dG,
+            // plus the chunk decay's term, which every token's decay enters
+            const float acc = gdg + row_suffix16(dG);
+            // the gate a = max(y, lb), y = -A softplus(g + dt_bias): no
+            // gradient through the clamped branch; dy/dA_log = y
+            const float x2 = elem(gq, 4 * hh + j) * LOG2E + dtb2[j];
+            const float y2 = A > 0.f ? -A * fast_log2(1.f + fast_exp2(x2)) : 0.f;
+            const float dy = (live && y2 >= lb2) ? acc : 0.f;
+            const float dx = -dy * A * __builtin_amdgcn_rcpf(1.f + fast_exp2(-x2));
+            pa += dy * (y2 * LN2);
+            pd[j] = row_sum16(dx);
+            vq[j] = dQe + daq * kv[j];
+            vk[j] = dKe + dKi + daq * qv[j];
+            vg[j] = dx;
+        }
+        const u32x2_t oq = {pack2(vq[0], vq[1]), pack2(vq[2], vq[3])};
+        const u32x2_t ok = {pack2(vk[0], vk[1]), pack2(vk[2], vk[3])};
+        const u32x2_t og = {pack2(vg[0], vg[1]), pack2(vg[2], vg[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(oq, r_dq, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(ok, r_dk, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(og, r_dg, off, 0, 0);
+        if (tok == 0) *(f32x4_t *)&part_dtb[sh * HD + c0] = *(const f32x4_t *)&pd[0];
+    }
+    if (tok == 0) {                                         // channels past the head dimension
+#pragma unroll
+        for (int kb = NKB; kb < HD / 32; ++kb) {
+            float *o = part_dtb + sh * HD + 32 * kb + 8 * grp;
+            *(f32x4_t *)&o[0] = zero;
+            *(f32x4_t *)&o[4] = zero;
         }
     }
-    __syncthreads();
-    if (tid == 0) part_alog[sh] = L.red[0] + L.red[1];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) pa += __shfl_xor(pa, o, 64);
+    if (l == 0) part_alog[sh] = pa;
 }
 
 // ---------------------------------------------------------------------------
@@ -705,9 +916,12 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
     if (e == hipSuccess)
         e = launch_bwd_rscan(dout, rrec, cu, N, T, H, K, dfin, dinit, dv, dst1, dxws, stream);
     mark(3);
-    hipLaunchKernelGGL(bwd_chunk_kernel, chunks, dim3(BT), 0, stream,
-                       q, k, g, beta, A_log, dt_bias, lower_bound, scale, dout, cu, N, T, H, K,
-                       st0, dst1, xws, dxws, dq, dk, dg, dbeta, palog, pdtb);
+#define KDA_BWD_CHUNK(KD_)                                                                    \
+    hipLaunchKernelGGL(bwd_chunk_kernel<KD_>, chunks, dim3(64), 0, stream, q, k, g, beta, A_log, \
+                       dt_bias, lower_bound, scale, dout, cu, N, T, H, st0, dst1, xws, dxws, dq, dk, \
+                       dg, dbeta, palog, pdtb)
+    if (K == HD) KDA_BWD_CHUNK(HD); else KDA_BWD_CHUNK(64);
+#undef KDA_BWD_CHUNK
     mark(4);
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)H), dim3(HD), 0, stream,
                        palog, pdtb, num_slots, H, K, dA_log, ddt_bias);
