@@ -227,11 +227,17 @@ kda_status_t kda_decode(const void *q, const void *k, const void *v, const void 
  *   ddt_bias       fp32 [H*K] or NULL (not written)
  *   d_initial_state fp32 [N, H, K, V] or NULL (not written)
  *
- * Arithmetic is fp32 throughout; every sum runs in a fixed order, so the
- * results are bitwise reproducible.  Device workspace of about 157 KiB per
- * (16-token chunk slot, head) comes from the library's stream-ordered pool
- * (the fp32 chunk factors and every chunk's start state and state
- * gradient).  Returns KDA_OK, KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED
+ * Products run on bf16 MFMAs with fp32 accumulation: the stored states and
+ * the scans' records are bf16, and fp32 operands whose precision matters
+ * enter as (hi, lo) bf16 pairs; elementwise work is fp32.  Every sum runs in
+ * a fixed order, so the results are bitwise reproducible.  Device workspace
+ * of about 110 KiB per (16-token chunk slot, head) comes from the library's
+ * stream-ordered pool (the two scans' records, every chunk's start state and
+ * state gradient in bf16, X and dX in fp32).  The reverse scan runs on a
+ * second stream the library creates once per device (non-blocking, default
+ * priority), forked from `stream` after the prep kernel and joined back
+ * before the chunk kernel by events, so the call as a whole stays ordered on
+ * `stream`.  Returns KDA_OK, KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED
  * before any HIP call, KDA_ERR_OUT_OF_MEMORY, or KDA_ERR_LAUNCH.
  */
 kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
@@ -351,8 +357,10 @@ kda_status_t kda_set_stage_events(void *before_intra, void *before_scan, void *a
 /*
  * kda_set_bwd_stage_events — the same instrumentation for kda_bwd: `events`
  * is NULL (stop) or an array of six hipEvent_t handles, recorded on the
- * call's stream before each of the five backward kernels (prep, states,
- * dstates, chunk, reduce) and after the last.  Per host thread; the array is
+ * call's stream: before the prep kernel, before the two scans, after the
+ * states scan, after both scans (the reverse scan runs beside the states
+ * scan on a library-owned second stream and is joined here), after the
+ * chunk kernel and after the reduce kernel.  Per host thread; the array is
  * read at this call and the events are not owned.  Always returns KDA_OK.
  */
 kda_status_t kda_set_bwd_stage_events(void *const *events);

@@ -40,6 +40,8 @@
 // Every sum runs in a fixed order, so results are bitwise reproducible.
 #include <math.h>
 
+#include <mutex>
+
 #include "kda_device.h"
 #include "kda_intra_dev.h"                            // mm16: 16 x 16 fp32 products on MFMA
 #include "kda_launch.h"
@@ -874,6 +876,45 @@ __global__ __launch_bounds__(HD) void bwd_reduce_kernel(
 
 }  // namespace
 
+// One side stream (and its fork / join events) per device, created on first
+// use and kept for the life of the process.  The mutex makes each call's
+// record / wait / launch sequence on them atomic with respect to other host
+// threads.
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int MAX_DEVICES = 64;
+std::mutex g_side_mutex;
+SideStream g_side[MAX_DEVICES];
+
+// The current device's side stream (called with g_side_mutex held).
+hipError_t side_stream(SideStream *&out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    SideStream &ss = g_side[dev];
+    if (!ss.stream) {
+        hipStream_t st = nullptr;
+        hipEvent_t a = nullptr, b = nullptr;
+        e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&b, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            if (b) (void)hipEventDestroy(b);
+            if (a) (void)hipEventDestroy(a);
+            if (st) (void)hipStreamDestroy(st);
+            return e;
+        }
+        ss.fork = a;
+        ss.join = b;
+        ss.stream = st;
+    }
+    out = &ss;
+    return hipSuccess;
+}
+
 size_t bwd_workspace_bytes(int64_t num_slots, int H) {
     const size_t sh = (size_t)num_slots * H;
     return sh * ((size_t)StatesRec::BYTES + (size_t)RecLayout<HD>::BYTES +
@@ -910,11 +951,24 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
     hipLaunchKernelGGL(bwd_prep_kernel, chunks, dim3(BT), 0, stream,
                        q, k, g, beta, A_log, dt_bias, lower_bound, scale, cu, N, T, H, K, srec, rrec);
     mark(1);
-    if (e == hipSuccess)
-        e = launch_bwd_fscan(v, srec, cu, N, T, H, K, init, init_fp32, st0, xws, stream);
-    mark(2);
-    if (e == hipSuccess)
-        e = launch_bwd_rscan(dout, rrec, cu, N, T, H, K, dfin, dinit, dv, dst1, dxws, stream);
+    // The reverse scan needs only the prep kernel's records and dO, not the
+    // states scan's output: it runs on the device's side stream, forked after
+    // prep and joined before the chunk kernel, so that the two
+    // latency-bound scans share the compute units.
+    if (e == hipSuccess) {
+        std::lock_guard<std::mutex> lock(g_side_mutex);
+        SideStream *ss = nullptr;
+        e = side_stream(ss);
+        if (e == hipSuccess) e = hipEventRecord(ss->fork, stream);
+        if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
+        if (e == hipSuccess)
+            e = launch_bwd_rscan(dout, rrec, cu, N, T, H, K, dfin, dinit, dv, dst1, dxws, ss->stream);
+        if (e == hipSuccess) e = hipEventRecord(ss->join, ss->stream);
+        if (e == hipSuccess)
+            e = launch_bwd_fscan(v, srec, cu, N, T, H, K, init, init_fp32, st0, xws, stream);
+        mark(2);
+        if (e == hipSuccess) e = hipStreamWaitEvent(stream, ss->join, 0);
+    }
     mark(3);
 #define KDA_BWD_CHUNK(KD_)                                                                    \
     hipLaunchKernelGGL(bwd_chunk_kernel<KD_>, chunks, dim3(64), 0, stream, q, k, g, beta, A_log, \

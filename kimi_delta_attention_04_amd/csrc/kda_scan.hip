@@ -460,7 +460,7 @@ __global__ __launch_bounds__(64 * (NW + 1), VD > HD ? 1 : (CT == 2 ? 3 : 2)) voi
 // One slice per wave on the 128-wide tiles (K = V = 128, or 64 with V = 64
 // columns and the rows from 64 on zero).
 template <int NW, int VD>
-__global__ __launch_bounds__(64 * (NW + 1), 2) void rscan_kernel(
+__global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
     const uint16_t *__restrict__ dout, const uint8_t *__restrict__ rrec,
     const int32_t *__restrict__ cu, int N, int T, int H,
     const float *__restrict__ dfin, float *__restrict__ dinit, uint16_t *__restrict__ dv,
@@ -678,7 +678,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 2) void rscan_kernel(
 // chunk decay; its Qt and M slots are not used.  One slice per wave on the
 // 128-wide tiles (K = V = 128, or 64 with V = 64 columns).
 template <int NW, int VD>
-__global__ __launch_bounds__(64 * (NW + 1), 2) void fscan_kernel(
+__global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
     const uint16_t *__restrict__ v, const uint8_t *__restrict__ srec,
     const int32_t *__restrict__ cu, int N, int T, int H,
     const void *__restrict__ init, int init_fp32, uint16_t *__restrict__ s0, float *__restrict__ xws)
@@ -931,22 +931,34 @@ hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, 
     return hipGetLastError();
 }
 
+// Column-part width of the backward's two scans, which run side by side
+// (the reverse scan on a second stream): the narrowest of 32, 64 and 128
+// columns (V = 64: 32 or 64) at which the workgroups of both fit on the
+// compute units at once, one each, else the widest.  A scan workgroup of
+// one part cannot share a compute unit with one of the other scan, so a
+// width that overfills the chip leaves part of the second scan waiting for
+// the first.
+int bwd_scan_width(int64_t units, int V) {
+    const int64_t cus = num_cus();
+    const int64_t u8 = 8 * ((units + 7) / 8);
+    for (int cw = 32; cw < V; cw *= 2)
+        if (2 * (V / cw) * u8 <= cus) return cw;
+    return V;
+}
+
 hipError_t launch_bwd_rscan(const uint16_t *dout, const uint8_t *rrec, const int32_t *cu, int N,
                             int T, int H, int V, const float *dfin, float *dinit, uint16_t *dv,
                             uint16_t *ds1, float *dxws, hipStream_t stream)
 {
     const int64_t units = (int64_t)N * H;
     if (units <= 0) return hipSuccess;
-    // parts of 32 columns while four (two at V = 64) parts a head leave
-    // compute units free, else 64 columns
-    const int cus = num_cus();
-    const int cw = (V / 32) * units <= cus ? 32 : 64;
+    const int cw = bwd_scan_width(units, V);
     const int64_t blocks = 8 * (V / cw) * ((units + 7) / 8);
 #define KDA_RSCAN(NW_, VD_)                                                                       \
     hipLaunchKernelGGL((rscan_kernel<NW_, VD_>), dim3((unsigned)blocks), dim3(64 * (NW_ + 1)), 0, stream, \
                        dout, rrec, cu, N, T, H, dfin, dinit, dv, ds1, dxws)
     if (V == HD) {
-        if (cw == 32) KDA_RSCAN(2, HD); else KDA_RSCAN(4, HD);
+        if (cw == 32) KDA_RSCAN(2, HD); else if (cw == 64) KDA_RSCAN(4, HD); else KDA_RSCAN(8, HD);
     } else {
         if (cw == 32) KDA_RSCAN(2, 64); else KDA_RSCAN(4, 64);
     }
@@ -960,14 +972,13 @@ hipError_t launch_bwd_fscan(const uint16_t *v, const uint8_t *srec, const int32_
 {
     const int64_t units = (int64_t)N * H;
     if (units <= 0) return hipSuccess;
-    const int cus = num_cus();
-    const int cw = (V / 32) * units <= cus ? 32 : 64;
+    const int cw = bwd_scan_width(units, V);
     const int64_t blocks = 8 * (V / cw) * ((units + 7) / 8);
 #define KDA_FSCAN(NW_, VD_)                                                                       \
     hipLaunchKernelGGL((fscan_kernel<NW_, VD_>), dim3((unsigned)blocks), dim3(64 * (NW_ + 1)), 0, stream, \
                        v, srec, cu, N, T, H, init, init_fp32, s0, xws)
     if (V == HD) {
-        if (cw == 32) KDA_FSCAN(2, HD); else KDA_FSCAN(4, HD);
+        if (cw == 32) KDA_FSCAN(2, HD); else if (cw == 64) KDA_FSCAN(4, HD); else KDA_FSCAN(8, HD);
     } else {
         if (cw == 32) KDA_FSCAN(2, 64); else KDA_FSCAN(4, 64);
     }
