@@ -24,9 +24,10 @@
 // dA_log and ddt_bias (no gradient through the clamped branch).
 //
 // Five launches:
-//   prep    (chunk slot, head)  the chunk factors in fp32: Kt and Wm (with the
-//           chunk decay) for the states scan, and the reverse scan's bf16
-//           record (Wm, scale Qt, -Kt, scale M^T in MFMA operand layouts)
+//   prep    (chunk slot, head), one wave  the chunk factors into the states
+//           scan's record (Kt and Wm with the chunk decay, (hi, lo) bf16) and
+//           the reverse scan's bf16 record (Wm, scale Qt, -Kt, scale M^T),
+//           in MFMA operand layouts
 //   states  (sequence, head, column part)  forward scan on the forward
 //           scan's structure (kda_scan.hip), storing every chunk's start
 //           state S0 (bf16 rows) and X (fp32)
@@ -43,29 +44,14 @@
 #include <mutex>
 
 #include "kda_device.h"
-#include "kda_intra_dev.h"                            // mm16: 16 x 16 fp32 products on MFMA
+#include "kda_intra_dev.h"                            // intra_load, mm16, the decay prefix
 #include "kda_launch.h"
 
 namespace kda {
 
 namespace {
 
-constexpr int BT = 256;               // threads per workgroup
-constexpr int RS = HD + 4;            // padded LDS row stride (floats)
-constexpr int SP = CS + 1;            // padded stride of 16 x 16 tiles
-
-// The transcendentals on the hardware base-2 units (v_exp_f32, v_log_f32,
-// v_rcp_f32).  softplus keeps the form max(x, 0) + log(1 + e^-|x|), finite
-// for every finite x, so that -exp(A_log) softplus(x) is -0, not NaN, when
-// A_log = -inf.
 constexpr float LN2 = 0.6931471805599453f;
-__device__ __forceinline__ float softplus_f(float x) {
-    return fmaxf(x, 0.f) + LN2 * fast_log2(1.f + fast_exp2(-fabsf(x) * LOG2E));
-}
-__device__ __forceinline__ float sigmoid_f(float x) {
-    return __builtin_amdgcn_rcpf(1.f + fast_exp2(-x * LOG2E));
-}
-__device__ __forceinline__ float exp_f(float x) { return fast_exp2(x * LOG2E); }
 
 // Token range of chunk slot `slot`: returns its token count (0 for a gap
 // slot) and the first token row in t0.
@@ -80,227 +66,6 @@ __device__ int slot_chunk(const int32_t *cu, int N, int T, int64_t slot, int64_t
     t0 = start + (slot - seq_slot0(cu, lo, T)) * CS;
     return t0 >= end ? 0 : (int)min((int64_t)CS, end - t0);
 }
-
-// ---------------------------------------------------------------------------
-// Chunk factors of one (chunk, head) in LDS.  Rows from `len` on are padding:
-// zero k, q and beta and a zero log-decay, which makes every factor row and
-// column they touch zero (and e^{G_last} that of the last real token).
-// ---------------------------------------------------------------------------
-struct FactorsBase {
-    float kt[CS][RS], qt[CS][RS], kb[CS][RS], e[CS][RS];
-    float A[CS][SP], aqk[CS][SP], T[CS][SP], P[CS][SP], M[CS][SP];
-    float beta[CS], gam[HD], dtb[HD];
-};
-struct Factors : FactorsBase {
-    float wm[CS][RS];                 // Wm = P^T Kb Gam (the prep kernel's record)
-};
-
-// WANT_W: also form Wm in L.wm (L a Factors; the prep kernel stores it).  The
-// chunk kernel does not use Wm and passes a FactorsBase.
-// KEEP_GATE: also return, per row, the gate before its clamp,
-// y = -exp(A_log) softplus(g + dt_bias), and sigmoid(g + dt_bias) in ysv /
-// sgv (the calling thread's channel, threads below HD), for the gate chain
-// of the chunk kernel.
-template <bool WANT_W, bool KEEP_GATE = false, class FL>
-__device__ __forceinline__ void chunk_factors(FL &L, const uint16_t *__restrict__ q,
-                              const uint16_t *__restrict__ k, const uint16_t *__restrict__ g,
-                              const uint16_t *__restrict__ bl, float Aexp,
-                              const float *__restrict__ dt_bias, float lb, int64_t t0, int len,
-                              int H, int h, int kd, float *ysv = nullptr, float *sgv = nullptr) {
-    const int tid = threadIdx.x;
-    if (tid < HD) {
-        // one channel per thread: gate, in-chunk cumulative log-decay G
-        // (natural log) and the scaled rows
-        const int c = tid;
-        // head dimension kd = 64 runs on the 128-wide tiles: channels from kd
-        // on have zero k and q (and zero gate inputs), so every factor row
-        // and column they touch is zero
-        const bool ch = c < kd;
-        const int cc = ch ? c : 0;                   // an address that is always in range
-        const float dtb = (dt_bias && ch) ? dt_bias[(size_t)h * kd + c] : 0.f;
-        L.dtb[c] = dtb;
-        // every row's loads first and unconditionally, so that their
-        // latencies overlap (rows past len read row len-1; both are masked
-        // after the loads)
-        uint16_t gw[CS], kw[CS], qw[CS];
-#pragma unroll
-        for (int r = 0; r < CS; ++r) {
-            const size_t off = ((size_t)(t0 + (r < len ? r : len - 1)) * H + h) * kd + cc;
-            gw[r] = g[off];
-            kw[r] = k[off];
-            qw[r] = q[off];
-        }
-        float gr[CS], kr[CS], qr[CS];
-#pragma unroll
-        for (int r = 0; r < CS; ++r) {
-            gr[r] = ch ? bf16f(gw[r]) : 0.f;
-            kr[r] = ch ? bf16f(kw[r]) : 0.f;
-            qr[r] = ch ? bf16f(qw[r]) : 0.f;
-        }
-        float G = 0.f;
-#pragma unroll
-        for (int r = 0; r < CS; ++r) {
-            float kv = 0.f, qv = 0.f;
-            if (r < len) {
-                const float y = -Aexp * softplus_f(gr[r] + dtb);
-                if (KEEP_GATE) {
-                    ysv[r] = y;
-                    sgv[r] = sigmoid_f(gr[r] + dtb);
-                }
-                G += fmaxf(y, lb);
-                kv = kr[r];
-                qv = qr[r];
-            }
-            const float e = exp_f(G);
-            L.e[r][c] = e;
-            L.kt[r][c] = kv * e;
-            L.qt[r][c] = qv * e;
-            L.kb[r][c] = kv * exp_f(-G);
-        }
-        L.gam[c] = L.e[CS - 1][c];
-    } else if (tid < HD + CS) {
-        const int r = tid - HD;
-        L.beta[r] = r < len ? sigmoid_f(bf16f(bl[(size_t)(t0 + r) * H + h])) : 0.f;
-    }
-    __syncthreads();
-    {
-        // A = strict_lower(Kt Kb^T) on wave 0, Aqk = lower_incl(Qt Kb^T) on
-        // wave 1: fp32 16x16x4 MFMAs over the 128 channels (lane l supplies
-        // row l%16, channel 4ks + l/16 of each operand and holds rows
-        // 4(l/16) .. +3, column l%16 of the product)
-        const int wave = tid >> 6, l = tid & 63;
-        if (wave < 2) {
-            const float(&lhs)[CS][RS] = wave == 0 ? L.kt : L.qt;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-            for (int ks = 0; ks < HD / 4; ++ks)
-                acc = mfma_k4(lhs[l & 15][4 * ks + (l >> 4)], L.kb[l & 15][4 * ks + (l >> 4)], acc);
-            const int i = l & 15;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * (l >> 4) + j;
-                if (wave == 0) L.A[r][i] = i < r ? acc[j] : 0.f;
-                else L.aqk[r][i] = i <= r ? acc[j] : 0.f;
-            }
-        }
-    }
-    __syncthreads();
-    if (tid < 64) {
-        // T = (I + diag(beta) A)^-1 = (I - N)^-1 with N = -diag(beta) A
-        // strictly lower, hence nilpotent: (I + N)(I + N^2)(I + N^4)(I + N^8),
-        // on fp32 16x16x4 MFMAs in one wave.  Lane l holds rows 4(l/16) + j,
-        // column l%16 of each matrix and of its transpose (the A-operand
-        // layout of the matrix itself).
-        const int l = tid, grp = l >> 4, cg = l & 15;
-        f32x4_t N1, N1t, I;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 4 * grp + j;
-            N1[j] = -L.beta[r] * L.A[r][cg];          // A is zero on and above the diagonal
-            N1t[j] = -L.beta[cg] * L.A[cg][r];
-            I[j] = r == cg ? 1.f : 0.f;
-        }
-        const f32x4_t P1t = I + N1t;
-        const f32x4_t N2 = mm16(N1t, N1), N2t = mm16(N1, N1t);
-        const f32x4_t Q12t = mm16(I + N2, P1t);       // ((I+N)(I+N^2))^T
-        const f32x4_t N4 = mm16(N2t, N2), N4t = mm16(N2, N2t);
-        const f32x4_t Q3t = mm16(I + N4, Q12t);       // ((I+N)(I+N^2)(I+N^4))^T
-        const f32x4_t N8 = mm16(N4t, N4);
-        const f32x4_t Tm = mm16(Q3t, I + N8);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) L.T[4 * grp + j][cg] = Tm[j];
-    }
-    __syncthreads();
-    {
-        const int r = tid >> 4, i = tid & 15;
-        L.P[r][i] = L.T[r][i] * L.beta[i];
-    }
-    __syncthreads();
-    {
-        const int r = tid >> 4, i = tid & 15;
-        float m = 0.f;
-        for (int s = 0; s < CS; ++s) m += L.aqk[r][s] * L.P[s][i];
-        L.M[r][i] = m;
-        if constexpr (WANT_W) {
-            // Wm = P^T Kb Gam on fp32 16x16x4 MFMAs, wave w taking channel
-            // tiles 2w and 2w+1 (lane l: A = P^T row l%16, token 4ks + l/16;
-            // B = Kb token 4ks + l/16, channel l%16; result rows 4(l/16) + j)
-            const int wave = tid >> 6, l = tid & 63;
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const int c = 16 * (2 * wave + tt) + (l & 15);
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    acc = mfma_k4(L.P[4 * ks + (l >> 4)][l & 15], L.kb[4 * ks + (l >> 4)][c], acc);
-                const float gc = L.gam[c];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) L.wm[4 * (l >> 4) + j][c] = acc[j] * gc;
-            }
-        }
-    }
-    __syncthreads();
-}
-
-// ---------------------------------------------------------------------------
-// prep: the chunk factors in fp32, into the two scans' bf16 records (in the
-// forward record's MFMA operand layouts, RecLayout<HD>):
-//   states record (StatesRec): Kt and Wm = P^T Kb Gam as (hi, lo) bf16
-//     pairs in the Kt and W^T layouts, and the chunk decay, the operands of
-//     X = V - Kt S0 and S1 = Gam S0 + Wm^T X;
-//   reverse record: Wm as the A operand of Wm dS (the Kt slot), scale Qt
-//     and -Kt transposed as the A operands of the state-gradient update (the
-//     Qt and W^T slots, both in the W^T layout), scale M^T (the M slot) and
-//     the chunk decay.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(BT) void bwd_prep_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
-    const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb, float scale,
-    const int32_t *__restrict__ cu, int N, int T, int H, int kd, uint8_t *__restrict__ srec,
-    uint8_t *__restrict__ rrec)
-{
-    __shared__ __attribute__((aligned(16))) Factors L;
-    const int64_t slot = blockIdx.x / (unsigned)H;
-    const int h = (int)(blockIdx.x % (unsigned)H);
-    int64_t t0;
-    const int len = slot_chunk(cu, N, T, slot, t0);
-    if (len == 0) return;                                   // gap slot
-    chunk_factors<true>(L, q, k, g, beta, expf(A_log[h]), dt_bias, lb, t0, len, H, h, kd);
-    const int tid = threadIdx.x;
-
-    typedef RecLayout<HD> R;
-    typedef StatesRec SR;
-    uint8_t *sr = srec + ((size_t)slot * H + h) * SR::BYTES;
-    uint8_t *rr = rrec + ((size_t)slot * H + h) * R::BYTES;
-    uint16_t *s_kt = (uint16_t *)(sr + SR::KTH), *s_ktl = (uint16_t *)(sr + SR::KTL);
-    uint16_t *s_wt = (uint16_t *)(sr + SR::WTH), *s_wtl = (uint16_t *)(sr + SR::WTL);
-    uint16_t *r_kt = (uint16_t *)(rr + R::KTO), *r_qt = (uint16_t *)(rr + R::QT);
-    uint16_t *r_wt = (uint16_t *)(rr + R::WT), *r_m = (uint16_t *)(rr + R::M);
-    // Kt slot: element (kb, lane l, i) = X[l%16][32 kb + 8 (l/16) + i]
-    // W^T-layout slots: element (tp, lane l, 4 hf + j) = X[4 (l/16) + j][chan(2 tp + hf, l%16)]
-    for (int e = tid; e < 4 * 64 * 8; e += BT) {
-        const int kb = e >> 9, l = (e >> 3) & 63, i = e & 7;
-        const int ck = 32 * kb + 8 * (l >> 4) + i;
-        const float ktv = L.kt[l & 15][ck];
-        s_kt[e] = tobf16(ktv);
-        s_ktl[e] = tobf16(ktv - bf16f(s_kt[e]));
-        r_kt[e] = tobf16(L.wm[l & 15][ck]);
-        const int tok = 4 * (l >> 4) + (i & 3), ch = state_chan(2 * kb + (i >> 2), l & 15);
-        const float wmv = L.wm[tok][ch];
-        s_wt[e] = tobf16(wmv);
-        s_wtl[e] = tobf16(wmv - bf16f(s_wt[e]));
-        r_qt[e] = tobf16(scale * L.qt[tok][ch]);
-        r_wt[e] = tobf16(-L.kt[tok][ch]);
-    }
-    // M slot: element (lane l, j) = scale M[4 (l/16) + j][l%16]
-    r_m[tid] = tobf16(scale * L.M[4 * ((tid >> 2) >> 4) + (tid & 3)][(tid >> 2) & 15]);
-    if (tid < HD) {
-        ((float *)(sr + SR::GAM))[tid] = L.gam[tid];
-        ((float *)(rr + R::GAM))[tid] = L.gam[tid];
-    }
-}
-
 
 // ---------------------------------------------------------------------------
 // chunk: one wave per (chunk slot, head), everything that needs S0 and dS1
@@ -843,6 +608,207 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
 }
 
 // ---------------------------------------------------------------------------
+// prep: one wave per (chunk slot, head), the chunk factors into the two
+// scans' bf16 records (in the forward record's MFMA operand layouts,
+// RecLayout<HD>):
+//   states record (StatesRec): Kt and Wm = P^T Kb Gam as (hi, lo) bf16
+//     pairs in the Kt and W^T layouts, and the chunk decay, the operands of
+//     X = V - Kt S0 and S1 = Gam S0 + Wm^T X;
+//   reverse record: Wm in the Kt layout (the A operand of Wm dS), scale Qt
+//     and -Kt in the W^T layout (the A operands of the state-gradient
+//     update), scale M^T (the M slot) and the chunk decay.
+// The factors are formed as in the chunk kernel: Grams of the rescaled rows
+// from (hi, lo) operands, T on fp32 MFMAs, P^T Kb Gam from (hi, lo)
+// operands; layouts change through the identity.  Head dimension 64 runs on
+// all four channel blocks: its loads leave blocks 2 and 3 zero, which makes
+// their record entries zero.
+// ---------------------------------------------------------------------------
+struct PrepWaveLds {
+    float beta[CS];
+    float dtb[HD];                    // dt_bias in log2 units
+    float gam[HD];                    // e^{G_last} per key channel
+    float gl[HD];                     // G_last in log2 units
+    float tile[CS][CS + 1];           // 16 x 16 transposes
+};
+
+__global__ __launch_bounds__(64) void bwd_prep_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
+    const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb, float scale,
+    const int32_t *__restrict__ cu, int N, int T, int H, int kd, uint8_t *__restrict__ srec,
+    uint8_t *__restrict__ rrec)
+{
+    constexpr int NKB = HD / 32, NT = 2 * NKB;
+    typedef RecLayout<HD> R;
+    typedef StatesRec SR;
+    __shared__ __attribute__((aligned(16))) PrepWaveLds L;
+    const int64_t slot = blockIdx.x / (unsigned)H;
+    const int h = (int)(blockIdx.x % (unsigned)H);
+    const int l = threadIdx.x, tok = l & 15, grp = l >> 4;
+    const size_t sh = (size_t)slot * H + h;
+    int64_t t0;
+    const int len = slot_chunk(cu, N, T, slot, t0);
+    if (len == 0) return;                                   // gap slot: no scan reads it
+    const bool live = tok < len;
+    const float A = expf(A_log[h]);
+    const float lb2 = lb * LOG2E;
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+    const u32x2_t eye = identity_b();
+    uint8_t *sr = srec + sh * SR::BYTES;
+    uint8_t *rr = rrec + sh * R::BYTES;
+
+    stage_dtb<false, HD>(L.dtb, dt_bias, h, kd);
+    IntraIn in;
+    intra_load<false, HD>(in, q, k, g, beta, t0, len, H, h, kd);
+    {
+        const float x = bf16f((uint16_t)in.beta);
+        const float b = __builtin_amdgcn_rcpf(1.f + fast_exp2(-x * LOG2E));
+        if (grp == 0) L.beta[tok] = live ? b : 0.f;
+    }
+    wave_lds_sync();
+
+    // per channel block: the Grams (rescaled rows), Kt for the states record,
+    // scale Qt and -Kt for the reverse record, Kb Gam in the W^T layout
+    f32x4_t Akk = zero, AkkT = zero, Aqk = zero;
+    u32x2_t kgh[NT], kgl[NT];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        float G[8];
+        block_decay<8>(in.g[kb], L.dtb, kb, 0, A, lb2, live, G);
+        if (tok == CS - 1) {
+            f32x4_t g0, g1, l0, l1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                g0[i] = fast_exp2(G[i]); g1[i] = fast_exp2(G[4 + i]);
+                l0[i] = G[i]; l1[i] = G[4 + i];
+            }
+            *(f32x4_t *)&L.gam[32 * kb + 8 * grp] = g0;
+            *(f32x4_t *)&L.gam[32 * kb + 8 * grp + 4] = g1;
+            *(f32x4_t *)&L.gl[32 * kb + 8 * grp] = l0;
+            *(f32x4_t *)&L.gl[32 * kb + 8 * grp + 4] = l1;
+        }
+        wave_lds_sync();
+        float gl[8];
+        *(f32x4_t *)&gl[0] = *(const f32x4_t *)&L.gl[32 * kb + 8 * grp];
+        *(f32x4_t *)&gl[4] = *(const f32x4_t *)&L.gl[32 * kb + 8 * grp + 4];
+        u32x4_t kth, ktl, qth, qtl, kbh, kbl, kgh4, kgl4, Kh, Kl, qs, nk;
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+            float kt[2], qt[2], kbv[2], kg[2], Kt[2], sq[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i = 2 * wd + e;
+                const float gh = 0.5f * gl[i];
+                const float rs = fast_exp2(G[i] - gh), ri = fast_exp2(gh - G[i]);
+                const float eg = fast_exp2(G[i]);
+                const float kv = elem(in.k[kb], i), qv = elem(in.q[kb], i);
+                kt[e] = kv * rs;
+                qt[e] = qv * rs;
+                kbv[e] = kv * ri;
+                kg[e] = kv * fast_exp2(gl[i] - G[i]);
+                Kt[e] = kv * eg;
+                sq[e] = scale * (qv * eg);
+            }
+            uint32_t a, b;
+            split2(kt[0], kt[1], a, b); kth[wd] = a; ktl[wd] = b;
+            split2(qt[0], qt[1], a, b); qth[wd] = a; qtl[wd] = b;
+            split2(kbv[0], kbv[1], a, b); kbh[wd] = a; kbl[wd] = b;
+            split2(kg[0], kg[1], a, b); kgh4[wd] = a; kgl4[wd] = b;
+            split2(Kt[0], Kt[1], a, b); Kh[wd] = a; Kl[wd] = b;
+            qs[wd] = pack2(sq[0], sq[1]);
+            nk[wd] = pack2(-Kt[0], -Kt[1]);
+        }
+        Akk = mm3_k32(kth, ktl, kbh, kbl, Akk);             // Akk[r][c]  = Kt_r . Kb_c
+        AkkT = mm3_k32(kbh, kbl, kth, ktl, AkkT);           // AkkT[r][c] = Akk[c][r]
+        Aqk = mm3_k32(qth, qtl, kbh, kbl, Aqk);             // Aqk[r][c]  = Qt_r . Kb_c
+        __builtin_nontemporal_store(Kh, (u32x4_t *)(sr + SR::KTH + (kb * 64 + l) * 16));
+        __builtin_nontemporal_store(Kl, (u32x4_t *)(sr + SR::KTL + (kb * 64 + l) * 16));
+        u32x4_t qw, nw;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int t = 2 * kb + hh;
+            const u32x2_t kh2 = {kgh4[2 * hh], kgh4[2 * hh + 1]}, kl2 = {kgl4[2 * hh], kgl4[2 * hh + 1]};
+            const u32x2_t q2 = {qs[2 * hh], qs[2 * hh + 1]}, n2 = {nk[2 * hh], nk[2 * hh + 1]};
+            kgh[t] = to_wt(kh2, eye);
+            kgl[t] = to_wt(kl2, eye);
+            const u32x2_t a = to_wt(q2, eye);
+            const u32x2_t b = to_wt(n2, eye);
+            qw[2 * hh] = a[0]; qw[2 * hh + 1] = a[1];
+            nw[2 * hh] = b[0]; nw[2 * hh + 1] = b[1];
+        }
+        __builtin_nontemporal_store(qw, (u32x4_t *)(rr + R::QT + (kb * 64 + l) * 16));
+        __builtin_nontemporal_store(nw, (u32x4_t *)(rr + R::WT + (kb * 64 + l) * 16));
+    }
+    // the chunk decay into both records, one coalesced store each
+    wave_lds_sync();
+    {
+        const u32x2_t gv = *(const u32x2_t *)&L.gam[2 * l];
+        __builtin_nontemporal_store(gv, (u32x2_t *)(sr + SR::GAM + l * 8));
+        __builtin_nontemporal_store(gv, (u32x2_t *)(rr + R::GAM + l * 8));
+    }
+
+    // T = (I + diag(beta) strict_lower(Akk))^-1 as in the chunk kernel
+    float br[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) br[j] = L.beta[4 * grp + j];
+    const float bc = L.beta[tok];
+    f32x4_t Tm;
+    {
+        f32x4_t N1, N1t, I;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * grp + j;
+            N1[j] = tok < r ? -br[j] * Akk[j] : 0.f;
+            N1t[j] = r < tok ? -bc * AkkT[j] : 0.f;
+            I[j] = r == tok ? 1.f : 0.f;
+        }
+        const f32x4_t N2 = mm16(N1t, N1), N2t = mm16(N1, N1t);
+        const f32x4_t Q12t = mm16(I + N2, I + N1t);
+        const f32x4_t N4 = mm16(N2t, N2), N4t = mm16(N2, N2t);
+        const f32x4_t Q3t = mm16(I + N4, Q12t);
+        const f32x4_t N8 = mm16(N4t, N4);
+        Tm = mm16(Q3t, I + N8);
+    }
+    f32x4_t P, Aq;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        P[j] = Tm[j] * bc;                                  // P = T diag(beta)
+        Aq[j] = tok <= 4 * grp + j ? Aqk[j] : 0.f;          // lower_incl(Qt Kb^T)
+    }
+    {
+        // M = Aqk P; the M slot holds scale M^T as an A operand, i.e. scale M
+        // in the tile layout
+        const f32x4_t M = mm16(tr16(L.tile, Aq), P);
+        const u32x2_t mo = {pack2(scale * M[0], scale * M[1]), pack2(scale * M[2], scale * M[3])};
+        __builtin_nontemporal_store(mo, (u32x2_t *)(rr + R::M + l * 8));
+    }
+    // Wm = P^T Kb Gam, tile t in the W^T layout (A = P^T: the tile layout of
+    // P), as (hi, lo) for the states record and, through the identity, in
+    // the Kt layout for the reverse record
+    u32x2_t pAh, pAl;
+    split4(P, pAh, pAl);
+#pragma unroll
+    for (int tp = 0; tp < NKB; ++tp) {
+        u32x4_t wh, wl, wk;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int t = 2 * tp + hh;
+            const f32x4_t W = mm3_k16(pAh, pAl, kgh[t], kgl[t], zero);
+            u32x2_t a, b;
+            split4(W, a, b);
+            wh[2 * hh] = a[0]; wh[2 * hh + 1] = a[1];
+            wl[2 * hh] = b[0]; wl[2 * hh + 1] = b[1];
+            const f32x4_t d = mfma_k16(a, eye, zero);       // exact: bf16 values
+            wk[2 * hh] = pack2(d[0], d[1]);
+            wk[2 * hh + 1] = pack2(d[2], d[3]);
+        }
+        __builtin_nontemporal_store(wh, (u32x4_t *)(sr + SR::WTH + (tp * 64 + l) * 16));
+        __builtin_nontemporal_store(wl, (u32x4_t *)(sr + SR::WTL + (tp * 64 + l) * 16));
+        __builtin_nontemporal_store(wk, (u32x4_t *)(rr + R::KTO + (tp * 64 + l) * 16));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // reduce: per head, the parameter gradients summed over chunk slots in slot
 // order (128 threads: one channel each; dA_log by a fixed tree).
 // ---------------------------------------------------------------------------
@@ -948,7 +914,7 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
         if (events && events[i] && e == hipSuccess) e = hipEventRecord(events[i], stream);
     };
     mark(0);
-    hipLaunchKernelGGL(bwd_prep_kernel, chunks, dim3(BT), 0, stream,
+    hipLaunchKernelGGL(bwd_prep_kernel, chunks, dim3(64), 0, stream,
                        q, k, g, beta, A_log, dt_bias, lower_bound, scale, cu, N, T, H, K, srec, rrec);
     mark(1);
     // The reverse scan needs only the prep kernel's records and dO, not the
