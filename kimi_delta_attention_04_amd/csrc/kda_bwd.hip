@@ -496,24 +496,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     const __amdgpu_buffer_rsrc_t r_dq = make_rsrc(dq + rbase, rbytes);
     const __amdgpu_buffer_rsrc_t r_dk = make_rsrc(dk + rbase, rbytes);
     const __amdgpu_buffer_rsrc_t r_dg = make_rsrc(dg + rbase, rbytes);
-    // q, k and g again, four channels at a time (the first loads are
-    // cache hits), so that the chunk's inputs need not stay in registers
+    // q, k and g again, one 32-channel block at a time (cache hits, mostly),
+    // so that the chunk's inputs need not stay in registers
     const __amdgpu_buffer_rsrc_t r_q = make_rsrc(q + rbase, rbytes);
     const __amdgpu_buffer_rsrc_t r_k = make_rsrc(k + rbase, rbytes);
     const __amdgpu_buffer_rsrc_t r_g = make_rsrc(g + rbase, rbytes);
     float pa = 0.f;
+    u32x4_t oq, ok, og;                                     // one 16-byte row piece of each output
+    u32x4_t gq, kq, qq;                                     // and of each input, block kb
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int kb = t >> 1, hh = t & 1, c0 = 32 * kb + 8 * grp + 4 * hh;
-        const int off = (int)((tok * rowe + c0) * 2);
-        u32x4_t gq = {0u, 0u, 0u, 0u}, kq = gq, qq = gq;    // words 2hh, 2hh + 1 used
-        {
-            const u32x2_t gw = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r_g, off, 0, 0));
-            const u32x2_t kw = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r_k, off, 0, 0));
-            const u32x2_t qw = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r_q, off, 0, 0));
-            gq[2 * hh] = gw[0]; gq[2 * hh + 1] = gw[1];
-            kq[2 * hh] = kw[0]; kq[2 * hh + 1] = kw[1];
-            qq[2 * hh] = qw[0]; qq[2 * hh + 1] = qw[1];
+        if (hh == 0) {
+            const int off = (int)((tok * rowe + c0) * 2);
+            gq = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_g, off, 0, 0));
+            kq = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_k, off, 0, 0));
+            qq = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_q, off, 0, 0));
         }
         float G[4];
         block_decay<4>(gq, L.dtb, kb, 4 * hh, A, lb2, live, G);
@@ -586,12 +584,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
             vk[j] = dKe + dKi + daq * qv[j];
             vg[j] = dx;
         }
-        const u32x2_t oq = {pack2(vq[0], vq[1]), pack2(vq[2], vq[3])};
-        const u32x2_t ok = {pack2(vk[0], vk[1]), pack2(vk[2], vk[3])};
-        const u32x2_t og = {pack2(vg[0], vg[1]), pack2(vg[2], vg[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(oq, r_dq, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b64(ok, r_dk, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b64(og, r_dg, off, 0, 0);
+        oq[2 * hh] = pack2(vq[0], vq[1]);
+        oq[2 * hh + 1] = pack2(vq[2], vq[3]);
+        ok[2 * hh] = pack2(vk[0], vk[1]);
+        ok[2 * hh + 1] = pack2(vk[2], vk[3]);
+        og[2 * hh] = pack2(vg[0], vg[1]);
+        og[2 * hh + 1] = pack2(vg[2], vg[3]);
+        if (hh == 1) {                                      // both tiles of block kb done
+            const int off = (int)((tok * rowe + c0 - 4) * 2);
+            __builtin_amdgcn_raw_buffer_store_b128(oq, r_dq, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(ok, r_dk, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(og, r_dg, off, 0, 0);
+        }
         if (tok == 0) *(f32x4_t *)&part_dtb[sh * HD + c0] = *(const f32x4_t *)&pd[0];
     }
     if (tok == 0) {                                         // channels past the head dimension
