@@ -225,7 +225,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb, float scale,
     const uint16_t *__restrict__ dout, const int32_t *__restrict__ cu, int N, int T, int H,
     const uint16_t *__restrict__ st0, const uint16_t *__restrict__ dst1,
-    const float *__restrict__ xws, const float *__restrict__ dxws,
+    const uint16_t *__restrict__ xws, const uint16_t *__restrict__ dvv,
     uint16_t *__restrict__ dq, uint16_t *__restrict__ dk, uint16_t *__restrict__ dg,
     uint16_t *__restrict__ dbeta, float *__restrict__ part_alog, float *__restrict__ part_dtb)
 {
@@ -276,8 +276,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
         auto sld = [&](const uint16_t *b, int s, int t) {
             return *(const u32x4_t *)&b[((size_t)2 * s * HD + state_chan(t, tok)) * 16];
         };
-        const float *xr = xws + sh * CS * HD + tok * HD + 8 * grp;
-        const float *dxr = dxws + sh * CS * HD + tok * HD + 8 * grp;
+        const uint16_t *xr = xws + sh * CS * HD + tok * HD + 8 * grp;
+        const __amdgpu_buffer_rsrc_t r_dx = make_rsrc(dvv + rbase, rbytes);
         // a ring of DEPTH (S0, dS1) operand pairs in flight; the step loop
         // stays rolled so that the loads are issued where written
         constexpr int DEPTH = 4;
@@ -286,21 +286,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
         for (int p = 0; p < DEPTH; ++p) { ra[p] = sld(S0, 0, p); rd[p] = sld(DS, 0, p); }
         u32x4_t on = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_do, row_off(0), 0, 0));
-        f32x4_t xa = *(const f32x4_t *)&xr[0], xb = *(const f32x4_t *)&xr[4];
-        f32x4_t da = *(const f32x4_t *)&dxr[0], db = *(const f32x4_t *)&dxr[4];
+        u32x4_t xn = *(const u32x4_t *)&xr[0];
+        u32x4_t dn = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_dx, row_off(0), 0, 0));
 #pragma unroll 1
         for (int s = 0; s < NKB; ++s) {
-            const u32x4_t ob = on;
-            u32x4_t xh, xl, dxh, dxl;
-            split8(xa, xb, xh, xl);
-            split8(da, db, dxh, dxl);
+            const u32x4_t ob = on, xh = xn, dxh = dn;
             const bool more = s + 1 < NKB;
             if (more) {
                 on = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_do, row_off(s + 1), 0, 0));
-                xa = *(const f32x4_t *)&xr[32 * (s + 1)];
-                xb = *(const f32x4_t *)&xr[32 * (s + 1) + 4];
-                da = *(const f32x4_t *)&dxr[32 * (s + 1)];
-                db = *(const f32x4_t *)&dxr[32 * (s + 1) + 4];
+                xn = *(const u32x4_t *)&xr[32 * (s + 1)];
+                dn = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_dx, row_off(s + 1), 0, 0));
             }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
@@ -314,16 +309,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
                 }
                 QS[t] = mfma_k32(sa, ob, QS[t]);
                 KS[t] = mfma_k32(sa, dxh, KS[t]);
-                KS[t] = mfma_k32(sa, dxl, KS[t]);
                 WW[t] = mfma_k32(xh, sd, WW[t]);
-                WW[t] = mfma_k32(xl, sd, WW[t]);
                 float d = dgp[t];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) d = fmaf(elem(sa, i), elem(sd, i), d);
                 dgp[t] = d;
             }
             dM = mfma_k32(ob, xh, dM);
-            dM = mfma_k32(ob, xl, dM);
         }
     }
 #pragma unroll
@@ -888,7 +880,7 @@ hipError_t side_stream(SideStream *&out) {
 size_t bwd_workspace_bytes(int64_t num_slots, int H) {
     const size_t sh = (size_t)num_slots * H;
     return sh * ((size_t)StatesRec::BYTES + (size_t)RecLayout<HD>::BYTES +
-                 2 * (size_t)HD * HD * sizeof(uint16_t) + (2 * (size_t)CS * HD + HD + 1) * sizeof(float));
+                 (2 * (size_t)HD * HD + (size_t)CS * HD) * sizeof(uint16_t) + ((size_t)HD + 1) * sizeof(float));
 }
 
 hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
@@ -908,9 +900,8 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
     uint8_t *rrec = srec + sh * StatesRec::BYTES;
     uint16_t *st0 = (uint16_t *)(rrec + sh * RecLayout<HD>::BYTES);
     uint16_t *dst1 = st0 + sh * HD * HD;
-    float *xws = (float *)(dst1 + sh * HD * HD);
-    float *dxws = xws + sh * CS * HD;
-    float *pdtb = dxws + sh * CS * HD;
+    uint16_t *xws = dst1 + sh * HD * HD;
+    float *pdtb = (float *)(xws + sh * CS * HD);
     float *palog = pdtb + sh * HD;
     const dim3 chunks((unsigned)sh);
     hipError_t e = hipSuccess;
@@ -932,7 +923,7 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
         if (e == hipSuccess) e = hipEventRecord(ss->fork, stream);
         if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
         if (e == hipSuccess)
-            e = launch_bwd_rscan(dout, rrec, cu, N, T, H, K, dfin, dinit, dv, dst1, dxws, ss->stream);
+            e = launch_bwd_rscan(dout, rrec, cu, N, T, H, K, dfin, dinit, dv, dst1, ss->stream);
         if (e == hipSuccess) e = hipEventRecord(ss->join, ss->stream);
         if (e == hipSuccess)
             e = launch_bwd_fscan(v, srec, cu, N, T, H, K, init, init_fp32, st0, xws, stream);
@@ -942,7 +933,7 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
     mark(3);
 #define KDA_BWD_CHUNK(KD_)                                                                    \
     hipLaunchKernelGGL(bwd_chunk_kernel<KD_>, chunks, dim3(64), 0, stream, q, k, g, beta, A_log, \
-                       dt_bias, lower_bound, scale, dout, cu, N, T, H, st0, dst1, xws, dxws, dq, dk, \
+                       dt_bias, lower_bound, scale, dout, cu, N, T, H, st0, dst1, xws, dv, dq, dk, \
                        dg, dbeta, palog, pdtb)
     if (K == HD) KDA_BWD_CHUNK(HD); else KDA_BWD_CHUNK(64);
 #undef KDA_BWD_CHUNK

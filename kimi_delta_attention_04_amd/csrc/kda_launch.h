@@ -32,7 +32,7 @@ hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, 
 // stores per (chunk slot, head) S0 (bf16, [part of 16 columns][128 rows][16])
 // and X (fp32 [16][128]).
 hipError_t launch_bwd_fscan(const uint16_t *v, const uint8_t *srec, const int32_t *cu, int N, int T,
-                            int H, int V, const void *init, int init_fp32, uint16_t *s0, float *xws,
+                            int H, int V, const void *init, int init_fp32, uint16_t *s0, uint16_t *xws,
                             hipStream_t stream);
 
 // Reverse scan of the backward (K = V = 128 or 64): the state gradient from
@@ -42,7 +42,7 @@ hipError_t launch_bwd_fscan(const uint16_t *v, const uint8_t *srec, const int32_
 // 16 columns][128 rows][16]) and dX (fp32 [16][128]).
 hipError_t launch_bwd_rscan(const uint16_t *dout, const uint8_t *rrec, const int32_t *cu, int N,
                             int T, int H, int V, const float *dfin, float *dinit, uint16_t *dv,
-                            uint16_t *ds1, float *dxws, hipStream_t stream);
+                            uint16_t *ds1, hipStream_t stream);
 
 // One-token decode step on N x H states of D x D (D = 64, 128 or 256) in
 // place (fp32 or bf16).

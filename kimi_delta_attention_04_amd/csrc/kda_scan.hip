@@ -464,7 +464,7 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
     const uint16_t *__restrict__ dout, const uint8_t *__restrict__ rrec,
     const int32_t *__restrict__ cu, int N, int T, int H,
     const float *__restrict__ dfin, float *__restrict__ dinit, uint16_t *__restrict__ dv,
-    uint16_t *__restrict__ ds1, float *__restrict__ dxws)
+    uint16_t *__restrict__ ds1)
 {
     constexpr int CW = NW * 16;
     constexpr int V = VD;
@@ -604,14 +604,11 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
             S[2 * tp] = mfma_k16(klo, dXb, S[2 * tp]);
             S[2 * tp + 1] = mfma_k16(khi, dXb, S[2 * tp + 1]);
         }
-        // stores (off the chain): dX in fp32 for the chunk kernel (rows past
-        // the chunk's tokens are zeros), dV = dX in bf16 through the identity
-        // (lane (grp, cg): token cg, columns 4grp .. +3), dS1 in bf16 as rows
-        // (the identity turns tile t into lane (grp, cg): state row
-        // chan(t, cg), columns 4grp .. +3 of the slice)
-        float *xo = dxws + sh * CS * HD + col0 + wcol0 + cg;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xo[(4 * grp + j) * HD] = dX[j];
+        // stores (off the chain): dV = dX in bf16 through the identity (lane
+        // (grp, cg): token cg, columns 4grp .. +3), which the chunk kernel
+        // also takes as dX, and dS1 in bf16 as rows (the identity turns tile
+        // t into lane (grp, cg): state row chan(t, cg), columns 4grp .. +3 of
+        // the slice)
         const __amdgpu_buffer_rsrc_t ro =
             make_rsrc(dv_base + (size_t)ci * row_stride, (uint32_t)((len - 1) * row_bytes + CW * 2));
         const f32x4_t vt = mfma_k16(dXb, eye, zero);
@@ -681,7 +678,7 @@ template <int NW, int VD>
 __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
     const uint16_t *__restrict__ v, const uint8_t *__restrict__ srec,
     const int32_t *__restrict__ cu, int N, int T, int H,
-    const void *__restrict__ init, int init_fp32, uint16_t *__restrict__ s0, float *__restrict__ xws)
+    const void *__restrict__ init, int init_fp32, uint16_t *__restrict__ s0, uint16_t *__restrict__ xws)
 {
     constexpr int CW = NW * 16;
     constexpr int V = VD;
@@ -834,10 +831,14 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
             S[2 * tp] = mfma_k16(l0, Xb, S[2 * tp]);
             S[2 * tp + 1] = mfma_k16(l1, Xb, S[2 * tp + 1]);
         }
-        // stores (off the chain): X in fp32, S0 in bf16 as rows (see rscan_kernel)
-        float *xo = xws + sh * CS * HD + col0 + wcol0 + cg;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xo[(4 * grp + j) * HD] = X[j];
+        // stores (off the chain): X in bf16 through the identity (lane (grp,
+        // cg): token cg, columns 4grp .. +3, [16][128] per chunk), S0 in bf16
+        // as rows (see rscan_kernel)
+        {
+            const f32x4_t xt = mfma_k16(Xb, eye, zero);
+            const u32x2_t xv = {pack2(xt[0], xt[1]), pack2(xt[2], xt[3])};
+            *(u32x2_t *)&xws[sh * CS * HD + cg * HD + col0 + wcol0 + 4 * grp] = xv;
+        }
         uint16_t *so = s0 + sh * HD * HD + (size_t)p16 * HD * 16 + 4 * grp;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -948,7 +949,7 @@ int bwd_scan_width(int64_t units, int V) {
 
 hipError_t launch_bwd_rscan(const uint16_t *dout, const uint8_t *rrec, const int32_t *cu, int N,
                             int T, int H, int V, const float *dfin, float *dinit, uint16_t *dv,
-                            uint16_t *ds1, float *dxws, hipStream_t stream)
+                            uint16_t *ds1, hipStream_t stream)
 {
     const int64_t units = (int64_t)N * H;
     if (units <= 0) return hipSuccess;
@@ -956,7 +957,7 @@ hipError_t launch_bwd_rscan(const uint16_t *dout, const uint8_t *rrec, const int
     const int64_t blocks = 8 * (V / cw) * ((units + 7) / 8);
 #define KDA_RSCAN(NW_, VD_)                                                                       \
     hipLaunchKernelGGL((rscan_kernel<NW_, VD_>), dim3((unsigned)blocks), dim3(64 * (NW_ + 1)), 0, stream, \
-                       dout, rrec, cu, N, T, H, dfin, dinit, dv, ds1, dxws)
+                       dout, rrec, cu, N, T, H, dfin, dinit, dv, ds1)
     if (V == HD) {
         if (cw == 32) KDA_RSCAN(2, HD); else if (cw == 64) KDA_RSCAN(4, HD); else KDA_RSCAN(8, HD);
     } else {
@@ -967,7 +968,7 @@ hipError_t launch_bwd_rscan(const uint16_t *dout, const uint8_t *rrec, const int
 }
 
 hipError_t launch_bwd_fscan(const uint16_t *v, const uint8_t *srec, const int32_t *cu, int N, int T,
-                            int H, int V, const void *init, int init_fp32, uint16_t *s0, float *xws,
+                            int H, int V, const void *init, int init_fp32, uint16_t *s0, uint16_t *xws,
                             hipStream_t stream)
 {
     const int64_t units = (int64_t)N * H;
