@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_api.hip", "kda_intra.hip", "kda_scan.hip",
-           "kda_decode.hip", "kda_bwd.hip"]
+           "kda_decode.hip", "kda_bwd.hip", "kda_bwd_scan.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: no packed fp32 VALU instructions in the device code.

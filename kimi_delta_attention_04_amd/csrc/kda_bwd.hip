@@ -29,11 +29,12 @@
 //           the reverse scan's bf16 record (Wm, scale Qt, -Kt, scale M^T),
 //           in MFMA operand layouts
 //   states  (sequence, head, column part)  forward scan on the forward
-//           scan's structure (kda_scan.hip), storing every chunk's start
-//           state S0 (bf16 rows) and X (fp32)
+//           scan's structure (kda_bwd_scan.hip), storing every chunk's start
+//           state S0 (bf16 rows) and X (bf16)
 //   rscan   (sequence, head, column part)  reverse scan of dS on the same
-//           structure, storing every chunk's dS1 (bf16 rows) and dX,
-//           writing dv and the initial-state gradient
+//           structure, beside the states scan on a second stream, storing
+//           every chunk's dS1 (bf16 rows), writing dv (= dX, which the
+//           chunk kernel reads back) and the initial-state gradient
 //   chunk   (chunk slot, head), one wave  the products with S0 / dS1 and the
 //           in-chunk backward on bf16 MFMAs with (hi, lo) operands: dq, dk,
 //           dg, dbeta, per-chunk dA_log / ddt_bias sums

@@ -20,7 +20,14 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SCAN = os.path.join(ROOT, "kimi_delta_attention_04_amd", "csrc", "kda_scan.hip")
+CSRC = os.path.join(ROOT, "kimi_delta_attention_04_amd", "csrc")
+SCAN_FILES = ("kda_scan_dev.h", "kda_scan.hip", "kda_bwd_scan.hip")
+
+
+def scan_source() -> str:
+    """The scan kernels' sources: the ring helpers, the forward scan and the
+    backward's two scans."""
+    return "\n".join(open(os.path.join(CSRC, f)).read() for f in SCAN_FILES)
 REC_BYTES, CS = 13312, 16
 VMCNT_MAX = 63
 
@@ -31,7 +38,7 @@ def ring_depth(cw: int) -> int:
 
 
 def test_source_constants_match_model():
-    src = open(SCAN).read()
+    src = scan_source()
     assert re.search(r"RING_DEPTH\s*=\s*CW\s*<=\s*64\s*\?\s*5\s*:\s*4", src)
     assert "wait_vm_barrier<(DEPTH - 1) * UNITS>()" in src
     assert "wait_vm_barrier<(DEPTH - 2) * UNITS>()" in src
@@ -92,7 +99,7 @@ REC_BYTES_256 = 26624                # head dimension 256: 26 KB records
 
 
 def test_wide_source_constants_match_model():
-    src = open(SCAN).read()
+    src = scan_source()
     assert re.search(r"RING_DEPTH_256\s*=\s*4;", src)
     assert re.search(r"ONESET\s*=\s*WIDE\s*\|\|\s*CT\s*==\s*2;", src)
     assert "for (int c = 0; c < DEPTH - 1; ++c) issue(c, c);" in src
