@@ -489,23 +489,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     const __amdgpu_buffer_rsrc_t r_dq = make_rsrc(dq + rbase, rbytes);
     const __amdgpu_buffer_rsrc_t r_dk = make_rsrc(dk + rbase, rbytes);
     const __amdgpu_buffer_rsrc_t r_dg = make_rsrc(dg + rbase, rbytes);
-    // q, k and g again, one 32-channel block at a time (cache hits, mostly),
-    // so that the chunk's inputs need not stay in registers
-    const __amdgpu_buffer_rsrc_t r_q = make_rsrc(q + rbase, rbytes);
-    const __amdgpu_buffer_rsrc_t r_k = make_rsrc(k + rbase, rbytes);
-    const __amdgpu_buffer_rsrc_t r_g = make_rsrc(g + rbase, rbytes);
     float pa = 0.f;
     u32x4_t oq, ok, og;                                     // one 16-byte row piece of each output
     u32x4_t gq, kq, qq;                                     // and of each input, block kb
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int kb = t >> 1, hh = t & 1, c0 = 32 * kb + 8 * grp + 4 * hh;
-        if (hh == 0) {
-            const int off = (int)((tok * rowe + c0) * 2);
-            gq = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_g, off, 0, 0));
-            kq = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_k, off, 0, 0));
-            qq = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_q, off, 0, 0));
-        }
+        if (hh == 0) { gq = in.g[kb]; kq = in.k[kb]; qq = in.q[kb]; }
         float G[4];
         block_decay<4>(gq, L.dtb, kb, 4 * hh, A, lb2, live, G);
         // as in the factors: Kt, Qt, Kb rescaled by e^{-+G_last/2} (rs, ri) for
