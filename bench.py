@@ -262,10 +262,10 @@ def bench_backward(args, torch, kda, kda_inputs):
             "hbm_frac": path_gbs / HBM_PEAK_GBS, "stage_ms": stage,
             "stage_traffic_bytes": {k: (t["total_bytes"] if t else None) for k, t in
                                     ((k, stored_traffic(name, k, backward=True)) for k in names)},
-            # per (chunk slot, head): the two scans' records (17 KB + 13 KB),
+            # per (chunk slot, head): the two scans' records (9 KB + 13 KB),
             # S0 and dS1 (bf16 128 x 128), X (bf16 16 x 128), partial sums
             "workspace_bytes": int(w.H * (w.tokens // BWD_CHUNK + w.num_seqs) *
-                                   (17408 + 13312 + 2 * w.K * w.V * 2 + BWD_CHUNK * w.V * 2 +
+                                   (9216 + 13312 + 2 * w.K * w.V * 2 + BWD_CHUNK * w.V * 2 +
                                     (w.K + 1) * 4))}
     cpu = None
     if not args.no_cpu_baseline:

@@ -231,7 +231,7 @@ kda_status_t kda_decode(const void *q, const void *k, const void *v, const void 
  * the scans' records are bf16, and fp32 operands whose precision matters
  * enter as (hi, lo) bf16 pairs; elementwise work is fp32.  Every sum runs in
  * a fixed order, so the results are bitwise reproducible.  Device workspace
- * of about 99 KiB per (16-token chunk slot, head) comes from the library's
+ * of about 91 KiB per (16-token chunk slot, head) comes from the library's
  * stream-ordered pool (the two scans' records, every chunk's start state,
  * state gradient and X in bf16; dX is read back from dv).  The reverse scan runs on a
  * second stream the library creates once per device (non-blocking, default

@@ -104,8 +104,8 @@ def load():
 # The sources the forward kernels (intra stage and scan) are compiled from,
 # and those of the backward kernels.
 FORWARD_KERNEL_SOURCES = ("kda_device.h", "kda_intra_dev.h", "kda_intra.hip", "kda_scan_dev.h", "kda_scan.hip")
-BACKWARD_KERNEL_SOURCES = ("kda_device.h", "kda_intra_dev.h", "kda_bwd.hip", "kda_scan_dev.h",
-                           "kda_bwd_scan.hip")
+BACKWARD_KERNEL_SOURCES = ("kda_device.h", "kda_intra_dev.h", "kda_bwd_dev.h", "kda_bwd.hip",
+                           "kda_scan_dev.h", "kda_bwd_scan.hip")
 
 
 def source_digest(sources=FORWARD_KERNEL_SOURCES) -> str:

@@ -25,7 +25,7 @@
 //
 // Five launches:
 //   prep    (chunk slot, head), one wave  the chunk factors into the states
-//           scan's record (Kt and Wm with the chunk decay, (hi, lo) bf16) and
+//           scan's record (Kt and Wm with the chunk decay, bf16) and
 //           the reverse scan's bf16 record (Wm, scale Qt, -Kt, scale M^T),
 //           in MFMA operand layouts
 //   states  (sequence, head, column part)  forward scan on the forward
@@ -45,6 +45,7 @@
 #include <mutex>
 
 #include "kda_device.h"
+#include "kda_bwd_dev.h"
 #include "kda_intra_dev.h"                            // intra_load, mm16, the decay prefix
 #include "kda_launch.h"
 
@@ -598,8 +599,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
 // prep: one wave per (chunk slot, head), the chunk factors into the two
 // scans' bf16 records (in the forward record's MFMA operand layouts,
 // RecLayout<HD>):
-//   states record (StatesRec): Kt and Wm = P^T Kb Gam as (hi, lo) bf16
-//     pairs in the Kt and W^T layouts, and the chunk decay, the operands of
+//   states record (StatesRec, kda_bwd_dev.h): Kt and Wm = P^T Kb Gam in the
+//     Kt and W^T layouts, and the chunk decay, the operands of
 //     X = V - Kt S0 and S1 = Gam S0 + Wm^T X;
 //   reverse record: Wm in the Kt layout (the A operand of Wm dS), scale Qt
 //     and -Kt in the W^T layout (the A operands of the state-gradient
@@ -678,7 +679,7 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(
         float gl[8];
         *(f32x4_t *)&gl[0] = *(const f32x4_t *)&L.gl[32 * kb + 8 * grp];
         *(f32x4_t *)&gl[4] = *(const f32x4_t *)&L.gl[32 * kb + 8 * grp + 4];
-        u32x4_t kth, ktl, qth, qtl, kbh, kbl, kgh4, kgl4, Kh, Kl, qs, nk;
+        u32x4_t kth, ktl, qth, qtl, kbh, kbl, kgh4, kgl4, Kh, qs, nk;
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd) {
             float kt[2], qt[2], kbv[2], kg[2], Kt[2], sq[2];
@@ -701,7 +702,7 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(
             split2(qt[0], qt[1], a, b); qth[wd] = a; qtl[wd] = b;
             split2(kbv[0], kbv[1], a, b); kbh[wd] = a; kbl[wd] = b;
             split2(kg[0], kg[1], a, b); kgh4[wd] = a; kgl4[wd] = b;
-            split2(Kt[0], Kt[1], a, b); Kh[wd] = a; Kl[wd] = b;
+            Kh[wd] = pack2(Kt[0], Kt[1]);
             qs[wd] = pack2(sq[0], sq[1]);
             nk[wd] = pack2(-Kt[0], -Kt[1]);
         }
@@ -709,7 +710,6 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(
         AkkT = mm3_k32(kbh, kbl, kth, ktl, AkkT);           // AkkT[r][c] = Akk[c][r]
         Aqk = mm3_k32(qth, qtl, kbh, kbl, Aqk);             // Aqk[r][c]  = Qt_r . Kb_c
         __builtin_nontemporal_store(Kh, (u32x4_t *)(sr + SR::KTH + (kb * 64 + l) * 16));
-        __builtin_nontemporal_store(Kl, (u32x4_t *)(sr + SR::KTL + (kb * 64 + l) * 16));
         u32x4_t qw, nw;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -770,27 +770,24 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(
         __builtin_nontemporal_store(mo, (u32x2_t *)(rr + R::M + l * 8));
     }
     // Wm = P^T Kb Gam, tile t in the W^T layout (A = P^T: the tile layout of
-    // P), as (hi, lo) for the states record and, through the identity, in
-    // the Kt layout for the reverse record
+    // P), in bf16 for the states record and, through the identity, in the
+    // Kt layout for the reverse record
     u32x2_t pAh, pAl;
     split4(P, pAh, pAl);
 #pragma unroll
     for (int tp = 0; tp < NKB; ++tp) {
-        u32x4_t wh, wl, wk;
+        u32x4_t wh, wk;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int t = 2 * tp + hh;
             const f32x4_t W = mm3_k16(pAh, pAl, kgh[t], kgl[t], zero);
-            u32x2_t a, b;
-            split4(W, a, b);
+            const u32x2_t a = {pack2(W[0], W[1]), pack2(W[2], W[3])};
             wh[2 * hh] = a[0]; wh[2 * hh + 1] = a[1];
-            wl[2 * hh] = b[0]; wl[2 * hh + 1] = b[1];
             const f32x4_t d = mfma_k16(a, eye, zero);       // exact: bf16 values
             wk[2 * hh] = pack2(d[0], d[1]);
             wk[2 * hh + 1] = pack2(d[2], d[3]);
         }
         __builtin_nontemporal_store(wh, (u32x4_t *)(sr + SR::WTH + (tp * 64 + l) * 16));
-        __builtin_nontemporal_store(wl, (u32x4_t *)(sr + SR::WTL + (tp * 64 + l) * 16));
         __builtin_nontemporal_store(wk, (u32x4_t *)(rr + R::KTO + (tp * 64 + l) * 16));
     }
 }

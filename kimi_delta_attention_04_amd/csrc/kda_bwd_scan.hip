@@ -9,6 +9,7 @@
 // only the prep kernel's records and the token inputs), and the backward
 // launches them side by side on two streams.
 #include "kda_device.h"
+#include "kda_bwd_dev.h"
 #include "kda_launch.h"
 #include "kda_scan_dev.h"
 
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
     constexpr int V_KB = CS * CW * 2 / 1024;
     constexpr int UNITS = RKB + V_KB;
     constexpr int VROW_LANES = CW * 2 / 16;
-    constexpr int DEPTH = 4;                       // (DEPTH - 1) x 19 DMAs within vmcnt
+    constexpr int DEPTH = 4;                       // (DEPTH - 1) x UNITS DMAs within vmcnt
     __shared__ ScanSlot<CW, R::BYTES> ring[DEPTH];
     static_assert((DEPTH - 1) * UNITS <= 63, "vmcnt holds at most 63");
 
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
         }
     };
     struct Ops {
-        u32x4_t kt[NKB], ktl[NKB], wt[NKB], wtl[NKB];
+        u32x4_t kt[NKB], wt[NKB];
         float gm[2];
         u32x2_t v;
     };
@@ -342,9 +343,7 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             op.kt[kb] = *(const u32x4_t *)(Rp + R::KTH + (kb * 64 + l) * 16);
-            op.ktl[kb] = *(const u32x4_t *)(Rp + R::KTL + (kb * 64 + l) * 16);
             op.wt[kb] = *(const u32x4_t *)(Rp + R::WTH + (kb * 64 + l) * 16);
-            op.wtl[kb] = *(const u32x4_t *)(Rp + R::WTL + (kb * 64 + l) * 16);
         }
         const int gch = 32 * (cg >> 2) + 8 * grp + 4 * ((cg >> 1) & 1) + 2 * (cg & 1);
         const u32x2_t g2 = *(const u32x2_t *)(Rp + R::GAM + gch * 4);
@@ -359,10 +358,9 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
         eye[0] = (d == 0 ? one : 0u) | (d == 1 ? one << 16 : 0u);
         eye[1] = (d == 2 ? one : 0u) | (d == 3 ? one << 16 : 0u);
     }
-    // Every product is an fp32-accurate sum of three bf16 products of (hi,
-    // lo) pairs (the state, X, Kt and Wm), so X and the state match fp32
-    // arithmetic closely: the chunk kernel's gradient products take them,
-    // and S0 rounded to bf16, as fp32 operands.
+    // The state and X enter their products as (hi, lo) bf16 pairs, Kt and
+    // Wm as bf16 (two products each): the recurrence keeps the state's fp32
+    // accumulation, and the chunk kernel takes S0 and X rounded to bf16.
     auto hi2 = [](float a, float b) { return pack2(a, b); };
     auto lo2 = [](float a, float b, uint32_t hi) { return pack2(a - bf16lo(hi), b - bf16hi(hi)); };
     auto compute = [&](int c, const Ops &op) {
@@ -384,7 +382,6 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
         for (int i = 0; i < NKB; ++i) {
             P0 = mfma_k32(op.kt[i], Sb[i], P0);
             P1 = mfma_k32(op.kt[i], Sl[i], P1);
-            P1 = mfma_k32(op.ktl[i], Sb[i], P1);
         }
         const f32x4_t vv = mfma_k16(op.v, eye, zero);
         decay_tiles<0, NT>(S, op.gm);
@@ -395,15 +392,12 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
         const u32x2_t Xb = {xh0, xh1}, Xl = {lo2(X[0], X[1], xh0), lo2(X[2], X[3], xh1)};
 #pragma unroll
         for (int tp = 0; tp < NKB; ++tp) {
-            // tiles 2tp (bf16 0..3) and 2tp+1 (bf16 4..7) of Wm^T, hi and lo parts
+            // tiles 2tp (bf16 0..3) and 2tp+1 (bf16 4..7) of Wm^T
             const u32x2_t t0 = {op.wt[tp][0], op.wt[tp][1]}, t1 = {op.wt[tp][2], op.wt[tp][3]};
-            const u32x2_t l0 = {op.wtl[tp][0], op.wtl[tp][1]}, l1 = {op.wtl[tp][2], op.wtl[tp][3]};
             S[2 * tp] = mfma_k16(t0, Xb, S[2 * tp]);
             S[2 * tp + 1] = mfma_k16(t1, Xb, S[2 * tp + 1]);
             S[2 * tp] = mfma_k16(t0, Xl, S[2 * tp]);
             S[2 * tp + 1] = mfma_k16(t1, Xl, S[2 * tp + 1]);
-            S[2 * tp] = mfma_k16(l0, Xb, S[2 * tp]);
-            S[2 * tp + 1] = mfma_k16(l1, Xb, S[2 * tp + 1]);
         }
         // stores (off the chain): X in bf16 through the identity (lane (grp,
         // cg): token cg, columns 4grp .. +3, [16][128] per chunk), S0 in bf16

@@ -63,18 +63,6 @@ constexpr int REC_BYTES = 13312;
 // dimension 256): KT/32 channel blocks in KT, QT and WT, KT chunk decays,
 // and the whole padded to a multiple of 1 KB (the scan moves records in
 // 1 KB DMA units).
-// Record of the backward's forward scan (kda_scan.hip fscan_kernel), per
-// (chunk slot, head): Kt and Wm as (hi, lo) bf16 pairs in the Kt and W^T
-// operand layouts of RecLayout<128>, and the chunk decay.
-struct StatesRec {
-    static constexpr int KTH = 0;
-    static constexpr int KTL = 4096;
-    static constexpr int WTH = 8192;
-    static constexpr int WTL = 12288;
-    static constexpr int GAM = 16384;
-    static constexpr int BYTES = 17408;       // 17 one-kilobyte units
-};
-
 template <int KT>
 struct RecLayout {
     static_assert(KT == 128 || KT == 256, "tile widths");
