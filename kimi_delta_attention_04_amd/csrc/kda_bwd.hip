@@ -56,17 +56,25 @@ namespace {
 constexpr float LN2 = 0.6931471805599453f;
 
 // Token range of chunk slot `slot`: returns its token count (0 for a gap
-// slot) and the first token row in t0.
-__device__ int slot_chunk(const int32_t *cu, int N, int T, int64_t slot, int64_t &t0) {
+// slot) and the first token row in t0; also the chunk's index within its
+// sequence (ci) and the sequence's end row.
+__device__ int slot_chunk(const int32_t *cu, int N, int T, int64_t slot, int64_t &t0, int &ci,
+                          int64_t &end) {
     int lo = 0, hi = N - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (seq_slot0(cu, mid, T) <= slot) lo = mid; else hi = mid - 1;
     }
-    int64_t start, end;
+    int64_t start;
     seq_range(cu, lo, T, start, end);
-    t0 = start + (slot - seq_slot0(cu, lo, T)) * CS;
+    ci = (int)(slot - seq_slot0(cu, lo, T));
+    t0 = start + (int64_t)ci * CS;
     return t0 >= end ? 0 : (int)min((int64_t)CS, end - t0);
+}
+__device__ int slot_chunk(const int32_t *cu, int N, int T, int64_t slot, int64_t &t0) {
+    int ci;
+    int64_t end;
+    return slot_chunk(cu, N, T, slot, t0, ci, end);
 }
 
 // ---------------------------------------------------------------------------
@@ -97,7 +105,9 @@ struct ChunkWaveLds {
     float dtb[HD];                    // dt_bias in log2 units
     float gam[HD];                    // e^{G_last} per key channel
     float gl[HD];                     // G_last in log2 units
-    float dgs[HD];                    // diag(dS1 S0^T) per key channel
+    float dgs[HD];                    // diag(dS1 S0^T) per key channel, in two parts
+    float dgs2[HD];
+    float gnb[HD];                    // chunk decay of the neighbour chunk whose state is used
     float tile[CS][CS + 1];           // 16 x 16 transposes
     f32x4_t qs[HD / 16][64];          // (dO S0^T)^T and (dX S0^T)^T per state row
     f32x4_t ks[HD / 16][64];          // tile and lane, between their two phases
@@ -228,6 +238,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     const uint16_t *__restrict__ dout, const int32_t *__restrict__ cu, int N, int T, int H,
     const uint16_t *__restrict__ st0, const uint16_t *__restrict__ dst1,
     const uint16_t *__restrict__ xws, const uint16_t *__restrict__ dvv,
+    const uint8_t *__restrict__ srec, const uint8_t *__restrict__ rrec,
     uint16_t *__restrict__ dq, uint16_t *__restrict__ dk, uint16_t *__restrict__ dg,
     uint16_t *__restrict__ dbeta, float *__restrict__ part_alog, float *__restrict__ part_dtb)
 {
@@ -238,8 +249,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     const int h = (int)(blockIdx.x % (unsigned)H);
     const int l = threadIdx.x, tok = l & 15, grp = l >> 4;
     const size_t sh = (size_t)slot * H + h;
-    int64_t t0;
-    const int len = slot_chunk(cu, N, T, slot, t0);
+    int64_t t0, tend;
+    int ci;
+    const int len = slot_chunk(cu, N, T, slot, t0, ci, tend);
     if (len == 0) {                                         // gap slot: zero partial sums
         part_dtb[sh * HD + l] = 0.f;
         part_dtb[sh * HD + 64 + l] = 0.f;
@@ -261,73 +273,174 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     auto row_off = [&](int kb) { return (int)((tok * rowe + 32 * kb + 8 * grp) * 2); };
 
     // ---- products with the states ------------------------------------------
-    // Over the value columns in 32-column steps s, state row tile t:
+    // The states scan stores S0 of a sequence's even chunks (index within the
+    // sequence) and the reverse scan dS1 of its odd chunks and of its last
+    // one.  An odd chunk takes S0 of the chunk before (p) and an even chunk
+    // other than the last takes dS1 of the chunk after (n), through the
+    // chunk steps
+    //   S0  = Gam_p S0_p + Wm_p^T X_p,
+    //   dS1 = Gam_n dS1_n + scale Qt_n^T dO_n - Kt_n^T dX_n,
+    // so each product with the state it lacks is the same product with the
+    // stored one, scaled per channel, plus 16 x 16 by 16 x 128 terms from the
+    // neighbour's X, dO, dX and its records (Wm_p, the chunk decays, scale
+    // Qt_n and -Kt_n).  Neighbouring chunks of a head are 8 H workgroups
+    // apart, so their reads of the shared state rows meet in one L2.
+    //
+    // Over the value columns in 32-column steps s, per state row tile t:
     //   (dO S0^T)^T, (dX S0^T)^T   rows chan(t, .): token-per-lane results
     //   dWm = X dS1^T              W^T layout (A = X, B = dS1 rows)
-    //   dM / scale = dO X^T        tile
     //   diag(dS1 S0^T)             per lane, summed over its four lane groups
-    // The stored states are bf16 rows [16-column part][128 rows][16]; the A
-    // operand of tile t, step s is row chan(t, tok), columns 32s + 8grp .. +7.
-    f32x4_t QS[NT], KS[NT], WW[NT], dM = zero;
-    float dgp[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) { QS[t] = KS[t] = WW[t] = zero; dgp[t] = 0.f; }
+    // and once: dM / scale = dO X^T (tile).  The stored states are bf16 rows
+    // [16-column part][128 rows][16]; the A operand of tile t, step s is row
+    // chan(t, tok), columns 32s + 8grp .. +7.
+    const bool odd = (ci & 1) != 0;                         // S0 from the chunk before
+    const bool reb = !odd && t0 + CS < tend;                // dS1 from the chunk after
+    typedef RecLayout<HD> R;
+    typedef StatesRec SR;
+    const size_t shS = odd ? sh - H : sh, shD = reb ? sh + H : sh;
+    // the neighbour's chunk decay (p's for an odd chunk, n's for a rebuilt dS1)
     {
-        const uint16_t *S0 = st0 + sh * HD * HD + (size_t)(l >> 5) * HD * 16 + 8 * ((l >> 4) & 1);
-        const uint16_t *DS = dst1 + sh * HD * HD + (size_t)(l >> 5) * HD * 16 + 8 * ((l >> 4) & 1);
+        const uint8_t *gsrc = srec + (odd ? shS : shD) * SR::BYTES + SR::GAM;
+        *(u32x2_t *)&L.gnb[2 * l] = *(const u32x2_t *)(gsrc + 8 * l);
+    }
+    f32x4_t dM = zero;
+    u32x2_t wwh[NT], wwl[NT];
+    {
+        const uint16_t *S0 = st0 + shS * HD * HD + (size_t)(l >> 5) * HD * 16 + 8 * ((l >> 4) & 1);
+        const uint16_t *DS = dst1 + shD * HD * HD + (size_t)(l >> 5) * HD * 16 + 8 * ((l >> 4) & 1);
         auto sld = [&](const uint16_t *b, int s, int t) {
             return *(const u32x4_t *)&b[((size_t)2 * s * HD + state_chan(t, tok)) * 16];
         };
-        const uint16_t *xr = xws + sh * CS * HD + tok * HD + 8 * grp;
+        // the token-per-lane operands of every step: this chunk's dO, X, dX;
+        // e1, e2: the neighbour's X (odd) or dO, dX (rebuilt dS1)
+        const int len_n = reb ? (int)min((int64_t)CS, tend - t0 - CS) : 1;
+        const size_t rbase_n = rbase + (size_t)CS * rowe;
+        const uint32_t rbytes_n = (uint32_t)(((size_t)(len_n - 1) * rowe + KD) * 2);
         const __amdgpu_buffer_rsrc_t r_dx = make_rsrc(dvv + rbase, rbytes);
-        // a ring of DEPTH (S0, dS1) operand pairs in flight; the step loop
-        // stays rolled so that the loads are issued where written
-        constexpr int DEPTH = 4;
-        static_assert(NT % DEPTH == 0, "ring slots repeat every step");
-        u32x4_t ra[DEPTH], rd[DEPTH];
+        const __amdgpu_buffer_rsrc_t r_don = make_rsrc(dout + rbase_n, reb ? rbytes_n : 0u);
+        const __amdgpu_buffer_rsrc_t r_dxn = make_rsrc(dvv + rbase_n, reb ? rbytes_n : 0u);
+        const uint16_t *xr = xws + sh * CS * HD + tok * HD + 8 * grp;
+        const uint16_t *xp = xws + shS * CS * HD + tok * HD + 8 * grp;
+        u32x4_t ob[NKB], xb[NKB], db[NKB], e1[NKB], e2[NKB];
 #pragma unroll
-        for (int p = 0; p < DEPTH; ++p) { ra[p] = sld(S0, 0, p); rd[p] = sld(DS, 0, p); }
-        u32x4_t on = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_do, row_off(0), 0, 0));
-        u32x4_t xn = *(const u32x4_t *)&xr[0];
-        u32x4_t dn = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_dx, row_off(0), 0, 0));
-#pragma unroll 1
-        for (int s = 0; s < NKB; ++s) {
-            const u32x4_t ob = on, xh = xn, dxh = dn;
-            const bool more = s + 1 < NKB;
-            if (more) {
-                on = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_do, row_off(s + 1), 0, 0));
-                xn = *(const u32x4_t *)&xr[32 * (s + 1)];
-                dn = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_dx, row_off(s + 1), 0, 0));
+        for (int st = 0; st < NKB; ++st) {
+            ob[st] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_do, row_off(st), 0, 0));
+            xb[st] = *(const u32x4_t *)&xr[32 * st];
+            db[st] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_dx, row_off(st), 0, 0));
+            if (odd) {
+                e1[st] = *(const u32x4_t *)&xp[32 * st];
+                e2[st] = e1[st];
+            } else {
+                e1[st] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_don, row_off(st), 0, 0));
+                e2[st] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_dxn, row_off(st), 0, 0));
             }
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const u32x4_t sa = ra[t % DEPTH], sd = rd[t % DEPTH];
-                if (t + DEPTH < NT) {
-                    ra[t % DEPTH] = sld(S0, s, t + DEPTH);
-                    rd[t % DEPTH] = sld(DS, s, t + DEPTH);
-                } else if (more) {
-                    ra[t % DEPTH] = sld(S0, s + 1, t + DEPTH - NT);
-                    rd[t % DEPTH] = sld(DS, s + 1, t + DEPTH - NT);
-                }
-                QS[t] = mfma_k32(sa, ob, QS[t]);
-                KS[t] = mfma_k32(sa, dxh, KS[t]);
-                WW[t] = mfma_k32(xh, sd, WW[t]);
-                float d = dgp[t];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) d = fmaf(elem(sa, i), elem(sd, i), d);
-                dgp[t] = d;
-            }
-            dM = mfma_k32(ob, xh, dM);
         }
-    }
+        // 16 x 16 products over the value columns: dM; for an odd chunk
+        // Z1 = X_p dO^T and Z2 = X_p dX^T (tiles); for a rebuilt dS1
+        // Z1 = dO_n X^T and Z2 = dX_n X^T (tiles, i.e. X dO_n^T and X dX_n^T in
+        // the A operand layout)
+        f32x4_t Z1 = zero, Z2 = zero;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        float d = dgp[t];
-        d += __shfl_xor(d, 16, 64);
-        d += __shfl_xor(d, 32, 64);
-        if (grp == 0) L.dgs[state_chan(t, tok)] = d;
-        L.qs[t][l] = QS[t];
-        L.ks[t][l] = KS[t];
+        for (int st = 0; st < NKB; ++st) {
+            dM = mfma_k32(ob[st], xb[st], dM);
+            if (odd) {
+                Z1 = mfma_k32(e1[st], ob[st], Z1);
+                Z2 = mfma_k32(e1[st], db[st], Z2);
+            } else if (reb) {
+                Z1 = mfma_k32(e1[st], xb[st], Z1);
+                Z2 = mfma_k32(e2[st], xb[st], Z2);
+            }
+        }
+        u32x2_t z1h, z1l, z2h, z2l;
+        split4(Z1, z1h, z1l);
+        split4(Z2, z2h, z2l);
+        wave_lds_sync();                                    // the neighbour's decay staged
+        u32x4_t sa[NKB], sd[NKB];
+#pragma unroll
+        for (int st = 0; st < NKB; ++st) { sa[st] = sld(S0, st, 0); sd[st] = sld(DS, st, 0); }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            u32x4_t na[NKB], nd[NKB];                       // the next tile's rows in flight
+            if (t + 1 < NT) {
+#pragma unroll
+                for (int st = 0; st < NKB; ++st) { na[st] = sld(S0, st, t + 1); nd[st] = sld(DS, st, t + 1); }
+            }
+            f32x4_t Qa = zero, Ka = zero, Wa = zero, Ea = zero, Eb = zero;
+            float dg = 0.f;
+#pragma unroll
+            for (int st = 0; st < NKB; ++st) {
+                Qa = mfma_k32(sa[st], ob[st], Qa);
+                Ka = mfma_k32(sa[st], db[st], Ka);
+                Wa = mfma_k32(xb[st], sd[st], Wa);
+                if (odd) {
+                    Ea = mfma_k32(e1[st], sd[st], Ea);          // X_p dS1^T (W^T layout)
+                } else if (reb) {
+                    Ea = mfma_k32(sa[st], e1[st], Ea);          // (dO_n S0^T)^T
+                    Eb = mfma_k32(sa[st], e2[st], Eb);          // (dX_n S0^T)^T
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) dg = fmaf(elem(sa[st], i), elem(sd[st], i), dg);
+            }
+            dg += __shfl_xor(dg, 16, 64);
+            dg += __shfl_xor(dg, 32, 64);                   // channel chan(t, tok)
+            const int ct = state_chan(t, tok);
+            float dg2[4] = {0.f, 0.f, 0.f, 0.f};            // channels chan(t, 4grp + j)
+            if (odd) {
+                // S0 = Gam_p S0_p + Wm_p^T X_p: rows chan(t, 4grp + j) of the
+                // products scale by their decay, plus Wm_p^T (X_p dO^T); the
+                // decay's own term adds X_p dS1^T o Wm_p summed over tokens
+                const u32x2_t wmp = *(const u32x2_t *)(srec + shS * SR::BYTES + SR::WTH +
+                                                       ((t >> 1) * 64 + l) * 16 + 8 * (t & 1));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float gr = L.gnb[state_chan(t, 4 * grp + j)];
+                    Qa[j] *= gr;
+                    Ka[j] *= gr;
+                }
+                Qa = mfma_k16(wmp, z1h, Qa);
+                Qa = mfma_k16(wmp, z1l, Qa);
+                Ka = mfma_k16(wmp, z2h, Ka);
+                Ka = mfma_k16(wmp, z2l, Ka);
+                float wx = Ea[0] * bf16lo(wmp[0]) + Ea[1] * bf16hi(wmp[0]) +
+                           Ea[2] * bf16lo(wmp[1]) + Ea[3] * bf16hi(wmp[1]);
+                wx += __shfl_xor(wx, 16, 64);
+                wx += __shfl_xor(wx, 32, 64);
+                dg = L.gnb[ct] * dg + wx;
+            } else if (reb) {
+                // dS1 = Gam_n dS1_n + scale Qt_n^T dO_n - Kt_n^T dX_n: dWm's
+                // columns scale by their decay, plus (X dO_n^T) scale Qt_n and
+                // (X dX_n^T) (-Kt_n); diag(dS1 S0^T) takes the decay and the
+                // sums over tokens of scale Qt_n o (dO_n S0^T) and
+                // -Kt_n o (dX_n S0^T)
+                const size_t ro = shD * R::BYTES + ((t >> 1) * 64 + l) * 16 + 8 * (t & 1);
+                const u32x2_t qtn = *(const u32x2_t *)(rrec + ro + R::QT);
+                const u32x2_t ktn = *(const u32x2_t *)(rrec + ro + R::WT);
+                const float gc = L.gnb[ct];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Wa[j] *= gc;
+                Wa = mfma_k16(z1h, qtn, Wa);
+                Wa = mfma_k16(z1l, qtn, Wa);
+                Wa = mfma_k16(z2h, ktn, Wa);
+                Wa = mfma_k16(z2l, ktn, Wa);
+                const f32x4_t qtl = mfma_k16(qtn, eye, zero);   // token tok, channels chan(t, 4grp + j)
+                const f32x4_t ktl = mfma_k16(ktn, eye, zero);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dg2[j] = row_sum16(Ea[j] * qtl[j] + Eb[j] * ktl[j]);
+                dg = gc * dg;
+            }
+            if (grp == 0) L.dgs[ct] = dg;
+            if (tok == 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) L.dgs2[state_chan(t, 4 * grp + j)] = dg2[j];
+            }
+            L.qs[t][l] = Qa;
+            L.ks[t][l] = Ka;
+            split4(Wa, wwh[t], wwl[t]);
+            if (t + 1 < NT) {
+#pragma unroll
+                for (int st = 0; st < NKB; ++st) { sa[st] = na[st]; sd[st] = nd[st]; }
+            }
+        }
     }
 
     // ---- chunk factors, and Y = Kb Gam dWm^T --------------------------------
@@ -339,10 +452,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
         const float b = __builtin_amdgcn_rcpf(1.f + fast_exp2(-x * LOG2E));
         if (grp == 0) L.beta[tok] = live ? b : 0.f;
     }
-    // dWm (hi, lo) in the W^T layout as computed
-    u32x2_t wwh[NT], wwl[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) split4(WW[t], wwh[t], wwl[t]);
     wave_lds_sync();                                        // dt_bias staged
     f32x4_t Akk = zero, AkkT = zero, Aqk = zero, Y = zero;
 #pragma unroll
@@ -537,7 +646,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
         const f32x4_t pg = mm3_k16(wwh[t], wwl[t], pTh, pTl, zero);
         const f32x4_t pb = mm3_k16(kwh, kwl, dAh, dAl, mm3_k16(qwh, qwl, dQh, dQl, zero));
         const f32x4_t qs = L.qs[t][l], ks = L.ks[t][l];
-        const f32x4_t gm = *(const f32x4_t *)&L.gam[c0], dgs = *(const f32x4_t *)&L.dgs[c0];
+        const f32x4_t gm = *(const f32x4_t *)&L.gam[c0];
+        const f32x4_t dgs = *(const f32x4_t *)&L.dgs[c0] + *(const f32x4_t *)&L.dgs2[c0];
         const f32x4_t dtb2 = *(const f32x4_t *)&L.dtb[c0];
         const float daq = L.daq[tok];
         float vq[4], vk[4], vg[4], pd[4];
@@ -921,7 +1031,7 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
     mark(3);
 #define KDA_BWD_CHUNK(KD_)                                                                    \
     hipLaunchKernelGGL(bwd_chunk_kernel<KD_>, chunks, dim3(64), 0, stream, q, k, g, beta, A_log, \
-                       dt_bias, lower_bound, scale, dout, cu, N, T, H, st0, dst1, xws, dv, dq, dk, \
+                       dt_bias, lower_bound, scale, dout, cu, N, T, H, st0, dst1, xws, dv, srec, rrec, dq, dk, \
                        dg, dbeta, palog, pdtb)
     if (K == HD) KDA_BWD_CHUNK(HD); else KDA_BWD_CHUNK(64);
 #undef KDA_BWD_CHUNK

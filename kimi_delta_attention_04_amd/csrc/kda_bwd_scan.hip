@@ -189,7 +189,10 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
         const f32x4_t vt = mfma_k16(dXb, eye, zero);
         const u32x2_t vs = {pack2(vt[0], vt[1]), pack2(vt[2], vt[3])};
         __builtin_amdgcn_raw_buffer_store_b64(vs, ro, (int)(cg * row_bytes) + (wcol0 + 4 * grp) * 2, 0, 0);
+        // dS1 of the odd chunks and of the last one only (the chunk kernel
+        // rebuilds an even chunk's products from the chunk after)
         uint16_t *so = ds1 + sh * HD * HD + (size_t)p16 * HD * 16 + 4 * grp;
+        if ((ci & 1) == 1 || ci == nch - 1)
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const u32x2_t a = {Sb[t >> 1][2 * (t & 1)], Sb[t >> 1][2 * (t & 1) + 1]};
@@ -407,7 +410,10 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
             const u32x2_t xv = {pack2(xt[0], xt[1]), pack2(xt[2], xt[3])};
             *(u32x2_t *)&xws[sh * CS * HD + cg * HD + col0 + wcol0 + 4 * grp] = xv;
         }
+        // S0 of the even chunks only (the chunk kernel rebuilds an odd
+        // chunk's products from the chunk before)
         uint16_t *so = s0 + sh * HD * HD + (size_t)p16 * HD * 16 + 4 * grp;
+        if ((c & 1) == 0)
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const u32x2_t a = {Sb[t >> 1][2 * (t & 1)], Sb[t >> 1][2 * (t & 1) + 1]};

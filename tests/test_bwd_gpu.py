@@ -183,8 +183,9 @@ def test_head_dim_64_matches_oracle(kw):
 
 def test_many_heads_sampled():
     """N x H = 80 (sequence, head) units: ten groups of eight in the scans'
-    XCD-aware block mapping; with 8 x 80 < 3 x 256 the launch takes the
-    two-part scan workgroups."""
+    XCD-aware block mapping; the two scans run side by side with one
+    128-column part per unit (two scans of two parts would not fit on 256
+    compute units at once)."""
     inp = kda_inputs.random_small(971, B=2, T=100, H=40, initial_state=True)
     d_out, d_final = kda_inputs.output_grads(972, 2, 100, 40)
     out = run_bwd(to_device(inp), d_out, d_final)
@@ -203,9 +204,20 @@ def test_full_size_varlen_sampled_heads(name):
     check(inp, out, d_out, d_final, heads=RESIDUE_HEADS_96)
 
 
-def test_four_part_scans_with_empty_sequences():
-    """200 (sequence, head) units take the four-part scan workgroups; the
-    batch holds empty and one-token sequences."""
+def test_two_part_scans():
+    """N x H = 48 (sequence, head) units: the scans take two 64-column parts
+    per unit (2 scans x 2 parts x 48 fit on 256 compute units, four parts
+    would not)."""
+    inp = kda_inputs.random_small(991, B=2, T=50, H=24, initial_state=True)
+    d_out, d_final = kda_inputs.output_grads(992, 2, 50, 24)
+    out = run_bwd(to_device(inp), d_out, d_final)
+    check(inp, out, d_out, d_final, heads=[0, 9, 23])
+
+
+def test_many_units_with_empty_sequences():
+    """200 (sequence, head) units, one 128-column part each; the batch
+    holds empty and one-token sequences.  (Four-part scans, 32 columns per
+    part, are what the small cases of test_matches_oracle take.)"""
     lens = (0, 17, 1, 60, 0)
     inp = kda_inputs.random_small(981, B=1, T=sum(lens), H=40, seq_lens=lens, initial_state=True)
     d_out, d_final = kda_inputs.output_grads(982, 1, sum(lens), 40, N=len(lens))
