@@ -232,8 +232,9 @@ kda_status_t kda_decode(const void *q, const void *k, const void *v, const void 
  * enter as (hi, lo) bf16 pairs; elementwise work is fp32.  Every sum runs in
  * a fixed order, so the results are bitwise reproducible.  Device workspace
  * of about 91 KiB per (16-token chunk slot, head) comes from the library's
- * stream-ordered pool (the two scans' records, every chunk's start state,
- * state gradient and X in bf16; dX is read back from dv).  The reverse scan runs on a
+ * stream-ordered pool (the two scans' records; X of every chunk and the
+ * start state or the state gradient of every other chunk, in bf16; dX is
+ * read back from dv).  The reverse scan runs on a
  * second stream the library creates once per device (non-blocking, default
  * priority), forked from `stream` after the prep kernel and joined back
  * before the chunk kernel by events, so the call as a whole stays ordered on

@@ -29,12 +29,13 @@
 //           the reverse scan's bf16 record (Wm, scale Qt, -Kt, scale M^T),
 //           in MFMA operand layouts
 //   states  (sequence, head, column part)  forward scan on the forward
-//           scan's structure (kda_bwd_scan.hip), storing every chunk's start
-//           state S0 (bf16 rows) and X (bf16)
+//           scan's structure (kda_bwd_scan.hip), storing the start state S0
+//           of the even chunks of each sequence (bf16 rows) and every X (bf16)
 //   rscan   (sequence, head, column part)  reverse scan of dS on the same
 //           structure, beside the states scan on a second stream, storing
-//           every chunk's dS1 (bf16 rows), writing dv (= dX, which the
-//           chunk kernel reads back) and the initial-state gradient
+//           dS1 of the odd chunks and of the last one (bf16 rows), writing
+//           dv (= dX, which the chunk kernel reads back) and the
+//           initial-state gradient
 //   chunk   (chunk slot, head), one wave  the products with S0 / dS1 and the
 //           in-chunk backward on bf16 MFMAs with (hi, lo) operands: dq, dk,
 //           dg, dbeta, per-chunk dA_log / ddt_bias sums

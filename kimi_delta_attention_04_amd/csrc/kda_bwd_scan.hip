@@ -3,9 +3,11 @@
 // waves one 16-column slice of the 128-row state in MFMA accumulators, and
 // one more wave fills an LDS ring with each chunk's record and token tile by
 // DMA (kda_scan_dev.h).  The states scan runs the chunk recurrence forward
-// from the initial state and stores every chunk's start state S0 and X; the
-// reverse scan runs the state gradient backward from d_final_state and
-// stores every chunk's dS1 and dv (= dX).  They are independent (both read
+// from the initial state and stores the start state S0 of a sequence's even
+// chunks and every chunk's X; the reverse scan runs the state gradient
+// backward from d_final_state and stores dS1 of the odd chunks and of the
+// last one, and dv (= dX).  The chunk kernel rebuilds the other half's
+// products from the neighbouring chunk.  They are independent (both read
 // only the prep kernel's records and the token inputs), and the backward
 // launches them side by side on two streams.
 #include "kda_device.h"
@@ -30,8 +32,9 @@ namespace {
 // S1 = diag(gamma) S0 + Wm^T X, X = V - Kt S0).  The record of each chunk
 // (written by the backward's prep kernel) holds Wm in the Kt slot, scale Qt
 // and -Kt transposed in the Qt and W^T slots, scale M^T in the M slot.
-// Stored per chunk for the chunk kernel: dS1 rounded to bf16, as rows of
-// each 16-column part ([part][row][16 columns]), and dX in fp32 ([16][V]).
+// Stored for the chunk kernel: dS1 rounded to bf16 (odd chunks of the
+// sequence and the last one), as rows of each 16-column part ([part][row]
+// [16 columns]), and dV = dX in bf16.
 // One slice per wave on the 128-wide tiles (K = V = 128, or 64 with V = 64
 // columns and the rows from 64 on zero).
 template <int NW, int VD>
@@ -246,9 +249,9 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
 // from the initial state through every chunk (X = V - Kt S0,
 // S1 = diag(gamma) S0 + Wm^T X, with the state and X as (hi, lo) bf16
 // operands), without the output, storing
-// per chunk for the chunk kernel the start state S0 rounded to bf16 (rows of
-// each 16-column part, [part][128 rows][16 columns]) and X in fp32
-// ([16][V]).  The record of each chunk (written by the backward's prep
+// for the chunk kernel the start state S0 rounded to bf16 of the sequence's
+// even chunks (rows of each 16-column part, [part][128 rows][16 columns])
+// and X in bf16 ([16][V]) of every chunk.  The record of each chunk (written by the backward's prep
 // kernel) holds Kt and Wm in the forward record's Kt and W^T slots and the
 // chunk decay; its Qt and M slots are not used.  One slice per wave on the
 // 128-wide tiles (K = V = 128, or 64 with V = 64 columns).
