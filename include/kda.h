@@ -90,8 +90,8 @@ typedef enum {
  *                  gets its initial state)
  *   B, T, H, K, V  sizes; K = V = 128, K = V = 256 (sixteen state row
  *                  tiles per column slice, 26 KB hand-off records), or
- *                  K = V = 64 (run on the 128-wide kernels with the channels
- *                  and columns from 64 on held at zero).  When B*T == 0 the
+ *                  K = V = 64 (four state row tiles, 7 KB records).  When
+ *                  B*T == 0 the
  *                  token buffers (q, k, v, g, beta, out) may be NULL; the
  *                  call then only writes final_state (= initial state)
  *
@@ -295,8 +295,8 @@ size_t kda_workspace_reserved(void);
 size_t kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs);
 
 /*
- * The same for any supported head dimension K (64, 128 or 256): K = 64 and
- * 128 take 13 KB records per chunk slot and head, K = 256 26 KB records.
+ * The same for any supported head dimension K (64, 128 or 256): records of
+ * 7 KB (K = 64), 13 KB (K = 128) or 26 KB (K = 256) per chunk slot and head.
  * 0 on invalid sizes or an unsupported K.
  */
 size_t kda_workspace_size_hd(int32_t B, int32_t T, int32_t H, int32_t num_seqs, int32_t K);
@@ -307,8 +307,8 @@ size_t kda_workspace_size_hd(int32_t B, int32_t T, int32_t H, int32_t num_seqs, 
  * writes the hand-off record of every (chunk slot, head) into the caller's
  * `workspace` (device, kda_record_workspace_size(B, T, H, num_seqs, K)
  * bytes, 16-byte aligned).  Arguments as kda_fwd.  Record layout (per
- * 16-token chunk slot and head: 13312 bytes for K = 64 and 128, 26624
- * bytes for K = 256) is described in the library source; tests decode it to
+ * 16-token chunk slot and head: 7168, 13312 or 26624 bytes for K = 64, 128
+ * or 256) is described in the library source; tests decode it to
  * compare each stage with fp64 maths.
  */
 size_t kda_record_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs, int32_t K);

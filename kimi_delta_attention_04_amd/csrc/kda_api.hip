@@ -71,7 +71,7 @@ kda_status_t check_sizes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
                          const int32_t *cu, int32_t N) {
     if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID_ARG;
     if (cu ? (B != 1) : (N != B)) return KDA_ERR_INVALID_ARG;
-    // K = V = 128 or 256, or K = V = 64 (computed on the 128-wide tiles)
+    // K = V = 64, 128 or 256
     if (K != V || (K != kda::HD && K != 2 * kda::HD && K != 64)) return KDA_ERR_UNSUPPORTED;
     // token-row and unit counts must fit the int32 grid / index arithmetic
     if ((int64_t)B * T > INT32_MAX) return KDA_ERR_UNSUPPORTED;
@@ -168,8 +168,7 @@ size_t kda_workspace_reserved(void) {
 size_t kda_record_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs, int32_t K) {
     if (B < 1 || T < 0 || H < 1 || num_seqs < 1) return 0;
     if (K != 64 && K != kda::HD && K != 2 * kda::HD) return 0;
-    const size_t rec = K > kda::HD ? (size_t)kda::RecLayout<2 * kda::HD>::BYTES
-                                   : (size_t)kda::RecLayout<kda::HD>::BYTES;
+    const size_t rec = (size_t)kda::rec_bytes_for(K);
     return (size_t)num_slots(B, T, num_seqs) * (size_t)H * rec;
 }
 

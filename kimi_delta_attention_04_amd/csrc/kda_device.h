@@ -26,7 +26,7 @@
 
 namespace kda {
 
-constexpr int HD = 128;          // head dimension of the tiles (K = V; 64 runs on them zero-padded)
+constexpr int HD = 128;          // head dimension of the 128-wide tiles (the backward runs K = 64 on them zero-padded)
 constexpr int CS = 16;           // tokens per chunk
 constexpr int CS_TOKENS = CS;
 constexpr float LOG2E = 1.4426950408889634f;
@@ -59,13 +59,13 @@ constexpr int REC_M = 12288;
 constexpr int REC_GAM = 12800;
 constexpr int REC_BYTES = 13312;
 
-// The same record for tiles of KT key channels (128, or 256 for head
-// dimension 256): KT/32 channel blocks in KT, QT and WT, KT chunk decays,
+// The same record for tiles of KT key channels (the head dimension: 64, 128
+// or 256): KT/32 channel blocks in KT, QT and WT, KT chunk decays,
 // and the whole padded to a multiple of 1 KB (the scan moves records in
 // 1 KB DMA units).
 template <int KT>
 struct RecLayout {
-    static_assert(KT == 128 || KT == 256, "tile widths");
+    static_assert(KT == 64 || KT == 128 || KT == 256, "tile widths");
     static constexpr int KTO = 0;
     static constexpr int QT = CS_TOKENS * KT * 2;
     static constexpr int WT = 2 * QT;
@@ -77,9 +77,9 @@ static_assert(RecLayout<128>::QT == REC_QT && RecLayout<128>::WT == REC_WT &&
               RecLayout<128>::M == REC_M && RecLayout<128>::GAM == REC_GAM &&
               RecLayout<128>::BYTES == REC_BYTES, "the 128-wide record");
 
-// Record bytes for head dimension K (64 and 128 share the 128-wide tiles).
+// Record bytes for head dimension K (64, 128 or 256).
 __host__ __device__ constexpr int rec_bytes_for(int K) {
-    return K > 128 ? RecLayout<256>::BYTES : RecLayout<128>::BYTES;
+    return K > 128 ? RecLayout<256>::BYTES : (K == 64 ? RecLayout<64>::BYTES : RecLayout<128>::BYTES);
 }
 
 __host__ __device__ constexpr int state_chan(int t, int rho) {

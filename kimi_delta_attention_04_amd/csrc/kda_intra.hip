@@ -10,8 +10,8 @@ namespace kda {
 namespace {
 
 // One wave per (chunk slot, head), a workgroup of its own.  SG: scalar
-// (per-head) gate, g [B*T, H] and dt_bias [H].  KD: head dimension (128,
-// 256, or 64 computed on 128 channels of which the last 64 are zeros).
+// (per-head) gate, g [B*T, H] and dt_bias [H].  KD: head dimension (64,
+// 128 or 256), the width of the tiles and of the record.
 template <bool SG, int KD>
 __global__ __launch_bounds__(64, 2) void intra_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -20,7 +20,7 @@ __global__ __launch_bounds__(64, 2) void intra_kernel(
     const int32_t *__restrict__ cu, int N, int T, int H, uint8_t *__restrict__ ws)
 {
     constexpr int K = KD;
-    constexpr int KT = KD > HD ? 2 * HD : HD;     // channels of the tiles
+    constexpr int KT = KD;                        // channels of the tiles
     __shared__ __attribute__((aligned(16))) WaveLdsT<KT> lds;
     // Head fastest: the workgroups running together read neighbouring pieces
     // of the same token rows and write neighbouring records.  The records

@@ -41,7 +41,7 @@ using WaveLds = WaveLdsT<HD>;
 // in-chunk Gram products and the Kt / Qt records come straight from the
 // registers; the cumulative decay over tokens runs across the 16 lanes of a
 // DPP row.
-// NKB 32-channel blocks: 4 for the 128-wide tiles, 8 for head dimension 256.
+// NKB 32-channel blocks: 2, 4 or 8 for head dimension 64, 128 or 256.
 template <int NKB>
 struct IntraInT {
     u32x4_t g[NKB], q[NKB], k[NKB]; // [kb]: 8 bf16 channels of this lane's token
@@ -280,9 +280,13 @@ __device__ __forceinline__ void intra_compute(WaveLdsT<KT> &L, const IntraInT<KT
     wave_lds_sync();
     // the chunk decay into the record from LDS in one coalesced store (four
     // lanes' 16-byte pieces per block cost several times as much)
+    if constexpr (KT == 64) {
+        __builtin_nontemporal_store(*(const uint32_t *)&L.gam[l], (uint32_t *)(rec + R::GAM + l * 4));
+    } else {
 #pragma unroll
-    for (int p = 0; p < KT / 128; ++p)
-        __builtin_nontemporal_store(*(const u32x2_t *)&L.gam[2 * (64 * p + l)], (u32x2_t *)(rec + R::GAM + (64 * p + l) * 8));
+        for (int p = 0; p < KT / 128; ++p)
+            __builtin_nontemporal_store(*(const u32x2_t *)&L.gam[2 * (64 * p + l)], (u32x2_t *)(rec + R::GAM + (64 * p + l) * 8));
+    }
 
     // ---- T = (I + L)^{-1}, L = diag(beta) strict_lower(Akk) ---------------
     float br[4];

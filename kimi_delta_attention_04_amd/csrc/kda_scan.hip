@@ -33,8 +33,8 @@ namespace kda {
 namespace {
 
 // CT 16-column slices per compute wave, NW compute waves (and the DMA wave)
-// per workgroup; head dimension K = V = VD (128, 256, or 64 on the 128-wide
-// tiles).
+// per workgroup; head dimension K = V = VD (64, 128 or 256), which is also
+// the width of the tiles: VD / 16 state row tiles per slice.
 //
 // Two ring protocols.  One slice per wave on 128-wide tiles: the compute
 // waves read chunk c+1's operands into registers while they compute chunk c
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(64 * (NW + 1), VD > HD ? 1 : (CT == 2 ? 3 : 2)) voi
     constexpr int CW = NW * 16 * CT;                 // columns per workgroup
     constexpr int K = VD, V = VD;
     constexpr bool WIDE = VD > HD;                   // 256-wide tiles
-    constexpr int KTL = WIDE ? 2 * HD : HD;          // key channels of the tiles
+    constexpr int KTL = VD;                          // key channels of the tiles (64, 128, 256)
     constexpr int NT = KTL / 16;                     // state row tiles per slice
     constexpr int NKB = KTL / 32;                    // 32-channel blocks
     typedef RecLayout<KTL> R;
@@ -91,9 +91,6 @@ __global__ __launch_bounds__(64 * (NW + 1), VD > HD ? 1 : (CT == 2 ? 3 : 2)) voi
     const int64_t L = end - start;
     const int nch = (int)((L + CS - 1) / CS);
     const int64_t slot0 = seq_slot0(cu, n, T);
-    // K = V = 128 or 256, or 64 on the 128-wide tiles: state rows from K on stay zero
-    // (they load as zeros from the range-checked state buffers, receive no
-    // updates since their key channels are zero, and are not stored)
     const size_t row_bytes = (size_t)H * V * 2;       // one token row of v / out
 
     // ---- state slices: S[ct][t][j] = state[chan(t, 4grp+j)][col] -------------
@@ -172,8 +169,11 @@ __global__ __launch_bounds__(64 * (NW + 1), VD > HD ? 1 : (CT == 2 ? 3 : 2)) voi
         }
         op.m = *(const u32x2_t *)(Rp + R::M + l * 8);
         const int gch = 32 * (cg >> 2) + 8 * grp + 4 * ((cg >> 1) & 1) + 2 * (cg & 1);
+        // (64-wide tiles: lanes cg < 8 hold the decays of channels 0 .. 63,
+        // which are the ones decay_of reads; the others read the record's
+        // padding)
 #pragma unroll
-        for (int p = 0; p < NKB / 4; ++p) {
+        for (int p = 0; p < (NKB >= 4 ? NKB / 4 : 1); ++p) {
             const u32x2_t g2 = *(const u32x2_t *)(Rp + R::GAM + (128 * p + gch) * 4);
             op.gm[2 * p] = __uint_as_float(g2[0]);
             op.gm[2 * p + 1] = __uint_as_float(g2[1]);

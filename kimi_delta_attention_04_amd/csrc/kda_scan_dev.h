@@ -83,7 +83,7 @@ template <int CT, int NKB = 4>
 struct ChunkOps {
     u32x4_t kt[NKB], qt[NKB], wt[NKB];
     u32x2_t m;
-    float gm[NKB / 2];        // chunk decay of two state rows per 128 channels (see load_ops)
+    float gm[NKB >= 4 ? NKB / 2 : 2];   // chunk decay of two state rows per 128 channels (see load_ops)
     u32x2_t v[CT];            // v[row l%16][4(l/16) .. +3] of each slice: an MFMA A operand
 };
 

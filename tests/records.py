@@ -1,8 +1,8 @@
 """Codec of the 16-token hand-off record, test helper.
 
-A record holds one (16-token chunk, head) for KT key channels (128, also
-used by K = 64 with the channels from 64 on zero, or 256) in the register
-layouts of the scan's MFMA operands; lane l of a wave holds row l % 16:
+A record holds one (16-token chunk, head) for KT key channels (the head
+dimension: 64, 128 or 256) in the register layouts of the scan's MFMA
+operands; lane l of a wave holds row l % 16:
   KT  [kb 0..KT/32-1][lane][8 bf16]  Kt[l%16][32 kb + 8 (l/16) + i]
   QT  the same for Qt                                       (at 32 KT bytes)
   WT  [tp 0..KT/32-1][lane][8 bf16]  W[4 (l/16) + j][state_chan(2 tp + h, l%16)]
@@ -10,8 +10,8 @@ layouts of the scan's MFMA operands; lane l of a wave holds row l % 16:
                                                             (at 64 KT bytes)
   M   [lane][4 bf16]                 M[l%16][4 (l/16) + j]  (at 96 KT bytes)
   GAM [KT fp32]                      chunk decay per key channel (512 bytes on)
-and the whole padded to a multiple of 1 KB (13312 bytes at KT = 128, 26624
-at 256).  state_chan is the state-row order of the scan's accumulator
+and the whole padded to a multiple of 1 KB (7168 bytes at KT = 64, 13312 at
+128, 26624 at 256).  state_chan is the state-row order of the scan's accumulator
 tiles.
 """
 from __future__ import annotations

@@ -60,14 +60,14 @@ def test_constants(lib):
 
 
 def test_workspace_size(lib):
-    # 16-token chunks with 13 KB records at K = 64 and 128
+    # 16-token chunks with 13 KB records at K = 128
     assert kda.workspace_size(1, 8192, 96, 1) == (8192 // 16 + 1) * 96 * 13312
     assert kda.workspace_size(1, 8192, 96, 12) == (8192 // 16 + 12) * 96 * 13312
     assert kda.workspace_size(3, 37, 2, 3) == (111 // 16 + 3) * 2 * 13312
     assert kda.workspace_size(0, 16, 1, 1) == 0
     assert kda.workspace_size(1, 16, 1, 0) == 0
-    # head dimension 64 shares the 128-wide records; 256 takes 26 KB ones
-    assert kda.workspace_size(1, 8192, 96, 1, K=64) == (8192 // 16 + 1) * 96 * 13312
+    # head dimension 64 takes 7 KB records, 256 26 KB ones
+    assert kda.workspace_size(1, 8192, 96, 1, K=64) == (8192 // 16 + 1) * 96 * 7168
     assert kda.workspace_size(1, 8192, 96, 1, K=256) == (8192 // 16 + 1) * 96 * 26624
     assert kda.workspace_size(1, 8192, 96, 1, K=96) == 0
     assert lib.kda_workspace_size(1, 100, 3, 1) == kda.workspace_size(1, 100, 3, 1, K=128)

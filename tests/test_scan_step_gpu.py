@@ -39,8 +39,9 @@ LENGTHS = [16, 9, 1]
 
 
 def tile(D):
-    """Key channels of the record tiles at head dimension D."""
-    return 256 if D == 256 else 128
+    """Key channels of the record tiles at head dimension D (the head
+    dimension itself)."""
+    return D
 
 
 def test_record_codec_round_trip():

@@ -48,7 +48,8 @@ def rel(a, b):
 
 
 @pytest.mark.parametrize("T,lb,K", [(64, -5.0, 128), (45, -5.0, 128), (64, -5.4, 128),
-                                    (48, -5.0, 256), (37, -5.0, 256)])
+                                    (48, -5.0, 256), (37, -5.0, 256), (48, -5.0, 64),
+                                    (29, -5.0, 64)])
 def test_intra_stage_records(T, lb, K):
     """Whole chunks, ragged tails (45 = 2 x 16 + 13, 37 = 2 x 16 + 5), the
     lowest supported lower bound with large gates (the in-chunk factors at
