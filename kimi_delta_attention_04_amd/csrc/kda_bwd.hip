@@ -204,18 +204,23 @@ __device__ __forceinline__ u32x2_t to_wt(u32x2_t a, u32x2_t eye) {
 // channels 32kb + 8grp + i0 + i of this lane's token: per (token, channel)
 // x2 = (g + dt_bias) log2 e, the clamped gate max(-A log2(1 + 2^x2),
 // lb log2 e) (zero on padding rows), and its inclusive cumulative sum G over
-// the chunk's tokens (across the 16 lanes of the DPP row).
+// the chunk's tokens (across the 16 lanes of the DPP row).  U, SG (when
+// given): the gate before its clamp, y = -A u with u = log2(1 + 2^x2), as u,
+// and sigmoid(g + dt_bias) = 2^(x2 - u) (since 2^u = 1 + 2^x2).
 template <int NI>
 __device__ __forceinline__ void block_decay(const u32x4_t gw, const float *__restrict__ dtb_lds,
                                             int kb, int i0, float A, float lb2, bool live,
-                                            float (&G)[NI]) {
+                                            float (&G)[NI], float *U = nullptr, float *SG = nullptr) {
     const int grp = (threadIdx.x & 63) >> 4;
     if (A > 0.f) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const float x2 = elem(gw, i0 + i) * LOG2E + dtb_lds[32 * kb + 8 * grp + i0 + i];
-            const float la = fmaxf(-A * fast_log2(1.f + fast_exp2(x2)), lb2);
+            const float u = fast_log2(1.f + fast_exp2(x2));
+            const float la = fmaxf(-A * u, lb2);
             G[i] = live ? la : 0.f;
+            if (U) U[i] = u;
+            if (SG) SG[i] = fast_exp2(x2 - u);
         }
 #pragma unroll
         for (int i = 0; i < NI; ++i) G[i] += row_shr<1>(G[i]);
@@ -227,7 +232,11 @@ __device__ __forceinline__ void block_decay(const u32x4_t gw, const float *__res
         for (int i = 0; i < NI; ++i) G[i] += row_shr<8>(G[i]);
     } else {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) G[i] = 0.f;
+        for (int i = 0; i < NI; ++i) {
+            G[i] = 0.f;
+            if (U) U[i] = 0.f;
+            if (SG) SG[i] = 0.f;
+        }
     }
 }
 
@@ -607,8 +616,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     for (int t = 0; t < NT; ++t) {
         const int kb = t >> 1, hh = t & 1, c0 = 32 * kb + 8 * grp + 4 * hh;
         if (hh == 0) { gq = in.g[kb]; kq = in.k[kb]; qq = in.q[kb]; }
-        float G[4];
-        block_decay<4>(gq, L.dtb, kb, 4 * hh, A, lb2, live, G);
+        float G[4], U[4], SG[4];
+        block_decay<4>(gq, L.dtb, kb, 4 * hh, A, lb2, live, G, U, SG);
         // as in the factors: Kt, Qt, Kb rescaled by e^{-+G_last/2} (rs, ri) for
         // the products with the 16 x 16 gradients, whose results are then
         // scaled back into dq = dQt e^G and dk = dKt e^G + dKb e^-G directly
@@ -649,7 +658,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
         const f32x4_t qs = L.qs[t][l], ks = L.ks[t][l];
         const f32x4_t gm = *(const f32x4_t *)&L.gam[c0];
         const f32x4_t dgs = *(const f32x4_t *)&L.dgs[c0] + *(const f32x4_t *)&L.dgs2[c0];
-        const f32x4_t dtb2 = *(const f32x4_t *)&L.dtb[c0];
         const float daq = L.daq[tok];
         float vq[4], vk[4], vg[4], pd[4];
 #pragma unroll
@@ -669,10 +677,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
             const float acc = gdg + row_suffix16(dG);
             // the gate a = max(y, lb), y = -A softplus(g + dt_bias): no
             // gradient through the clamped branch; dy/dA_log = y
-            const float x2 = elem(gq, 4 * hh + j) * LOG2E + dtb2[j];
-            const float y2 = A > 0.f ? -A * fast_log2(1.f + fast_exp2(x2)) : 0.f;
+            const float y2 = -A * U[j];
             const float dy = (live && y2 >= lb2) ? acc : 0.f;
-            const float dx = -dy * A * __builtin_amdgcn_rcpf(1.f + fast_exp2(-x2));
+            const float dx = -dy * A * SG[j];
             pa += dy * (y2 * LN2);
             pd[j] = row_sum16(dx);
             vq[j] = dQe + daq * kv[j];
