@@ -299,7 +299,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     // Over the value columns in 32-column steps s, per state row tile t:
     //   (dO S0^T)^T, (dX S0^T)^T   rows chan(t, .): token-per-lane results
     //   dWm = X dS1^T              W^T layout (A = X, B = dS1 rows)
-    //   diag(dS1 S0^T)             per lane, summed over its four lane groups
+    //   diag(dS1 S0^T)             the diagonal of S0 rows x dS1 rows^T
     // and once: dM / scale = dO X^T (tile).  The stored states are bf16 rows
     // [16-column part][128 rows][16]; the A operand of tile t, step s is row
     // chan(t, tok), columns 32s + 8grp .. +7.
@@ -375,8 +375,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
                 for (int st = 0; st < NKB; ++st) { na[st] = sld(S0, st, t + 1); nd[st] = sld(DS, st, t + 1); }
             }
-            f32x4_t Qa = zero, Ka = zero, Wa = zero, Ea = zero, Eb = zero;
-            float dg = 0.f;
+            f32x4_t Qa = zero, Ka = zero, Wa = zero, Ea = zero, Eb = zero, Dg = zero;
 #pragma unroll
             for (int st = 0; st < NKB; ++st) {
                 Qa = mfma_k32(sa[st], ob[st], Qa);
@@ -388,9 +387,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
                     Ea = mfma_k32(sa[st], e1[st], Ea);          // (dO_n S0^T)^T
                     Eb = mfma_k32(sa[st], e2[st], Eb);          // (dX_n S0^T)^T
                 }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) dg = fmaf(elem(sa[st], i), elem(sd[st], i), dg);
+                // S0 rows against dS1 rows (the same registers are the B
+                // operand of their transpose): diag(dS1 S0^T) on the diagonal
+                Dg = mfma_k32(sa[st], sd[st], Dg);
             }
+            // lane (tok, grp = tok / 4) holds the diagonal element of channel
+            // chan(t, tok) in slot tok % 4; summed over the lane groups
+            float dg = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dg = 4 * grp + j == tok ? Dg[j] : dg;
             dg += __shfl_xor(dg, 16, 64);
             dg += __shfl_xor(dg, 32, 64);                   // channel chan(t, tok)
             const int ct = state_chan(t, tok);
