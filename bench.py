@@ -186,9 +186,13 @@ def bench_backward(args, torch, kda, kda_inputs):
     """One step = one kda_bwd call over the workload (all five kernels)."""
     name = args.workload or kda_inputs.HEADLINE
     w = kda_inputs.WORKLOADS[name]
+    if args.head_dim != w.K:
+        import dataclasses
+        w = dataclasses.replace(w, name=f"{w.name}_D{args.head_dim}", K=args.head_dim, V=args.head_dim)
+        name = w.name
     log(f"[bench] backward: generating {name} ...")
     inp = kda_inputs.generate(w)
-    d_out, d_final = kda_inputs.output_grads(w.seed + 1, w.B, w.T, w.H, N=w.num_seqs)
+    d_out, d_final = kda_inputs.output_grads(w.seed + 1, w.B, w.T, w.H, V=w.V, N=w.num_seqs, K=w.K)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
@@ -262,11 +266,12 @@ def bench_backward(args, torch, kda, kda_inputs):
             "hbm_frac": path_gbs / HBM_PEAK_GBS, "stage_ms": stage,
             "stage_traffic_bytes": {k: (t["total_bytes"] if t else None) for k, t in
                                     ((k, stored_traffic(name, k, backward=True)) for k in names)},
-            # per (chunk slot, head): the two scans' records (9 KB + 13 KB),
-            # S0 and dS1 (bf16 128 x 128), X (bf16 16 x 128), partial sums
+            # per (chunk slot, head): the two scans' records (9 KB + 13 KB at
+            # K = 128, 5 KB + 7 KB at 64), S0 and dS1 (bf16 K x V), X (bf16
+            # 16 x V), the partial sums (129 floats)
             "workspace_bytes": int(w.H * (w.tokens // BWD_CHUNK + w.num_seqs) *
-                                   (9216 + 13312 + 2 * w.K * w.V * 2 + BWD_CHUNK * w.V * 2 +
-                                    (w.K + 1) * 4))}
+                                   ((9216 + 13312 if w.K == 128 else 5120 + 7168) +
+                                    2 * w.K * w.V * 2 + BWD_CHUNK * w.V * 2 + 129 * 4))}
     cpu = None
     if not args.no_cpu_baseline:
         import oracle

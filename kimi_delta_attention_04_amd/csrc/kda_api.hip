@@ -417,7 +417,7 @@ kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
 
     hipStream_t s = (hipStream_t)stream;
     const int64_t slots = num_slots(B, T, num_seqs);
-    const size_t bytes = kda::bwd_workspace_bytes(slots, H);
+    const size_t bytes = kda::bwd_workspace_bytes(slots, H, K);
     hipMemPool_t pool;
     if ((st = device_pool(&pool)) != KDA_OK) return st;
     if (cu_seqlens && cu_check_enabled() &&

@@ -305,8 +305,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     // chan(t, tok), columns 32s + 8grp .. +7.
     const bool odd = (ci & 1) != 0;                         // S0 from the chunk before
     const bool reb = !odd && t0 + CS < tend;                // dS1 from the chunk after
-    typedef RecLayout<HD> R;
-    typedef StatesRec SR;
+    typedef RecLayout<KD> R;
+    typedef StatesRecT<KD> SR;
     const size_t shS = odd ? sh - H : sh, shD = reb ? sh + H : sh;
     // the neighbour's chunk decay (p's for an odd chunk, n's for a rebuilt dS1)
     {
@@ -316,10 +316,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     f32x4_t dM = zero;
     u32x2_t wwh[NT], wwl[NT];
     {
-        const uint16_t *S0 = st0 + shS * HD * HD + (size_t)(l >> 5) * HD * 16 + 8 * ((l >> 4) & 1);
-        const uint16_t *DS = dst1 + shD * HD * HD + (size_t)(l >> 5) * HD * 16 + 8 * ((l >> 4) & 1);
+        const uint16_t *S0 = st0 + shS * KD * KD + (size_t)(l >> 5) * KD * 16 + 8 * ((l >> 4) & 1);
+        const uint16_t *DS = dst1 + shD * KD * KD + (size_t)(l >> 5) * KD * 16 + 8 * ((l >> 4) & 1);
         auto sld = [&](const uint16_t *b, int s, int t) {
-            return *(const u32x4_t *)&b[((size_t)2 * s * HD + state_chan(t, tok)) * 16];
+            return *(const u32x4_t *)&b[((size_t)2 * s * KD + state_chan(t, tok)) * 16];
         };
         // the token-per-lane operands of every step: this chunk's dO, X, dX;
         // e1, e2: the neighbour's X (odd) or dO, dX (rebuilt dS1)
@@ -329,8 +329,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
         const __amdgpu_buffer_rsrc_t r_dx = make_rsrc(dvv + rbase, rbytes);
         const __amdgpu_buffer_rsrc_t r_don = make_rsrc(dout + rbase_n, reb ? rbytes_n : 0u);
         const __amdgpu_buffer_rsrc_t r_dxn = make_rsrc(dvv + rbase_n, reb ? rbytes_n : 0u);
-        const uint16_t *xr = xws + sh * CS * HD + tok * HD + 8 * grp;
-        const uint16_t *xp = xws + shS * CS * HD + tok * HD + 8 * grp;
+        const uint16_t *xr = xws + sh * CS * KD + tok * KD + 8 * grp;
+        const uint16_t *xp = xws + shS * CS * KD + tok * KD + 8 * grp;
         u32x4_t ob[NKB], xb[NKB], db[NKB], e1[NKB], e2[NKB];
 #pragma unroll
         for (int st = 0; st < NKB; ++st) {
@@ -459,9 +459,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     }
 
     // ---- chunk factors, and Y = Kb Gam dWm^T --------------------------------
-    stage_dtb<false, HD>(L.dtb, dt_bias, h, KD);
-    IntraIn in;
-    intra_load<false, HD>(in, q, k, g, beta, t0, len, H, h, KD);
+    stage_dtb<false, KD>(L.dtb, dt_bias, h, KD);
+    IntraInT<NKB> in;
+    intra_load<false, KD>(in, q, k, g, beta, t0, len, H, h, KD);
     {
         const float x = bf16f((uint16_t)in.beta);
         const float b = __builtin_amdgcn_rcpf(1.f + fast_exp2(-x * LOG2E));
@@ -721,8 +721,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
 // ---------------------------------------------------------------------------
 // prep: one wave per (chunk slot, head), the chunk factors into the two
 // scans' bf16 records (in the forward record's MFMA operand layouts,
-// RecLayout<HD>):
-//   states record (StatesRec, kda_bwd_dev.h): Kt and Wm = P^T Kb Gam in the
+// RecLayout<KD>, at head dimension KD = 64 or 128):
+//   states record (StatesRecT<KD>, kda_bwd_dev.h): Kt and Wm = P^T Kb Gam in the
 //     Kt and W^T layouts, and the chunk decay, the operands of
 //     X = V - Kt S0 and S1 = Gam S0 + Wm^T X;
 //   reverse record: Wm in the Kt layout (the A operand of Wm dS), scale Qt
@@ -730,9 +730,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
 //     update), scale M^T (the M slot) and the chunk decay.
 // The factors are formed as in the chunk kernel: Grams of the rescaled rows
 // from (hi, lo) operands, T on fp32 MFMAs, P^T Kb Gam from (hi, lo)
-// operands; layouts change through the identity.  Head dimension 64 runs on
-// all four channel blocks: its loads leave blocks 2 and 3 zero, which makes
-// their record entries zero.
+// operands; layouts change through the identity.  The decay regions cover
+// 128 channels at either head dimension (zeros past KD).
 // ---------------------------------------------------------------------------
 struct PrepWaveLds {
     float beta[CS];
@@ -742,16 +741,17 @@ struct PrepWaveLds {
     float tile[CS][CS + 1];           // 16 x 16 transposes
 };
 
+template <int KD>
 __global__ __launch_bounds__(64) void bwd_prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
     const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb, float scale,
-    const int32_t *__restrict__ cu, int N, int T, int H, int kd, uint8_t *__restrict__ srec,
+    const int32_t *__restrict__ cu, int N, int T, int H, uint8_t *__restrict__ srec,
     uint8_t *__restrict__ rrec)
 {
-    constexpr int NKB = HD / 32, NT = 2 * NKB;
-    typedef RecLayout<HD> R;
-    typedef StatesRec SR;
+    constexpr int NKB = KD / 32, NT = 2 * NKB;
+    typedef RecLayout<KD> R;
+    typedef StatesRecT<KD> SR;
     __shared__ __attribute__((aligned(16))) PrepWaveLds L;
     const int64_t slot = blockIdx.x / (unsigned)H;
     const int h = (int)(blockIdx.x % (unsigned)H);
@@ -768,9 +768,9 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(
     uint8_t *sr = srec + sh * SR::BYTES;
     uint8_t *rr = rrec + sh * R::BYTES;
 
-    stage_dtb<false, HD>(L.dtb, dt_bias, h, kd);
-    IntraIn in;
-    intra_load<false, HD>(in, q, k, g, beta, t0, len, H, h, kd);
+    stage_dtb<false, KD>(L.dtb, dt_bias, h, KD);
+    IntraInT<NKB> in;
+    intra_load<false, KD>(in, q, k, g, beta, t0, len, H, h, KD);
     {
         const float x = bf16f((uint16_t)in.beta);
         const float b = __builtin_amdgcn_rcpf(1.f + fast_exp2(-x * LOG2E));
@@ -849,10 +849,12 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(
         __builtin_nontemporal_store(qw, (u32x4_t *)(rr + R::QT + (kb * 64 + l) * 16));
         __builtin_nontemporal_store(nw, (u32x4_t *)(rr + R::WT + (kb * 64 + l) * 16));
     }
-    // the chunk decay into both records, one coalesced store each
+    // the chunk decay into both records, one coalesced store each (128
+    // channels, zeros past KD)
     wave_lds_sync();
     {
-        const u32x2_t gv = *(const u32x2_t *)&L.gam[2 * l];
+        const u32x2_t z2 = {0u, 0u};
+        const u32x2_t gv = 2 * l < KD ? *(const u32x2_t *)&L.gam[2 * l] : z2;
         __builtin_nontemporal_store(gv, (u32x2_t *)(sr + SR::GAM + l * 8));
         __builtin_nontemporal_store(gv, (u32x2_t *)(rr + R::GAM + l * 8));
     }
@@ -988,10 +990,20 @@ hipError_t side_stream(SideStream *&out) {
     return hipSuccess;
 }
 
-size_t bwd_workspace_bytes(int64_t num_slots, int H) {
+namespace {
+// Per (chunk slot, head): the two scans' records, S0 and dS1 (bf16 KD x KD),
+// X (bf16 16 x KD), the dt_bias partial sums (128 floats at either head
+// dimension) and the A_log partial sum.
+template <int KD>
+constexpr size_t bwd_slot_bytes() {
+    return (size_t)StatesRecT<KD>::BYTES + (size_t)RecLayout<KD>::BYTES +
+           (2 * (size_t)KD * KD + (size_t)CS * KD) * sizeof(uint16_t) + ((size_t)HD + 1) * sizeof(float);
+}
+}  // namespace
+
+size_t bwd_workspace_bytes(int64_t num_slots, int H, int K) {
     const size_t sh = (size_t)num_slots * H;
-    return sh * ((size_t)StatesRec::BYTES + (size_t)RecLayout<HD>::BYTES +
-                 (2 * (size_t)HD * HD + (size_t)CS * HD) * sizeof(uint16_t) + ((size_t)HD + 1) * sizeof(float));
+    return sh * (K == 64 ? bwd_slot_bytes<64>() : bwd_slot_bytes<HD>());
 }
 
 hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
@@ -1006,13 +1018,17 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
     const size_t sh = (size_t)num_slots * H;
     // every region starts at a multiple of 256 bytes (each per-(slot, head)
     // size is one, the last region's aside)
-    static_assert(RecLayout<HD>::BYTES % 256 == 0 && StatesRec::BYTES % 256 == 0, "256-byte regions");
+    static_assert(RecLayout<HD>::BYTES % 256 == 0 && StatesRecT<HD>::BYTES % 256 == 0 &&
+                  RecLayout<64>::BYTES % 256 == 0 && StatesRecT<64>::BYTES % 256 == 0, "256-byte regions");
+    const bool k64 = K == 64;
+    const size_t srb = k64 ? StatesRecT<64>::BYTES : StatesRecT<HD>::BYTES;
+    const size_t rrb = k64 ? RecLayout<64>::BYTES : RecLayout<HD>::BYTES;
     uint8_t *srec = (uint8_t *)ws;
-    uint8_t *rrec = srec + sh * StatesRec::BYTES;
-    uint16_t *st0 = (uint16_t *)(rrec + sh * RecLayout<HD>::BYTES);
-    uint16_t *dst1 = st0 + sh * HD * HD;
-    uint16_t *xws = dst1 + sh * HD * HD;
-    float *pdtb = (float *)(xws + sh * CS * HD);
+    uint8_t *rrec = srec + sh * srb;
+    uint16_t *st0 = (uint16_t *)(rrec + sh * rrb);
+    uint16_t *dst1 = st0 + sh * K * K;
+    uint16_t *xws = dst1 + sh * K * K;
+    float *pdtb = (float *)(xws + sh * CS * K);
     float *palog = pdtb + sh * HD;
     const dim3 chunks((unsigned)sh);
     hipError_t e = hipSuccess;
@@ -1020,8 +1036,12 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
         if (events && events[i] && e == hipSuccess) e = hipEventRecord(events[i], stream);
     };
     mark(0);
-    hipLaunchKernelGGL(bwd_prep_kernel, chunks, dim3(64), 0, stream,
-                       q, k, g, beta, A_log, dt_bias, lower_bound, scale, cu, N, T, H, K, srec, rrec);
+    if (k64)
+        hipLaunchKernelGGL(bwd_prep_kernel<64>, chunks, dim3(64), 0, stream,
+                           q, k, g, beta, A_log, dt_bias, lower_bound, scale, cu, N, T, H, srec, rrec);
+    else
+        hipLaunchKernelGGL(bwd_prep_kernel<HD>, chunks, dim3(64), 0, stream,
+                           q, k, g, beta, A_log, dt_bias, lower_bound, scale, cu, N, T, H, srec, rrec);
     mark(1);
     // The reverse scan needs only the prep kernel's records and dO, not the
     // states scan's output: it runs on the device's side stream, forked after
@@ -1046,7 +1066,7 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
     hipLaunchKernelGGL(bwd_chunk_kernel<KD_>, chunks, dim3(64), 0, stream, q, k, g, beta, A_log, \
                        dt_bias, lower_bound, scale, dout, cu, N, T, H, st0, dst1, xws, dv, srec, rrec, dq, dk, \
                        dg, dbeta, palog, pdtb)
-    if (K == HD) KDA_BWD_CHUNK(HD); else KDA_BWD_CHUNK(64);
+    if (k64) KDA_BWD_CHUNK(64); else KDA_BWD_CHUNK(HD);
 #undef KDA_BWD_CHUNK
     mark(4);
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)H), dim3(HD), 0, stream,

@@ -35,8 +35,7 @@ namespace {
 // Stored for the chunk kernel: dS1 rounded to bf16 (odd chunks of the
 // sequence and the last one), as rows of each 16-column part ([part][row]
 // [16 columns]), and dV = dX in bf16.
-// One slice per wave on the 128-wide tiles (K = V = 128, or 64 with V = 64
-// columns and the rows from 64 on zero).
+// One slice per wave on tiles as wide as the head (K = V = VD, 64 or 128).
 template <int NW, int VD>
 __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
     const uint16_t *__restrict__ dout, const uint8_t *__restrict__ rrec,
@@ -46,17 +45,23 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
 {
     constexpr int CW = NW * 16;
     constexpr int V = VD;
-    constexpr int NT = HD / 16, NKB = HD / 32;
-    typedef RecLayout<HD> R;
+    constexpr int NT = VD / 16, NKB = VD / 32;
+    typedef RecLayout<VD> R;
     constexpr int RKB = R::BYTES / 1024;
     constexpr int NSPLIT = V / CW;
     static_assert(NSPLIT * CW == V, "column parts cover the head");
     constexpr int V_KB = CS * CW * 2 / 1024;
     constexpr int UNITS = RKB + V_KB;
     constexpr int VROW_LANES = CW * 2 / 16;
-    constexpr int DEPTH = RING_DEPTH<CW>;
+    // LAG (eight compute waves, which must fit 168 registers: three waves
+    // share a SIMD): the compute waves read a chunk's state-update operands
+    // (scale Qt, -Kt) at the top of its own iteration instead of one chunk
+    // ahead, and the ring has one more slot, which the DMA wave refills one
+    // chunk later (chunk c-1's slot in iteration c).
+    constexpr bool LAG = NW > 4;
+    constexpr int DEPTH = RING_DEPTH<CW> + (LAG ? 1 : 0);
     __shared__ ScanSlot<CW, R::BYTES> ring[DEPTH];
-    static_assert((DEPTH - 1) * UNITS <= 63, "vmcnt holds at most 63");
+    static_assert((DEPTH - (LAG ? 2 : 1)) * UNITS <= 63, "vmcnt holds at most 63");
 
     const int b = blockIdx.x;
     const int u = 8 * (b / (8 * NSPLIT)) + (b & 7);
@@ -88,9 +93,8 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int row = state_chan(t, 4 * grp + j);
-                const int idx = row * V + col0 + wcol0 + cg;
-                S[t][j] = row < V ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, idx * 4, 0, 0)) : 0.f;
+                const int idx = state_chan(t, 4 * grp + j) * V + col0 + wcol0 + cg;
+                S[t][j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, idx * 4, 0, 0));
             }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -119,15 +123,22 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
             dma16(rv, &sl.v[vrow0][0], (int)((vrow0 + l / VROW_LANES) * row_bytes) + (l % VROW_LANES) * 16);
         }
     };
+    // the state-update operands (scale Qt and -Kt in the W^T layout)
+    auto load_update = [&](int slot, ChunkOps<1, NKB> &op) {
+        const uint8_t *Rp = ring[slot].rec;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            op.qt[kb] = *(const u32x4_t *)(Rp + R::QT + (kb * 64 + l) * 16);
+            op.wt[kb] = *(const u32x4_t *)(Rp + R::WT + (kb * 64 + l) * 16);
+        }
+    };
+    // the chunk's other operands, and (not LAG) the update operands
     auto load_ops = [&](int slot, ChunkOps<1, NKB> &op) {
         const ScanSlot<CW, R::BYTES> &sl = ring[slot];
         const uint8_t *Rp = sl.rec;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            op.kt[kb] = *(const u32x4_t *)(Rp + R::KTO + (kb * 64 + l) * 16);
-            op.qt[kb] = *(const u32x4_t *)(Rp + R::QT + (kb * 64 + l) * 16);
-            op.wt[kb] = *(const u32x4_t *)(Rp + R::WT + (kb * 64 + l) * 16);
-        }
+        for (int kb = 0; kb < NKB; ++kb) op.kt[kb] = *(const u32x4_t *)(Rp + R::KTO + (kb * 64 + l) * 16);
+        if constexpr (!LAG) load_update(slot, op);
         op.m = *(const u32x2_t *)(Rp + R::M + l * 8);
         const int gch = 32 * (cg >> 2) + 8 * grp + 4 * ((cg >> 1) & 1) + 2 * (cg & 1);
         const u32x2_t g2 = *(const u32x2_t *)(Rp + R::GAM + gch * 4);
@@ -194,7 +205,7 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
         __builtin_amdgcn_raw_buffer_store_b64(vs, ro, (int)(cg * row_bytes) + (wcol0 + 4 * grp) * 2, 0, 0);
         // dS1 of the odd chunks and of the last one only (the chunk kernel
         // rebuilds an even chunk's products from the chunk after)
-        uint16_t *so = ds1 + sh * HD * HD + (size_t)p16 * HD * 16 + 4 * grp;
+        uint16_t *so = ds1 + sh * V * V + (size_t)p16 * V * 16 + 4 * grp;
         if ((ci & 1) == 1 || ci == nch - 1)
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -205,16 +216,34 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
         }
     };
 
-    // the two-operand-set protocol of scan_kernel
+    // The two-operand-set protocol of scan_kernel (chunk c in ring slot
+    // c % DEPTH).  Not LAG: the DMA wave refills chunk c's slot in iteration
+    // c, whose operands the compute waves then hold in registers.  LAG: the
+    // compute waves still read chunk c's update operands in iteration c, so
+    // the DMA wave refills chunk c-1's slot; DEPTH-1 chunks go out before the
+    // first iteration, and at the top of iteration c chunk c+1 has landed
+    // when the DMAs issued after its own number (DEPTH-3) UNITS.
     if (dma_wave) {
+        if constexpr (LAG) {
 #pragma unroll
-        for (int c = 0; c < DEPTH; ++c) issue(c, c);
-        wait_vm_barrier<(DEPTH - 1) * UNITS>();
-        int slot = 0;
-        for (int c = 0; c < nch; ++c) {
-            wait_vm_barrier<(DEPTH - 2) * UNITS>();
-            issue(c + DEPTH, slot);
-            slot = slot == DEPTH - 1 ? 0 : slot + 1;
+            for (int c = 0; c < DEPTH - 1; ++c) issue(c, c);
+            wait_vm_barrier<(DEPTH - 2) * UNITS>();   // chunk 0 landed
+            int slot = DEPTH - 1;                     // ring slot of chunk c-1
+            for (int c = 0; c < nch; ++c) {
+                wait_vm_barrier<(DEPTH - 3) * UNITS>();  // chunk c+1 landed; slot of c-1 free
+                issue(c + DEPTH - 1, slot);
+                slot = slot == DEPTH - 1 ? 0 : slot + 1;
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < DEPTH; ++c) issue(c, c);
+            wait_vm_barrier<(DEPTH - 1) * UNITS>();
+            int slot = 0;
+            for (int c = 0; c < nch; ++c) {
+                wait_vm_barrier<(DEPTH - 2) * UNITS>();
+                issue(c + DEPTH, slot);
+                slot = slot == DEPTH - 1 ? 0 : slot + 1;
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         return;
@@ -222,12 +251,14 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
     lds_barrier();
     ChunkOps<1, NKB> opA, opB;
     load_ops(0, opA);
-    int next = 1;
-    auto step = [&](int c, const ChunkOps<1, NKB> &cur, ChunkOps<1, NKB> &nxt) {
-        lds_barrier();
+    int cur = 0;                                      // ring slot of chunk c
+    auto step = [&](int c, ChunkOps<1, NKB> &now, ChunkOps<1, NKB> &nxt) {
+        lds_barrier();                                // own reads of chunk c-1 done; chunk c+1 landed
+        const int next = cur == DEPTH - 1 ? 0 : cur + 1;
         load_ops(next, nxt);
-        compute(c, cur);
-        next = next == DEPTH - 1 ? 0 : next + 1;
+        if constexpr (LAG) load_update(cur, now);
+        compute(c, now);
+        cur = next;
     };
     for (int c = 0; c < nch; c += 2) {
         step(c, opA, opB);
@@ -239,8 +270,7 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int row = state_chan(t, 4 * grp + j);
-                if (row < V) dinit[base + (size_t)row * V + col0 + wcol0 + cg] = S[t][j];
+                dinit[base + (size_t)state_chan(t, 4 * grp + j) * V + col0 + wcol0 + cg] = S[t][j];
             }
     }
 }
@@ -250,11 +280,11 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
 // S1 = diag(gamma) S0 + Wm^T X, with the state and X as (hi, lo) bf16
 // operands), without the output, storing
 // for the chunk kernel the start state S0 rounded to bf16 of the sequence's
-// even chunks (rows of each 16-column part, [part][128 rows][16 columns])
-// and X in bf16 ([16][V]) of every chunk.  The record of each chunk (written by the backward's prep
-// kernel) holds Kt and Wm in the forward record's Kt and W^T slots and the
-// chunk decay; its Qt and M slots are not used.  One slice per wave on the
-// 128-wide tiles (K = V = 128, or 64 with V = 64 columns).
+// even chunks (rows of each 16-column part, [part][VD rows][16 columns])
+// and X in bf16 ([16][V]) of every chunk.  The record of each chunk
+// (StatesRecT<VD>, written by the backward's prep kernel) holds Kt and Wm in
+// the forward record's Kt and W^T layouts and the chunk decay.  One slice
+// per wave on tiles as wide as the head (K = V = VD, 64 or 128).
 template <int NW, int VD>
 __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
     const uint16_t *__restrict__ v, const uint8_t *__restrict__ srec,
@@ -263,8 +293,8 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
 {
     constexpr int CW = NW * 16;
     constexpr int V = VD;
-    constexpr int NT = HD / 16, NKB = HD / 32;
-    typedef StatesRec R;
+    constexpr int NT = VD / 16, NKB = VD / 32;
+    typedef StatesRecT<VD> R;
     constexpr int RKB = R::BYTES / 1024;
     constexpr int NSPLIT = V / CW;
     static_assert(NSPLIT * CW == V, "column parts cover the head");
@@ -305,13 +335,9 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int row = state_chan(t, 4 * grp + j);
-                const int idx = row * V + col0 + wcol0 + cg;
-                float x = 0.f;
-                if (row < V)
-                    x = init_fp32 ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, idx * 4, 0, 0))
-                                  : bf16f(__builtin_amdgcn_raw_buffer_load_b16(rs, idx * 2, 0, 0));
-                S[t][j] = x;
+                const int idx = state_chan(t, 4 * grp + j) * V + col0 + wcol0 + cg;
+                S[t][j] = init_fp32 ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, idx * 4, 0, 0))
+                                    : bf16f(__builtin_amdgcn_raw_buffer_load_b16(rs, idx * 2, 0, 0));
             }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -411,11 +437,11 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
         {
             const f32x4_t xt = mfma_k16(Xb, eye, zero);
             const u32x2_t xv = {pack2(xt[0], xt[1]), pack2(xt[2], xt[3])};
-            *(u32x2_t *)&xws[sh * CS * HD + cg * HD + col0 + wcol0 + 4 * grp] = xv;
+            *(u32x2_t *)&xws[sh * CS * V + cg * V + col0 + wcol0 + 4 * grp] = xv;
         }
         // S0 of the even chunks only (the chunk kernel rebuilds an odd
         // chunk's products from the chunk before)
-        uint16_t *so = s0 + sh * HD * HD + (size_t)p16 * HD * 16 + 4 * grp;
+        uint16_t *so = s0 + sh * V * V + (size_t)p16 * V * 16 + 4 * grp;
         if ((c & 1) == 0)
 #pragma unroll
         for (int t = 0; t < NT; ++t) {

@@ -28,18 +28,18 @@ hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, 
 
 // Forward scan of the backward (K = V = 128 or 64): the state from init
 // (bf16 or fp32 [N, H, V, V], or NULL) through every chunk over the states
-// records srec (RecLayout<HD>: Kt, Wm in the W^T slot, the chunk decay);
-// stores per (chunk slot, head) S0 (bf16, [part of 16 columns][128 rows][16])
-// and X (fp32 [16][128]).
+// records srec (StatesRecT<V>: Kt, Wm, the chunk decay); stores per (chunk
+// slot, head) S0 of the even chunks (bf16, [part of 16 columns][V rows][16])
+// and X (bf16 [16][V]).
 hipError_t launch_bwd_fscan(const uint16_t *v, const uint8_t *srec, const int32_t *cu, int N, int T,
                             int H, int V, const void *init, int init_fp32, uint16_t *s0, uint16_t *xws,
                             hipStream_t stream);
 
 // Reverse scan of the backward (K = V = 128 or 64): the state gradient from
 // dfin (fp32 [N, H, V, V] or NULL) back through every chunk, over the
-// reverse records rrec (RecLayout<HD>, per (chunk slot, head)); writes dv,
-// dinit (fp32, if not NULL), and per (chunk slot, head) dS1 (bf16, [part of
-// 16 columns][128 rows][16]) and dX (fp32 [16][128]).
+// reverse records rrec (RecLayout<V>, per (chunk slot, head)); writes dv
+// (= dX), dinit (fp32, if not NULL), and per (chunk slot, head) dS1 of the
+// odd chunks and the last one (bf16, [part of 16 columns][V rows][16]).
 hipError_t launch_bwd_rscan(const uint16_t *dout, const uint8_t *rrec, const int32_t *cu, int N,
                             int T, int H, int V, const float *dfin, float *dinit, uint16_t *dv,
                             uint16_t *ds1, hipStream_t stream);
@@ -52,12 +52,12 @@ hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v
                          int H, int D, void *state, int state_fp32, uint16_t *out,
                          hipStream_t stream);
 
-// Backward pass (K = V = 128, or 64 on the 128-wide kernels with the
-// channels and columns from 64 on held at zero): five launches on `stream`
-// using the caller's workspace of bwd_workspace_bytes(num_slots, H) bytes
+// Backward pass (K = V = 128 or 64, each on kernels as wide as the head):
+// five launches on `stream` (one of them on a side stream, joined back)
+// using the caller's workspace of bwd_workspace_bytes(num_slots, H, K) bytes
 // (16-byte aligned).  events: NULL, or six events recorded before each
 // launch and after the last.
-size_t bwd_workspace_bytes(int64_t num_slots, int H);
+size_t bwd_workspace_bytes(int64_t num_slots, int H, int K);
 hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
                       const uint16_t *beta, float scale, const float *A_log,
                       const float *dt_bias, float lower_bound, const int32_t *cu, int N, int T,

@@ -171,14 +171,26 @@ def test_full_size_h96_sampled_heads():
     dict(B=1, T=300, H=2, seq_lens=(0, 17, 1, 200, 82), initial_state=True),
 ])
 def test_head_dim_64_matches_oracle(kw):
-    """K = V = 64 on the 128-wide kernels (channels and columns from 64 on
-    held at zero): every gradient against the oracle at K = V = 64."""
+    """K = V = 64 on the 64-wide kernels (5 KB states records, 7 KB reverse
+    records, 64 x 64 stored states; the scans in two 32-column parts): every
+    gradient against the oracle at K = V = 64."""
     inp = kda_inputs.random_small(950 + kw["T"] + kw["H"], K=64, V=64, **kw)
     N = len(kw["seq_lens"]) if "seq_lens" in kw else kw["B"]
     d_out, d_final = kda_inputs.output_grads(951 + kw["T"], kw["B"], kw["T"], kw["H"], V=64, N=N,
                                              K=64)
     out = run_bwd(to_device(inp), d_out, d_final)
     check(inp, out, d_out, d_final)
+
+
+def test_head_dim_64_one_part_scans():
+    """K = V = 64 with N x H = 144 (sequence, head) units: the scans take one
+    64-column part per unit (two scans of two parts would not fit on 256
+    compute units); one head per unit residue mod 8 of each sequence against
+    the oracle, every head checked for unwritten elements."""
+    inp = kda_inputs.random_small(931, B=2, T=150, H=72, K=64, V=64, initial_state=True)
+    d_out, d_final = kda_inputs.output_grads(932, 2, 150, 72, V=64, K=64)
+    out = run_bwd(to_device(inp), d_out, d_final)
+    check(inp, out, d_out, d_final, heads=[0, 9, 18, 27, 36, 45, 54, 71])
 
 
 def test_many_heads_sampled():

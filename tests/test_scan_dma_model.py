@@ -155,3 +155,61 @@ def test_dma_wait_ladder_wide(rec_bytes, cw, nch):
         slot = 0 if slot == depth - 1 else slot + 1
     wait(0)
     assert completed == len(issued)
+
+
+def test_lag_source_constants_match_model():
+    src = scan_source()
+    assert "constexpr bool LAG = NW > 4;" in src
+    assert "constexpr int DEPTH = RING_DEPTH<CW> + (LAG ? 1 : 0);" in src
+    assert "wait_vm_barrier<(DEPTH - 3) * UNITS>()" in src
+    assert "issue(c + DEPTH - 1, slot);" in src
+
+
+@pytest.mark.parametrize("rec_bytes", [13312])
+@pytest.mark.parametrize("nch", [0, 1, 2, 3, 4, 5, 7, 64])
+def test_dma_wait_ladder_lag(rec_bytes, nch):
+    """The backward reverse scan's protocol with eight compute waves (128
+    columns): DEPTH = RING_DEPTH + 1 slots, DEPTH-1 chunks issued before the
+    first iteration and a wait of (DEPTH-2) x UNITS for chunk 0; at the top
+    of iteration c a wait of (DEPTH-3) x UNITS leaves chunk c+1 landed; after
+    the barrier the compute waves read chunk c+1's first operands and chunk
+    c's update operands, and the DMA wave refills chunk c-1's slot with chunk
+    c-1+DEPTH."""
+    cw = 128
+    units = rec_bytes // 1024 + CS * cw * 2 // 1024
+    depth = ring_depth(cw) + 1
+    assert (depth - 2) * units <= VMCNT_MAX
+
+    issued, completed = [], 0
+    slot_of = {}
+
+    def issue(c, slot):
+        issued.extend([c] * units)
+        slot_of[c] = slot
+
+    def wait(n):
+        nonlocal completed
+        completed = max(completed, len(issued) - n)
+
+    def landed(c):
+        return all(i < completed for i, x in enumerate(issued) if x == c)
+
+    for c in range(depth - 1):
+        issue(c, c)
+    wait((depth - 2) * units)
+    assert landed(0)                 # the compute waves read chunk 0's first operands
+    slot = depth - 1
+    for c in range(nch):
+        wait((depth - 3) * units)
+        assert landed(c + 1), (nch, c)
+        # barrier: the reads of chunk c-1 (update operands) and of chunk c
+        # (first operands) are complete; now chunk c+1's first operands and
+        # chunk c's update operands are read from their slots
+        assert slot_of[c] == c % depth and slot_of[c + 1] == (c + 1) % depth
+        assert slot == (c - 1) % depth
+        holder = [x for x, s in slot_of.items() if s == slot]
+        assert all(x <= c - 1 for x in holder)
+        issue(c - 1 + depth, slot)
+        slot = 0 if slot == depth - 1 else slot + 1
+    wait(0)
+    assert completed == len(issued)
