@@ -19,6 +19,18 @@ namespace kda {
 
 namespace {
 
+// Ring slots of the backward's scans: as many as the DMA wave's vmcnt (at
+// most 63 one-kilobyte DMAs outstanding: DEPTH-1 chunks of UNITS each, or
+// DEPTH-2 with LAG) allows, at most 8.  The scans store a state every other
+// chunk, and their record and token-tile reads queue behind those stores, so
+// they run with as many chunks in flight as fit (at K = V = 64 the two scans
+// take 0.41 ms with 8 slots against 0.57 ms with 4 or 5; at 128 the depth
+// changes nothing measurable).
+template <int UNITS, bool LAG>
+constexpr int bwd_ring_depth() {
+    return 63 / UNITS + (LAG ? 2 : 1) > 8 ? 8 : 63 / UNITS + (LAG ? 2 : 1);
+}
+
 // Reverse scan of the backward pass: the state gradient dS (key channels x
 // value columns) of one (sequence, head), chunk by chunk from the last, on
 // the forward scan's structure (each compute wave one 16-column slice in
@@ -56,10 +68,10 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
     // LAG (eight compute waves, which must fit 168 registers: three waves
     // share a SIMD): the compute waves read a chunk's state-update operands
     // (scale Qt, -Kt) at the top of its own iteration instead of one chunk
-    // ahead, and the ring has one more slot, which the DMA wave refills one
-    // chunk later (chunk c-1's slot in iteration c).
+    // ahead, and the DMA wave refills a slot one chunk later (chunk c-1's
+    // slot in iteration c).
     constexpr bool LAG = NW > 4;
-    constexpr int DEPTH = RING_DEPTH<CW> + (LAG ? 1 : 0);
+    constexpr int DEPTH = bwd_ring_depth<UNITS, LAG>();
     __shared__ ScanSlot<CW, R::BYTES> ring[DEPTH];
     static_assert((DEPTH - (LAG ? 2 : 1)) * UNITS <= 63, "vmcnt holds at most 63");
 
@@ -301,7 +313,7 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
     constexpr int V_KB = CS * CW * 2 / 1024;
     constexpr int UNITS = RKB + V_KB;
     constexpr int VROW_LANES = CW * 2 / 16;
-    constexpr int DEPTH = 4;                       // (DEPTH - 1) x UNITS DMAs within vmcnt
+    constexpr int DEPTH = bwd_ring_depth<UNITS, false>();
     __shared__ ScanSlot<CW, R::BYTES> ring[DEPTH];
     static_assert((DEPTH - 1) * UNITS <= 63, "vmcnt holds at most 63");
 

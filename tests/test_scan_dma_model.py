@@ -49,8 +49,11 @@ def test_source_constants_match_model():
 def test_dma_wait_ladder(cw, nch):
     rec_kb = REC_BYTES // 1024
     v_kb = CS * cw * 2 // 1024
-    units = rec_kb + v_kb
-    depth = ring_depth(cw)
+    two_set_ladder(rec_kb + v_kb, ring_depth(cw), nch)
+
+
+def two_set_ladder(units, depth, nch):
+    """Replay of the two-operand-set protocol (see the module docstring)."""
     assert (depth - 1) * units <= VMCNT_MAX
 
     issued = []                      # chunk index of each issued load, in order
@@ -79,7 +82,7 @@ def test_dma_wait_ladder(cw, nch):
     for c in range(nch):
         wait((depth - 2) * units)    # top of iteration c
         if c + 1 < nch + depth:
-            assert landed(c + 1), (cw, nch, c)
+            assert landed(c + 1), (units, depth, nch, c)
         # barrier: the compute waves' reads of chunk c (issued in iteration
         # c-1) are complete; they now read chunk c+1
         assert c in reads_done
@@ -157,27 +160,52 @@ def test_dma_wait_ladder_wide(rec_bytes, cw, nch):
     assert completed == len(issued)
 
 
+def bwd_ring_depth(units: int, lag: bool) -> int:
+    """bwd_ring_depth<UNITS, LAG> of the backward's scans: as deep as the
+    vmcnt field allows, at most 8 slots."""
+    return min(8, VMCNT_MAX // units + (2 if lag else 1))
+
+
+# (record bytes, column-part width, LAG) of every backward scan instance:
+# the reverse scan's record is the forward layout (13 KB at K = 128, 7 KB at
+# 64), the states scan's 9 KB or 5 KB; LAG with eight compute waves.
+BWD_SCANS = [(13312, 32, False), (13312, 64, False), (13312, 128, True),
+             (7168, 32, False), (7168, 64, False),
+             (9216, 32, False), (9216, 64, False), (9216, 128, False),
+             (5120, 32, False), (5120, 64, False)]
+
+
 def test_lag_source_constants_match_model():
     src = scan_source()
     assert "constexpr bool LAG = NW > 4;" in src
-    assert "constexpr int DEPTH = RING_DEPTH<CW> + (LAG ? 1 : 0);" in src
+    assert "63 / UNITS + (LAG ? 2 : 1) > 8 ? 8 : 63 / UNITS + (LAG ? 2 : 1)" in src
+    assert "constexpr int DEPTH = bwd_ring_depth<UNITS, LAG>();" in src
+    assert "constexpr int DEPTH = bwd_ring_depth<UNITS, false>();" in src
     assert "wait_vm_barrier<(DEPTH - 3) * UNITS>()" in src
     assert "issue(c + DEPTH - 1, slot);" in src
 
 
-@pytest.mark.parametrize("rec_bytes", [13312])
+@pytest.mark.parametrize("rec_bytes,cw,lag", BWD_SCANS)
 @pytest.mark.parametrize("nch", [0, 1, 2, 3, 4, 5, 7, 64])
-def test_dma_wait_ladder_lag(rec_bytes, nch):
-    """The backward reverse scan's protocol with eight compute waves (128
-    columns): DEPTH = RING_DEPTH + 1 slots, DEPTH-1 chunks issued before the
-    first iteration and a wait of (DEPTH-2) x UNITS for chunk 0; at the top
-    of iteration c a wait of (DEPTH-3) x UNITS leaves chunk c+1 landed; after
-    the barrier the compute waves read chunk c+1's first operands and chunk
-    c's update operands, and the DMA wave refills chunk c-1's slot with chunk
-    c-1+DEPTH."""
-    cw = 128
+def test_dma_wait_ladder_bwd(rec_bytes, cw, lag, nch):
+    """The backward's scans: the two-operand-set ladder at their ring depths,
+    and the lagged one for eight compute waves."""
     units = rec_bytes // 1024 + CS * cw * 2 // 1024
-    depth = ring_depth(cw) + 1
+    depth = bwd_ring_depth(units, lag)
+    assert depth >= 4
+    if lag:
+        lag_ladder(units, depth, nch)
+    else:
+        two_set_ladder(units, depth, nch)
+
+
+def lag_ladder(units, depth, nch):
+    """The reverse scan's protocol with eight compute waves (128 columns):
+    DEPTH-1 chunks issued before the first iteration and a wait of
+    (DEPTH-2) x UNITS for chunk 0; at the top of iteration c a wait of
+    (DEPTH-3) x UNITS leaves chunk c+1 landed; after the barrier the compute
+    waves read chunk c+1's first operands and chunk c's update operands, and
+    the DMA wave refills chunk c-1's slot with chunk c-1+DEPTH."""
     assert (depth - 2) * units <= VMCNT_MAX
 
     issued, completed = [], 0
