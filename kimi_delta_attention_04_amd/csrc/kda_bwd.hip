@@ -100,18 +100,25 @@ __device__ int slot_chunk(const int32_t *cu, int N, int T, int64_t slot, int64_t
 // back, exactly.  fp32 operands enter the bf16 MFMAs as (hi, lo) pairs with
 // three products (hi hi + hi lo + lo hi), about 16 significant bits.
 // ---------------------------------------------------------------------------
+// Per key channel of head dimension KD.  20160 bytes at KD = 128, so that
+// eight one-wave workgroups (two per SIMD, as the registers allow) fit a
+// compute unit's 160 KB in 512-byte allocation units.
+template <int KD>
 struct ChunkWaveLds {
     float beta[CS];
     float daq[CS];                    // diagonal of dAqk
-    float dtb[HD];                    // dt_bias in log2 units
-    float gam[HD];                    // e^{G_last} per key channel
-    float gl[HD];                     // G_last in log2 units
-    float dgs[HD];                    // diag(dS1 S0^T) per key channel, in two parts
-    float dgs2[HD];
-    float gnb[HD];                    // chunk decay of the neighbour chunk whose state is used
+    float dtb[KD];                    // dt_bias in log2 units
+    union {                           // (one wave: program order separates the two)
+        float gnb[KD];                // the state products: chunk decay of the
+                                      // neighbour chunk whose state is used
+        float gam[KD];                // from the chunk factors on: e^{G_last} per key channel
+    };
+    float gl[KD];                     // G_last in log2 units
+    float dgs[KD];                    // diag(dS1 S0^T) per key channel, in two parts
+    float dgs2[KD];
     float tile[CS][CS + 1];           // 16 x 16 transposes
-    f32x4_t qs[HD / 16][64];          // (dO S0^T)^T and (dX S0^T)^T per state row
-    f32x4_t ks[HD / 16][64];          // tile and lane, between their two phases
+    f32x4_t qs[KD / 16][64];          // (dO S0^T)^T and (dX S0^T)^T per state row
+    f32x4_t ks[KD / 16][64];          // tile and lane, between their two phases
 };
 
 // The tile layout of Z -> the tile layout of Z^T, through the wave's LDS.
@@ -254,7 +261,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
 {
     constexpr int NKB = KD / 32;                            // channel blocks = 32-column steps
     constexpr int NT = 2 * NKB;                             // state row tiles
-    __shared__ __attribute__((aligned(16))) ChunkWaveLds L;
+    __shared__ __attribute__((aligned(16))) ChunkWaveLds<KD> L;
     const int64_t slot = blockIdx.x / (unsigned)H;
     const int h = (int)(blockIdx.x % (unsigned)H);
     const int l = threadIdx.x, tok = l & 15, grp = l >> 4;
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     // the neighbour's chunk decay (p's for an odd chunk, n's for a rebuilt dS1)
     {
         const uint8_t *gsrc = srec + (odd ? shS : shD) * SR::BYTES + SR::GAM;
-        *(u32x2_t *)&L.gnb[2 * l] = *(const u32x2_t *)(gsrc + 8 * l);
+        if (2 * l < KD) *(u32x2_t *)&L.gnb[2 * l] = *(const u32x2_t *)(gsrc + 8 * l);
     }
     f32x4_t dM = zero;
     u32x2_t wwh[NT], wwl[NT];
