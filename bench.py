@@ -266,12 +266,13 @@ def bench_backward(args, torch, kda, kda_inputs):
             "hbm_frac": path_gbs / HBM_PEAK_GBS, "stage_ms": stage,
             "stage_traffic_bytes": {k: (t["total_bytes"] if t else None) for k, t in
                                     ((k, stored_traffic(name, k, backward=True)) for k in names)},
-            # per (chunk slot, head): the two scans' records (9 KB + 13 KB at
-            # K = 128, 5 KB + 7 KB at 64), S0 and dS1 (bf16 K x V), X (bf16
-            # 16 x V), the partial sums (129 floats)
+            # per (chunk slot, head): the two scans' records (5 + 7, 9 + 13 or
+            # 17 + 26 KB at K = 64, 128, 256), S0 and dS1 (bf16 K x V), X
+            # (bf16 16 x V), the partial sums (max(K, 128) + 1 floats)
             "workspace_bytes": int(w.H * (w.tokens // BWD_CHUNK + w.num_seqs) *
-                                   ((9216 + 13312 if w.K == 128 else 5120 + 7168) +
-                                    2 * w.K * w.V * 2 + BWD_CHUNK * w.V * 2 + 129 * 4))}
+                                   ({64: 5120 + 7168, 128: 9216 + 13312, 256: 17408 + 26624}[w.K] +
+                                    2 * w.K * w.V * 2 + BWD_CHUNK * w.V * 2 +
+                                    (max(w.K, 128) + 1) * 4))}
     cpu = None
     if not args.no_cpu_baseline:
         import oracle

@@ -21,7 +21,7 @@
  * section "Limitations before you integrate"); this library also takes
  * K = V = 64 and K = V = 256 in kda_fwd, kda_fwd_scalar_gate and kda_decode.  The
  * original ships only the forward pass (same section); kda_bwd here adds
- * the gradients (K = V = 64 or 128).
+ * the gradients (K = V = 64, 128 or 256).
  *
  * Conventions shared by every entry point:
  *   - Pointers are device pointers unless stated; every tensor is dense and
@@ -213,8 +213,8 @@ kda_status_t kda_decode(const void *q, const void *k, const void *v, const void 
  *
  * (no gradient flows through the clamped branch of the gate).
  *
- * Inputs (as kda_fwd; K = V = 128 or 64, each on kernels as wide as the
- * head):
+ * Inputs (as kda_fwd; K = V = 64, 128 or 256, each on kernels as wide as
+ * the head):
  *   q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens,
  *   num_seqs, initial_state (+ dtype), B, T, H, K, V
  *   d_out          bf16 [B, T, H, V]   gradient reaching o
@@ -231,8 +231,8 @@ kda_status_t kda_decode(const void *q, const void *k, const void *v, const void 
  * the scans' records are bf16, and fp32 operands whose precision matters
  * enter as (hi, lo) bf16 pairs; elementwise work is fp32.  Every sum runs in
  * a fixed order, so the results are bitwise reproducible.  Device workspace
- * of about 91 KiB per (16-token chunk slot, head) at K = 128 (31 KiB at 64)
- * comes from the library's stream-ordered pool (the two scans' records; X of every chunk and the
+ * of about 91 KiB per (16-token chunk slot, head) at K = 128 (31 KiB at 64,
+ * 308 KiB at 256) comes from the library's stream-ordered pool (the two scans' records; X of every chunk and the
  * start state or the state gradient of every other chunk, in bf16; dX is
  * read back from dv).  The reverse scan runs on a
  * second stream the library creates once per device (non-blocking, default

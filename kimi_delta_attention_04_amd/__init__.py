@@ -306,7 +306,7 @@ def bwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, d_out, dq, dk, dv,
     """Gradients of L = <d_out, o> + <d_final_state, final_state> of the
     forward with these inputs, written into the caller's tensors.
 
-    Inputs as fwd (K = V = 128); d_out: bf16 [B, T, H, V]; d_final_state:
+    Inputs as fwd (K = V = 64, 128 or 256); d_out: bf16 [B, T, H, V]; d_final_state:
     fp32 [N, H, K, V] or None.  Outputs: dq, dk, dg bf16 [B, T, H, K]; dv
     bf16 [B, T, H, V]; dbeta bf16 [B, T, H]; dA_log fp32 [H]; ddt_bias fp32
     [H*K] or None; d_initial_state fp32 [N, H, K, V] or None.  Enqueued on

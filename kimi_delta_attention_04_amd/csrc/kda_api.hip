@@ -412,7 +412,7 @@ kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
     if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
     kda_status_t st = check_sizes(B, T, H, K, V, cu_seqlens, num_seqs);
     if (st != KDA_OK) return st;
-    if (K != kda::HD && K != 64) return KDA_ERR_UNSUPPORTED;   // K = V = 128 or 64
+    if (K != kda::HD && K != 64 && K != 2 * kda::HD) return KDA_ERR_UNSUPPORTED;   // K = V = 64, 128 or 256
     if ((st = check_gate(lower_bound)) != KDA_OK) return st;
 
     hipStream_t s = (hipStream_t)stream;

@@ -248,7 +248,7 @@ __device__ __forceinline__ void block_decay(const u32x4_t gw, const float *__res
 }
 
 template <int KD>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_chunk_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KD > 128 ? 1 : 2))) void bwd_chunk_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
     const float *__restrict__ A_log, const float *__restrict__ dt_bias, float lb, float scale,
@@ -261,6 +261,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
 {
     constexpr int NKB = KD / 32;                            // channel blocks = 32-column steps
     constexpr int NT = 2 * NKB;                             // state row tiles
+    constexpr int PD = bwd_pd_stride<KD>();                 // dt_bias partial sums per (slot, head)
     __shared__ __attribute__((aligned(16))) ChunkWaveLds<KD> L;
     const int64_t slot = blockIdx.x / (unsigned)H;
     const int h = (int)(blockIdx.x % (unsigned)H);
@@ -270,8 +271,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     int ci;
     const int len = slot_chunk(cu, N, T, slot, t0, ci, tend);
     if (len == 0) {                                         // gap slot: zero partial sums
-        part_dtb[sh * HD + l] = 0.f;
-        part_dtb[sh * HD + 64 + l] = 0.f;
+#pragma unroll
+        for (int i = 0; i < PD; i += 64) part_dtb[sh * PD + i + l] = 0.f;
         if (l == 0) part_alog[sh] = 0.f;
         return;
     }
@@ -318,7 +319,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     // the neighbour's chunk decay (p's for an odd chunk, n's for a rebuilt dS1)
     {
         const uint8_t *gsrc = srec + (odd ? shS : shD) * SR::BYTES + SR::GAM;
-        if (2 * l < KD) *(u32x2_t *)&L.gnb[2 * l] = *(const u32x2_t *)(gsrc + 8 * l);
+#pragma unroll
+        for (int c = 2 * l; c < KD; c += 128) *(u32x2_t *)&L.gnb[c] = *(const u32x2_t *)(gsrc + 4 * c);
     }
     f32x4_t dM = zero;
     u32x2_t wwh[NT], wwl[NT];
@@ -710,12 +712,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
             __builtin_amdgcn_raw_buffer_store_b128(ok, r_dk, off, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b128(og, r_dg, off, 0, 0);
         }
-        if (tok == 0) *(f32x4_t *)&part_dtb[sh * HD + c0] = *(const f32x4_t *)&pd[0];
+        if (tok == 0) *(f32x4_t *)&part_dtb[sh * PD + c0] = *(const f32x4_t *)&pd[0];
     }
     if (tok == 0) {                                         // channels past the head dimension
 #pragma unroll
-        for (int kb = NKB; kb < HD / 32; ++kb) {
-            float *o = part_dtb + sh * HD + 32 * kb + 8 * grp;
+        for (int kb = NKB; kb < PD / 32; ++kb) {
+            float *o = part_dtb + sh * PD + 32 * kb + 8 * grp;
             *(f32x4_t *)&o[0] = zero;
             *(f32x4_t *)&o[4] = zero;
         }
@@ -740,11 +742,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
 // operands; layouts change through the identity.  The decay regions cover
 // 128 channels at either head dimension (zeros past KD).
 // ---------------------------------------------------------------------------
+template <int KD>
 struct PrepWaveLds {
     float beta[CS];
-    float dtb[HD];                    // dt_bias in log2 units
-    float gam[HD];                    // e^{G_last} per key channel
-    float gl[HD];                     // G_last in log2 units
+    float dtb[KD];                    // dt_bias in log2 units
+    float gam[KD];                    // e^{G_last} per key channel
+    float gl[KD];                     // G_last in log2 units
     float tile[CS][CS + 1];           // 16 x 16 transposes
 };
 
@@ -759,7 +762,7 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(
     constexpr int NKB = KD / 32, NT = 2 * NKB;
     typedef RecLayout<KD> R;
     typedef StatesRecT<KD> SR;
-    __shared__ __attribute__((aligned(16))) PrepWaveLds L;
+    __shared__ __attribute__((aligned(16))) PrepWaveLds<KD> L;
     const int64_t slot = blockIdx.x / (unsigned)H;
     const int h = (int)(blockIdx.x % (unsigned)H);
     const int l = threadIdx.x, tok = l & 15, grp = l >> 4;
@@ -861,9 +864,12 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(
     wave_lds_sync();
     {
         const u32x2_t z2 = {0u, 0u};
-        const u32x2_t gv = 2 * l < KD ? *(const u32x2_t *)&L.gam[2 * l] : z2;
-        __builtin_nontemporal_store(gv, (u32x2_t *)(sr + SR::GAM + l * 8));
-        __builtin_nontemporal_store(gv, (u32x2_t *)(rr + R::GAM + l * 8));
+#pragma unroll
+        for (int c = 2 * l; c < SR::GAMC; c += 128) {
+            const u32x2_t gv = c < KD ? *(const u32x2_t *)&L.gam[c] : z2;
+            __builtin_nontemporal_store(gv, (u32x2_t *)(sr + SR::GAM + c * 4));
+            __builtin_nontemporal_store(gv, (u32x2_t *)(rr + R::GAM + c * 4));
+        }
     }
 
     // T = (I + diag(beta) strict_lower(Akk))^-1 as in the chunk kernel
@@ -926,13 +932,14 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(
 
 // ---------------------------------------------------------------------------
 // reduce: per head, the parameter gradients summed over chunk slots in slot
-// order (128 threads: one channel each; dA_log by a fixed tree).
+// order (PD = max(K, 128) threads: one channel each; dA_log by a fixed tree).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(HD) void bwd_reduce_kernel(
+template <int PD>
+__global__ __launch_bounds__(PD) void bwd_reduce_kernel(
     const float *__restrict__ part_alog, const float *__restrict__ part_dtb, int64_t slots,
     int H, int kd, float *__restrict__ dA_log, float *__restrict__ ddt_bias)
 {
-    __shared__ float red[HD];
+    __shared__ float red[PD];
     const int h = blockIdx.x, c = threadIdx.x;
     float s = 0.f, a = 0.f;
     // slot order, sixteen loads issued ahead of their adds
@@ -940,16 +947,16 @@ __global__ __launch_bounds__(HD) void bwd_reduce_kernel(
     for (; sl + 16 <= slots; sl += 16) {
         float pv[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pv[i] = part_dtb[((size_t)(sl + i) * H + h) * HD + c];
+        for (int i = 0; i < 16; ++i) pv[i] = part_dtb[((size_t)(sl + i) * H + h) * PD + c];
 #pragma unroll
         for (int i = 0; i < 16; ++i) s += pv[i];
     }
-    for (; sl < slots; ++sl) s += part_dtb[((size_t)sl * H + h) * HD + c];
-    for (int64_t sl = c; sl < slots; sl += HD) a += part_alog[(size_t)sl * H + h];
+    for (; sl < slots; ++sl) s += part_dtb[((size_t)sl * H + h) * PD + c];
+    for (int64_t sl = c; sl < slots; sl += PD) a += part_alog[(size_t)sl * H + h];
     if (ddt_bias && c < kd) ddt_bias[(size_t)h * kd + c] = s;
     red[c] = a;
     __syncthreads();
-    for (int o = HD / 2; o >= 1; o >>= 1) {
+    for (int o = PD / 2; o >= 1; o >>= 1) {
         if (c < o) red[c] += red[c + o];
         __syncthreads();
     }
@@ -999,18 +1006,19 @@ hipError_t side_stream(SideStream *&out) {
 
 namespace {
 // Per (chunk slot, head): the two scans' records, S0 and dS1 (bf16 KD x KD),
-// X (bf16 16 x KD), the dt_bias partial sums (128 floats at either head
-// dimension) and the A_log partial sum.
+// X (bf16 16 x KD), the dt_bias partial sums (max(KD, 128) floats) and the
+// A_log partial sum.
 template <int KD>
 constexpr size_t bwd_slot_bytes() {
     return (size_t)StatesRecT<KD>::BYTES + (size_t)RecLayout<KD>::BYTES +
-           (2 * (size_t)KD * KD + (size_t)CS * KD) * sizeof(uint16_t) + ((size_t)HD + 1) * sizeof(float);
+           (2 * (size_t)KD * KD + (size_t)CS * KD) * sizeof(uint16_t) +
+           ((size_t)bwd_pd_stride<KD>() + 1) * sizeof(float);
 }
 }  // namespace
 
 size_t bwd_workspace_bytes(int64_t num_slots, int H, int K) {
     const size_t sh = (size_t)num_slots * H;
-    return sh * (K == 64 ? bwd_slot_bytes<64>() : bwd_slot_bytes<HD>());
+    return sh * (K == 64 ? bwd_slot_bytes<64>() : K == 2 * HD ? bwd_slot_bytes<2 * HD>() : bwd_slot_bytes<HD>());
 }
 
 hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
@@ -1026,29 +1034,31 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
     // every region starts at a multiple of 256 bytes (each per-(slot, head)
     // size is one, the last region's aside)
     static_assert(RecLayout<HD>::BYTES % 256 == 0 && StatesRecT<HD>::BYTES % 256 == 0 &&
-                  RecLayout<64>::BYTES % 256 == 0 && StatesRecT<64>::BYTES % 256 == 0, "256-byte regions");
-    const bool k64 = K == 64;
-    const size_t srb = k64 ? StatesRecT<64>::BYTES : StatesRecT<HD>::BYTES;
-    const size_t rrb = k64 ? RecLayout<64>::BYTES : RecLayout<HD>::BYTES;
+                  RecLayout<64>::BYTES % 256 == 0 && StatesRecT<64>::BYTES % 256 == 0 &&
+                  RecLayout<2 * HD>::BYTES % 256 == 0 && StatesRecT<2 * HD>::BYTES % 256 == 0,
+                  "256-byte regions");
+    const bool k64 = K == 64, k256 = K == 2 * HD;
+    const size_t srb = k64 ? StatesRecT<64>::BYTES : k256 ? StatesRecT<2 * HD>::BYTES : StatesRecT<HD>::BYTES;
+    const size_t rrb = k64 ? RecLayout<64>::BYTES : k256 ? RecLayout<2 * HD>::BYTES : RecLayout<HD>::BYTES;
+    const int pd = k256 ? bwd_pd_stride<2 * HD>() : bwd_pd_stride<HD>();
     uint8_t *srec = (uint8_t *)ws;
     uint8_t *rrec = srec + sh * srb;
     uint16_t *st0 = (uint16_t *)(rrec + sh * rrb);
     uint16_t *dst1 = st0 + sh * K * K;
     uint16_t *xws = dst1 + sh * K * K;
     float *pdtb = (float *)(xws + sh * CS * K);
-    float *palog = pdtb + sh * HD;
+    float *palog = pdtb + sh * pd;
     const dim3 chunks((unsigned)sh);
     hipError_t e = hipSuccess;
     auto mark = [&](int i) {
         if (events && events[i] && e == hipSuccess) e = hipEventRecord(events[i], stream);
     };
     mark(0);
-    if (k64)
-        hipLaunchKernelGGL(bwd_prep_kernel<64>, chunks, dim3(64), 0, stream,
-                           q, k, g, beta, A_log, dt_bias, lower_bound, scale, cu, N, T, H, srec, rrec);
-    else
-        hipLaunchKernelGGL(bwd_prep_kernel<HD>, chunks, dim3(64), 0, stream,
-                           q, k, g, beta, A_log, dt_bias, lower_bound, scale, cu, N, T, H, srec, rrec);
+#define KDA_BWD_PREP(KD_)                                                                     \
+    hipLaunchKernelGGL(bwd_prep_kernel<KD_>, chunks, dim3(64), 0, stream,                     \
+                       q, k, g, beta, A_log, dt_bias, lower_bound, scale, cu, N, T, H, srec, rrec)
+    if (k64) KDA_BWD_PREP(64); else if (k256) KDA_BWD_PREP(2 * HD); else KDA_BWD_PREP(HD);
+#undef KDA_BWD_PREP
     mark(1);
     // The reverse scan needs only the prep kernel's records and dO, not the
     // states scan's output: it runs on the device's side stream, forked after
@@ -1073,11 +1083,15 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
     hipLaunchKernelGGL(bwd_chunk_kernel<KD_>, chunks, dim3(64), 0, stream, q, k, g, beta, A_log, \
                        dt_bias, lower_bound, scale, dout, cu, N, T, H, st0, dst1, xws, dv, srec, rrec, dq, dk, \
                        dg, dbeta, palog, pdtb)
-    if (k64) KDA_BWD_CHUNK(64); else KDA_BWD_CHUNK(HD);
+    if (k64) KDA_BWD_CHUNK(64); else if (k256) KDA_BWD_CHUNK(2 * HD); else KDA_BWD_CHUNK(HD);
 #undef KDA_BWD_CHUNK
     mark(4);
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)H), dim3(HD), 0, stream,
-                       palog, pdtb, num_slots, H, K, dA_log, ddt_bias);
+    if (k256)
+        hipLaunchKernelGGL(bwd_reduce_kernel<2 * HD>, dim3((unsigned)H), dim3(2 * HD), 0, stream,
+                           palog, pdtb, num_slots, H, K, dA_log, ddt_bias);
+    else
+        hipLaunchKernelGGL(bwd_reduce_kernel<HD>, dim3((unsigned)H), dim3(HD), 0, stream,
+                           palog, pdtb, num_slots, H, K, dA_log, ddt_bias);
     mark(5);
     const hipError_t le = hipGetLastError();
     return e != hipSuccess ? e : le;

@@ -21,7 +21,7 @@ namespace {
 
 // Ring slots of the backward's scans: as many as the DMA wave's vmcnt (at
 // most 63 one-kilobyte DMAs outstanding: DEPTH-1 chunks of UNITS each, or
-// DEPTH-2 with LAG) allows, at most 8.  The scans store a state every other
+// DEPTH-2 when the DMA wave refills a slot one chunk late) allows, at most 8.  The scans store a state every other
 // chunk, and their record and token-tile reads queue behind those stores, so
 // they run with as many chunks in flight as fit (at K = V = 64 the two scans
 // take 0.41 ms with 8 slots against 0.57 ms with 4 or 5; at 128 the depth
@@ -70,10 +70,14 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
     // (scale Qt, -Kt) at the top of its own iteration instead of one chunk
     // ahead, and the DMA wave refills a slot one chunk later (chunk c-1's
     // slot in iteration c).
-    constexpr bool LAG = NW > 4;
-    constexpr int DEPTH = bwd_ring_depth<UNITS, LAG>();
+    // ONESET (256-wide tiles): one operand set in registers, all of chunk
+    // c's operands read at the top of iteration c, and the DMA wave refilling
+    // chunk c-1's slot, as the forward scan does at that width.
+    constexpr bool ONESET = VD > HD;
+    constexpr bool LAG = !ONESET && NW > 4;
+    constexpr int DEPTH = bwd_ring_depth<UNITS, LAG || ONESET>();
     __shared__ ScanSlot<CW, R::BYTES> ring[DEPTH];
-    static_assert((DEPTH - (LAG ? 2 : 1)) * UNITS <= 63, "vmcnt holds at most 63");
+    static_assert((DEPTH - (LAG || ONESET ? 2 : 1)) * UNITS <= 63, "vmcnt holds at most 63");
 
     const int b = blockIdx.x;
     const int u = 8 * (b / (8 * NSPLIT)) + (b & 7);
@@ -153,9 +157,12 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
         if constexpr (!LAG) load_update(slot, op);
         op.m = *(const u32x2_t *)(Rp + R::M + l * 8);
         const int gch = 32 * (cg >> 2) + 8 * grp + 4 * ((cg >> 1) & 1) + 2 * (cg & 1);
-        const u32x2_t g2 = *(const u32x2_t *)(Rp + R::GAM + gch * 4);
-        op.gm[0] = __uint_as_float(g2[0]);
-        op.gm[1] = __uint_as_float(g2[1]);
+#pragma unroll
+        for (int p = 0; p < (NKB >= 4 ? NKB / 4 : 1); ++p) {
+            const u32x2_t g2 = *(const u32x2_t *)(Rp + R::GAM + (128 * p + gch) * 4);
+            op.gm[2 * p] = __uint_as_float(g2[0]);
+            op.gm[2 * p + 1] = __uint_as_float(g2[1]);
+        }
         op.v[0] = *(const u32x2_t *)&sl.v[cg][wcol0 + 4 * grp];
     };
     u32x2_t eye;
@@ -236,7 +243,16 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
     // first iteration, and at the top of iteration c chunk c+1 has landed
     // when the DMAs issued after its own number (DEPTH-3) UNITS.
     if (dma_wave) {
-        if constexpr (LAG) {
+        if constexpr (ONESET) {
+#pragma unroll
+            for (int c = 0; c < DEPTH - 1; ++c) issue(c, c);
+            int slot = DEPTH - 1;                     // ring slot of chunk c-1
+            for (int c = 0; c < nch; ++c) {
+                wait_vm_barrier<(DEPTH - 2) * UNITS>();  // chunk c landed; slot of c-1 free
+                issue(c - 1 + DEPTH, slot);
+                slot = slot == DEPTH - 1 ? 0 : slot + 1;
+            }
+        } else if constexpr (LAG) {
 #pragma unroll
             for (int c = 0; c < DEPTH - 1; ++c) issue(c, c);
             wait_vm_barrier<(DEPTH - 2) * UNITS>();   // chunk 0 landed
@@ -260,6 +276,16 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         return;
     }
+    if constexpr (ONESET) {
+        ChunkOps<1, NKB> op;
+        int cur = 0;                                  // ring slot of chunk c
+        for (int c = 0; c < nch; ++c) {
+            lds_barrier();                            // own reads of chunk c-1 done; chunk c landed
+            load_ops(cur, op);
+            compute(c, op);
+            cur = cur == DEPTH - 1 ? 0 : cur + 1;
+        }
+    } else {
     lds_barrier();
     ChunkOps<1, NKB> opA, opB;
     load_ops(0, opA);
@@ -275,6 +301,7 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
     for (int c = 0; c < nch; c += 2) {
         step(c, opA, opB);
         if (c + 1 < nch) step(c + 1, opB, opA);
+    }
     }
     if (dinit) {
         const size_t base = ((size_t)n * H + h) * V * V;
@@ -313,9 +340,10 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
     constexpr int V_KB = CS * CW * 2 / 1024;
     constexpr int UNITS = RKB + V_KB;
     constexpr int VROW_LANES = CW * 2 / 16;
-    constexpr int DEPTH = bwd_ring_depth<UNITS, false>();
+    constexpr bool ONESET = VD > HD;                // as in rscan_kernel
+    constexpr int DEPTH = bwd_ring_depth<UNITS, ONESET>();
     __shared__ ScanSlot<CW, R::BYTES> ring[DEPTH];
-    static_assert((DEPTH - 1) * UNITS <= 63, "vmcnt holds at most 63");
+    static_assert((DEPTH - (ONESET ? 2 : 1)) * UNITS <= 63, "vmcnt holds at most 63");
 
     const int b = blockIdx.x;
     const int u = 8 * (b / (8 * NSPLIT)) + (b & 7);
@@ -378,7 +406,7 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
     };
     struct Ops {
         u32x4_t kt[NKB], wt[NKB];
-        float gm[2];
+        float gm[NKB >= 4 ? NKB / 2 : 2];
         u32x2_t v;
     };
     auto load_ops = [&](int slot, Ops &op) {
@@ -390,9 +418,12 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
             op.wt[kb] = *(const u32x4_t *)(Rp + R::WTH + (kb * 64 + l) * 16);
         }
         const int gch = 32 * (cg >> 2) + 8 * grp + 4 * ((cg >> 1) & 1) + 2 * (cg & 1);
-        const u32x2_t g2 = *(const u32x2_t *)(Rp + R::GAM + gch * 4);
-        op.gm[0] = __uint_as_float(g2[0]);
-        op.gm[1] = __uint_as_float(g2[1]);
+#pragma unroll
+        for (int p = 0; p < (NKB >= 4 ? NKB / 4 : 1); ++p) {
+            const u32x2_t g2 = *(const u32x2_t *)(Rp + R::GAM + (128 * p + gch) * 4);
+            op.gm[2 * p] = __uint_as_float(g2[0]);
+            op.gm[2 * p + 1] = __uint_as_float(g2[1]);
+        }
         op.v = *(const u32x2_t *)&sl.v[cg][wcol0 + 4 * grp];
     };
     u32x2_t eye;
@@ -465,16 +496,38 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
     };
 
     if (dma_wave) {
+        if constexpr (ONESET) {
 #pragma unroll
-        for (int c = 0; c < DEPTH; ++c) issue(c, c);
-        wait_vm_barrier<(DEPTH - 1) * UNITS>();
-        int slot = 0;
-        for (int c = 0; c < nch; ++c) {
-            wait_vm_barrier<(DEPTH - 2) * UNITS>();
-            issue(c + DEPTH, slot);
-            slot = slot == DEPTH - 1 ? 0 : slot + 1;
+            for (int c = 0; c < DEPTH - 1; ++c) issue(c, c);
+            int slot = DEPTH - 1;                     // ring slot of chunk c-1
+            for (int c = 0; c < nch; ++c) {
+                wait_vm_barrier<(DEPTH - 2) * UNITS>();  // chunk c landed; slot of c-1 free
+                issue(c - 1 + DEPTH, slot);
+                slot = slot == DEPTH - 1 ? 0 : slot + 1;
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < DEPTH; ++c) issue(c, c);
+            wait_vm_barrier<(DEPTH - 1) * UNITS>();
+            int slot = 0;
+            for (int c = 0; c < nch; ++c) {
+                wait_vm_barrier<(DEPTH - 2) * UNITS>();
+                issue(c + DEPTH, slot);
+                slot = slot == DEPTH - 1 ? 0 : slot + 1;
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        return;
+    }
+    if constexpr (ONESET) {
+        Ops op;
+        int cur = 0;                                  // ring slot of chunk c
+        for (int c = 0; c < nch; ++c) {
+            lds_barrier();                            // own reads of chunk c-1 done; chunk c landed
+            load_ops(cur, op);
+            compute(c, op);
+            cur = cur == DEPTH - 1 ? 0 : cur + 1;
+        }
         return;
     }
     lds_barrier();
@@ -505,9 +558,12 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
 int bwd_scan_width(int64_t units, int V) {
     const int64_t cus = num_cus();
     const int64_t u8 = 8 * ((units + 7) / 8);
-    for (int cw = 32; cw < V; cw *= 2)
+    // 256-wide tiles: parts of at most 64 columns (a wave's state and one
+    // operand set take about 200 registers, so two waves per SIMD at most)
+    const int widest = V > HD ? 64 : V;
+    for (int cw = 32; cw < widest; cw *= 2)
         if (2 * (V / cw) * u8 <= cus) return cw;
-    return V;
+    return widest;
 }
 
 hipError_t launch_bwd_rscan(const uint16_t *dout, const uint8_t *rrec, const int32_t *cu, int N,
@@ -523,6 +579,8 @@ hipError_t launch_bwd_rscan(const uint16_t *dout, const uint8_t *rrec, const int
                        dout, rrec, cu, N, T, H, dfin, dinit, dv, ds1)
     if (V == HD) {
         if (cw == 32) KDA_RSCAN(2, HD); else if (cw == 64) KDA_RSCAN(4, HD); else KDA_RSCAN(8, HD);
+    } else if (V == 2 * HD) {
+        if (cw == 32) KDA_RSCAN(2, 2 * HD); else KDA_RSCAN(4, 2 * HD);
     } else {
         if (cw == 32) KDA_RSCAN(2, 64); else KDA_RSCAN(4, 64);
     }
@@ -543,6 +601,8 @@ hipError_t launch_bwd_fscan(const uint16_t *v, const uint8_t *srec, const int32_
                        v, srec, cu, N, T, H, init, init_fp32, s0, xws)
     if (V == HD) {
         if (cw == 32) KDA_FSCAN(2, HD); else if (cw == 64) KDA_FSCAN(4, HD); else KDA_FSCAN(8, HD);
+    } else if (V == 2 * HD) {
+        if (cw == 32) KDA_FSCAN(2, 2 * HD); else KDA_FSCAN(4, 2 * HD);
     } else {
         if (cw == 32) KDA_FSCAN(2, 64); else KDA_FSCAN(4, 64);
     }

@@ -7,26 +7,25 @@
 namespace kda {
 
 // Intra-chunk stage over num_slots chunk slots x H heads; writes hand-off
-// records (REC_BYTES each, slot-major then head) into ws.  K = 128 or 64
-// (channels from K on computed as zeros).  scalar_gate: g is [B*T, H] and
-// dt_bias [H] (one gate value per token and head).
+// records (RecLayout<K>::BYTES each, slot-major then head) into ws.
+// K = 64, 128 or 256, the width of the record's tiles.  scalar_gate: g is
+// [B*T, H] and dt_bias [H] (one gate value per token and head).
 hipError_t launch_intra(const uint16_t *q, const uint16_t *k, const uint16_t *g,
                         const uint16_t *beta, const float *A_log, const float *dt_bias,
                         float lower_bound, const int32_t *cu, int N, int T, int H, int K,
                         int64_t num_slots, uint8_t *ws, hipStream_t stream,
                         bool scalar_gate = false);
 
-// Inter-chunk scan over N sequences x H heads.  K = V = 128 or 64 (the
-// 128 x 128 state tiles carry zeros in the rows from K on and the columns
-// from V on), or 256.  part_cols: columns of the state per workgroup (32,
-// 64 or 128, at most V); 0 = chosen from the number of (sequence, head)
-// units and compute units.
+// Inter-chunk scan over N sequences x H heads.  K = V = 64, 128 or 256, the
+// height of the state tiles.  part_cols: columns of the state per workgroup
+// (32, 64 or 128, at most V); 0 = chosen from the number of (sequence,
+// head) units and compute units.
 hipError_t launch_scan(const uint16_t *v, const uint8_t *ws, const int32_t *cu, int N, int T,
                        int H, int K, int V, float scale, const void *init, int init_fp32,
                        void *fin, int fin_fp32, uint16_t *out, hipStream_t stream,
                        int part_cols = 0);
 
-// Forward scan of the backward (K = V = 128 or 64): the state from init
+// Forward scan of the backward (K = V = 64, 128 or 256): the state from init
 // (bf16 or fp32 [N, H, V, V], or NULL) through every chunk over the states
 // records srec (StatesRecT<V>: Kt, Wm, the chunk decay); stores per (chunk
 // slot, head) S0 of the even chunks (bf16, [part of 16 columns][V rows][16])
@@ -35,7 +34,7 @@ hipError_t launch_bwd_fscan(const uint16_t *v, const uint8_t *srec, const int32_
                             int H, int V, const void *init, int init_fp32, uint16_t *s0, uint16_t *xws,
                             hipStream_t stream);
 
-// Reverse scan of the backward (K = V = 128 or 64): the state gradient from
+// Reverse scan of the backward (K = V = 64, 128 or 256): the state gradient from
 // dfin (fp32 [N, H, V, V] or NULL) back through every chunk, over the
 // reverse records rrec (RecLayout<V>, per (chunk slot, head)); writes dv
 // (= dX), dinit (fp32, if not NULL), and per (chunk slot, head) dS1 of the
@@ -52,7 +51,7 @@ hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v
                          int H, int D, void *state, int state_fp32, uint16_t *out,
                          hipStream_t stream);
 
-// Backward pass (K = V = 128 or 64, each on kernels as wide as the head):
+// Backward pass (K = V = 64, 128 or 256, each on kernels as wide as the head):
 // five launches on `stream` (one of them on a side stream, joined back)
 // using the caller's workspace of bwd_workspace_bytes(num_slots, H, K) bytes
 // (16-byte aligned).  events: NULL, or six events recorded before each

@@ -203,7 +203,8 @@ def call_bwd(lib, **over):
     (dict(dk=FAKE + 8), INVALID), (dict(dinit=FAKE + 4), INVALID), (dict(dfin=FAKE + 4), INVALID),
     (dict(ddtb=FAKE + 2), INVALID), (dict(init_dt=5), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(lb=0.5), INVALID), (dict(lb=-6.0), UNSUPPORTED),
-    (dict(K=96, V=96), UNSUPPORTED), (dict(K=256, V=256), UNSUPPORTED), (dict(V=64), UNSUPPORTED),
+    (dict(K=96, V=96), UNSUPPORTED), (dict(K=512, V=512), UNSUPPORTED), (dict(V=64), UNSUPPORTED),
+    (dict(K=256, V=128), UNSUPPORTED),
     (dict(N=2), INVALID), (dict(cu=FAKE, B=2, N=2), INVALID), (dict(H=0), INVALID),
     (dict(T=2 ** 26, H=1024), UNSUPPORTED),
 ])

@@ -55,7 +55,7 @@ def run_bwd(d, d_out, d_final, want_dtb=True, want_dinit=True):
     return o
 
 
-def compare(name, got, ref):
+def compare(name, got, ref, rel_l2=None):
     x = got.float().cpu().numpy().astype(np.float64) if isinstance(got, torch.Tensor) else got
     ref = np.asarray(ref, dtype=np.float64).reshape(x.shape)
     assert np.isfinite(x).all(), f"{name}: non-finite (unwritten) elements"
@@ -66,7 +66,8 @@ def compare(name, got, ref):
     rl2 = float(np.linalg.norm(x - ref) / np.linalg.norm(ref))
     mx = float(np.max(np.abs(x - ref)) / scale)
     print(f"{name}: rel_l2={rl2:.2e} max/scale={mx:.2e}", flush=True)
-    assert rl2 <= REL_L2 and mx <= MAX_REL, (name, rl2, mx)
+    bar = REL_L2 if rel_l2 is None else rel_l2
+    assert rl2 <= bar and mx <= max(MAX_REL, bar), (name, rl2, mx)
     return rl2
 
 
@@ -76,7 +77,7 @@ def compare(name, got, ref):
 RESIDUE_HEADS_96 = [0, 9, 18, 27, 36, 45, 54, 95]
 
 
-def check(inp, out, d_out, d_final, heads=None):
+def check(inp, out, d_out, d_final, heads=None, alog_rel_l2=None):
     # every element of every output is written (outputs were NaN-poisoned),
     # including the heads the oracle does not sample
     for key, val in out.items():
@@ -87,7 +88,7 @@ def check(inp, out, d_out, d_final, heads=None):
     for key in TOKEN_GRADS:
         got = out[key][:, :, sel]
         compare(key, got, ref[key])
-    compare("dA_log", out["dA_log"][sel], ref["dA_log"])
+    compare("dA_log", out["dA_log"][sel], ref["dA_log"], alog_rel_l2)
     if out["ddt_bias"] is not None:
         H = inp["q"].shape[2]
         got = out["ddt_bias"].reshape(H, -1)[sel].reshape(-1)
@@ -191,6 +192,39 @@ def test_head_dim_64_one_part_scans():
     d_out, d_final = kda_inputs.output_grads(932, 2, 150, 72, V=64, K=64)
     out = run_bwd(to_device(inp), d_out, d_final)
     check(inp, out, d_out, d_final, heads=[0, 9, 18, 27, 36, 45, 54, 71])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=1, T=64, H=2, initial_state=True),
+    dict(B=2, T=37, H=3),
+    dict(B=1, T=200, H=2, seq_lens=(0, 17, 1, 100, 82), initial_state=True),
+])
+def test_head_dim_256_matches_oracle(kw):
+    """K = V = 256 on the 256-wide kernels (17 KB states records, 26 KB
+    reverse records, 256 x 256 stored states; the scans in 32-column parts
+    with one operand set per wave): every gradient against the oracle.
+
+    dA_log is held to 3e-2 here instead of 5e-3: it is a sum over every
+    (token, channel) whose terms cancel by a factor of up to about 230 on
+    these inputs at K = 256 (about 30 at 128), and the bf16 records and
+    stored states put 1.9e-2 of relative error on it in an fp64 emulation of
+    the same roundings (measured on the GPU: 2.0e-2); every other gradient
+    keeps the 5e-3 bar."""
+    inp = kda_inputs.random_small(910 + kw["T"] + kw["H"], K=256, V=256, **kw)
+    N = len(kw["seq_lens"]) if "seq_lens" in kw else kw["B"]
+    d_out, d_final = kda_inputs.output_grads(911 + kw["T"], kw["B"], kw["T"], kw["H"], V=256, N=N,
+                                             K=256)
+    out = run_bwd(to_device(inp), d_out, d_final)
+    check(inp, out, d_out, d_final, alog_rel_l2=3e-2)
+
+
+def test_head_dim_256_two_part_scans():
+    """K = V = 256 with N x H = 48 units: the scans take 64-column parts (four
+    per unit); heads of every unit residue mod 8 against the oracle."""
+    inp = kda_inputs.random_small(921, B=2, T=70, H=24, K=256, V=256, initial_state=True)
+    d_out, d_final = kda_inputs.output_grads(922, 2, 70, 24, V=256, K=256)
+    out = run_bwd(to_device(inp), d_out, d_final)
+    check(inp, out, d_out, d_final, heads=[0, 1, 2, 3, 4, 5, 6, 7, 23], alog_rel_l2=3e-2)
 
 
 def test_many_heads_sampled():

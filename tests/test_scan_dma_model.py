@@ -114,16 +114,18 @@ def test_wide_source_constants_match_model():
                                           (REC_BYTES, 128)])
 @pytest.mark.parametrize("nch", [0, 1, 2, 3, 4, 5, 7, 64])
 def test_dma_wait_ladder_wide(rec_bytes, cw, nch):
+    rec_kb = rec_bytes // 1024
+    v_kb = CS * cw * 2 // 1024
+    one_set_ladder(rec_kb + v_kb, 4, nch)
+
+
+def one_set_ladder(units, depth, nch):
     """The one-operand-set protocol (256-wide tiles, and two slices per
     wave at 128): DEPTH-1 chunks issued before the first
     iteration; at the top of iteration c a wait of (DEPTH-2) x UNITS leaves
     chunk c landed; after the barrier the compute waves read chunk c (their
     reads of chunk c-1 completed before it) and the DMA wave refills chunk
     c-1's slot with chunk c-1+DEPTH."""
-    rec_kb = rec_bytes // 1024
-    v_kb = CS * cw * 2 // 1024
-    units = rec_kb + v_kb
-    depth = 4
     assert (depth - 2) * units <= VMCNT_MAX
 
     issued, completed = [], 0
@@ -146,7 +148,7 @@ def test_dma_wait_ladder_wide(rec_bytes, cw, nch):
     slot = depth - 1
     for c in range(nch):
         wait((depth - 2) * units)
-        assert landed(c), (cw, nch, c)
+        assert landed(c), (units, depth, nch, c)
         # barrier: reads of chunk c-1 are complete; the compute waves read chunk c
         reading = c
         assert slot_of[c] == c % depth
@@ -166,35 +168,43 @@ def bwd_ring_depth(units: int, lag: bool) -> int:
     return min(8, VMCNT_MAX // units + (2 if lag else 1))
 
 
-# (record bytes, column-part width, LAG) of every backward scan instance:
-# the reverse scan's record is the forward layout (13 KB at K = 128, 7 KB at
-# 64), the states scan's 9 KB or 5 KB; LAG with eight compute waves.
-BWD_SCANS = [(13312, 32, False), (13312, 64, False), (13312, 128, True),
-             (7168, 32, False), (7168, 64, False),
-             (9216, 32, False), (9216, 64, False), (9216, 128, False),
-             (5120, 32, False), (5120, 64, False)]
+# (record bytes, column-part width, protocol) of every backward scan
+# instance: the reverse scan's record is the forward layout (7, 13 or 26 KB
+# at K = 64, 128, 256), the states scan's 5, 9 or 17 KB; "lag" with eight
+# compute waves, "one" (one operand set) on the 256-wide tiles.
+BWD_SCANS = [(13312, 32, "two"), (13312, 64, "two"), (13312, 128, "lag"),
+             (7168, 32, "two"), (7168, 64, "two"),
+             (26624, 32, "one"), (26624, 64, "one"),
+             (9216, 32, "two"), (9216, 64, "two"), (9216, 128, "two"),
+             (5120, 32, "two"), (5120, 64, "two"),
+             (17408, 32, "one"), (17408, 64, "one")]
 
 
 def test_lag_source_constants_match_model():
     src = scan_source()
-    assert "constexpr bool LAG = NW > 4;" in src
+    assert "constexpr bool ONESET = VD > HD;" in src
+    assert "constexpr bool LAG = !ONESET && NW > 4;" in src
     assert "63 / UNITS + (LAG ? 2 : 1) > 8 ? 8 : 63 / UNITS + (LAG ? 2 : 1)" in src
-    assert "constexpr int DEPTH = bwd_ring_depth<UNITS, LAG>();" in src
-    assert "constexpr int DEPTH = bwd_ring_depth<UNITS, false>();" in src
+    assert "constexpr int DEPTH = bwd_ring_depth<UNITS, LAG || ONESET>();" in src
+    assert "constexpr int DEPTH = bwd_ring_depth<UNITS, ONESET>();" in src
     assert "wait_vm_barrier<(DEPTH - 3) * UNITS>()" in src
     assert "issue(c + DEPTH - 1, slot);" in src
+    assert "issue(c - 1 + DEPTH, slot);" in src
+    assert "const int widest = V > HD ? 64 : V;" in src
 
 
-@pytest.mark.parametrize("rec_bytes,cw,lag", BWD_SCANS)
+@pytest.mark.parametrize("rec_bytes,cw,proto", BWD_SCANS)
 @pytest.mark.parametrize("nch", [0, 1, 2, 3, 4, 5, 7, 64])
-def test_dma_wait_ladder_bwd(rec_bytes, cw, lag, nch):
+def test_dma_wait_ladder_bwd(rec_bytes, cw, proto, nch):
     """The backward's scans: the two-operand-set ladder at their ring depths,
-    and the lagged one for eight compute waves."""
+    the lagged one for eight compute waves, the one-set one at 256."""
     units = rec_bytes // 1024 + CS * cw * 2 // 1024
-    depth = bwd_ring_depth(units, lag)
+    depth = bwd_ring_depth(units, proto != "two")
     assert depth >= 4
-    if lag:
+    if proto == "lag":
         lag_ladder(units, depth, nch)
+    elif proto == "one":
+        one_set_ladder(units, depth, nch)
     else:
         two_set_ladder(units, depth, nch)
 
