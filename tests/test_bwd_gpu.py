@@ -207,9 +207,9 @@ def test_head_dim_256_matches_oracle(kw):
     dA_log is held to 3e-2 here instead of 5e-3: it is a sum over every
     (token, channel) whose terms cancel by a factor of up to about 230 on
     these inputs at K = 256 (about 30 at 128), and the bf16 records and
-    stored states put 1.9e-2 of relative error on it in an fp64 emulation of
-    the same roundings (measured on the GPU: 2.0e-2); every other gradient
-    keeps the 5e-3 bar."""
+    stored states put 1.9e-2 of relative error on it in an fp64 restatement
+    with the same roundings (tests/test_bwd_rounding_model.py; measured on
+    the GPU: 2.0e-2); every other gradient keeps the 5e-3 bar."""
     inp = kda_inputs.random_small(910 + kw["T"] + kw["H"], K=256, V=256, **kw)
     N = len(kw["seq_lens"]) if "seq_lens" in kw else kw["B"]
     d_out, d_final = kda_inputs.output_grads(911 + kw["T"], kw["B"], kw["T"], kw["H"], V=256, N=N,
