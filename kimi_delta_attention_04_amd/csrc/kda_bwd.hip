@@ -309,7 +309,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KD > 128 ? 1
     //   dWm = X dS1^T              W^T layout (A = X, B = dS1 rows)
     //   diag(dS1 S0^T)             the diagonal of S0 rows x dS1 rows^T
     // and once: dM / scale = dO X^T (tile).  The stored states are bf16 rows
-    // [16-column part][128 rows][16]; the A operand of tile t, step s is row
+    // [16-column part][KD rows][16]; the A operand of tile t, step s is row
     // chan(t, tok), columns 32s + 8grp .. +7.
     const bool odd = (ci & 1) != 0;                         // S0 from the chunk before
     const bool reb = !odd && t0 + CS < tend;                // dS1 from the chunk after

@@ -475,7 +475,7 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
             S[2 * tp + 1] = mfma_k16(t1, Xl, S[2 * tp + 1]);
         }
         // stores (off the chain): X in bf16 through the identity (lane (grp,
-        // cg): token cg, columns 4grp .. +3, [16][128] per chunk), S0 in bf16
+        // cg): token cg, columns 4grp .. +3, [16][V] per chunk), S0 in bf16
         // as rows (see rscan_kernel)
         {
             const f32x4_t xt = mfma_k16(Xb, eye, zero);
