@@ -218,6 +218,29 @@ def test_head_dim_256_matches_oracle(kw):
     check(inp, out, d_out, d_final, alog_rel_l2=3e-2)
 
 
+def test_head_dim_256_edges():
+    """K = V = 256: no d_final_state and no optional outputs; an fp32 initial
+    state without dt_bias; no tokens (the initial-state gradient is d_final)."""
+    inp = kda_inputs.random_small(941, B=1, T=50, H=2, K=256, V=256, initial_state=True)
+    d_out, _ = kda_inputs.output_grads(942, 1, 50, 2, V=256, K=256, final=False)
+    out = run_bwd(to_device(inp), d_out, None, want_dtb=False, want_dinit=False)
+    check(inp, out, d_out, None, alog_rel_l2=3e-2)
+
+    inp = kda_inputs.random_small(943, B=2, T=40, H=2, K=256, V=256, initial_state=True)
+    inp["initial_state"] = inp["initial_state"].float() * 3.0
+    inp["dt_bias"] = None
+    d_out, d_final = kda_inputs.output_grads(944, 2, 40, 2, V=256, K=256)
+    out = run_bwd(to_device(inp), d_out, d_final)
+    check(inp, out, d_out, d_final, alog_rel_l2=3e-2)
+
+    inp = kda_inputs.random_small(945, B=1, T=0, H=2, K=256, V=256, initial_state=True)
+    d_out, d_final = kda_inputs.output_grads(946, 1, 0, 2, V=256, K=256)
+    out = run_bwd(to_device(inp), d_out, d_final)
+    assert torch.equal(out["dA_log"].cpu(), torch.zeros(2))
+    assert torch.equal(out["ddt_bias"].cpu(), torch.zeros(2 * 256))
+    assert torch.equal(out["d_initial_state"].cpu(), d_final)
+
+
 def test_head_dim_256_two_part_scans():
     """K = V = 256 with N x H = 48 units: the scans take 64-column parts (four
     per unit); heads of every unit residue mod 8 against the oracle."""
