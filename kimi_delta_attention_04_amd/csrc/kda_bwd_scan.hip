@@ -235,13 +235,16 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
         }
     };
 
-    // The two-operand-set protocol of scan_kernel (chunk c in ring slot
-    // c % DEPTH).  Not LAG: the DMA wave refills chunk c's slot in iteration
-    // c, whose operands the compute waves then hold in registers.  LAG: the
-    // compute waves still read chunk c's update operands in iteration c, so
-    // the DMA wave refills chunk c-1's slot; DEPTH-1 chunks go out before the
-    // first iteration, and at the top of iteration c chunk c+1 has landed
-    // when the DMAs issued after its own number (DEPTH-3) UNITS.
+    // Ring protocols (chunk c in ring slot c % DEPTH).  Two operand sets
+    // (the forward scan's): the compute waves read chunk c+1's operands in
+    // iteration c and the DMA wave refills chunk c's slot in iteration c.
+    // LAG: as that, but the update operands of chunk c are read in iteration
+    // c, so the DMA wave refills chunk c-1's slot; DEPTH-1 chunks go out
+    // before the first iteration, and at the top of iteration c chunk c+1
+    // has landed when the DMAs issued after its own number (DEPTH-3) UNITS.
+    // ONESET: all of chunk c's operands are read in iteration c, the DMA
+    // wave refills chunk c-1's slot, and at the top of iteration c chunk c
+    // has landed when (DEPTH-2) UNITS remain.
     if (dma_wave) {
         if constexpr (ONESET) {
 #pragma unroll
@@ -286,22 +289,22 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void rscan_kernel(
             cur = cur == DEPTH - 1 ? 0 : cur + 1;
         }
     } else {
-    lds_barrier();
-    ChunkOps<1, NKB> opA, opB;
-    load_ops(0, opA);
-    int cur = 0;                                      // ring slot of chunk c
-    auto step = [&](int c, ChunkOps<1, NKB> &now, ChunkOps<1, NKB> &nxt) {
-        lds_barrier();                                // own reads of chunk c-1 done; chunk c+1 landed
-        const int next = cur == DEPTH - 1 ? 0 : cur + 1;
-        load_ops(next, nxt);
-        if constexpr (LAG) load_update(cur, now);
-        compute(c, now);
-        cur = next;
-    };
-    for (int c = 0; c < nch; c += 2) {
-        step(c, opA, opB);
-        if (c + 1 < nch) step(c + 1, opB, opA);
-    }
+        lds_barrier();
+        ChunkOps<1, NKB> opA, opB;
+        load_ops(0, opA);
+        int cur = 0;                                  // ring slot of chunk c
+        auto step = [&](int c, ChunkOps<1, NKB> &now, ChunkOps<1, NKB> &nxt) {
+            lds_barrier();                            // own reads of chunk c-1 done; chunk c+1 landed
+            const int next = cur == DEPTH - 1 ? 0 : cur + 1;
+            load_ops(next, nxt);
+            if constexpr (LAG) load_update(cur, now);
+            compute(c, now);
+            cur = next;
+        };
+        for (int c = 0; c < nch; c += 2) {
+            step(c, opA, opB);
+            if (c + 1 < nch) step(c + 1, opB, opA);
+        }
     }
     if (dinit) {
         const size_t base = ((size_t)n * H + h) * V * V;
@@ -528,21 +531,21 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
             compute(c, op);
             cur = cur == DEPTH - 1 ? 0 : cur + 1;
         }
-        return;
-    }
-    lds_barrier();
-    Ops opA, opB;
-    load_ops(0, opA);
-    int next = 1;
-    auto step = [&](int c, const Ops &cur, Ops &nxt) {
+    } else {
         lds_barrier();
-        load_ops(next, nxt);
-        compute(c, cur);
-        next = next == DEPTH - 1 ? 0 : next + 1;
-    };
-    for (int c = 0; c < nch; c += 2) {
-        step(c, opA, opB);
-        if (c + 1 < nch) step(c + 1, opB, opA);
+        Ops opA, opB;
+        load_ops(0, opA);
+        int next = 1;
+        auto step = [&](int c, const Ops &cur, Ops &nxt) {
+            lds_barrier();
+            load_ops(next, nxt);
+            compute(c, cur);
+            next = next == DEPTH - 1 ? 0 : next + 1;
+        };
+        for (int c = 0; c < nch; c += 2) {
+            step(c, opA, opB);
+            if (c + 1 < nch) step(c + 1, opB, opA);
+        }
     }
 }
 
