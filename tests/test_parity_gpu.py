@@ -167,6 +167,18 @@ def test_no_decay_alpha_one():
     check_against_oracle(inp, out, fin)
 
 
+@pytest.mark.parametrize("T,A_log", [(65536, None), (32768, -math.inf)])
+def test_long_sequence(T, A_log):
+    """4096 chunk steps with the recipe's decay, and 2048 with none at all
+    (alpha = 1: the fp32 state carries every update to the end): the state
+    accumulated over the whole sequence stays within the parity bar."""
+    inp = kda_inputs.random_small(23 + T, B=1, T=T, H=2, initial_state=True)
+    if A_log is not None:
+        inp["A_log"] = torch.full_like(inp["A_log"], A_log)
+    out, fin = run_kda(to_device(inp))
+    check_against_oracle(inp, out, fin)
+
+
 @pytest.mark.parametrize("logit", [-math.inf, math.inf])
 def test_beta_saturated(logit):
     inp = kda_inputs.random_small(17, B=1, T=60, H=2, initial_state=True)
