@@ -96,6 +96,31 @@ def test_prefill_then_decode_equals_longer_prefill(T):
     print(f"T={T}: o rel_l2={ro[0]:.3e}; state rel_l2={rf[0]:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("state_dtype", [torch.float32, torch.bfloat16])
+def test_many_steps_equal_longer_prefill(state_dtype):
+    """A 32-token prefill, then 256 decode steps one token at a time on the
+    same state in place (fp32, or bf16 rounded after every step), against
+    the oracle's prefill of all 288 tokens: every step's output and the final
+    state."""
+    P, S = 32, 256
+    full = kda_inputs.random_small(777, B=2, T=P + S, H=3, initial_state=True)
+    head = {k: v for k, v in full.items()}
+    for name in ("q", "k", "v", "g", "beta"):
+        head[name] = full[name][:, :P].contiguous()
+    _, state = run_kda(to_device(head), final_dtype=state_dtype)
+    outs = []
+    for t in range(P, P + S):
+        step = {k: v for k, v in full.items()}
+        for name in ("q", "k", "v", "g", "beta"):
+            step[name] = full[name][:, t:t + 1].contiguous()
+        outs.append(run_decode(step, state))
+    o_ref, f_ref = oracle.cref_forward(full)
+    o = np.stack([np64(x) for x in outs], axis=1)           # [B, S, H, V]
+    ro = assert_close("o", o, o_ref[:, P:])
+    rf = assert_close("state", np64(state), f_ref)
+    print(f"{state_dtype}: o rel_l2={ro[0]:.3e}; state rel_l2={rf[0]:.3e}", flush=True)
+
+
 def test_no_decay_and_saturated_beta():
     inp = single_token_inputs(7, 4, 3, torch.float32)
     inp["A_log"] = torch.full_like(inp["A_log"], -math.inf)       # alpha = 1 exactly
