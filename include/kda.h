@@ -302,6 +302,28 @@ size_t kda_workspace_size(int32_t B, int32_t T, int32_t H, int32_t num_seqs);
 size_t kda_workspace_size_hd(int32_t B, int32_t T, int32_t H, int32_t num_seqs, int32_t K);
 
 /*
+ * kda_debug_gate — test entry: runs only the gate and the in-chunk
+ * cumulative decay, through the same device code as the intra-chunk stage.
+ * For every token t of head h (chunks of 16 tokens from each sequence's
+ * start, the last one partial), with x = g[t, h, c] + dt_bias[h K + c]:
+ *   a = max(-exp(A_log[h]) softplus(x), lower_bound)          (natural log)
+ *   G[t, h, c]  = log2(e) * sum of a over the tokens of t's chunk up to t
+ *   beta_out[t, h] = sigmoid(beta[t, h])
+ * (the channel-wise decay and beta activation of "Moonshot AI Rilis
+ * FlashKDA", API paragraphs, and "Moonshot AI Open-Sources FlashKDA",
+ * section "Why KDA?"; base 2 as in section "What makes the kernel fast").
+ * g, beta, A_log, dt_bias, lower_bound, cu_seqlens, num_seqs, B, T, H, K
+ * as kda_fwd (K = 64, 128 or 256).  G: device fp32 [B, T, H, K], 16-byte
+ * aligned; beta_out: device fp32 [B, T, H].  Every token's entries are
+ * written.  Asynchronous on `stream`; errors as kda_fwd.
+ */
+kda_status_t kda_debug_gate(const void *g, const void *beta,
+                            const float *A_log, const float *dt_bias, float lower_bound,
+                            const int32_t *cu_seqlens, int32_t num_seqs,
+                            float *G, float *beta_out,
+                            int32_t B, int32_t T, int32_t H, int32_t K, void *stream);
+
+/*
  * kda_debug_intra — test entry: runs only the intra-chunk stage (gate,
  * in-chunk cumulative decay, A_kk / A_qk products, triangular inverse) and
  * writes the hand-off record of every (chunk slot, head) into the caller's

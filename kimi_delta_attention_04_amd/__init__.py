@@ -26,7 +26,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "fwd_noalloc", "fwd_scalar_gate", "decode", "bwd", "debug_intra", "debug_scan_step", "set_stage_events", "set_bwd_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
+__all__ = ["fwd", "fwd_noalloc", "fwd_scalar_gate", "decode", "bwd", "debug_gate", "debug_intra", "debug_scan_step", "set_stage_events", "set_bwd_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
            "status_string", "KDAError", "library_path", "load", "HEAD_DIM"]
 
 HEAD_DIM = 128
@@ -84,6 +84,8 @@ def load():
     lib.kda_bwd.restype = ctypes.c_int
     lib.kda_bwd.argtypes = [P, P, P, P, P, f32, P, P, f32, P, i32, P, ctypes.c_int, P, P,
                             P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
+    lib.kda_debug_gate.restype = ctypes.c_int
+    lib.kda_debug_gate.argtypes = [P, P, P, P, f32, P, i32, P, P, i32, i32, i32, i32, P]
     lib.kda_debug_intra.restype = ctypes.c_int
     lib.kda_debug_intra.argtypes = [P, P, P, P, P, P, f32, P, i32, i32, i32, i32, i32, P, P]
     lib.kda_debug_scan_step.restype = ctypes.c_int
@@ -406,6 +408,25 @@ def debug_scan_step(v, records, scale, out, initial_state=None, final_state=None
                                  int(part_cols), _stream(v.device))
     if rc != 0:
         raise KDAError(rc, "kda_debug_scan_step")
+
+
+def debug_gate(g, beta, A_log, dt_bias, lower_bound, cu_seqlens=None):
+    """Run only the gate and the in-chunk cumulative decay; returns (G, beta)
+    as fp32 device tensors [B, T, H, K] and [B, T, H]: G is the inclusive
+    cumulative base-2 log-decay of each token within its 16-token chunk,
+    beta the sigmoid of the logits."""
+    import torch
+    lib = load()
+    B, T, H, K = g.shape
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    G = torch.empty((B, T, H, K), dtype=torch.float32, device=g.device)
+    b = torch.empty((B, T, H), dtype=torch.float32, device=g.device)
+    rc = lib.kda_debug_gate(_ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias), float(lower_bound),
+                            _ptr(cu_seqlens), int(N), _ptr(G), _ptr(b), int(B), int(T), int(H),
+                            int(K), _stream(g.device))
+    if rc != 0:
+        raise KDAError(rc, "kda_debug_gate")
+    return G, b
 
 
 def debug_intra(q, k, g, beta, A_log, dt_bias, lower_bound, cu_seqlens=None):

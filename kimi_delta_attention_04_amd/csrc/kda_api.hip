@@ -310,6 +310,28 @@ kda_status_t kda_fwd_scalar_gate(const void *q, const void *k, const void *v, co
                     B, T, H, K, V, stream, true);
 }
 
+kda_status_t kda_debug_gate(const void *g, const void *beta,
+                            const float *A_log, const float *dt_bias, float lower_bound,
+                            const int32_t *cu_seqlens, int32_t num_seqs,
+                            float *G, float *beta_out,
+                            int32_t B, int32_t T, int32_t H, int32_t K, void *stream)
+{
+    const bool no_tokens = (int64_t)B * T == 0;
+    if (!A_log || (!no_tokens && (!g || !beta || !G || !beta_out))) return KDA_ERR_INVALID_ARG;
+    if (!aligned(g, 16) || !aligned(G, 16) || !aligned(beta, 2) || !aligned(beta_out, 4) ||
+        !aligned(A_log, 4) || !aligned(dt_bias, 4) || !aligned(cu_seqlens, 4))
+        return KDA_ERR_INVALID_ARG;
+    kda_status_t st = check_sizes(B, T, H, K, K, cu_seqlens, num_seqs);
+    if (st != KDA_OK) return st;
+    if ((st = check_gate(lower_bound)) != KDA_OK) return st;
+    if (no_tokens) return KDA_OK;
+    const hipError_t e =
+        kda::launch_gate((const uint16_t *)g, (const uint16_t *)beta, A_log, dt_bias, lower_bound,
+                         cu_seqlens, num_seqs, T, H, K, num_slots(B, T, num_seqs), G, beta_out,
+                         (hipStream_t)stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 kda_status_t kda_debug_intra(const void *q, const void *k, const void *g,
                              const void *beta,
                              const float *A_log, const float *dt_bias, float lower_bound,

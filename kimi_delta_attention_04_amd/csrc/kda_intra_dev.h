@@ -148,6 +148,34 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
     lo = pack2(a - bf16lo(hi), b - bf16hi(hi));
 }
 
+// beta = sigmoid(logit) of one token, the logit a bf16 word.
+__device__ __forceinline__ float beta_sigmoid(uint32_t logit) {
+    const float x = bf16f((uint16_t)logit);
+    return __builtin_amdgcn_rcpf(1.f + fast_exp2(-x * LOG2E));
+}
+
+// The gate of the lane's token on the eight channels 32kb + 8grp + i of
+// g8 (bf16 pre-activation gate values), in base 2:
+//   log2 alpha = max(-A log2(1 + 2^{x2}), lb2),  x2 = g log2 e + dt_bias log2 e,
+// zero for a token past the chunk's length (live false), then the
+// inclusive cumulative sum over the chunk's tokens, which are the 16 lanes
+// of a DPP row.  dtb_lds: the head's dt_bias in log2 units.
+__device__ __forceinline__ void gate_cumsum(float (&G)[8], const u32x4_t &g8,
+                                            const float *__restrict__ dtb_lds, int kb, int grp,
+                                            float A, float lb2, bool live) {
+    float dtb2[8];
+    *(f32x4_t *)&dtb2[0] = *(const f32x4_t *)&dtb_lds[32 * kb + 8 * grp];
+    *(f32x4_t *)&dtb2[4] = *(const f32x4_t *)&dtb_lds[32 * kb + 8 * grp + 4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float x2 = elem(g8, i) * LOG2E + dtb2[i];
+        const float u = fast_log2(1.f + fast_exp2(x2));
+        const float la = fmaxf(-A * u, lb2);
+        G[i] = live ? la : 0.f;
+    }
+    row_prefix8(G);
+}
+
 // One (chunk, head) by one wave, inputs in the token-per-lane layout.
 // FULL: all 16 rows are tokens of the sequence (no masking of the
 // cumulative decay).  SG: the Gated DeltaNet form, one gate value per
@@ -171,8 +199,7 @@ __device__ __forceinline__ void intra_compute(WaveLdsT<KT> &L, const IntraInT<KT
     const bool live = FULL || tok < len;
 
     {
-        const float x = bf16f((uint16_t)in.beta);
-        const float b = __builtin_amdgcn_rcpf(1.f + fast_exp2(-x * LOG2E));
+        const float b = beta_sigmoid(in.beta);
         if (grp == 0) L.beta[tok] = live ? b : 0.f;
     }
 
@@ -213,17 +240,7 @@ __device__ __forceinline__ void intra_compute(WaveLdsT<KT> &L, const IntraInT<KT
 #pragma unroll
             for (int i = 0; i < 8; ++i) G[i] = Gs;
         } else if (A > 0.f) {
-            float dtb2[8];
-            *(f32x4_t *)&dtb2[0] = *(const f32x4_t *)&dtb_lds[32 * kb + 8 * grp];
-            *(f32x4_t *)&dtb2[4] = *(const f32x4_t *)&dtb_lds[32 * kb + 8 * grp + 4];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float x2 = elem(in.g[kb], i) * LOG2E + dtb2[i];
-                const float u = fast_log2(1.f + fast_exp2(x2));
-                const float la = fmaxf(-A * u, lb2);
-                G[i] = live ? la : 0.f;
-            }
-            row_prefix8(G);
+            gate_cumsum(G, in.g[kb], dtb_lds, kb, grp, A, lb2, live);
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) G[i] = 0.f;

@@ -16,6 +16,14 @@ hipError_t launch_intra(const uint16_t *q, const uint16_t *k, const uint16_t *g,
                         int64_t num_slots, uint8_t *ws, hipStream_t stream,
                         bool scalar_gate = false);
 
+// The gate stage alone (a stage entry): G [B*T, H, K] fp32, the in-chunk
+// inclusive cumulative base-2 log-decay of every token, and beta
+// [B*T, H] fp32.  K = 64, 128 or 256.
+hipError_t launch_gate(const uint16_t *g, const uint16_t *beta, const float *A_log,
+                       const float *dt_bias, float lower_bound, const int32_t *cu, int N, int T,
+                       int H, int K, int64_t num_slots, float *G_out, float *beta_out,
+                       hipStream_t stream);
+
 // Inter-chunk scan over N sequences x H heads.  K = V = 64, 128 or 256, the
 // height of the state tiles.  part_cols: columns of the state per workgroup
 // (32, 64 or 128, at most V); 0 = chosen from the number of (sequence,

@@ -174,6 +174,19 @@ def test_debug_intra_validates(lib):
     assert f(ws=None) == INVALID
 
 
+def test_debug_gate_validates(lib):
+    P = ctypes.c_void_p
+    f = lambda **o: lib.kda_debug_gate(P(FAKE), P(FAKE), P(FAKE), None, o.get("lb", -5.0), None,
+                                       1, o.get("G", P(FAKE)), P(FAKE), 1, o.get("T", 16), 1,
+                                       o.get("K", 128), None)
+    assert f(K=512) == UNSUPPORTED and f(K=32) == UNSUPPORTED
+    assert f(lb=-7.0) == UNSUPPORTED
+    assert f(lb=0.5) == INVALID and f(lb=float("nan")) == INVALID
+    assert f(G=None) == INVALID
+    assert f(G=P(FAKE + 4)) == INVALID                      # G must be 16-byte aligned
+    assert f(T=0, G=None) == OK                             # no tokens: nothing to write or launch
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     import kimi_delta_attention_04_amd as mod
     monkeypatch.setattr(mod, "_lib", None)
