@@ -26,7 +26,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "fwd_noalloc", "fwd_scalar_gate", "decode", "bwd", "debug_gate", "debug_intra", "debug_scan_step", "set_stage_events", "set_bwd_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
+__all__ = ["attention", "fwd", "fwd_noalloc", "fwd_scalar_gate", "decode", "bwd", "debug_gate", "debug_intra", "debug_scan_step", "set_stage_events", "set_bwd_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
            "status_string", "KDAError", "library_path", "load", "HEAD_DIM"]
 
 HEAD_DIM = 128
@@ -352,6 +352,69 @@ def bwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, d_out, dq, dk, dv,
                      int(V), _stream(q.device))
     if rc != 0:
         raise KDAError(rc, "kda_bwd")
+
+
+_attention_fn = None
+
+
+def _attention_function():
+    """The torch.autograd.Function behind attention(), made on first use
+    (the module itself imports torch only when a call needs it)."""
+    global _attention_fn
+    if _attention_fn is not None:
+        return _attention_fn
+    import torch
+
+    class _Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, scale,
+                    lower_bound, output_final_state):
+            B, T, H, K = q.shape
+            V = v.shape[-1]
+            N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+            o = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=q.device)
+            fs = None
+            if output_final_state:
+                fs = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
+            fwd(q, k, v, g, beta, scale, o, A_log, dt_bias, lower_bound,
+                initial_state=initial_state, final_state=fs, cu_seqlens=cu_seqlens)
+            ctx.save_for_backward(q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens)
+            ctx.scale, ctx.lower_bound = scale, lower_bound
+            return o, fs
+
+        @staticmethod
+        def backward(ctx, d_o, d_fs):
+            q, k, v, g, beta, A_log, dt_bias, init, cu = ctx.saved_tensors
+            d_o = d_o.to(torch.bfloat16).contiguous()        # autograd passes zeros if unused
+            d_fs = None if d_fs is None else d_fs.to(torch.float32).contiguous()
+            dq, dk, dg = torch.empty_like(q), torch.empty_like(k), torch.empty_like(g)
+            dv, dbeta, dA = torch.empty_like(v), torch.empty_like(beta), torch.empty_like(A_log)
+            ddt = torch.empty_like(dt_bias) if dt_bias is not None else None
+            dinit = None
+            if init is not None and ctx.needs_input_grad[7]:
+                dinit = torch.empty(init.shape, dtype=torch.float32, device=q.device)
+            bwd(q, k, v, g, beta, ctx.scale, A_log, dt_bias, ctx.lower_bound, d_o, dq, dk, dv,
+                dg, dbeta, dA, ddt_bias=ddt, initial_state=init, d_final_state=d_fs,
+                d_initial_state=dinit, cu_seqlens=cu)
+            if dinit is not None:
+                dinit = dinit.to(init.dtype)
+            return dq, dk, dv, dg, dbeta, dA, ddt, dinit, None, None, None, None
+
+    _attention_fn = _Attention
+    return _attention_fn
+
+
+def attention(q, k, v, g, beta, A_log, dt_bias, lower_bound, scale=None, initial_state=None,
+              output_final_state=False, cu_seqlens=None):
+    """Differentiable KDA: returns (o, final_state), o bf16 [B, T, H, V] and
+    final_state fp32 [N, H, K, V] (None unless output_final_state), with
+    gradients through kda_bwd for q, k, v, g, beta, A_log, dt_bias and
+    initial_state.  Arguments as fwd; scale defaults to K^-1/2."""
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    return _attention_function().apply(q, k, v, g, beta, A_log, dt_bias, initial_state,
+                                       cu_seqlens, float(scale), float(lower_bound),
+                                       bool(output_final_state))
 
 
 def set_bwd_stage_events(events=None):
