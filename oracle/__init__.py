@@ -8,7 +8,9 @@ implementations of the same token recurrence:
   * cref_forward         - the C/OpenMP version in kda_ref_cpu.c (full sizes,
                            optionally a subset of heads);
 and the exact gradient of that recurrence, kda_ref_bwd.kda_backward (numpy,
-reverse-mode through the token steps; numpy_backward below).
+reverse-mode through the token steps; numpy_backward below) and its C/OpenMP
+restatement kda_ref_backward in kda_ref_cpu.c (cref_backward below, for full
+sizes).
 """
 from __future__ import annotations
 
@@ -39,6 +41,10 @@ def _load():
     lib.kda_ref_forward.argtypes = [P, P, P, P, P, P, P, ctypes.c_double, ctypes.c_double,
                                     P, i32, i32, i32, i32, i32, i32,
                                     P, i32, P, i32, P, P, i32]
+    lib.kda_ref_backward.restype = ctypes.c_int
+    lib.kda_ref_backward.argtypes = [P, P, P, P, P, P, P, ctypes.c_double, ctypes.c_double,
+                                     P, i32, i32, i32, i32, i32, i32, P, i32, P, P,
+                                     P, i32, i32, P, P, P, P, P, P, P, P, i32]
     lib.kda_ref_max_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -98,6 +104,58 @@ def cref_forward(inp: dict, heads=None, threads: int = 0, want_final: bool = Tru
     if rc != 0:
         raise RuntimeError(f"kda_ref_forward failed with {rc}")
     return out, final
+
+
+def cref_backward(inp: dict, d_out, d_final=None, heads=None, threads: int = 0,
+                  checkpoint: int = 64):
+    """Run the C gradient oracle (kda_ref_backward in kda_ref_cpu.c) on a
+    generated input dict: the same gradients as numpy_backward, in the same
+    dict layout, at full sizes.
+
+    d_out: bf16 [B, T, H, V] tensor; d_final: fp32 [N, H, K, V] tensor or
+    None.  heads: optional list of head indices; every output then holds
+    only those heads, in that order.
+    """
+    import torch
+    lib = _load()
+    q, k, v, g, beta = (inp[x] for x in ("q", "k", "v", "g", "beta"))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    cu = inp.get("cu_seqlens")
+    N = B if cu is None else int(cu.numel()) - 1
+    sel = list(range(H)) if heads is None else [int(h) for h in heads]
+    ns = len(sel)
+    bq, bk, bv, bg, bb, bdo = (_bits(x) for x in (q, k, v, g, beta, d_out))
+    A_log = inp["A_log"].to(torch.float32).contiguous().numpy()
+    dtb = inp.get("dt_bias")
+    dtb = None if dtb is None else dtb.to(torch.float32).contiguous().numpy()
+    init = inp.get("initial_state")
+    init_arr, init_dtype = None, 0
+    if init is not None:
+        if init.dtype == torch.bfloat16:
+            init_arr, init_dtype = _bits(init), 0
+        else:
+            init_arr, init_dtype = init.to(torch.float32).contiguous().numpy(), 1
+    dfin = None if d_final is None else d_final.to(torch.float32).contiguous().numpy()
+    cu_arr = None if cu is None else cu.to(torch.int32).contiguous().numpy()
+    heads_arr = np.asarray(sel, dtype=np.int32)
+    out = dict(dq=np.zeros((B, T, ns, K)), dk=np.zeros((B, T, ns, K)), dg=np.zeros((B, T, ns, K)),
+               dv=np.zeros((B, T, ns, V)), dbeta=np.zeros((B, T, ns)), dA_log=np.zeros(ns),
+               ddt_bias=np.zeros(ns * K), d_initial_state=np.zeros((N, ns, K, V)))
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+    rc = lib.kda_ref_backward(ptr(bq), ptr(bk), ptr(bv), ptr(bg), ptr(bb), ptr(A_log), ptr(dtb),
+                              float(inp["lower_bound"]), float(inp["scale"]),
+                              ptr(cu_arr), N, B, T, H, K, V, ptr(init_arr), init_dtype,
+                              ptr(bdo), ptr(dfin), ptr(heads_arr), ns, int(checkpoint),
+                              *(ptr(out[x]) for x in ("dq", "dk", "dv", "dg", "dbeta", "dA_log",
+                                                      "ddt_bias", "d_initial_state")),
+                              int(threads))
+    if rc != 0:
+        raise RuntimeError(f"kda_ref_backward failed with {rc}")
+    return out
 
 
 def numpy_forward(inp: dict):

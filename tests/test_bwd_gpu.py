@@ -1,6 +1,7 @@
 """GPU parity of the backward pass (kda_bwd through the C-ABI) against the
-fp64 gradient oracle (oracle/kda_ref_bwd.py) on the same seeded inputs and
-incoming gradients.
+fp64 gradient oracle (oracle/kda_ref_bwd.py; at full size its C restatement,
+oracle.cref_backward, on every head) on the same seeded inputs and incoming
+gradients.
 
 Bar, per gradient tensor: relative L2 error <= 5e-3 (the forward's bar) and
 max-abs error <= 2e-2 x the largest reference magnitude.  The kernels compute
@@ -71,19 +72,40 @@ def compare(name, got, ref, rel_l2=None):
     return rl2
 
 
-# Heads whose (sequence, head) units cover every residue mod 8 when H is a
-# multiple of 8 (the scans place unit u's workgroups by u mod 8), plus the
-# first and the last head.
-RESIDUE_HEADS_96 = [0, 9, 18, 27, 36, 45, 54, 95]
-
-
-def check(inp, out, d_out, d_final, heads=None, alog_rel_l2=None):
+def check(inp, out, d_out, d_final, heads=None, alog_rel_l2=None, full=False):
+    """Every gradient against the oracle: the numpy one (heads: a sample of
+    heads), or with full=True the C restatement on every head, each head's
+    token gradients and initial-state gradient then also held to the bar on
+    their own so that one wrong head cannot hide in a whole-tensor norm."""
     # every element of every output is written (outputs were NaN-poisoned),
     # including the heads the oracle does not sample
     for key, val in out.items():
         if val is not None:
             assert torch.isfinite(val).all().item(), f"{key}: non-finite (unwritten) elements"
-    ref = oracle.numpy_backward(inp, d_out, d_final, heads=heads)
+    if full:
+        assert heads is None
+        ref = oracle.cref_backward(inp, d_out, d_final)
+        H = inp["q"].shape[2]
+        for key in TOKEN_GRADS + ("d_initial_state",):
+            if out[key] is None:
+                continue
+            x = out[key].float().cpu().numpy().astype(np.float64)
+            r = ref[key]
+            ax = 2 if key in TOKEN_GRADS else 1
+            worst = 0.0
+            for h in range(H):
+                xh, rh = np.take(x, h, axis=ax), np.take(r, h, axis=ax)
+                nr = np.linalg.norm(rh)
+                if nr == 0.0:
+                    assert not np.any(xh), (key, h)
+                    continue
+                rl2 = float(np.linalg.norm(xh - rh) / nr)
+                mx = float(np.max(np.abs(xh - rh)) / np.max(np.abs(rh)))
+                assert rl2 <= REL_L2 and mx <= MAX_REL, (key, h, rl2, mx)
+                worst = max(worst, rl2)
+            print(f"{key}: worst head rel_l2={worst:.2e}", flush=True)
+    else:
+        ref = oracle.numpy_backward(inp, d_out, d_final, heads=heads)
     sel = slice(None) if heads is None else heads
     for key in TOKEN_GRADS:
         got = out[key][:, :, sel]
@@ -157,13 +179,23 @@ def test_deterministic_bitwise():
 
 
 @pytest.mark.slow
-def test_full_size_h96_sampled_heads():
-    """Eight heads, one per unit residue mod 8, against the oracle; every
-    head checked for unwritten elements."""
+def test_full_size_h96_all_heads():
+    """T = 8192, H = 96 in the benchmark's launch configuration: every head's
+    gradients against the C gradient oracle."""
     inp = kda_inputs.random_small(961, B=1, T=8192, H=96, initial_state=True)
     d_out, d_final = kda_inputs.output_grads(962, 1, 8192, 96)
     out = run_bwd(to_device(inp), d_out, d_final)
-    check(inp, out, d_out, d_final, heads=RESIDUE_HEADS_96)
+    check(inp, out, d_out, d_final, full=True)
+
+
+@pytest.mark.slow
+def test_full_size_head_dim_64_all_heads():
+    """T = 8192, H = 96 at K = V = 64 (the 64-wide kernels, as the benchmark
+    runs them): every head's gradients against the C gradient oracle."""
+    inp = kda_inputs.random_small(963, B=1, T=8192, H=96, K=64, V=64, initial_state=True)
+    d_out, d_final = kda_inputs.output_grads(964, 1, 8192, 96, V=64, K=64)
+    out = run_bwd(to_device(inp), d_out, d_final)
+    check(inp, out, d_out, d_final, full=True)
 
 
 @pytest.mark.parametrize("kw", [
@@ -263,14 +295,14 @@ def test_many_heads_sampled():
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["varlen_mixed12_H96", "varlen_uniform_8x1024_H96"])
-def test_full_size_varlen_sampled_heads(name):
-    """The benchmark's varlen workloads at full size (8192 tokens, 96 heads),
-    every gradient of the sampled heads against the oracle."""
+def test_full_size_varlen_all_heads(name):
+    """The benchmark's varlen workloads at full size (8192 tokens, 96 heads):
+    every head's gradients against the C gradient oracle."""
     w = kda_inputs.WORKLOADS[name]
     inp = kda_inputs.generate(w)
     d_out, d_final = kda_inputs.output_grads(w.seed + 1, w.B, w.T, w.H, N=w.num_seqs)
     out = run_bwd(to_device(inp), d_out, d_final)
-    check(inp, out, d_out, d_final, heads=RESIDUE_HEADS_96)
+    check(inp, out, d_out, d_final, full=True)
 
 
 def test_two_part_scans():

@@ -148,3 +148,47 @@ def test_head_subset_matches_full():
     np.testing.assert_array_equal(sub["ddt_bias"].reshape(2, 8),
                                   full["ddt_bias"].reshape(3, 8)[[2, 0]])
     np.testing.assert_array_equal(sub["d_initial_state"], full["d_initial_state"][:, [2, 0]])
+
+
+@pytest.mark.parametrize("case", [
+    dict(kw=dict(B=1, T=300, H=2, seq_lens=(0, 17, 1, 200, 82), initial_state=True)),
+    dict(kw=dict(B=2, T=70, H=3, initial_state=True), fp32_init=True, no_dtb=True, no_final=True),
+    dict(kw=dict(B=1, T=48, H=2, initial_state=True, lower_bound=-5.4), gate_shift=4.0),
+    dict(kw=dict(B=1, T=90, H=4, initial_state=True), heads=[3, 1]),
+    dict(kw=dict(B=1, T=40, H=2, K=64, V=64, initial_state=True)),
+    dict(kw=dict(B=1, T=20, H=1, K=256, V=256, initial_state=True)),
+    dict(kw=dict(B=1, T=0, H=2, initial_state=True)),
+])
+def test_c_gradient_oracle_matches_numpy(case):
+    """The C restatement of the gradient oracle (cref_backward, for full
+    sizes) gives the numpy oracle's gradients, which the tests above pin by
+    finite differences, to rounding order: ragged varlen with empty and
+    one-token sequences, fp32 initial state without dt_bias or d_final, gates
+    clamped at the lowest lower bound, a head subset in a given order, head
+    dimensions 64 and 256, and no tokens."""
+    kw = case["kw"]
+    inp = kda_inputs.random_small(1300 + kw["T"] + kw["H"], **kw)
+    if case.get("fp32_init"):
+        inp["initial_state"] = inp["initial_state"].float() * 2.0
+    if case.get("no_dtb"):
+        inp["dt_bias"] = None
+    if case.get("gate_shift"):
+        inp["g"] = (inp["g"].float() + case["gate_shift"]).to(torch.bfloat16)
+    N = len(kw["seq_lens"]) if "seq_lens" in kw else kw["B"]
+    K = kw.get("K", 128)
+    d_out, d_final = kda_inputs.output_grads(1301 + kw["T"], kw["B"], kw["T"], kw["H"], V=K, N=N,
+                                             K=K)
+    if case.get("no_final"):
+        d_final = None
+    heads = case.get("heads")
+    ref = oracle.numpy_backward(inp, d_out, d_final, heads=heads)
+    got = oracle.cref_backward(inp, d_out, d_final, heads=heads, threads=4)
+    for key, r in ref.items():
+        r = np.asarray(r)
+        x = got[key]
+        assert x.shape == r.shape, key
+        nr = np.linalg.norm(r)
+        if nr == 0.0:
+            assert not np.any(x), key
+            continue
+        assert np.linalg.norm(x - r) / nr < 1e-11, (key, np.linalg.norm(x - r) / nr)
