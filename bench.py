@@ -276,15 +276,17 @@ def bench_backward(args, torch, kda, kda_inputs):
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        heads = list(range(min(2, w.H)))
-        log(f"[bench] gradient oracle CPU baseline on heads {heads}")
+        # every head at K <= 128 (about 10 s on 16 threads at 128), a quarter
+        # of them at 256 (four times the work per head)
+        heads = list(range(w.H if w.K <= 128 else max(1, w.H // 4)))
+        log(f"[bench] gradient oracle CPU baseline on heads 0..{heads[-1]}")
         t0 = time.perf_counter()
-        oracle.numpy_backward(inp, d_out, d_final, heads=heads)
+        oracle.cref_backward(inp, d_out, d_final, heads=heads)
         dt = time.perf_counter() - t0
-        cpu = {"value": w.tokens / (dt * w.H / len(heads)), "unit": "tokens/s", "cores": 1,
-               "kind": "oracle",
+        cpu = {"value": w.tokens / (dt * w.H / len(heads)), "unit": "tokens/s",
+               "cores": oracle.max_threads(), "cpu_model": cpu_model(), "kind": "oracle",
                "sample": f"{w.name}: heads {heads[0]}..{heads[-1]} of {w.H}, all {w.tokens} "
-                         f"tokens, fp64 numpy reverse-mode token recurrence, {dt:.2f} s wall"}
+                         f"tokens, fp64 C/OpenMP reverse-mode token recurrence, {dt:.2f} s wall"}
     rec = {"metric": f"KDA bwd tokens/s @T={w.T},H={w.H},D={w.K} (gradients of every input)",
            "value": w.tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
