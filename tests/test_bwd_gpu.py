@@ -75,8 +75,12 @@ def compare(name, got, ref, rel_l2=None):
 def check(inp, out, d_out, d_final, heads=None, alog_rel_l2=None, full=False):
     """Every gradient against the oracle: the numpy one (heads: a sample of
     heads), or with full=True the C restatement on every head, each head's
-    token gradients and initial-state gradient then also held to the bar on
-    their own so that one wrong head cannot hide in a whole-tensor norm."""
+    slice of the token gradients and the initial-state gradient then also
+    held to the bar on its own, so that one wrong head cannot hide in a
+    whole-tensor norm.  The per-head check covers slices of at least 4096
+    elements: dbeta of a short sequence holds a few hundred values per head,
+    and its bf16 rounding noise alone comes near the bar there (the
+    whole-tensor bar still applies to it)."""
     # every element of every output is written (outputs were NaN-poisoned),
     # including the heads the oracle does not sample
     for key, val in out.items():
@@ -92,9 +96,11 @@ def check(inp, out, d_out, d_final, heads=None, alog_rel_l2=None, full=False):
             x = out[key].float().cpu().numpy().astype(np.float64)
             r = ref[key]
             ax = 2 if key in TOKEN_GRADS else 1
-            worst = 0.0
+            worst = None
             for h in range(H):
                 xh, rh = np.take(x, h, axis=ax), np.take(r, h, axis=ax)
+                if rh.size < 4096:
+                    break
                 nr = np.linalg.norm(rh)
                 if nr == 0.0:
                     assert not np.any(xh), (key, h)
@@ -102,8 +108,9 @@ def check(inp, out, d_out, d_final, heads=None, alog_rel_l2=None, full=False):
                 rl2 = float(np.linalg.norm(xh - rh) / nr)
                 mx = float(np.max(np.abs(xh - rh)) / np.max(np.abs(rh)))
                 assert rl2 <= REL_L2 and mx <= MAX_REL, (key, h, rl2, mx)
-                worst = max(worst, rl2)
-            print(f"{key}: worst head rel_l2={worst:.2e}", flush=True)
+                worst = rl2 if worst is None else max(worst, rl2)
+            if worst is not None:
+                print(f"{key}: worst head rel_l2={worst:.2e}", flush=True)
     else:
         ref = oracle.numpy_backward(inp, d_out, d_final, heads=heads)
     sel = slice(None) if heads is None else heads
@@ -189,6 +196,18 @@ def test_full_size_h96_all_heads():
 
 
 @pytest.mark.slow
+def test_full_size_head_dim_256_all_heads():
+    """T = 8192, H = 96 at K = V = 256 (the 256-wide kernels, as the
+    benchmark runs them): every head's gradients against the C gradient
+    oracle, dA_log to its 3e-2 bar at this width (see
+    test_head_dim_256_matches_oracle)."""
+    inp = kda_inputs.random_small(965, B=1, T=8192, H=96, K=256, V=256, initial_state=True)
+    d_out, d_final = kda_inputs.output_grads(966, 1, 8192, 96, V=256, K=256)
+    out = run_bwd(to_device(inp), d_out, d_final)
+    check(inp, out, d_out, d_final, alog_rel_l2=3e-2, full=True)
+
+
+@pytest.mark.slow
 def test_full_size_head_dim_64_all_heads():
     """T = 8192, H = 96 at K = V = 64 (the 64-wide kernels, as the benchmark
     runs them): every head's gradients against the C gradient oracle."""
@@ -218,12 +237,11 @@ def test_head_dim_64_matches_oracle(kw):
 def test_head_dim_64_one_part_scans():
     """K = V = 64 with N x H = 144 (sequence, head) units: the scans take one
     64-column part per unit (two scans of two parts would not fit on 256
-    compute units); one head per unit residue mod 8 of each sequence against
-    the oracle, every head checked for unwritten elements."""
+    compute units); every head against the oracle."""
     inp = kda_inputs.random_small(931, B=2, T=150, H=72, K=64, V=64, initial_state=True)
     d_out, d_final = kda_inputs.output_grads(932, 2, 150, 72, V=64, K=64)
     out = run_bwd(to_device(inp), d_out, d_final)
-    check(inp, out, d_out, d_final, heads=[0, 9, 18, 27, 36, 45, 54, 71])
+    check(inp, out, d_out, d_final, full=True)
 
 
 @pytest.mark.parametrize("kw", [
@@ -275,14 +293,14 @@ def test_head_dim_256_edges():
 
 def test_head_dim_256_two_part_scans():
     """K = V = 256 with N x H = 48 units: the scans take 64-column parts (four
-    per unit); heads of every unit residue mod 8 against the oracle."""
+    per unit); every head against the oracle."""
     inp = kda_inputs.random_small(921, B=2, T=70, H=24, K=256, V=256, initial_state=True)
     d_out, d_final = kda_inputs.output_grads(922, 2, 70, 24, V=256, K=256)
     out = run_bwd(to_device(inp), d_out, d_final)
-    check(inp, out, d_out, d_final, heads=[0, 1, 2, 3, 4, 5, 6, 7, 23], alog_rel_l2=3e-2)
+    check(inp, out, d_out, d_final, alog_rel_l2=3e-2, full=True)
 
 
-def test_many_heads_sampled():
+def test_many_heads():
     """N x H = 80 (sequence, head) units: ten groups of eight in the scans'
     XCD-aware block mapping; the two scans run side by side with one
     128-column part per unit (two scans of two parts would not fit on 256
@@ -290,7 +308,7 @@ def test_many_heads_sampled():
     inp = kda_inputs.random_small(971, B=2, T=100, H=40, initial_state=True)
     d_out, d_final = kda_inputs.output_grads(972, 2, 100, 40)
     out = run_bwd(to_device(inp), d_out, d_final)
-    check(inp, out, d_out, d_final, heads=[0, 17, 39])
+    check(inp, out, d_out, d_final, full=True)
 
 
 @pytest.mark.slow
@@ -312,7 +330,7 @@ def test_two_part_scans():
     inp = kda_inputs.random_small(991, B=2, T=50, H=24, initial_state=True)
     d_out, d_final = kda_inputs.output_grads(992, 2, 50, 24)
     out = run_bwd(to_device(inp), d_out, d_final)
-    check(inp, out, d_out, d_final, heads=[0, 9, 23])
+    check(inp, out, d_out, d_final, full=True)
 
 
 def test_many_units_with_empty_sequences():
@@ -323,4 +341,4 @@ def test_many_units_with_empty_sequences():
     inp = kda_inputs.random_small(981, B=1, T=sum(lens), H=40, seq_lens=lens, initial_state=True)
     d_out, d_final = kda_inputs.output_grads(982, 1, sum(lens), 40, N=len(lens))
     out = run_bwd(to_device(inp), d_out, d_final)
-    check(inp, out, d_out, d_final, heads=[0, 21, 39])
+    check(inp, out, d_out, d_final, full=True)
