@@ -561,8 +561,10 @@ __global__ __launch_bounds__(64 * (NW + 1), NW > 4 ? 1 : 2) void fscan_kernel(
 int bwd_scan_width(int64_t units, int V) {
     const int64_t cus = num_cus();
     const int64_t u8 = 8 * ((units + 7) / 8);
-    // 256-wide tiles: parts of at most 64 columns (a wave's state and one
-    // operand set take about 200 registers, so two waves per SIMD at most)
+    // 256-wide tiles: parts of at most 64 columns.  128-column parts (eight
+    // compute waves of 152-161 registers) measure the same at T = 8192,
+    // H = 96 (6.60 ms per backward step): there the two scans' workgroups
+    // outnumber the compute units at either width.
     const int widest = V > HD ? 64 : V;
     for (int cw = 32; cw < widest; cw *= 2)
         if (2 * (V / cw) * u8 <= cus) return cw;
