@@ -251,6 +251,35 @@ kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
                      float *dA_log, float *ddt_bias, float *d_initial_state,
                      int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, void *stream);
 
+/*
+ * kda_bwd_scalar_gate — the backward of kda_fwd_scalar_gate (the Gated
+ * DeltaNet form: one gate value per token and head for all key channels,
+ * "Moonshot AI Open-Sources FlashKDA", section "Why KDA?").  That forward is
+ * the channel-wise one with every channel's gate input equal, so this runs
+ * kda_bwd on the gate and dt_bias broadcast over the channels and returns
+ * the gate's and dt_bias's gradients summed over them (fp32 sums of the
+ * channel-wise bf16 gate gradients, in channel order).
+ *
+ * Arguments as kda_bwd except:
+ *   g         bf16 [B, T, H]   one pre-activation gate value per token, head
+ *   dt_bias   fp32 [H] or NULL
+ *   dg        bf16 [B, T, H]   (output)
+ *   ddt_bias  fp32 [H] or NULL (output)
+ * It takes, besides kda_bwd's workspace, 4 B T H K bytes (the broadcast
+ * gate and its channel-wise gradient) and 8 H K bytes from the same pool,
+ * stream-ordered.  Errors as kda_bwd.
+ */
+kda_status_t kda_bwd_scalar_gate(const void *q, const void *k, const void *v, const void *g,
+                                 const void *beta, float scale,
+                                 const float *A_log, const float *dt_bias, float lower_bound,
+                                 const int32_t *cu_seqlens, int32_t num_seqs,
+                                 const void *initial_state, kda_dtype_t initial_state_dtype,
+                                 const void *d_out, const float *d_final_state,
+                                 void *dq, void *dk, void *dv, void *dg, void *dbeta,
+                                 float *dA_log, float *ddt_bias, float *d_initial_state,
+                                 int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                 void *stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *kda_status_string(kda_status_t status);
 

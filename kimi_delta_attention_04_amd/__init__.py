@@ -26,7 +26,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["attention", "fwd", "fwd_noalloc", "fwd_scalar_gate", "decode", "bwd", "debug_gate", "debug_intra", "debug_scan_step", "set_stage_events", "set_bwd_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
+__all__ = ["attention", "fwd", "fwd_noalloc", "fwd_scalar_gate", "decode", "bwd", "bwd_scalar_gate", "debug_gate", "debug_intra", "debug_scan_step", "set_stage_events", "set_bwd_stage_events", "workspace_size", "lower_bound_min", "chunk_size",
            "status_string", "KDAError", "library_path", "load", "HEAD_DIM"]
 
 HEAD_DIM = 128
@@ -84,6 +84,8 @@ def load():
     lib.kda_bwd.restype = ctypes.c_int
     lib.kda_bwd.argtypes = [P, P, P, P, P, f32, P, P, f32, P, i32, P, ctypes.c_int, P, P,
                             P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
+    lib.kda_bwd_scalar_gate.restype = ctypes.c_int
+    lib.kda_bwd_scalar_gate.argtypes = lib.kda_bwd.argtypes
     lib.kda_debug_gate.restype = ctypes.c_int
     lib.kda_debug_gate.argtypes = [P, P, P, P, f32, P, i32, P, P, i32, i32, i32, i32, P]
     lib.kda_debug_intra.restype = ctypes.c_int
@@ -302,6 +304,17 @@ def decode(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, state):
     return out
 
 
+def bwd_scalar_gate(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, d_out, dq, dk, dv,
+                    dg, dbeta, dA_log, ddt_bias=None, initial_state=None, d_final_state=None,
+                    d_initial_state=None, cu_seqlens=None):
+    """The backward of fwd_scalar_gate: as bwd, but g and dg are bf16
+    [B, T, H] (one gate value per token and head) and dt_bias, ddt_bias fp32
+    [H] or None."""
+    _bwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, d_out, dq, dk, dv, dg, dbeta,
+         dA_log, ddt_bias, initial_state, d_final_state, d_initial_state, cu_seqlens,
+         scalar_gate=True)
+
+
 def bwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, d_out, dq, dk, dv, dg, dbeta,
         dA_log, ddt_bias=None, initial_state=None, d_final_state=None, d_initial_state=None,
         cu_seqlens=None):
@@ -314,6 +327,14 @@ def bwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, d_out, dq, dk, dv,
     [H*K] or None; d_initial_state fp32 [N, H, K, V] or None.  Enqueued on
     the current stream.
     """
+    _bwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, d_out, dq, dk, dv, dg, dbeta,
+         dA_log, ddt_bias, initial_state, d_final_state, d_initial_state, cu_seqlens,
+         scalar_gate=False)
+
+
+def _bwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, d_out, dq, dk, dv, dg, dbeta,
+         dA_log, ddt_bias, initial_state, d_final_state, d_initial_state, cu_seqlens,
+         scalar_gate):
     import torch
     lib = load()
     if q.dim() != 4:
@@ -321,17 +342,18 @@ def bwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, d_out, dq, dk, dv,
     B, T, H, K = q.shape
     V = v.shape[-1]
     bf, f32 = torch.bfloat16, torch.float32
-    for t, name, shape in ((q, "q", None), (k, "k", q.shape), (g, "g", q.shape),
+    gshape = (B, T, H) if scalar_gate else q.shape
+    for t, name, shape in ((q, "q", None), (k, "k", q.shape), (g, "g", gshape),
                            (v, "v", (B, T, H, V)), (beta, "beta", (B, T, H)),
                            (d_out, "d_out", (B, T, H, V)), (dq, "dq", q.shape),
-                           (dk, "dk", q.shape), (dg, "dg", q.shape), (dv, "dv", (B, T, H, V)),
+                           (dk, "dk", q.shape), (dg, "dg", gshape), (dv, "dv", (B, T, H, V)),
                            (dbeta, "dbeta", (B, T, H))):
         _check(t, name, bf, shape)
     _check(A_log, "A_log", f32, (H,))
     _check(dA_log, "dA_log", f32, (H,))
     for t, name in ((dt_bias, "dt_bias"), (ddt_bias, "ddt_bias")):
         if t is not None:
-            _check(t, name, f32, (H * K,))
+            _check(t, name, f32, (H,) if scalar_gate else (H * K,))
     if cu_seqlens is not None:
         _check(cu_seqlens, "cu_seqlens", torch.int32)
         N = cu_seqlens.numel() - 1
@@ -344,14 +366,15 @@ def bwd(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, d_out, dq, dk, dv,
     for t, name in ((d_final_state, "d_final_state"), (d_initial_state, "d_initial_state")):
         if t is not None:
             _check(t, name, f32, (N, H, K, V))
-    rc = lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(A_log),
+    fn = lib.kda_bwd_scalar_gate if scalar_gate else lib.kda_bwd
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(A_log),
                      _ptr(dt_bias), float(lower_bound), _ptr(cu_seqlens), int(N),
                      _ptr(initial_state), init_dt, _ptr(d_out), _ptr(d_final_state),
                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dA_log),
                      _ptr(ddt_bias), _ptr(d_initial_state), int(B), int(T), int(H), int(K),
                      int(V), _stream(q.device))
     if rc != 0:
-        raise KDAError(rc, "kda_bwd")
+        raise KDAError(rc, "kda_bwd_scalar_gate" if scalar_gate else "kda_bwd")
 
 
 _attention_fn = None

@@ -3,6 +3,7 @@
 #include <stdlib.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include <hip/hip_runtime.h>
@@ -276,6 +277,17 @@ kda_status_t fwd_impl(const void *q, const void *k, const void *v, const void *g
     return KDA_OK;
 }
 
+
+kda_status_t bwd_launch_all(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, float scale, const float *A_log,
+                            const float *dt_bias, float lower_bound, const int32_t *cu_seqlens,
+                            int32_t num_seqs, const void *initial_state,
+                            kda_dtype_t initial_state_dtype, const void *d_out,
+                            const float *d_final_state, void *dq, void *dk, void *dv, void *dg,
+                            void *dbeta, float *dA_log, float *ddt_bias, float *d_initial_state,
+                            int32_t B, int32_t T, int32_t H, int32_t K, void *stream,
+                            uint16_t *dg_scalar);
+
 }  // namespace
 
 extern "C" {
@@ -436,7 +448,29 @@ kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
     if (st != KDA_OK) return st;
     if (K != kda::HD && K != 64 && K != 2 * kda::HD) return KDA_ERR_UNSUPPORTED;   // K = V = 64, 128 or 256
     if ((st = check_gate(lower_bound)) != KDA_OK) return st;
+    return bwd_launch_all(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens,
+                          num_seqs, initial_state, initial_state_dtype, d_out, d_final_state, dq,
+                          dk, dv, dg, dbeta, dA_log, ddt_bias, d_initial_state, B, T, H, K, stream,
+                          nullptr);
+}
 
+}  // extern "C"
+
+namespace {
+
+// The backward's workspace, the optional cu_seqlens check and its launches,
+// for arguments already validated.  dg_scalar: see kda::launch_bwd.
+kda_status_t bwd_launch_all(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, float scale, const float *A_log,
+                            const float *dt_bias, float lower_bound, const int32_t *cu_seqlens,
+                            int32_t num_seqs, const void *initial_state,
+                            kda_dtype_t initial_state_dtype, const void *d_out,
+                            const float *d_final_state, void *dq, void *dk, void *dv, void *dg,
+                            void *dbeta, float *dA_log, float *ddt_bias, float *d_initial_state,
+                            int32_t B, int32_t T, int32_t H, int32_t K, void *stream,
+                            uint16_t *dg_scalar)
+{
+    kda_status_t st;
     hipStream_t s = (hipStream_t)stream;
     const int64_t slots = num_slots(B, T, num_seqs);
     const size_t bytes = kda::bwd_workspace_bytes(slots, H, K);
@@ -457,10 +491,119 @@ kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
                                    (const uint16_t *)d_out, d_final_state, (uint16_t *)dq,
                                    (uint16_t *)dk, (uint16_t *)dv, (uint16_t *)dg,
                                    (uint16_t *)dbeta, dA_log, ddt_bias, d_initial_state, ws, s,
-                                   t_bwd_events);
+                                   t_bwd_events, dg_scalar);
     hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess || ef != hipSuccess) return KDA_ERR_LAUNCH;
     return KDA_OK;
+}
+
+// The Gated DeltaNet backward around the channel-wise one: its forward is
+// the channel-wise forward with every key channel's gate input equal to the
+// token's one value (and dt_bias[h] for every channel of head h), so its
+// gradients are the channel-wise ones with the gate's and dt_bias's summed
+// over the channels (the chunk kernel sums the gate's, kda::launch_bwd's
+// dg_scalar).  gate_broadcast_kernel writes that channel-wise gate (one
+// 16-byte piece of eight channels per thread, grid-stride) and dt_bias.
+__global__ void gate_broadcast_kernel(const uint16_t *__restrict__ g, const float *__restrict__ dtb,
+                                      int64_t pieces, int K, int H, uint16_t *__restrict__ gb,
+                                      float *__restrict__ dtbb) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int per = K / 8;                                  // pieces per (token, head)
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pieces; i += stride) {
+        const uint32_t w = g[i / per];
+        const uint32_t two = w | (w << 16);
+        uint4 v;
+        v.x = v.y = v.z = v.w = two;
+        *(uint4 *)(gb + 8 * i) = v;
+    }
+    if (dtbb)
+        for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < (int64_t)H * K; j += stride)
+            dtbb[j] = dtb[j / K];
+}
+
+// ddt[h] = sum over the channels of ddtb[h, c], in channel order (fp32).
+__global__ void dtb_reduce_kernel(const float *__restrict__ ddtb, int H, int K,
+                                  float *__restrict__ ddt) {
+    for (int h = blockIdx.x * blockDim.x + threadIdx.x; h < H; h += gridDim.x * blockDim.x) {
+        float acc = 0.f;
+        for (int c = 0; c < K; ++c) acc += ddtb[(size_t)h * K + c];
+        ddt[h] = acc;
+    }
+}
+
+constexpr size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_bwd_scalar_gate(const void *q, const void *k, const void *v, const void *g,
+                                 const void *beta, float scale,
+                                 const float *A_log, const float *dt_bias, float lower_bound,
+                                 const int32_t *cu_seqlens, int32_t num_seqs,
+                                 const void *initial_state, kda_dtype_t initial_state_dtype,
+                                 const void *d_out, const float *d_final_state,
+                                 void *dq, void *dk, void *dv, void *dg, void *dbeta,
+                                 float *dA_log, float *ddt_bias, float *d_initial_state,
+                                 int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                 void *stream)
+{
+    const bool no_tokens = (int64_t)B * T == 0;
+    if (!A_log || !dA_log) return KDA_ERR_INVALID_ARG;
+    if (!no_tokens && (!q || !k || !v || !g || !beta || !d_out || !dq || !dk || !dv || !dg ||
+                       !dbeta))
+        return KDA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 2) ||
+        !aligned(d_out, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        !aligned(dg, 2) || !aligned(beta, 2) || !aligned(dbeta, 2) || !aligned(A_log, 4) ||
+        !aligned(dt_bias, 4) || !aligned(dA_log, 4) || !aligned(ddt_bias, 4) ||
+        !aligned(cu_seqlens, 4) || !aligned(initial_state, 16) ||
+        !aligned(d_final_state, 16) || !aligned(d_initial_state, 16))
+        return KDA_ERR_INVALID_ARG;
+    if (initial_state_dtype != KDA_DTYPE_BF16 && initial_state_dtype != KDA_DTYPE_FP32)
+        return KDA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    kda_status_t st = check_sizes(B, T, H, K, V, cu_seqlens, num_seqs);
+    if (st != KDA_OK) return st;
+    if ((st = check_gate(lower_bound)) != KDA_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t rows = (int64_t)B * T * H;                // (token, head) pairs
+    const size_t gbytes = round256((size_t)rows * K * 2);
+    const size_t hbytes = round256((size_t)H * K * 4);
+    const size_t bytes = gbytes + (dt_bias ? hbytes : 0) + (ddt_bias ? hbytes : 0);
+    hipMemPool_t pool;
+    if ((st = device_pool(&pool)) != KDA_OK) return st;
+    void *buf = nullptr;
+    if (bytes > 0) {
+        if (hipMallocFromPoolAsync(&buf, bytes, pool, s) != hipSuccess || !buf) {
+            (void)hipGetLastError();
+            return KDA_ERR_OUT_OF_MEMORY;
+        }
+    }
+    uint8_t *p = (uint8_t *)buf;
+    uint16_t *gb = (uint16_t *)p;                           // the gate, broadcast
+    float *dtbb = dt_bias ? (float *)(p + gbytes) : nullptr;
+    float *ddtb = ddt_bias ? (float *)(p + gbytes + (dt_bias ? hbytes : 0)) : nullptr;
+    const unsigned blocks = (unsigned)std::min<int64_t>(4096, std::max<int64_t>(1, (rows * K / 8 + 255) / 256));
+    kda_status_t r = KDA_OK;
+    if (rows > 0 || dtbb) {
+        hipLaunchKernelGGL(gate_broadcast_kernel, dim3(blocks), dim3(256), 0, s, (const uint16_t *)g,
+                           dt_bias, rows * K / 8, K, H, gb, dtbb);
+        if (hipGetLastError() != hipSuccess) r = KDA_ERR_LAUNCH;
+    }
+    if (r == KDA_OK)
+        r = bwd_launch_all(q, k, v, gb, beta, scale, A_log, dtbb, lower_bound, cu_seqlens, num_seqs,
+                           initial_state, initial_state_dtype, d_out, d_final_state, dq, dk, dv,
+                           nullptr, dbeta, dA_log, ddtb, d_initial_state, B, T, H, K, stream,
+                           (uint16_t *)dg);
+    if (r == KDA_OK && ddtb) {
+        hipLaunchKernelGGL(dtb_reduce_kernel, dim3((unsigned)((H + 255) / 256)), dim3(256), 0, s,
+                           ddtb, H, K, ddt_bias);
+        if (hipGetLastError() != hipSuccess) r = KDA_ERR_LAUNCH;
+    }
+    if (buf && hipFreeAsync(buf, s) != hipSuccess) r = KDA_ERR_LAUNCH;
+    return r;
 }
 
 }  // extern "C"

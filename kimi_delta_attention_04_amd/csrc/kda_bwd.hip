@@ -247,7 +247,11 @@ __device__ __forceinline__ void block_decay(const u32x4_t gw, const float *__res
     }
 }
 
-template <int KD>
+// SCALAR: the Gated DeltaNet form (one gate value per token and head, g and
+// dt_bias broadcast over the channels by the caller): the gate gradient is
+// summed over the channels in fp32 and written to dgs [token, head] in bf16,
+// and the channel-wise dg is not written.
+template <int KD, bool SCALAR = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KD > 128 ? 1 : 2))) void bwd_chunk_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ g, const uint16_t *__restrict__ beta,
@@ -257,7 +261,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KD > 128 ? 1
     const uint16_t *__restrict__ xws, const uint16_t *__restrict__ dvv,
     const uint8_t *__restrict__ srec, const uint8_t *__restrict__ rrec,
     uint16_t *__restrict__ dq, uint16_t *__restrict__ dk, uint16_t *__restrict__ dg,
-    uint16_t *__restrict__ dbeta, float *__restrict__ part_alog, float *__restrict__ part_dtb)
+    uint16_t *__restrict__ dbeta, float *__restrict__ part_alog, float *__restrict__ part_dtb,
+    uint16_t *__restrict__ dgs)
 {
     constexpr int NKB = KD / 32;                            // channel blocks = 32-column steps
     constexpr int NT = 2 * NKB;                             // state row tiles
@@ -624,6 +629,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KD > 128 ? 1
     const __amdgpu_buffer_rsrc_t r_dk = make_rsrc(dk + rbase, rbytes);
     const __amdgpu_buffer_rsrc_t r_dg = make_rsrc(dg + rbase, rbytes);
     float pa = 0.f;
+    float gsum = 0.f;                                       // SCALAR: this lane's channels of dg
     u32x4_t oq, ok, og;                                     // one 16-byte row piece of each output
     u32x4_t gq, kq, qq;                                     // and of each input, block kb
 #pragma unroll
@@ -699,6 +705,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KD > 128 ? 1
             vq[j] = dQe + daq * kv[j];
             vk[j] = dKe + dKi + daq * qv[j];
             vg[j] = dx;
+            if constexpr (SCALAR) gsum += dx;
         }
         oq[2 * hh] = pack2(vq[0], vq[1]);
         oq[2 * hh + 1] = pack2(vq[2], vq[3]);
@@ -710,7 +717,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KD > 128 ? 1
             const int off = (int)((tok * rowe + c0 - 4) * 2);
             __builtin_amdgcn_raw_buffer_store_b128(oq, r_dq, off, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b128(ok, r_dk, off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(og, r_dg, off, 0, 0);
+            if constexpr (!SCALAR) __builtin_amdgcn_raw_buffer_store_b128(og, r_dg, off, 0, 0);
         }
         if (tok == 0) *(f32x4_t *)&part_dtb[sh * PD + c0] = *(const f32x4_t *)&pd[0];
     }
@@ -725,6 +732,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KD > 128 ? 1
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) pa += __shfl_xor(pa, o, 64);
     if (l == 0) part_alog[sh] = pa;
+    if constexpr (SCALAR) {
+        gsum += __shfl_xor(gsum, 16, 64);                   // the four lane groups' channels
+        gsum += __shfl_xor(gsum, 32, 64);
+        if (grp == 0 && live) dgs[(size_t)(t0 + tok) * H + h] = tobf16(gsum);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1028,7 +1040,7 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
                       const uint16_t *dout, const float *dfin, uint16_t *dq, uint16_t *dk,
                       uint16_t *dv, uint16_t *dg, uint16_t *dbeta, float *dA_log,
                       float *ddt_bias, float *dinit, void *ws, hipStream_t stream,
-                      const hipEvent_t *events)
+                      const hipEvent_t *events, uint16_t *dg_scalar)
 {
     const size_t sh = (size_t)num_slots * H;
     // every region starts at a multiple of 256 bytes (each per-(slot, head)
@@ -1079,11 +1091,15 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
         if (e == hipSuccess) e = hipStreamWaitEvent(stream, ss->join, 0);
     }
     mark(3);
-#define KDA_BWD_CHUNK(KD_)                                                                    \
-    hipLaunchKernelGGL(bwd_chunk_kernel<KD_>, chunks, dim3(64), 0, stream, q, k, g, beta, A_log, \
-                       dt_bias, lower_bound, scale, dout, cu, N, T, H, st0, dst1, xws, dv, srec, rrec, dq, dk, \
-                       dg, dbeta, palog, pdtb)
-    if (k64) KDA_BWD_CHUNK(64); else if (k256) KDA_BWD_CHUNK(2 * HD); else KDA_BWD_CHUNK(HD);
+#define KDA_BWD_CHUNK(KD_, SC_)                                                               \
+    hipLaunchKernelGGL((bwd_chunk_kernel<KD_, SC_>), chunks, dim3(64), 0, stream, q, k, g, beta, \
+                       A_log, dt_bias, lower_bound, scale, dout, cu, N, T, H, st0, dst1, xws, dv, srec, \
+                       rrec, dq, dk, dg, dbeta, palog, pdtb, dg_scalar)
+    if (dg_scalar) {
+        if (k64) KDA_BWD_CHUNK(64, true); else if (k256) KDA_BWD_CHUNK(2 * HD, true); else KDA_BWD_CHUNK(HD, true);
+    } else {
+        if (k64) KDA_BWD_CHUNK(64, false); else if (k256) KDA_BWD_CHUNK(2 * HD, false); else KDA_BWD_CHUNK(HD, false);
+    }
 #undef KDA_BWD_CHUNK
     mark(4);
     if (k256)

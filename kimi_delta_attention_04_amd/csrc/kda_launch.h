@@ -63,7 +63,10 @@ hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v
 // five launches on `stream` (one of them on a side stream, joined back)
 // using the caller's workspace of bwd_workspace_bytes(num_slots, H, K) bytes
 // (16-byte aligned).  events: NULL, or six events recorded before each
-// launch and after the last.
+// launch and after the last.  dg_scalar: the Gated DeltaNet form (g and
+// dt_bias broadcast over the channels by the caller): the gate gradient
+// summed over the channels in fp32, written there as bf16 [B*T, H]; dg is
+// then not written.
 size_t bwd_workspace_bytes(int64_t num_slots, int H, int K);
 hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
                       const uint16_t *beta, float scale, const float *A_log,
@@ -72,6 +75,6 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
                       const uint16_t *dout, const float *dfin, uint16_t *dq, uint16_t *dk,
                       uint16_t *dv, uint16_t *dg, uint16_t *dbeta, float *dA_log,
                       float *ddt_bias, float *dinit, void *ws, hipStream_t stream,
-                      const hipEvent_t *events);
+                      const hipEvent_t *events, uint16_t *dg_scalar = nullptr);
 
 }  // namespace kda

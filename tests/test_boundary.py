@@ -195,19 +195,20 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
         mod.load()
 
 
-def call_bwd(lib, **over):
+def call_bwd(lib, scalar_gate=False, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=0.088, A_log=FAKE, dt_bias=None,
              lb=-5.0, cu=None, N=1, init=None, init_dt=0, dout=FAKE, dfin=None,
              dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, dbeta=FAKE, dA_log=FAKE, ddtb=None, dinit=None,
              B=1, T=32, H=2, K=128, V=128)
     a.update(over)
     P = lambda x: None if x is None else ctypes.c_void_p(x)
-    return lib.kda_bwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]), a["scale"],
-                       P(a["A_log"]), P(a["dt_bias"]), a["lb"], P(a["cu"]), a["N"],
-                       P(a["init"]), a["init_dt"], P(a["dout"]), P(a["dfin"]),
-                       P(a["dq"]), P(a["dk"]), P(a["dv"]), P(a["dg"]), P(a["dbeta"]),
-                       P(a["dA_log"]), P(a["ddtb"]), P(a["dinit"]),
-                       a["B"], a["T"], a["H"], a["K"], a["V"], None)
+    fn = lib.kda_bwd_scalar_gate if scalar_gate else lib.kda_bwd
+    return fn(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]), a["scale"],
+              P(a["A_log"]), P(a["dt_bias"]), a["lb"], P(a["cu"]), a["N"],
+              P(a["init"]), a["init_dt"], P(a["dout"]), P(a["dfin"]),
+              P(a["dq"]), P(a["dk"]), P(a["dv"]), P(a["dg"]), P(a["dbeta"]),
+              P(a["dA_log"]), P(a["ddtb"]), P(a["dinit"]),
+              a["B"], a["T"], a["H"], a["K"], a["V"], None)
 
 
 @pytest.mark.parametrize("over,code", [
@@ -223,3 +224,12 @@ def call_bwd(lib, **over):
 ])
 def test_bwd_rejects_before_any_hip_call(lib, over, code):
     assert call_bwd(lib, **over) == code
+    # the scalar-gate backward validates the same arguments the same way
+    # (its g and dg need only 2-byte alignment)
+    assert call_bwd(lib, scalar_gate=True, **over) == code
+
+
+def test_bwd_scalar_gate_alignment(lib):
+    assert call_bwd(lib, scalar_gate=True, g=FAKE + 1) == INVALID
+    assert call_bwd(lib, scalar_gate=True, dg=FAKE + 1) == INVALID
+    assert call_bwd(lib, g=FAKE + 2) == INVALID
