@@ -25,7 +25,8 @@ the timed pass).
 
 `--scalar-gate` measures the Gated DeltaNet form (kda_fwd_scalar_gate) on
 the same workload with g [B, T, H] and dt_bias [H]: g then moves 2 B per
-(token, head) instead of 256.
+(token, head) instead of 256; with `--backward`, its backward
+(kda_bwd_scalar_gate).
 
 `--head-dim 64` measures the same workload at K = V = 64.
 
@@ -205,12 +206,21 @@ def bench_backward(args, torch, kda, kda_inputs):
     dA = torch.empty(w.H, device=dev)
     ddtb = torch.empty(w.H * w.K, device=dev)
     dinit = torch.empty(w.num_seqs, w.H, w.K, w.V, device=dev)
+    bwd = kda.bwd
+    if args.scalar_gate:
+        # the Gated DeltaNet form: one gate value per (token, head), channel 0
+        # of the workload's gate, and dt_bias per head
+        d["g"] = d["g"][..., 0].contiguous()
+        d["dt_bias"] = d["dt_bias"].view(w.H, w.K)[:, 0].contiguous()
+        dg = torch.empty(w.B, w.T, w.H, dtype=bf, device=dev)
+        ddtb = torch.empty(w.H, device=dev)
+        bwd = kda.bwd_scalar_gate
 
     def step():
-        kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], d["A_log"], d["dt_bias"],
-                d["lower_bound"], dO, dq, dk, dv, dg, dbeta, dA, ddt_bias=ddtb,
-                initial_state=d["initial_state"], d_final_state=dF, d_initial_state=dinit,
-                cu_seqlens=d["cu_seqlens"])
+        bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], d["A_log"], d["dt_bias"],
+            d["lower_bound"], dO, dq, dk, dv, dg, dbeta, dA, ddt_bias=ddtb,
+            initial_state=d["initial_state"], d_final_state=dF, d_initial_state=dinit,
+            cu_seqlens=d["cu_seqlens"])
 
     log(f"[bench] backward warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -256,7 +266,7 @@ def bench_backward(args, torch, kda, kda_inputs):
     total_bytes = th * 2308 + st_in + 2 * st32
     dom = max(names, key=lambda n: stage[n])
     achieved = kb[dom] / (stage[dom] * 1e-3) / 1e9
-    tr = stored_traffic(name, dom, backward=True)
+    tr = None if args.scalar_gate else stored_traffic(name, dom, backward=True)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": tr["total_bytes"] if tr else None,
                 "traffic_x_algorithmic": tr["total_bytes"] / kb[dom] if tr else None,
@@ -265,7 +275,8 @@ def bench_backward(args, torch, kda, kda_inputs):
     path = {"algorithmic_bytes": total_bytes, "hbm_achieved_GBs": path_gbs,
             "hbm_frac": path_gbs / HBM_PEAK_GBS, "stage_ms": stage,
             "stage_traffic_bytes": {k: (t["total_bytes"] if t else None) for k, t in
-                                    ((k, stored_traffic(name, k, backward=True)) for k in names)},
+                                    ((k, None if args.scalar_gate else
+                                      stored_traffic(name, k, backward=True)) for k in names)},
             # per (chunk slot, head): the two scans' records (5 + 7, 9 + 13 or
             # 17 + 26 KB at K = 64, 128, 256), S0 and dS1 (bf16 K x V), X
             # (bf16 16 x V), the partial sums (max(K, 128) + 1 floats)
@@ -274,7 +285,7 @@ def bench_backward(args, torch, kda, kda_inputs):
                                     2 * w.K * w.V * 2 + BWD_CHUNK * w.V * 2 +
                                     (max(w.K, 128) + 1) * 4))}
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.scalar_gate:
         import oracle
         # every head at K <= 128 (about 10 s on 16 threads at 128), a quarter
         # of them at 256 (four times the work per head)
@@ -287,7 +298,8 @@ def bench_backward(args, torch, kda, kda_inputs):
                "cores": oracle.max_threads(), "cpu_model": cpu_model(), "kind": "oracle",
                "sample": f"{w.name}: heads {heads[0]}..{heads[-1]} of {w.H}, all {w.tokens} "
                          f"tokens, fp64 C/OpenMP reverse-mode token recurrence, {dt:.2f} s wall"}
-    rec = {"metric": f"KDA bwd tokens/s @T={w.T},H={w.H},D={w.K} (gradients of every input)",
+    form = " (Gated DeltaNet form)" if args.scalar_gate else ""
+    rec = {"metric": f"KDA bwd tokens/s @T={w.T},H={w.H},D={w.K} (gradients of every input){form}",
            "value": w.tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
