@@ -392,6 +392,7 @@ def _attention_function():
         @staticmethod
         def forward(ctx, q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, scale,
                     lower_bound, output_final_state):
+            scalar = g.dim() == 3                           # Gated DeltaNet form
             B, T, H, K = q.shape
             V = v.shape[-1]
             N = B if cu_seqlens is None else cu_seqlens.numel() - 1
@@ -399,10 +400,11 @@ def _attention_function():
             fs = None
             if output_final_state:
                 fs = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
-            fwd(q, k, v, g, beta, scale, o, A_log, dt_bias, lower_bound,
+            (fwd_scalar_gate if scalar else fwd)(
+                q, k, v, g, beta, scale, o, A_log, dt_bias, lower_bound,
                 initial_state=initial_state, final_state=fs, cu_seqlens=cu_seqlens)
             ctx.save_for_backward(q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens)
-            ctx.scale, ctx.lower_bound = scale, lower_bound
+            ctx.scale, ctx.lower_bound, ctx.scalar = scale, lower_bound, scalar
             return o, fs
 
         @staticmethod
@@ -416,7 +418,8 @@ def _attention_function():
             dinit = None
             if init is not None and ctx.needs_input_grad[7]:
                 dinit = torch.empty(init.shape, dtype=torch.float32, device=q.device)
-            bwd(q, k, v, g, beta, ctx.scale, A_log, dt_bias, ctx.lower_bound, d_o, dq, dk, dv,
+            (bwd_scalar_gate if ctx.scalar else bwd)(
+                q, k, v, g, beta, ctx.scale, A_log, dt_bias, ctx.lower_bound, d_o, dq, dk, dv,
                 dg, dbeta, dA, ddt_bias=ddt, initial_state=init, d_final_state=d_fs,
                 d_initial_state=dinit, cu_seqlens=cu)
             if dinit is not None:
@@ -432,7 +435,9 @@ def attention(q, k, v, g, beta, A_log, dt_bias, lower_bound, scale=None, initial
     """Differentiable KDA: returns (o, final_state), o bf16 [B, T, H, V] and
     final_state fp32 [N, H, K, V] (None unless output_final_state), with
     gradients through kda_bwd for q, k, v, g, beta, A_log, dt_bias and
-    initial_state.  Arguments as fwd; scale defaults to K^-1/2."""
+    initial_state.  Arguments as fwd; scale defaults to K^-1/2.  A gate g of
+    shape [B, T, H] (dt_bias [H] or None) selects the Gated DeltaNet form
+    (fwd_scalar_gate, bwd_scalar_gate)."""
     if scale is None:
         scale = q.shape[-1] ** -0.5
     return _attention_function().apply(q, k, v, g, beta, A_log, dt_bias, initial_state,

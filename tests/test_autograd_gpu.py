@@ -82,3 +82,35 @@ def test_output_only_and_default_scale():
     assert torch.equal(o, o_ref)
     for n, t in x.items():
         assert torch.equal(t.grad, gr[n]), n
+
+
+def test_scalar_gate_form():
+    """A gate of shape [B, T, H] selects the Gated DeltaNet form: outputs and
+    gradients equal to fwd_scalar_gate and bwd_scalar_gate called directly."""
+    inp = kda_inputs.random_small(624, B=1, T=70, H=2, seq_lens=(30, 40), initial_state=True)
+    d = to_device(inp)
+    d["g"] = d["g"][..., 0].contiguous()
+    d["dt_bias"] = d["dt_bias"].view(2, -1)[:, 0].contiguous()
+    init = d["initial_state"].float()
+    d_out, d_final = kda_inputs.output_grads(625, 1, 70, 2, N=2)
+    d_out, d_final = d_out.cuda(), d_final.cuda()
+    x = leaves(d, init)
+    o, fs = kda.attention(x["q"], x["k"], x["v"], x["g"], x["beta"], x["A_log"], x["dt_bias"],
+                          d["lower_bound"], scale=d["scale"], initial_state=x["initial_state"],
+                          output_final_state=True, cu_seqlens=d["cu_seqlens"])
+    ((o.float() * d_out.float()).sum() + (fs * d_final).sum()).backward()
+    o_ref = torch.empty_like(o)
+    fs_ref = torch.empty_like(fs)
+    kda.fwd_scalar_gate(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], o_ref, d["A_log"],
+                        d["dt_bias"], d["lower_bound"], initial_state=init, final_state=fs_ref,
+                        cu_seqlens=d["cu_seqlens"])
+    gr = {n: torch.empty_like(d[n]) for n in NAMES}
+    gr["initial_state"] = torch.empty_like(init)
+    kda.bwd_scalar_gate(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], d["A_log"],
+                        d["dt_bias"], d["lower_bound"], d_out, gr["q"], gr["k"], gr["v"], gr["g"],
+                        gr["beta"], gr["A_log"], ddt_bias=gr["dt_bias"], initial_state=init,
+                        d_final_state=d_final, d_initial_state=gr["initial_state"],
+                        cu_seqlens=d["cu_seqlens"])
+    assert torch.equal(o, o_ref) and torch.equal(fs, fs_ref)
+    for n, t in x.items():
+        assert torch.equal(t.grad, gr[n]), n
